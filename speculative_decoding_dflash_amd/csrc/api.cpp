@@ -1,0 +1,673 @@
+// Host side of libdflash: argument checking, workspace layout, KV page tables, and the launch
+// sequences of the three step calls.  See include/dflash.h for the contract.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+using namespace df;
+
+namespace {
+
+thread_local std::string g_err;
+
+dflash_status fail(dflash_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_OK(expr)                                                                                 \
+  do {                                                                                               \
+    hipError_t e_ = (expr);                                                                          \
+    if (e_ != hipSuccess) return fail(DFLASH_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
+
+constexpr int kSplitMax = 16;    // GEMM K splits
+constexpr int kAttnSplitMax = 64;
+constexpr int kCounters = 8192;
+
+// Workspace carve-up; offsets in bytes.
+struct Layout {
+  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, partial, counters, att_o, att_ml, cbuf, dlogits, cid, cp,
+      cn, total;
+  size_t partial_floats, att_rows;
+};
+
+Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t R = cap->max_rows, H = c->hidden, QD = (size_t)c->q_heads * c->head_dim,
+               KD = (size_t)c->kv_heads * c->head_dim, F = c->ffn, V = c->vocab, es = esize(c);
+  const size_t B = d->block_size;
+  L.state = take(sizeof(SlotState) * cap->max_slots);
+  L.err = take(sizeof(int32_t) * ERR_COUNT);
+  L.bt = take(sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq);
+  for (int s = 0; s < 3; ++s)
+    for (int k = 0; k < 4; ++k) L.rows[s][k] = take(sizeof(int32_t) * R);
+  L.x = take(sizeof(float) * R * H);
+  L.xn = take(es * R * H);
+  L.qbuf = take(es * R * QD);
+  L.attn = take(es * R * QD);
+  L.ffn = take(es * R * F);
+  size_t nmax = std::max({QD + 2 * KD, 2 * F, H, (size_t)d->layers * 2 * KD});
+  L.partial_floats = (size_t)kSplitMax * kGemmMaxRows * nmax;
+  L.partial = take(sizeof(float) * L.partial_floats);
+  L.counters = take(sizeof(int32_t) * kCounters);
+  L.att_rows = (size_t)cap->max_slots * B;
+  L.att_o = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * c->head_dim);
+  L.att_ml = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * 2);
+  L.cbuf = take(sizeof(float) * R * H);
+  L.dlogits = take(sizeof(float) * cap->max_slots * (B > 1 ? B - 1 : 1) * V);
+  const size_t srows = (size_t)cap->max_slots * std::max<size_t>(B, 1);
+  L.cid = take(sizeof(int32_t) * srows * kMaxTopK);
+  L.cp = take(sizeof(float) * srows * kMaxTopK);
+  L.cn = take(sizeof(int32_t) * srows);
+  L.total = off;
+  return L;
+}
+
+const char *check_cfg(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
+  if (!c || !d || !cap) return "null configuration";
+  if (c->dtype != DFLASH_BF16 && c->dtype != DFLASH_F32) return "dtype must be DFLASH_BF16 or DFLASH_F32";
+  if (c->layers < 1 || c->hidden < 32 || c->q_heads < 1 || c->kv_heads < 1 || c->ffn < 16 || c->vocab < 2)
+    return "model dimensions must be positive";
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 32, 64 or 128";
+  if (c->q_heads % c->kv_heads) return "q_heads must be a multiple of kv_heads";
+  if (c->q_heads / c->kv_heads > 64) return "at most 64 query heads per KV head";
+  const int qd = c->q_heads * c->head_dim, kd = c->kv_heads * c->head_dim;
+  if (c->hidden % 128 || qd % 128 || kd % 128 || c->vocab % 128)
+    return "hidden, q_heads*head_dim, kv_heads*head_dim and vocab must be multiples of 128";
+  if (c->ffn % 64) return "ffn must be a multiple of 64";
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps > 0.f)) return "rope_theta and rms_eps must be positive";
+  if (d->layers < 1 || d->n_taps < 1 || d->n_taps > DFLASH_MAX_TAPS) return "drafter layers / taps out of range";
+  for (int i = 0; i < d->n_taps; ++i)
+    if (d->taps[i] < 0 || d->taps[i] >= c->layers) return "tap layer out of range";
+  if (d->block_size < 1 || d->block_size > DFLASH_MAX_BLOCK) return "block_size out of range";
+  if (d->mask_id < 0 || d->mask_id >= c->vocab) return "mask_id out of range";
+  if (d->window < 0) return "window must be >= 0";
+  if (cap->max_slots < 1 || cap->max_slots > DFLASH_MAX_BATCH) return "max_slots out of range";
+  if (cap->max_rows < cap->max_slots * d->block_size) return "max_rows must be at least max_slots * block_size";
+  if (cap->page_tokens != 16) return "page_tokens must be 16";
+  if (cap->num_pages < 1 || cap->max_pages_per_seq < 1) return "page counts must be positive";
+  return nullptr;
+}
+
+}  // namespace
+
+struct dflash_ctx {
+  dflash_model_cfg cfg;
+  dflash_drafter_cfg dcfg;
+  dflash_capacity cap;
+  std::vector<dflash_layer_weights> tl, dl;
+  const void *embed, *final_norm, *lm_head, *fc, *hidden_norm, *d_final_norm;
+  char *tkv, *dkv, *ws;
+  Layout L;
+  KVLayout kvl;
+  size_t layer_elems;  // elements of one layer's pool
+  // host page tables
+  std::vector<std::vector<int32_t>> pages;
+  std::vector<int32_t> free_pages;
+  std::vector<int> prefilled;
+  // the last verify call, for draft / accept consistency
+  int last_qlen = 0, last_nlogit = 0, last_batch = 0;
+  std::vector<int32_t> last_slots;
+  bool verified = false;
+
+  template <typename P> P *wsp(size_t off) const { return reinterpret_cast<P *>(ws + off); }
+  SlotState *state() const { return wsp<SlotState>(L.state); }
+  int32_t *err() const { return wsp<int32_t>(L.err); }
+  int32_t *bt() const { return wsp<int32_t>(L.bt); }
+  Rows rows(int s) const {
+    Rows r;
+    r.pos = wsp<int32_t>(L.rows[s][0]);
+    r.slot = wsp<int32_t>(L.rows[s][1]);
+    r.valid = wsp<int32_t>(L.rows[s][2]);
+    r.tok = wsp<int32_t>(L.rows[s][3]);
+    return r;
+  }
+  int dt() const { return cfg.dtype == DFLASH_BF16 ? 0 : 1; }
+  int es() const { return esize(&cfg); }
+  void *tlayer(int l) const { return tkv + (size_t)l * layer_elems * es(); }
+  void *dlayer(int l) const { return dkv + (size_t)l * layer_elems * es(); }
+  int max_ctx(const int32_t *slots, int batch) const {
+    int m = 0;
+    for (int b = 0; b < batch; ++b) m = std::max<int>(m, (int)pages[slots[b]].size() * cap.page_tokens);
+    return m;
+  }
+};
+
+namespace {
+
+int gemm_target_wgs() {
+  static int v = [] {
+    const char *e = getenv("DFLASH_GEMM_WGS");
+    return e ? std::max(1, atoi(e)) : 1024;
+  }();
+  return v;
+}
+
+// K split so that the launch has about gemm_target_wgs() work-groups.
+void choose_split(int tiles, int K, int kstep, int *split, int *kchunk) {
+  const int quantum = kstep * 4;
+  const int max_split = std::max(1, K / quantum);
+  int s = std::max(1, gemm_target_wgs() / std::max(1, tiles));
+  s = std::min({s, kSplitMax, max_split});
+  int kc = (K + s - 1) / s;
+  kc = (kc + quantum - 1) / quantum * quantum;
+  *kchunk = kc;
+  *split = (K + kc - 1) / kc;
+}
+
+GemmArgs gemm_base(dflash_ctx *c, const void *x, int ldx, int M, int N, int K, int epi, int group) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.ldx = ldx;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.epi = epi;
+  a.group = group;
+  a.partial = c->wsp<float>(c->L.partial);
+  a.counters = c->wsp<int32_t>(c->L.counters);
+  a.block_table = c->bt();
+  a.bt_stride = c->cap.max_pages_per_seq;
+  a.kv = c->kvl;
+  a.theta = c->cfg.rope_theta;
+  a.eps = c->cfg.rms_eps;
+  a.err = c->err();
+  const int tiles = epi == EPI_SWIGLU ? N / 16 : N / 32;
+  choose_split(tiles, K, c->cfg.dtype == DFLASH_BF16 ? 32 : 16, &a.split, &a.kchunk);
+  return a;
+}
+
+// Run a GEMM over R rows in chunks of kGemmMaxRows.  `a.x` points at row 0; input rows advance by ldx.
+dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
+  const char *x0 = (const char *)a.x;
+  for (int r0 = 0; r0 < R; r0 += kGemmMaxRows) {
+    GemmArgs b = a;
+    b.M = std::min(kGemmMaxRows, R - r0);
+    b.x = x0 + (size_t)r0 * a.ldx * c->es();
+    b.row_off = r0;
+    if ((size_t)b.split * b.M * (b.epi == EPI_SWIGLU ? 2 * b.N : b.N) > c->L.partial_floats)
+      return fail(DFLASH_E_INVAL, "GEMM partial buffer too small");
+    HIP_OK(launch_gemm(b, c->dt(), s));
+  }
+  return DFLASH_OK;
+}
+
+dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_len, int mode, void *kv, int ctx_bound,
+                            hipStream_t s) {
+  const dflash_model_cfg &m = c->cfg;
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = c->wsp<void>(c->L.qbuf);
+  a.ldq = m.q_heads * m.head_dim;
+  a.kv = kv;
+  a.kvl = c->kvl;
+  a.block_table = c->bt();
+  a.bt_stride = c->cap.max_pages_per_seq;
+  a.rows = rows;
+  a.n_seq = n_seq;
+  a.q_len = q_len;
+  a.q_heads = m.q_heads;
+  a.mode = mode;
+  a.window = c->dcfg.window;
+  const int G = m.q_heads / m.kv_heads;
+  a.q_tile = std::max(1, std::min(q_len, 64 / G));
+  const int ntile = (q_len + a.q_tile - 1) / a.q_tile;
+  const int wgs = n_seq * m.kv_heads * ntile;
+  const int pt = c->cap.page_tokens;
+  int key_span = ctx_bound + pt;  // keys of the widest work-group, rounded out to pages
+  if (mode == 1 && c->dcfg.window > 0) key_span = std::min(key_span, c->dcfg.window + q_len + 2 * pt);
+  const int pages = (key_span + pt - 1) / pt;
+  int splits = 1;
+  if ((size_t)n_seq * q_len <= c->L.att_rows) {
+    splits = std::max(1, 512 / std::max(1, wgs));
+    splits = std::min({splits, kAttnSplitMax, std::max(1, pages / 4)});
+  }
+  const int pps = (pages + splits - 1) / splits;
+  a.n_splits = (pages + pps - 1) / pps;
+  a.split_tokens = pps * pt;
+  a.part_o = c->wsp<float>(c->L.att_o);
+  a.part_ml = c->wsp<float>(c->L.att_ml);
+  a.out = c->wsp<void>(c->L.attn);
+  a.ldo = m.q_heads * m.head_dim;
+  a.err = c->err();
+  (void)wgs;
+  HIP_OK(launch_attention(a, c->dt(), s));
+  return DFLASH_OK;
+}
+
+// One decoder layer over R rows (x fp32 in place).  feat: optional tap output (act, row stride ld_feat).
+dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows, int n_seq,
+                        int q_len, int attn_mode, int ctx_bound, void *feat, int ld_feat, hipStream_t s) {
+  const dflash_model_cfg &m = c->cfg;
+  const int R = n_seq * q_len, H = m.hidden, QD = m.q_heads * m.head_dim, KD = m.kv_heads * m.head_dim, F = m.ffn;
+  float *x = c->wsp<float>(c->L.x);
+  void *xn = c->wsp<void>(c->L.xn);
+  dflash_status st;
+  HIP_OK(launch_rmsnorm(x, H, R, R, 0, R, (const float *)w.attn_norm, m.rms_eps, H, xn, H, c->dt(), s));
+  {
+    GemmArgs a = gemm_base(c, xn, H, R, QD + 2 * KD, H, EPI_QKV, 128);
+    a.nseg = 3;
+    a.seg[0] = GemmSeg{w.wq, QD, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
+    a.seg[1] = GemmSeg{w.wk, KD, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
+    a.seg[2] = GemmSeg{w.wv, KD, ROLE_V, nullptr, kv_layer, 0};
+    a.rows = rows;
+    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+  }
+  if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, s)) != DFLASH_OK) return st;
+  {
+    GemmArgs a = gemm_base(c, c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID, 32);
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{w.wo, H, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.resid = x;
+    a.ld_resid = H;
+    a.rows = rows;
+    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+  }
+  HIP_OK(launch_rmsnorm(x, H, R, R, 0, R, (const float *)w.ffn_norm, m.rms_eps, H, xn, H, c->dt(), s));
+  {
+    GemmArgs a = gemm_base(c, xn, H, R, F, H, EPI_SWIGLU, 32);
+    a.nseg = 2;
+    a.seg[0] = GemmSeg{w.w_gate, F, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.seg[1] = GemmSeg{w.w_up, F, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.out_act = c->wsp<void>(c->L.ffn);
+    a.ld_out = F;
+    a.rows = rows;
+    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+  }
+  {
+    GemmArgs a = gemm_base(c, c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID, 32);
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{w.w_down, H, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.resid = x;
+    a.ld_resid = H;
+    a.feat = feat;
+    a.ld_feat = ld_feat;
+    a.rows = rows;
+    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status check_slots(dflash_ctx *c, int batch, const int32_t *slots, bool need_prefilled) {
+  if (batch < 1 || batch > c->cap.max_slots) return fail(DFLASH_E_INVAL, "batch %d out of range", batch);
+  if (!slots) return fail(DFLASH_E_INVAL, "slots is null");
+  for (int b = 0; b < batch; ++b) {
+    const int s = slots[b];
+    if (s < 0 || s >= c->cap.max_slots) return fail(DFLASH_E_INVAL, "slot %d out of range", s);
+    for (int q = 0; q < b; ++q)
+      if (slots[q] == s) return fail(DFLASH_E_INVAL, "slot %d repeated", s);
+    if (c->pages[s].empty()) return fail(DFLASH_E_STATE, "slot %d has no KV pages (call dflash_kv_alloc)", s);
+    if (need_prefilled && !c->prefilled[s]) return fail(DFLASH_E_STATE, "slot %d has not been prefilled", s);
+  }
+  return DFLASH_OK;
+}
+
+bool same_slots(dflash_ctx *c, int batch, const int32_t *slots) {
+  if (batch != c->last_batch) return false;
+  for (int b = 0; b < batch; ++b)
+    if (slots[b] != c->last_slots[b]) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_last_error(void) { return g_err.c_str(); }
+
+size_t dflash_kv_pool_bytes(const dflash_model_cfg *cfg, int32_t layers, const dflash_capacity *cap) {
+  if (!cfg || !cap || layers < 1 || cap->num_pages < 1 || cap->page_tokens < 1) return 0;
+  return (size_t)layers * cap->num_pages * 2 * cfg->kv_heads * cap->page_tokens * cfg->head_dim * esize(cfg);
+}
+
+size_t dflash_workspace_bytes(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg, const dflash_capacity *cap) {
+  if (check_cfg(cfg, dcfg, cap)) return 0;
+  return make_layout(cfg, dcfg, cap).total;
+}
+
+dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg, const dflash_target_weights *tw,
+                            const dflash_drafter_weights *dw, const dflash_capacity *cap, void *d_target_kv,
+                            void *d_drafter_kv, void *d_workspace, hipStream_t stream, dflash_ctx **out) {
+  if (!out) return fail(DFLASH_E_INVAL, "out is null");
+  *out = nullptr;
+  if (const char *why = check_cfg(cfg, dcfg, cap)) return fail(DFLASH_E_INVAL, "%s", why);
+  if (!tw || !dw || !tw->layers || !dw->layers || !tw->embed || !tw->final_norm || !tw->lm_head || !dw->fc ||
+      !dw->hidden_norm || !dw->final_norm)
+    return fail(DFLASH_E_INVAL, "missing weight pointer");
+  auto layer_ok = [](const dflash_layer_weights &w) {
+    return w.attn_norm && w.wq && w.wk && w.wv && w.q_norm && w.k_norm && w.wo && w.ffn_norm && w.w_gate && w.w_up &&
+           w.w_down;
+  };
+  for (int l = 0; l < cfg->layers; ++l)
+    if (!layer_ok(tw->layers[l])) return fail(DFLASH_E_INVAL, "missing weight pointer in target layer %d", l);
+  for (int l = 0; l < dcfg->layers; ++l)
+    if (!layer_ok(dw->layers[l])) return fail(DFLASH_E_INVAL, "missing weight pointer in drafter layer %d", l);
+  if (!d_target_kv || !d_drafter_kv || !d_workspace) return fail(DFLASH_E_INVAL, "null pool or workspace");
+  if (((uintptr_t)d_target_kv | (uintptr_t)d_drafter_kv | (uintptr_t)d_workspace) & 255)
+    return fail(DFLASH_E_INVAL, "pools and workspace must be 256-byte aligned");
+
+  dflash_ctx *c = new dflash_ctx();
+  c->cfg = *cfg;
+  c->dcfg = *dcfg;
+  c->cap = *cap;
+  c->tl.assign(tw->layers, tw->layers + cfg->layers);
+  c->dl.assign(dw->layers, dw->layers + dcfg->layers);
+  c->embed = tw->embed;
+  c->final_norm = tw->final_norm;
+  c->lm_head = tw->lm_head;
+  c->fc = dw->fc;
+  c->hidden_norm = dw->hidden_norm;
+  c->d_final_norm = dw->final_norm;
+  c->tkv = (char *)d_target_kv;
+  c->dkv = (char *)d_drafter_kv;
+  c->ws = (char *)d_workspace;
+  c->L = make_layout(cfg, dcfg, cap);
+  c->kvl = KVLayout{cap->page_tokens, cfg->kv_heads, cfg->head_dim};
+  c->layer_elems = (size_t)cap->num_pages * c->kvl.page_elems();
+  c->pages.assign(cap->max_slots, {});
+  c->prefilled.assign(cap->max_slots, 0);
+  for (int p = cap->num_pages - 1; p >= 0; --p) c->free_pages.push_back(p);
+  hipError_t e = hipMemsetAsync(c->ws + c->L.state, 0, c->L.rows[0][0] - c->L.state, stream);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(c->ws + c->L.bt, 0xff, sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq, stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->ws + c->L.counters, 0, sizeof(int32_t) * kCounters, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
+  }
+  *out = c;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_destroy(dflash_ctx *ctx) {
+  delete ctx;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_kv_alloc(dflash_ctx *c, int32_t slot, int32_t n_tokens) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  if (slot < 0 || slot >= c->cap.max_slots) return fail(DFLASH_E_INVAL, "slot %d out of range", slot);
+  if (n_tokens < 1) return fail(DFLASH_E_INVAL, "n_tokens must be positive");
+  const int need = (n_tokens + c->cap.page_tokens - 1) / c->cap.page_tokens;
+  if (need > c->cap.max_pages_per_seq)
+    return fail(DFLASH_E_INVAL, "%d tokens exceed max_pages_per_seq", n_tokens);
+  std::vector<int32_t> &pg = c->pages[slot];
+  const int have = (int)pg.size();
+  if (need <= have) return DFLASH_OK;
+  if ((int)c->free_pages.size() < need - have)
+    return fail(DFLASH_E_NOMEM, "KV pool exhausted: slot %d needs %d more pages, %zu free", slot, need - have,
+                c->free_pages.size());
+  for (int i = have; i < need; ++i) {
+    pg.push_back(c->free_pages.back());
+    c->free_pages.pop_back();
+  }
+  hipError_t e = hipMemcpy(c->bt() + (size_t)slot * c->cap.max_pages_per_seq + have, pg.data() + have,
+                           sizeof(int32_t) * (need - have), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    for (int i = need - 1; i >= have; --i) {
+      c->free_pages.push_back(pg[i]);
+      pg.pop_back();
+    }
+    return fail(DFLASH_E_DEVICE, "block-table upload: %s", hipGetErrorString(e));
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_kv_free(dflash_ctx *c, int32_t slot) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  if (slot < 0 || slot >= c->cap.max_slots) return fail(DFLASH_E_INVAL, "slot %d out of range", slot);
+  std::vector<int32_t> &pg = c->pages[slot];
+  if (!pg.empty()) {
+    std::vector<int32_t> neg(pg.size(), -1);
+    hipError_t e = hipMemcpy(c->bt() + (size_t)slot * c->cap.max_pages_per_seq, neg.data(), sizeof(int32_t) * neg.size(),
+                             hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(DFLASH_E_DEVICE, "block-table clear: %s", hipGetErrorString(e));
+    for (int i = (int)pg.size() - 1; i >= 0; --i) c->free_pages.push_back(pg[i]);
+    pg.clear();
+  }
+  c->prefilled[slot] = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots,
+                                  const int32_t *d_tokens, int32_t q_len, int32_t new_sequence, int32_t n_logit_rows,
+                                  float *d_logits, void *d_feats) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  dflash_status st = check_slots(c, batch, slots, !new_sequence);
+  if (st != DFLASH_OK) return st;
+  if (q_len < 1 || (size_t)batch * q_len > (size_t)c->cap.max_rows)
+    return fail(DFLASH_E_INVAL, "q_len %d with batch %d exceeds max_rows %d", q_len, batch, c->cap.max_rows);
+  if (n_logit_rows < 1 || n_logit_rows > q_len) return fail(DFLASH_E_INVAL, "n_logit_rows out of range");
+  if ((size_t)batch * n_logit_rows > (size_t)c->cap.max_rows)
+    return fail(DFLASH_E_INVAL, "batch * n_logit_rows exceeds max_rows");
+  if (!d_tokens || !d_logits) return fail(DFLASH_E_INVAL, "null tokens or logits");
+  for (int b = 0; b < batch; ++b)
+    if ((int)c->pages[slots[b]].size() * c->cap.page_tokens < q_len)
+      return fail(DFLASH_E_NOMEM, "slot %d holds fewer KV pages than q_len", slots[b]);
+
+  const dflash_model_cfg &m = c->cfg;
+  const int R = batch * q_len, H = m.hidden;
+  Rows rows = c->rows(0);
+  PrepArgs p;
+  memset(&p, 0, sizeof p);
+  p.batch = batch;
+  for (int b = 0; b < batch; ++b) p.slots[b] = slots[b];
+  p.q_len = q_len;
+  p.new_sequence = new_sequence;
+  p.state = c->state();
+  p.rows = rows;
+  p.tokens = d_tokens;
+  p.mode = 0;
+  p.vocab = m.vocab;
+  p.err = c->err();
+  HIP_OK(launch_prep(p, s));
+  HIP_OK(launch_embed(c->embed, c->dt(), rows, R, H, m.vocab, c->wsp<float>(c->L.x), c->err(), s));
+  const int ctx_bound = c->max_ctx(slots, batch);
+  const int ld_feat = c->dcfg.n_taps * H;
+  for (int l = 0; l < m.layers; ++l) {
+    void *feat = nullptr;
+    for (int t = 0; t < c->dcfg.n_taps; ++t)
+      if (c->dcfg.taps[t] == l && d_feats) feat = (char *)d_feats + (size_t)t * H * c->es();
+    st = run_layer(c, c->tl[l], c->tlayer(l), rows, batch, q_len, 0, ctx_bound, feat, ld_feat, s);
+    if (st != DFLASH_OK) return st;
+  }
+  const int nl = n_logit_rows;
+  HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.x), H, nl, q_len, q_len - nl, batch * nl, (const float *)c->final_norm,
+                        m.rms_eps, H, c->wsp<void>(c->L.xn), H, c->dt(), s));
+  GemmArgs a = gemm_base(c, c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32, 32);
+  a.nseg = 1;
+  a.seg[0] = GemmSeg{c->lm_head, m.vocab, ROLE_PLAIN, nullptr, nullptr, 0};
+  a.out_f32 = d_logits;
+  a.ld_out = m.vocab;
+  if ((st = run_gemm(c, a, batch * nl, s)) != DFLASH_OK) return st;
+
+  for (int b = 0; b < batch; ++b)
+    if (new_sequence) c->prefilled[slots[b]] = 1;
+  c->last_qlen = q_len;
+  c->last_nlogit = nl;
+  c->last_batch = batch;
+  c->last_slots.assign(slots, slots + batch);
+  c->verified = true;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_accept_resample(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots,
+                                     const float *d_logits, const int32_t *d_block, int32_t n_draft,
+                                     const dflash_sampling *sampling, int32_t *d_out, int32_t *d_n_out,
+                                     int32_t *d_cand_ids, float *d_cand_p) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  dflash_status st = check_slots(c, batch, slots, true);
+  if (st != DFLASH_OK) return st;
+  if (!c->verified || !same_slots(c, batch, slots))
+    return fail(DFLASH_E_STATE, "accept_resample must follow dflash_verify_block on the same slots");
+  if (n_draft < 0 || n_draft + 1 != c->last_nlogit)
+    return fail(DFLASH_E_INVAL, "n_draft + 1 must equal the n_logit_rows of the last verify (%d)", c->last_nlogit);
+  if (n_draft > 0 && !d_block) return fail(DFLASH_E_INVAL, "null block");
+  if (!d_logits || !d_out || !d_n_out || !sampling) return fail(DFLASH_E_INVAL, "null argument");
+  for (int b = 0; b < batch; ++b) {
+    const dflash_sampling &sp = sampling[b];
+    if (!(sp.temperature >= 0.f)) return fail(DFLASH_E_INVAL, "temperature must be >= 0");
+    if (sp.temperature > 0.f) {
+      if (sp.top_k < 1 || sp.top_k > DFLASH_MAX_TOPK) return fail(DFLASH_E_INVAL, "top_k must be in [1, %d]", DFLASH_MAX_TOPK);
+      if (!(sp.top_p > 0.f) || sp.top_p > 1.f) return fail(DFLASH_E_INVAL, "top_p must be in (0, 1]");
+    }
+  }
+  const int rows = batch * (n_draft + 1);
+  if ((size_t)rows > (size_t)c->cap.max_slots * std::max(1, c->dcfg.block_size))
+    return fail(DFLASH_E_INVAL, "batch * (n_draft + 1) exceeds max_slots * block_size");
+  FilterArgs f;
+  memset(&f, 0, sizeof f);
+  f.logits = d_logits;
+  f.rows = rows;
+  f.vocab = c->cfg.vocab;
+  f.rows_per_seq = n_draft + 1;
+  for (int b = 0; b < batch; ++b) {
+    f.temperature[b] = sampling[b].temperature;
+    f.top_k[b] = sampling[b].top_k;
+    f.top_p[b] = sampling[b].top_p;
+  }
+  f.cand_id = c->wsp<int32_t>(c->L.cid);
+  f.cand_p = c->wsp<float>(c->L.cp);
+  f.cand_n = c->wsp<int32_t>(c->L.cn);
+  HIP_OK(launch_filter(f, s));
+  DecideArgs d;
+  memset(&d, 0, sizeof d);
+  d.batch = batch;
+  for (int b = 0; b < batch; ++b) {
+    d.slots[b] = slots[b];
+    d.seed[b] = sampling[b].seed;
+  }
+  d.n_draft = n_draft;
+  d.block = d_block;
+  d.cand_id = f.cand_id;
+  d.cand_p = f.cand_p;
+  d.cand_n = f.cand_n;
+  d.state = c->state();
+  d.out = d_out;
+  d.n_out = d_n_out;
+  d.err = c->err();
+  HIP_OK(launch_decide(d, s));
+  if (d_cand_ids || d_cand_p) HIP_OK(launch_copy_cands(f.cand_id, f.cand_p, f.cand_n, rows, d_cand_ids, d_cand_p, s));
+  c->verified = false;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const void *d_feats,
+                                 int32_t *d_block, float *d_logits) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  dflash_status st = check_slots(c, batch, slots, true);
+  if (st != DFLASH_OK) return st;
+  if (!d_feats || !d_block) return fail(DFLASH_E_INVAL, "null features or block");
+  if (c->last_qlen < 1 || !same_slots(c, batch, slots))
+    return fail(DFLASH_E_STATE, "draft_block must use the slots of the last verified block");
+  const dflash_model_cfg &m = c->cfg;
+  const dflash_drafter_cfg &dc = c->dcfg;
+  const int B = dc.block_size, H = m.hidden, KD = m.kv_heads * m.head_dim;
+  if (B < 2) return fail(DFLASH_E_INVAL, "block_size 1 has no drafts");
+  for (int b = 0; b < batch; ++b)
+    if ((int)c->pages[slots[b]].size() * c->cap.page_tokens < B)
+      return fail(DFLASH_E_NOMEM, "slot %d holds fewer KV pages than the block", slots[b]);
+
+  // 1. KV injection of the rows committed by the last accept.
+  const int Q = c->last_qlen, Ri = batch * Q;
+  Rows ri = c->rows(1);
+  PrepArgs p;
+  memset(&p, 0, sizeof p);
+  p.batch = batch;
+  for (int b = 0; b < batch; ++b) p.slots[b] = slots[b];
+  p.q_len = Q;
+  p.state = c->state();
+  p.rows = ri;
+  p.mode = 1;
+  p.mask_id = dc.mask_id;
+  p.vocab = m.vocab;
+  p.err = c->err();
+  HIP_OK(launch_prep(p, s));
+  {
+    GemmArgs a = gemm_base(c, d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_STORE_F32, 32);
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{c->fc, H, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.out_f32 = c->wsp<float>(c->L.cbuf);
+    a.ld_out = H;
+    if ((st = run_gemm(c, a, Ri, s)) != DFLASH_OK) return st;
+  }
+  HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.cbuf), H, Ri, Ri, 0, Ri, (const float *)c->hidden_norm, m.rms_eps, H,
+                        c->wsp<void>(c->L.xn), H, c->dt(), s));
+  {
+    GemmArgs a = gemm_base(c, c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_QKV, 128);
+    if (2 * dc.layers > kGemmMaxSeg) return fail(DFLASH_E_INVAL, "too many drafter layers for one injection launch");
+    a.nseg = 2 * dc.layers;
+    for (int j = 0; j < dc.layers; ++j) {
+      a.seg[2 * j] = GemmSeg{c->dl[j].wk, KD, ROLE_K, (const float *)c->dl[j].k_norm, c->dlayer(j), 0};
+      a.seg[2 * j + 1] = GemmSeg{c->dl[j].wv, KD, ROLE_V, nullptr, c->dlayer(j), 0};
+    }
+    a.rows = ri;
+    if ((st = run_gemm(c, a, Ri, s)) != DFLASH_OK) return st;
+  }
+  // 2. The block [anchor, MASK x (B-1)].
+  Rows rd = c->rows(2);
+  p.rows = rd;
+  p.q_len = B;
+  p.mode = 2;
+  p.block_out = d_block;
+  HIP_OK(launch_prep(p, s));
+  const int R = batch * B;
+  HIP_OK(launch_embed(c->embed, c->dt(), rd, R, H, m.vocab, c->wsp<float>(c->L.x), c->err(), s));
+  const int ctx_bound = c->max_ctx(slots, batch);
+  for (int j = 0; j < dc.layers; ++j) {
+    st = run_layer(c, c->dl[j], c->dlayer(j), rd, batch, B, 1, ctx_bound, nullptr, 0, s);
+    if (st != DFLASH_OK) return st;
+  }
+  const int nd = B - 1;
+  HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.x), H, nd, B, 1, batch * nd, (const float *)c->d_final_norm, m.rms_eps, H,
+                        c->wsp<void>(c->L.xn), H, c->dt(), s));
+  float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
+  GemmArgs a = gemm_base(c, c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32, 32);
+  a.nseg = 1;
+  a.seg[0] = GemmSeg{c->lm_head, m.vocab, ROLE_PLAIN, nullptr, nullptr, 0};
+  a.out_f32 = logits;
+  a.ld_out = m.vocab;
+  if ((st = run_gemm(c, a, batch * nd, s)) != DFLASH_OK) return st;
+  HIP_OK(launch_argmax(logits, batch * nd, m.vocab, nd, B, 1, d_block, s));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_device_status(dflash_ctx *c, hipStream_t s) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  HIP_OK(hipStreamSynchronize(s));
+  int32_t flags[ERR_COUNT];
+  HIP_OK(hipMemcpy(flags, c->err(), sizeof flags, hipMemcpyDeviceToHost));
+  if (flags[ERR_TOKEN] || flags[ERR_PAGE] || flags[ERR_STATE]) {
+    HIP_OK(hipMemset(c->err(), 0, sizeof flags));
+    return fail(DFLASH_E_DEVICE, "device check failed:%s%s%s", flags[ERR_TOKEN] ? " token id out of range" : "",
+                flags[ERR_PAGE] ? " position without a KV page" : "", flags[ERR_STATE] ? " inconsistent slot state" : "");
+  }
+  return DFLASH_OK;
+}
+
+}  // extern "C"

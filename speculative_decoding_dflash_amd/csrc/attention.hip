@@ -1,0 +1,287 @@
+// Paged attention on MFMA for the verify block (causal) and the draft block (bidirectional block +
+// sliding-window injected context), gfx950.
+//
+// One work-group = (sequence, KV head, tile of query positions, key split); its 4 waves take the key
+// pages of the split round-robin and merge through LDS at the end.  All query heads of the KV head's
+// group and all positions of the tile are packed as "query vectors" (qv) into 16-wide MFMA tiles, so
+// every K/V page is read once per work-group.
+//   scores    S^T[key][qv] = K[key] . Q[qv]   (A = K page rows, B = Q^T held in registers)
+//   output    O^T[dim][qv] += V^T[dim][key] P^T[key][qv]
+// The accumulator layout of S^T (lane: qv = lane % 16, keys 4*(lane/16) + r) is exactly the B
+// operand layout of the second product, so probabilities never leave registers.  K is stored
+// token-major and V dim-major inside a page, so both A operands are contiguous loads.
+// Softmax is online in fp32 (running max per qv, corrections applied to the accumulators); a split
+// that sees no allowed key publishes m = -inf, l = 0.  Several splits are merged by a second kernel.
+#include "kernels.h"
+
+namespace df {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int D> struct AttnFrag;
+
+template <int D> struct AttnFrag<bf16, D> {
+  static constexpr int kSteps = D / 32;  // QK^T steps of 32 dims (8 per lane)
+  static DF_DEVICE u32x4 load_q(const bf16 *qrow, int ks, int g) {
+    return *reinterpret_cast<const u32x4 *>(qrow + ks * 32 + g * 8);
+  }
+  static DF_DEVICE void qk(f32x4 &acc, const bf16 *kblk, int key, int g, const u32x4 *q) {
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const u32x4 k = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 32 + g * 8);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), __builtin_bit_cast(bf16x8, q[ks]),
+                                                    acc, 0, 0, 0);
+    }
+  }
+  // p[r]: probability of key 4g + r for this lane's qv.
+  static DF_DEVICE void pv(f32x4 *o, const bf16 *vblk, int l16, int g, const float *p) {
+    s16x4 pb;
+    pb[0] = (short)f32_to_bf16(p[0]);
+    pb[1] = (short)f32_to_bf16(p[1]);
+    pb[2] = (short)f32_to_bf16(p[2]);
+    pb[3] = (short)f32_to_bf16(p[3]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2 v = *reinterpret_cast<const u32x2 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb, o[dt], 0, 0, 0);
+    }
+  }
+};
+
+template <int D> struct AttnFrag<float, D> {
+  static constexpr int kSteps = D / 16;  // 16 dims per step (4 per lane), as 4 K=4 slices
+  static DF_DEVICE u32x4 load_q(const float *qrow, int ks, int g) {
+    return *reinterpret_cast<const u32x4 *>(qrow + ks * 16 + g * 4);
+  }
+  static DF_DEVICE void qk(f32x4 &acc, const float *kblk, int key, int g, const u32x4 *q) {
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const u32x4 k = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 16 + g * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[j]), __builtin_bit_cast(float, q[ks][j]),
+                                                   acc, 0, 0, 0);
+    }
+  }
+  static DF_DEVICE void pv(f32x4 *o, const float *vblk, int l16, int g, const float *p) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[j]), p[j], o[dt], 0, 0, 0);
+    }
+  }
+};
+
+template <typename T, int D, int NQT>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  using F = AttnFrag<T, D>;
+  __shared__ float so[4][16][D + 1];
+  __shared__ float sm[4][NQT * 16], sl[4][NQT * 16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int kvh = a.kvl.kv_heads, G = a.q_heads / kvh;
+  const int ntile = (a.q_len + a.q_tile - 1) / a.q_tile;
+  int bx = blockIdx.x;
+  const int qt = bx % ntile;
+  bx /= ntile;
+  const int kh = bx % kvh;
+  const int b = bx / kvh;
+  const int split = blockIdx.y;
+  const int p0 = qt * a.q_tile;
+  const int np = min(a.q_tile, a.q_len - p0);
+  const int nqv = np * G;
+  const int rbase = b * a.q_len + p0;
+  const float scale = 1.0f / sqrtf((float)D);
+  const float NEG = -INFINITY;
+
+  int qpos[NQT];
+  bool qok[NQT];
+  u32x4 q[NQT][F::kSteps];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int qv = t * 16 + l16;
+    qok[t] = qv < nqv;
+    const int row = rbase + (qok[t] ? qv / G : 0);
+    const int head = kh * G + (qok[t] ? qv % G : 0);
+    qpos[t] = a.rows.pos[row];
+    const T *qrow = (const T *)a.q + (size_t)row * a.ldq + head * D;
+#pragma unroll
+    for (int ks = 0; ks < F::kSteps; ++ks) q[t][ks] = F::load_q(qrow, ks, g);
+  }
+
+  const int first_pos = a.rows.pos[rbase], last_pos = a.rows.pos[rbase + np - 1];
+  int klo, khi, nblk = 0;
+  if (a.mode == 0) {
+    klo = 0;
+    khi = last_pos + 1;
+  } else {
+    nblk = a.rows.pos[b * a.q_len];
+    khi = nblk + a.q_len;
+    klo = a.window > 0 ? max(0, first_pos - a.window + 1) : 0;
+  }
+  const int pt = a.kvl.page_tokens;
+  const int kstart = (klo / pt) * pt + split * a.split_tokens;
+  const int kstop = min(khi, kstart + a.split_tokens);
+  const int slot = a.rows.slot[rbase];
+  const int32_t *bt = a.block_table + (size_t)slot * a.bt_stride;
+
+  float m[NQT], l[NQT];
+  f32x4 o[NQT][D / 16];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    m[t] = NEG;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int ps = kstart + wave * pt; ps < kstop; ps += 4 * pt) {
+    const int pidx = ps / pt;
+    const int page = pidx < a.bt_stride ? bt[pidx] : -1;
+    if (page < 0) {
+      if (lane == 0) raise_err(a.err, ERR_PAGE);
+      continue;
+    }
+    const T *kblk = (const T *)a.kv + a.kvl.block(page, 0, kh);
+    const T *vblk = (const T *)a.kv + a.kvl.block(page, 1, kh);
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      F::qk(s, kblk, l16, g, q[t]);  // lane holds S^T[key = 4g + r][qv = l16]... keys index A rows
+      float sv[4], mx = NEG;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = ps + 4 * g + r;
+        bool ok = qok[t] && kp >= klo && kp < khi;
+        if (a.mode == 0) ok = ok && kp <= qpos[t];
+        else ok = ok && (kp >= nblk || a.window <= 0 || qpos[t] - kp < a.window);
+        sv[r] = ok ? s[r] * scale : NEG;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[t], mx);
+      const float corr = (m[t] == NEG) ? 0.f : expf(m[t] - mn);
+      float p[4], ps_sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = (sv[r] == NEG) ? 0.f : expf(sv[r] - mn);
+        ps_sum += p[r];
+      }
+      l[t] = l[t] * corr + ps_sum;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
+      F::pv(o[t], vblk, l16, g, p);
+      m[t] = mn;
+    }
+  }
+
+  // Merge the four waves, one 16-qv tile at a time.
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (g == 0) {
+      sm[wave][t * 16 + l16] = m[t];
+      sl[wave][t * 16 + l16] = lt;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) so[wave][l16][dt * 16 + 4 * g + r] = o[t][dt][r];
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int qi = e / D, dim = e % D;
+      const int qv = t * 16 + qi;
+      if (qv >= nqv) continue;
+      float M = NEG;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][t * 16 + qi]);
+      float L = 0.f, O = 0.f;
+      if (M != NEG) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mw = sm[w][t * 16 + qi];
+          const float f = (mw == NEG) ? 0.f : expf(mw - M);
+          L += f * sl[w][t * 16 + qi];
+          O += f * so[w][qi][dim];
+        }
+      }
+      const int row = rbase + qv / G, head = kh * G + qv % G;
+      if (a.n_splits == 1) {
+        Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
+      } else {
+        const size_t pi = ((size_t)row * a.q_heads + head) * a.n_splits + split;
+        a.part_o[pi * D + dim] = O;
+        if (dim == 0) {
+          a.part_ml[pi * 2] = M;
+          a.part_ml[pi * 2 + 1] = L;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out[row][head] = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s  (splits in order)
+template <typename T>
+__global__ void attn_merge_kernel(AttnArgs a, int n_rows) {
+  const int rh = blockIdx.x;  // row * q_heads + head
+  const int D = a.kvl.head_dim;
+  const int row = rh / a.q_heads, head = rh % a.q_heads;
+  const float NEG = -INFINITY;
+  const float *ml = a.part_ml + (size_t)rh * a.n_splits * 2;
+  float M = NEG;
+  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int dim = threadIdx.x; dim < D; dim += blockDim.x) {
+    float L = 0.f, O = 0.f;
+    if (M != NEG) {
+      for (int s = 0; s < a.n_splits; ++s) {
+        const float ms = ml[2 * s];
+        const float f = (ms == NEG) ? 0.f : expf(ms - M);
+        L += f * ml[2 * s + 1];
+        O += f * a.part_o[((size_t)rh * a.n_splits + s) * D + dim];
+      }
+    }
+    Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
+  const int G = a.q_heads / a.kvl.kv_heads;
+  const int nqt = (a.q_tile * G + 15) / 16;
+  const int ntile = (a.q_len + a.q_tile - 1) / a.q_tile;
+  dim3 grid(a.n_seq * a.kvl.kv_heads * ntile, a.n_splits), block(256);
+  switch (nqt) {
+    case 1: hipLaunchKernelGGL((attn_kernel<T, D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<T, D, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attn_kernel<T, D, 3>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_kernel<T, D, 4>), grid, block, 0, s, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  const int n_rows = a.n_seq * a.q_len;
+  hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(n_rows * a.q_heads), dim3(D), 0, s, a, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s) {
+  const int D = a.kvl.head_dim;
+  if (dtype == 0) {
+    if (D == 128) return launch_attn_t<bf16, 128>(a, s);
+    if (D == 64) return launch_attn_t<bf16, 64>(a, s);
+    if (D == 32) return launch_attn_t<bf16, 32>(a, s);
+  } else {
+    if (D == 128) return launch_attn_t<float, 128>(a, s);
+    if (D == 64) return launch_attn_t<float, 64>(a, s);
+    if (D == 32) return launch_attn_t<float, 32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace df

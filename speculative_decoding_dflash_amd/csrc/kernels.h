@@ -1,0 +1,142 @@
+// Internal launch interface between the host side (api.cpp) and the kernels.  Not part of the ABI.
+#pragma once
+#include "common.h"
+
+namespace df {
+
+// ---------------------------------------------------------------- GEMM: Y = X W^T with fused epilogues
+constexpr int kGemmMaxSeg = 16;
+constexpr int kGemmMaxRows = 64;  // rows per launch; longer inputs are chunked by the host
+
+enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+enum SegRole { ROLE_PLAIN = 0, ROLE_Q = 1, ROLE_K = 2, ROLE_V = 3 };
+
+struct GemmSeg {
+  const void *w;      // [n, K] row-major weight rows of this segment
+  int32_t n;          // rows
+  int32_t role;       // SegRole (EPI_QKV only)
+  const float *gain;  // per-head RMSNorm gain (ROLE_Q, ROLE_K)
+  void *dst;          // ROLE_Q: dense output [rows][ld_dst]; ROLE_K/ROLE_V: KV pool base of the layer
+  int32_t ld_dst;
+};
+
+struct GemmArgs {
+  const void *x;
+  int32_t ldx;
+  int32_t M, N, K;      // N: output columns (SWIGLU: ffn width; otherwise total segment rows)
+  int32_t split, kchunk;  // K is cut into `split` ranges of kchunk elements
+  int32_t group;        // epilogue group width (columns); 32 for column-local epilogues
+  float *partial;       // [split][M][N] fp32 when several work-groups meet in one group
+  int32_t *counters;    // one arrival counter per group, zero between launches
+  int32_t nseg;
+  GemmSeg seg[kGemmMaxSeg];
+  int32_t epi;
+  float *out_f32;       // EPI_STORE_F32
+  void *out_act;        // EPI_STORE_ACT, EPI_SWIGLU
+  int32_t ld_out;
+  float *resid;         // EPI_RESID: resid += Y
+  int32_t ld_resid;
+  void *feat;           // EPI_RESID, optional: feat = act(resid after the add)
+  int32_t ld_feat;
+  Rows rows;
+  int32_t row_off;      // global row of local row 0
+  const int32_t *block_table;
+  int32_t bt_stride;
+  KVLayout kv;
+  float theta, eps;
+  int32_t *err;
+};
+
+// dtype: 0 bf16, 1 fp32.  Returns hipSuccess or the launch error.
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- small kernels
+struct PrepArgs {
+  int32_t batch;
+  int32_t slots[64];
+  int32_t q_len;
+  int32_t new_sequence;
+  SlotState *state;
+  Rows rows;
+  const int32_t *tokens;  // verify: caller tokens [batch*q_len]
+  int32_t mode;           // 0 verify, 1 draft-inject rows, 2 draft block rows
+  int32_t mask_id;
+  int32_t vocab;
+  int32_t *block_out;     // mode 2: block[b * q_len] = anchor
+  int32_t *err;
+};
+hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
+
+// x[r] = embed[tok[r]] (fp32 residual stream)
+hipError_t launch_embed(const void *embed, int dtype, const Rows &rows, int32_t n_rows, int32_t hidden, int32_t vocab,
+                        float *x, int32_t *err, hipStream_t s);
+
+// Row i of out = act(rmsnorm(row (i / take) * stride + offset + i % take of in) * gain); in is fp32.
+hipError_t launch_rmsnorm(const float *in, int32_t ld_in, int32_t take, int32_t stride, int32_t offset, int32_t n_rows,
+                          const float *gain, float eps, int32_t hidden, void *out, int32_t ld_out, int dtype,
+                          hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void *q;
+  int32_t ldq;
+  const void *kv;  // layer pool base
+  KVLayout kvl;
+  const int32_t *block_table;
+  int32_t bt_stride;
+  Rows rows;
+  int32_t n_seq, q_len;  // rows are [n_seq][q_len]
+  int32_t q_heads;
+  int32_t mode;          // 0 causal (keys <= query position); 1 draft (block keys + window context)
+  int32_t window;        // draft: context key k allowed when qpos - k < window (0: unbounded)
+  int32_t q_tile;        // query positions per work-group
+  int32_t n_splits;      // key-range splits
+  int32_t split_tokens;  // keys per split (multiple of page_tokens)
+  float *part_o;         // [rows*q_heads][n_splits][head_dim]
+  float *part_ml;        // [rows*q_heads][n_splits][2]
+  void *out;             // [rows][q_heads*head_dim] act
+  int32_t ldo;
+  int32_t *err;
+};
+hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- sampler
+struct FilterArgs {
+  const float *logits;  // [rows][vocab]
+  int32_t rows, vocab;
+  int32_t rows_per_seq;
+  float temperature[64];
+  int32_t top_k[64];
+  float top_p[64];
+  int32_t *cand_id;     // [rows][kMaxTopK]
+  float *cand_p;        // [rows][kMaxTopK]
+  int32_t *cand_n;      // [rows]
+};
+constexpr int kMaxTopK = 256;
+hipError_t launch_filter(const FilterArgs &a, hipStream_t s);
+
+struct DecideArgs {
+  int32_t batch;
+  int32_t slots[64];
+  uint64_t seed[64];
+  int32_t n_draft;
+  const int32_t *block;   // [batch][n_draft + 1]: anchor, then drafts
+  const int32_t *cand_id;
+  const float *cand_p;
+  const int32_t *cand_n;
+  SlotState *state;
+  int32_t *out;
+  int32_t *n_out;
+  int32_t *err;
+};
+hipError_t launch_decide(const DecideArgs &a, hipStream_t s);
+
+// Row argmax of fp32 logits (lowest index on ties); row r goes to out[(r / take) * stride + offset + r % take].
+hipError_t launch_argmax(const float *logits, int32_t rows, int32_t vocab, int32_t take, int32_t stride, int32_t offset,
+                         int32_t *out, hipStream_t s);
+
+// copy candidate lists out for tests
+hipError_t launch_copy_cands(const int32_t *cid, const float *cp, const int32_t *cn, int32_t rows, int32_t *oid,
+                             float *op, hipStream_t s);
+
+}  // namespace df

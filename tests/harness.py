@@ -1,0 +1,143 @@
+"""Shared helpers of the GPU parity tests: build oracle and device models from the same synthetic
+weights, run the device path step by step, and compare it with the oracle teacher-forced on the
+device's own tokens (a flagged near-tie at one position cannot cascade)."""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from oracle.model import Drafter, Target
+from oracle.sampling import decide, sample_dist
+from synth import weights as sw
+
+
+def tol_of(cfg) -> float:
+    return 1e-4 if cfg.target.dtype == "fp32" else 2e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err_rows(g: np.ndarray, o: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64).reshape(len(o), -1)
+    o = np.asarray(o, dtype=np.float64).reshape(len(o), -1)
+    return np.abs(g - o).max(axis=1) / np.maximum(np.abs(o).max(axis=1), 1e-30)
+
+
+def near_tie_argmax(z: np.ndarray, tol: float) -> bool:
+    """Top-2 gap of a logit row within the comparison tolerance."""
+    s = np.sort(np.asarray(z, dtype=np.float64))[::-1]
+    return (s[0] - s[1]) <= 2 * tol * np.abs(z).max()
+
+
+def near_tie_filter(z: np.ndarray, sp, tol: float) -> bool:
+    """The top-k boundary or the top-p cut of a row sits within the tolerance."""
+    z = np.asarray(z, dtype=np.float64)
+    if sp.temperature <= 0:
+        return near_tie_argmax(z, tol)
+    s = np.sort(z / sp.temperature)[::-1]
+    scale = 2 * tol * np.abs(z).max() / sp.temperature
+    k = min(sp.top_k, len(s))
+    if k < len(s) and s[k - 1] - s[k] <= scale:
+        return True
+    e = np.exp(s[:k] - s[0])
+    c = np.cumsum(e / e.sum())
+    if sp.top_p < 1.0 and np.min(np.abs(c - sp.top_p)) < 50 * tol:
+        return True
+    return False
+
+
+def torch_weights(W: Dict[str, np.ndarray], cfg, device="cuda"):
+    import torch
+    dt = torch.bfloat16 if cfg.target.dtype == "bf16" else torch.float32
+    out = {}
+    for k, v in W.items():
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        out[k] = (t.to(torch.float32) if v.ndim == 1 else t.to(dt)).to(device)
+    return out
+
+
+@dataclass
+class StepReport:
+    logits_err: List[float] = field(default_factory=list)
+    draft_err: List[float] = field(default_factory=list)
+    flagged: int = 0
+    positions: int = 0
+    draft_flagged: int = 0
+    draft_mismatch: int = 0
+    taus: List[int] = field(default_factory=list)
+
+
+class OracleFollower:
+    """The oracle, teacher-forced on the device's committed tokens."""
+
+    def __init__(self, cfg, W, request: int):
+        self.cfg = cfg
+        self.t = Target(cfg.target, W, taps=cfg.drafter.taps)
+        self.d = Drafter(cfg.target, cfg.drafter, W)
+        self.tc = self.t.new_cache()
+        self.dc = self.d.new_cache()
+        self.n = 0
+        self.anchor = -1
+        self.request = request
+
+    def prefill(self, prompt):
+        z, feats = self.t.forward(self.tc, list(prompt), 0, logit_rows=len(prompt))
+        return z, feats
+
+    def commit(self, feats, start, committed, anchor):
+        self.d.inject(self.dc, feats[:committed], start)
+        self.n = start + committed
+        self.anchor = anchor
+
+
+def check_step(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_logits: np.ndarray,
+               g_dlogits: Optional[np.ndarray], g_ids: np.ndarray, g_p: np.ndarray, g_out: List[int], tol: float):
+    """Compare one device step with the oracle; returns the oracle's features for the commit."""
+    B = len(block)
+    n = fol.n
+    assert int(block[0]) == fol.anchor, (block[0], fol.anchor)
+    if g_dlogits is not None:
+        dz = fol.d.draft_logits(fol.dc, fol.anchor, n)
+        rep.draft_err.extend(rel_err_rows(g_dlogits, dz).tolist())
+        o_drafts = [int(np.argmax(r.astype(np.float32))) for r in dz]
+        for i in range(B - 1):
+            if o_drafts[i] != int(block[1 + i]):
+                if near_tie_argmax(dz[i], tol):
+                    rep.draft_flagged += 1
+                else:
+                    rep.draft_mismatch += 1
+    z, feats = fol.t.forward(fol.tc, [int(x) for x in block], n, logit_rows=B)
+    rep.logits_err.extend(rel_err_rows(g_logits, z).tolist())
+    # decide stage: bit-exact given the device's candidates
+    rows_g = []
+    for r in range(B):
+        k = int((g_ids[r] >= 0).sum())
+        rows_g.append((g_ids[r, :k].astype(np.int64), g_p[r, :k].astype(np.float32)))
+    want = decide(rows_g, [int(x) for x in block[1:]], n, sp.seed, fol.request)
+    assert want == list(g_out), ("decide mismatch", want, list(g_out))
+    # filter stage, same fp32 inputs: the oracle's filter applied to the device's logits gives the
+    # device's candidates (ids exactly; probabilities up to the last bits of exp)
+    for r in range(B):
+        rep.positions += 1
+        ids_o, p_o = sample_dist(g_logits[r].astype(np.float32), sp.temperature, sp.top_k, sp.top_p)
+        ids_g, p_g = rows_g[r]
+        if len(ids_o) != len(ids_g) or not np.array_equal(ids_o, ids_g) or \
+                np.abs(p_o.astype(np.float64) - p_g).max() > 2e-6:
+            # only a top-p cut sitting within float32 rounding of the threshold may differ
+            assert np.array_equal(ids_o[:min(len(ids_o), len(ids_g))], ids_g[:min(len(ids_o), len(ids_g))]), \
+                ("filter ids", r, ids_o[:8], ids_g[:8])
+            rep.flagged += 1
+        # the oracle's decision from its own logits agrees unless this position is a near tie
+        if r < len(g_out):
+            ids_x, _ = sample_dist(z[r].astype(np.float32), sp.temperature, sp.top_k, sp.top_p)
+            if sp.temperature <= 0 and int(ids_x[0]) != int(ids_g[0]):
+                assert near_tie_argmax(z[r], tol), ("greedy argmax differs without a near tie", r)
+                rep.draft_flagged += 1
+    rep.taus.append(len(g_out))
+    return feats

@@ -1,0 +1,76 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every function that
+include/dflash.h declares, sizes buffers, and rejects bad configurations before touching the device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|dflash_status|const char \*)\s*(dflash_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_step_calls():
+    names = header_functions()
+    for n in ("dflash_draft_block", "dflash_verify_block", "dflash_accept_resample", "dflash_kv_alloc",
+              "dflash_kv_free"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    from speculative_decoding_dflash_amd import binding as B
+    lib = C.CDLL(B.LIB_PATH)
+    for n in header_functions():
+        assert hasattr(lib, n), n
+
+
+def _cfgs(**over):
+    import synth
+    from speculative_decoding_dflash_amd.runner import drafter_cfg, model_cfg
+    from speculative_decoding_dflash_amd import binding as B
+    c = synth.SMALL
+    mc, dc = model_cfg(c.target), drafter_cfg(c.drafter)
+    cap = B.Capacity(4, 512, 16, 256, 64)
+    for k, v in over.items():
+        for o in (mc, dc, cap):
+            if hasattr(o, k):
+                setattr(o, k, v)
+                break
+    return mc, dc, cap
+
+
+def test_sizes_and_validation():
+    from speculative_decoding_dflash_amd import binding as B
+    mc, dc, cap = _cfgs()
+    ws = B.dflash_workspace_bytes(mc, dc, cap)
+    assert ws > 0
+    # KV pool: layers * pages * 2 * kv_heads * 16 * head_dim * 2 bytes
+    assert B.dflash_kv_pool_bytes(mc, 8, cap) == 8 * 256 * 2 * 8 * 16 * 64 * 2
+    for bad in (dict(head_dim=48), dict(q_heads=12), dict(block_size=0), dict(block_size=17), dict(mask_id=32000),
+                dict(page_tokens=8), dict(max_slots=65), dict(window=-1), dict(hidden=1000), dict(dtype=7)):
+        mc, dc, cap = _cfgs(**bad)
+        assert B.dflash_workspace_bytes(mc, dc, cap) == 0, bad
+
+
+def test_create_rejects_missing_pointers_without_device_work():
+    from speculative_decoding_dflash_amd import binding as B
+    mc, dc, cap = _cfgs()
+    tw, dw = B.TargetWeights(), B.DrafterWeights()
+    out = C.c_void_p()
+    st = B.lib.dflash_create(C.byref(mc), C.byref(dc), C.byref(tw), C.byref(dw), C.byref(cap), None, None, None, None,
+                             C.byref(out))
+    assert st == B.E_INVAL and out.value is None
+    assert "missing" in B.dflash_last_error()
+
+
+def test_null_context_calls_fail_cleanly():
+    from speculative_decoding_dflash_amd import binding as B
+    assert B.lib.dflash_kv_alloc(None, 0, 16) == B.E_INVAL
+    assert B.lib.dflash_kv_free(None, 0) == B.E_INVAL
+    assert B.lib.dflash_verify_block(None, None, 1, None, None, 8, 0, 8, None, None) == B.E_INVAL
+    assert B.lib.dflash_draft_block(None, None, 1, None, None, None, None) == B.E_INVAL
+    assert B.lib.dflash_accept_resample(None, None, 1, None, None, None, 7, None, None, None, None, None) == B.E_INVAL

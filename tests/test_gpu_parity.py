@@ -1,0 +1,235 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerances: logits rel-err (max |g - o| / max |o| per row) <= 1e-4 for fp32 models and <= 2e-2 for
+bf16 models.  Token decisions are compared bit-exactly where both sides take them from the same
+fp32 numbers (the decide stage given the device's candidates; the filter given the device's
+logits); decisions the oracle takes from its own logits may differ only at flagged near-ties.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import (OracleFollower, StepReport, check_step, log, near_tie_argmax, rel_err_rows, tol_of,
+                     torch_weights)
+from oracle.sampling import decide, sample_dist
+from oracle.spec import Sampling as OSampling
+from oracle.spec import SpecDecoder, ar_generate
+from synth import weights as sw
+
+pytestmark = pytest.mark.gpu
+
+
+def engine(cfg, W, **kw):
+    from speculative_decoding_dflash_amd.runner import Engine
+    return Engine(cfg, torch_weights(W, cfg), **kw)
+
+
+def samp(sp):
+    from speculative_decoding_dflash_amd.runner import sampling
+    return sampling(sp.temperature, sp.top_k, sp.top_p, sp.seed)
+
+
+def small_short(prompt_len=128, layers=8):
+    from dataclasses import replace
+    c = synth.SMALL
+    return replace(c, prompt_len=prompt_len, target=replace(c.target, layers=layers))
+
+
+CASES = {
+    "tiny": lambda: synth.TINY,
+    "small": lambda: small_short(),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_prefill_logits_and_features(name):
+    cfg = CASES[name]()
+    log(f"[prefill] {name}")
+    W = sw.model_weights(cfg, gain_std=0.1)
+    tol = tol_of(cfg)
+    P = cfg.prompt_len
+    eng = engine(cfg, W)
+    eng.kv_alloc(0, P + 64)
+    prompt = sw.prompt_ids(cfg.target.vocab, cfg.drafter.mask_id, P, 0)
+    toks = torch.from_numpy(prompt).to("cuda")
+    logits = torch.empty(P * cfg.target.vocab, dtype=torch.float32, device="cuda")
+    eng.verify([0], toks, P, True, P, logits=logits)
+    eng.status()
+    g = logits.view(P, -1).cpu().numpy()
+    gf = eng.feats[:P * len(cfg.drafter.taps) * cfg.target.hidden].view(P, len(cfg.drafter.taps), -1).float().cpu().numpy()
+    fol = OracleFollower(cfg, W, request=0)
+    z, feats = fol.prefill(prompt)
+    e = rel_err_rows(g, z)
+    ef = rel_err_rows(gf.reshape(P, -1), feats.reshape(P, -1))
+    log(f"  logits rel-err max {e.max():.3e} mean {e.mean():.3e}; features rel-err max {ef.max():.3e}")
+    assert e.max() <= tol
+    assert ef.max() <= (1e-4 if cfg.target.dtype == "fp32" else 2e-2)
+
+
+def run_e2e(cfg, W, sp, n_tokens, log_every=4):
+    tol = tol_of(cfg)
+    B = cfg.drafter.block_size
+    P = cfg.prompt_len
+    V = cfg.target.vocab
+    eng = engine(cfg, W)
+    eng.kv_alloc(0, P + n_tokens + 2 * B)
+    prompt = sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)
+    fol = OracleFollower(cfg, W, request=0)
+    s = samp(sp)
+    # prefill
+    eng.verify([0], torch.from_numpy(prompt).to("cuda"), P, True, 1)
+    eng.accept([0], 0, [s], cands=True)
+    z, feats = fol.prefill(prompt)
+    g_ids = eng.cand_ids[:256].cpu().numpy()
+    g_p = eng.cand_p[:256].cpu().numpy()
+    k = int((g_ids >= 0).sum())
+    first = decide([(g_ids[:k].astype(np.int64), g_p[:k])], [], P - 1, sp.seed, 0)
+    out0 = int(eng.out[0].item())
+    assert first == [out0]
+    fol.commit(feats, 0, P, out0)
+    stream = [out0]
+    rep = StepReport()
+    step = 0
+    while len(stream) < n_tokens:
+        eng.spec_step([0], [s], cands=True, draft_logits=True)
+        block = eng.block[:B].cpu().numpy()
+        g_logits = eng.logits[:B * V].view(B, V).cpu().numpy()
+        g_dl = eng.draft_logits[:(B - 1) * V].view(B - 1, V).cpu().numpy()
+        ids = eng.cand_ids[:B * 256].view(B, 256).cpu().numpy()
+        pp = eng.cand_p[:B * 256].view(B, 256).cpu().numpy()
+        tau = int(eng.n_out[0].item())
+        outs = [int(x) for x in eng.out[:tau].cpu().numpy()]
+        start = fol.n
+        feats = check_step(rep, fol, sp, block, g_logits, g_dl, ids, pp, outs, tol)
+        fol.commit(feats, start, tau, outs[-1])
+        stream.extend(outs)
+        if step % log_every == 0:
+            log(f"  step {step} tau {tau} logits err {max(rep.logits_err[-B:]):.2e} draft err "
+                f"{max(rep.draft_err[-(B - 1):]):.2e}")
+        step += 1
+    eng.status()
+    return stream[:n_tokens], rep, prompt
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+@pytest.mark.parametrize("mode", ["greedy", "sampled"])
+def test_e2e_teacher_forced(name, mode):
+    cfg = CASES[name]()
+    log(f"[e2e] {name} {mode}")
+    W = sw.model_weights(cfg, gain_std=0.1)
+    sp = synth.GREEDY if mode == "greedy" else cfg.sampling
+    n_tok = 64 if name == "tiny" else 24
+    stream, rep, prompt = run_e2e(cfg, W, sp, n_tok)
+    tol = tol_of(cfg)
+    le, de = np.array(rep.logits_err), np.array(rep.draft_err)
+    log(f"  logits err max {le.max():.3e}, draft logits err max {de.max():.3e}, flagged {rep.flagged}/"
+        f"{rep.positions}, draft flagged {rep.draft_flagged} mismatched {rep.draft_mismatch}, taus {rep.taus}")
+    assert le.max() <= tol and de.max() <= tol
+    assert rep.draft_mismatch == 0
+    if mode == "greedy" and name == "tiny":
+        from oracle.model import Target
+        tg = Target(cfg.target, W, taps=cfg.drafter.taps)
+        ar = ar_generate(tg, prompt, n_tok, OSampling(0.0, 0, 1.0, 1))
+        assert stream == ar
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_gpu_greedy_spec_equals_gpu_greedy_ar(name):
+    """Greedy speculative decoding on the device emits exactly the device's own greedy AR stream."""
+    cfg = CASES[name]()
+    log(f"[greedy spec == AR] {name}")
+    W = sw.model_weights(cfg)
+    P, B, V = cfg.prompt_len, cfg.drafter.block_size, cfg.target.vocab
+    n_tok = 48
+    prompt = torch.from_numpy(sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)).to("cuda")
+    g = samp(synth.GREEDY)
+    eng = engine(cfg, W)
+    eng.kv_alloc(0, P + n_tok + 2 * B)
+    eng.prefill([0], prompt.view(1, -1), [g])
+    ar = [int(eng.out[0].item())]
+    while len(ar) < n_tok:
+        eng.ar_step([0], [g])
+        ar.append(int(eng.out[0].item()))
+    eng.prefill([0], prompt.view(1, -1), [g])
+    spec = [int(eng.out[0].item())]
+    taus = []
+    while len(spec) < n_tok:
+        eng.spec_step([0], [g])
+        tau = int(eng.n_out[0].item())
+        taus.append(tau)
+        spec.extend(int(x) for x in eng.out[:tau].cpu().numpy())
+    eng.status()
+    log(f"  taus {taus[:20]}")
+    assert spec[:n_tok] == ar
+
+
+def test_sampler_chi_square_and_bitexact():
+    """Device accept/resample with planted drafts over many draws: decisions are bit-exact with the
+    oracle's rule applied to the device's candidates; the acceptance rate of a draft x is p(x) and the
+    rejection resample follows p without x (chi-square); candidate filter matches the oracle's."""
+    import scipy.stats
+    cfg = synth.TINY
+    W = sw.model_weights(cfg)
+    V, B = cfg.target.vocab, cfg.drafter.block_size
+    S = 64
+    eng = engine(cfg, W, max_slots=S, max_rows=S * B)
+    for s_ in range(S):
+        eng.kv_alloc(s_, 4 * B)
+    rng = np.random.default_rng(5)
+    # a fixed row distribution concentrated on 8 tokens, the rest far below
+    base = np.full(V, -30.0, dtype=np.float32)
+    hot = rng.choice(V, 8, replace=False)
+    base[hot] = rng.normal(0, 1.0, 8).astype(np.float32)
+    sp = synth.SamplingCfg(temperature=1.0, top_k=6, top_p=0.9, seed=0)
+    ids_o, p_o = sample_dist(base, 1.0, 6, 0.9)
+    x = int(ids_o[1])  # a mid-rank draft
+    logits = torch.from_numpy(np.tile(base, S * B)).to("cuda")
+    block = torch.full((S * B,), x, dtype=torch.int32, device="cuda")
+    toks = torch.zeros(S * B, dtype=torch.int32, device="cuda")
+    acc = 0
+    resample = np.zeros(V)
+    draws = 0
+    for call in range(60):
+        samplings = [samp(synth.SamplingCfg(1.0, 6, 0.9, 1000 * call + s_)) for s_ in range(S)]
+        eng.verify(list(range(S)), toks, B, True, B)
+        eng.accept(list(range(S)), B - 1, samplings, block=block, cands=True, logits=logits)
+        out = eng.out[:S * B].view(S, B).cpu().numpy()
+        nout = eng.n_out[:S].cpu().numpy()
+        gi_all = eng.cand_ids[:S * B * 256].view(S * B, 256).cpu().numpy()
+        gp_all = eng.cand_p[:S * B * 256].view(S * B, 256).cpu().numpy()
+        gi, gp = gi_all[0], gp_all[0]
+        k = int((gi >= 0).sum())
+        assert np.array_equal(gi[:k], ids_o) and np.abs(gp[:k] - p_o).max() <= 2e-6
+        assert (gi_all == gi).all() and (gp_all == gp).all()
+        rows = [(gi[:k].astype(np.int64), gp[:k])] * B
+        for s_ in range(S):
+            tau = int(nout[s_])
+            want = decide(rows, [x] * (B - 1), 0, 1000 * call + s_, s_)
+            assert want == list(out[s_, :tau]), (call, s_, want, out[s_, :tau])
+            draws += 1
+            if tau == 1:
+                resample[out[s_, 0]] += 1
+            else:
+                acc += 1
+    px = float(p_o[list(ids_o).index(x)])
+    z = (acc / draws - px) / np.sqrt(px * (1 - px) / draws)
+    log(f"  accept rate {acc / draws:.4f} vs p(x) {px:.4f} (z {z:.2f}); resample counts {resample[hot]}")
+    assert abs(z) < 4.5
+    r = np.zeros(V)
+    r[ids_o] = p_o
+    r[x] = 0
+    r /= r.sum()
+    sup = r > 0
+    assert resample[~sup].sum() == 0
+    assert scipy.stats.chisquare(resample[sup], r[sup] * resample.sum()).pvalue > 1e-4
+
+
+def test_gpu_generator_matches_cpu():
+    """The synthetic-weight fill on the device equals the CPU definition bit for bit."""
+    from synth import gpu as sg
+    for dtype, name, shape in [("bf16", "t.L0.wq", (96, 64)), ("fp32", "d.fc", (33, 17)), ("bf16", "t.embed", (7, 5))]:
+        t = torch.empty(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+        sg.fill(t, name, "w", 0, 0.02, dtype)
+        ref = sw.tensor(name, shape, "w", 0, 0.02, dtype)
+        assert np.array_equal(t.float().cpu().numpy(), ref)
