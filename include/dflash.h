@@ -142,8 +142,9 @@ size_t dflash_workspace_bytes(const dflash_model_cfg *cfg, const dflash_drafter_
 
 /* Create a context.  Pointers are borrowed.  d_target_kv must hold dflash_kv_pool_bytes(cfg,
  * cfg->layers, cap) bytes, d_drafter_kv dflash_kv_pool_bytes(cfg, dcfg->layers, cap) bytes and
- * d_workspace dflash_workspace_bytes(...) bytes, 256-byte aligned.  Clears the workspace's state on
- * `stream` and waits for it. */
+ * d_workspace dflash_workspace_bytes(...) bytes, 256-byte aligned.  Zero-fills both KV pools and the
+ * workspace's state on `stream` and waits for it (unwritten key slots of a page take part in the
+ * attention product with zero weight, which is exact only for finite contents). */
 dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg,
                             const dflash_target_weights *tw, const dflash_drafter_weights *dw,
                             const dflash_capacity *cap, void *d_target_kv, void *d_drafter_kv,
@@ -197,6 +198,13 @@ dflash_status dflash_accept_resample(dflash_ctx *ctx, hipStream_t stream, int32_
  * (d_logits != NULL) also writes those logits, fp32 [batch][B-1][vocab]. */
 dflash_status dflash_draft_block(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
                                  const void *d_feats, int32_t *d_block, float *d_logits);
+
+/* Operator-level access to the projection kernel used by every step (test and measurement access):
+ * d_y[m][n] = sum_k d_x[m][k] * d_w[n][k] (fp32 output) for m < M, with d_x [M][K] and d_w [N][K] in
+ * `dtype` (dflash_dtype), on the same code path as the model's projections.  N must be a multiple of
+ * 16 and K of 32 (bf16) or 16 (fp32).  Asynchronous on `stream`; needs no context. */
+dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
+                               const void *d_w, float *d_y);
 
 /* Synchronise `stream` and report device-side errors raised since the last call (sticky flags). */
 dflash_status dflash_device_status(dflash_ctx *ctx, hipStream_t stream);

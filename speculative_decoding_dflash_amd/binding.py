@@ -80,6 +80,7 @@ def _load() -> C.CDLL:
         "dflash_accept_resample": (I, [V, V, I, P(I), V, V, I, P(Sampling), V, V, V, V]),
         "dflash_draft_block": (I, [V, V, I, P(I), V, V, V]),
         "dflash_device_status": (I, [V, V]),
+        "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
         "dflash_last_error": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -159,6 +160,10 @@ def dflash_accept_resample(ctx: int, slots: Sequence[int], logits, block, n_draf
 def dflash_draft_block(ctx: int, slots: Sequence[int], feats, block, logits=None, stream=None):
     _check(lib.dflash_draft_block(ctx, _stream(stream), len(slots), _slots(slots), _ptr(feats), _ptr(block),
                                   _ptr(logits)))
+
+
+def dflash_op_linear(dtype: int, M: int, N: int, K: int, x, w, y, stream=None):
+    _check(lib.dflash_op_linear(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y)))
 
 
 def dflash_device_status(ctx: int, stream=None):

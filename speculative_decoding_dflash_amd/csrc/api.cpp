@@ -37,15 +37,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 
-constexpr int kSplitMax = 16;    // GEMM K splits
 constexpr int kAttnSplitMax = 64;
-constexpr int kCounters = 8192;
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, partial, counters, att_o, att_ml, cbuf, dlogits, cid, cp,
-      cn, total;
-  size_t partial_floats, att_rows;
+  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, qkvf, att_o, att_ml, cbuf, dlogits, cid, cp, cn, total;
+  size_t qkvf_cols, att_rows;
 };
 
 Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
@@ -69,10 +66,8 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.qbuf = take(es * R * QD);
   L.attn = take(es * R * QD);
   L.ffn = take(es * R * F);
-  size_t nmax = std::max({QD + 2 * KD, 2 * F, H, (size_t)d->layers * 2 * KD});
-  L.partial_floats = (size_t)kSplitMax * kGemmMaxRows * nmax;
-  L.partial = take(sizeof(float) * L.partial_floats);
-  L.counters = take(sizeof(int32_t) * kCounters);
+  L.qkvf_cols = std::max(QD + 2 * KD, (size_t)d->layers * 2 * KD);
+  L.qkvf = take(sizeof(float) * R * L.qkvf_cols);
   L.att_rows = (size_t)cap->max_slots * B;
   L.att_o = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * c->head_dim);
   L.att_ml = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * 2);
@@ -158,27 +153,7 @@ struct dflash_ctx {
 
 namespace {
 
-int gemm_target_wgs() {
-  static int v = [] {
-    const char *e = getenv("DFLASH_GEMM_WGS");
-    return e ? std::max(1, atoi(e)) : 1024;
-  }();
-  return v;
-}
-
-// K split so that the launch has about gemm_target_wgs() work-groups.
-void choose_split(int tiles, int K, int kstep, int *split, int *kchunk) {
-  const int quantum = kstep * 4;
-  const int max_split = std::max(1, K / quantum);
-  int s = std::max(1, gemm_target_wgs() / std::max(1, tiles));
-  s = std::min({s, kSplitMax, max_split});
-  int kc = (K + s - 1) / s;
-  kc = (kc + quantum - 1) / quantum * quantum;
-  *kchunk = kc;
-  *split = (K + kc - 1) / kc;
-}
-
-GemmArgs gemm_base(dflash_ctx *c, const void *x, int ldx, int M, int N, int K, int epi, int group) {
+GemmArgs gemm_base(const void *x, int ldx, int M, int N, int K, int epi) {
   GemmArgs a;
   memset(&a, 0, sizeof a);
   a.x = x;
@@ -187,33 +162,37 @@ GemmArgs gemm_base(dflash_ctx *c, const void *x, int ldx, int M, int N, int K, i
   a.N = N;
   a.K = K;
   a.epi = epi;
-  a.group = group;
-  a.partial = c->wsp<float>(c->L.partial);
-  a.counters = c->wsp<int32_t>(c->L.counters);
-  a.block_table = c->bt();
-  a.bt_stride = c->cap.max_pages_per_seq;
-  a.kv = c->kvl;
-  a.theta = c->cfg.rope_theta;
-  a.eps = c->cfg.rms_eps;
-  a.err = c->err();
-  const int tiles = epi == EPI_SWIGLU ? N / 16 : N / 32;
-  choose_split(tiles, K, c->cfg.dtype == DFLASH_BF16 ? 32 : 16, &a.split, &a.kchunk);
   return a;
 }
 
 // Run a GEMM over R rows in chunks of kGemmMaxRows.  `a.x` points at row 0; input rows advance by ldx.
-dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
+dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s) {
   const char *x0 = (const char *)a.x;
   for (int r0 = 0; r0 < R; r0 += kGemmMaxRows) {
     GemmArgs b = a;
     b.M = std::min(kGemmMaxRows, R - r0);
-    b.x = x0 + (size_t)r0 * a.ldx * c->es();
+    b.x = x0 + (size_t)r0 * a.ldx * es;
     b.row_off = r0;
-    if ((size_t)b.split * b.M * (b.epi == EPI_SWIGLU ? 2 * b.N : b.N) > c->L.partial_floats)
-      return fail(DFLASH_E_INVAL, "GEMM partial buffer too small");
-    HIP_OK(launch_gemm(b, c->dt(), s));
+    HIP_OK(launch_gemm(b, dt, s));
   }
   return DFLASH_OK;
+}
+
+dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) { return run_gemm(c->es(), c->dt(), a, R, s); }
+
+QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
+  QkvPostArgs p;
+  memset(&p, 0, sizeof p);
+  p.src = c->wsp<float>(c->L.qkvf);
+  p.n_rows = n_rows;
+  p.rows = rows;
+  p.block_table = c->bt();
+  p.bt_stride = c->cap.max_pages_per_seq;
+  p.kv = c->kvl;
+  p.theta = c->cfg.rope_theta;
+  p.eps = c->cfg.rms_eps;
+  p.err = c->err();
+  return p;
 }
 
 dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_len, int mode, void *kv, int ctx_bound,
@@ -269,44 +248,50 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   dflash_status st;
   HIP_OK(launch_rmsnorm(x, H, R, R, 0, R, (const float *)w.attn_norm, m.rms_eps, H, xn, H, c->dt(), s));
   {
-    GemmArgs a = gemm_base(c, xn, H, R, QD + 2 * KD, H, EPI_QKV, 128);
+    GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_STORE_F32);
     a.nseg = 3;
-    a.seg[0] = GemmSeg{w.wq, QD, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
-    a.seg[1] = GemmSeg{w.wk, KD, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
-    a.seg[2] = GemmSeg{w.wv, KD, ROLE_V, nullptr, kv_layer, 0};
-    a.rows = rows;
+    a.seg[0] = GemmSeg{w.wq, QD};
+    a.seg[1] = GemmSeg{w.wk, KD};
+    a.seg[2] = GemmSeg{w.wv, KD};
+    a.out_f32 = c->wsp<float>(c->L.qkvf);
+    a.ld_out = QD + 2 * KD;
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+    QkvPostArgs p = post_base(c, rows, R);
+    p.ld_src = QD + 2 * KD;
+    p.nseg = 3;
+    p.seg[0] = PostSeg{m.q_heads, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
+    p.seg[1] = PostSeg{m.kv_heads, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
+    p.seg[2] = PostSeg{m.kv_heads, ROLE_V, nullptr, kv_layer, 0};
+    p.total_heads = m.q_heads + 2 * m.kv_heads;
+    HIP_OK(launch_qkv_post(p, c->dt(), s));
   }
   if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, s)) != DFLASH_OK) return st;
   {
-    GemmArgs a = gemm_base(c, c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID, 32);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID);
     a.nseg = 1;
-    a.seg[0] = GemmSeg{w.wo, H, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.seg[0] = GemmSeg{w.wo, H};
     a.resid = x;
     a.ld_resid = H;
-    a.rows = rows;
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   HIP_OK(launch_rmsnorm(x, H, R, R, 0, R, (const float *)w.ffn_norm, m.rms_eps, H, xn, H, c->dt(), s));
   {
-    GemmArgs a = gemm_base(c, xn, H, R, F, H, EPI_SWIGLU, 32);
+    GemmArgs a = gemm_base(xn, H, R, F, H, EPI_SWIGLU);
     a.nseg = 2;
-    a.seg[0] = GemmSeg{w.w_gate, F, ROLE_PLAIN, nullptr, nullptr, 0};
-    a.seg[1] = GemmSeg{w.w_up, F, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.seg[0] = GemmSeg{w.w_gate, F};
+    a.seg[1] = GemmSeg{w.w_up, F};
     a.out_act = c->wsp<void>(c->L.ffn);
     a.ld_out = F;
-    a.rows = rows;
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   {
-    GemmArgs a = gemm_base(c, c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID, 32);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID);
     a.nseg = 1;
-    a.seg[0] = GemmSeg{w.w_down, H, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.seg[0] = GemmSeg{w.w_down, H};
     a.resid = x;
     a.ld_resid = H;
     a.feat = feat;
     a.ld_feat = ld_feat;
-    a.rows = rows;
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   return DFLASH_OK;
@@ -391,10 +376,13 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
   c->pages.assign(cap->max_slots, {});
   c->prefilled.assign(cap->max_slots, 0);
   for (int p = cap->num_pages - 1; p >= 0; --p) c->free_pages.push_back(p);
-  hipError_t e = hipMemsetAsync(c->ws + c->L.state, 0, c->L.rows[0][0] - c->L.state, stream);
+  // Pools start zeroed: unwritten key slots of a page are multiplied by zero probabilities in the
+  // attention product, which is only exact for finite contents.  Only finite values are stored later.
+  hipError_t e = hipMemsetAsync(c->tkv, 0, dflash_kv_pool_bytes(cfg, cfg->layers, cap), stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->dkv, 0, dflash_kv_pool_bytes(cfg, dcfg->layers, cap), stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->ws + c->L.state, 0, c->L.rows[0][0] - c->L.state, stream);
   if (e == hipSuccess)
     e = hipMemsetAsync(c->ws + c->L.bt, 0xff, sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq, stream);
-  if (e == hipSuccess) e = hipMemsetAsync(c->ws + c->L.counters, 0, sizeof(int32_t) * kCounters, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     delete c;
@@ -499,9 +487,9 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   const int nl = n_logit_rows;
   HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.x), H, nl, q_len, q_len - nl, batch * nl, (const float *)c->final_norm,
                         m.rms_eps, H, c->wsp<void>(c->L.xn), H, c->dt(), s));
-  GemmArgs a = gemm_base(c, c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32, 32);
+  GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;
-  a.seg[0] = GemmSeg{c->lm_head, m.vocab, ROLE_PLAIN, nullptr, nullptr, 0};
+  a.seg[0] = GemmSeg{c->lm_head, m.vocab};
   a.out_f32 = d_logits;
   a.ld_out = m.vocab;
   if ((st = run_gemm(c, a, batch * nl, s)) != DFLASH_OK) return st;
@@ -609,9 +597,9 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
   {
-    GemmArgs a = gemm_base(c, d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_STORE_F32, 32);
+    GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_STORE_F32);
     a.nseg = 1;
-    a.seg[0] = GemmSeg{c->fc, H, ROLE_PLAIN, nullptr, nullptr, 0};
+    a.seg[0] = GemmSeg{c->fc, H};
     a.out_f32 = c->wsp<float>(c->L.cbuf);
     a.ld_out = H;
     if ((st = run_gemm(c, a, Ri, s)) != DFLASH_OK) return st;
@@ -619,15 +607,22 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.cbuf), H, Ri, Ri, 0, Ri, (const float *)c->hidden_norm, m.rms_eps, H,
                         c->wsp<void>(c->L.xn), H, c->dt(), s));
   {
-    GemmArgs a = gemm_base(c, c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_QKV, 128);
-    if (2 * dc.layers > kGemmMaxSeg) return fail(DFLASH_E_INVAL, "too many drafter layers for one injection launch");
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_STORE_F32);
     a.nseg = 2 * dc.layers;
+    QkvPostArgs p = post_base(c, ri, Ri);
+    p.ld_src = dc.layers * 2 * KD;
+    p.nseg = 2 * dc.layers;
     for (int j = 0; j < dc.layers; ++j) {
-      a.seg[2 * j] = GemmSeg{c->dl[j].wk, KD, ROLE_K, (const float *)c->dl[j].k_norm, c->dlayer(j), 0};
-      a.seg[2 * j + 1] = GemmSeg{c->dl[j].wv, KD, ROLE_V, nullptr, c->dlayer(j), 0};
+      a.seg[2 * j] = GemmSeg{c->dl[j].wk, KD};
+      a.seg[2 * j + 1] = GemmSeg{c->dl[j].wv, KD};
+      p.seg[2 * j] = PostSeg{m.kv_heads, ROLE_K, (const float *)c->dl[j].k_norm, c->dlayer(j), 0};
+      p.seg[2 * j + 1] = PostSeg{m.kv_heads, ROLE_V, nullptr, c->dlayer(j), 0};
     }
-    a.rows = ri;
+    p.total_heads = dc.layers * 2 * m.kv_heads;
+    a.out_f32 = c->wsp<float>(c->L.qkvf);
+    a.ld_out = dc.layers * 2 * KD;
     if ((st = run_gemm(c, a, Ri, s)) != DFLASH_OK) return st;
+    HIP_OK(launch_qkv_post(p, c->dt(), s));
   }
   // 2. The block [anchor, MASK x (B-1)].
   Rows rd = c->rows(2);
@@ -647,14 +642,28 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.x), H, nd, B, 1, batch * nd, (const float *)c->d_final_norm, m.rms_eps, H,
                         c->wsp<void>(c->L.xn), H, c->dt(), s));
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
-  GemmArgs a = gemm_base(c, c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32, 32);
+  GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;
-  a.seg[0] = GemmSeg{c->lm_head, m.vocab, ROLE_PLAIN, nullptr, nullptr, 0};
+  a.seg[0] = GemmSeg{c->lm_head, m.vocab};
   a.out_f32 = logits;
   a.ld_out = m.vocab;
   if ((st = run_gemm(c, a, batch * nd, s)) != DFLASH_OK) return st;
   HIP_OK(launch_argmax(logits, batch * nd, m.vocab, nd, B, 1, d_block, s));
   return DFLASH_OK;
+}
+
+dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
+                               const void *d_w, float *d_y) {
+  if (dtype != DFLASH_BF16 && dtype != DFLASH_F32) return fail(DFLASH_E_INVAL, "bad dtype");
+  const int kstep = dtype == DFLASH_BF16 ? 32 : 16;
+  if (M < 1 || N < 16 || N % 16 || K < kstep || K % kstep) return fail(DFLASH_E_INVAL, "bad GEMM shape");
+  if (!d_x || !d_w || !d_y) return fail(DFLASH_E_INVAL, "null pointer");
+  GemmArgs a = gemm_base(d_x, K, M, N, K, EPI_STORE_F32);
+  a.nseg = 1;
+  a.seg[0] = GemmSeg{d_w, N};
+  a.out_f32 = d_y;
+  a.ld_out = N;
+  return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, s);
 }
 
 dflash_status dflash_device_status(dflash_ctx *c, hipStream_t s) {

@@ -58,20 +58,18 @@ template <int D> struct AttnFrag<float, D> {
   static DF_DEVICE void qk(f32x4 &acc, const float *kblk, int key, int g, const u32x4 *q) {
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      const u32x4 k = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 16 + g * 4);
+      const f32x4 k = *reinterpret_cast<const f32x4 *>(kblk + key * D + ks * 16 + g * 4);
+      const f32x4 qf = __builtin_bit_cast(f32x4, q[ks]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[j]), __builtin_bit_cast(float, q[ks][j]),
-                                                   acc, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k[j], qf[j], acc, 0, 0, 0);
     }
   }
   static DF_DEVICE void pv(f32x4 *o, const float *vblk, int l16, int g, const float *p) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[j]), p[j], o[dt], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], p[j], o[dt], 0, 0, 0);
     }
   }
 };

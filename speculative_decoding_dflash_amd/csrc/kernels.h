@@ -8,27 +8,19 @@ namespace df {
 constexpr int kGemmMaxSeg = 16;
 constexpr int kGemmMaxRows = 64;  // rows per launch; longer inputs are chunked by the host
 
-enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
 enum SegRole { ROLE_PLAIN = 0, ROLE_Q = 1, ROLE_K = 2, ROLE_V = 3 };
 
 struct GemmSeg {
-  const void *w;      // [n, K] row-major weight rows of this segment
-  int32_t n;          // rows
-  int32_t role;       // SegRole (EPI_QKV only)
-  const float *gain;  // per-head RMSNorm gain (ROLE_Q, ROLE_K)
-  void *dst;          // ROLE_Q: dense output [rows][ld_dst]; ROLE_K/ROLE_V: KV pool base of the layer
-  int32_t ld_dst;
+  const void *w;  // [n, K] row-major weight rows of this segment
+  int32_t n;      // rows
 };
 
 struct GemmArgs {
   const void *x;
   int32_t ldx;
   int32_t M, N, K;      // N: output columns (SWIGLU: ffn width; otherwise total segment rows)
-  int32_t split, kchunk;  // K is cut into `split` ranges of kchunk elements
-  int32_t group;        // epilogue group width (columns); 32 for column-local epilogues
-  float *partial;       // [split][M][N] fp32 when several work-groups meet in one group
-  int32_t *counters;    // one arrival counter per group, zero between launches
-  int32_t nseg;
+  int32_t nseg;         // segments concatenated along N (SWIGLU: 0 = gate, 1 = up)
   GemmSeg seg[kGemmMaxSeg];
   int32_t epi;
   float *out_f32;       // EPI_STORE_F32
@@ -38,17 +30,35 @@ struct GemmArgs {
   int32_t ld_resid;
   void *feat;           // EPI_RESID, optional: feat = act(resid after the add)
   int32_t ld_feat;
-  Rows rows;
   int32_t row_off;      // global row of local row 0
+};
+
+// dtype: 0 bf16, 1 fp32.  Returns hipSuccess or the launch error.
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s);
+
+// Per-head q/k RMSNorm + RoPE, then q to a dense buffer and k/v to the paged cache.
+struct PostSeg {
+  int32_t heads;
+  int32_t role;       // ROLE_Q / ROLE_K / ROLE_V
+  const float *gain;  // head-dim RMSNorm gain (Q, K)
+  void *dst;          // Q: dense [rows][ld_dst]; K/V: KV pool base of the layer
+  int32_t ld_dst;
+};
+struct QkvPostArgs {
+  const float *src;  // [rows][total_heads * head_dim] fp32 projections
+  int32_t ld_src;
+  int32_t n_rows;
+  int32_t nseg;
+  PostSeg seg[kGemmMaxSeg];
+  int32_t total_heads;
+  Rows rows;
   const int32_t *block_table;
   int32_t bt_stride;
   KVLayout kv;
   float theta, eps;
   int32_t *err;
 };
-
-// dtype: 0 bf16, 1 fp32.  Returns hipSuccess or the launch error.
-hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s);
+hipError_t launch_qkv_post(const QkvPostArgs &a, int dtype, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 struct PrepArgs {

@@ -36,13 +36,22 @@ def small_short(prompt_len=128, layers=8):
     return replace(c, prompt_len=prompt_len, target=replace(c.target, layers=layers))
 
 
+def _variant(base, dtype=None, layers=None, prompt_len=None):
+    from dataclasses import replace
+    t = base.target
+    t = replace(t, dtype=dtype or t.dtype, layers=layers or t.layers)
+    return replace(base, target=t, prompt_len=prompt_len or base.prompt_len)
+
+
 CASES = {
     "tiny": lambda: synth.TINY,
     "small": lambda: small_short(),
+    "tiny_bf16": lambda: _variant(synth.TINY, dtype="bf16"),
+    "small_fp32": lambda: _variant(small_short(32), dtype="fp32"),
 }
 
 
-@pytest.mark.parametrize("name", ["tiny", "small"])
+@pytest.mark.parametrize("name", ["tiny", "small", "tiny_bf16", "small_fp32"])
 def test_prefill_logits_and_features(name):
     cfg = CASES[name]()
     log(f"[prefill] {name}")
@@ -233,3 +242,28 @@ def test_gpu_generator_matches_cpu():
         sg.fill(t, name, "w", 0, 0.02, dtype)
         ref = sw.tensor(name, shape, "w", 0, 0.02, dtype)
         assert np.array_equal(t.float().cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (4, 384, 128), (8, 7168, 5120), (13, 5120, 17408), (64, 256, 1024),
+                                   (37, 512, 96), (100, 160, 64)])
+def test_op_linear(dtype, M, N, K):
+    """The projection kernel against float64 matmul of the same (storage-typed) inputs, tiles and ragged
+    row counts included; fp32 accumulation bounds the error."""
+    from speculative_decoding_dflash_amd import binding as Bd
+    if dtype == "bf16" and K % 32:
+        pytest.skip("bf16 needs K % 32 == 0")
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xt = torch.from_numpy(x).to(tdt).cuda()
+    wt = torch.from_numpy(w).to(tdt).cuda()
+    y = torch.zeros(M * N, dtype=torch.float32, device="cuda")
+    Bd.dflash_op_linear(Bd.BF16 if dtype == "bf16" else Bd.F32, M, N, K, xt, wt, y)
+    torch.cuda.synchronize()
+    ref = xt.double().cpu().numpy() @ wt.double().cpu().numpy().T
+    got = y.view(M, N).cpu().numpy()
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    log(f"  linear {dtype} {M}x{N}x{K}: rel err {err:.2e}")
+    assert err < 1e-5
