@@ -206,6 +206,13 @@ dflash_status dflash_draft_block(dflash_ctx *ctx, hipStream_t stream, int32_t ba
 dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
                                const void *d_w, float *d_y);
 
+/* Measurement access: with profiling enabled, every projection launch of the step calls is bracketed
+ * by HIP events on the caller's stream.  dflash_profile_read waits for them and returns the summed
+ * kernel time (ms), the summed algorithmic weight bytes of those launches and their number since
+ * profiling was enabled.  Enabling or disabling resets the sums. */
+dflash_status dflash_profile(dflash_ctx *ctx, int32_t enable);
+dflash_status dflash_profile_read(dflash_ctx *ctx, double *gemm_ms, double *gemm_bytes, int32_t *gemm_launches);
+
 /* Synchronise `stream` and report device-side errors raised since the last call (sticky flags). */
 dflash_status dflash_device_status(dflash_ctx *ctx, hipStream_t stream);
 

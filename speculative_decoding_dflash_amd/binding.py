@@ -81,6 +81,8 @@ def _load() -> C.CDLL:
         "dflash_draft_block": (I, [V, V, I, P(I), V, V, V]),
         "dflash_device_status": (I, [V, V]),
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
+        "dflash_profile": (I, [V, I]),
+        "dflash_profile_read": (I, [V, P(C.c_double), P(C.c_double), P(I)]),
         "dflash_last_error": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -164,6 +166,17 @@ def dflash_draft_block(ctx: int, slots: Sequence[int], feats, block, logits=None
 
 def dflash_op_linear(dtype: int, M: int, N: int, K: int, x, w, y, stream=None):
     _check(lib.dflash_op_linear(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y)))
+
+
+def dflash_profile(ctx: int, enable: bool):
+    _check(lib.dflash_profile(ctx, int(bool(enable))))
+
+
+def dflash_profile_read(ctx: int):
+    """(gemm_ms, gemm_bytes, gemm_launches) summed since profiling was enabled."""
+    ms, by, n = C.c_double(), C.c_double(), C.c_int32()
+    _check(lib.dflash_profile_read(ctx, C.byref(ms), C.byref(by), C.byref(n)))
+    return ms.value, by.value, n.value
 
 
 def dflash_device_status(ctx: int, stream=None):

@@ -127,6 +127,12 @@ struct dflash_ctx {
   int last_qlen = 0, last_nlogit = 0, last_batch = 0;
   std::vector<int32_t> last_slots;
   bool verified = false;
+  // optional timing of the projection launches (HIP events on the caller's stream)
+  bool profiling = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<std::pair<int, double>> ev_pending;  // (index of the start event, algorithmic bytes)
+  double prof_ms = 0.0, prof_bytes = 0.0;
+  int prof_launches = 0;
 
   template <typename P> P *wsp(size_t off) const { return reinterpret_cast<P *>(ws + off); }
   SlotState *state() const { return wsp<SlotState>(L.state); }
@@ -178,7 +184,23 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s) {
   return DFLASH_OK;
 }
 
-dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) { return run_gemm(c->es(), c->dt(), a, R, s); }
+dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
+  if (!c->profiling) return run_gemm(c->es(), c->dt(), a, R, s);
+  const size_t need = c->ev_pending.size() * 2 + 2;
+  while (c->ev_pool.size() < need) {
+    hipEvent_t e;
+    HIP_OK(hipEventCreate(&e));
+    c->ev_pool.push_back(e);
+  }
+  const int i = (int)c->ev_pending.size() * 2;
+  HIP_OK(hipEventRecord(c->ev_pool[i], s));
+  dflash_status st = run_gemm(c->es(), c->dt(), a, R, s);
+  HIP_OK(hipEventRecord(c->ev_pool[i + 1], s));
+  // weight bytes once per launch chunk (the algorithmic traffic of a weight-streaming projection)
+  const int chunks = (R + kGemmMaxRows - 1) / kGemmMaxRows;
+  c->ev_pending.push_back({i, (double)a.N * (a.epi == EPI_SWIGLU ? 2 : 1) * a.K * c->es() * chunks});
+  return st;
+}
 
 QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
   QkvPostArgs p;
@@ -393,6 +415,8 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
 }
 
 dflash_status dflash_destroy(dflash_ctx *ctx) {
+  if (ctx)
+    for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
   delete ctx;
   return DFLASH_OK;
 }
@@ -664,6 +688,32 @@ dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t 
   a.out_f32 = d_y;
   a.ld_out = N;
   return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, s);
+}
+
+dflash_status dflash_profile(dflash_ctx *c, int32_t enable) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  c->profiling = enable != 0;
+  c->ev_pending.clear();
+  c->prof_ms = c->prof_bytes = 0.0;
+  c->prof_launches = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_read(dflash_ctx *c, double *gemm_ms, double *gemm_bytes, int32_t *gemm_launches) {
+  if (!c || !gemm_ms || !gemm_bytes || !gemm_launches) return fail(DFLASH_E_INVAL, "null argument");
+  for (auto &pe : c->ev_pending) {
+    HIP_OK(hipEventSynchronize(c->ev_pool[pe.first + 1]));
+    float ms = 0.f;
+    HIP_OK(hipEventElapsedTime(&ms, c->ev_pool[pe.first], c->ev_pool[pe.first + 1]));
+    c->prof_ms += ms;
+    c->prof_bytes += pe.second;
+    ++c->prof_launches;
+  }
+  c->ev_pending.clear();
+  *gemm_ms = c->prof_ms;
+  *gemm_bytes = c->prof_bytes;
+  *gemm_launches = c->prof_launches;
+  return DFLASH_OK;
 }
 
 dflash_status dflash_device_status(dflash_ctx *c, hipStream_t s) {

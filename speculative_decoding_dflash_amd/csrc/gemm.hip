@@ -3,9 +3,14 @@
 // The decode step is weight-streaming: M (block x batch rows) is small, so every weight byte is read
 // once from HBM and the matrix cores are far from busy.  The kernel is shaped for that:
 //   * a work-group owns 16 or 32 weight rows (one or two 16-row MFMA column tiles) over the whole K;
-//     its NW waves take interleaved K steps, so at any moment the work-group reads NW * 64
-//     contiguous bytes of each row, every lane issuing 16-byte loads, four steps in flight per wave;
-//   * X fragments come straight from global memory (X is at most 64 x K and stays in cache);
+//     its NW waves take interleaved 256-byte K windows ("super-steps");
+//   * weights are loaded in a layout that HBM streams well -- one wave instruction covers 4 rows x
+//     256 contiguous bytes (16 bytes per lane) -- while the next super-step is already in flight;
+//     each wave stages its rows in a private, padded LDS tile and reads the MFMA operand layout
+//     (16 rows x 64 bytes per instruction, which streams ~25% slower from HBM) back from LDS;
+//     a wave only ever reads what it wrote itself, so the main loop needs no barrier;
+//   * X windows take the same path (quad-layout loads, wave-private LDS), which costs a few percent
+//     where loading X directly in the MFMA layout cost a quarter of the bandwidth;
 //   * v_mfma_f32_16x16x32_bf16 (or 4 x v_mfma_f32_16x16x4f32 for fp32 models) accumulates in fp32;
 //   * the NW waves reduce their partial tiles through LDS in a fixed order, then the whole
 //     work-group runs the epilogue on its columns.  No state crosses work-groups, so no device-scope
@@ -47,18 +52,27 @@ template <typename T, int MT, int CT, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Frag<T>;
   constexpr int COLS = 16 * CT;
+  constexpr int XR = 16 * MT;              // X rows staged (padded to whole MFMA tiles)
   constexpr int NT = NW * 64;
-  __shared__ float lds[NW * 16 * MT * COLS];
+  constexpr int ROWB = 256 + 16;           // LDS bytes per staged row (256 B of K plus padding)
+  constexpr int NQ = COLS / 4;             // weight quad loads per super-step (4 rows x 256 B each)
+  constexpr int NXQ = XR / 4;              // X quad loads per super-step (rows >= M skipped)
+  constexpr int SK = 256 / sizeof(T);      // K elements per super-step (256 bytes of a row)
+  constexpr int KS = SK / F::kStep;        // MFMA K steps per super-step (4)
+  constexpr int kEnt = 16 * MT * COLS;     // entries of one wave's partial tile
+  constexpr int kTileB = NW * (COLS + XR) * ROWB, kRedB = NW * kEnt * 4;
+  // wave-private staging of weights and X during the main loop; the cross-wave reduction reuses it
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kTileB > kRedB ? kTileB : kRedB];
+  float *lds = reinterpret_cast<float *>(smem);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int c = blockIdx.x;
 
-  // Weight rows of this lane in the CT column tiles.
-  const T *wp[CT];
+  const T *wbase[CT];  // row 16*ct of the tile
   if (swiglu) {
-    wp[0] = (const T *)a.seg[0].w + (size_t)(16 * c + r16) * a.K;
-    wp[CT - 1] = (const T *)a.seg[1].w + (size_t)(16 * c + r16) * a.K;
+    wbase[0] = (const T *)a.seg[0].w + (size_t)(16 * c) * a.K;
+    wbase[CT - 1] = (const T *)a.seg[1].w + (size_t)(16 * c) * a.K;
   } else {
     const int r0 = COLS * c;
     int si = 0, base = 0;
@@ -68,15 +82,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     }
     const T *w = (const T *)a.seg[si].w;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) wp[ct] = w + (size_t)(r0 - base + 16 * ct + r16) * a.K;
+    for (int ct = 0; ct < CT; ++ct) wbase[ct] = w + (size_t)(r0 - base + 16 * ct) * a.K;
   }
-  const T *xp[MT];
-  bool xok[MT];
+  // Quad layout: load q covers rows 4q .. 4q+3, lane (g = lane / 16) takes row 4q + g and bytes
+  // 16 * r16 .. 16 * r16 + 15 of the 256-byte window.
+  const T *qrow[NQ];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + r16;
-    xok[mt] = m < a.M;
-    xp[mt] = (const T *)a.x + (size_t)(xok[mt] ? m : 0) * a.ldx;
+  for (int q = 0; q < NQ; ++q) qrow[q] = wbase[q / 4] + (size_t)(4 * (q % 4) + g) * a.K + r16 * F::kEPL;
+  const T *xrow[NXQ];
+  bool xq[NXQ];
+#pragma unroll
+  for (int q = 0; q < NXQ; ++q) {
+    const int m = 4 * q + g;
+    xq[q] = m < a.M;
+    xrow[q] = (const T *)a.x + (size_t)(xq[q] ? m : 0) * a.ldx + r16 * F::kEPL;
   }
 
   f32x4 acc[MT][CT];
@@ -85,42 +104,60 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = a.K / F::kStep;
-  const int loff = g * F::kEPL;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  int s = wave;
-  for (; s + 3 * NW < nsteps; s += 4 * NW) {
-    u32x4 wv[4][CT], xv[4][MT];
+  unsigned char *wt = smem + wave * (COLS + XR) * ROWB;
+  unsigned char *xt = wt + COLS * ROWB;
+  const int nsup = a.K / SK;  // streamed super-steps; wave w takes w, w + NW, ...
+  u32x4 cur[NQ], curx[NXQ];
+  int sup = wave;
+  if (sup < nsup) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = loff + (s + NW * u) * F::kStep;
+    for (int q = 0; q < NQ; ++q) cur[q] = ld16(qrow[q] + (size_t)sup * SK);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) wv[u][ct] = ld16(wp[ct] + k);
+    for (int q = 0; q < NXQ; ++q) curx[q] = xq[q] ? ld16(xrow[q] + (size_t)sup * SK) : zero;
+  }
+  for (; sup < nsup; sup += NW) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xv[u][mt] = xok[mt] ? ld16(xp[mt] + k) : zero;
+    for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = cur[q];
+#pragma unroll
+    for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = curx[q];
+    // keep the next super-step in flight while this one is consumed
+    const int nxt = sup + NW;
+    if (nxt < nsup) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) cur[q] = ld16(qrow[q] + (size_t)nxt * SK);
+#pragma unroll
+      for (int q = 0; q < NXQ; ++q) curx[q] = xq[q] ? ld16(xrow[q] + (size_t)nxt * SK) : zero;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 xv[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
+        xv[mt] = (mt * 16 + r16 < a.M) ? *reinterpret_cast<const u32x4 *>(xt + (mt * 16 + r16) * ROWB + ks * 64 + 16 * g)
+                                       : zero;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) F::mma(acc[mt][ct], xv[u][mt], wv[u][ct]);
+      for (int ct = 0; ct < CT; ++ct) {
+        const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * ct + r16) * ROWB + ks * 64 + 16 * g);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) F::mma(acc[mt][ct], xv[mt], wv);
+      }
+    }
   }
-  for (; s < nsteps; s += NW) {
-    const int k = loff + s * F::kStep;
-    u32x4 wv[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) wv[ct] = ld16(wp[ct] + k);
+  // K tail (K not a multiple of the super-step): direct MFMA-layout loads
+  for (int st = nsup * KS + wave; st < a.K / F::kStep; st += NW) {
+    const int k = st * F::kStep + g * F::kEPL;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 xv = xok[mt] ? ld16(xp[mt] + k) : zero;
+      const int m = mt * 16 + r16;
+      const u32x4 xv = m < a.M ? ld16((const T *)a.x + (size_t)m * a.ldx + k) : zero;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) F::mma(acc[mt][ct], xv, wv[ct]);
+      for (int ct = 0; ct < CT; ++ct) F::mma(acc[mt][ct], xv, ld16(wbase[ct] + (size_t)r16 * a.K + k));
     }
   }
 
   // Reduce the waves' partial tiles: C[m][n] sits at lane (n = lane % 16, m = 4 * (lane / 16) + r).
-  constexpr int kEnt = 16 * MT * COLS;
+  __syncthreads();  // every wave is done with its staging tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -180,12 +217,17 @@ template <typename T, int MT>
 static void launch_mt(const GemmArgs &a, int ct, int nw, hipStream_t s) {
   const int tiles = a.epi == EPI_SWIGLU ? a.N / 16 : a.N / (16 * ct);
   dim3 grid(tiles);
-  if (ct == 1) {
-    if (nw == 8) hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 8>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, a);
-  } else {
-    if (nw == 8) hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 8>), grid, dim3(512), 0, s, a);
+  if constexpr (MT == 4) {  // 8 waves would not fit their 64 staged X rows in LDS
+    if (ct == 1) hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, a);
+  } else {
+    if (ct == 1) {
+      if (nw == 8) hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, a);
+    } else {
+      if (nw == 8) hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, a);
+    }
   }
 }
 
@@ -197,7 +239,7 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s) {
   int ct = a.epi == EPI_SWIGLU ? 2 : (env_ct ? env_ct : (a.N / 32 >= wide_tiles ? 2 : 1));
   if (a.epi != EPI_SWIGLU && a.N % (16 * ct)) ct = 1;
   const int MT = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
-  int nw = env_nw ? env_nw : (MT == 1 ? 8 : 4);
+  int nw = env_nw ? env_nw : (MT <= 2 ? 8 : 4);
   if (nw != 4 && nw != 8) nw = 4;
   if (dtype == 0) {
     if (MT == 1) launch_mt<bf16, 1>(a, ct, nw, s);
