@@ -155,6 +155,7 @@ def main():
     ap.add_argument("--config", default="27b")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ar", action="store_true", help="skip plain decoding (and so the planted sweep)")
     ap.add_argument("--profile-steps", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -213,44 +214,45 @@ def main():
         f"{dec_ms / args.profile_steps:.3f} ms/step of {prof_step_ms:.3f}, {achieved:.0f} GB/s")
 
     # 3. same-kernel plain decoding (also the greedy stream for the planted drafter)
-    n_ar_needed = (Wm + K + 1) * B + 2 * B
-    log(f"[bench] plain decoding: {n_ar_needed} greedy tokens")
-    eng.prefill([0], prompt.view(1, -1), [s_greedy])
-    gen = [eng.out[:1].clone()]
-    ar_t = Timer(torch)
-    ar_timed = min(K * 2, n_ar_needed - 1)
-    ar_ms = 0.0
-    for i in range(n_ar_needed - 1):
-        if i == n_ar_needed - 1 - ar_timed:
-            ar_t.start()
-        eng.ar_step([0], [s_greedy])
-        gen.append(eng.out[:1].clone())
-    ar_ms = ar_t.stop()
-    eng.status()
-    G = np.concatenate([prompt.cpu().numpy(), torch.cat(gen).cpu().numpy()]).astype(np.int64)
-    ar_tok_s = ar_timed / (ar_ms / 1e3)
-    n_ar = P + n_ar_needed - ar_timed
-    ar_gbs = sum(ar_bytes(cfg, n_ar + i) for i in range(ar_timed)) / (ar_ms / 1e3) / 1e9
-    log(f"[bench]   {ar_tok_s:.1f} tok/s, {ar_ms / ar_timed:.3f} ms/token, {ar_gbs:.0f} GB/s algorithmic")
-
-    # 4. planted drafter, greedy verification, forced acceptance length tau* = 1 .. B
+    ar = None
     sweep = {}
-    if not args.no_sweep:
-        for ts in range(1, B + 1):
-            plans, n = [], P
-            for i in range(Wm + K):
-                plans.append(sw.planted_drafts(G, n, B - 1, V, d.mask_id, 0.0,
-                                               force_reject_at=ts if ts < B else None))
-                n += ts
-            planted = torch.from_numpy(np.stack(plans)).to("cuda")
-            ms_p, taus_p = run_spec(eng, torch, prompt, s_greedy, Wm, K, planted=planted)
-            got = sum(taus_p[Wm:]) / K
-            assert all(x == ts for x in taus_p), (ts, taus_p)
-            nsw = [P + ts * (Wm + i) for i in range(K)]
-            gbs = sum(step_bytes(cfg, x) for x in nsw) / (ms_p / 1e3) / 1e9
-            sweep[str(ts)] = {"tok_s": round(ts * K / (ms_p / 1e3), 1), "ms_per_step": round(ms_p / K, 3),
-                              "tau": got, "step_hbm_gbs": round(gbs, 1)}
-            log(f"[bench]   planted tau*={ts}: {sweep[str(ts)]}")
+    if not args.no_ar:
+        n_ar_needed = (Wm + K + 1) * B + 2 * B
+        log(f"[bench] plain decoding: {n_ar_needed} greedy tokens")
+        eng.prefill([0], prompt.view(1, -1), [s_greedy])
+        gen = [eng.out[:1].clone()]
+        ar_t = Timer(torch)
+        ar_timed = min(K * 2, n_ar_needed - 1)
+        for i in range(n_ar_needed - 1):
+            if i == n_ar_needed - 1 - ar_timed:
+                ar_t.start()
+            eng.ar_step([0], [s_greedy])
+            gen.append(eng.out[:1].clone())
+        ar_ms = ar_t.stop()
+        eng.status()
+        G = np.concatenate([prompt.cpu().numpy(), torch.cat(gen).cpu().numpy()]).astype(np.int64)
+        n_ar = P + n_ar_needed - ar_timed
+        ar_gbs = sum(ar_bytes(cfg, n_ar + i) for i in range(ar_timed)) / (ar_ms / 1e3) / 1e9
+        ar = {"tok_s": round(ar_timed / (ar_ms / 1e3), 2), "ms_per_token": round(ar_ms / ar_timed, 4),
+              "hbm_gbs": round(ar_gbs, 1)}
+        log(f"[bench]   {ar}")
+
+        # 4. planted drafter, greedy verification, forced acceptance length tau* = 1 .. B
+        if not args.no_sweep:
+            for ts in range(1, B + 1):
+                plans, n = [], P
+                for i in range(Wm + K):
+                    plans.append(sw.planted_drafts(G, n, B - 1, V, d.mask_id, 0.0,
+                                                   force_reject_at=ts if ts < B else None))
+                    n += ts
+                planted = torch.from_numpy(np.stack(plans)).to("cuda")
+                ms_p, taus_p = run_spec(eng, torch, prompt, s_greedy, Wm, K, planted=planted)
+                assert all(x == ts for x in taus_p), (ts, taus_p)
+                nsw = [P + ts * (Wm + i) for i in range(K)]
+                gbs = sum(step_bytes(cfg, x) for x in nsw) / (ms_p / 1e3) / 1e9
+                sweep[str(ts)] = {"tok_s": round(ts * K / (ms_p / 1e3), 1), "ms_per_step": round(ms_p / K, 3),
+                                  "step_hbm_gbs": round(gbs, 1)}
+                log(f"[bench]   planted tau*={ts}: {sweep[str(ts)]}")
 
     cpu = None
     if not args.no_cpu:
@@ -283,8 +285,7 @@ def main():
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_bytes": bytes_step,
-        "ar_baseline": {"tok_s": round(ar_tok_s, 2), "ms_per_token": round(ar_ms / ar_timed, 4),
-                        "hbm_gbs": round(ar_gbs, 1)},
+        "ar_baseline": ar,
         "tau_sweep_planted_greedy": sweep,
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel (all projections of the step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -41,7 +41,8 @@ constexpr int kAttnSplitMax = 64;
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, qkvf, att_o, att_ml, cbuf, dlogits, cid, cp, cn, total;
+  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, qkvf, att_o, att_ml, cbuf, dlogits, cid, cp, cn, skey,
+      sidx, total;
   size_t qkvf_cols, att_rows;
 };
 
@@ -77,6 +78,8 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.cid = take(sizeof(int32_t) * srows * kMaxTopK);
   L.cp = take(sizeof(float) * srows * kMaxTopK);
   L.cn = take(sizeof(int32_t) * srows);
+  L.skey = take(sizeof(uint32_t) * srows * kFilterScratch);
+  L.sidx = take(sizeof(int32_t) * srows * kFilterScratch);
   L.total = off;
   return L;
 }
@@ -172,14 +175,16 @@ GemmArgs gemm_base(const void *x, int ldx, int M, int N, int K, int epi) {
 }
 
 // Run a GEMM over R rows in chunks of kGemmMaxRows.  `a.x` points at row 0; input rows advance by ldx.
-dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s) {
+// e0 / e1 (may be null) time the first chunk's start and the last chunk's end.
+dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr) {
   const char *x0 = (const char *)a.x;
   for (int r0 = 0; r0 < R; r0 += kGemmMaxRows) {
     GemmArgs b = a;
     b.M = std::min(kGemmMaxRows, R - r0);
     b.x = x0 + (size_t)r0 * a.ldx * es;
     b.row_off = r0;
-    HIP_OK(launch_gemm(b, dt, s));
+    HIP_OK(launch_gemm(b, dt, s, r0 == 0 ? e0 : nullptr, r0 + kGemmMaxRows >= R ? e1 : nullptr));
   }
   return DFLASH_OK;
 }
@@ -193,9 +198,7 @@ dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
     c->ev_pool.push_back(e);
   }
   const int i = (int)c->ev_pending.size() * 2;
-  HIP_OK(hipEventRecord(c->ev_pool[i], s));
-  dflash_status st = run_gemm(c->es(), c->dt(), a, R, s);
-  HIP_OK(hipEventRecord(c->ev_pool[i + 1], s));
+  dflash_status st = run_gemm(c->es(), c->dt(), a, R, s, c->ev_pool[i], c->ev_pool[i + 1]);
   // weight bytes once per launch chunk (the algorithmic traffic of a weight-streaming projection)
   const int chunks = (R + kGemmMaxRows - 1) / kGemmMaxRows;
   c->ev_pending.push_back({i, (double)a.N * (a.epi == EPI_SWIGLU ? 2 : 1) * a.K * c->es() * chunks});
@@ -566,6 +569,12 @@ dflash_status dflash_accept_resample(dflash_ctx *c, hipStream_t s, int32_t batch
   f.cand_id = c->wsp<int32_t>(c->L.cid);
   f.cand_p = c->wsp<float>(c->L.cp);
   f.cand_n = c->wsp<int32_t>(c->L.cn);
+  f.stage_key = c->wsp<uint32_t>(c->L.skey);
+  f.stage_idx = c->wsp<int32_t>(c->L.sidx);
+  int kmax = 1;
+  for (int b = 0; b < batch; ++b)
+    if (sampling[b].temperature > 0.f) kmax = std::max(kmax, std::min(sampling[b].top_k, c->cfg.vocab));
+  filter_plan(f, kmax);
   HIP_OK(launch_filter(f, s));
   DecideArgs d;
   memset(&d, 0, sizeof d);
@@ -672,7 +681,20 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   a.out_f32 = logits;
   a.ld_out = m.vocab;
   if ((st = run_gemm(c, a, batch * nd, s)) != DFLASH_OK) return st;
-  HIP_OK(launch_argmax(logits, batch * nd, m.vocab, nd, B, 1, d_block, s));
+  FilterArgs f;
+  memset(&f, 0, sizeof f);
+  f.logits = logits;
+  f.rows = batch * nd;
+  f.vocab = m.vocab;
+  f.rows_per_seq = nd;
+  f.stage_key = c->wsp<uint32_t>(c->L.skey);
+  f.stage_idx = c->wsp<int32_t>(c->L.sidx);
+  f.argmax_out = d_block;
+  f.am_take = nd;
+  f.am_stride = B;
+  f.am_offset = 1;
+  filter_plan(f, 1);
+  HIP_OK(launch_filter(f, s));
   return DFLASH_OK;
 }
 

@@ -18,6 +18,8 @@
 // Epilogues: fp32 store (logits, q/k/v before their per-head normalisation), activation store,
 // residual add (+ optional feature tap), and SwiGLU (gate and up rows of the same output column in
 // one work-group).
+#include <hip/hip_ext.h>
+
 #include "kernels.h"
 
 namespace df {
@@ -214,41 +216,47 @@ int env_int(const char *name, int dflt) {
 }  // namespace
 
 template <typename T, int MT>
-static void launch_mt(const GemmArgs &a, int ct, int nw, hipStream_t s) {
+static void launch_mt(const GemmArgs &a, int ct, int nw, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = a.epi == EPI_SWIGLU ? a.N / 16 : a.N / (16 * ct);
   dim3 grid(tiles);
+  // hipExtLaunchKernelGGL carries the optional timing events in the dispatch itself
   if constexpr (MT == 4) {  // 8 waves would not fit their 64 staged X rows in LDS
-    if (ct == 1) hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, a);
+    if (ct == 1) hipExtLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
   } else {
     if (ct == 1) {
-      if (nw == 8) hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 8>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, a);
+      if (nw == 8) hipExtLaunchKernelGGL((gemm_kernel<T, MT, 1, 8>), grid, dim3(512), 0, s, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
     } else {
-      if (nw == 8) hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 8>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, a);
+      if (nw == 8) hipExtLaunchKernelGGL((gemm_kernel<T, MT, 2, 8>), grid, dim3(512), 0, s, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
     }
   }
 }
 
-hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s) {
-  // Tile width: SwiGLU pairs gate and up rows (two tiles); other projections use 16-row tiles unless
-  // there are plenty of them.  Waves per work-group: 8 for decode-sized M, 4 for larger M.
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  // Tile width and waves per work-group, from the MI355X sweep at M = 8: 32-row tiles with 8 waves
+  // stream best except for mid-sized N with short K (q/k/v, injected k/v), where 16-row tiles with
+  // 4 waves spread better over the 256 CUs.  SwiGLU always pairs gate and up rows (two tiles).
   static const int env_ct = env_int("DFLASH_GEMM_CT", 0), env_nw = env_int("DFLASH_GEMM_NW", 0);
-  static const int wide_tiles = env_int("DFLASH_GEMM_WIDE_TILES", 2048);
-  int ct = a.epi == EPI_SWIGLU ? 2 : (env_ct ? env_ct : (a.N / 32 >= wide_tiles ? 2 : 1));
+  int ct = 2, nw = 8;
+  if (a.epi != EPI_SWIGLU && a.N >= 6144 && a.N <= 12288 && a.K <= 8192) {
+    ct = 1;
+    nw = 4;
+  }
+  if (env_ct && a.epi != EPI_SWIGLU) ct = env_ct;
+  if (env_nw) nw = env_nw;
   if (a.epi != EPI_SWIGLU && a.N % (16 * ct)) ct = 1;
   const int MT = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
-  int nw = env_nw ? env_nw : (MT <= 2 ? 8 : 4);
   if (nw != 4 && nw != 8) nw = 4;
   if (dtype == 0) {
-    if (MT == 1) launch_mt<bf16, 1>(a, ct, nw, s);
-    else if (MT == 2) launch_mt<bf16, 2>(a, ct, nw, s);
-    else launch_mt<bf16, 4>(a, ct, nw, s);
+    if (MT == 1) launch_mt<bf16, 1>(a, ct, nw, s, e0, e1);
+    else if (MT == 2) launch_mt<bf16, 2>(a, ct, nw, s, e0, e1);
+    else launch_mt<bf16, 4>(a, ct, nw, s, e0, e1);
   } else {
-    if (MT == 1) launch_mt<float, 1>(a, ct, nw, s);
-    else if (MT == 2) launch_mt<float, 2>(a, ct, nw, s);
-    else launch_mt<float, 4>(a, ct, nw, s);
+    if (MT == 1) launch_mt<float, 1>(a, ct, nw, s, e0, e1);
+    else if (MT == 2) launch_mt<float, 2>(a, ct, nw, s, e0, e1);
+    else launch_mt<float, 4>(a, ct, nw, s, e0, e1);
   }
   return hipGetLastError();
 }

@@ -33,8 +33,8 @@ struct GemmArgs {
   int32_t row_off;      // global row of local row 0
 };
 
-// dtype: 0 bf16, 1 fp32.  Returns hipSuccess or the launch error.
-hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s);
+// dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Per-head q/k RMSNorm + RoPE, then q to a dense buffer and k/v to the paged cache.
 struct PostSeg {
@@ -115,14 +115,23 @@ struct FilterArgs {
   const float *logits;  // [rows][vocab]
   int32_t rows, vocab;
   int32_t rows_per_seq;
-  float temperature[64];
+  float temperature[64];  // per sequence; 0 = greedy
   int32_t top_k[64];
   float top_p[64];
   int32_t *cand_id;     // [rows][kMaxTopK]
   float *cand_p;        // [rows][kMaxTopK]
   int32_t *cand_n;      // [rows]
+  // two-stage plan (filter_plan) and its scratch: [rows][n_chunks][kmax] candidate keys and ids
+  int32_t chunk, n_chunks, kmax;
+  uint32_t *stage_key;
+  int32_t *stage_idx;
+  // argmax mode (drafts): row r's argmax goes to argmax_out[(r / take) * stride + offset + r % take]
+  int32_t *argmax_out;
+  int32_t am_take, am_stride, am_offset;
 };
 constexpr int kMaxTopK = 256;
+constexpr int kFilterScratch = 8192;  // stage-1 candidates per row (chunks * kmax)
+void filter_plan(FilterArgs &a, int kmax);
 hipError_t launch_filter(const FilterArgs &a, hipStream_t s);
 
 struct DecideArgs {
@@ -140,10 +149,6 @@ struct DecideArgs {
   int32_t *err;
 };
 hipError_t launch_decide(const DecideArgs &a, hipStream_t s);
-
-// Row argmax of fp32 logits (lowest index on ties); row r goes to out[(r / take) * stride + offset + r % take].
-hipError_t launch_argmax(const float *logits, int32_t rows, int32_t vocab, int32_t take, int32_t stride, int32_t offset,
-                         int32_t *out, hipStream_t s);
 
 // copy candidate lists out for tests
 hipError_t launch_copy_cands(const int32_t *cid, const float *cp, const int32_t *cn, int32_t rows, int32_t *oid,

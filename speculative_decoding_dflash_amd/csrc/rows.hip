@@ -106,71 +106,63 @@ DF_DEVICE float block_sum(float v, float *red) {
   return t;
 }
 
-// out row i = act(in row (i / take) * stride + offset + i % take, normalised) * gain
-template <typename T>
-__global__ void rmsnorm_kernel(const float *in, int ld_in, int take, int stride, int offset, const float *gain,
-                               float eps, int hidden, T *out, int ld_out) {
-  __shared__ float red[16];
+// out row i = act(in row (i / take) * stride + offset + i % take, normalised) * gain.
+// One work-group per row; every thread loads its float4 slices once (all loads issued before any is
+// used), keeps them in registers for the second pass, and the sum of squares is reduced in a fixed
+// order.
+template <typename T, int VPT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *in, int ld_in, int take, int stride, int offset,
+                                                      const float *gain, float eps, int hidden, T *out, int ld_out) {
+  __shared__ float red[4];
   const int i = blockIdx.x;
   const int src = (i / take) * stride + offset + (i % take);
-  const float *x = in + (size_t)src * ld_in;
+  const float4 *x = reinterpret_cast<const float4 *>(in + (size_t)src * ld_in);
+  const int nv = hidden / 4;
+  float4 v[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int q = threadIdx.x + 256 * j;
+    v[j] = q < nv ? x[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float ss = 0.f;
-  for (int h = threadIdx.x; h < hidden; h += blockDim.x) ss += x[h] * x[h];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)hidden + eps);
   T *y = out + (size_t)i * ld_out;
-  for (int h = threadIdx.x; h < hidden; h += blockDim.x) Elem<T>::store(y + h, x[h] * r * gain[h]);
+  const float4 *gv = reinterpret_cast<const float4 *>(gain);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int q = threadIdx.x + 256 * j;
+    if (q < nv) {
+      const float4 gg = gv[q];
+      Elem<T>::store(y + 4 * q + 0, v[j].x * r * gg.x);
+      Elem<T>::store(y + 4 * q + 1, v[j].y * r * gg.y);
+      Elem<T>::store(y + 4 * q + 2, v[j].z * r * gg.z);
+      Elem<T>::store(y + 4 * q + 3, v[j].w * r * gg.w);
+    }
+  }
+}
+
+template <typename T>
+static void launch_rms_t(const float *in, int ld_in, int take, int stride, int offset, int n_rows, const float *gain,
+                         float eps, int hidden, T *out, int ld_out, hipStream_t s) {
+  const int vpt = (hidden / 4 + 255) / 256;
+  dim3 g(n_rows), b(256);
+  if (vpt <= 1) hipLaunchKernelGGL((rmsnorm_kernel<T, 1>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
+  else if (vpt <= 2) hipLaunchKernelGGL((rmsnorm_kernel<T, 2>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
+  else if (vpt <= 4) hipLaunchKernelGGL((rmsnorm_kernel<T, 4>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
+  else if (vpt <= 8) hipLaunchKernelGGL((rmsnorm_kernel<T, 8>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
+  else hipLaunchKernelGGL((rmsnorm_kernel<T, 16>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
 }
 
 hipError_t launch_rmsnorm(const float *in, int32_t ld_in, int32_t take, int32_t stride, int32_t offset, int32_t n_rows,
                           const float *gain, float eps, int32_t hidden, void *out, int32_t ld_out, int dtype,
                           hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL((rmsnorm_kernel<bf16>), dim3(n_rows), dim3(256), 0, s, in, ld_in, take, stride, offset, gain, eps,
-                       hidden, (bf16 *)out, ld_out);
-  else
-    hipLaunchKernelGGL((rmsnorm_kernel<float>), dim3(n_rows), dim3(256), 0, s, in, ld_in, take, stride, offset, gain, eps,
-                       hidden, (float *)out, ld_out);
-  return hipGetLastError();
-}
-
-// Row argmax; ties resolve to the lowest index.
-__global__ void argmax_kernel(const float *logits, int vocab, int take, int stride, int offset, int32_t *out) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  const float *z = logits + (size_t)blockIdx.x * vocab;
-  float best = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int j = threadIdx.x; j < vocab; j += blockDim.x) {
-    const float v = z[j];
-    if (v > best) {  // strided scan visits increasing j, so '>' keeps the lowest index per thread
-      best = v;
-      bi = j;
-    }
-  }
-  sv[threadIdx.x] = best;
-  si[threadIdx.x] = bi;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) {
-      const float v = sv[threadIdx.x + off];
-      const int i = si[threadIdx.x + off];
-      if (v > sv[threadIdx.x] || (v == sv[threadIdx.x] && i < si[threadIdx.x])) {
-        sv[threadIdx.x] = v;
-        si[threadIdx.x] = i;
-      }
-    }
-    __syncthreads();
-  }
-  const int r = blockIdx.x;
-  if (threadIdx.x == 0) out[(r / take) * stride + offset + r % take] = si[0] == 0x7fffffff ? 0 : si[0];
-}
-
-hipError_t launch_argmax(const float *logits, int32_t rows, int32_t vocab, int32_t take, int32_t stride, int32_t offset,
-                         int32_t *out, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, logits, vocab, take, stride, offset, out);
+  if (hidden % 4 || ld_in % 4 || hidden > 16384) return hipErrorInvalidValue;
+  if (dtype == 0) launch_rms_t<bf16>(in, ld_in, take, stride, offset, n_rows, gain, eps, hidden, (bf16 *)out, ld_out, s);
+  else launch_rms_t<float>(in, ld_in, take, stride, offset, n_rows, gain, eps, hidden, (float *)out, ld_out, s);
   return hipGetLastError();
 }
 

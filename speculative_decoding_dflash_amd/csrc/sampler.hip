@@ -1,21 +1,26 @@
-// Candidate filter of the sampler, one work-group (1024 threads) per logits row (gfx950).
+// Candidate filter of the sampler and row argmax, in two stages (gfx950).
 //
 // For T > 0: s = z / T (IEEE division), keep the top_k scores ordered by (score desc, token id asc),
 // softmax over them, keep the smallest prefix whose running sum reaches top_p (inclusive), and
 // renormalise.  Sums run sequentially in sorted order in fp32 so that the accept / resample stage can
 // reproduce them exactly.  For T = 0 the single candidate is the argmax (lowest id on ties).
 //
-// Top-k is an exact radix select over order-preserving 32-bit keys: three histogram passes (12, 12
-// and 8 bits) find the k-th largest key; a fourth pass gathers every element whose key is at least
-// that key (usually exactly k of them) into LDS, where a bitonic sort orders them by (key desc,
-// id asc).  If ties at the threshold are so numerous that the gathered set would overflow LDS, an
-// ordered scan takes the lowest-id ties instead.
+// Stage 1: each row is cut into chunks of at most kChunkMax elements, one work-group per chunk.  The
+// chunk's order-preserving 32-bit keys are cached in LDS; an 8-bit-digit radix select finds the
+// chunk's k-th largest key; the chunk then emits exactly k candidates: every key above it, plus the
+// lowest-id keys equal to it (ordered by an exclusive scan over contiguous sub-ranges).
+// Stage 2: one work-group per row sorts the union of its chunks' candidates by (key desc, id asc) --
+// the row's top k is the top k of that union -- and computes the distribution.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace df {
 
-constexpr int kFT = 1024;      // threads per row
-constexpr int kGather = 1024;  // LDS capacity of the gathered set
+constexpr int kChunkMax = 8192;  // elements per stage-1 chunk
+constexpr int kMergeMax = kFilterScratch;  // stage-2 candidates per row (chunks * k)
+constexpr int kT1 = 256;
+constexpr int kT2 = 1024;
 
 DF_DEVICE uint32_t order_key(float s) {
   if (s == 0.0f) s = 0.0f;  // -0 and +0 are the same score
@@ -27,6 +32,8 @@ DF_DEVICE float key_value(uint32_t k) {
   return __builtin_bit_cast(float, u);
 }
 
+// Exclusive prefix sum over the block (fixed order); *total receives the block sum.
+template <int NT>
 DF_DEVICE int block_excl_scan(int v, int *wsum, int *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -38,175 +45,169 @@ DF_DEVICE int block_excl_scan(int v, int *wsum, int *total) {
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
-  for (int w = 0; w < kFT / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     if (w < wave) before += wsum[w];
     all += wsum[w];
   }
   *total = all;
+  __syncthreads();
   return before + x - v;
 }
 
-// Among bins (descending), find the bin holding the need-th largest element; returns the bin and
-// how many elements lie in higher bins.
-DF_DEVICE void find_bin(const int *hist, int nbins, int need, int *wsum, int *s_bin, int *s_above) {
-  const int per = nbins / kFT;  // bins per thread (>= 1)
-  const int t = threadIdx.x;
-  int local = 0;
-  for (int j = 0; j < per; ++j) local += hist[nbins - 1 - (t * per + j)];
-  int total;
-  const int before = block_excl_scan(local, wsum, &total);
-  if (before < need && need <= before + local) {
-    int cum = before;
-    for (int j = 0; j < per; ++j) {
-      const int bin = nbins - 1 - (t * per + j);
-      if (cum + hist[bin] >= need) {
-        *s_bin = bin;
-        *s_above = cum;
-        break;
-      }
-      cum += hist[bin];
-    }
+// Histogram increment with wave-level aggregation: lanes holding the same bin add once per distinct
+// bin, so a skewed digit (most logits share a sign and exponent) does not serialise the LDS atomics.
+// Must be called by all lanes of the wave.
+DF_DEVICE void hist_add(int *hist, int bin, bool active) {
+  uint64_t todo = __ballot(active);
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int lbin = __shfl(bin, leader);
+    const uint64_t same = __ballot(active && bin == lbin);
+    if ((int)__lane_id() == leader) atomicAdd(&hist[lbin], (int)__popcll(same));
+    todo &= ~same;
   }
-  __syncthreads();
 }
 
-__global__ __launch_bounds__(kFT) void filter_kernel(FilterArgs a) {
-  __shared__ int hist[4096];
-  __shared__ uint32_t gkey[kGather];
-  __shared__ int gidx[kGather];
-  __shared__ float ge[kMaxTopK];
-  __shared__ int wsum[kFT / 64];
-  __shared__ int s_bin, s_above, s_cnt, s_keep;
-  __shared__ float s_kept;
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
+DF_DEVICE void row_params(const FilterArgs &a, int row, float *T, int *K) {
   const int seq = row / a.rows_per_seq;
-  const float T = a.temperature[seq];
-  const float *z = a.logits + (size_t)row * a.vocab;
-  int32_t *cid = a.cand_id + (size_t)row * kMaxTopK;
-  float *cp = a.cand_p + (size_t)row * kMaxTopK;
-  const int V = a.vocab;
+  const float t = a.temperature[seq];
+  *T = t;
+  *K = t > 0.0f ? a.top_k[seq] : 1;
+}
 
-  if (!(T > 0.0f)) {  // greedy: argmax, lowest id on ties
-    float best = -INFINITY;
+__global__ __launch_bounds__(kT1) void topk_stage1(FilterArgs a) {
+  __shared__ uint32_t skey[kChunkMax];
+  __shared__ int hist[256];
+  __shared__ int wsum[kT1 / 64];
+  __shared__ int s_bin, s_above, s_cnt;
+  const int row = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
+  float T;
+  int K;
+  row_params(a, row, &T, &K);
+  const int c0 = chunk * a.chunk, c1 = min(a.vocab, c0 + a.chunk);
+  const int n = c1 - c0;
+  const float *z = a.logits + (size_t)row * a.vocab + c0;
+  for (int j = tid; j < n; j += kT1) skey[j] = order_key(T > 0.0f ? __fdiv_rn(z[j], T) : z[j]);
+  __syncthreads();
+  const int Kc = min(K, n);
+  uint32_t *okey = a.stage_key + ((size_t)row * a.n_chunks + chunk) * a.kmax;
+  int32_t *oidx = a.stage_idx + ((size_t)row * a.n_chunks + chunk) * a.kmax;
+  for (int j = Kc + tid; j < a.kmax; j += kT1) {
+    okey[j] = 0u;
+    oidx[j] = 0x7fffffff;
+  }
+  if (Kc == 1) {  // argmax: largest key, lowest index among equals
+    uint32_t bk = 0u;
     int bi = 0x7fffffff;
-    for (int j = tid; j < V; j += kFT) {
-      const float v = z[j];
-      if (v > best) {
-        best = v;
+    for (int j = tid; j < n; j += kT1)
+      if (skey[j] > bk || bi == 0x7fffffff) {  // strided scan visits increasing j: '>' keeps the first
+        bk = skey[j];
         bi = j;
       }
-    }
-    __shared__ float bv[kFT];
-    __shared__ int bix[kFT];
-    bv[tid] = best;
-    bix[tid] = bi;
+    __shared__ uint32_t rk[kT1];
+    __shared__ int ri[kT1];
+    rk[tid] = bk;
+    ri[tid] = bi;
     __syncthreads();
-    for (int off = kFT / 2; off > 0; off >>= 1) {
+    for (int off = kT1 / 2; off > 0; off >>= 1) {
       if (tid < off) {
-        const float v = bv[tid + off];
-        const int i = bix[tid + off];
-        if (v > bv[tid] || (v == bv[tid] && i < bix[tid])) {
-          bv[tid] = v;
-          bix[tid] = i;
+        const uint32_t k2 = rk[tid + off];
+        const int i2 = ri[tid + off];
+        if (i2 != 0x7fffffff && (ri[tid] == 0x7fffffff || k2 > rk[tid] || (k2 == rk[tid] && i2 < ri[tid]))) {
+          rk[tid] = k2;
+          ri[tid] = i2;
         }
       }
       __syncthreads();
     }
     if (tid == 0) {
-      cid[0] = bix[0] == 0x7fffffff ? 0 : bix[0];
-      cp[0] = 1.0f;
-      a.cand_n[row] = 1;
+      okey[0] = rk[0];
+      oidx[0] = c0 + ri[0];
     }
     return;
   }
-
-  const int K = min(a.top_k[seq], V);
-  // ---- radix select of the K-th largest key
+  // radix select of the Kc-th largest key, 8 bits at a time
   uint32_t prefix = 0;
-  int need = K;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    const int nb = 1 << widths[lvl];
-    for (int j = tid; j < nb; j += kFT) hist[j] = 0;
+  int need = Kc;
+  for (int lvl = 0; lvl < 4; ++lvl) {
+    const int shift = 24 - 8 * lvl;
+    hist[tid] = 0;
     __syncthreads();
-    const int hi_shift = shifts[lvl] + widths[lvl];
-    for (int j = tid; j < V; j += kFT) {
-      const uint32_t k = order_key(__fdiv_rn(z[j], T));
-      if (lvl == 0 || (k >> hi_shift) == prefix) atomicAdd(&hist[(k >> shifts[lvl]) & (nb - 1)], 1);
+    for (int base = 0; base < n; base += kT1) {
+      const int j = base + tid;
+      const uint32_t k = j < n ? skey[j] : 0u;
+      hist_add(hist, (int)((k >> shift) & 255), j < n && (lvl == 0 || (k >> (shift + 8)) == prefix));
     }
     __syncthreads();
-    if (nb >= kFT) {
-      find_bin(hist, nb, need, wsum, &s_bin, &s_above);
-    } else {
-      if (tid == 0) {
-        int cum = 0;
-        for (int bin = nb - 1; bin >= 0; --bin) {
-          if (cum + hist[bin] >= need) {
-            s_bin = bin;
-            s_above = cum;
-            break;
-          }
-          cum += hist[bin];
+    if (tid == 0) {
+      int cum = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        if (cum + hist[bin] >= need) {
+          s_bin = bin;
+          s_above = cum;
+          break;
         }
+        cum += hist[bin];
       }
-      __syncthreads();
     }
-    prefix = (prefix << widths[lvl]) | (uint32_t)s_bin;
-    need -= s_above;
     __syncthreads();
+    prefix = (prefix << 8) | (uint32_t)s_bin;
+    need -= s_above;
   }
-  const uint32_t kth = prefix;  // the K-th largest key; `need` elements equal to it are taken
-  const int n_eq = hist[kth & 0xff];
-  const int n_gt = K - need;
-
-  // ---- gather
+  const uint32_t kth = prefix;  // `need` keys equal to it are taken, the lowest ids first
   if (tid == 0) s_cnt = 0;
   __syncthreads();
-  const bool all_fit = n_gt + n_eq <= kGather;
-  for (int j = tid; j < V; j += kFT) {
-    const uint32_t k = order_key(__fdiv_rn(z[j], T));
-    if (k > kth || (all_fit && k == kth)) {
+  for (int j = tid; j < n; j += kT1) {
+    if (skey[j] > kth) {
       const int slot = atomicAdd(&s_cnt, 1);
-      gkey[slot] = k;
-      gidx[slot] = j;
+      okey[slot] = skey[j];
+      oidx[slot] = c0 + j;
     }
   }
-  __syncthreads();
-  if (!all_fit) {
-    // Ordered scan: each thread owns a contiguous chunk, so thread order is index order.
-    const int chunk = (V + kFT - 1) / kFT;
-    const int j0 = tid * chunk, j1 = min(V, j0 + chunk);
-    int mine = 0;
-    for (int j = j0; j < j1; ++j) mine += order_key(__fdiv_rn(z[j], T)) == kth;
-    int total;
-    int rank = block_excl_scan(mine, wsum, &total);
-    for (int j = j0; j < j1 && rank < need; ++j) {
-      if (order_key(__fdiv_rn(z[j], T)) == kth) {
-        gkey[n_gt + rank] = kth;
-        gidx[n_gt + rank] = j;
-        ++rank;
-      }
+  const int n_gt = Kc - need;
+  // ties in index order: contiguous sub-ranges per thread, exclusive scan of their counts
+  const int per = (n + kT1 - 1) / kT1;
+  const int j0 = tid * per, j1 = min(n, j0 + per);
+  int mine = 0;
+  for (int j = j0; j < j1; ++j) mine += skey[j] == kth;
+  int total;
+  int rank = block_excl_scan<kT1>(mine, wsum, &total);
+  for (int j = j0; j < j1 && rank < need; ++j) {
+    if (skey[j] == kth) {
+      okey[n_gt + rank] = kth;
+      oidx[n_gt + rank] = c0 + j;
+      ++rank;
     }
-    if (tid == 0) s_cnt = K;
-    __syncthreads();
   }
-  const int cnt = s_cnt;
-  // ---- bitonic sort of the gathered set by (key desc, id asc); padding sorts last
+}
+
+__global__ __launch_bounds__(kT2) void topk_stage2(FilterArgs a) {
+  __shared__ uint32_t gkey[kMergeMax];
+  __shared__ int gidx[kMergeMax];
+  __shared__ float ge[kMaxTopK];
+  __shared__ int s_keep;
+  __shared__ float s_kept;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  float T;
+  int K;
+  row_params(a, row, &T, &K);
+  const int cnt = a.n_chunks * a.kmax;
+  const uint32_t *ik = a.stage_key + (size_t)row * cnt;
+  const int32_t *ii = a.stage_idx + (size_t)row * cnt;
   int n2 = 1;
   while (n2 < cnt) n2 <<= 1;
-  for (int j = cnt + tid; j < n2; j += kFT) {
-    gkey[j] = 0u;
-    gidx[j] = 0x7fffffff;
+  for (int j = tid; j < n2; j += kT2) {
+    gkey[j] = j < cnt ? ik[j] : 0u;
+    gidx[j] = j < cnt ? ii[j] : 0x7fffffff;
   }
   __syncthreads();
+  // bitonic sort by (key desc, id asc); padding (key 0, id max) sorts last
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += kFT) {
+      for (int i = tid; i < n2 / 2; i += kT2) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
-        const bool desc = ((lo & size) == 0);  // first half of each merge runs in sorted ("greater first") order
+        const bool desc = ((lo & size) == 0);
         const uint32_t ka = gkey[lo], kb = gkey[hi];
         const int ia = gidx[lo], ib = gidx[hi];
         const bool a_first = (ka > kb) || (ka == kb && ia < ib);
@@ -220,18 +221,32 @@ __global__ __launch_bounds__(kFT) void filter_kernel(FilterArgs a) {
       __syncthreads();
     }
   }
-  // ---- softmax over the top K, nucleus cut, renormalisation
+  if (a.argmax_out) {  // drafter argmax: the first entry
+    if (tid == 0) a.argmax_out[(row / a.am_take) * a.am_stride + a.am_offset + row % a.am_take] = gidx[0];
+    return;
+  }
+  int32_t *cid = a.cand_id + (size_t)row * kMaxTopK;
+  float *cp = a.cand_p + (size_t)row * kMaxTopK;
+  if (!(T > 0.0f)) {
+    for (int j = tid; j < kMaxTopK; j += kT2) {
+      cid[j] = j == 0 ? gidx[0] : -1;
+      cp[j] = j == 0 ? 1.0f : 0.f;
+    }
+    if (tid == 0) a.cand_n[row] = 1;
+    return;
+  }
+  const int Kr = min(K, a.vocab);
   const float s0 = key_value(gkey[0]);
-  for (int j = tid; j < K; j += kFT) ge[j] = expf(key_value(gkey[j]) - s0);
+  for (int j = tid; j < Kr; j += kT2) ge[j] = expf(key_value(gkey[j]) - s0);
   __syncthreads();
   if (tid == 0) {
     float Z = 0.f;
-    for (int j = 0; j < K; ++j) Z = Z + ge[j];
-    const float tp = a.top_p[seq];
-    int keep = K;
+    for (int j = 0; j < Kr; ++j) Z = Z + ge[j];
+    const float tp = a.top_p[row / a.rows_per_seq];
+    int keep = Kr;
     float acc = 0.f;
     if (tp < 1.0f) {
-      for (int j = 0; j < K; ++j) {
+      for (int j = 0; j < Kr; ++j) {
         acc = acc + __fdiv_rn(ge[j], Z);
         if (acc >= tp) {
           keep = j + 1;
@@ -243,11 +258,11 @@ __global__ __launch_bounds__(kFT) void filter_kernel(FilterArgs a) {
     for (int j = 0; j < keep; ++j) kept = kept + __fdiv_rn(ge[j], Z);
     s_keep = keep;
     s_kept = kept;
-    for (int j = 0; j < K; ++j) ge[j] = __fdiv_rn(ge[j], Z);  // q_j
+    for (int j = 0; j < Kr; ++j) ge[j] = __fdiv_rn(ge[j], Z);  // q_j
   }
   __syncthreads();
   const int keep = s_keep;
-  for (int j = tid; j < kMaxTopK; j += kFT) {
+  for (int j = tid; j < kMaxTopK; j += kT2) {
     if (j < keep) {
       cid[j] = gidx[j];
       cp[j] = __fdiv_rn(ge[j], s_kept);
@@ -259,9 +274,22 @@ __global__ __launch_bounds__(kFT) void filter_kernel(FilterArgs a) {
   if (tid == 0) a.cand_n[row] = keep;
 }
 
+// Chunking of a row: enough chunks to spread the row over the device, few enough that the stage-2
+// union (chunks * kmax) fits in LDS.
+void filter_plan(FilterArgs &a, int kmax) {
+  a.kmax = kmax;
+  int chunks = (a.vocab + 3999) / 4000;
+  chunks = std::max(1, std::min(chunks, kMergeMax / kmax));
+  int chunk = (a.vocab + chunks - 1) / chunks;
+  a.chunk = chunk;
+  a.n_chunks = (a.vocab + chunk - 1) / chunk;
+}
+
 hipError_t launch_filter(const FilterArgs &a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(filter_kernel, dim3(a.rows), dim3(kFT), 0, s, a);
+  if (a.chunk > kChunkMax || a.n_chunks * a.kmax > kMergeMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_stage1, dim3(a.rows, a.n_chunks), dim3(kT1), 0, s, a);
+  hipLaunchKernelGGL(topk_stage2, dim3(a.rows), dim3(kT2), 0, s, a);
   return hipGetLastError();
 }
 
