@@ -206,12 +206,15 @@ dflash_status dflash_draft_block(dflash_ctx *ctx, hipStream_t stream, int32_t ba
 dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
                                const void *d_w, float *d_y);
 
-/* Measurement access: with profiling enabled, every projection launch of the step calls is bracketed
- * by HIP events on the caller's stream.  dflash_profile_read waits for them and returns the summed
- * kernel time (ms), the summed algorithmic weight bytes of those launches and their number since
- * profiling was enabled.  Enabling or disabling resets the sums. */
+/* Measurement access.  While profiling is enabled, the library records the projection launches
+ * (kernel, shape and pointers) issued by the step calls.  dflash_profile_replay, called with
+ * profiling disabled, re-issues exactly those launches `iters` times back to back on `stream`
+ * (the optional feature-tap side output is suppressed; every other buffer they write is workspace
+ * scratch), bracketed by one pair of HIP events, and returns the elapsed ms, the algorithmic weight
+ * bytes of one pass over the recorded launches and their number.  Enabling clears the record. */
 dflash_status dflash_profile(dflash_ctx *ctx, int32_t enable);
-dflash_status dflash_profile_read(dflash_ctx *ctx, double *gemm_ms, double *gemm_bytes, int32_t *gemm_launches);
+dflash_status dflash_profile_replay(dflash_ctx *ctx, hipStream_t stream, int32_t iters, double *ms, double *bytes,
+                                    int32_t *launches);
 
 /* Synchronise `stream` and report device-side errors raised since the last call (sticky flags). */
 dflash_status dflash_device_status(dflash_ctx *ctx, hipStream_t stream);

@@ -82,7 +82,7 @@ def _load() -> C.CDLL:
         "dflash_device_status": (I, [V, V]),
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
         "dflash_profile": (I, [V, I]),
-        "dflash_profile_read": (I, [V, P(C.c_double), P(C.c_double), P(I)]),
+        "dflash_profile_replay": (I, [V, V, I, P(C.c_double), P(C.c_double), P(I)]),
         "dflash_last_error": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -172,10 +172,10 @@ def dflash_profile(ctx: int, enable: bool):
     _check(lib.dflash_profile(ctx, int(bool(enable))))
 
 
-def dflash_profile_read(ctx: int):
-    """(gemm_ms, gemm_bytes, gemm_launches) summed since profiling was enabled."""
+def dflash_profile_replay(ctx: int, iters: int, stream=None):
+    """Replay the recorded projection launches: (elapsed ms, weight bytes per pass, launches per pass)."""
     ms, by, n = C.c_double(), C.c_double(), C.c_int32()
-    _check(lib.dflash_profile_read(ctx, C.byref(ms), C.byref(by), C.byref(n)))
+    _check(lib.dflash_profile_replay(ctx, _stream(stream), iters, C.byref(ms), C.byref(by), C.byref(n)))
     return ms.value, by.value, n.value
 
 

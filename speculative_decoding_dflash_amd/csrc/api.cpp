@@ -130,12 +130,13 @@ struct dflash_ctx {
   int last_qlen = 0, last_nlogit = 0, last_batch = 0;
   std::vector<int32_t> last_slots;
   bool verified = false;
-  // optional timing of the projection launches (HIP events on the caller's stream)
+  // measurement: the projection launches issued while profiling is on, kept for replay
   bool profiling = false;
-  std::vector<hipEvent_t> ev_pool;
-  std::vector<std::pair<int, double>> ev_pending;  // (index of the start event, algorithmic bytes)
-  double prof_ms = 0.0, prof_bytes = 0.0;
-  int prof_launches = 0;
+  struct Rec {
+    GemmArgs a;
+    int rows;
+  };
+  std::vector<Rec> recorded;
 
   template <typename P> P *wsp(size_t off) const { return reinterpret_cast<P *>(ws + off); }
   SlotState *state() const { return wsp<SlotState>(L.state); }
@@ -190,19 +191,12 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s, hipEven
 }
 
 dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
-  if (!c->profiling) return run_gemm(c->es(), c->dt(), a, R, s);
-  const size_t need = c->ev_pending.size() * 2 + 2;
-  while (c->ev_pool.size() < need) {
-    hipEvent_t e;
-    HIP_OK(hipEventCreate(&e));
-    c->ev_pool.push_back(e);
+  if (c->profiling) {
+    GemmArgs r = a;
+    r.feat = nullptr;  // a replay must not touch the caller's feature buffer
+    c->recorded.push_back({r, R});
   }
-  const int i = (int)c->ev_pending.size() * 2;
-  dflash_status st = run_gemm(c->es(), c->dt(), a, R, s, c->ev_pool[i], c->ev_pool[i + 1]);
-  // weight bytes once per launch chunk (the algorithmic traffic of a weight-streaming projection)
-  const int chunks = (R + kGemmMaxRows - 1) / kGemmMaxRows;
-  c->ev_pending.push_back({i, (double)a.N * (a.epi == EPI_SWIGLU ? 2 : 1) * a.K * c->es() * chunks});
-  return st;
+  return run_gemm(c->es(), c->dt(), a, R, s);
 }
 
 QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
@@ -418,8 +412,6 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
 }
 
 dflash_status dflash_destroy(dflash_ctx *ctx) {
-  if (ctx)
-    for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
   delete ctx;
   return DFLASH_OK;
 }
@@ -715,26 +707,39 @@ dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t 
 dflash_status dflash_profile(dflash_ctx *c, int32_t enable) {
   if (!c) return fail(DFLASH_E_INVAL, "null context");
   c->profiling = enable != 0;
-  c->ev_pending.clear();
-  c->prof_ms = c->prof_bytes = 0.0;
-  c->prof_launches = 0;
+  if (enable) c->recorded.clear();
   return DFLASH_OK;
 }
 
-dflash_status dflash_profile_read(dflash_ctx *c, double *gemm_ms, double *gemm_bytes, int32_t *gemm_launches) {
-  if (!c || !gemm_ms || !gemm_bytes || !gemm_launches) return fail(DFLASH_E_INVAL, "null argument");
-  for (auto &pe : c->ev_pending) {
-    HIP_OK(hipEventSynchronize(c->ev_pool[pe.first + 1]));
-    float ms = 0.f;
-    HIP_OK(hipEventElapsedTime(&ms, c->ev_pool[pe.first], c->ev_pool[pe.first + 1]));
-    c->prof_ms += ms;
-    c->prof_bytes += pe.second;
-    ++c->prof_launches;
+dflash_status dflash_profile_replay(dflash_ctx *c, hipStream_t s, int32_t iters, double *ms, double *bytes,
+                                    int32_t *launches) {
+  if (!c || !ms || !bytes || !launches || iters < 1) return fail(DFLASH_E_INVAL, "bad argument");
+  if (c->profiling) return fail(DFLASH_E_STATE, "disable profiling before replaying");
+  double by = 0.0;
+  int n = 0;
+  for (const auto &r : c->recorded) {
+    const int chunks = (r.rows + kGemmMaxRows - 1) / kGemmMaxRows;
+    by += (double)r.a.N * (r.a.epi == EPI_SWIGLU ? 2 : 1) * r.a.K * c->es() * chunks;
+    n += chunks;
   }
-  c->ev_pending.clear();
-  *gemm_ms = c->prof_ms;
-  *gemm_bytes = c->prof_bytes;
-  *gemm_launches = c->prof_launches;
+  hipEvent_t e0, e1;
+  HIP_OK(hipEventCreate(&e0));
+  HIP_OK(hipEventCreate(&e1));
+  HIP_OK(hipEventRecord(e0, s));
+  for (int it = 0; it < iters; ++it)
+    for (const auto &r : c->recorded) {
+      dflash_status st = run_gemm(c->es(), c->dt(), r.a, r.rows, s);
+      if (st != DFLASH_OK) return st;
+    }
+  HIP_OK(hipEventRecord(e1, s));
+  HIP_OK(hipEventSynchronize(e1));
+  float t = 0.f;
+  HIP_OK(hipEventElapsedTime(&t, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *ms = t;
+  *bytes = by;
+  *launches = n;
   return DFLASH_OK;
 }
 

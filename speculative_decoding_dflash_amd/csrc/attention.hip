@@ -22,52 +22,68 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, int D> struct AttnFrag;
 
+// K fragments: kSteps 16-byte vectors per lane (A operand of S^T = K Q^T, row = key = lane % 16).
+// V fragments: D/16 vectors per lane (A operand of O^T += V^T P^T, row = dim, 4 keys per lane).
 template <int D> struct AttnFrag<bf16, D> {
   static constexpr int kSteps = D / 32;  // QK^T steps of 32 dims (8 per lane)
+  using VF = u32x2;                      // 4 bf16 keys of one dim
   static DF_DEVICE u32x4 load_q(const bf16 *qrow, int ks, int g) {
     return *reinterpret_cast<const u32x4 *>(qrow + ks * 32 + g * 8);
   }
-  static DF_DEVICE void qk(f32x4 &acc, const bf16 *kblk, int key, int g, const u32x4 *q) {
+  static DF_DEVICE void load_k(u32x4 *kf, const bf16 *kblk, int key, int g) {
 #pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
-      const u32x4 k = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 32 + g * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), __builtin_bit_cast(bf16x8, q[ks]),
+    for (int ks = 0; ks < kSteps; ++ks) kf[ks] = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 32 + g * 8);
+  }
+  static DF_DEVICE void load_v(VF *vf, const bf16 *vblk, int l16, int g) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x2 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
+  }
+  static DF_DEVICE void qk(f32x4 &acc, const u32x4 *kf, const u32x4 *q) {
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, q[ks]),
                                                     acc, 0, 0, 0);
-    }
   }
   // p[r]: probability of key 4g + r for this lane's qv.
-  static DF_DEVICE void pv(f32x4 *o, const bf16 *vblk, int l16, int g, const float *p) {
+  static DF_DEVICE void pv(f32x4 *o, const VF *vf, const float *p) {
     s16x4 pb;
     pb[0] = (short)f32_to_bf16(p[0]);
     pb[1] = (short)f32_to_bf16(p[1]);
     pb[2] = (short)f32_to_bf16(p[2]);
     pb[3] = (short)f32_to_bf16(p[3]);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x2 v = *reinterpret_cast<const u32x2 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb, o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < D / 16; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf[dt]), pb, o[dt], 0, 0, 0);
   }
 };
 
 template <int D> struct AttnFrag<float, D> {
   static constexpr int kSteps = D / 16;  // 16 dims per step (4 per lane), as 4 K=4 slices
+  using VF = u32x4;                      // 4 fp32 keys of one dim
   static DF_DEVICE u32x4 load_q(const float *qrow, int ks, int g) {
     return *reinterpret_cast<const u32x4 *>(qrow + ks * 16 + g * 4);
   }
-  static DF_DEVICE void qk(f32x4 &acc, const float *kblk, int key, int g, const u32x4 *q) {
+  static DF_DEVICE void load_k(u32x4 *kf, const float *kblk, int key, int g) {
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) kf[ks] = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 16 + g * 4);
+  }
+  static DF_DEVICE void load_v(VF *vf, const float *vblk, int l16, int g) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x4 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
+  }
+  static DF_DEVICE void qk(f32x4 &acc, const u32x4 *kf, const u32x4 *q) {
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      const f32x4 k = *reinterpret_cast<const f32x4 *>(kblk + key * D + ks * 16 + g * 4);
+      const f32x4 k = __builtin_bit_cast(f32x4, kf[ks]);
       const f32x4 qf = __builtin_bit_cast(f32x4, q[ks]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k[j], qf[j], acc, 0, 0, 0);
     }
   }
-  static DF_DEVICE void pv(f32x4 *o, const float *vblk, int l16, int g, const float *p) {
+  static DF_DEVICE void pv(f32x4 *o, const VF *vf, const float *p) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
+      const f32x4 v = __builtin_bit_cast(f32x4, vf[dt]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], p[j], o[dt], 0, 0, 0);
     }
@@ -136,45 +152,66 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int ps = kstart + wave * pt; ps < kstop; ps += 4 * pt) {
+  // Each wave walks its pages with the next page's K/V fragments already in flight; every page's
+  // fragments are loaded once and used by all query tiles.
+  auto page_of = [&](int ps) {
     const int pidx = ps / pt;
-    const int page = pidx < a.bt_stride ? bt[pidx] : -1;
+    return pidx < a.bt_stride ? bt[pidx] : -1;
+  };
+  u32x4 kf[F::kSteps], kn[F::kSteps];
+  typename F::VF vf[D / 16], vn[D / 16];
+  int ps = kstart + wave * pt;
+  int page = ps < kstop ? page_of(ps) : -1;
+  if (ps < kstop && page >= 0) {
+    F::load_k(kf, (const T *)a.kv + a.kvl.block(page, 0, kh), l16, g);
+    F::load_v(vf, (const T *)a.kv + a.kvl.block(page, 1, kh), l16, g);
+  }
+  for (; ps < kstop; ps += 4 * pt) {
+    const int nps = ps + 4 * pt;
+    const int npage = nps < kstop ? page_of(nps) : -1;
+    if (npage >= 0) {
+      F::load_k(kn, (const T *)a.kv + a.kvl.block(npage, 0, kh), l16, g);
+      F::load_v(vn, (const T *)a.kv + a.kvl.block(npage, 1, kh), l16, g);
+    }
     if (page < 0) {
       if (lane == 0) raise_err(a.err, ERR_PAGE);
-      continue;
-    }
-    const T *kblk = (const T *)a.kv + a.kvl.block(page, 0, kh);
-    const T *vblk = (const T *)a.kv + a.kvl.block(page, 1, kh);
+    } else {
 #pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      F::qk(s, kblk, l16, g, q[t]);  // lane holds S^T[key = 4g + r][qv = l16]... keys index A rows
-      float sv[4], mx = NEG;
+      for (int t = 0; t < NQT; ++t) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        F::qk(s, kf, q[t]);  // lane holds S^T[key = 4g + r][qv = l16]
+        float sv[4], mx = NEG;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kp = ps + 4 * g + r;
-        bool ok = qok[t] && kp >= klo && kp < khi;
-        if (a.mode == 0) ok = ok && kp <= qpos[t];
-        else ok = ok && (kp >= nblk || a.window <= 0 || qpos[t] - kp < a.window);
-        sv[r] = ok ? s[r] * scale : NEG;
-        mx = fmaxf(mx, sv[r]);
+        for (int r = 0; r < 4; ++r) {
+          const int kp = ps + 4 * g + r;
+          bool ok = qok[t] && kp >= klo && kp < khi;
+          if (a.mode == 0) ok = ok && kp <= qpos[t];
+          else ok = ok && (kp >= nblk || a.window <= 0 || qpos[t] - kp < a.window);
+          sv[r] = ok ? s[r] * scale : NEG;
+          mx = fmaxf(mx, sv[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m[t], mx);
+        const float corr = (m[t] == NEG) ? 0.f : expf(m[t] - mn);
+        float p[4], ps_sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = (sv[r] == NEG) ? 0.f : expf(sv[r] - mn);
+          ps_sum += p[r];
+        }
+        l[t] = l[t] * corr + ps_sum;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
+        F::pv(o[t], vf, p);
+        m[t] = mn;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[t], mx);
-      const float corr = (m[t] == NEG) ? 0.f : expf(m[t] - mn);
-      float p[4], ps_sum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = (sv[r] == NEG) ? 0.f : expf(sv[r] - mn);
-        ps_sum += p[r];
-      }
-      l[t] = l[t] * corr + ps_sum;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
-      F::pv(o[t], vblk, l16, g, p);
-      m[t] = mn;
     }
+    page = npage;
+#pragma unroll
+    for (int k = 0; k < F::kSteps; ++k) kf[k] = kn[k];
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) vf[k] = vn[k];
   }
 
   // Merge the four waves, one 16-qv tile at a time.
@@ -225,26 +262,36 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// out[row][head] = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s  (splits in order)
+// out[row][head] = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s  (splits in order).
+// One work-group per (row, head): thread s reads split s's (m, l) in parallel; then each thread sums its
+// dimension over the splits with independent, unrolled loads.
 template <typename T>
-__global__ void attn_merge_kernel(AttnArgs a, int n_rows) {
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows) {
+  __shared__ float sw[64];
+  __shared__ float s_L;
   const int rh = blockIdx.x;  // row * q_heads + head
   const int D = a.kvl.head_dim;
   const int row = rh / a.q_heads, head = rh % a.q_heads;
   const float NEG = -INFINITY;
   const float *ml = a.part_ml + (size_t)rh * a.n_splits * 2;
-  float M = NEG;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, ml[2 * s]);
-  for (int dim = threadIdx.x; dim < D; dim += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    if (M != NEG) {
-      for (int s = 0; s < a.n_splits; ++s) {
-        const float ms = ml[2 * s];
-        const float f = (ms == NEG) ? 0.f : expf(ms - M);
-        L += f * ml[2 * s + 1];
-        O += f * a.part_o[((size_t)rh * a.n_splits + s) * D + dim];
-      }
-    }
+  const int tid = threadIdx.x;
+  const float ms = tid < a.n_splits ? ml[2 * tid] : NEG;
+  float M = ms;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));  // wave 0 holds all splits
+  if (tid < 64) sw[tid] = (tid < a.n_splits && ms != NEG && M != NEG) ? expf(ms - M) : 0.f;
+  __syncthreads();
+  if (tid == 0) {
+    float L = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) L += sw[s] * ml[2 * s + 1];
+    s_L = L;
+  }
+  __syncthreads();
+  const float L = s_L;
+  const float *po = a.part_o + (size_t)rh * a.n_splits * D;
+  for (int dim = tid; dim < D; dim += blockDim.x) {
+    float O = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < a.n_splits; ++s) O += sw[s] * po[(size_t)s * D + dim];
     Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
   }
 }
@@ -264,7 +311,7 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   const int n_rows = a.n_seq * a.q_len;
-  hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(n_rows * a.q_heads), dim3(D), 0, s, a, n_rows);
+  hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(n_rows * a.q_heads), dim3(128), 0, s, a, n_rows);
   return hipGetLastError();
 }
 
