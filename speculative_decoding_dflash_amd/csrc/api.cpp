@@ -38,12 +38,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 
 constexpr int kAttnSplitMax = 64;
+constexpr int kMaxKSplit = 8;
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, qkvf, att_o, att_ml, cbuf, dlogits, cid, cp, cn, skey,
-      sidx, total;
-  size_t qkvf_cols, att_rows;
+  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, part, att_o, att_ml, dlogits, cid, cp, cn, skey, sidx,
+      total;
+  size_t part_elems, att_rows;
 };
 
 Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
@@ -67,12 +68,14 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.qbuf = take(es * R * QD);
   L.attn = take(es * R * QD);
   L.ffn = take(es * R * F);
-  L.qkvf_cols = std::max(QD + 2 * KD, (size_t)d->layers * 2 * KD);
-  L.qkvf = take(sizeof(float) * R * L.qkvf_cols);
+  // fp32 K-range partials of one projection: up to kMaxKSplit ranges of a single row chunk, or one
+  // range over all rows
+  const size_t part_cols = std::max({QD + 2 * KD, (size_t)d->layers * 2 * KD, H});
+  L.part_elems = std::max(R, (size_t)kMaxKSplit * kGemmMaxRows) * part_cols;
+  L.part = take(sizeof(float) * L.part_elems);
   L.att_rows = (size_t)cap->max_slots * B;
   L.att_o = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * c->head_dim);
   L.att_ml = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * 2);
-  L.cbuf = take(sizeof(float) * R * H);
   L.dlogits = take(sizeof(float) * cap->max_slots * (B > 1 ? B - 1 : 1) * V);
   const size_t srows = (size_t)cap->max_slots * std::max<size_t>(B, 1);
   L.cid = take(sizeof(int32_t) * srows * kMaxTopK);
@@ -172,6 +175,7 @@ GemmArgs gemm_base(const void *x, int ldx, int M, int N, int K, int epi) {
   a.N = N;
   a.K = K;
   a.epi = epi;
+  a.ksplit = 1;
   return a;
 }
 
@@ -191,18 +195,51 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s, hipEven
 }
 
 dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
-  if (c->profiling) {
-    GemmArgs r = a;
-    r.feat = nullptr;  // a replay must not touch the caller's feature buffer
-    c->recorded.push_back({r, R});
-  }
+  if (c->profiling) c->recorded.push_back({a, R});
   return run_gemm(c->es(), c->dt(), a, R, s);
+}
+
+// A projection whose K ranges write fp32 partial slices [range][R][N] into the partial buffer; the
+// consumer (norm_kernel, qkv_post_kernel) adds the *n_part slices in order.
+dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *n_part) {
+  a.epi = EPI_PARTIAL;
+  a.out_f32 = c->wsp<float>(c->L.part);
+  a.ld_out = a.N;
+  a.ksplit = R <= kGemmMaxRows ? std::min(kMaxKSplit, gemm_ksplit(R, a.N, a.K, c->dt(), c->L.part_elems)) : 1;
+  a.part_stride = (int64_t)R * a.N;
+  *n_part = a.ksplit;
+  return run_gemm(c, a, R, s);
+}
+
+// RMSNorm of all R rows of the hidden width into xn (no residual, no partials yet).
+NormArgs norm_base(dflash_ctx *c, int R, const void *gain) {
+  NormArgs n;
+  memset(&n, 0, sizeof n);
+  n.gain = (const float *)gain;
+  n.eps = c->cfg.rms_eps;
+  n.hidden = c->cfg.hidden;
+  n.out = c->wsp<void>(c->L.xn);
+  n.ld_out = c->cfg.hidden;
+  n.n_rows = R;
+  n.take = R;
+  n.stride = R;
+  n.offset = 0;
+  return n;
+}
+
+// Adds the partial slices of the last projection (N = hidden) to the norm's row values.
+void norm_parts(dflash_ctx *c, NormArgs &n, int n_part) {
+  n.part = c->wsp<float>(c->L.part);
+  n.n_part = n_part;
+  n.ld_part = c->cfg.hidden;
+  n.part_stride = (int64_t)n.n_rows * c->cfg.hidden;
 }
 
 QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
   QkvPostArgs p;
   memset(&p, 0, sizeof p);
-  p.src = c->wsp<float>(c->L.qkvf);
+  p.src = c->wsp<float>(c->L.part);
+  p.n_part = 1;
   p.n_rows = n_rows;
   p.rows = rows;
   p.block_table = c->bt();
@@ -234,17 +271,18 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   const int G = m.q_heads / m.kv_heads;
   a.q_tile = std::max(1, std::min(q_len, 64 / G));
   const int ntile = (q_len + a.q_tile - 1) / a.q_tile;
-  const int wgs = n_seq * m.kv_heads * ntile;
   const int pt = c->cap.page_tokens;
   int key_span = ctx_bound + pt;  // keys of the widest work-group, rounded out to pages
   if (mode == 1 && c->dcfg.window > 0) key_span = std::min(key_span, c->dcfg.window + q_len + 2 * pt);
   const int pages = (key_span + pt - 1) / pt;
+  // Decode-sized calls split the keys into ranges of about six pages (the fastest on MI355X at 1-2K
+  // keys: a few pages per wave, merged by attn_merge_kernel); larger calls keep one range.
   int splits = 1;
-  if ((size_t)n_seq * q_len <= c->L.att_rows) {
-    splits = std::max(1, 512 / std::max(1, wgs));
-    splits = std::min({splits, kAttnSplitMax, std::max(1, pages / 4)});
-  }
-  const int pps = (pages + splits - 1) / splits;
+  if ((size_t)n_seq * q_len <= c->L.att_rows) splits = std::min(kAttnSplitMax, std::max(1, (pages + 5) / 6));
+  int pps = (pages + splits - 1) / splits;
+  static const int env_pps = getenv("DFLASH_ATTN_PPS") ? atoi(getenv("DFLASH_ATTN_PPS")) : 0;
+  if (env_pps > 0 && (pages + env_pps - 1) / env_pps <= kAttnSplitMax && (size_t)n_seq * q_len <= c->L.att_rows)
+    pps = env_pps;
   a.n_splits = (pages + pps - 1) / pps;
   a.split_tokens = pps * pt;
   a.part_o = c->wsp<float>(c->L.att_o);
@@ -252,31 +290,33 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.out = c->wsp<void>(c->L.attn);
   a.ldo = m.q_heads * m.head_dim;
   a.err = c->err();
-  (void)wgs;
   HIP_OK(launch_attention(a, c->dt(), s));
   return DFLASH_OK;
 }
 
-// One decoder layer over R rows (x fp32 in place).  feat: optional tap output (act, row stride ld_feat).
+// One decoder layer over R rows.  On entry xn holds the attention-normalised rows; the residual x
+// (fp32) is updated in place.  `next` is the RMSNorm that follows the layer (the next layer's attention
+// norm, or the final norm over the rows that need logits); feat: optional tap of the layer's output.
 dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows, int n_seq,
-                        int q_len, int attn_mode, int ctx_bound, void *feat, int ld_feat, hipStream_t s) {
+                        int q_len, int attn_mode, int ctx_bound, void *feat, int ld_feat, NormArgs next,
+                        hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   const int R = n_seq * q_len, H = m.hidden, QD = m.q_heads * m.head_dim, KD = m.kv_heads * m.head_dim, F = m.ffn;
   float *x = c->wsp<float>(c->L.x);
   void *xn = c->wsp<void>(c->L.xn);
   dflash_status st;
-  HIP_OK(launch_rmsnorm(x, H, R, R, 0, R, (const float *)w.attn_norm, m.rms_eps, H, xn, H, c->dt(), s));
+  int np = 1;
   {
-    GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_STORE_F32);
+    GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_PARTIAL);
     a.nseg = 3;
     a.seg[0] = GemmSeg{w.wq, QD};
     a.seg[1] = GemmSeg{w.wk, KD};
     a.seg[2] = GemmSeg{w.wv, KD};
-    a.out_f32 = c->wsp<float>(c->L.qkvf);
-    a.ld_out = QD + 2 * KD;
-    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+    if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
     QkvPostArgs p = post_base(c, rows, R);
     p.ld_src = QD + 2 * KD;
+    p.n_part = np;
+    p.part_stride = (int64_t)R * (QD + 2 * KD);
     p.nseg = 3;
     p.seg[0] = PostSeg{m.q_heads, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
     p.seg[1] = PostSeg{m.kv_heads, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
@@ -286,14 +326,16 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   }
   if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, s)) != DFLASH_OK) return st;
   {
-    GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_PARTIAL);
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.wo, H};
-    a.resid = x;
-    a.ld_resid = H;
-    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+    if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
+    NormArgs n = norm_base(c, R, w.ffn_norm);
+    n.x = x;
+    n.ld_x = H;
+    norm_parts(c, n, np);
+    HIP_OK(launch_norm(n, c->dt(), s));
   }
-  HIP_OK(launch_rmsnorm(x, H, R, R, 0, R, (const float *)w.ffn_norm, m.rms_eps, H, xn, H, c->dt(), s));
   {
     GemmArgs a = gemm_base(xn, H, R, F, H, EPI_SWIGLU);
     a.nseg = 2;
@@ -304,14 +346,16 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   {
-    GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_PARTIAL);
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.w_down, H};
-    a.resid = x;
-    a.ld_resid = H;
-    a.feat = feat;
-    a.ld_feat = ld_feat;
-    if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
+    if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
+    next.x = x;
+    next.ld_x = H;
+    next.feat = feat;
+    next.ld_feat = ld_feat;
+    norm_parts(c, next, np);
+    HIP_OK(launch_norm(next, c->dt(), s));
   }
   return DFLASH_OK;
 }
@@ -494,18 +538,28 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
   HIP_OK(launch_embed(c->embed, c->dt(), rows, R, H, m.vocab, c->wsp<float>(c->L.x), c->err(), s));
+  {
+    NormArgs n = norm_base(c, R, c->tl[0].attn_norm);
+    n.x = c->wsp<float>(c->L.x);
+    n.ld_x = H;
+    HIP_OK(launch_norm(n, c->dt(), s));
+  }
   const int ctx_bound = c->max_ctx(slots, batch);
   const int ld_feat = c->dcfg.n_taps * H;
+  const int nl = n_logit_rows;
   for (int l = 0; l < m.layers; ++l) {
     void *feat = nullptr;
     for (int t = 0; t < c->dcfg.n_taps; ++t)
       if (c->dcfg.taps[t] == l && d_feats) feat = (char *)d_feats + (size_t)t * H * c->es();
-    st = run_layer(c, c->tl[l], c->tlayer(l), rows, batch, q_len, 0, ctx_bound, feat, ld_feat, s);
+    NormArgs next = norm_base(c, R, l + 1 < m.layers ? c->tl[l + 1].attn_norm : c->final_norm);
+    if (l + 1 == m.layers) {  // final norm: the last nl rows of every sequence, packed
+      next.take = nl;
+      next.stride = q_len;
+      next.offset = q_len - nl;
+    }
+    st = run_layer(c, c->tl[l], c->tlayer(l), rows, batch, q_len, 0, ctx_bound, feat, ld_feat, next, s);
     if (st != DFLASH_OK) return st;
   }
-  const int nl = n_logit_rows;
-  HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.x), H, nl, q_len, q_len - nl, batch * nl, (const float *)c->final_norm,
-                        m.rms_eps, H, c->wsp<void>(c->L.xn), H, c->dt(), s));
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
@@ -622,17 +676,17 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
   {
-    GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_STORE_F32);
+    GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_PARTIAL);
     a.nseg = 1;
     a.seg[0] = GemmSeg{c->fc, H};
-    a.out_f32 = c->wsp<float>(c->L.cbuf);
-    a.ld_out = H;
-    if ((st = run_gemm(c, a, Ri, s)) != DFLASH_OK) return st;
+    int np = 1;
+    if ((st = run_partial(c, a, Ri, s, &np)) != DFLASH_OK) return st;
+    NormArgs n = norm_base(c, Ri, c->hidden_norm);
+    norm_parts(c, n, np);
+    HIP_OK(launch_norm(n, c->dt(), s));
   }
-  HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.cbuf), H, Ri, Ri, 0, Ri, (const float *)c->hidden_norm, m.rms_eps, H,
-                        c->wsp<void>(c->L.xn), H, c->dt(), s));
   {
-    GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_STORE_F32);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_PARTIAL);
     a.nseg = 2 * dc.layers;
     QkvPostArgs p = post_base(c, ri, Ri);
     p.ld_src = dc.layers * 2 * KD;
@@ -644,9 +698,10 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
       p.seg[2 * j + 1] = PostSeg{m.kv_heads, ROLE_V, nullptr, c->dlayer(j), 0};
     }
     p.total_heads = dc.layers * 2 * m.kv_heads;
-    a.out_f32 = c->wsp<float>(c->L.qkvf);
-    a.ld_out = dc.layers * 2 * KD;
-    if ((st = run_gemm(c, a, Ri, s)) != DFLASH_OK) return st;
+    int np = 1;
+    if ((st = run_partial(c, a, Ri, s, &np)) != DFLASH_OK) return st;
+    p.n_part = np;
+    p.part_stride = (int64_t)Ri * (dc.layers * 2 * KD);
     HIP_OK(launch_qkv_post(p, c->dt(), s));
   }
   // 2. The block [anchor, MASK x (B-1)].
@@ -658,14 +713,24 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   HIP_OK(launch_prep(p, s));
   const int R = batch * B;
   HIP_OK(launch_embed(c->embed, c->dt(), rd, R, H, m.vocab, c->wsp<float>(c->L.x), c->err(), s));
+  {
+    NormArgs n = norm_base(c, R, c->dl[0].attn_norm);
+    n.x = c->wsp<float>(c->L.x);
+    n.ld_x = H;
+    HIP_OK(launch_norm(n, c->dt(), s));
+  }
   const int ctx_bound = c->max_ctx(slots, batch);
+  const int nd = B - 1;
   for (int j = 0; j < dc.layers; ++j) {
-    st = run_layer(c, c->dl[j], c->dlayer(j), rd, batch, B, 1, ctx_bound, nullptr, 0, s);
+    NormArgs next = norm_base(c, R, j + 1 < dc.layers ? c->dl[j + 1].attn_norm : c->d_final_norm);
+    if (j + 1 == dc.layers) {  // final norm: the B - 1 mask positions of every block, packed
+      next.take = nd;
+      next.stride = B;
+      next.offset = 1;
+    }
+    st = run_layer(c, c->dl[j], c->dlayer(j), rd, batch, B, 1, ctx_bound, nullptr, 0, next, s);
     if (st != DFLASH_OK) return st;
   }
-  const int nd = B - 1;
-  HIP_OK(launch_rmsnorm(c->wsp<float>(c->L.x), H, nd, B, 1, batch * nd, (const float *)c->d_final_norm, m.rms_eps, H,
-                        c->wsp<void>(c->L.xn), H, c->dt(), s));
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;

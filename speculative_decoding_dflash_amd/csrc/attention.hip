@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int np = min(a.q_tile, a.q_len - p0);
   const int nqv = np * G;
   const int rbase = b * a.q_len + p0;
-  const float scale = 1.0f / sqrtf((float)D);
+  // scores are kept in log2 units (scaled by log2 e), so that every exponential is one v_exp_f32
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
   const float NEG = -INFINITY;
 
   int qpos[NQT];
@@ -136,6 +137,22 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     khi = nblk + a.q_len;
     klo = a.window > 0 ? max(0, first_pos - a.window + 1) : 0;
   }
+  // Key range [lo, hi) of every query vector: causal (mode 0); block keys plus the sliding window of
+  // context keys (mode 1, the drafter); empty for padding query vectors.
+  int lo[NQT], hi[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    if (!qok[t]) {
+      lo[t] = 1;
+      hi[t] = 0;
+    } else if (a.mode == 0) {
+      lo[t] = klo;
+      hi[t] = min(khi, qpos[t] + 1);
+    } else {
+      lo[t] = a.window > 0 ? max(klo, min(nblk, qpos[t] - a.window + 1)) : klo;
+      hi[t] = khi;
+    }
+  }
   const int pt = a.kvl.page_tokens;
   const int kstart = (klo / pt) * pt + split * a.split_tokens;
   const int kstop = min(khi, kstart + a.split_tokens);
@@ -152,66 +169,74 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // Each wave walks its pages with the next page's K/V fragments already in flight; every page's
-  // fragments are loaded once and used by all query tiles.
-  auto page_of = [&](int ps) {
-    const int pidx = ps / pt;
-    return pidx < a.bt_stride ? bt[pidx] : -1;
-  };
-  u32x4 kf[F::kSteps], kn[F::kSteps];
-  typename F::VF vf[D / 16], vn[D / 16];
-  int ps = kstart + wave * pt;
-  int page = ps < kstop ? page_of(ps) : -1;
-  if (ps < kstop && page >= 0) {
-    F::load_k(kf, (const T *)a.kv + a.kvl.block(page, 0, kh), l16, g);
-    F::load_v(vf, (const T *)a.kv + a.kvl.block(page, 1, kh), l16, g);
-  }
-  for (; ps < kstop; ps += 4 * pt) {
-    const int nps = ps + 4 * pt;
-    const int npage = nps < kstop ? page_of(nps) : -1;
-    if (npage >= 0) {
-      F::load_k(kn, (const T *)a.kv + a.kvl.block(npage, 0, kh), l16, g);
-      F::load_v(vn, (const T *)a.kv + a.kvl.block(npage, 1, kh), l16, g);
+  // Wave w takes the split's pages w, w + 4, ..., in chunks of 64: lane i holds the block-table entry
+  // of the chunk's page i (read once per chunk), and two pages' K/V fragments are in flight while one
+  // is consumed.  Loads past the chunk's last page read a valid dummy block (the pool's first), so
+  // that every load is unconditional.
+  const int npg = kstop > kstart ? (kstop - kstart + pt - 1) / pt : 0;
+  const int n_all = wave < npg ? (npg - wave + 3) / 4 : 0;
+  const T *kvb = (const T *)a.kv;
+  const T *dummy = kvb;
+  u32x4 kf[2][F::kSteps];
+  typename F::VF vf[2][D / 16];
+  for (int c0 = 0; c0 < n_all; c0 += 64) {
+    const int n_my = min(64, n_all - c0);
+    int my_bt = -1;
+    if (lane < n_my) {
+      const int pidx = (kstart + (wave + 4 * (c0 + lane)) * pt) / pt;
+      my_bt = pidx < a.bt_stride ? bt[pidx] : -1;
     }
-    if (page < 0) {
-      if (lane == 0) raise_err(a.err, ERR_PAGE);
-    } else {
 #pragma unroll
-      for (int t = 0; t < NQT; ++t) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        F::qk(s, kf, q[t]);  // lane holds S^T[key = 4g + r][qv = l16]
-        float sv[4], mx = NEG;
+    for (int p = 0; p < 2; ++p) {
+      const int pg = p < n_my ? __builtin_amdgcn_readlane(my_bt, p) : -1;
+      F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
+      F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
+    }
+    for (int i0 = 0; i0 < n_my; i0 += 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kp = ps + 4 * g + r;
-          bool ok = qok[t] && kp >= klo && kp < khi;
-          if (a.mode == 0) ok = ok && kp <= qpos[t];
-          else ok = ok && (kp >= nblk || a.window <= 0 || qpos[t] - kp < a.window);
-          sv[r] = ok ? s[r] * scale : NEG;
-          mx = fmaxf(mx, sv[r]);
+      for (int p = 0; p < 2; ++p) {
+        const int ii = i0 + p;
+        if (ii < n_my) {  // wave-uniform
+          const int ps = kstart + (wave + 4 * (c0 + ii)) * pt;
+          if (__builtin_amdgcn_readlane(my_bt, ii) < 0) {
+            if (lane == 0) raise_err(a.err, ERR_PAGE);
+          } else {
+#pragma unroll
+            for (int t = 0; t < NQT; ++t) {
+              f32x4 s = {0.f, 0.f, 0.f, 0.f};
+              F::qk(s, kf[p], q[t]);  // lane holds S^T[key = 4g + r][qv = l16]
+              float sv[4], mx = NEG;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int kp = ps + 4 * g + r;
+                sv[r] = (kp >= lo[t] && kp < hi[t]) ? s[r] * scale : NEG;
+                mx = fmaxf(mx, sv[r]);
+              }
+              mx = fmaxf(mx, __shfl_xor(mx, 16));
+              mx = fmaxf(mx, __shfl_xor(mx, 32));
+              const float mn = fmaxf(m[t], mx);
+              const float mb = (mn == NEG) ? 0.f : mn;  // exp2(-inf - mb) = 0 for masked keys
+              const float corr = __builtin_amdgcn_exp2f(m[t] - mb);
+              float pr[4], ps_sum = 0.f;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                pr[r] = __builtin_amdgcn_exp2f(sv[r] - mb);
+                ps_sum += pr[r];
+              }
+              l[t] = l[t] * corr + ps_sum;
+#pragma unroll
+              for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
+              F::pv(o[t], vf[p], pr);
+              m[t] = mn;
+            }
+          }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[t], mx);
-        const float corr = (m[t] == NEG) ? 0.f : expf(m[t] - mn);
-        float p[4], ps_sum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = (sv[r] == NEG) ? 0.f : expf(sv[r] - mn);
-          ps_sum += p[r];
-        }
-        l[t] = l[t] * corr + ps_sum;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
-        F::pv(o[t], vf, p);
-        m[t] = mn;
+        const int nx = ii + 2;
+        const int pg = nx < n_my ? __builtin_amdgcn_readlane(my_bt, nx) : -1;
+        F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
+        F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
       }
     }
-    page = npage;
-#pragma unroll
-    for (int k = 0; k < F::kSteps; ++k) kf[k] = kn[k];
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) vf[k] = vn[k];
   }
 
   // Merge the four waves, one 16-qv tile at a time.
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float mw = sm[w][t * 16 + qi];
-          const float f = (mw == NEG) ? 0.f : expf(mw - M);
+          const float f = (mw == NEG) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
           L += f * sl[w][t * 16 + qi];
           O += f * so[w][qi][dim];
         }
@@ -262,7 +287,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// out[row][head] = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s  (splits in order).
+// out[row][head] = sum_s 2^{m_s - M} O_s / sum_s 2^{m_s - M} l_s  (splits in order; m in log2 units).
 // One work-group per (row, head): thread s reads split s's (m, l) in parallel; then each thread sums its
 // dimension over the splits with independent, unrolled loads.
 template <typename T>
@@ -278,7 +303,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows)
   const float ms = tid < a.n_splits ? ml[2 * tid] : NEG;
   float M = ms;
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));  // wave 0 holds all splits
-  if (tid < 64) sw[tid] = (tid < a.n_splits && ms != NEG && M != NEG) ? expf(ms - M) : 0.f;
+  if (tid < 64) sw[tid] = (tid < a.n_splits && ms != NEG && M != NEG) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
   __syncthreads();
   if (tid == 0) {
     float L = 0.f;

@@ -15,9 +15,9 @@
 //   * the NW waves reduce their partial tiles through LDS in a fixed order, then the whole
 //     work-group runs the epilogue on its columns.  No state crosses work-groups, so no device-scope
 //     fences (which write back and invalidate the per-XCD L2s) are needed anywhere.
-// Epilogues: fp32 store (logits, q/k/v before their per-head normalisation), activation store,
-// residual add (+ optional feature tap), and SwiGLU (gate and up rows of the same output column in
-// one work-group).
+// Epilogues: fp32 store (logits), activation store, fp32 partial store of one K range (grid row y;
+// the consumer sums the ranges in order: residual add + RMSNorm, q/k/v post-processing), and SwiGLU
+// (gate and up rows of the same output column in one work-group).
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
@@ -50,11 +50,12 @@ template <typename T> DF_DEVICE u32x4 ld16(const T *p) { return *reinterpret_cas
 
 DF_DEVICE float silu(float g) { return g / (1.0f + expf(-g)); }
 
-template <typename T, int MT, int CT, int NW>
+template <typename T, int MT, int CT, int NW, int PD, int XR>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Frag<T>;
   constexpr int COLS = 16 * CT;
-  constexpr int XR = 16 * MT;              // X rows staged (padded to whole MFMA tiles)
+  // XR: X rows staged per super-step (8 when M <= 8, else padded to whole MFMA tiles, 16 * MT)
+  static_assert(XR == 16 * MT || (MT == 1 && XR == 8), "X staging rows");
   constexpr int NT = NW * 64;
   constexpr int ROWB = 256 + 16;           // LDS bytes per staged row (256 B of K plus padding)
   constexpr int NQ = COLS / 4;             // weight quad loads per super-step (4 rows x 256 B each)
@@ -70,6 +71,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   const int r16 = lane & 15, g = lane >> 4;
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int c = blockIdx.x;
+  const int split = blockIdx.y;
+  const int Kc = a.K / a.ksplit;  // this work-group's K range: [split * Kc, (split + 1) * Kc)
+  const int k0 = split * Kc;
 
   const T *wbase[CT];  // row 16*ct of the tile
   if (swiglu) {
@@ -90,14 +94,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   // 16 * r16 .. 16 * r16 + 15 of the 256-byte window.
   const T *qrow[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) qrow[q] = wbase[q / 4] + (size_t)(4 * (q % 4) + g) * a.K + r16 * F::kEPL;
+  for (int q = 0; q < NQ; ++q) qrow[q] = wbase[q / 4] + (size_t)(4 * (q % 4) + g) * a.K + k0 + r16 * F::kEPL;
+  // X rows >= M load row 0 (never read back: the operand read below masks them), so that every
+  // load in the streaming loop is unconditional and the compiler can count outstanding loads exactly.
   const T *xrow[NXQ];
-  bool xq[NXQ];
 #pragma unroll
   for (int q = 0; q < NXQ; ++q) {
     const int m = 4 * q + g;
-    xq[q] = m < a.M;
-    xrow[q] = (const T *)a.x + (size_t)(xq[q] ? m : 0) * a.ldx + r16 * F::kEPL;
+    xrow[q] = (const T *)a.x + (size_t)(m < a.M ? m : 0) * a.ldx + k0 + r16 * F::kEPL;
   }
 
   f32x4 acc[MT][CT];
@@ -109,46 +113,62 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
   unsigned char *wt = smem + wave * (COLS + XR) * ROWB;
   unsigned char *xt = wt + COLS * ROWB;
-  const int nsup = a.K / SK;  // streamed super-steps; wave w takes w, w + NW, ...
-  u32x4 cur[NQ], curx[NXQ];
-  int sup = wave;
-  if (sup < nsup) {
+  const int nsup = Kc / SK;  // streamed super-steps; wave w takes w, w + NW, ...
+  // PD register buffers per wave: PD super-steps are in flight while one is consumed.  Loads past the
+  // wave's last super-step are redirected to X's first 256 bytes (cache-resident, never consumed),
+  // which keeps them unconditional.
+  const T *dummy = (const T *)a.x + r16 * F::kEPL;
+  u32x4 buf[PD][NQ], bufx[PD][NXQ];
+  if (nsup > 0) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) cur[q] = ld16(qrow[q] + (size_t)sup * SK);
+    for (int p = 0; p < PD; ++p) {
+      const int s0 = wave + p * NW;
+      const bool ok = s0 < nsup;
 #pragma unroll
-    for (int q = 0; q < NXQ; ++q) curx[q] = xq[q] ? ld16(xrow[q] + (size_t)sup * SK) : zero;
-  }
-  for (; sup < nsup; sup += NW) {
+      for (int q = 0; q < NQ; ++q) buf[p][q] = ld16(ok ? qrow[q] + (size_t)s0 * SK : dummy);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = cur[q];
-#pragma unroll
-    for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = curx[q];
-    // keep the next super-step in flight while this one is consumed
-    const int nxt = sup + NW;
-    if (nxt < nsup) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) cur[q] = ld16(qrow[q] + (size_t)nxt * SK);
-#pragma unroll
-      for (int q = 0; q < NXQ; ++q) curx[q] = xq[q] ? ld16(xrow[q] + (size_t)nxt * SK) : zero;
+      for (int q = 0; q < NXQ; ++q) bufx[p][q] = ld16(ok ? xrow[q] + (size_t)s0 * SK : dummy);
+      __builtin_amdgcn_sched_barrier(0);  // keep buffer p's loads ahead of buffer p + 1's
     }
+  }
+  for (int sup = wave; sup < nsup; sup += PD * NW) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 xv[MT];
+    for (int p = 0; p < PD; ++p) {
+      const int cs = sup + p * NW;
+      if (cs < nsup) {  // wave-uniform
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        xv[mt] = (mt * 16 + r16 < a.M) ? *reinterpret_cast<const u32x4 *>(xt + (mt * 16 + r16) * ROWB + ks * 64 + 16 * g)
-                                       : zero;
+        for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = buf[p][q];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * ct + r16) * ROWB + ks * 64 + 16 * g);
+        for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[p][q];
+      }
+      const int nxt = cs + PD * NW;
+      const bool ok = nxt < nsup;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) F::mma(acc[mt][ct], xv[mt], wv);
+      for (int q = 0; q < NQ; ++q) buf[p][q] = ld16(ok ? qrow[q] + (size_t)nxt * SK : dummy);
+#pragma unroll
+      for (int q = 0; q < NXQ; ++q) bufx[p][q] = ld16(ok ? xrow[q] + (size_t)nxt * SK : dummy);
+      if (cs < nsup) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 xv[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            xv[mt] = (mt * 16 + r16 < a.M)
+                         ? *reinterpret_cast<const u32x4 *>(xt + (mt * 16 + (r16 < XR ? r16 : 0)) * ROWB + ks * 64 + 16 * g)
+                         : zero;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * ct + r16) * ROWB + ks * 64 + 16 * g);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) F::mma(acc[mt][ct], xv[mt], wv);
+          }
+        }
       }
     }
   }
   // K tail (K not a multiple of the super-step): direct MFMA-layout loads
-  for (int st = nsup * KS + wave; st < a.K / F::kStep; st += NW) {
-    const int k = st * F::kStep + g * F::kEPL;
+  for (int st = nsup * KS + wave; st < Kc / F::kStep; st += NW) {
+    const int k = k0 + st * F::kStep + g * F::kEPL;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r16;
@@ -189,15 +209,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
         Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + COLS * c + j, lds[m * COLS + j]);
       }
       break;
-    case EPI_RESID:
+    case EPI_PARTIAL: {
+      float *o = a.out_f32 + (size_t)split * a.part_stride;
       for (int e = tid; e < M * COLS; e += NT) {
         const int m = e / COLS, j = e % COLS;
-        const size_t idx = (size_t)(a.row_off + m) * a.ld_resid + COLS * c + j;
-        const float v = a.resid[idx] + lds[m * COLS + j];
-        a.resid[idx] = v;
-        if (a.feat) Elem<T>::store((T *)a.feat + (size_t)(a.row_off + m) * a.ld_feat + COLS * c + j, v);
+        o[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j];
       }
       break;
+    }
     case EPI_SWIGLU:
       for (int e = tid; e < M * 16; e += NT) {
         const int m = e / 16, j = e % 16;
@@ -215,48 +234,108 @@ int env_int(const char *name, int dflt) {
 }
 }  // namespace
 
-template <typename T, int MT>
-static void launch_mt(const GemmArgs &a, int ct, int nw, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const int tiles = a.epi == EPI_SWIGLU ? a.N / 16 : a.N / (16 * ct);
-  dim3 grid(tiles);
+template <typename T, int MT, int CT, int NW, int XR>
+static void launch_xr(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   // hipExtLaunchKernelGGL carries the optional timing events in the dispatch itself
+  if constexpr (MT == 1) {
+    if (pd == 3) {
+      hipExtLaunchKernelGGL((gemm_kernel<T, MT, CT, NW, 3, XR>), grid, dim3(NW * 64), 0, s, e0, e1, 0, a);
+      return;
+    }
+    if (pd == 2) {
+      hipExtLaunchKernelGGL((gemm_kernel<T, MT, CT, NW, 2, XR>), grid, dim3(NW * 64), 0, s, e0, e1, 0, a);
+      return;
+    }
+  }
+  hipExtLaunchKernelGGL((gemm_kernel<T, MT, CT, NW, 1, XR>), grid, dim3(NW * 64), 0, s, e0, e1, 0, a);
+}
+
+template <typename T, int MT, int CT, int NW>
+static void launch_pd(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if constexpr (MT == 1) {
+    if (a.M <= 8) {
+      launch_xr<T, MT, CT, NW, 8>(a, pd, grid, s, e0, e1);
+      return;
+    }
+  }
+  launch_xr<T, MT, CT, NW, 16 * MT>(a, pd, grid, s, e0, e1);
+}
+
+template <typename T, int MT>
+static void launch_mt(const GemmArgs &a, int ct, int nw, int pd, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const int tiles = a.epi == EPI_SWIGLU ? a.N / 16 : a.N / (16 * ct);
+  dim3 grid(tiles, a.ksplit);
   if constexpr (MT == 4) {  // 8 waves would not fit their 64 staged X rows in LDS
-    if (ct == 1) hipExtLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
-    else hipExtLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
+    if (ct == 1) launch_pd<T, MT, 1, 4>(a, pd, grid, s, e0, e1);
+    else launch_pd<T, MT, 2, 4>(a, pd, grid, s, e0, e1);
   } else {
     if (ct == 1) {
-      if (nw == 8) hipExtLaunchKernelGGL((gemm_kernel<T, MT, 1, 8>), grid, dim3(512), 0, s, e0, e1, 0, a);
-      else hipExtLaunchKernelGGL((gemm_kernel<T, MT, 1, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
+      if (nw == 8) launch_pd<T, MT, 1, 8>(a, pd, grid, s, e0, e1);
+      else launch_pd<T, MT, 1, 4>(a, pd, grid, s, e0, e1);
     } else {
-      if (nw == 8) hipExtLaunchKernelGGL((gemm_kernel<T, MT, 2, 8>), grid, dim3(512), 0, s, e0, e1, 0, a);
-      else hipExtLaunchKernelGGL((gemm_kernel<T, MT, 2, 4>), grid, dim3(256), 0, s, e0, e1, 0, a);
+      if (nw == 8) launch_pd<T, MT, 2, 8>(a, pd, grid, s, e0, e1);
+      else launch_pd<T, MT, 2, 4>(a, pd, grid, s, e0, e1);
     }
   }
 }
 
-hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  // Tile width and waves per work-group, from the MI355X sweep at M = 8: 32-row tiles with 8 waves
-  // stream best except for mid-sized N with short K (q/k/v, injected k/v), where 16-row tiles with
-  // 4 waves spread better over the 256 CUs.  SwiGLU always pairs gate and up rows (two tiles).
-  static const int env_ct = env_int("DFLASH_GEMM_CT", 0), env_nw = env_int("DFLASH_GEMM_NW", 0);
-  int ct = 2, nw = 8;
-  if (a.epi != EPI_SWIGLU && a.N >= 6144 && a.N <= 12288 && a.K <= 8192) {
-    ct = 1;
-    nw = 4;
+struct TileCfg {
+  int ct, nw, pd;
+};
+
+// Tile width and waves per work-group, from MI355X sweeps at M = 8 (one launch per shape, weights
+// rotated through more memory than the memory-side cache holds): 32-row tiles with 8 waves stream best
+// for hidden-width outputs (o / down / fc projections) and SwiGLU pairs; 16-row tiles with 4 waves for
+// mid-sized outputs with short K (q/k/v, injected k/v); 32-row tiles with 4 waves for the LM head.
+static TileCfg pick_tiles(int epi, int N, int K) {
+  static const int env_ct = env_int("DFLASH_GEMM_CT", 0), env_nw = env_int("DFLASH_GEMM_NW", 0),
+                   env_pd = env_int("DFLASH_GEMM_PD", 0), env_pct = env_int("DFLASH_GEMM_PART_CT", 0),
+                   env_pnw = env_int("DFLASH_GEMM_PART_NW", 0);
+  TileCfg t{2, 8, 1};
+  if (epi != EPI_SWIGLU && N >= 6144 && N <= 12288 && K <= 8192) {
+    t.ct = 1;
+    t.nw = 4;
+  } else if (epi != EPI_SWIGLU && N >= 65536) {
+    t.nw = 4;
   }
-  if (env_ct && a.epi != EPI_SWIGLU) ct = env_ct;
-  if (env_nw) nw = env_nw;
-  if (a.epi != EPI_SWIGLU && a.N % (16 * ct)) ct = 1;
+  if (env_ct && epi != EPI_SWIGLU) t.ct = env_ct;
+  if (env_nw) t.nw = env_nw;
+  if (env_pct && epi == EPI_PARTIAL) t.ct = env_pct;
+  if (env_pnw && epi == EPI_PARTIAL) t.nw = env_pnw;
+  if (env_pd) t.pd = env_pd;
+  if (epi != EPI_SWIGLU && N % (16 * t.ct)) t.ct = 1;
+  if (t.ct != 1 && t.ct != 2) t.ct = 1;
+  if (t.nw != 4 && t.nw != 8) t.nw = 4;
+  if (t.pd < 1 || t.pd > 3) t.pd = 1;
+  return t;
+}
+
+int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems) {
+  // Splitting K did not pay at the 27B decode shapes on MI355X (more, shorter work-groups stream
+  // no faster), so ranges are used only on request (DFLASH_GEMM_SPLIT).
+  static const int env_split = env_int("DFLASH_GEMM_SPLIT", 1);
+  if (M > 16 || env_split <= 1) return 1;
+  const TileCfg t = pick_tiles(EPI_PARTIAL, N, K);
+  const int tiles = N / (16 * t.ct);
+  const int sk = 256 / (dtype == 0 ? 2 : 4);  // K elements per super-step
+  (void)tiles;
+  int split = 1;
+  while (split < env_split && K % (2 * split * sk) == 0 && (size_t)2 * split * M * N <= cap_elems) split *= 2;
+  return split;
+}
+
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (a.ksplit < 1 || a.K % a.ksplit || (a.ksplit > 1 && a.epi != EPI_PARTIAL)) return hipErrorInvalidValue;
+  const TileCfg t = pick_tiles(a.epi, a.N, a.K);
   const int MT = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
-  if (nw != 4 && nw != 8) nw = 4;
   if (dtype == 0) {
-    if (MT == 1) launch_mt<bf16, 1>(a, ct, nw, s, e0, e1);
-    else if (MT == 2) launch_mt<bf16, 2>(a, ct, nw, s, e0, e1);
-    else launch_mt<bf16, 4>(a, ct, nw, s, e0, e1);
+    if (MT == 1) launch_mt<bf16, 1>(a, t.ct, t.nw, t.pd, s, e0, e1);
+    else if (MT == 2) launch_mt<bf16, 2>(a, t.ct, t.nw, t.pd, s, e0, e1);
+    else launch_mt<bf16, 4>(a, t.ct, t.nw, t.pd, s, e0, e1);
   } else {
-    if (MT == 1) launch_mt<float, 1>(a, ct, nw, s, e0, e1);
-    else if (MT == 2) launch_mt<float, 2>(a, ct, nw, s, e0, e1);
-    else launch_mt<float, 4>(a, ct, nw, s, e0, e1);
+    if (MT == 1) launch_mt<float, 1>(a, t.ct, t.nw, t.pd, s, e0, e1);
+    else if (MT == 2) launch_mt<float, 2>(a, t.ct, t.nw, t.pd, s, e0, e1);
+    else launch_mt<float, 4>(a, t.ct, t.nw, t.pd, s, e0, e1);
   }
   return hipGetLastError();
 }
@@ -283,6 +362,10 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
   const int head = head_all - base;
   const float *src = a.src + (size_t)row * a.ld_src + (size_t)(live ? head_all : 0) * d;
   float v1 = src[i], v2 = src[i + half];
+  for (int sp = 1; sp < a.n_part; ++sp) {  // K-range partial sums, in order
+    v1 += src[(size_t)sp * a.part_stride + i];
+    v2 += src[(size_t)sp * a.part_stride + i + half];
+  }
   if (sg.role == ROLE_Q || sg.role == ROLE_K) {
     float ss = v1 * v1 + v2 * v2;
     for (int off = half / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);

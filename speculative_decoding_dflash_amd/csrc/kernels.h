@@ -8,7 +8,7 @@ namespace df {
 constexpr int kGemmMaxSeg = 16;
 constexpr int kGemmMaxRows = 64;  // rows per launch; longer inputs are chunked by the host
 
-enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_PARTIAL = 2, EPI_SWIGLU = 3 };
 enum SegRole { ROLE_PLAIN = 0, ROLE_Q = 1, ROLE_K = 2, ROLE_V = 3 };
 
 struct GemmSeg {
@@ -23,18 +23,19 @@ struct GemmArgs {
   int32_t nseg;         // segments concatenated along N (SWIGLU: 0 = gate, 1 = up)
   GemmSeg seg[kGemmMaxSeg];
   int32_t epi;
-  float *out_f32;       // EPI_STORE_F32
+  float *out_f32;       // EPI_STORE_F32; EPI_PARTIAL: K range s writes out_f32 + s * part_stride
   void *out_act;        // EPI_STORE_ACT, EPI_SWIGLU
   int32_t ld_out;
-  float *resid;         // EPI_RESID: resid += Y
-  int32_t ld_resid;
-  void *feat;           // EPI_RESID, optional: feat = act(resid after the add)
-  int32_t ld_feat;
+  int32_t ksplit;       // K ranges, one per grid row (> 1 only with EPI_PARTIAL)
+  int64_t part_stride;  // EPI_PARTIAL: elements between the K ranges' output slices
   int32_t row_off;      // global row of local row 0
 };
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// K ranges for an EPI_PARTIAL projection of M rows: enough work-groups to cover the CUs several times
+// over, each range a whole number of 256-byte super-steps, and split * M * N <= cap_elems.
+int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);
 
 // Per-head q/k RMSNorm + RoPE, then q to a dense buffer and k/v to the paged cache.
 struct PostSeg {
@@ -45,8 +46,10 @@ struct PostSeg {
   int32_t ld_dst;
 };
 struct QkvPostArgs {
-  const float *src;  // [rows][total_heads * head_dim] fp32 projections
+  const float *src;  // [n_part][rows][ld_src] fp32 partial projections, summed in order
   int32_t ld_src;
+  int32_t n_part;
+  int64_t part_stride;
   int32_t n_rows;
   int32_t nseg;
   PostSeg seg[kGemmMaxSeg];
@@ -81,10 +84,27 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
 hipError_t launch_embed(const void *embed, int dtype, const Rows &rows, int32_t n_rows, int32_t hidden, int32_t vocab,
                         float *x, int32_t *err, hipStream_t s);
 
-// Row i of out = act(rmsnorm(row (i / take) * stride + offset + i % take of in) * gain); in is fp32.
-hipError_t launch_rmsnorm(const float *in, int32_t ld_in, int32_t take, int32_t stride, int32_t offset, int32_t n_rows,
-                          const float *gain, float eps, int32_t hidden, void *out, int32_t ld_out, int dtype,
-                          hipStream_t s);
+// Residual update + RMSNorm over n_rows rows r:
+//   v = (x ? x[r] : 0) + sum_s part[s][r]   (s in order; part may be null)
+//   x[r] = v (if x), feat[r] = act(v) (if feat),
+//   and, when offset <= r % stride < offset + take, out[(r / stride) * take + r % stride - offset] =
+//   act(v / sqrt(mean(v^2) + eps) * gain).
+struct NormArgs {
+  float *x;
+  int32_t ld_x;
+  const float *part;
+  int32_t n_part, ld_part;
+  int64_t part_stride;
+  void *feat;
+  int32_t ld_feat;
+  const float *gain;
+  float eps;
+  int32_t hidden;
+  void *out;
+  int32_t ld_out;
+  int32_t n_rows, take, stride, offset;
+};
+hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

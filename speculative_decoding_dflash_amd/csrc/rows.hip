@@ -106,63 +106,84 @@ DF_DEVICE float block_sum(float v, float *red) {
   return t;
 }
 
-// out row i = act(in row (i / take) * stride + offset + i % take, normalised) * gain.
-// One work-group per row; every thread loads its float4 slices once (all loads issued before any is
-// used), keeps them in registers for the second pass, and the sum of squares is reduced in a fixed
-// order.
+// One work-group per row: the row value is the fp32 residual plus the projection's K-range partial
+// sums (added in range order), written back and optionally copied out as a feature tap; selected rows
+// are then RMS-normalised.  Every thread keeps its float4 slices in registers between the passes, and
+// the sum of squares is reduced in a fixed order.
 template <typename T, int VPT>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *in, int ld_in, int take, int stride, int offset,
-                                                      const float *gain, float eps, int hidden, T *out, int ld_out) {
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   __shared__ float red[4];
-  const int i = blockIdx.x;
-  const int src = (i / take) * stride + offset + (i % take);
-  const float4 *x = reinterpret_cast<const float4 *>(in + (size_t)src * ld_in);
-  const int nv = hidden / 4;
+  const int r = blockIdx.x;
+  const int j = r % a.stride - a.offset;
+  const bool sel = a.out != nullptr && j >= 0 && j < a.take;
+  if (!sel && !a.x && !a.feat) return;  // uniform over the work-group
+  const int nv = a.hidden / 4;
+  float4 *x = a.x ? reinterpret_cast<float4 *>(a.x + (size_t)r * a.ld_x) : nullptr;
+  const float4 *p = a.part ? reinterpret_cast<const float4 *>(a.part + (size_t)r * a.ld_part) : nullptr;
+  const size_t ps = (size_t)(a.part_stride / 4);
   float4 v[VPT];
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int q = threadIdx.x + 256 * j;
-    v[j] = q < nv ? x[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < VPT; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q < nv) {
+      if (x) t = x[q];
+      for (int sp = 0; sp < a.n_part; ++sp) {  // K-range partial sums, in order
+        const float4 u = p[sp * ps + q];
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
+      }
+      if (x && a.n_part) x[q] = t;
+      if (a.feat) {
+        T *f = (T *)a.feat + (size_t)r * a.ld_feat + 4 * q;
+        Elem<T>::store(f + 0, t.x);
+        Elem<T>::store(f + 1, t.y);
+        Elem<T>::store(f + 2, t.z);
+        Elem<T>::store(f + 3, t.w);
+      }
+    }
+    v[k] = t;
   }
+  if (!sel) return;
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  for (int k = 0; k < VPT; ++k) ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   ss = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)hidden + eps);
-  T *y = out + (size_t)i * ld_out;
-  const float4 *gv = reinterpret_cast<const float4 *>(gain);
+  const float rs = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
+  T *y = (T *)a.out + (size_t)((r / a.stride) * a.take + j) * a.ld_out;
+  const float4 *gv = reinterpret_cast<const float4 *>(a.gain);
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int q = threadIdx.x + 256 * j;
+  for (int k = 0; k < VPT; ++k) {
+    const int q = threadIdx.x + 256 * k;
     if (q < nv) {
       const float4 gg = gv[q];
-      Elem<T>::store(y + 4 * q + 0, v[j].x * r * gg.x);
-      Elem<T>::store(y + 4 * q + 1, v[j].y * r * gg.y);
-      Elem<T>::store(y + 4 * q + 2, v[j].z * r * gg.z);
-      Elem<T>::store(y + 4 * q + 3, v[j].w * r * gg.w);
+      Elem<T>::store(y + 4 * q + 0, v[k].x * rs * gg.x);
+      Elem<T>::store(y + 4 * q + 1, v[k].y * rs * gg.y);
+      Elem<T>::store(y + 4 * q + 2, v[k].z * rs * gg.z);
+      Elem<T>::store(y + 4 * q + 3, v[k].w * rs * gg.w);
     }
   }
 }
 
 template <typename T>
-static void launch_rms_t(const float *in, int ld_in, int take, int stride, int offset, int n_rows, const float *gain,
-                         float eps, int hidden, T *out, int ld_out, hipStream_t s) {
-  const int vpt = (hidden / 4 + 255) / 256;
-  dim3 g(n_rows), b(256);
-  if (vpt <= 1) hipLaunchKernelGGL((rmsnorm_kernel<T, 1>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
-  else if (vpt <= 2) hipLaunchKernelGGL((rmsnorm_kernel<T, 2>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
-  else if (vpt <= 4) hipLaunchKernelGGL((rmsnorm_kernel<T, 4>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
-  else if (vpt <= 8) hipLaunchKernelGGL((rmsnorm_kernel<T, 8>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
-  else hipLaunchKernelGGL((rmsnorm_kernel<T, 16>), g, b, 0, s, in, ld_in, take, stride, offset, gain, eps, hidden, out, ld_out);
+static void launch_norm_t(const NormArgs &a, hipStream_t s) {
+  const int vpt = (a.hidden / 4 + 255) / 256;
+  dim3 g(a.n_rows), b(256);
+  if (vpt <= 1) hipLaunchKernelGGL((norm_kernel<T, 1>), g, b, 0, s, a);
+  else if (vpt <= 2) hipLaunchKernelGGL((norm_kernel<T, 2>), g, b, 0, s, a);
+  else if (vpt <= 4) hipLaunchKernelGGL((norm_kernel<T, 4>), g, b, 0, s, a);
+  else if (vpt <= 8) hipLaunchKernelGGL((norm_kernel<T, 8>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((norm_kernel<T, 16>), g, b, 0, s, a);
 }
 
-hipError_t launch_rmsnorm(const float *in, int32_t ld_in, int32_t take, int32_t stride, int32_t offset, int32_t n_rows,
-                          const float *gain, float eps, int32_t hidden, void *out, int32_t ld_out, int dtype,
-                          hipStream_t s) {
-  if (n_rows == 0) return hipSuccess;
-  if (hidden % 4 || ld_in % 4 || hidden > 16384) return hipErrorInvalidValue;
-  if (dtype == 0) launch_rms_t<bf16>(in, ld_in, take, stride, offset, n_rows, gain, eps, hidden, (bf16 *)out, ld_out, s);
-  else launch_rms_t<float>(in, ld_in, take, stride, offset, n_rows, gain, eps, hidden, (float *)out, ld_out, s);
+hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s) {
+  if (a.n_rows == 0) return hipSuccess;
+  if (a.hidden % 4 || a.hidden > 16384 || a.stride < 1 || (a.x && a.ld_x % 4) || (a.part && (a.ld_part % 4 || a.part_stride % 4)))
+    return hipErrorInvalidValue;
+  if (dtype == 0) launch_norm_t<bf16>(a, s);
+  else launch_norm_t<float>(a, s);
   return hipGetLastError();
 }
 
