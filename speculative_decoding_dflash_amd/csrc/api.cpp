@@ -42,9 +42,10 @@ constexpr int kMaxKSplit = 8;
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, bt, rows[3][4], x, xn, qbuf, attn, ffn, part, att_o, att_ml, dlogits, cid, cp, cn, skey, sidx,
-      total;
+  size_t state, err, bt, rows[3][4], x, xn, ss, qbuf, attn, ffn, part, att_o, att_ml, dlogits, cid, cp, cn, skey,
+      sidx, total;
   size_t part_elems, att_rows;
+  int ss_ld;
 };
 
 Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
@@ -64,6 +65,9 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   for (int s = 0; s < 3; ++s)
     for (int k = 0; k < 4; ++k) L.rows[s][k] = take(sizeof(int32_t) * R);
   L.x = take(sizeof(float) * R * H);
+  // per-32-column sums of squares of the rows awaiting RMSNorm: [R][ss_ld]
+  L.ss_ld = (int)((H / 32 + 3) / 4 * 4);
+  L.ss = take(sizeof(float) * L.ss_ld * R);
   L.xn = take(es * R * H);
   L.qbuf = take(es * R * QD);
   L.attn = take(es * R * QD);
@@ -211,10 +215,21 @@ dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *
   return run_gemm(c, a, R, s);
 }
 
-// RMSNorm of all R rows of the hidden width into xn (no residual, no partials yet).
-NormArgs norm_base(dflash_ctx *c, int R, const void *gain) {
+// The RMSNorm that follows a residual update, deferred to the next projection: xn receives
+// act(x * gain) for the selected rows (compacted), L.ss the sums of squares, and the projection that
+// reads xn applies 1/rms to its outputs.
+struct NextNorm {
+  const void *gain;
+  int take, stride, offset;
+};
+NextNorm all_rows(const void *gain, int R) { return NextNorm{gain, R, R, 0}; }
+
+// Deferred RMSNorm of the fp32 rows x (after the embedding): one partial per row.
+dflash_status prep_norm(dflash_ctx *c, int R, const void *gain, hipStream_t s) {
   NormArgs n;
   memset(&n, 0, sizeof n);
+  n.x = c->wsp<float>(c->L.x);
+  n.ld_x = c->cfg.hidden;
   n.gain = (const float *)gain;
   n.eps = c->cfg.rms_eps;
   n.hidden = c->cfg.hidden;
@@ -224,15 +239,40 @@ NormArgs norm_base(dflash_ctx *c, int R, const void *gain) {
   n.take = R;
   n.stride = R;
   n.offset = 0;
-  return n;
+  n.ss_out = c->wsp<float>(c->L.ss);
+  n.ss_ld = c->L.ss_ld;
+  HIP_OK(launch_norm(n, c->dt(), s));
+  return DFLASH_OK;
 }
 
-// Adds the partial slices of the last projection (N = hidden) to the norm's row values.
-void norm_parts(dflash_ctx *c, NormArgs &n, int n_part) {
-  n.part = c->wsp<float>(c->L.part);
-  n.n_part = n_part;
-  n.ld_part = c->cfg.hidden;
-  n.part_stride = (int64_t)n.n_rows * c->cfg.hidden;
+// A projection whose X rows are xn awaiting their 1/rms factor (ss_n partial sums per row in L.ss).
+void with_norm(dflash_ctx *c, GemmArgs &a, int ss_n) {
+  a.ss_in = c->wsp<float>(c->L.ss);
+  a.ss_n = ss_n;
+  a.ss_ld = c->L.ss_ld;
+  a.norm_dim = c->cfg.hidden;
+  a.eps = c->cfg.rms_eps;
+}
+
+// A hidden-width projection whose output is added to the residual (resid may be null: the output is
+// the new row) and then RMS-normalised with the deferred scheme; returns ss_n for the consumer.
+dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, void *feat, int ld_feat,
+                             const NextNorm &nx, hipStream_t s, int *ss_n) {
+  a.epi = EPI_RESID_NORM;
+  a.resid = resid;
+  a.ld_resid = c->cfg.hidden;
+  a.feat = feat;
+  a.ld_feat = ld_feat;
+  a.gain = (const float *)nx.gain;
+  a.xg = c->wsp<void>(c->L.xn);
+  a.ld_xg = c->cfg.hidden;
+  a.ss_out = c->wsp<float>(c->L.ss);
+  a.ss_out_ld = c->L.ss_ld;
+  a.sel_take = nx.take;
+  a.sel_stride = nx.stride;
+  a.sel_offset = nx.offset;
+  *ss_n = a.N / 32;
+  return run_gemm(c, a, R, s);
 }
 
 QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
@@ -294,24 +334,26 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   return DFLASH_OK;
 }
 
-// One decoder layer over R rows.  On entry xn holds the attention-normalised rows; the residual x
-// (fp32) is updated in place.  `next` is the RMSNorm that follows the layer (the next layer's attention
-// norm, or the final norm over the rows that need logits); feat: optional tap of the layer's output.
+// One decoder layer over R rows.  On entry xn holds act(x * attn_norm) and L.ss its ss_n partial sums
+// of squares (deferred RMSNorm); the residual x (fp32) is updated in place.  `next` is the RMSNorm that
+// follows the layer (the next layer's attention norm, or the final norm over the rows that need
+// logits); feat: optional tap of the layer's output.  Returns the ss_n of the deferred next norm.
 dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows, int n_seq,
-                        int q_len, int attn_mode, int ctx_bound, void *feat, int ld_feat, NormArgs next,
-                        hipStream_t s) {
+                        int q_len, int attn_mode, int ctx_bound, void *feat, int ld_feat, const NextNorm &next,
+                        int *ss_n, hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   const int R = n_seq * q_len, H = m.hidden, QD = m.q_heads * m.head_dim, KD = m.kv_heads * m.head_dim, F = m.ffn;
   float *x = c->wsp<float>(c->L.x);
   void *xn = c->wsp<void>(c->L.xn);
   dflash_status st;
-  int np = 1;
   {
     GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_PARTIAL);
     a.nseg = 3;
     a.seg[0] = GemmSeg{w.wq, QD};
     a.seg[1] = GemmSeg{w.wk, KD};
     a.seg[2] = GemmSeg{w.wv, KD};
+    with_norm(c, a, *ss_n);
+    int np = 1;
     if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
     QkvPostArgs p = post_base(c, rows, R);
     p.ld_src = QD + 2 * KD;
@@ -326,15 +368,10 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   }
   if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, s)) != DFLASH_OK) return st;
   {
-    GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_PARTIAL);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID_NORM);
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.wo, H};
-    if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
-    NormArgs n = norm_base(c, R, w.ffn_norm);
-    n.x = x;
-    n.ld_x = H;
-    norm_parts(c, n, np);
-    HIP_OK(launch_norm(n, c->dt(), s));
+    if ((st = run_resid_norm(c, a, R, x, nullptr, 0, all_rows(w.ffn_norm, R), s, ss_n)) != DFLASH_OK) return st;
   }
   {
     GemmArgs a = gemm_base(xn, H, R, F, H, EPI_SWIGLU);
@@ -343,19 +380,14 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     a.seg[1] = GemmSeg{w.w_up, F};
     a.out_act = c->wsp<void>(c->L.ffn);
     a.ld_out = F;
+    with_norm(c, a, *ss_n);
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   {
-    GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_PARTIAL);
+    GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID_NORM);
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.w_down, H};
-    if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
-    next.x = x;
-    next.ld_x = H;
-    next.feat = feat;
-    next.ld_feat = ld_feat;
-    norm_parts(c, next, np);
-    HIP_OK(launch_norm(next, c->dt(), s));
+    if ((st = run_resid_norm(c, a, R, x, feat, ld_feat, next, s, ss_n)) != DFLASH_OK) return st;
   }
   return DFLASH_OK;
 }
@@ -538,12 +570,8 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
   HIP_OK(launch_embed(c->embed, c->dt(), rows, R, H, m.vocab, c->wsp<float>(c->L.x), c->err(), s));
-  {
-    NormArgs n = norm_base(c, R, c->tl[0].attn_norm);
-    n.x = c->wsp<float>(c->L.x);
-    n.ld_x = H;
-    HIP_OK(launch_norm(n, c->dt(), s));
-  }
+  if ((st = prep_norm(c, R, c->tl[0].attn_norm, s)) != DFLASH_OK) return st;
+  int ss_n = 1;
   const int ctx_bound = c->max_ctx(slots, batch);
   const int ld_feat = c->dcfg.n_taps * H;
   const int nl = n_logit_rows;
@@ -551,18 +579,16 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
     void *feat = nullptr;
     for (int t = 0; t < c->dcfg.n_taps; ++t)
       if (c->dcfg.taps[t] == l && d_feats) feat = (char *)d_feats + (size_t)t * H * c->es();
-    NormArgs next = norm_base(c, R, l + 1 < m.layers ? c->tl[l + 1].attn_norm : c->final_norm);
-    if (l + 1 == m.layers) {  // final norm: the last nl rows of every sequence, packed
-      next.take = nl;
-      next.stride = q_len;
-      next.offset = q_len - nl;
-    }
-    st = run_layer(c, c->tl[l], c->tlayer(l), rows, batch, q_len, 0, ctx_bound, feat, ld_feat, next, s);
+    // after the last layer: the final norm over the last nl rows of every sequence, packed
+    const NextNorm next = l + 1 < m.layers ? all_rows(c->tl[l + 1].attn_norm, R)
+                                           : NextNorm{c->final_norm, nl, q_len, q_len - nl};
+    st = run_layer(c, c->tl[l], c->tlayer(l), rows, batch, q_len, 0, ctx_bound, feat, ld_feat, next, &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
+  with_norm(c, a, ss_n);
   a.out_f32 = d_logits;
   a.ld_out = m.vocab;
   if ((st = run_gemm(c, a, batch * nl, s)) != DFLASH_OK) return st;
@@ -675,15 +701,13 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   p.vocab = m.vocab;
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
+  int ss_n = 1;
   {
-    GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_PARTIAL);
+    GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_RESID_NORM);
     a.nseg = 1;
     a.seg[0] = GemmSeg{c->fc, H};
-    int np = 1;
-    if ((st = run_partial(c, a, Ri, s, &np)) != DFLASH_OK) return st;
-    NormArgs n = norm_base(c, Ri, c->hidden_norm);
-    norm_parts(c, n, np);
-    HIP_OK(launch_norm(n, c->dt(), s));
+    if ((st = run_resid_norm(c, a, Ri, nullptr, nullptr, 0, all_rows(c->hidden_norm, Ri), s, &ss_n)) != DFLASH_OK)
+      return st;
   }
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_PARTIAL);
@@ -698,6 +722,7 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
       p.seg[2 * j + 1] = PostSeg{m.kv_heads, ROLE_V, nullptr, c->dlayer(j), 0};
     }
     p.total_heads = dc.layers * 2 * m.kv_heads;
+    with_norm(c, a, ss_n);
     int np = 1;
     if ((st = run_partial(c, a, Ri, s, &np)) != DFLASH_OK) return st;
     p.n_part = np;
@@ -713,28 +738,21 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   HIP_OK(launch_prep(p, s));
   const int R = batch * B;
   HIP_OK(launch_embed(c->embed, c->dt(), rd, R, H, m.vocab, c->wsp<float>(c->L.x), c->err(), s));
-  {
-    NormArgs n = norm_base(c, R, c->dl[0].attn_norm);
-    n.x = c->wsp<float>(c->L.x);
-    n.ld_x = H;
-    HIP_OK(launch_norm(n, c->dt(), s));
-  }
+  if ((st = prep_norm(c, R, c->dl[0].attn_norm, s)) != DFLASH_OK) return st;
+  ss_n = 1;
   const int ctx_bound = c->max_ctx(slots, batch);
   const int nd = B - 1;
   for (int j = 0; j < dc.layers; ++j) {
-    NormArgs next = norm_base(c, R, j + 1 < dc.layers ? c->dl[j + 1].attn_norm : c->d_final_norm);
-    if (j + 1 == dc.layers) {  // final norm: the B - 1 mask positions of every block, packed
-      next.take = nd;
-      next.stride = B;
-      next.offset = 1;
-    }
-    st = run_layer(c, c->dl[j], c->dlayer(j), rd, batch, B, 1, ctx_bound, nullptr, 0, next, s);
+    // after the last layer: the final norm over the B - 1 mask positions of every block, packed
+    const NextNorm next = j + 1 < dc.layers ? all_rows(c->dl[j + 1].attn_norm, R) : NextNorm{c->d_final_norm, nd, B, 1};
+    st = run_layer(c, c->dl[j], c->dlayer(j), rd, batch, B, 1, ctx_bound, nullptr, 0, next, &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
+  with_norm(c, a, ss_n);
   a.out_f32 = logits;
   a.ld_out = m.vocab;
   if ((st = run_gemm(c, a, batch * nd, s)) != DFLASH_OK) return st;

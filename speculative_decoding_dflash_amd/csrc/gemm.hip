@@ -66,6 +66,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   constexpr int kTileB = NW * (COLS + XR) * ROWB, kRedB = NW * kEnt * 4;
   // wave-private staging of weights and X during the main loop; the cross-wave reduction reuses it
   __shared__ __attribute__((aligned(16))) unsigned char smem[kTileB > kRedB ? kTileB : kRedB];
+  __shared__ float s_ssp[4 * NT], s_rstd[16 * MT];
   float *lds = reinterpret_cast<float *>(smem);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -114,6 +115,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   unsigned char *wt = smem + wave * (COLS + XR) * ROWB;
   unsigned char *xt = wt + COLS * ROWB;
   const int nsup = Kc / SK;  // streamed super-steps; wave w takes w, w + NW, ...
+  // Deferred RMSNorm of the X rows: the partial sums of squares of row m sit at ss_in[(row_off + m) *
+  // ss_ld + p] (p < ss_n, ss_ld a multiple of 4).  Thread t loads the 4-vectors t + k * NT, k < kSS4
+  // (unconditionally; surplus loads read the first vector again), before the weight stream starts.
+  constexpr int kSS4 = 4;
+  const int ss_q = a.ss_ld / 4;  // 4-vectors per row
+  const bool ss_fast = a.ss_in && a.M * ss_q <= kSS4 * NT;
+  float4 ssv[kSS4];
+  if (ss_fast) {
+    const float4 *base = reinterpret_cast<const float4 *>(a.ss_in + (size_t)a.row_off * a.ss_ld);
+#pragma unroll
+    for (int k = 0; k < kSS4; ++k) {
+      const int idx = tid + k * NT;
+      ssv[k] = base[idx < a.M * ss_q ? idx : 0];
+    }
+  }
+
   // PD register buffers per wave: PD super-steps are in flight while one is consumed.  Loads past the
   // wave's last super-step are redirected to X's first 256 bytes (cache-resident, never consumed),
   // which keeps them unconditional.
@@ -129,6 +146,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < NXQ; ++q) bufx[p][q] = ld16(ok ? xrow[q] + (size_t)s0 * SK : dummy);
       __builtin_amdgcn_sched_barrier(0);  // keep buffer p's loads ahead of buffer p + 1's
+    }
+  }
+  if (ss_fast) {
+#pragma unroll
+    for (int k = 0; k < kSS4; ++k) {
+      const int idx = tid + k * NT;
+      if (idx < a.M * ss_q) {
+        const int p0 = (idx % ss_q) * 4;  // partials p0 .. p0 + 3 of row idx / ss_q
+        const float4 v = ssv[k];
+        s_ssp[idx] = (p0 < a.ss_n ? v.x : 0.f) + (p0 + 1 < a.ss_n ? v.y : 0.f) + (p0 + 2 < a.ss_n ? v.z : 0.f) +
+                     (p0 + 3 < a.ss_n ? v.w : 0.f);  // read after the reduction barrier below
+      }
     }
   }
   for (int sup = wave; sup < nsup; sup += PD * NW) {
@@ -193,14 +222,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     for (int w = 1; w < NW; ++w) v += lds[w * kEnt + e];
     lds[e] = v;  // entry e is read and written by this thread only
   }
+  if (a.ss_in && tid < a.M) {
+    float tot = 0.f;
+    if (ss_fast) {
+      const int nq = (a.ss_n + 3) / 4;
+      for (int i = 0; i < nq; ++i) tot += s_ssp[tid * ss_q + i];
+    } else {
+      for (int pp = 0; pp < a.ss_n; pp += 4) {  // same association as the fast path
+        const float *q = a.ss_in + (size_t)(a.row_off + tid) * a.ss_ld + pp;
+        tot += (q[0] + (pp + 1 < a.ss_n ? q[1] : 0.f)) + (pp + 2 < a.ss_n ? q[2] : 0.f) + (pp + 3 < a.ss_n ? q[3] : 0.f);
+      }
+    }
+    s_rstd[tid] = 1.0f / sqrtf(tot / (float)a.norm_dim + a.eps);
+  }
   __syncthreads();
 
   const int M = a.M;
+  const bool rs = a.ss_in != nullptr;
   switch (a.epi) {
     case EPI_STORE_F32:
       for (int e = tid; e < M * COLS; e += NT) {
         const int m = e / COLS, j = e % COLS;
-        a.out_f32[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j];
+        a.out_f32[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
       }
       break;
     case EPI_STORE_ACT:
@@ -213,15 +256,44 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       float *o = a.out_f32 + (size_t)split * a.part_stride;
       for (int e = tid; e < M * COLS; e += NT) {
         const int m = e / COLS, j = e % COLS;
-        o[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j];
+        o[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
       }
       break;
     }
     case EPI_SWIGLU:
       for (int e = tid; e < M * 16; e += NT) {
         const int m = e / 16, j = e % 16;
-        const float gt = lds[m * COLS + j], up = lds[m * COLS + 16 + j];
+        const float r = rs ? s_rstd[m] : 1.f;
+        const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + 16 + j] * r;
         Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + 16 * c + j, silu(gt) * up);
+      }
+      break;
+    case EPI_RESID_NORM:
+      if constexpr (COLS == 32) {
+        for (int e = tid; e < M * COLS; e += NT) {
+          const int m = e / COLS, j = e % COLS;
+          const int r = a.row_off + m, n = COLS * c + j;
+          float v = lds[m * COLS + j];
+          if (a.resid) {
+            const size_t idx = (size_t)r * a.ld_resid + n;
+            v += a.resid[idx];
+            a.resid[idx] = v;
+          }
+          if (a.feat) Elem<T>::store((T *)a.feat + (size_t)r * a.ld_feat + n, v);
+          const int jj = r % a.sel_stride - a.sel_offset;
+          if (jj >= 0 && jj < a.sel_take)
+            Elem<T>::store((T *)a.xg + (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
+          lds[m * COLS + j] = v * v;  // entry owned by this thread
+        }
+        __syncthreads();
+        if (tid < M) {
+          const int r = a.row_off + tid, jj = r % a.sel_stride - a.sel_offset;
+          if (jj >= 0 && jj < a.sel_take) {
+            float t = 0.f;
+            for (int j = 0; j < COLS; ++j) t += lds[tid * COLS + j];
+            a.ss_out[(size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ss_out_ld + c] = t;
+          }
+        }
       }
       break;
   }
@@ -304,6 +376,7 @@ static TileCfg pick_tiles(int epi, int N, int K) {
   if (env_pnw && epi == EPI_PARTIAL) t.nw = env_pnw;
   if (env_pd) t.pd = env_pd;
   if (epi != EPI_SWIGLU && N % (16 * t.ct)) t.ct = 1;
+  if (epi == EPI_RESID_NORM) t.ct = 2;  // its sums of squares are per 32 columns
   if (t.ct != 1 && t.ct != 2) t.ct = 1;
   if (t.nw != 4 && t.nw != 8) t.nw = 4;
   if (t.pd < 1 || t.pd > 3) t.pd = 1;
@@ -326,6 +399,10 @@ int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems) {
 
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.ksplit < 1 || a.K % a.ksplit || (a.ksplit > 1 && a.epi != EPI_PARTIAL)) return hipErrorInvalidValue;
+  if (a.epi == EPI_RESID_NORM && (a.N % 32 || a.sel_stride < 1 || !a.gain || !a.xg || !a.ss_out))
+    return hipErrorInvalidValue;
+  if (a.ss_in && (a.ss_n < 1 || a.norm_dim < 1 || a.ss_ld % 4 || a.ss_n > a.ss_ld)) return hipErrorInvalidValue;
+  if (a.epi == EPI_RESID_NORM && a.N / 32 > a.ss_out_ld) return hipErrorInvalidValue;
   const TileCfg t = pick_tiles(a.epi, a.N, a.K);
   const int MT = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
   if (dtype == 0) {

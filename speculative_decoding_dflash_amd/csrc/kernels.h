@@ -8,7 +8,7 @@ namespace df {
 constexpr int kGemmMaxSeg = 16;
 constexpr int kGemmMaxRows = 64;  // rows per launch; longer inputs are chunked by the host
 
-enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_PARTIAL = 2, EPI_SWIGLU = 3 };
+enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_PARTIAL = 2, EPI_SWIGLU = 3, EPI_RESID_NORM = 4 };
 enum SegRole { ROLE_PLAIN = 0, ROLE_Q = 1, ROLE_K = 2, ROLE_V = 3 };
 
 struct GemmSeg {
@@ -29,6 +29,27 @@ struct GemmArgs {
   int32_t ksplit;       // K ranges, one per grid row (> 1 only with EPI_PARTIAL)
   int64_t part_stride;  // EPI_PARTIAL: elements between the K ranges' output slices
   int32_t row_off;      // global row of local row 0
+  // Optional RMSNorm of the X rows, applied to Y (EPI_STORE_F32, EPI_PARTIAL, EPI_SWIGLU): X holds
+  // act(x * gain) and Y[m] is scaled by rstd[m] = 1 / sqrt(sum_p ss_in[(row_off + m) * ss_ld + p] /
+  // norm_dim + eps), the ss_n partial sums of squares added in order (ss_ld a multiple of 4).
+  const float *ss_in;
+  int32_t ss_n, ss_ld, norm_dim;
+  float eps;
+  // EPI_RESID_NORM (32-column tiles): v = (resid ? resid[m][n] : 0) + Y[m][n]; resid[m][n] = v;
+  // feat[m][n] = act(v) (optional); rows selected by (sel_take, sel_stride, sel_offset), compacted to
+  // o = (r / sel_stride) * sel_take + r % sel_stride - sel_offset, also get xg[o][n] = act(v * gain[n])
+  // and ss_out[o * ss_out_ld + tile] = the sum of v^2 over the tile's 32 columns (the next projection's
+  // ss_in, ss_n = N / 32).
+  float *resid;
+  int32_t ld_resid;
+  void *feat;
+  int32_t ld_feat;
+  const float *gain;
+  void *xg;
+  int32_t ld_xg;
+  float *ss_out;
+  int32_t ss_out_ld;
+  int32_t sel_take, sel_stride, sel_offset;
 };
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
@@ -103,6 +124,10 @@ struct NormArgs {
   void *out;
   int32_t ld_out;
   int32_t n_rows, take, stride, offset;
+  // Deferred normalisation: when set, selected rows get out = act(v * gain) (no 1/rms factor) and
+  // ss_out[o * ss_ld] = sum of v^2 (a single partial for a projection's ss_in, ss_n = 1).
+  float *ss_out;
+  int32_t ss_ld;
 };
 hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s);
 

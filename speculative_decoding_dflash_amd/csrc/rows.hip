@@ -151,8 +151,13 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
 #pragma unroll
   for (int k = 0; k < VPT; ++k) ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   ss = block_sum(ss, red);
-  const float rs = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
-  T *y = (T *)a.out + (size_t)((r / a.stride) * a.take + j) * a.ld_out;
+  const int o = (r / a.stride) * a.take + j;
+  float rs = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
+  if (a.ss_out) {  // deferred: the consumer applies 1/rms
+    if (threadIdx.x == 0) a.ss_out[(size_t)o * a.ss_ld] = ss;
+    rs = 1.f;
+  }
+  T *y = (T *)a.out + (size_t)o * a.ld_out;
   const float4 *gv = reinterpret_cast<const float4 *>(a.gain);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
