@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   const int k0 = split * Kc;
 
   const T *wbase[CT];  // row 16*ct of the tile
-  if (swiglu) {
+  if (swiglu) {  // CT == 2: a gate tile and an up tile of 16 rows each (CT == 1: see below)
     wbase[0] = (const T *)a.seg[0].w + (size_t)(16 * c) * a.K;
     wbase[CT - 1] = (const T *)a.seg[1].w + (size_t)(16 * c) * a.K;
   } else {
@@ -96,6 +96,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   const T *qrow[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) qrow[q] = wbase[q / 4] + (size_t)(4 * (q % 4) + g) * a.K + k0 + r16 * F::kEPL;
+  if constexpr (CT == 1) {
+    if (swiglu) {  // one 16-column tile: gate rows 8c .. 8c + 7 (quads 0, 1), up rows 8c .. 8c + 7 (quads 2, 3)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        qrow[q] = (const T *)a.seg[q / 2].w + (size_t)(8 * c + 4 * (q % 2) + g) * a.K + k0 + r16 * F::kEPL;
+    }
+  }
   // X rows >= M load row 0 (never read back: the operand read below masks them), so that every
   // load in the streaming loop is unconditional and the compiler can count outstanding loads exactly.
   const T *xrow[NXQ];
@@ -260,14 +267,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       }
       break;
     }
-    case EPI_SWIGLU:
-      for (int e = tid; e < M * 16; e += NT) {
-        const int m = e / 16, j = e % 16;
+    case EPI_SWIGLU: {
+      constexpr int HC = COLS / 2;  // output columns of the tile: gate in [0, HC), up in [HC, COLS)
+      for (int e = tid; e < M * HC; e += NT) {
+        const int m = e / HC, j = e % HC;
         const float r = rs ? s_rstd[m] : 1.f;
-        const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + 16 + j] * r;
-        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + 16 * c + j, silu(gt) * up);
+        const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + HC + j] * r;
+        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
       }
       break;
+    }
     case EPI_RESID_NORM:
       if constexpr (COLS == 32) {
         for (int e = tid; e < M * COLS; e += NT) {
@@ -335,7 +344,7 @@ static void launch_pd(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEv
 
 template <typename T, int MT>
 static void launch_mt(const GemmArgs &a, int ct, int nw, int pd, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const int tiles = a.epi == EPI_SWIGLU ? a.N / 16 : a.N / (16 * ct);
+  const int tiles = a.epi == EPI_SWIGLU ? a.N / (8 * ct) : a.N / (16 * ct);
   dim3 grid(tiles, a.ksplit);
   if constexpr (MT == 4) {  // 8 waves would not fit their 64 staged X rows in LDS
     if (ct == 1) launch_pd<T, MT, 1, 4>(a, pd, grid, s, e0, e1);
@@ -370,6 +379,12 @@ static TileCfg pick_tiles(int epi, int N, int K) {
   } else if (epi != EPI_SWIGLU && N >= 65536) {
     t.nw = 4;
   }
+  if (epi == EPI_SWIGLU) {  // 8 gate + 8 up rows per 16-column tile
+    t.ct = 1;
+    t.nw = 8;
+  }
+  static const int env_sct = env_int("DFLASH_GEMM_SWIGLU_CT", 0);
+  if (env_sct && epi == EPI_SWIGLU) t.ct = env_sct;
   if (env_ct && epi != EPI_SWIGLU) t.ct = env_ct;
   if (env_nw) t.nw = env_nw;
   if (env_pct && epi == EPI_PARTIAL) t.ct = env_pct;
