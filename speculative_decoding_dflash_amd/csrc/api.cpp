@@ -42,8 +42,8 @@ constexpr int kMaxKSplit = 8;
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, bt, rows[3][4], x, xn, ss, qbuf, attn, ffn, part, att_o, att_ml, dlogits, cid, cp, cn, skey,
-      sidx, total;
+  size_t state, err, cnt, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, att_o, att_ml, dlogits, cid, cp, cn,
+      skey, sidx, total;
   size_t part_elems, att_rows;
   int ss_ld;
 };
@@ -61,10 +61,13 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   const size_t B = d->block_size;
   L.state = take(sizeof(SlotState) * cap->max_slots);
   L.err = take(sizeof(int32_t) * ERR_COUNT);
+  L.cnt = take(sizeof(int32_t) * cap->max_slots * c->kv_heads);  // attention merge counters (zeroed)
   L.bt = take(sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq);
   for (int s = 0; s < 3; ++s)
     for (int k = 0; k < 4; ++k) L.rows[s][k] = take(sizeof(int32_t) * R);
   L.x = take(sizeof(float) * R * H);
+  // rotary (cos, sin) for every position a sequence can reach
+  L.rope = take(sizeof(float) * 2 * (size_t)cap->max_pages_per_seq * cap->page_tokens * (c->head_dim / 2));
   // per-32-column sums of squares of the rows awaiting RMSNorm: [R][ss_ld]
   L.ss_ld = (int)((H / 32 + 3) / 4 * 4);
   L.ss = take(sizeof(float) * L.ss_ld * R);
@@ -158,6 +161,7 @@ struct dflash_ctx {
     return r;
   }
   int dt() const { return cfg.dtype == DFLASH_BF16 ? 0 : 1; }
+  int rope_rows() const { return cap.max_pages_per_seq * cap.page_tokens; }
   int es() const { return esize(&cfg); }
   void *tlayer(int l) const { return tkv + (size_t)l * layer_elems * es(); }
   void *dlayer(int l) const { return dkv + (size_t)l * layer_elems * es(); }
@@ -285,14 +289,17 @@ QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
   p.block_table = c->bt();
   p.bt_stride = c->cap.max_pages_per_seq;
   p.kv = c->kvl;
-  p.theta = c->cfg.rope_theta;
+  p.rope = c->wsp<float2>(c->L.rope);
+  p.rope_rows = c->rope_rows();
   p.eps = c->cfg.rms_eps;
   p.err = c->err();
   return p;
 }
 
+// raw_qkv (optional, calls with one query tile per sequence): the layer's raw fp32 q/k/v rows, which the
+// attention kernel normalises, rotates and writes to the pool itself (no separate post kernel).
 dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_len, int mode, void *kv, int ctx_bound,
-                            hipStream_t s) {
+                            const dflash_layer_weights *raw_w, hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   AttnArgs a;
   memset(&a, 0, sizeof a);
@@ -323,6 +330,10 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   static const int env_pps = getenv("DFLASH_ATTN_PPS") ? atoi(getenv("DFLASH_ATTN_PPS")) : 0;
   if (env_pps > 0 && (pages + env_pps - 1) / env_pps <= kAttnSplitMax && (size_t)n_seq * q_len <= c->L.att_rows)
     pps = env_pps;
+  // the last-arriver merge keeps m and l of every (query vector, split) in the head_dim-sized LDS tile
+  const char *mz = getenv("DFLASH_ATTN_MERGE");
+  const bool arrive = raw_w && mz && atoi(mz) == 1;
+  if (arrive && (pages + pps - 1) / pps > m.head_dim / 2) pps = (pages + m.head_dim / 2 - 1) / (m.head_dim / 2);
   a.n_splits = (pages + pps - 1) / pps;
   a.split_tokens = pps * pt;
   a.part_o = c->wsp<float>(c->L.att_o);
@@ -330,6 +341,16 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.out = c->wsp<void>(c->L.attn);
   a.ldo = m.q_heads * m.head_dim;
   a.err = c->err();
+  if (raw_w) {
+    a.raw = c->wsp<float>(c->L.part);
+    a.ld_raw = (m.q_heads + 2 * m.kv_heads) * m.head_dim;
+    a.q_gain = (const float *)raw_w->q_norm;
+    a.k_gain = (const float *)raw_w->k_norm;
+    a.eps = m.rms_eps;
+    a.rope = c->wsp<float2>(c->L.rope);
+    a.rope_rows = c->rope_rows();
+    a.counters = arrive ? c->wsp<int32_t>(c->L.cnt) : nullptr;
+  }
   HIP_OK(launch_attention(a, c->dt(), s));
   return DFLASH_OK;
 }
@@ -346,6 +367,7 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   float *x = c->wsp<float>(c->L.x);
   void *xn = c->wsp<void>(c->L.xn);
   dflash_status st;
+  bool fused = false;
   {
     GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_PARTIAL);
     a.nseg = 3;
@@ -355,18 +377,28 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     with_norm(c, a, *ss_n);
     int np = 1;
     if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
-    QkvPostArgs p = post_base(c, rows, R);
-    p.ld_src = QD + 2 * KD;
-    p.n_part = np;
-    p.part_stride = (int64_t)R * (QD + 2 * KD);
-    p.nseg = 3;
-    p.seg[0] = PostSeg{m.q_heads, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
-    p.seg[1] = PostSeg{m.kv_heads, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
-    p.seg[2] = PostSeg{m.kv_heads, ROLE_V, nullptr, kv_layer, 0};
-    p.total_heads = m.q_heads + 2 * m.kv_heads;
-    HIP_OK(launch_qkv_post(p, c->dt(), s));
+    // One query tile per sequence: the attention kernel can post-process q / k / v itself
+    // (DFLASH_ATTN_FUSED=1).  Off by default: on MI355X at the 27B decode shape the fused prologue
+    // (raw q loads, RMSNorm, rotary table reads) costs the attention kernel more than the separate
+    // post-processing launch it saves.
+    const char *fz = getenv("DFLASH_ATTN_FUSED");
+    fused = fz && atoi(fz) == 1 && np == 1 && q_len * (m.q_heads / m.kv_heads) <= 64;
+    if (!fused) {
+      QkvPostArgs p = post_base(c, rows, R);
+      p.ld_src = QD + 2 * KD;
+      p.n_part = np;
+      p.part_stride = (int64_t)R * (QD + 2 * KD);
+      p.nseg = 3;
+      p.seg[0] = PostSeg{m.q_heads, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
+      p.seg[1] = PostSeg{m.kv_heads, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
+      p.seg[2] = PostSeg{m.kv_heads, ROLE_V, nullptr, kv_layer, 0};
+      p.total_heads = m.q_heads + 2 * m.kv_heads;
+      HIP_OK(launch_qkv_post(p, c->dt(), s));
+    }
   }
-  if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, s)) != DFLASH_OK) return st;
+  if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, fused ? &w : nullptr, s)) !=
+      DFLASH_OK)
+    return st;
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID_NORM);
     a.nseg = 1;
@@ -478,6 +510,8 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
   if (e == hipSuccess) e = hipMemsetAsync(c->ws + c->L.state, 0, c->L.rows[0][0] - c->L.state, stream);
   if (e == hipSuccess)
     e = hipMemsetAsync(c->ws + c->L.bt, 0xff, sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq, stream);
+  if (e == hipSuccess)
+    e = launch_rope_table(c->wsp<float2>(c->L.rope), cfg->rope_theta, cfg->head_dim, c->rope_rows(), stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     delete c;

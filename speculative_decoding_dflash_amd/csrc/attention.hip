@@ -26,7 +26,14 @@ template <typename T, int D> struct AttnFrag;
 // V fragments: D/16 vectors per lane (A operand of O^T += V^T P^T, row = dim, 4 keys per lane).
 template <int D> struct AttnFrag<bf16, D> {
   static constexpr int kSteps = D / 32;  // QK^T steps of 32 dims (8 per lane)
+  static constexpr int kEPL = 8;         // dims per lane per step: ks * 32 + (lane / 16) * 8 + e
   using VF = u32x2;                      // 4 bf16 keys of one dim
+  static DF_DEVICE u32x4 pack(const float *v) {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+    return r;
+  }
   static DF_DEVICE u32x4 load_q(const bf16 *qrow, int ks, int g) {
     return *reinterpret_cast<const u32x4 *>(qrow + ks * 32 + g * 8);
   }
@@ -59,7 +66,14 @@ template <int D> struct AttnFrag<bf16, D> {
 
 template <int D> struct AttnFrag<float, D> {
   static constexpr int kSteps = D / 16;  // 16 dims per step (4 per lane), as 4 K=4 slices
+  static constexpr int kEPL = 4;         // dims per lane per step: ks * 16 + (lane / 16) * 4 + e
   using VF = u32x4;                      // 4 fp32 keys of one dim
+  static DF_DEVICE u32x4 pack(const float *v) {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = __builtin_bit_cast(uint32_t, v[j]);
+    return r;
+  }
   static DF_DEVICE u32x4 load_q(const float *qrow, int ks, int g) {
     return *reinterpret_cast<const u32x4 *>(qrow + ks * 16 + g * 4);
   }
@@ -115,6 +129,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   int qpos[NQT];
   bool qok[NQT];
   u32x4 q[NQT][F::kSteps];
+  const bool fused = a.raw != nullptr;
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int qv = t * 16 + l16;
@@ -122,9 +137,60 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int row = rbase + (qok[t] ? qv / G : 0);
     const int head = kh * G + (qok[t] ? qv % G : 0);
     qpos[t] = a.rows.pos[row];
-    const T *qrow = (const T *)a.q + (size_t)row * a.ldq + head * D;
+    if (!fused) {
+      const T *qrow = (const T *)a.q + (size_t)row * a.ldq + head * D;
 #pragma unroll
-    for (int ks = 0; ks < F::kSteps; ++ks) q[t][ks] = F::load_q(qrow, ks, g);
+      for (int ks = 0; ks < F::kSteps; ++ks) q[t][ks] = F::load_q(qrow, ks, g);
+    } else {
+      // raw q -> RMSNorm (q_gain) -> rotate-half RoPE, in the fragment layout: this lane holds dims
+      // ks * SD + g * EPL + e; the rotation partner of dim i < D/2 (step ks < kSteps / 2) is step
+      // ks + kSteps / 2 of the same lane.
+      constexpr int EPL = F::kEPL, SD = 4 * EPL, KH = F::kSteps / 2;
+      const float *src = a.raw + (size_t)row * a.ld_raw + head * D;
+      float v[F::kSteps][EPL];
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < F::kSteps; ++ks)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+          const float4 u = *reinterpret_cast<const float4 *>(src + ks * SD + g * EPL + e);
+          v[ks][e] = u.x;
+          v[ks][e + 1] = u.y;
+          v[ks][e + 2] = u.z;
+          v[ks][e + 3] = u.w;
+          ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+        }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+      const int pos = qpos[t];
+      const bool pos_ok = pos >= 0 && pos < a.rope_rows;
+      if (!pos_ok && qok[t] && g == 0) raise_err(a.err, ERR_PAGE);
+      const float2 *rp = a.rope + (size_t)(pos_ok ? pos : 0) * (D / 2);
+      if constexpr (KH > 0) {
+#pragma unroll
+        for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            const int i = ks * SD + g * EPL + e;
+            const float v1 = v[ks][e] * r * a.q_gain[i], v2 = v[ks + KH][e] * r * a.q_gain[i + D / 2];
+            const float2 cs = rp[i];
+            v[ks][e] = v1 * cs.x - v2 * cs.y;
+            v[ks + KH][e] = v2 * cs.x + v1 * cs.y;
+          }
+      } else {  // a single step (D == SD): dims g * EPL + e, the partner lives in lane ^ 32 (g ^ 2)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const int d = g * EPL + e, i = (g & 1) * EPL + e;
+          const float own = v[0][e] * r * a.q_gain[d];
+          const float other = __shfl_xor(own, 32);
+          const float2 cs = rp[i];
+          v[0][e] = g < 2 ? own * cs.x - other * cs.y : own * cs.x + other * cs.y;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < F::kSteps; ++ks) q[t][ks] = F::pack(v[ks]);
+    }
   }
 
   const int first_pos = a.rows.pos[rbase], last_pos = a.rows.pos[rbase + np - 1];
@@ -167,6 +233,41 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     l[t] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (fused) {
+    // The block's own keys that fall in this split: RMSNorm (k_gain) + RoPE of k, then k and v to the
+    // pool (wave j % 4 takes block row j; lane i < D/2 holds dims i and i + D/2).
+    for (int j = wave; j < a.q_len; j += 4) {
+      const int row = b * a.q_len + j, pos = a.rows.pos[row];
+      if (!a.rows.valid[row] || pos < kstart || pos >= kstop) continue;  // wave-uniform
+      const int i = lane < D / 2 ? lane : 0;
+      const float *kr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kh) * D;
+      const float *vr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kvh + kh) * D;
+      float k1 = kr[i], k2 = kr[i + D / 2];
+      float ss = lane < D / 2 ? k1 * k1 + k2 * k2 : 0.f;
+      for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+      k1 = k1 * r * a.k_gain[i];
+      k2 = k2 * r * a.k_gain[i + D / 2];
+      const int pidx = pos / pt, tok = pos % pt;
+      const int page = (pidx < a.bt_stride && pos < a.rope_rows) ? bt[pidx] : -1;
+      if (page < 0) {
+        if (lane == 0) raise_err(a.err, ERR_PAGE);
+        continue;
+      }
+      const float2 cs = a.rope[(size_t)pos * (D / 2) + i];
+      const float o1 = k1 * cs.x - k2 * cs.y, o2 = k2 * cs.x + k1 * cs.y;
+      if (lane < D / 2) {
+        T *kd = (T *)a.kv + a.kvl.k_index(page, kh, tok, 0);
+        T *vd = (T *)a.kv + a.kvl.v_index(page, kh, tok, 0);
+        Elem<T>::store(kd + i, o1);
+        Elem<T>::store(kd + i + D / 2, o2);
+        Elem<T>::store(vd + (size_t)i * pt, vr[i]);
+        Elem<T>::store(vd + (size_t)(i + D / 2) * pt, vr[i + D / 2]);
+      }
+    }
+    __syncthreads();  // the block's keys are in the pool before any wave reads its pages
   }
 
   // Wave w takes the split's pages w, w + 4, ..., in chunks of 64: lane i holds the block-table entry
@@ -276,15 +377,97 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
       } else {
         const size_t pi = ((size_t)row * a.q_heads + head) * a.n_splits + split;
-        a.part_o[pi * D + dim] = O;
-        if (dim == 0) {
-          a.part_ml[pi * 2] = M;
-          a.part_ml[pi * 2 + 1] = L;
+        if (a.counters) {  // written through to memory: the merging work-group may sit on another XCD
+          __hip_atomic_store(&a.part_o[pi * D + dim], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (dim == 0) {
+            __hip_atomic_store(&a.part_ml[pi * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.part_ml[pi * 2 + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        } else {
+          a.part_o[pi * D + dim] = O;
+          if (dim == 0) {
+            a.part_ml[pi * 2] = M;
+            a.part_ml[pi * 2 + 1] = L;
+          }
         }
       }
     }
     __syncthreads();
   }
+  if (!a.counters || a.n_splits == 1) return;
+
+  // Last-arriver merge of the splits of (sequence b, KV head kh).  Every thread's partial stores have
+  // completed (vmcnt 0) before the work-group's arrival is counted; the work-group that sees all other
+  // splits arrived reads their partials back (m, l through the coherent path; O blocks are whole cache
+  // lines written only by their split and read only here) and writes the output.
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+  __syncthreads();
+  int *cnt = a.counters + b * kvh + kh;
+  if (tid == 0) s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n_splits - 1;
+  __syncthreads();
+  if (!s_last) return;
+  const int ns = a.n_splits;
+  // LDS (the merge tile): m of every (qv, split), then l, then 1 / L per qv; ns <= D / 2 (host bound)
+  float *wm = &so[0][0][0];
+  float *wl = wm + nqv * ns;
+  float *linv = wl + nqv * ns;
+  for (int e = tid; e < nqv * ns; e += 256) {
+    const int qv = e / ns, sp = e % ns;
+    const int row = rbase + qv / G, head = kh * G + qv % G;
+    const float *ml = a.part_ml + (((size_t)row * a.q_heads + head) * ns + sp) * 2;
+    wm[e] = __hip_atomic_load(&ml[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wl[e] = __hip_atomic_load(&ml[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  for (int qv = tid; qv < nqv; qv += 256) {
+    float M = NEG;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, wm[qv * ns + sp]);
+    float L = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float ms = wm[qv * ns + sp];
+      const float w = (ms == NEG || M == NEG) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      wm[qv * ns + sp] = w;  // now the split's weight
+      L += w * wl[qv * ns + sp];
+    }
+    linv[qv] = L > 0.f ? 1.0f / L : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < nqv * (D / 4); e += 256) {
+    const int qv = e / (D / 4), d4 = (e % (D / 4)) * 4;
+    const int row = rbase + qv / G, head = kh * G + qv % G;
+    const float4 *po = reinterpret_cast<const float4 *>(a.part_o + ((size_t)row * a.q_heads + head) * ns * D + d4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int sp = 0;
+    for (; sp + 4 <= ns; sp += 4) {  // four splits' loads in flight at once
+      float4 u[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = po[(size_t)(sp + k) * (D / 4)];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = wm[qv * ns + sp + k];
+        acc.x += w * u[k].x;
+        acc.y += w * u[k].y;
+        acc.z += w * u[k].z;
+        acc.w += w * u[k].w;
+      }
+    }
+    for (; sp < ns; ++sp) {
+      const float w = wm[qv * ns + sp];
+      const float4 u = po[(size_t)sp * (D / 4)];
+      acc.x += w * u.x;
+      acc.y += w * u.y;
+      acc.z += w * u.z;
+      acc.w += w * u.w;
+    }
+    const float li = linv[qv];
+    T *out = (T *)a.out + (size_t)row * a.ldo + head * D + d4;
+    Elem<T>::store(out + 0, acc.x * li);
+    Elem<T>::store(out + 1, acc.y * li);
+    Elem<T>::store(out + 2, acc.z * li);
+    Elem<T>::store(out + 3, acc.w * li);
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // out[row][head] = sum_s 2^{m_s - M} O_s / sum_s 2^{m_s - M} l_s  (splits in order; m in log2 units).
@@ -334,7 +517,7 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
     default: hipLaunchKernelGGL((attn_kernel<T, D, 4>), grid, block, 0, s, a); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
+  if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;
   const int n_rows = a.n_seq * a.q_len;
   hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(n_rows * a.q_heads), dim3(128), 0, s, a, n_rows);
   return hipGetLastError();

@@ -464,9 +464,10 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
     const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
     v1 = v1 * r * sg.gain[i];
     v2 = v2 * r * sg.gain[i + half];
-    const double inv = pow((double)a.theta, -2.0 * (double)i / (double)d);
-    const double ang = (double)a.rows.pos[row] * inv;
-    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const int pos = a.rows.pos[row];
+    const float2 cr = (pos >= 0 && pos < a.rope_rows) ? a.rope[(size_t)pos * half + i] : make_float2(1.f, 0.f);
+    if ((pos < 0 || pos >= a.rope_rows) && live && i == 0) raise_err(a.err, ERR_PAGE);
+    const float cs = cr.x, sn = cr.y;
     const float o1 = v1 * cs - v2 * sn, o2 = v2 * cs + v1 * sn;
     v1 = o1;
     v2 = o2;

@@ -79,7 +79,9 @@ struct QkvPostArgs {
   const int32_t *block_table;
   int32_t bt_stride;
   KVLayout kv;
-  float theta, eps;
+  const float2 *rope;  // [position][head_dim / 2] (cos, sin) of the rotary angles
+  int32_t rope_rows;   // positions in the table
+  float eps;
   int32_t *err;
 };
 hipError_t launch_qkv_post(const QkvPostArgs &a, int dtype, hipStream_t s);
@@ -131,6 +133,9 @@ struct NormArgs {
 };
 hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s);
 
+// table[p][i] = (cos, sin) of p * theta^(-2 i / head_dim), angles in fp64, for p < n_pos, i < head_dim / 2
+hipError_t launch_rope_table(float2 *table, float theta, int32_t head_dim, int32_t n_pos, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
   const void *q;
@@ -152,6 +157,19 @@ struct AttnArgs {
   void *out;             // [rows][q_heads*head_dim] act
   int32_t ldo;
   int32_t *err;
+  // Fused post-processing (calls with one query tile per sequence; q is then unused): q, k, v of the
+  // block arrive as raw fp32 projections, row r at raw + r * ld_raw with q heads at column 0, k heads
+  // at q_heads * d and v heads at (q_heads + kv_heads) * d.  Each work-group RMS-normalises (q_gain /
+  // k_gain) and rotates its query vectors, writes the block's k / v that fall in its key range to the
+  // pool, and the last split of a (sequence, KV head) to finish merges all splits (counters: one per
+  // (sequence, KV head), zero between calls).
+  const float *raw;
+  int32_t ld_raw;
+  const float *q_gain, *k_gain;
+  float eps;
+  const float2 *rope;
+  int32_t rope_rows;
+  int32_t *counters;
 };
 hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s);
 

@@ -192,4 +192,22 @@ hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rotary table: the angle p * theta^(-2i/d) in fp64, then its cosine and sine rounded to fp32.
+__global__ void rope_table_kernel(float2 *table, double theta, int half, int d, int n_pos) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_pos * half) return;
+  const int pos = e / half, i = e % half;
+  const double inv = pow(theta, -2.0 * (double)i / (double)d);
+  const double ang = (double)pos * inv;
+  table[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+hipError_t launch_rope_table(float2 *table, float theta, int32_t head_dim, int32_t n_pos, hipStream_t s) {
+  const int half = head_dim / 2, n = n_pos * half;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, table, (double)theta, half, head_dim,
+                     n_pos);
+  return hipGetLastError();
+}
+
 }  // namespace df

@@ -143,6 +143,24 @@ def test_e2e_teacher_forced(name, mode):
         assert stream == ar
 
 
+@pytest.mark.parametrize("merge", ["kernel", "last_arriver"])
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_e2e_fused_attention(name, merge, monkeypatch):
+    """The optional attention path that post-processes q / k / v itself (and optionally merges its key
+    splits in the last work-group to finish) matches the oracle like the default path."""
+    monkeypatch.setenv("DFLASH_ATTN_FUSED", "1")
+    monkeypatch.setenv("DFLASH_ATTN_MERGE", "1" if merge == "last_arriver" else "0")
+    cfg = CASES[name]()
+    log(f"[e2e fused attention] {name} {merge}")
+    W = sw.model_weights(cfg, gain_std=0.1)
+    stream, rep, prompt = run_e2e(cfg, W, cfg.sampling, 24)
+    tol = tol_of(cfg)
+    le, de = np.array(rep.logits_err), np.array(rep.draft_err)
+    log(f"  logits err max {le.max():.3e}, draft logits err max {de.max():.3e}")
+    assert le.max() <= tol and de.max() <= tol
+    assert rep.draft_mismatch == 0
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_gpu_greedy_spec_equals_gpu_greedy_ar(name):
     """Greedy speculative decoding on the device emits exactly the device's own greedy AR stream."""
