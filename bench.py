@@ -78,22 +78,34 @@ class Timer:
         return self.e0.elapsed_time(self.e1)
 
 
-def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=False):
+def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=False, graph=True):
     """Prefill, then warmup + timed speculative steps with no host synchronisation inside the timed
-    region (device-resident sequence state).  Returns (ms for the timed steps, taus per step); with
-    profile=True the library's projection-launch events cover exactly the timed steps."""
+    region (device-resident sequence state).  With graph=True the step is captured once into a HIP
+    graph after the warmup and replayed (every launch parameter of a step is fixed on the host);
+    planted drafts are then copied into the captured buffer before each replay.  Returns (ms for the
+    timed steps, taus per step); with profile=True (eager steps) the library records the projection
+    launches of the timed steps."""
     from speculative_decoding_dflash_amd import binding as Bd
     taus = torch.zeros(warmup + steps, dtype=torch.int32, device="cuda")
     eng.prefill([0], prompt.view(1, -1), [samp])
     for i in range(warmup):
         eng.spec_step([0], [samp], planted=None if planted is None else planted[i])
         taus[i:i + 1].copy_(eng.n_out[:1])
+    g = pl = None
+    if graph and not profile:
+        pl = None if planted is None else planted[0].clone()
+        g = eng.capture_spec_step([0], [samp], planted=pl)
     tm = Timer(torch)
     tm.start()
     if profile:
         Bd.dflash_profile(eng.ctx, True)
     for i in range(warmup, warmup + steps):
-        eng.spec_step([0], [samp], planted=None if planted is None else planted[i])
+        if g is not None:
+            if pl is not None:
+                pl.copy_(planted[i])
+            g.replay()
+        else:
+            eng.spec_step([0], [samp], planted=None if planted is None else planted[i])
         taus[i:i + 1].copy_(eng.n_out[:1])
     ms = tm.stop()
     eng.status()
@@ -157,6 +169,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ar", action="store_true", help="skip plain decoding (and so the planted sweep)")
     ap.add_argument("--profile-steps", type=int, default=8, help="replay passes for the projection roofline")
+    ap.add_argument("--no-graph", action="store_true", help="issue every timed step eagerly instead of replaying "
+                                                            "a captured HIP graph of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build measures the "
@@ -192,7 +206,8 @@ def main():
 
     # 1. the configured run: real drafter, T=1 / top-k / top-p
     log(f"[bench] configured run: {Wm} warmup + {K} timed steps")
-    ms, taus = run_spec(eng, torch, prompt, s_conf, Wm, K)
+    graph = not args.no_graph
+    ms, taus = run_spec(eng, torch, prompt, s_conf, Wm, K, graph=graph)
     tk = taus[Wm:]
     tau = sum(tk) / K
     ms_step = ms / K
@@ -247,7 +262,7 @@ def main():
                                                    force_reject_at=ts if ts < B else None))
                     n += ts
                 planted = torch.from_numpy(np.stack(plans)).to("cuda")
-                ms_p, taus_p = run_spec(eng, torch, prompt, s_greedy, Wm, K, planted=planted)
+                ms_p, taus_p = run_spec(eng, torch, prompt, s_greedy, Wm, K, planted=planted, graph=graph)
                 assert all(x == ts for x in taus_p), (ts, taus_p)
                 nsw = [P + ts * (Wm + i) for i in range(K)]
                 gbs = sum(step_bytes(cfg, x) for x in nsw) / (ms_p / 1e3) / 1e9
@@ -283,6 +298,7 @@ def main():
             "block": B, "concurrency": 1, "prompt_len": P,
         },
         "tau": round(tau, 4),
+        "step_launch": "one captured HIP graph per step, replayed" if graph else "eager launches",
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_bytes": bytes_step,

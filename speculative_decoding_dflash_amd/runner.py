@@ -127,6 +127,19 @@ class Engine:
         self.verify(slots, self.block, self.B, False, self.B)
         self.accept(slots, self.B - 1, samplings, cands=cands)
 
+    def capture_spec_step(self, slots: Sequence[int], samplings: Sequence[B.Sampling],
+                          planted: Optional[torch.Tensor] = None) -> "torch.cuda.CUDAGraph":
+        """Captures one spec_step (draft -> verify -> accept) into a HIP graph; each replay performs the
+        next step.  Every launch parameter of a step is fixed on the host for fixed slots and KV
+        allocations (positions, lengths and the accepted tokens live in device memory), so one capture
+        serves every later step.  Capture records work without running it, so the library's host-side
+        bookkeeping advances as if a step had been issued; call it after the prefill (or a step) and
+        then only replay.  planted: a fixed device tensor copied into the drafts at every replay."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.spec_step(slots, samplings, planted=planted)
+        return g
+
     def ar_step(self, slots: Sequence[int], samplings: Sequence[B.Sampling]):
         """One plain decoding step: verify the anchor alone (the token emitted by the previous prefill or
         ar_step, out[b]) and draw the next token."""

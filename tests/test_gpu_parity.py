@@ -285,3 +285,40 @@ def test_op_linear(dtype, M, N, K):
     err = np.abs(got - ref).max() / np.abs(ref).max()
     log(f"  linear {dtype} {M}x{N}x{K}: rel err {err:.2e}")
     assert err < 1e-5
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_graph_replay_equals_eager_steps(name):
+    """A speculative step captured into a HIP graph and replayed performs exactly the eager steps: same
+    emitted tokens, acceptance counts, drafts and logits at every replay, with eager work and device
+    synchronisation between the replays."""
+    cfg = CASES[name]()
+    log(f"[graph replay] {name}")
+    W = sw.model_weights(cfg)
+    P, B, V = cfg.prompt_len, cfg.drafter.block_size, cfg.target.vocab
+    steps = 6
+    prompt = torch.from_numpy(sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)).to("cuda")
+    s = samp(cfg.sampling)
+
+    def run(use_graph):
+        eng = engine(cfg, W)
+        eng.kv_alloc(0, P + (steps + 2) * B)
+        eng.prefill([0], prompt.view(1, -1), [s])
+        g = eng.capture_spec_step([0], [s]) if use_graph else None
+        rec = []
+        for _ in range(steps):
+            if g is not None:
+                g.replay()
+            else:
+                eng.spec_step([0], [s])
+            torch.cuda.synchronize()
+            n = int(eng.n_out[0])
+            rec.append((n, eng.out[:n].cpu().clone(), eng.block[:B].cpu().clone(), eng.logits[: B * V].cpu().clone()))
+        eng.status()
+        return rec
+
+    eager, graph = run(False), run(True)
+    for i, (a, b) in enumerate(zip(eager, graph)):
+        assert a[0] == b[0], f"step {i}: n_out {a[0]} vs {b[0]}"
+        assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), f"step {i}: tokens or drafts differ"
+        assert torch.equal(a[3], b[3]), f"step {i}: logits differ"
