@@ -12,8 +12,10 @@ emitted per second over the timed steps); with random weights the acceptance len
 the same kernels are also run with a planted drafter (drafts taken from the target's greedy stream
 and forced to fail at a chosen position, greedy verification) for acceptance lengths 1..8, and as
 plain decoding (one target forward per token) for the same-kernel AR baseline.  `roofline` reports
-the projection kernel (the dominant one: ~99% of the step's bytes) from HIP events around each of
-its launches on the step's stream; `cpu_baseline` times the CPU oracle on a bounded sample.
+the projection kernel (the dominant one: ~99% of the step's bytes): the projection launches of one
+step are recorded by the library and replayed back to back between two HIP events on the step's
+stream; `traffic` is the HBM bytes per launch measured with rocprofv3 counters.  `cpu_baseline` times
+the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -30,6 +32,10 @@ if ROOT not in sys.path:
 
 METRIC = "accepted tokens/s at conc 1 (27B-shape, block 8); step HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per projection launch of the decode step, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+# scaled by a plain 1 GiB copy (profiles/gemm_kernel_27b_conc1_traffic.txt), and the hash of the
+# kernel source they were taken on: a changed kernel reports null until the counters are retaken.
+GEMM_TRAFFIC = {"bytes_per_launch": 178703270, "gemm_src_sha256_16": "f2fd76198796102f"}
 
 
 def log(msg: str):
@@ -171,6 +177,9 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=8, help="replay passes for the projection roofline")
     ap.add_argument("--no-graph", action="store_true", help="issue every timed step eagerly instead of replaying "
                                                             "a captured HIP graph of the step")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first copy 1 GiB device to device (a plain copy of known size, the reference for "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build measures the "
@@ -190,6 +199,14 @@ def main():
     t, d = cfg.target, cfg.drafter
     B, P, V = d.block_size, cfg.prompt_len, t.vocab
     K, Wm = args.steps, args.warmup
+    if args.calibration_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1 GiB read, 1 GiB written")
+        del src, dst
     log(f"[bench] {cfg.name}: generating weights on the GPU")
     t0 = time.time()
     weights = sgpu.model_weights(cfg)
@@ -277,6 +294,10 @@ def main():
         log(f"[bench]   {cpu}")
 
     step_gbs = bytes_step / (ms_step / 1e3) / 1e9
+    import hashlib
+    src = os.path.join(ROOT, "speculative_decoding_dflash_amd", "csrc", "gemm.hip")
+    traffic = GEMM_TRAFFIC["bytes_per_launch"] if args.config == "27b" and hashlib.sha256(
+        open(src, "rb").read()).hexdigest()[:16] == GEMM_TRAFFIC["gemm_src_sha256_16"] else None
     out = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -306,7 +327,11 @@ def main():
         "tau_sweep_planted_greedy": sweep,
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel (all projections of the step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
+                                     "factors from a 1 GiB copy)",
+                     "traffic_vs_algorithmic": None if traffic is None else round(
+                         traffic / (rep_bytes / max(rep_n, 1)), 4),
                      "launches_per_step": rep_n, "bytes_per_launch": rep_bytes / max(rep_n, 1),
                      "avg_launch_us": round(gemm_step_ms * 1e3 / max(rep_n, 1), 3),
                      "method": "the projection launches of one decode step recorded by the library and replayed "

@@ -299,7 +299,7 @@ QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
 // raw_qkv (optional, calls with one query tile per sequence): the layer's raw fp32 q/k/v rows, which the
 // attention kernel normalises, rotates and writes to the pool itself (no separate post kernel).
 dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_len, int mode, void *kv, int ctx_bound,
-                            const dflash_layer_weights *raw_w, hipStream_t s) {
+                            const int32_t *slots, const dflash_layer_weights *raw_w, hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   AttnArgs a;
   memset(&a, 0, sizeof a);
@@ -341,6 +341,9 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.out = c->wsp<void>(c->L.attn);
   a.ldo = m.q_heads * m.head_dim;
   a.err = c->err();
+  for (int i = 0; i < n_seq; ++i) a.seq_slot[i] = slots[i];
+  // klo = max(0, first_pos - window + 1) is 0 for every sequence when the allocation fits the window
+  a.abs_range = mode == 0 || c->dcfg.window <= 0 || ctx_bound <= c->dcfg.window;
   if (raw_w) {
     a.raw = c->wsp<float>(c->L.part);
     a.ld_raw = (m.q_heads + 2 * m.kv_heads) * m.head_dim;
@@ -359,9 +362,9 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
 // of squares (deferred RMSNorm); the residual x (fp32) is updated in place.  `next` is the RMSNorm that
 // follows the layer (the next layer's attention norm, or the final norm over the rows that need
 // logits); feat: optional tap of the layer's output.  Returns the ss_n of the deferred next norm.
-dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows, int n_seq,
-                        int q_len, int attn_mode, int ctx_bound, void *feat, int ld_feat, const NextNorm &next,
-                        int *ss_n, hipStream_t s) {
+dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows,
+                        const int32_t *slots, int n_seq, int q_len, int attn_mode, int ctx_bound, void *feat,
+                        int ld_feat, const NextNorm &next, int *ss_n, hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   const int R = n_seq * q_len, H = m.hidden, QD = m.q_heads * m.head_dim, KD = m.kv_heads * m.head_dim, F = m.ffn;
   float *x = c->wsp<float>(c->L.x);
@@ -396,7 +399,7 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
       HIP_OK(launch_qkv_post(p, c->dt(), s));
     }
   }
-  if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, fused ? &w : nullptr, s)) !=
+  if ((st = run_attention(c, rows, n_seq, q_len, attn_mode, kv_layer, ctx_bound, slots, fused ? &w : nullptr, s)) !=
       DFLASH_OK)
     return st;
   {
@@ -616,7 +619,8 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
     // after the last layer: the final norm over the last nl rows of every sequence, packed
     const NextNorm next = l + 1 < m.layers ? all_rows(c->tl[l + 1].attn_norm, R)
                                            : NextNorm{c->final_norm, nl, q_len, q_len - nl};
-    st = run_layer(c, c->tl[l], c->tlayer(l), rows, batch, q_len, 0, ctx_bound, feat, ld_feat, next, &ss_n, s);
+    st = run_layer(c, c->tl[l], c->tlayer(l), rows, slots, batch, q_len, 0, ctx_bound, feat, ld_feat, next, &ss_n,
+                   s);
     if (st != DFLASH_OK) return st;
   }
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32);
@@ -779,7 +783,7 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   for (int j = 0; j < dc.layers; ++j) {
     // after the last layer: the final norm over the B - 1 mask positions of every block, packed
     const NextNorm next = j + 1 < dc.layers ? all_rows(c->dl[j + 1].attn_norm, R) : NextNorm{c->d_final_norm, nd, B, 1};
-    st = run_layer(c, c->dl[j], c->dlayer(j), rd, batch, B, 1, ctx_bound, nullptr, 0, next, &ss_n, s);
+    st = run_layer(c, c->dl[j], c->dlayer(j), rd, slots, batch, B, 1, ctx_bound, nullptr, 0, next, &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);

@@ -126,6 +126,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const float scale = 1.4426950408889634f / sqrtf((float)D);
   const float NEG = -INFINITY;
 
+  // Block-table entries of this split's pages, issued before anything else when the split's key range
+  // is known on the host (lane i: the wave's page i).
+  const int pt = a.kvl.page_tokens;
+  const int32_t *bt = a.block_table + (size_t)a.seq_slot[b] * a.bt_stride;
+  const int pps = a.split_tokens / pt;
+  const bool pre = a.abs_range && pps <= 4 * 64;
+  int pre_bt = -1;
+  if (pre) {
+    const int pidx = split * pps + wave + 4 * lane;
+    if (lane < (pps - wave + 3) / 4 && pidx < a.bt_stride) pre_bt = bt[pidx];
+  }
+
   int qpos[NQT];
   bool qok[NQT];
   u32x4 q[NQT][F::kSteps];
@@ -219,11 +231,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       hi[t] = khi;
     }
   }
-  const int pt = a.kvl.page_tokens;
   const int kstart = (klo / pt) * pt + split * a.split_tokens;
   const int kstop = min(khi, kstart + a.split_tokens);
-  const int slot = a.rows.slot[rbase];
-  const int32_t *bt = a.block_table + (size_t)slot * a.bt_stride;
 
   float m[NQT], l[NQT];
   f32x4 o[NQT][D / 16];
@@ -283,7 +292,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int c0 = 0; c0 < n_all; c0 += 64) {
     const int n_my = min(64, n_all - c0);
     int my_bt = -1;
-    if (lane < n_my) {
+    if (pre && c0 == 0) {
+      my_bt = pre_bt;  // same pages: kstart = split * split_tokens when the range is absolute
+    } else if (lane < n_my) {
       const int pidx = (kstart + (wave + 4 * (c0 + lane)) * pt) / pt;
       my_bt = pidx < a.bt_stride ? bt[pidx] : -1;
     }

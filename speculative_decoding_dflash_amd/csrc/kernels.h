@@ -170,6 +170,11 @@ struct AttnArgs {
   const float2 *rope;
   int32_t rope_rows;
   int32_t *counters;
+  // Host-known facts that shorten the kernel's dependent-load chain: the slot of every sequence, and
+  // abs_range = 1 when no sequence's key range starts after key 0 (causal calls, or drafter calls whose
+  // allocated context fits the window), so the block-table entries of a split are read up front.
+  int32_t seq_slot[64];
+  int32_t abs_range;
 };
 hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s);
 
