@@ -322,3 +322,73 @@ def test_graph_replay_equals_eager_steps(name):
         assert a[0] == b[0], f"step {i}: n_out {a[0]} vs {b[0]}"
         assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), f"step {i}: tokens or drafts differ"
         assert torch.equal(a[3], b[3]), f"step {i}: logits differ"
+
+
+def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
+    """Several requests with ragged prompts: each is prefilled alone and drafts its first block alone
+    (the drafter injects the features of the verify call it follows), then all slots are decoded
+    together in batched verify -> accept -> draft calls, every slot compared with its own oracle."""
+    from speculative_decoding_dflash_amd import binding as Bd
+    tol = tol_of(cfg)
+    B, V = cfg.drafter.block_size, cfg.target.vocab
+    S = len(prompt_lens)
+    eng = engine(cfg, W, max_slots=S, max_rows=max(max(prompt_lens), S * B))
+    s = samp(sp)
+    fols = []
+    for b, P in enumerate(prompt_lens):
+        eng.kv_alloc(b, P + (n_steps + 2) * B)
+        prompt = sw.prompt_ids(V, cfg.drafter.mask_id, P, b)
+        eng.verify([b], torch.from_numpy(prompt).to("cuda"), P, True, 1)
+        eng.accept([b], 0, [s], cands=True)
+        fol = OracleFollower(cfg, W, request=b)
+        z, feats = fol.prefill(prompt)
+        g_ids = eng.cand_ids[:256].cpu().numpy()
+        g_p = eng.cand_p[:256].cpu().numpy()
+        k = int((g_ids >= 0).sum())
+        out0 = int(eng.out[0].item())
+        assert decide([(g_ids[:k].astype(np.int64), g_p[:k])], [], P - 1, sp.seed, b) == [out0]
+        fol.commit(feats, 0, P, out0)
+        fols.append(fol)
+        # this slot's first block, written at its place in the batched block / draft-logit buffers
+        Bd.dflash_draft_block(eng.ctx, [b], eng.feats, eng.block[b * B:], eng.draft_logits[b * (B - 1) * V:])
+    reps = [StepReport() for _ in range(S)]
+    slots = list(range(S))
+    for step in range(n_steps):
+        blocks = eng.block[:S * B].view(S, B).cpu().numpy()
+        dlog = eng.draft_logits[:S * (B - 1) * V].view(S, B - 1, V).cpu().numpy()
+        eng.verify(slots, eng.block, B, False, B)
+        eng.accept(slots, B - 1, [s] * S, cands=True)
+        logits = eng.logits[:S * B * V].view(S, B, V).cpu().numpy()
+        ids = eng.cand_ids[:S * B * 256].view(S, B, 256).cpu().numpy()
+        pp = eng.cand_p[:S * B * 256].view(S, B, 256).cpu().numpy()
+        taus = eng.n_out[:S].cpu().numpy()
+        outs = eng.out[:S * B].view(S, B).cpu().numpy()
+        for b in range(S):
+            tau = int(taus[b])
+            o = [int(x) for x in outs[b, :tau]]
+            start = fols[b].n
+            feats = check_step(reps[b], fols[b], sp, blocks[b], logits[b], dlog[b], ids[b], pp[b], o, tol)
+            fols[b].commit(feats, start, tau, o[-1])
+        log(f"  step {step} taus {[int(t) for t in taus]} logits err "
+            f"{max(max(r.logits_err[-B:]) for r in reps):.2e}")
+        eng.draft(slots, want_logits=True)
+    eng.status()
+    return reps
+
+
+@pytest.mark.parametrize("name,lens,mode", [("tiny", (32, 9, 21, 32), "sampled"), ("small", (128, 37, 90, 61), "greedy"),
+                                            ("small", (53, 128, 7, 100, 64, 31, 128, 80), "sampled")])
+def test_e2e_batched_ragged(name, lens, mode):
+    """Batched steps over requests at different lengths (rows M = batch x block: 16, 32 and 64, the
+    row-tile variants of the projections) match each request's oracle like the batch-1 runs."""
+    cfg = CASES[name]()
+    log(f"[e2e batched] {name} {mode} prompts {lens}")
+    W = sw.model_weights(cfg, gain_std=0.1)
+    sp = synth.GREEDY if mode == "greedy" else cfg.sampling
+    reps = run_e2e_batched(cfg, W, sp, 4, list(lens))
+    tol = tol_of(cfg)
+    for b, rep in enumerate(reps):
+        le, de = np.array(rep.logits_err), np.array(rep.draft_err)
+        log(f"  slot {b}: logits err max {le.max():.3e}, draft err max {de.max():.3e}, taus {rep.taus}")
+        assert le.max() <= tol and de.max() <= tol
+        assert rep.draft_mismatch == 0
