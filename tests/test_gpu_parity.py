@@ -392,3 +392,80 @@ def test_e2e_batched_ragged(name, lens, mode):
         log(f"  slot {b}: logits err max {le.max():.3e}, draft err max {de.max():.3e}, taus {rep.taus}")
         assert le.max() <= tol and de.max() <= tol
         assert rep.draft_mismatch == 0
+
+
+def _ar_with_logits(eng, slot, prompt, n, g):
+    """Device greedy plain decoding of n tokens for one slot; returns the tokens and, per token, the
+    fp32 logit row that produced it (on the host)."""
+    V = eng.cfg.target.vocab
+    eng.prefill([slot], prompt.view(1, -1), [g])
+    toks, rows = [int(eng.out[0])], [eng.logits[:V].cpu().numpy().copy()]
+    while len(toks) < n:
+        eng.ar_step([slot], [g])
+        toks.append(int(eng.out[0]))
+        rows.append(eng.logits[:V].cpu().numpy().copy())
+    return toks, rows
+
+
+@pytest.mark.parametrize("conc", [1, 8, 32])
+def test_27b_greedy_spec_equals_greedy_ar(conc):
+    """At the 27B shape with a 1024-token prompt (the measured configuration at concurrency 1, and the
+    batched verify / draft at concurrency 8 and 32): greedy speculative decoding emits the device's own
+    greedy plain-decoding stream for every request, and every verify logit row at a position both runs
+    reach with the same prefix agrees with the plain-decoding row within twice the bf16 tolerance (each
+    device path is held to the tolerance against the exact forward; the batched rows use other row
+    tiles, so their fp32 sums, and the bf16 roundings that follow, differ along 64 layers).  A stream
+    may diverge only at a near tie of the plain-decoding logits."""
+    from speculative_decoding_dflash_amd import binding as Bd
+    from synth import gpu as sg
+    cfg = synth.CONFIGS["27b"]
+    t, d = cfg.target, cfg.drafter
+    B, P, V = d.block_size, cfg.prompt_len, t.vocab
+    n = 16 if conc > 1 else 24
+    log(f"[27b greedy spec == AR] conc {conc}")
+    Wt = sg.model_weights(cfg)
+    from speculative_decoding_dflash_amd.runner import Engine
+    eng = Engine(cfg, Wt, max_slots=conc, max_rows=max(P, conc * B), max_pages_per_seq=(P + (n + 4) * B) // 16 + 4)
+    g = samp(synth.GREEDY)
+    prompts = [torch.from_numpy(sw.prompt_ids(V, d.mask_id, P, r)).to("cuda") for r in range(conc)]
+    for r in range(conc):
+        eng.kv_alloc(r, P + (n + 3) * B)
+    ar = [_ar_with_logits(eng, r, prompts[r], n, g) for r in range(conc)]
+    # speculative: each slot prefilled and primed alone, then batched verify -> accept -> draft
+    spec = [[] for _ in range(conc)]
+    spec_rows = [dict() for _ in range(conc)]  # position index in the stream -> verify logit row
+    for r in range(conc):
+        eng.prefill([r], prompts[r].view(1, -1), [g])
+        spec[r].append(int(eng.out[0]))
+        Bd.dflash_draft_block(eng.ctx, [r], eng.feats, eng.block[r * B:], None)
+    slots = list(range(conc))
+    while min(len(x) for x in spec) < n:
+        eng.verify(slots, eng.block, B, False, B)
+        eng.accept(slots, B - 1, [g] * conc)
+        taus = eng.n_out[:conc].cpu().numpy()
+        outs = eng.out[:conc * B].view(conc, B).cpu().numpy()
+        logits = eng.logits[:conc * B * V].view(conc, B, V)
+        for r in range(conc):
+            base = len(spec[r])
+            for i in range(int(taus[r])):
+                if base + i < n:
+                    spec_rows[r][base + i] = logits[r, i].cpu().numpy().copy()
+            spec[r].extend(int(x) for x in outs[r, :int(taus[r])])
+        eng.draft(slots)
+    eng.status()
+    tol = 2e-2
+    for r in range(conc):
+        a_toks, a_rows = ar[r]
+        s_toks = spec[r][:n]
+        k = next((i for i in range(n) if s_toks[i] != a_toks[i]), n)
+        if k < n:
+            z = a_rows[k]
+            assert near_tie_argmax(z, tol), f"request {r}: diverges at {k} without a near tie"
+        # every verify row whose prefix matches: indices up to and including the first divergence
+        errs = [float(rel_err_rows(spec_rows[r][i][None], a_rows[i][None])[0])
+                for i in range(1, min(k + 1, n)) if i in spec_rows[r]]
+        log(f"  request {r}: {k}/{n} tokens equal, {len(errs)} verify rows compared, max rel-err "
+            f"{max(errs) if errs else 0:.2e}")
+        assert errs and max(errs) <= 2 * tol
+    del eng, Wt
+    torch.cuda.empty_cache()
