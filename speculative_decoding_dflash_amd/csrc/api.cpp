@@ -316,18 +316,25 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.mode = mode;
   a.window = c->dcfg.window;
   const int G = m.q_heads / m.kv_heads;
-  a.q_tile = std::max(1, std::min(q_len, 64 / G));
+  // One 16-wide MFMA tile of query vectors per work-group (three work-groups per KV head and split at
+  // G = 5, block 8): on MI355X this beats packing the whole block into one work-group by ~40% at
+  // decode (more, lighter work-groups; each page's K/V is re-read from L2 by the tiles).
+  // Larger calls (prefill) and the fused path (one tile per sequence) pack up to 64 query vectors.
+  const char *qz = getenv("DFLASH_ATTN_QTILE");
+  const int qt_env = qz ? atoi(qz) : 0;
+  const bool decode = (size_t)n_seq * q_len <= c->L.att_rows;
+  a.q_tile = std::max(1, std::min(q_len, raw_w || !decode ? 64 / G : (qt_env > 0 ? qt_env : 16 / G)));
   const int ntile = (q_len + a.q_tile - 1) / a.q_tile;
   const int pt = c->cap.page_tokens;
   int key_span = ctx_bound + pt;  // keys of the widest work-group, rounded out to pages
   if (mode == 1 && c->dcfg.window > 0) key_span = std::min(key_span, c->dcfg.window + q_len + 2 * pt);
   const int pages = (key_span + pt - 1) / pt;
-  // Decode-sized calls split the keys into ranges of about six pages (the fastest on MI355X at 1-2K
-  // keys: a few pages per wave, merged by attn_merge_kernel); larger calls keep one range.
+  // Decode-sized calls split the keys into ranges of about nine pages (the fastest on MI355X at 1-2K
+  // keys with one query tile per work-group; merged by attn_merge_kernel); larger calls keep one range.
   int splits = 1;
-  if ((size_t)n_seq * q_len <= c->L.att_rows) splits = std::min(kAttnSplitMax, std::max(1, (pages + 5) / 6));
+  if ((size_t)n_seq * q_len <= c->L.att_rows) splits = std::min(kAttnSplitMax, std::max(1, (pages + 8) / 9));
   int pps = (pages + splits - 1) / splits;
-  static const int env_pps = getenv("DFLASH_ATTN_PPS") ? atoi(getenv("DFLASH_ATTN_PPS")) : 0;
+  const int env_pps = getenv("DFLASH_ATTN_PPS") ? atoi(getenv("DFLASH_ATTN_PPS")) : 0;
   if (env_pps > 0 && (pages + env_pps - 1) / env_pps <= kAttnSplitMax && (size_t)n_seq * q_len <= c->L.att_rows)
     pps = env_pps;
   // the last-arriver merge keeps m and l of every (query vector, split) in the head_dim-sized LDS tile
