@@ -246,7 +246,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   if (fused) {
     // The block's own keys that fall in this split: RMSNorm (k_gain) + RoPE of k, then k and v to the
-    // pool (wave j % 4 takes block row j; lane i < D/2 holds dims i and i + D/2).
+    // pool (wave j % 4 takes block row j; lane i < D/2 holds dims i and i + D/2).  Every query tile's
+    // work-group of the split writes the same values, so each reads back keys it wrote itself.
     for (int j = wave; j < a.q_len; j += 4) {
       const int row = b * a.q_len + j, pos = a.rows.pos[row];
       if (!a.rows.valid[row] || pos < kstart || pos >= kstop) continue;  // wave-uniform
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
   __syncthreads();
-  int *cnt = a.counters + b * kvh + kh;
+  int *cnt = a.counters + (b * kvh + kh) * ntile + qt;
   if (tid == 0) s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n_splits - 1;
   __syncthreads();
   if (!s_last) return;

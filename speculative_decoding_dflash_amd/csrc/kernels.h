@@ -161,8 +161,8 @@ struct AttnArgs {
   // block arrive as raw fp32 projections, row r at raw + r * ld_raw with q heads at column 0, k heads
   // at q_heads * d and v heads at (q_heads + kv_heads) * d.  Each work-group RMS-normalises (q_gain /
   // k_gain) and rotates its query vectors, writes the block's k / v that fall in its key range to the
-  // pool, and the last split of a (sequence, KV head) to finish merges all splits (counters: one per
-  // (sequence, KV head), zero between calls).
+  // pool, and the last split of a (sequence, KV head, query tile) to finish merges all splits
+  // (counters: one per (sequence, KV head, query tile), zero between calls).
   const float *raw;
   int32_t ld_raw;
   const float *q_gain, *k_gain;

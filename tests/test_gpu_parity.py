@@ -143,15 +143,16 @@ def test_e2e_teacher_forced(name, mode):
         assert stream == ar
 
 
-@pytest.mark.parametrize("merge", ["kernel", "last_arriver"])
+@pytest.mark.parametrize("variant", ["separate_post", "last_arriver"])
 @pytest.mark.parametrize("name", ["tiny", "small"])
-def test_e2e_fused_attention(name, merge, monkeypatch):
-    """The optional attention path that post-processes q / k / v itself (and optionally merges its key
-    splits in the last work-group to finish) matches the oracle like the default path."""
-    monkeypatch.setenv("DFLASH_ATTN_FUSED", "1")
-    monkeypatch.setenv("DFLASH_ATTN_MERGE", "1" if merge == "last_arriver" else "0")
+def test_e2e_attention_variants(name, variant, monkeypatch):
+    """The non-default decode attention variants match the oracle like the default (q / k / v post-
+    processed inside attention, splits merged by a second kernel): a separate post-processing kernel,
+    and the in-kernel merge by the last split to finish."""
+    monkeypatch.setenv("DFLASH_ATTN_FUSED", "0" if variant == "separate_post" else "1")
+    monkeypatch.setenv("DFLASH_ATTN_MERGE", "1" if variant == "last_arriver" else "0")
     cfg = CASES[name]()
-    log(f"[e2e fused attention] {name} {merge}")
+    log(f"[e2e attention variant] {name} {variant}")
     W = sw.model_weights(cfg, gain_std=0.1)
     stream, rep, prompt = run_e2e(cfg, W, cfg.sampling, 24)
     tol = tol_of(cfg)
