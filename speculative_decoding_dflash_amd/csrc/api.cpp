@@ -40,13 +40,14 @@ int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 constexpr int kAttnSplitMax = 64;
 constexpr int kMaxKSplit = 8;
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
+constexpr int kSkMaxWg = 1024;  // stream-K projection work-groups (one per CU)
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, cnt, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, att_o, att_ml, dlogits, cid, cp, cn,
-      skey, sidx, total;
+  size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, att_o, att_ml, dlogits, cid,
+      cp, cn, skey, sidx, total;
   size_t part_elems, att_rows;
-  int ss_ld;
+  int ss_ld, sk_tiles;
 };
 
 Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
@@ -64,6 +65,9 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.err = take(sizeof(int32_t) * ERR_COUNT);
   // attention merge counters, one per (slot, KV head, query tile of a block), zeroed
   L.cnt = take(sizeof(int32_t) * cap->max_slots * c->kv_heads * kMaxQTiles);
+  // stream-K projection tile counters (16-column tiles of the widest projection output), zeroed
+  L.sk_tiles = (int)(std::max({(size_t)c->ffn, (size_t)c->vocab, QD + 2 * KD, (size_t)d->layers * 2 * KD, H}) / 16);
+  L.skc = take(sizeof(int32_t) * L.sk_tiles);
   L.bt = take(sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq);
   for (int s = 0; s < 3; ++s)
     for (int k = 0; k < 4; ++k) L.rows[s][k] = take(sizeof(int32_t) * R);
@@ -82,6 +86,7 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   const size_t part_cols = std::max({QD + 2 * KD, (size_t)d->layers * 2 * KD, H});
   L.part_elems = std::max(R, (size_t)kMaxKSplit * kGemmMaxRows) * part_cols;
   L.part = take(sizeof(float) * L.part_elems);
+  L.skp = take(sizeof(float) * kSkMaxWg * 2 * kSkTileElems);  // stream-K partial tiles
   L.att_rows = (size_t)cap->max_slots * B;
   L.att_o = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * c->head_dim);
   L.att_ml = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * 2);
@@ -205,6 +210,10 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s, hipEven
 }
 
 dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
+  a.sk_part = c->wsp<float>(c->L.skp);
+  a.sk_cnt = c->wsp<int32_t>(c->L.skc);
+  a.sk_max_wg = kSkMaxWg;
+  a.sk_max_tiles = c->L.sk_tiles;
   if (c->profiling) c->recorded.push_back({a, R});
   return run_gemm(c->es(), c->dt(), a, R, s);
 }
@@ -392,8 +401,10 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     // Decode-sized calls: the attention kernel post-processes q / k / v itself (one query tile per
     // work-group keeps that prologue short; 0.2 ms per 27B step faster on MI355X than a separate
     // post-processing launch).  DFLASH_ATTN_FUSED=0 selects the separate kernel.
+    // The fused kernel needs q_len <= 64 (one position per lane) and a 16-byte aligned q gain.
     const char *fz = getenv("DFLASH_ATTN_FUSED");
-    fused = !(fz && atoi(fz) == 0) && np == 1 && (size_t)R <= c->L.att_rows;
+    fused = !(fz && atoi(fz) == 0) && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 64 &&
+            ((uintptr_t)w.q_norm & 15) == 0;
     if (!fused) {
       QkvPostArgs p = post_base(c, rows, R);
       p.ld_src = QD + 2 * KD;

@@ -104,20 +104,43 @@ template <int D> struct AttnFrag<float, D> {
   }
 };
 
-template <typename T, int D, int NQT>
+// Loads through the vector memory path even where the address is uniform: a scalar load's wait
+// (lgkmcnt, which has no order) would also be taken by every later kernel-argument load.
+template <typename X>
+DF_DEVICE X vload(const X *p, int i) {
+  asm volatile("" : "+v"(i));
+  return p[i];
+}
+
+template <typename T, int D, int NQT, bool FUSED>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using F = AttnFrag<T, D>;
-  __shared__ float so[4][16][D + 1];
+  __shared__ __attribute__((aligned(16))) float so[4][16][D + 4];  // rows 16-byte aligned
   __shared__ float sm[4][NQT * 16], sl[4][NQT * 16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  {
+    // Touch the argument block's first four 64-byte lines together: each first touch misses the
+    // scalar cache, and fetched as they are needed the misses would be waited for one after another.
+    const int k0 = a.ldq, k1 = a.q_len, k2 = a.ld_raw, k3 = a.abs_range;
+    asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3));
+  }
   const int kvh = a.kvl.kv_heads, G = a.q_heads / kvh;
   const int ntile = (a.q_len + a.q_tile - 1) / a.q_tile;
-  int bx = blockIdx.x;
+  // Work-groups are dealt to the 8 XCDs round-robin in launch order.  Renumbering them so that each
+  // XCD gets a contiguous range of (query tile, KV head, sequence, split) puts the query tiles of one
+  // (KV head, split) -- which read the same pages -- under one L2.
+  int bx = blockIdx.x, split = blockIdx.y;
+  const int gx = a.n_seq * kvh * ntile, n_wg = gx * a.n_splits;  // the launch grid, from the arguments
+  if (n_wg % 8 == 0) {
+    const int lin = blockIdx.x + gx * blockIdx.y;
+    const int v = (lin % 8) * (n_wg / 8) + lin / 8;
+    bx = v % gx;
+    split = v / gx;
+  }
   const int qt = bx % ntile;
   bx /= ntile;
   const int kh = bx % kvh;
   const int b = bx / kvh;
-  const int split = blockIdx.y;
   const int p0 = qt * a.q_tile;
   const int np = min(a.q_tile, a.q_len - p0);
   const int nqv = np * G;
@@ -126,77 +149,244 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const float scale = 1.4426950408889634f / sqrtf((float)D);
   const float NEG = -INFINITY;
 
-  // Block-table entries of this split's pages, issued before anything else when the split's key range
-  // is known on the host (lane i: the wave's page i).
+  // The prologue is ordered so that no load waits behind loads it does not need (a wave's loads return
+  // in issue order): (A) loads addressed by the arguments alone; (B) loads addressed by positions from
+  // (A): rotary rows and the block-table entries of the block's own keys; (C) the wave's first two K/V
+  // pages, which stream while (D) q is normalised and rotated and the block's k / v are written.
+  // Fused calls (raw q / k / v in, see AttnArgs) are a separate instantiation, so none of this is
+  // behind a run-time branch.
   const int pt = a.kvl.page_tokens;
   const int32_t *bt = a.block_table + (size_t)a.seq_slot[b] * a.bt_stride;
   const int pps = a.split_tokens / pt;
   const bool pre = a.abs_range && pps <= 4 * 64;
+  constexpr int EPL = F::kEPL, SD = 4 * EPL, KH = F::kSteps / 2, KHS = KH > 0 ? KH : 1;
+  constexpr int kWR = 2;  // block rows per wave (rows wave + 4 w) whose k / v loads are hoisted
+  // A wave can have at most 63 vector memory instructions outstanding; (A) issues ~30 (fused), so
+  // none of it waits for an earlier load to return.  Fused calls (q_len <= 64, checked by the host)
+  // read every block position once, lane j holding row j's, and share it by lane exchange.
+
+  // (A) block-table entries of the split's pages when its key range is known on the host (lane i: the
+  // wave's page i), the rows' positions, q (or raw q and its gain), the raw k / v of the block rows.
   int pre_bt = -1;
   if (pre) {
     const int pidx = split * pps + wave + 4 * lane;
     if (lane < (pps - wave + 3) / 4 && pidx < a.bt_stride) pre_bt = bt[pidx];
   }
-
+  int first_pos_v = 0, last_pos_v = 0, nblk_v = 0;
+  int bl_pos = 0, bl_val = 0;  // block row `lane` (fused): its position and validity
+  if constexpr (FUSED) {
+    const int row = b * a.q_len + (lane < a.q_len ? lane : 0);
+    bl_pos = a.rows.pos[row];
+    bl_val = a.rows.valid[row];
+  } else {
+    first_pos_v = vload(a.rows.pos, rbase);
+    last_pos_v = vload(a.rows.pos, rbase + np - 1);
+    nblk_v = vload(a.rows.pos, b * a.q_len);
+  }
   int qpos[NQT];
   bool qok[NQT];
   u32x4 q[NQT][F::kSteps];
-  const bool fused = a.raw != nullptr;
+  float qraw[NQT][F::kSteps][EPL], qg[F::kSteps][EPL];
+  const int wi = lane < D / 2 ? lane : 0;  // write rows: lane i < D/2 holds dims i and i + D/2
+  float w_k[kWR][2], w_v[kWR][2], kg[2];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int qv = t * 16 + l16;
     qok[t] = qv < nqv;
     const int row = rbase + (qok[t] ? qv / G : 0);
     const int head = kh * G + (qok[t] ? qv % G : 0);
-    qpos[t] = a.rows.pos[row];
-    if (!fused) {
+    if constexpr (!FUSED) {
+      qpos[t] = a.rows.pos[row];
       const T *qrow = (const T *)a.q + (size_t)row * a.ldq + head * D;
 #pragma unroll
       for (int ks = 0; ks < F::kSteps; ++ks) q[t][ks] = F::load_q(qrow, ks, g);
     } else {
-      // raw q -> RMSNorm (q_gain) -> rotate-half RoPE, in the fragment layout: this lane holds dims
-      // ks * SD + g * EPL + e; the rotation partner of dim i < D/2 (step ks < kSteps / 2) is step
-      // ks + kSteps / 2 of the same lane.
-      constexpr int EPL = F::kEPL, SD = 4 * EPL, KH = F::kSteps / 2;
+      qpos[t] = row - b * a.q_len;  // the row's index in the block for now; its position below
+      // this lane holds dims ks * SD + g * EPL + e of its query vector
       const float *src = a.raw + (size_t)row * a.ld_raw + head * D;
-      float v[F::kSteps][EPL];
-      float ss = 0.f;
 #pragma unroll
       for (int ks = 0; ks < F::kSteps; ++ks)
 #pragma unroll
         for (int e = 0; e < EPL; e += 4) {
           const float4 u = *reinterpret_cast<const float4 *>(src + ks * SD + g * EPL + e);
-          v[ks][e] = u.x;
-          v[ks][e + 1] = u.y;
-          v[ks][e + 2] = u.z;
-          v[ks][e + 3] = u.w;
-          ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+          qraw[t][ks][e] = u.x;
+          qraw[t][ks][e + 1] = u.y;
+          qraw[t][ks][e + 2] = u.z;
+          qraw[t][ks][e + 3] = u.w;
         }
+    }
+  }
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int ks = 0; ks < F::kSteps; ++ks)
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {  // 16-byte aligned (checked by the host)
+        const float4 u = *reinterpret_cast<const float4 *>(a.q_gain + ks * SD + g * EPL + e);
+        qg[ks][e] = u.x;
+        qg[ks][e + 1] = u.y;
+        qg[ks][e + 2] = u.z;
+        qg[ks][e + 3] = u.w;
+      }
+    kg[0] = a.k_gain[wi];
+    kg[1] = a.k_gain[wi + D / 2];
+#pragma unroll
+    for (int w = 0; w < kWR; ++w) {
+      const int j = wave + 4 * w;
+      const int row = b * a.q_len + (j < a.q_len ? j : 0);
+      const float *kr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kh) * D;
+      const float *vr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kvh + kh) * D;
+      w_k[w][0] = kr[wi];
+      w_k[w][1] = kr[wi + D / 2];
+      w_v[w][0] = vr[wi];
+      w_v[w][1] = vr[wi + D / 2];
+    }
+  }
+  int w_pos[kWR], w_val[kWR];
+  if constexpr (FUSED) {  // positions from the block's lanes (waits for (A)'s first loads)
+    first_pos_v = __builtin_amdgcn_readlane(bl_pos, p0);
+    last_pos_v = __builtin_amdgcn_readlane(bl_pos, p0 + np - 1);
+    nblk_v = __builtin_amdgcn_readlane(bl_pos, 0);
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) qpos[t] = __shfl(bl_pos, qpos[t]);
+#pragma unroll
+    for (int w = 0; w < kWR; ++w) {
+      const int j = wave + 4 * w;
+      w_pos[w] = __builtin_amdgcn_readlane(bl_pos, j < a.q_len ? j : 0);
+      w_val[w] = j < a.q_len && __builtin_amdgcn_readlane(bl_val, j < a.q_len ? j : 0);
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);  // (B) addresses wait for (A): keep them after all of (A)'s loads
+  // (B) rotary (cos, sin) of the query rows and of the write rows, and the write rows' pages
+  float2 qcs[NQT][KHS][EPL];
+  float2 w_cs[kWR];
+  int w_page[kWR];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const int pos = qpos[t];
+      const bool pos_ok = pos >= 0 && pos < a.rope_rows;
+      const float2 *rp = a.rope + (size_t)(pos_ok ? pos : 0) * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < KHS; ++ks)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qcs[t][ks][e] = rp[KH > 0 ? ks * SD + g * EPL + e : (g & 1) * EPL + e];
+    }
+#pragma unroll
+    for (int w = 0; w < kWR; ++w) {
+      const int pos = w_pos[w];
+      const bool ok = pos >= 0 && pos < a.rope_rows && pos / pt < a.bt_stride;
+      w_cs[w] = a.rope[(size_t)(ok ? pos : 0) * (D / 2) + wi];
+      const int pg = vload(bt, ok ? pos / pt : 0);
+      w_page[w] = ok ? pg : -1;
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // (C) the wave's first two pages.  With the split's pages known up front they need no position:
+  // entries past the sequence's pages are -1 (loads of a dummy block) and pages past the key range are
+  // loaded but never used.  Fused calls load pages holding a position at or after the lowest valid
+  // block row's only after writing the block's keys there.
+  // A block's rows hold consecutive positions, valid rows first (as the row preparation writes them),
+  // so the lowest valid position is row 0's when row 0 is valid.
+  int blk_lo = 0x7fffffff;
+  if constexpr (FUSED) {
+    if (__builtin_amdgcn_readlane(bl_val, 0)) blk_lo = __builtin_amdgcn_readlane(bl_pos, 0);
+  }
+  // key range of the split (uniform; read back into scalar registers)
+  int klo, khi;
+  if (a.mode == 0) {
+    klo = 0;
+    khi = last_pos_v + 1;
+  } else {
+    khi = nblk_v + a.q_len;
+    klo = a.window > 0 ? max(0, first_pos_v - a.window + 1) : 0;
+  }
+  const int kbase = pre ? 0 : __builtin_amdgcn_readfirstlane((klo / pt) * pt);  // 0 whenever pre holds
+  const int kstart = kbase + split * a.split_tokens;
+  const T *kvb = (const T *)a.kv;
+  const T *dummy = kvb;
+  u32x4 kf[2][F::kSteps];
+  typename F::VF vf[2][D / 16];
+  // Wave w takes the split's pages w, w + 4, ..., in chunks of 64: lane i holds the block-table entry
+  // of the chunk's page i (read once per chunk), and two pages' K/V fragments are in flight while one
+  // is consumed.  Loads past the chunk's last page read a valid dummy block (the pool's first), so
+  // that every load is unconditional.
+  auto chunk_bt = [&](int c0, int n_my) {
+    if (pre && c0 == 0) return pre_bt;  // same pages: kstart = split * split_tokens when the range is absolute
+    int e = -1;
+    if (lane < n_my) {
+      const int pidx = (kstart + (wave + 4 * (c0 + lane)) * pt) / pt;
+      e = pidx < a.bt_stride ? bt[pidx] : -1;
+    }
+    return e;
+  };
+  auto page_range = [&](int &kstop, int &n_all) {
+    kstop = __builtin_amdgcn_readfirstlane(min(khi, kstart + a.split_tokens));
+    const int npg = kstop > kstart ? (kstop - kstart + pt - 1) / pt : 0;
+    n_all = wave < npg ? (npg - wave + 3) / 4 : 0;
+  };
+  bool late[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) late[p] = FUSED && kstart + (wave + 4 * p + 1) * pt > blk_lo;
+  auto ring_loads = [&](int bts) {  // bts: lane p holds page p's block-table entry (-1: none)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int pg = __builtin_amdgcn_readlane(bts, p);
+      F::load_k(kf[p], pg >= 0 && !late[p] ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
+      F::load_v(vf[p], pg >= 0 && !late[p] ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
+    }
+  };
+  // Both branches issue their loads inside, so that neither path's wait covers the other's loads.
+  int kstop = 0, n_all = 0, n_my = 0, my_bt = -1;
+  if (pre) {
+    my_bt = pre_bt;  // -1 past the wave's pages
+    ring_loads(pre_bt);
+    page_range(kstop, n_all);
+    n_my = min(64, n_all);
+  } else {
+    page_range(kstop, n_all);
+    n_my = min(64, n_all);
+    my_bt = chunk_bt(0, n_my);  // -1 past n_my
+    ring_loads(my_bt);
+  }
+  const int first_pos = first_pos_v;
+  const int nblk = nblk_v;
+
+  // (D) raw q -> RMSNorm (q_gain) -> rotate-half RoPE in the fragment layout: the rotation partner of
+  // dim i < D/2 (step ks < kSteps / 2) is step ks + kSteps / 2 of the same lane; with a single step
+  // (D == SD) it lives in lane ^ 32.
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const int pos = qpos[t];
+      if (!(pos >= 0 && pos < a.rope_rows) && qok[t] && g == 0) raise_err(a.err, ERR_PAGE);
+      float(&v)[F::kSteps][EPL] = qraw[t];
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < F::kSteps; ++ks)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          ss += v[ks][e] * v[ks][e] + v[ks][e + 1] * v[ks][e + 1] + v[ks][e + 2] * v[ks][e + 2] + v[ks][e + 3] * v[ks][e + 3];
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-      const int pos = qpos[t];
-      const bool pos_ok = pos >= 0 && pos < a.rope_rows;
-      if (!pos_ok && qok[t] && g == 0) raise_err(a.err, ERR_PAGE);
-      const float2 *rp = a.rope + (size_t)(pos_ok ? pos : 0) * (D / 2);
       if constexpr (KH > 0) {
 #pragma unroll
         for (int ks = 0; ks < KH; ++ks)
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
-            const int i = ks * SD + g * EPL + e;
-            const float v1 = v[ks][e] * r * a.q_gain[i], v2 = v[ks + KH][e] * r * a.q_gain[i + D / 2];
-            const float2 cs = rp[i];
+            const float v1 = v[ks][e] * r * qg[ks][e], v2 = v[ks + KH][e] * r * qg[ks + KH][e];
+            const float2 cs = qcs[t][ks][e];
             v[ks][e] = v1 * cs.x - v2 * cs.y;
             v[ks + KH][e] = v2 * cs.x + v1 * cs.y;
           }
-      } else {  // a single step (D == SD): dims g * EPL + e, the partner lives in lane ^ 32 (g ^ 2)
+      } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          const int d = g * EPL + e, i = (g & 1) * EPL + e;
-          const float own = v[0][e] * r * a.q_gain[d];
+          const float own = v[0][e] * r * qg[0][e];
           const float other = __shfl_xor(own, 32);
-          const float2 cs = rp[i];
+          const float2 cs = qcs[t][0][e];
           v[0][e] = g < 2 ? own * cs.x - other * cs.y : own * cs.x + other * cs.y;
         }
       }
@@ -205,16 +395,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  const int first_pos = a.rows.pos[rbase], last_pos = a.rows.pos[rbase + np - 1];
-  int klo, khi, nblk = 0;
-  if (a.mode == 0) {
-    klo = 0;
-    khi = last_pos + 1;
-  } else {
-    nblk = a.rows.pos[b * a.q_len];
-    khi = nblk + a.q_len;
-    klo = a.window > 0 ? max(0, first_pos - a.window + 1) : 0;
-  }
   // Key range [lo, hi) of every query vector: causal (mode 0); block keys plus the sliding window of
   // context keys (mode 1, the drafter); empty for padding query vectors.
   int lo[NQT], hi[NQT];
@@ -231,8 +411,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       hi[t] = khi;
     }
   }
-  const int kstart = (klo / pt) * pt + split * a.split_tokens;
-  const int kstop = min(khi, kstart + a.split_tokens);
 
   float m[NQT], l[NQT];
   f32x4 o[NQT][D / 16];
@@ -244,66 +422,70 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  if (fused) {
+  if constexpr (FUSED) {
     // The block's own keys that fall in this split: RMSNorm (k_gain) + RoPE of k, then k and v to the
-    // pool (wave j % 4 takes block row j; lane i < D/2 holds dims i and i + D/2).  Every query tile's
-    // work-group of the split writes the same values, so each reads back keys it wrote itself.
-    for (int j = wave; j < a.q_len; j += 4) {
-      const int row = b * a.q_len + j, pos = a.rows.pos[row];
-      if (!a.rows.valid[row] || pos < kstart || pos >= kstop) continue;  // wave-uniform
-      const int i = lane < D / 2 ? lane : 0;
-      const float *kr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kh) * D;
-      const float *vr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kvh + kh) * D;
-      float k1 = kr[i], k2 = kr[i + D / 2];
+    // pool (wave j % 4 takes block row j).  Every query tile's work-group of the split writes the same
+    // values, so each reads back keys it wrote itself.
+    auto write_row = [&](int pos, int page, float k1, float k2, float v1, float v2, float2 cs) {
       float ss = lane < D / 2 ? k1 * k1 + k2 * k2 : 0.f;
       for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
       const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-      k1 = k1 * r * a.k_gain[i];
-      k2 = k2 * r * a.k_gain[i + D / 2];
-      const int pidx = pos / pt, tok = pos % pt;
+      k1 = k1 * r * kg[0];
+      k2 = k2 * r * kg[1];
+      const float o1 = k1 * cs.x - k2 * cs.y, o2 = k2 * cs.x + k1 * cs.y;
+      if (lane < D / 2) {
+        const int tok = pos % pt;
+        T *kd = (T *)a.kv + a.kvl.k_index(page, kh, tok, 0);
+        T *vd = (T *)a.kv + a.kvl.v_index(page, kh, tok, 0);
+        Elem<T>::store(kd + wi, o1);
+        Elem<T>::store(kd + wi + D / 2, o2);
+        Elem<T>::store(vd + (size_t)wi * pt, v1);
+        Elem<T>::store(vd + (size_t)(wi + D / 2) * pt, v2);
+      }
+    };
+#pragma unroll
+    for (int w = 0; w < kWR; ++w) {
+      const int pos = w_pos[w];
+      if (!w_val[w] || pos < kstart || pos >= kstop) continue;  // wave-uniform
+      if (w_page[w] < 0) {
+        if (lane == 0) raise_err(a.err, ERR_PAGE);
+        continue;
+      }
+      write_row(pos, w_page[w], w_k[w][0], w_k[w][1], w_v[w][0], w_v[w][1], w_cs[w]);
+    }
+    for (int j = wave + 4 * kWR; j < a.q_len; j += 4) {  // rows beyond the hoisted ones
+      const int row = b * a.q_len + j, pos = a.rows.pos[row];
+      if (!a.rows.valid[row] || pos < kstart || pos >= kstop) continue;  // wave-uniform
+      const int pidx = pos / pt;
       const int page = (pidx < a.bt_stride && pos < a.rope_rows) ? bt[pidx] : -1;
       if (page < 0) {
         if (lane == 0) raise_err(a.err, ERR_PAGE);
         continue;
       }
-      const float2 cs = a.rope[(size_t)pos * (D / 2) + i];
-      const float o1 = k1 * cs.x - k2 * cs.y, o2 = k2 * cs.x + k1 * cs.y;
-      if (lane < D / 2) {
-        T *kd = (T *)a.kv + a.kvl.k_index(page, kh, tok, 0);
-        T *vd = (T *)a.kv + a.kvl.v_index(page, kh, tok, 0);
-        Elem<T>::store(kd + i, o1);
-        Elem<T>::store(kd + i + D / 2, o2);
-        Elem<T>::store(vd + (size_t)i * pt, vr[i]);
-        Elem<T>::store(vd + (size_t)(i + D / 2) * pt, vr[i + D / 2]);
-      }
+      const float *kr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kh) * D;
+      const float *vr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kvh + kh) * D;
+      write_row(pos, page, kr[wi], kr[wi + D / 2], vr[wi], vr[wi + D / 2], a.rope[(size_t)pos * (D / 2) + wi]);
     }
     __syncthreads();  // the block's keys are in the pool before any wave reads its pages
   }
 
-  // Wave w takes the split's pages w, w + 4, ..., in chunks of 64: lane i holds the block-table entry
-  // of the chunk's page i (read once per chunk), and two pages' K/V fragments are in flight while one
-  // is consumed.  Loads past the chunk's last page read a valid dummy block (the pool's first), so
-  // that every load is unconditional.
-  const int npg = kstop > kstart ? (kstop - kstart + pt - 1) / pt : 0;
-  const int n_all = wave < npg ? (npg - wave + 3) / 4 : 0;
-  const T *kvb = (const T *)a.kv;
-  const T *dummy = kvb;
-  u32x4 kf[2][F::kSteps];
-  typename F::VF vf[2][D / 16];
-  for (int c0 = 0; c0 < n_all; c0 += 64) {
-    const int n_my = min(64, n_all - c0);
-    int my_bt = -1;
-    if (pre && c0 == 0) {
-      my_bt = pre_bt;  // same pages: kstart = split * split_tokens when the range is absolute
-    } else if (lane < n_my) {
-      const int pidx = (kstart + (wave + 4 * (c0 + lane)) * pt) / pt;
-      my_bt = pidx < a.bt_stride ? bt[pidx] : -1;
-    }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < 2; ++p)
+    if (late[p]) {  // wave-uniform
       const int pg = p < n_my ? __builtin_amdgcn_readlane(my_bt, p) : -1;
       F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
       F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
+    }
+  for (int c0 = 0; c0 < n_all; c0 += 64) {
+    if (c0 > 0) {
+      n_my = min(64, n_all - c0);
+      my_bt = chunk_bt(c0, n_my);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int pg = p < n_my ? __builtin_amdgcn_readlane(my_bt, p) : -1;
+        F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
+        F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
+      }
     }
     for (int i0 = 0; i0 < n_my; i0 += 2) {
 #pragma unroll
@@ -352,7 +534,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // Merge the four waves, one 16-qv tile at a time.
+  // Merge the four waves, one 16-qv tile at a time: thread (qi = tid / 16, c = tid % 16) combines
+  // dims [c * DPT, (c + 1) * DPT) of the tile's query vector qi, so all its LDS reads are independent.
+  constexpr int DPT = D / 16;
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     float lt = l[t];
@@ -367,37 +551,52 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) so[wave][l16][dt * 16 + 4 * g + r] = o[t][dt][r];
     __syncthreads();
-    for (int e = tid; e < 16 * D; e += 256) {
-      const int qi = e / D, dim = e % D;
-      const int qv = t * 16 + qi;
-      if (qv >= nqv) continue;
-      float M = NEG;
+    const int qi = tid >> 4, d0 = (tid & 15) * DPT;
+    const int qv = t * 16 + qi;
+    if (qv < nqv) {
+      float mw[4], M = NEG;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][t * 16 + qi]);
-      float L = 0.f, O = 0.f;
-      if (M != NEG) {
+      for (int w = 0; w < 4; ++w) {
+        mw[w] = sm[w][t * 16 + qi];
+        M = fmaxf(M, mw[w]);
+      }
+      float f[4], L = 0.f, O[DPT];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float mw = sm[w][t * 16 + qi];
-          const float f = (mw == NEG) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-          L += f * sl[w][t * 16 + qi];
-          O += f * so[w][qi][dim];
-        }
+      for (int w = 0; w < 4; ++w) {
+        f[w] = (mw[w] == NEG || M == NEG) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        L += f[w] * sl[w][t * 16 + qi];
+      }
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) {
+        O[d] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) O[d] += f[w] * so[w][qi][d0 + d];
       }
       const int row = rbase + qv / G, head = kh * G + qv % G;
       if (a.n_splits == 1) {
-        Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
+        T *out = (T *)a.out + (size_t)row * a.ldo + head * D + d0;
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) Elem<T>::store(out + d, L > 0.f ? O[d] / L : 0.f);
       } else {
         const size_t pi = ((size_t)row * a.q_heads + head) * a.n_splits + split;
+        float *po = a.part_o + pi * D + d0;
         if (a.counters) {  // written through to memory: the merging work-group may sit on another XCD
-          __hip_atomic_store(&a.part_o[pi * D + dim], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (dim == 0) {
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) __hip_atomic_store(po + d, O[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d0 == 0) {
             __hip_atomic_store(&a.part_ml[pi * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.part_ml[pi * 2 + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         } else {
-          a.part_o[pi * D + dim] = O;
-          if (dim == 0) {
+          if constexpr (DPT % 4 == 0) {  // part_o rows are 16-byte aligned (D a multiple of 16)
+#pragma unroll
+            for (int d = 0; d < DPT; d += 4)
+              *reinterpret_cast<float4 *>(po + d) = make_float4(O[d], O[d + 1], O[d + 2], O[d + 3]);
+          } else {
+#pragma unroll
+            for (int d = 0; d < DPT; ++d) po[d] = O[d];
+          }
+          if (d0 == 0) {
             a.part_ml[pi * 2] = M;
             a.part_ml[pi * 2 + 1] = L;
           }
@@ -522,11 +721,20 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   const int nqt = (a.q_tile * G + 15) / 16;
   const int ntile = (a.q_len + a.q_tile - 1) / a.q_tile;
   dim3 grid(a.n_seq * a.kvl.kv_heads * ntile, a.n_splits), block(256);
-  switch (nqt) {
-    case 1: hipLaunchKernelGGL((attn_kernel<T, D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<T, D, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((attn_kernel<T, D, 3>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_kernel<T, D, 4>), grid, block, 0, s, a); break;
+  if (a.raw) {
+    switch (nqt) {
+      case 1: hipLaunchKernelGGL((attn_kernel<T, D, 1, true>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((attn_kernel<T, D, 2, true>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((attn_kernel<T, D, 3, true>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_kernel<T, D, 4, true>), grid, block, 0, s, a); break;
+    }
+  } else {
+    switch (nqt) {
+      case 1: hipLaunchKernelGGL((attn_kernel<T, D, 1, false>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((attn_kernel<T, D, 2, false>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((attn_kernel<T, D, 3, false>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_kernel<T, D, 4, false>), grid, block, 0, s, a); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;

@@ -14,11 +14,17 @@
 //   * v_mfma_f32_16x16x32_bf16 (or 4 x v_mfma_f32_16x16x4f32 for fp32 models) accumulates in fp32;
 //   * the NW waves reduce their partial tiles through LDS in a fixed order, then the whole
 //     work-group runs the epilogue on its columns.  No state crosses work-groups, so no device-scope
-//     fences (which write back and invalidate the per-XCD L2s) are needed anywhere.
+//     fences (which write back and invalidate the per-XCD L2s) are needed anywhere;
+//   * gemm_sk_kernel, a stream-K variant for decode-sized M, spreads the items of projections whose
+//     tile count fits the CUs badly evenly over one work-group per CU; tiles shared by two or three
+//     work-groups are finished by the last to arrive, through write-through partial stores and one
+//     arrival counter per tile (again no fences).
 // Epilogues: fp32 store (logits), activation store, fp32 partial store of one K range (grid row y;
 // the consumer sums the ranges in order: residual add + RMSNorm, q/k/v post-processing), and SwiGLU
 // (gate and up rows of the same output column in one work-group).
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "kernels.h"
 
@@ -49,6 +55,127 @@ template <> struct Frag<float> {
 template <typename T> DF_DEVICE u32x4 ld16(const T *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 DF_DEVICE float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Prefetch of the deferred RMSNorm's partial sums of squares: those of X row m sit at
+// ss_in[(row_off + m) * ss_ld + p] (p < ss_n, ss_ld a multiple of 4).  Thread t loads the 4-vectors
+// t + k * NT, k < kSS4, unconditionally (surplus loads read the first vector again) before the weight
+// stream starts, and stores their sums to s_ssp[t + k * NT] once they are needed.  Beyond kSS4 * NT
+// vectors the rows' sums are read from memory in the epilogue instead.
+constexpr int kSS4 = 4;
+template <int NT>
+struct SsPrefetch {
+  float4 v[kSS4];
+  bool fast;
+  DF_DEVICE void load(const GemmArgs &a) {
+    const int ss_q = a.ss_ld / 4;  // 4-vectors per row
+    fast = a.ss_in && a.M * ss_q <= kSS4 * NT;
+    if (!fast) return;
+    const float4 *base = reinterpret_cast<const float4 *>(a.ss_in + (size_t)a.row_off * a.ss_ld);
+#pragma unroll
+    for (int k = 0; k < kSS4; ++k) {
+      const int idx = threadIdx.x + k * NT;
+      v[k] = base[idx < a.M * ss_q ? idx : 0];
+    }
+  }
+  DF_DEVICE void store(const GemmArgs &a, float *s_ssp) const {
+    if (!fast) return;
+    const int ss_q = a.ss_ld / 4;
+#pragma unroll
+    for (int k = 0; k < kSS4; ++k) {
+      const int idx = threadIdx.x + k * NT;
+      if (idx < a.M * ss_q) {
+        const int p0 = (idx % ss_q) * 4;  // partials p0 .. p0 + 3 of row idx / ss_q
+        s_ssp[idx] = (p0 < a.ss_n ? v[k].x : 0.f) + (p0 + 1 < a.ss_n ? v[k].y : 0.f) + (p0 + 2 < a.ss_n ? v[k].z : 0.f) +
+                     (p0 + 3 < a.ss_n ? v[k].w : 0.f);
+      }
+    }
+  }
+};
+
+// 1 / rms of X row m of the deferred RMSNorm: the row's ss_n partial sums of squares added in a fixed
+// order (4-vector sums first, as prefetched into s_ssp, else read from memory the same way).
+DF_DEVICE float gemm_rstd(const GemmArgs &a, int m, bool ss_fast, const float *s_ssp) {
+  float tot = 0.f;
+  if (ss_fast) {
+    const int nq = (a.ss_n + 3) / 4;
+    for (int i = 0; i < nq; ++i) tot += s_ssp[m * (a.ss_ld / 4) + i];
+  } else {
+    for (int pp = 0; pp < a.ss_n; pp += 4) {
+      const float *q = a.ss_in + (size_t)(a.row_off + m) * a.ss_ld + pp;
+      tot += (q[0] + (pp + 1 < a.ss_n ? q[1] : 0.f)) + (pp + 2 < a.ss_n ? q[2] : 0.f) + (pp + 3 < a.ss_n ? q[3] : 0.f);
+    }
+  }
+  return 1.0f / sqrtf(tot / (float)a.norm_dim + a.eps);
+}
+
+// Epilogue of output tile c (K range `split`): lds[m * COLS + j] holds the tile's sums for rows m < M.
+// Every thread of the work-group calls it (EPI_RESID_NORM synchronises the work-group).
+template <typename T, int COLS, int NT>
+DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, const float *s_rstd) {
+  const int tid = threadIdx.x;
+  const int M = a.M;
+  const bool rs = a.ss_in != nullptr;
+  switch (a.epi) {
+    case EPI_STORE_F32:
+      for (int e = tid; e < M * COLS; e += NT) {
+        const int m = e / COLS, j = e % COLS;
+        a.out_f32[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
+      }
+      break;
+    case EPI_STORE_ACT:
+      for (int e = tid; e < M * COLS; e += NT) {
+        const int m = e / COLS, j = e % COLS;
+        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + COLS * c + j, lds[m * COLS + j]);
+      }
+      break;
+    case EPI_PARTIAL: {
+      float *o = a.out_f32 + (size_t)split * a.part_stride;
+      for (int e = tid; e < M * COLS; e += NT) {
+        const int m = e / COLS, j = e % COLS;
+        o[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
+      }
+      break;
+    }
+    case EPI_SWIGLU: {
+      constexpr int HC = COLS / 2;  // output columns of the tile: gate in [0, HC), up in [HC, COLS)
+      for (int e = tid; e < M * HC; e += NT) {
+        const int m = e / HC, j = e % HC;
+        const float r = rs ? s_rstd[m] : 1.f;
+        const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + HC + j] * r;
+        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
+      }
+      break;
+    }
+    case EPI_RESID_NORM:
+      if constexpr (COLS == 32) {
+        for (int e = tid; e < M * COLS; e += NT) {
+          const int m = e / COLS, j = e % COLS;
+          const int r = a.row_off + m, n = COLS * c + j;
+          float v = lds[m * COLS + j];
+          if (a.resid) {
+            const size_t idx = (size_t)r * a.ld_resid + n;
+            v += a.resid[idx];
+            a.resid[idx] = v;
+          }
+          if (a.feat) Elem<T>::store((T *)a.feat + (size_t)r * a.ld_feat + n, v);
+          const int jj = r % a.sel_stride - a.sel_offset;
+          if (jj >= 0 && jj < a.sel_take)
+            Elem<T>::store((T *)a.xg + (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
+          lds[m * COLS + j] = v * v;  // entry owned by this thread
+        }
+        __syncthreads();
+        if (tid < M) {
+          const int r = a.row_off + tid, jj = r % a.sel_stride - a.sel_offset;
+          if (jj >= 0 && jj < a.sel_take) {
+            float t = 0.f;
+            for (int j = 0; j < COLS; ++j) t += lds[tid * COLS + j];
+            a.ss_out[(size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ss_out_ld + c] = t;
+          }
+        }
+      }
+      break;
+  }
+}
 
 template <typename T, int MT, int CT, int NW, int PD, int XR>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
@@ -122,21 +249,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   unsigned char *wt = smem + wave * (COLS + XR) * ROWB;
   unsigned char *xt = wt + COLS * ROWB;
   const int nsup = Kc / SK;  // streamed super-steps; wave w takes w, w + NW, ...
-  // Deferred RMSNorm of the X rows: the partial sums of squares of row m sit at ss_in[(row_off + m) *
-  // ss_ld + p] (p < ss_n, ss_ld a multiple of 4).  Thread t loads the 4-vectors t + k * NT, k < kSS4
-  // (unconditionally; surplus loads read the first vector again), before the weight stream starts.
-  constexpr int kSS4 = 4;
-  const int ss_q = a.ss_ld / 4;  // 4-vectors per row
-  const bool ss_fast = a.ss_in && a.M * ss_q <= kSS4 * NT;
-  float4 ssv[kSS4];
-  if (ss_fast) {
-    const float4 *base = reinterpret_cast<const float4 *>(a.ss_in + (size_t)a.row_off * a.ss_ld);
-#pragma unroll
-    for (int k = 0; k < kSS4; ++k) {
-      const int idx = tid + k * NT;
-      ssv[k] = base[idx < a.M * ss_q ? idx : 0];
-    }
-  }
+  // Deferred RMSNorm of the X rows: their partial sums of squares are loaded before the weight stream.
+  SsPrefetch<NT> ssp;
+  ssp.load(a);
 
   // PD register buffers per wave: PD super-steps are in flight while one is consumed.  Loads past the
   // wave's last super-step are redirected to X's first 256 bytes (cache-resident, never consumed),
@@ -155,18 +270,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);  // keep buffer p's loads ahead of buffer p + 1's
     }
   }
-  if (ss_fast) {
-#pragma unroll
-    for (int k = 0; k < kSS4; ++k) {
-      const int idx = tid + k * NT;
-      if (idx < a.M * ss_q) {
-        const int p0 = (idx % ss_q) * 4;  // partials p0 .. p0 + 3 of row idx / ss_q
-        const float4 v = ssv[k];
-        s_ssp[idx] = (p0 < a.ss_n ? v.x : 0.f) + (p0 + 1 < a.ss_n ? v.y : 0.f) + (p0 + 2 < a.ss_n ? v.z : 0.f) +
-                     (p0 + 3 < a.ss_n ? v.w : 0.f);  // read after the reduction barrier below
-      }
-    }
-  }
+  ssp.store(a, s_ssp);
   for (int sup = wave; sup < nsup; sup += PD * NW) {
 #pragma unroll
     for (int p = 0; p < PD; ++p) {
@@ -229,82 +333,183 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     for (int w = 1; w < NW; ++w) v += lds[w * kEnt + e];
     lds[e] = v;  // entry e is read and written by this thread only
   }
-  if (a.ss_in && tid < a.M) {
-    float tot = 0.f;
-    if (ss_fast) {
-      const int nq = (a.ss_n + 3) / 4;
-      for (int i = 0; i < nq; ++i) tot += s_ssp[tid * ss_q + i];
-    } else {
-      for (int pp = 0; pp < a.ss_n; pp += 4) {  // same association as the fast path
-        const float *q = a.ss_in + (size_t)(a.row_off + tid) * a.ss_ld + pp;
-        tot += (q[0] + (pp + 1 < a.ss_n ? q[1] : 0.f)) + (pp + 2 < a.ss_n ? q[2] : 0.f) + (pp + 3 < a.ss_n ? q[3] : 0.f);
-      }
-    }
-    s_rstd[tid] = 1.0f / sqrtf(tot / (float)a.norm_dim + a.eps);
-  }
+  if (a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
   __syncthreads();
+  gemm_epilogue<T, COLS, NT>(a, c, split, lds, s_rstd);
+}
 
-  const int M = a.M;
-  const bool rs = a.ss_in != nullptr;
-  switch (a.epi) {
-    case EPI_STORE_F32:
-      for (int e = tid; e < M * COLS; e += NT) {
-        const int m = e / COLS, j = e % COLS;
-        a.out_f32[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
-      }
-      break;
-    case EPI_STORE_ACT:
-      for (int e = tid; e < M * COLS; e += NT) {
-        const int m = e / COLS, j = e % COLS;
-        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + COLS * c + j, lds[m * COLS + j]);
-      }
-      break;
-    case EPI_PARTIAL: {
-      float *o = a.out_f32 + (size_t)split * a.part_stride;
-      for (int e = tid; e < M * COLS; e += NT) {
-        const int m = e / COLS, j = e % COLS;
-        o[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
-      }
-      break;
+// Stream-K variant (M <= 16, ksplit 1, K a whole number of super-steps; 32-column tiles, 8 waves).
+// With one tile per work-group, projections whose tile count is not a multiple of the CU count leave
+// CUs idle while others stream (160 hidden-width tiles on 256 CUs).  Here the projection's items
+// (tile, super-step), numbered tile-major, are cut into equal contiguous ranges, one per work-group
+// and one work-group per CU.  A work-group walks its range tile by tile; its waves take interleaved
+// items and their register prefetch runs on across tile boundaries.  At the end of each tile the waves'
+// partial tiles are reduced through LDS.  A tile covered by one work-group gets its epilogue at once;
+// a tile shared by several (only a range's first and last tile can be) is finished by whichever
+// arrives last: the others write their partial tile through to memory (the finisher may sit on
+// another XCD) and count their arrival on the tile's counter; the finisher adds the partials in
+// work-group order -- a fixed order, so the result does not depend on who arrives last -- runs the
+// epilogue and zeroes the counter for the next launch.  No work-group ever waits for another.
+template <typename T, int XR>
+__global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
+  using F = Frag<T>;
+  constexpr int NW = 8, NT = NW * 64, CT = 2, COLS = 32;
+  static_assert(XR == 8 || XR == 16, "X staging rows");
+  constexpr int ROWB = 256 + 16;
+  constexpr int NQ = COLS / 4, NXQ = XR / 4;
+  constexpr int SK = 256 / sizeof(T);
+  constexpr int KS = SK / F::kStep;
+  constexpr int kEnt = 16 * COLS;  // == kSkTileElems
+  constexpr int kPer = (kEnt + NT - 1) / NT;
+  constexpr int kTileB = NW * (COLS + XR) * ROWB, kRedB = 2 * NW * kEnt * 4;
+  // staging tiles (wave-private), then two reduction buffers (alternating tiles), then the tile sums
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kTileB + kRedB + kEnt * 4];
+  __shared__ float s_ssp[kSS4 * NT], s_rstd[16];
+  __shared__ int s_last;
+  float *red = reinterpret_cast<float *>(smem + kTileB);
+  float *fin = red + 2 * NW * kEnt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  const int ntile = swiglu ? a.N / 16 : a.N / COLS;
+  const int nsup = a.K / SK, items = ntile * nsup;
+  const int p = blockIdx.x;
+  const int lo = p * per, hi = min(items, lo + per);
+
+  // weight rows of tile t: SWIGLU takes 16 gate rows and 16 up rows; otherwise 32 consecutive rows of
+  // the concatenated segments (each segment a whole number of tiles)
+  auto tile_base = [&](int t, const T *&w0, const T *&w1) {
+    if (swiglu) {
+      w0 = (const T *)a.seg[0].w + (size_t)(16 * t) * a.K;
+      w1 = (const T *)a.seg[1].w + (size_t)(16 * t) * a.K;
+      return;
     }
-    case EPI_SWIGLU: {
-      constexpr int HC = COLS / 2;  // output columns of the tile: gate in [0, HC), up in [HC, COLS)
-      for (int e = tid; e < M * HC; e += NT) {
-        const int m = e / HC, j = e % HC;
-        const float r = rs ? s_rstd[m] : 1.f;
-        const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + HC + j] * r;
-        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
-      }
-      break;
+    int r0 = COLS * t, si = 0;
+    while (si + 1 < a.nseg && r0 >= a.seg[si].n) {
+      r0 -= a.seg[si].n;
+      ++si;
     }
-    case EPI_RESID_NORM:
-      if constexpr (COLS == 32) {
-        for (int e = tid; e < M * COLS; e += NT) {
-          const int m = e / COLS, j = e % COLS;
-          const int r = a.row_off + m, n = COLS * c + j;
-          float v = lds[m * COLS + j];
-          if (a.resid) {
-            const size_t idx = (size_t)r * a.ld_resid + n;
-            v += a.resid[idx];
-            a.resid[idx] = v;
-          }
-          if (a.feat) Elem<T>::store((T *)a.feat + (size_t)r * a.ld_feat + n, v);
-          const int jj = r % a.sel_stride - a.sel_offset;
-          if (jj >= 0 && jj < a.sel_take)
-            Elem<T>::store((T *)a.xg + (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
-          lds[m * COLS + j] = v * v;  // entry owned by this thread
-        }
-        __syncthreads();
-        if (tid < M) {
-          const int r = a.row_off + tid, jj = r % a.sel_stride - a.sel_offset;
-          if (jj >= 0 && jj < a.sel_take) {
-            float t = 0.f;
-            for (int j = 0; j < COLS; ++j) t += lds[tid * COLS + j];
-            a.ss_out[(size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ss_out_ld + c] = t;
-          }
+    w0 = (const T *)a.seg[si].w + (size_t)r0 * a.K;
+    w1 = w0 + (size_t)16 * a.K;
+  };
+  // quad layout as in gemm_kernel: load q covers rows 4 (q % 4) .. + 3 of the tile's 16-row half q / 4
+  size_t qoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qoff[q] = (size_t)(4 * q + g) * a.K + r16 * F::kEPL;
+  const T *xrow[NXQ];
+#pragma unroll
+  for (int q = 0; q < NXQ; ++q) {
+    const int m = 4 * q + g;
+    xrow[q] = (const T *)a.x + (size_t)(m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
+  }
+  SsPrefetch<NT> ssp;
+  ssp.load(a);
+
+  unsigned char *wt = smem + wave * (COLS + XR) * ROWB;
+  unsigned char *xt = wt + COLS * ROWB;
+  const T *dummy = (const T *)a.x + r16 * F::kEPL;
+  // load cursor: item li = (tile lt, super-step ls); the use cursor ui trails it by one item
+  int li = lo + wave;
+  int lt = li / nsup, ls = li - lt * nsup;
+  int ui = li;
+  const T *w0, *w1;
+  tile_base(lt < ntile ? lt : 0, w0, w1);
+  u32x4 buf[NQ], bufx[NXQ];
+  auto issue = [&]() {
+    const bool ok = li < hi;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) buf[q] = ld16(ok ? (q < 4 ? w0 : w1) + qoff[q % 4] + (size_t)ls * SK : dummy);
+#pragma unroll
+    for (int q = 0; q < NXQ; ++q) bufx[q] = ld16(ok ? xrow[q] + (size_t)ls * SK : dummy);
+    li += NW;
+    ls += NW;
+    if (ls >= nsup) {
+      while (ls >= nsup) {
+        ls -= nsup;
+        ++lt;
+      }
+      if (lt < ntile) tile_base(lt, w0, w1);
+    }
+  };
+  issue();
+  ssp.store(a, s_ssp);  // read after the first tile's reduction barrier
+
+  int seg = 0;
+  for (int t = lo / nsup; t * nsup < hi; ++t, ++seg) {
+    const int seg_hi = min(hi, (t + 1) * nsup);
+    f32x4 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (; ui < seg_hi; ui += NW) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = buf[q];
+#pragma unroll
+      for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[q];
+      issue();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 xv = r16 < a.M
+                             ? *reinterpret_cast<const u32x4 *>(xt + (r16 < XR ? r16 : 0) * ROWB + ks * 64 + 16 * g)
+                             : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * ct + r16) * ROWB + ks * 64 + 16 * g);
+          F::mma(acc[ct], xv, wv);
         }
       }
-      break;
+    }
+    // C[m][n] of a wave's partial tile sits at lane (n % 16, 4 * (lane / 16) + r) of acc[n / 16]
+    float *rb = red + (seg & 1) * NW * kEnt;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = acc[ct][r];
+    __syncthreads();
+    if (seg == 0 && a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + i * NT;
+      v[i] = 0.f;
+      if (e < a.M * COLS)
+        for (int w = 0; w < NW; ++w) v[i] += rb[w * kEnt + e];
+    }
+    if (t * nsup < lo || (t + 1) * nsup > hi) {  // shared tile
+      const int q0 = (t * nsup) / per, q1 = ((t + 1) * nsup - 1) / per;
+      const int slot = t * nsup < lo ? 0 : 1;  // the range's first or last tile
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int e = tid + i * NT;
+        if (e < a.M * COLS)
+          __hip_atomic_store(&a.sk_part[((size_t)p * 2 + slot) * kEnt + e], v[i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(&a.sk_cnt[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == q1 - q0;
+      __syncthreads();
+      if (!s_last) continue;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int e = tid + i * NT;
+        if (e >= a.M * COLS) continue;
+        float tot = 0.f;
+        for (int q = q0; q <= q1; ++q)
+          tot += q == p ? v[i]
+                        : __hip_atomic_load(&a.sk_part[((size_t)q * 2 + (t * nsup < q * per ? 0 : 1)) * kEnt + e],
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[i] = tot;
+      }
+      if (tid == 0) __hip_atomic_store(&a.sk_cnt[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + i * NT;
+      if (e < kEnt) fin[e] = v[i];
+    }
+    __syncthreads();
+    gemm_epilogue<T, COLS, NT>(a, t, 0, fin, s_rstd);
   }
 }
 
@@ -412,12 +617,54 @@ int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems) {
   return split;
 }
 
+// Stream-K launch: only with the caller's scratch, for shapes the kernel covers, and by default for the
+// hidden-width (residual + norm) and SwiGLU projections, where it measured faster on MI355X at M = 8
+// (o 15.0 -> 13.8 us, down 37.6 -> 33.7 us, gate/up 72 -> 64 us); q/k/v (448 16-column tiles) and the
+// LM head (4748 tiles) stream as fast or faster with one tile per work-group.
+// DFLASH_GEMM_SK=0 turns it off, =1 uses it wherever the shape allows.
+static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
+  const int env = env_int("DFLASH_GEMM_SK", -1);  // read per launch: tests switch it
+  if (!a.sk_part || !a.sk_cnt || env == 0 || a.M < 1 || a.M > 16 || a.ksplit != 1) return 0;
+  const int sk = dtype == 0 ? 128 : 64;  // K elements per super-step
+  if (a.K < sk || a.K % sk) return 0;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  if (swiglu ? a.N % 16 : a.N % 32) return 0;
+  if (!swiglu)
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].n % 32) return 0;
+  if (env != 1 && a.epi != EPI_RESID_NORM && !swiglu) return 0;
+  const long ntile = swiglu ? a.N / 16 : a.N / 32;
+  if (ntile > a.sk_max_tiles) return 0;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const long items = ntile * (a.K / sk);
+  const long wg = std::min<long>(cus[dev], a.sk_max_wg);
+  if (wg < 1) return 0;
+  const long per = (items + wg - 1) / wg;
+  *n_wg = (int)((items + per - 1) / per);
+  return (int)per;
+}
+
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.ksplit < 1 || a.K % a.ksplit || (a.ksplit > 1 && a.epi != EPI_PARTIAL)) return hipErrorInvalidValue;
   if (a.epi == EPI_RESID_NORM && (a.N % 32 || a.sel_stride < 1 || !a.gain || !a.xg || !a.ss_out))
     return hipErrorInvalidValue;
   if (a.ss_in && (a.ss_n < 1 || a.norm_dim < 1 || a.ss_ld % 4 || a.ss_n > a.ss_ld)) return hipErrorInvalidValue;
   if (a.epi == EPI_RESID_NORM && a.N / 32 > a.ss_out_ld) return hipErrorInvalidValue;
+  int n_wg = 0;
+  if (const int per = sk_per(a, dtype, &n_wg)) {
+    const dim3 grid(n_wg), block(512);
+    if (dtype == 0) {
+      if (a.M <= 8) hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8>), grid, block, 0, s, e0, e1, 0, a, per);
+      else hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16>), grid, block, 0, s, e0, e1, 0, a, per);
+    } else {
+      if (a.M <= 8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8>), grid, block, 0, s, e0, e1, 0, a, per);
+      else hipExtLaunchKernelGGL((gemm_sk_kernel<float, 16>), grid, block, 0, s, e0, e1, 0, a, per);
+    }
+    return hipGetLastError();
+  }
   const TileCfg t = pick_tiles(a.epi, a.N, a.K);
   const int MT = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
   if (dtype == 0) {

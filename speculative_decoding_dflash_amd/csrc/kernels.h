@@ -50,7 +50,16 @@ struct GemmArgs {
   float *ss_out;
   int32_t ss_out_ld;
   int32_t sel_take, sel_stride, sel_offset;
+  // Optional stream-K scratch (null: one work-group per tile).  With it, M <= 16, ksplit 1 and K a
+  // whole number of 256-byte super-steps, the launcher may spread the projection's (tile, super-step)
+  // items evenly over one work-group per CU: sk_part holds 2 * kSkTileElems fp32 partial-tile entries
+  // per work-group (at most sk_max_wg work-groups), sk_cnt one arrival counter per tile (at most
+  // sk_max_tiles), zero before the launch and zero again after it.
+  float *sk_part;
+  int32_t *sk_cnt;
+  int32_t sk_max_wg, sk_max_tiles;
 };
+constexpr int kSkTileElems = 16 * 32;  // entries of one partial tile (16 rows x 32 columns)
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
@@ -170,11 +179,12 @@ struct AttnArgs {
   const float2 *rope;
   int32_t rope_rows;
   int32_t *counters;
-  // Host-known facts that shorten the kernel's dependent-load chain: the slot of every sequence, and
-  // abs_range = 1 when no sequence's key range starts after key 0 (causal calls, or drafter calls whose
-  // allocated context fits the window), so the block-table entries of a split are read up front.
-  int32_t seq_slot[64];
+  // Host-known facts that shorten the kernel's dependent-load chain: abs_range = 1 when no sequence's
+  // key range starts after key 0 (causal calls, or drafter calls whose allocated context fits the
+  // window), so the block-table entries of a split are read up front; the slot of every sequence.
+  // (Fields the kernel's prologue reads sit in the first 256 bytes; seq_slot follows.)
   int32_t abs_range;
+  int32_t seq_slot[64];
 };
 hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s);
 
