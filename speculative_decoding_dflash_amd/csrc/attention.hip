@@ -682,35 +682,62 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 }
 
 // out[row][head] = sum_s 2^{m_s - M} O_s / sum_s 2^{m_s - M} l_s  (splits in order; m in log2 units).
-// One work-group per (row, head): thread s reads split s's (m, l) in parallel; then each thread sums its
-// dimension over the splits with independent, unrolled loads.
+// One work-group per (row, head), thread d for dimension d.
 template <typename T>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows) {
-  __shared__ float sw[64];
-  __shared__ float s_L;
+  // Up to kR splits: every thread loads all (m, l) pairs (the same addresses across the work-group)
+  // and its dimension's partial outputs at once, so the merge waits for one round of loads.
+  constexpr int kR = 16;
   const int rh = blockIdx.x;  // row * q_heads + head
-  const int D = a.kvl.head_dim;
+  const int D = a.kvl.head_dim, ns = a.n_splits;
   const int row = rh / a.q_heads, head = rh % a.q_heads;
   const float NEG = -INFINITY;
-  const float *ml = a.part_ml + (size_t)rh * a.n_splits * 2;
+  const float *ml = a.part_ml + (size_t)rh * ns * 2;
+  const float *po = a.part_o + (size_t)rh * ns * D;
   const int tid = threadIdx.x;
-  const float ms = tid < a.n_splits ? ml[2 * tid] : NEG;
+  if (ns <= kR) {
+    const int dim = tid < D ? tid : 0;
+    float mv[kR], lv[kR], pv[kR];
+#pragma unroll
+    for (int s = 0; s < kR; ++s) {
+      const int sc = s < ns ? s : 0;  // loads stay unconditional
+      mv[s] = ml[2 * sc];
+      lv[s] = ml[2 * sc + 1];
+      pv[s] = po[(size_t)sc * D + dim];
+    }
+    float M = NEG;
+#pragma unroll
+    for (int s = 0; s < kR; ++s)
+      if (s < ns) M = fmaxf(M, mv[s]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int s = 0; s < kR; ++s)
+      if (s < ns) {
+        const float w = (mv[s] == NEG || M == NEG) ? 0.f : __builtin_amdgcn_exp2f(mv[s] - M);
+        L += w * lv[s];
+        O += w * pv[s];
+      }
+    if (tid < D) Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + tid, L > 0.f ? O / L : 0.f);
+    return;
+  }
+  __shared__ float sw[64];
+  __shared__ float s_L;
+  const float ms = tid < ns ? ml[2 * tid] : NEG;
   float M = ms;
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));  // wave 0 holds all splits
-  if (tid < 64) sw[tid] = (tid < a.n_splits && ms != NEG && M != NEG) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+  if (tid < 64) sw[tid] = (tid < ns && ms != NEG && M != NEG) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
   __syncthreads();
   if (tid == 0) {
     float L = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) L += sw[s] * ml[2 * s + 1];
+    for (int s = 0; s < ns; ++s) L += sw[s] * ml[2 * s + 1];
     s_L = L;
   }
   __syncthreads();
   const float L = s_L;
-  const float *po = a.part_o + (size_t)rh * a.n_splits * D;
   for (int dim = tid; dim < D; dim += blockDim.x) {
     float O = 0.f;
 #pragma unroll 8
-    for (int s = 0; s < a.n_splits; ++s) O += sw[s] * po[(size_t)s * D + dim];
+    for (int s = 0; s < ns; ++s) O += sw[s] * po[(size_t)s * D + dim];
     Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
   }
 }
