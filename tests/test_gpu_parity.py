@@ -143,18 +143,22 @@ def test_e2e_teacher_forced(name, mode):
         assert stream == ar
 
 
-@pytest.mark.parametrize("variant", ["separate_post", "last_arriver", "gemm_one_tile_per_wg", "gemm_stream_k_all"])
+@pytest.mark.parametrize("variant", ["separate_post", "last_arriver", "one_page_splits", "gemm_one_tile_per_wg",
+                                     "gemm_stream_k_all"])
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_e2e_kernel_variants(name, variant, monkeypatch):
     """The non-default kernel variants match the oracle like the defaults.  Attention (default: q / k / v
-    post-processed inside attention, splits merged by a second kernel): a separate post-processing
-    kernel; the in-kernel merge by the last split to finish.  Projections (default: stream-K for the
-    residual + norm and SwiGLU projections at M <= 16, one tile per work-group elsewhere): one tile per
-    work-group everywhere; stream-K wherever the shape allows (q/k/v, LM heads, drafter k/v too)."""
+    post-processed inside attention, ~9-page key splits merged by a second kernel): a separate
+    post-processing kernel; the in-kernel merge by the last split to finish; one-page splits (on the
+    small model with a 320-token prompt: more than 16 splits, the merge kernel's general path).
+    Projections (default: stream-K for the residual + norm and SwiGLU projections at M <= 16, one tile
+    per work-group elsewhere): one tile per work-group everywhere; stream-K wherever the shape allows
+    (q/k/v, LM heads, drafter k/v too)."""
     monkeypatch.setenv("DFLASH_ATTN_FUSED", "0" if variant == "separate_post" else "1")
     monkeypatch.setenv("DFLASH_ATTN_MERGE", "1" if variant == "last_arriver" else "0")
+    monkeypatch.setenv("DFLASH_ATTN_PPS", "1" if variant == "one_page_splits" else "0")
     monkeypatch.setenv("DFLASH_GEMM_SK", {"gemm_one_tile_per_wg": "0", "gemm_stream_k_all": "1"}.get(variant, "-1"))
-    cfg = CASES[name]()
+    cfg = small_short(prompt_len=320) if (variant, name) == ("one_page_splits", "small") else CASES[name]()
     log(f"[e2e kernel variant] {name} {variant}")
     W = sw.model_weights(cfg, gain_std=0.1)
     stream, rep, prompt = run_e2e(cfg, W, cfg.sampling, 24)
