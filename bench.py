@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per projection launch of the decode step, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # scaled by a plain 1 GiB copy (profiles/gemm_kernel_27b_conc1_traffic.txt), and the hash of the
 # kernel source they were taken on: a changed kernel reports null until the counters are retaken.
-GEMM_TRAFFIC = {"bytes_per_launch": 178703270, "gemm_src_sha256_16": "f2fd76198796102f"}
+GEMM_TRAFFIC = {"bytes_per_launch": 179171779, "gemm_src_sha256_16": "71ba38c64992b5d7"}
 
 
 def log(msg: str):
@@ -325,7 +325,7 @@ def main():
         "step_bytes": bytes_step,
         "ar_baseline": ar,
         "tau_sweep_planted_greedy": sweep,
-        "roofline": {"bound": "hbm", "kernel": "gemm_kernel (all projections of the step)",
+        "roofline": {"bound": "hbm", "kernel": "gemm_kernel + gemm_sk_kernel (all projections of the step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
