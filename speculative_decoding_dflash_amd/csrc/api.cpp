@@ -401,9 +401,10 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     // Decode-sized calls: the attention kernel post-processes q / k / v itself (one query tile per
     // work-group keeps that prologue short; 0.2 ms per 27B step faster on MI355X than a separate
     // post-processing launch).  DFLASH_ATTN_FUSED=0 selects the separate kernel.
-    // The fused kernel needs q_len <= 64 (one position per lane) and a 16-byte aligned q gain.
+    // The fused kernel needs q_len <= 16 (the block's keys form one LDS page) and a 16-byte aligned
+    // q gain.
     const char *fz = getenv("DFLASH_ATTN_FUSED");
-    fused = !(fz && atoi(fz) == 0) && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 64 &&
+    fused = !(fz && atoi(fz) == 0) && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 16 &&
             ((uintptr_t)w.q_norm & 15) == 0;
     if (!fused) {
       QkvPostArgs p = post_base(c, rows, R);

@@ -117,6 +117,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using F = AttnFrag<T, D>;
   __shared__ __attribute__((aligned(16))) float so[4][16][D + 4];  // rows 16-byte aligned
   __shared__ float sm[4][NQT * 16], sl[4][NQT * 16];
+  // fused calls: the block's own keys as one page (K [16][D], V [D][16]), built here from raw k / v
+  __shared__ __attribute__((aligned(16))) T s_bk[FUSED ? 16 * D : 1], s_bv[FUSED ? D * 16 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   {
     // Touch the argument block's first four 64-byte lines together: each first touch misses the
@@ -148,6 +150,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // scores are kept in log2 units (scaled by log2 e), so that every exponential is one v_exp_f32
   const float scale = 1.4426950408889634f / sqrtf((float)D);
   const float NEG = -INFINITY;
+  int err_page = 0;  // raised at the end (see below)
 
   // The prologue is ordered so that no load waits behind loads it does not need (a wave's loads return
   // in issue order): (A) loads addressed by the arguments alone; (B) loads addressed by positions from
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int EPL = F::kEPL, SD = 4 * EPL, KH = F::kSteps / 2, KHS = KH > 0 ? KH : 1;
   constexpr int kWR = 2;  // block rows per wave (rows wave + 4 w) whose k / v loads are hoisted
   // A wave can have at most 63 vector memory instructions outstanding; (A) issues ~30 (fused), so
-  // none of it waits for an earlier load to return.  Fused calls (q_len <= 64, checked by the host)
+  // none of it waits for an earlier load to return.  Fused calls (q_len <= 16, checked by the host)
   // read every block position once, lane j holding row j's, and share it by lane exchange.
 
   // (A) block-table entries of the split's pages when its key range is known on the host (lane i: the
@@ -241,6 +244,35 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       w_v[w][1] = vr[wi + D / 2];
     }
   }
+  // (C, split range known up front) the wave's first two pool pages, which need only their
+  // block-table entries: entries past the sequence's pages are -1 (loads of a dummy block) and pages
+  // past the key range are loaded but never used.  Fused calls never read the block's own keys from
+  // the pool (they come from LDS, below), so no page has to wait for this call's K/V writes.
+  const T *kvb = (const T *)a.kv;
+  const T *dummy = kvb;
+  u32x4 kf[2][F::kSteps];
+  typename F::VF vf[2][D / 16];
+  auto ring_loads = [&](int bts) {  // bts: lane p holds page p's block-table entry (-1: none)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int pg = __builtin_amdgcn_readlane(bts, p);
+      F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
+      F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
+    }
+  };
+  // Unconditional (dummy blocks when the range is not known up front), like every global access up to
+  // the page loop: a wave's outstanding-load count must be the same on every path, or later waits
+  // fall back to waiting for everything, the K/V pages included.  For the same reason the kernel's
+  // conditional global writes (the block's K/V to the pool, error flags) are issued at its end.
+  ring_loads(pre ? pre_bt : -1);
+  if constexpr (FUSED) {  // zero the LDS block page rows this wave owns (rows j = wave mod 4)
+    for (int j = wave; j < 16; j += 4)
+      for (int d = lane; d < D; d += 64) {
+        Elem<T>::store(&s_bk[j * D + d], 0.f);
+        Elem<T>::store(&s_bv[d * 16 + j], 0.f);
+      }
+  }
+
   int w_pos[kWR], w_val[kWR];
   if constexpr (FUSED) {  // positions from the block's lanes (waits for (A)'s first loads)
     first_pos_v = __builtin_amdgcn_readlane(bl_pos, p0);
@@ -283,15 +315,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 
   __builtin_amdgcn_sched_barrier(0);
-  // (C) the wave's first two pages.  With the split's pages known up front they need no position:
-  // entries past the sequence's pages are -1 (loads of a dummy block) and pages past the key range are
-  // loaded but never used.  Fused calls load pages holding a position at or after the lowest valid
-  // block row's only after writing the block's keys there.
-  // A block's rows hold consecutive positions, valid rows first (as the row preparation writes them),
-  // so the lowest valid position is row 0's when row 0 is valid.
-  int blk_lo = 0x7fffffff;
+  // A block's rows hold consecutive positions, valid rows first (as the row preparation writes them):
+  // the block's keys are positions [blk_lo, blk_lo + n_valid).
+  int blk_lo = 0x7fffffff, n_valid = 0;
   if constexpr (FUSED) {
-    if (__builtin_amdgcn_readlane(bl_val, 0)) blk_lo = __builtin_amdgcn_readlane(bl_pos, 0);
+    n_valid = __popcll(__ballot(lane < a.q_len && bl_val));
+    if (n_valid > 0) blk_lo = __builtin_amdgcn_readlane(bl_pos, 0);
   }
   // key range of the split (uniform; read back into scalar registers)
   int klo, khi;
@@ -304,10 +333,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
   const int kbase = pre ? 0 : __builtin_amdgcn_readfirstlane((klo / pt) * pt);  // 0 whenever pre holds
   const int kstart = kbase + split * a.split_tokens;
-  const T *kvb = (const T *)a.kv;
-  const T *dummy = kvb;
-  u32x4 kf[2][F::kSteps];
-  typename F::VF vf[2][D / 16];
   // Wave w takes the split's pages w, w + 4, ..., in chunks of 64: lane i holds the block-table entry
   // of the chunk's page i (read once per chunk), and two pages' K/V fragments are in flight while one
   // is consumed.  Loads past the chunk's last page read a valid dummy block (the pool's first), so
@@ -326,30 +351,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int npg = kstop > kstart ? (kstop - kstart + pt - 1) / pt : 0;
     n_all = wave < npg ? (npg - wave + 3) / 4 : 0;
   };
-  bool late[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) late[p] = FUSED && kstart + (wave + 4 * p + 1) * pt > blk_lo;
-  auto ring_loads = [&](int bts) {  // bts: lane p holds page p's block-table entry (-1: none)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int pg = __builtin_amdgcn_readlane(bts, p);
-      F::load_k(kf[p], pg >= 0 && !late[p] ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
-      F::load_v(vf[p], pg >= 0 && !late[p] ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
-    }
-  };
-  // Both branches issue their loads inside, so that neither path's wait covers the other's loads.
-  int kstop = 0, n_all = 0, n_my = 0, my_bt = -1;
-  if (pre) {
-    my_bt = pre_bt;  // -1 past the wave's pages
-    ring_loads(pre_bt);
-    page_range(kstop, n_all);
-    n_my = min(64, n_all);
-  } else {
-    page_range(kstop, n_all);
-    n_my = min(64, n_all);
-    my_bt = chunk_bt(0, n_my);  // -1 past n_my
-    ring_loads(my_bt);
-  }
+  int kstop = 0, n_all = 0;
+  page_range(kstop, n_all);
+  int n_my = min(64, n_all), my_bt = pre_bt;  // pre: -1 past the wave's pages, its pages in flight
   const int first_pos = first_pos_v;
   const int nblk = nblk_v;
 
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
       const int pos = qpos[t];
-      if (!(pos >= 0 && pos < a.rope_rows) && qok[t] && g == 0) raise_err(a.err, ERR_PAGE);
+      err_page |= !(pos >= 0 && pos < a.rope_rows) && qok[t];
       float(&v)[F::kSteps][EPL] = qraw[t];
       float ss = 0.f;
 #pragma unroll
@@ -422,60 +426,102 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
+  auto pool_row = [&](int pos, int page, float k1, float k2, float v1, float v2) {
+    if (lane < D / 2) {
+      const int tok = pos % pt;
+      T *kd = (T *)a.kv + a.kvl.k_index(page, kh, tok, 0);
+      T *vd = (T *)a.kv + a.kvl.v_index(page, kh, tok, 0);
+      Elem<T>::store(kd + wi, k1);
+      Elem<T>::store(kd + wi + D / 2, k2);
+      Elem<T>::store(vd + (size_t)wi * pt, v1);
+      Elem<T>::store(vd + (size_t)(wi + D / 2) * pt, v2);
+    }
+  };
+  bool w_do[kWR] = {};  // hoisted block rows whose K/V go to the pool at the end
   if constexpr (FUSED) {
-    // The block's own keys that fall in this split: RMSNorm (k_gain) + RoPE of k, then k and v to the
-    // pool (wave j % 4 takes block row j).  Every query tile's work-group of the split writes the same
-    // values, so each reads back keys it wrote itself.
-    auto write_row = [&](int pos, int page, float k1, float k2, float v1, float v2, float2 cs) {
+    // The block's own keys that fall in this split: RMSNorm (k_gain) + RoPE of k; k and v go to the
+    // LDS page now and to the pool at the end (wave j % 4 takes block row j).  Every query tile's
+    // work-group of the split writes the same values to the pool.
+    auto norm_rope = [&](float &k1, float &k2, float2 cs) {
       float ss = lane < D / 2 ? k1 * k1 + k2 * k2 : 0.f;
       for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
       const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-      k1 = k1 * r * kg[0];
-      k2 = k2 * r * kg[1];
-      const float o1 = k1 * cs.x - k2 * cs.y, o2 = k2 * cs.x + k1 * cs.y;
+      const float n1 = k1 * r * kg[0], n2 = k2 * r * kg[1];
+      k1 = n1 * cs.x - n2 * cs.y;
+      k2 = n2 * cs.x + n1 * cs.y;
+    };
+    auto lds_row = [&](int j, float k1, float k2, float v1, float v2) {
       if (lane < D / 2) {
-        const int tok = pos % pt;
-        T *kd = (T *)a.kv + a.kvl.k_index(page, kh, tok, 0);
-        T *vd = (T *)a.kv + a.kvl.v_index(page, kh, tok, 0);
-        Elem<T>::store(kd + wi, o1);
-        Elem<T>::store(kd + wi + D / 2, o2);
-        Elem<T>::store(vd + (size_t)wi * pt, v1);
-        Elem<T>::store(vd + (size_t)(wi + D / 2) * pt, v2);
+        Elem<T>::store(&s_bk[j * D + wi], k1);
+        Elem<T>::store(&s_bk[j * D + wi + D / 2], k2);
+        Elem<T>::store(&s_bv[wi * 16 + j], v1);
+        Elem<T>::store(&s_bv[(wi + D / 2) * 16 + j], v2);
       }
     };
 #pragma unroll
     for (int w = 0; w < kWR; ++w) {
       const int pos = w_pos[w];
-      if (!w_val[w] || pos < kstart || pos >= kstop) continue;  // wave-uniform
-      if (w_page[w] < 0) {
-        if (lane == 0) raise_err(a.err, ERR_PAGE);
-        continue;
-      }
-      write_row(pos, w_page[w], w_k[w][0], w_k[w][1], w_v[w][0], w_v[w][1], w_cs[w]);
+      w_do[w] = w_val[w] && pos >= kstart && pos < kstop;  // wave-uniform
+      if (!w_do[w]) continue;
+      norm_rope(w_k[w][0], w_k[w][1], w_cs[w]);
+      lds_row(wave + 4 * w, w_k[w][0], w_k[w][1], w_v[w][0], w_v[w][1]);
+      err_page |= w_page[w] < 0;
+      w_do[w] = w_page[w] >= 0;
     }
-    for (int j = wave + 4 * kWR; j < a.q_len; j += 4) {  // rows beyond the hoisted ones
+    for (int j = wave + 4 * kWR; j < a.q_len; j += 4) {  // rows beyond the hoisted ones (q_len > 8)
       const int row = b * a.q_len + j, pos = a.rows.pos[row];
       if (!a.rows.valid[row] || pos < kstart || pos >= kstop) continue;  // wave-uniform
       const int pidx = pos / pt;
       const int page = (pidx < a.bt_stride && pos < a.rope_rows) ? bt[pidx] : -1;
-      if (page < 0) {
-        if (lane == 0) raise_err(a.err, ERR_PAGE);
-        continue;
-      }
       const float *kr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kh) * D;
       const float *vr = a.raw + (size_t)row * a.ld_raw + (size_t)(a.q_heads + kvh + kh) * D;
-      write_row(pos, page, kr[wi], kr[wi + D / 2], vr[wi], vr[wi + D / 2], a.rope[(size_t)pos * (D / 2) + wi]);
+      float k1 = kr[wi], k2 = kr[wi + D / 2];
+      const float v1 = vr[wi], v2 = vr[wi + D / 2];
+      norm_rope(k1, k2, a.rope[(size_t)(page >= 0 ? pos : 0) * (D / 2) + wi]);
+      lds_row(j, k1, k2, v1, v2);
+      if (page < 0) err_page = 1;
+      else pool_row(pos, page, k1, k2, v1, v2);
     }
-    __syncthreads();  // the block's keys are in the pool before any wave reads its pages
   }
 
+  // One page of 16 keys starting at position ps: scores, online softmax, P V.  Keys outside
+  // [lo, hi) of a query vector, or outside [klim_lo, klim_hi), are masked.
+  auto consume = [&](const u32x4 *kfp, const typename F::VF *vfp, int ps, int klim_lo, int klim_hi) {
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
-    if (late[p]) {  // wave-uniform
-      const int pg = p < n_my ? __builtin_amdgcn_readlane(my_bt, p) : -1;
-      F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
-      F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
+    for (int t = 0; t < NQT; ++t) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      F::qk(s, kfp, q[t]);  // lane holds S^T[key = 4g + r][qv = l16]
+      float sv[4], mx = NEG;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = ps + 4 * g + r;
+        sv[r] = (kp >= lo[t] && kp < hi[t] && kp >= klim_lo && kp < klim_hi) ? s[r] * scale : NEG;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[t], mx);
+      const float mb = (mn == NEG) ? 0.f : mn;  // exp2(-inf - mb) = 0 for masked keys
+      const float corr = __builtin_amdgcn_exp2f(m[t] - mb);
+      float pr[4], ps_sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(sv[r] - mb);
+        ps_sum += pr[r];
+      }
+      l[t] = l[t] * corr + ps_sum;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
+      F::pv(o[t], vfp, pr);
+      m[t] = mn;
     }
+  };
+  if (!pre) {  // the first chunk's pages, now that the key range is known
+    my_bt = chunk_bt(0, n_my);
+    ring_loads(my_bt);
+  }
+  // pool keys: all but the block's own (fused calls take those from LDS)
+  const int pool_hi = FUSED ? blk_lo : 0x7fffffff;
   for (int c0 = 0; c0 < n_all; c0 += 64) {
     if (c0 > 0) {
       n_my = min(64, n_all - c0);
@@ -493,44 +539,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int ii = i0 + p;
         if (ii < n_my) {  // wave-uniform
           const int ps = kstart + (wave + 4 * (c0 + ii)) * pt;
-          if (__builtin_amdgcn_readlane(my_bt, ii) < 0) {
-            if (lane == 0) raise_err(a.err, ERR_PAGE);
-          } else {
-#pragma unroll
-            for (int t = 0; t < NQT; ++t) {
-              f32x4 s = {0.f, 0.f, 0.f, 0.f};
-              F::qk(s, kf[p], q[t]);  // lane holds S^T[key = 4g + r][qv = l16]
-              float sv[4], mx = NEG;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int kp = ps + 4 * g + r;
-                sv[r] = (kp >= lo[t] && kp < hi[t]) ? s[r] * scale : NEG;
-                mx = fmaxf(mx, sv[r]);
-              }
-              mx = fmaxf(mx, __shfl_xor(mx, 16));
-              mx = fmaxf(mx, __shfl_xor(mx, 32));
-              const float mn = fmaxf(m[t], mx);
-              const float mb = (mn == NEG) ? 0.f : mn;  // exp2(-inf - mb) = 0 for masked keys
-              const float corr = __builtin_amdgcn_exp2f(m[t] - mb);
-              float pr[4], ps_sum = 0.f;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                pr[r] = __builtin_amdgcn_exp2f(sv[r] - mb);
-                ps_sum += pr[r];
-              }
-              l[t] = l[t] * corr + ps_sum;
-#pragma unroll
-              for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
-              F::pv(o[t], vf[p], pr);
-              m[t] = mn;
-            }
-          }
+          if (__builtin_amdgcn_readlane(my_bt, ii) < 0) err_page = 1;
+          else consume(kf[p], vf[p], ps, 0, pool_hi);
         }
         const int nx = ii + 2;
         const int pg = nx < n_my ? __builtin_amdgcn_readlane(my_bt, nx) : -1;
         F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
         F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
       }
+    }
+  }
+
+  if constexpr (FUSED) {
+    // the block's own keys in this split, [max(blk_lo, kstart), min(blk_lo + n_valid, kstop)), from
+    // the LDS page, by the wave with the fewest pool pages (wave 3)
+    __syncthreads();
+    const int b_lo = max(blk_lo, kstart), b_hi = min(blk_lo + n_valid, kstop);
+    if (wave == 3 && b_lo < b_hi) {
+      u32x4 kfb[F::kSteps];
+      typename F::VF vfb[D / 16];
+      F::load_k(kfb, s_bk, l16, g);
+      F::load_v(vfb, s_bv, l16, g);
+      consume(kfb, vfb, blk_lo, b_lo, b_hi);
     }
   }
 
@@ -605,6 +635,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int w = 0; w < kWR; ++w)
+      if (w_do[w]) pool_row(w_pos[w], w_page[w], w_k[w][0], w_k[w][1], w_v[w][0], w_v[w][1]);
+  }
+  if (err_page) raise_err(a.err, ERR_PAGE);
   if (!a.counters || a.n_splits == 1) return;
 
   // Last-arriver merge of the splits of (sequence b, KV head kh).  Every thread's partial stores have
