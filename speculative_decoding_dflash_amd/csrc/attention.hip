@@ -51,6 +51,12 @@ template <int D> struct AttnFrag<bf16, D> {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, q[ks]),
                                                     acc, 0, 0, 0);
   }
+  // element i (key 4g + i) of a V fragment, as raw bits
+  static DF_DEVICE void set_v(VF &v, int i, uint32_t bits) {
+    const int w = i >> 1, sh = (i & 1) * 16;
+    v[w] = (v[w] & ~(0xFFFFu << sh)) | (bits << sh);
+  }
+  static DF_DEVICE uint32_t raw(const bf16 &e) { return e.bits; }
   // p[r]: probability of key 4g + r for this lane's qv.
   static DF_DEVICE void pv(f32x4 *o, const VF *vf, const float *p) {
     s16x4 pb;
@@ -94,6 +100,8 @@ template <int D> struct AttnFrag<float, D> {
       for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k[j], qf[j], acc, 0, 0, 0);
     }
   }
+  static DF_DEVICE void set_v(VF &v, int i, uint32_t bits) { v[i] = bits; }
+  static DF_DEVICE uint32_t raw(const float &e) { return __builtin_bit_cast(uint32_t, e); }
   static DF_DEVICE void pv(f32x4 *o, const VF *vf, const float *p) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using F = AttnFrag<T, D>;
   __shared__ __attribute__((aligned(16))) float so[4][16][D + 4];  // rows 16-byte aligned
   __shared__ float sm[4][NQT * 16], sl[4][NQT * 16];
-  // fused calls: the block's own keys as one page (K [16][D], V [D][16]), built here from raw k / v
+  // fused calls: the block's own keys (K [16][D], V [D][16], row j = block row j), built here from raw k / v
   __shared__ __attribute__((aligned(16))) T s_bk[FUSED ? 16 * D : 1], s_bv[FUSED ? D * 16 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   {
@@ -246,8 +254,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
   // (C, split range known up front) the wave's first two pool pages, which need only their
   // block-table entries: entries past the sequence's pages are -1 (loads of a dummy block) and pages
-  // past the key range are loaded but never used.  Fused calls never read the block's own keys from
-  // the pool (they come from LDS, below), so no page has to wait for this call's K/V writes.
+  // past the key range are loaded but never used.  Fused calls take the block's own keys from an LDS
+  // copy (see `patch`), so no page has to wait for this call's K/V writes.
   const T *kvb = (const T *)a.kv;
   const T *dummy = kvb;
   u32x4 kf[2][F::kSteps];
@@ -482,6 +490,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       if (page < 0) err_page = 1;
       else pool_row(pos, page, k1, k2, v1, v2);
     }
+    __syncthreads();  // the LDS page is complete before any wave patches its fragments from it
   }
 
   // One page of 16 keys starting at position ps: scores, online softmax, P V.  Keys outside
@@ -520,8 +529,26 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     my_bt = chunk_bt(0, n_my);
     ring_loads(my_bt);
   }
-  // pool keys: all but the block's own (fused calls take those from LDS)
-  const int pool_hi = FUSED ? blk_lo : 0x7fffffff;
+  // Fused calls: a pool page holding block keys gets those keys' K/V from the LDS page (this call's
+  // pool writes are not yet visible, and need not be); every key keeps its page, wave and position in
+  // the online softmax, so the arithmetic is that of an all-pool read.
+  auto patch = [&](u32x4 *kfp, typename F::VF *vfp, int ps) {
+    const int off = ps - blk_lo;  // LDS row of the page's key 0
+    const int jk = off + l16;     // this lane's K row
+    const bool kin = jk >= 0 && jk < 16;
+    u32x4 kt[F::kSteps];
+    F::load_k(kt, s_bk, kin ? jk : 0, g);
+#pragma unroll
+    for (int ks = 0; ks < F::kSteps; ++ks)
+      if (kin) kfp[ks] = kt[ks];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jv = off + 4 * g + i;
+        if (jv >= 0 && jv < 16) F::set_v(vfp[dt], i, F::raw(s_bv[(dt * 16 + l16) * 16 + jv]));
+      }
+  };
   for (int c0 = 0; c0 < n_all; c0 += 64) {
     if (c0 > 0) {
       n_my = min(64, n_all - c0);
@@ -539,28 +566,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int ii = i0 + p;
         if (ii < n_my) {  // wave-uniform
           const int ps = kstart + (wave + 4 * (c0 + ii)) * pt;
-          if (__builtin_amdgcn_readlane(my_bt, ii) < 0) err_page = 1;
-          else consume(kf[p], vf[p], ps, 0, pool_hi);
+          if (__builtin_amdgcn_readlane(my_bt, ii) < 0) {
+            err_page = 1;
+          } else {
+            if (FUSED && ps + pt > blk_lo && ps < blk_lo + 16) patch(kf[p], vf[p], ps);  // wave-uniform
+            consume(kf[p], vf[p], ps, 0, 0x7fffffff);
+          }
         }
         const int nx = ii + 2;
         const int pg = nx < n_my ? __builtin_amdgcn_readlane(my_bt, nx) : -1;
         F::load_k(kf[p], pg >= 0 ? kvb + a.kvl.block(pg, 0, kh) : dummy, l16, g);
         F::load_v(vf[p], pg >= 0 ? kvb + a.kvl.block(pg, 1, kh) : dummy, l16, g);
       }
-    }
-  }
-
-  if constexpr (FUSED) {
-    // the block's own keys in this split, [max(blk_lo, kstart), min(blk_lo + n_valid, kstop)), from
-    // the LDS page, by the wave with the fewest pool pages (wave 3)
-    __syncthreads();
-    const int b_lo = max(blk_lo, kstart), b_hi = min(blk_lo + n_valid, kstop);
-    if (wave == 3 && b_lo < b_hi) {
-      u32x4 kfb[F::kSteps];
-      typename F::VF vfb[D / 16];
-      F::load_k(kfb, s_bk, l16, g);
-      F::load_v(vfb, s_bv, l16, g);
-      consume(kfb, vfb, blk_lo, b_lo, b_hi);
     }
   }
 
