@@ -28,10 +28,26 @@ Sources: see oracle/ops.py for the [P1]/[P2]/[P3] keys.
   decided.  u_acc = (word0 >> 40) * 2^-24 and u_smp = (word1 >> 40) * 2^-24,
   both exact in float32 and in [0, 1).
 
+* Stochastic drafts (the general rejection-sampling rule behind [P1]'s
+  cost-model sentence on rejection sampling; the deterministic rule above is
+  its special case): a draft drawn from the drafter's own filtered
+  distribution q is accepted with probability min(1, p(x)/q(x)), taken in
+  float32 as u_acc * q(x) < p(x); a rejected position is drawn from
+  max(0, p - q) renormalised, over p's candidates in their order.  Reading
+  where the pages are silent: the draft for position t is drawn from q by
+  inverse CDF with the uniform u_draft = top 24 bits of word 0 of Philox
+  counter (t, request, 1, 0) (stream 1; the target's decisions use stream 0),
+  and q uses the request's own temperature / top-k / top-p.  With q a point
+  mass at the draft, decide_q takes exactly decide's decisions.
+
 Pins: tests/test_oracle_sampling.py -- Philox against numpy.random.Philox;
 the filter against a brute-force sort and scipy's softmax; the rule's
 accept rate (binomial z-test) and resample law (chi-square) against the
-closed forms; greedy and B = 1 special cases.
+closed forms; greedy and B = 1 special cases; for stochastic drafts the
+closed-form law (output marginal p, acceptance sum_x min(p, q)), a
+Monte-Carlo chi-square of the float32 rule, and bit-equality with decide
+when q is a point mass.  tests/test_oracle_spec.py enumerates the whole
+loop's law with stochastic drafts against plain decoding.
 """
 from __future__ import annotations
 
@@ -153,6 +169,79 @@ def decide(rows: List[Tuple[np.ndarray, np.ndarray]], drafts: Sequence[int], n: 
     ids, p = rows[len(drafts)]
     _, u_smp = uniforms(seed, n + len(drafts) + 1, request)
     out.append(inverse_cdf(ids, p, u_smp, exclude=None))
+    return out
+
+
+def sample_draft(ids: np.ndarray, q: np.ndarray, seed: int, t: int, request: int) -> int:
+    """The draft for position t drawn from q (candidates ids, q) with u_draft of Philox stream 1."""
+    u, _ = uniforms(seed, t, request, stream=1)
+    return inverse_cdf(ids, q, u, exclude=None)
+
+
+def residual(ids: np.ndarray, p: np.ndarray, qids: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """max(0, p - q) on p's candidates (float32, in p's candidate order)."""
+    r = np.zeros(len(ids), dtype=np.float32)
+    for j, y in enumerate(ids):
+        d = F32(F32(p[j]) - prob_of(qids, q, int(y)))
+        r[j] = d if d > F32(0.0) else F32(0.0)
+    return r
+
+
+def decide_q(rows: List[Tuple[np.ndarray, np.ndarray]], qrows: List[Tuple[np.ndarray, np.ndarray]],
+             drafts: Sequence[int], n: int, seed: int, request: int) -> List[int]:
+    """Accept / resample one verified block whose drafts were drawn from qrows[i-1] (float32 rule).
+
+    Draft d_i is accepted iff u_acc * q(d_i) < p(d_i); at the first rejection the token is drawn by
+    inverse CDF (u_smp) from max(0, p - q) over p's candidates, or from p itself should that residual
+    vanish; after all accepts the bonus is drawn from the last row, as in ``decide``.
+    """
+    out: List[int] = []
+    for i, d in enumerate(drafts, start=1):
+        ids, p = rows[i - 1]
+        qids, q = qrows[i - 1]
+        u_acc, u_smp = uniforms(seed, n + i, request)
+        if F32(u_acc * prob_of(qids, q, d)) < prob_of(ids, p, d):
+            out.append(int(d))
+            continue
+        r = residual(ids, p, qids, q)
+        out.append(inverse_cdf(ids, r, u_smp, exclude=None) if seq_sum(r) > F32(0.0)
+                   else inverse_cdf(ids, p, u_smp, exclude=None))
+        return out
+    ids, p = rows[len(drafts)]
+    _, u_smp = uniforms(seed, n + len(drafts) + 1, request)
+    out.append(inverse_cdf(ids, p, u_smp, exclude=None))
+    return out
+
+
+def decide_q_law(rows: List[Tuple[np.ndarray, np.ndarray]], qrows: List[Tuple[np.ndarray, np.ndarray]],
+                 drafts: Sequence[int]) -> List[Tuple[List[int], float]]:
+    """Exact law (float64) of ``decide_q``'s output for fixed drafts: accept d_i with probability
+    min(1, p(d_i) / q(d_i)); on rejection emit y with probability max(0, p(y) - q(y)) / sum of those."""
+    out: List[Tuple[List[int], float]] = []
+    acc = 1.0
+    prefix: List[int] = []
+    for i, d in enumerate(drafts, start=1):
+        ids, p = rows[i - 1]
+        qids, q = qrows[i - 1]
+        p = np.asarray(p, dtype=np.float64)
+        q = np.asarray(q, dtype=np.float64)
+        pd = float(p[ids == d].sum())
+        qd = float(q[qids == d].sum())
+        a = 1.0 if qd <= pd else pd / qd
+        if a < 1.0:
+            r = np.array([max(0.0, float(py) - float(q[qids == y].sum())) for y, py in zip(ids, p)])
+            tot = r.sum()
+            for y, ry in zip(ids, r):
+                if ry > 0:
+                    out.append((prefix + [int(y)], acc * (1.0 - a) * ry / tot))
+        acc *= a
+        if acc == 0.0:
+            return out
+        prefix = prefix + [int(d)]
+    ids, p = rows[len(drafts)]
+    for y, py in zip(ids, np.asarray(p, dtype=np.float64)):
+        if py > 0:
+            out.append((prefix + [int(y)], acc * py))
     return out
 
 

@@ -19,11 +19,17 @@ features into the drafter.  The prompt is handled as a step whose block is
 the whole prompt with no drafts.  The first generated token counts toward
 max_new.
 
+With stochastic drafts (``stochastic=True``) each draft is drawn from the
+drafter's own filtered distribution at its position (see sampling.decide_q);
+the drafter's B-1 rows come from the same single forward, so the rows do not
+depend on the drafts drawn before them.
+
 Pins: greedy speculative output equals greedy autoregressive output token for
 token ([P3] section "先说结论"); with B = 1 sampled speculative output equals
 sampled autoregressive output bit for bit; exact enumeration of both output
-laws on tiny models agrees to 1e-12 (the lossless claim of [P1] and [P3]);
-the planted-drafter mean acceptance length matches its closed form.
+laws on tiny models agrees to 1e-12 (the lossless claim of [P1] and [P3]),
+with deterministic and with stochastic drafts; the planted-drafter mean
+acceptance length matches its closed form.
 """
 from __future__ import annotations
 
@@ -34,7 +40,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 from .model import Drafter, KVCache, Target
-from .sampling import decide, decide_law, sample_dist, sample_dist64
+from .sampling import decide, decide_law, decide_q, decide_q_law, sample_dist, sample_dist64, sample_draft
 
 
 @dataclass
@@ -67,12 +73,14 @@ class SpecDecoder:
     """Draft -> verify -> accept/resample, one sequence at a time."""
 
     def __init__(self, target: Target, drafter: Optional[Drafter], block_size: int, sampling: Sampling,
-                 request: int = 0):
+                 request: int = 0, stochastic: bool = False):
         self.target = target
         self.drafter = drafter
         self.B = block_size
         self.sp = sampling
         self.request = request
+        self.stochastic = stochastic
+        self.last_q = None  # the drafter's candidate distributions of the last stochastic block
 
     # -- one step, split so the law enumeration can branch between verify and commit
     def new_state(self) -> SeqState:
@@ -85,9 +93,17 @@ class SpecDecoder:
             return [int(t) for t in prompt], []
         if draft_fn is not None:
             drafts = [int(d) for d in draft_fn(st)]
+        elif self.stochastic:
+            self.last_q = self.draft_rows(st)
+            drafts = [sample_draft(ids, q, self.sp.seed, st.n + i, self.request)
+                      for i, (ids, q) in enumerate(self.last_q, start=1)]
         else:
             drafts = self.drafter.draft(st.dcache, st.anchor, st.n)
         return [st.anchor] + drafts, drafts
+
+    def draft_rows(self, st: SeqState, exact: bool = False):
+        """The drafter's filtered distributions q_1 .. q_{B-1} for the block at st.n."""
+        return self.rows(self.drafter.draft_logits(st.dcache, st.anchor, st.n), exact)
 
     def verify(self, st: SeqState, tokens: List[int], drafts: List[int]):
         """Target forward over the block; logits of the last len(drafts)+1 rows and all features."""
@@ -114,7 +130,10 @@ class SpecDecoder:
         tokens, drafts = self.block(st, prompt, draft_fn)
         logits, feats = self.verify(st, tokens, drafts)
         anchor_pos = st.n + len(tokens) - len(drafts) - 1
-        emitted = decide(self.rows(logits), drafts, anchor_pos, self.sp.seed, self.request)
+        if self.stochastic and drafts and draft_fn is None:
+            emitted = decide_q(self.rows(logits), self.last_q, drafts, anchor_pos, self.sp.seed, self.request)
+        else:
+            emitted = decide(self.rows(logits), drafts, anchor_pos, self.sp.seed, self.request)
         self.commit(st, tokens, drafts, emitted, feats)
         return emitted
 
@@ -177,6 +196,24 @@ def spec_law(dec: SpecDecoder, prompt: Sequence[int], k: int) -> Dict[Tuple[int,
     def rec(st: SeqState, prob: float, prompt_block: Optional[Sequence[int]]):
         if len(st.out) >= k:
             law[tuple(st.out[:k])] += prob
+            return
+        if dec.stochastic and prompt_block is None:
+            # branch on every draw of the drafts (each position from its own q) and then on every
+            # accept / reject outcome
+            qrows = dec.draft_rows(st, exact=True)
+            combos = [([], 1.0)]
+            for ids, q in qrows:
+                combos = [(ds + [int(y)], pr * float(qy)) for ds, pr in combos for y, qy in zip(ids, q) if qy > 0]
+            for drafts, pq in combos:
+                s1 = st.copy()
+                tokens = [s1.anchor] + drafts
+                logits, feats = dec.verify(s1, tokens, drafts)
+                for emitted, pe in decide_q_law(dec.rows(logits, exact=True), qrows, drafts):
+                    if pe <= 0.0:
+                        continue
+                    s2 = s1.copy()
+                    dec.commit(s2, tokens, drafts, emitted, feats)
+                    rec(s2, prob * pq * pe, None)
             return
         tokens, drafts = dec.block(st, prompt_block)
         logits, feats = dec.verify(st, tokens, drafts)

@@ -152,3 +152,76 @@ def test_inverse_cdf_extremes():
     assert S.inverse_cdf(ids, p, np.float32(0.0), None) == 3
     assert S.inverse_cdf(ids, p, np.float32(1 - 2 ** -24), None) == 1
     assert S.inverse_cdf(ids, p, np.float32(0.3), exclude=3) == 1
+
+
+# ---- stochastic drafts: accept min(1, p/q), resample from max(0, p - q)
+
+def test_decide_q_with_point_mass_q_equals_decide():
+    """q a point mass at the draft is the deterministic case: decide_q takes decide's decisions exactly."""
+    for t in range(400):
+        V = int(RNG.integers(3, 9))
+        nd = int(RNG.integers(1, 4))
+        rows = [_dist(V, zero_tail=int(RNG.integers(0, 2)))[:2] for _ in range(nd + 1)]
+        drafts = [int(RNG.integers(0, V)) for _ in range(nd)]
+        qrows = [(np.array([d]), np.array([1.0], np.float32)) for d in drafts]
+        assert S.decide_q(rows, qrows, drafts, 5 * t, 11, 2) == S.decide(rows, drafts, 5 * t, 11, 2)
+
+
+def test_decide_q_law_closed_form():
+    """Drawing the draft from q and applying the rule gives the target's p exactly; the draft is kept
+    with probability sum_x min(p(x), q(x))."""
+    for _ in range(20):
+        V = 7
+        ids, p32, p = _dist(V, zero_tail=1)
+        qids, q32, q = _dist(V, zero_tail=2)
+        bonus = _dist(V)[:2]
+        marg = np.zeros(V)
+        keep = 0.0
+        for x, qx in zip(qids, q32.astype(np.float64)):
+            for em, pr in S.decide_q_law([(ids, p32), bonus], [(qids, q32)], [int(x)]):
+                marg[em[0]] += qx * pr
+                if len(em) == 2:
+                    keep += qx * pr
+        p64 = np.zeros(V)
+        p64[ids] = p32
+        q64 = np.zeros(V)
+        q64[qids] = q32
+        assert np.abs(marg - p64 / p64.sum()).max() < 1e-6
+        assert abs(keep - np.minimum(p64, q64).sum()) < 1e-6
+
+
+@pytest.mark.parametrize("overlap", ["disjoint_tail", "shared"])
+def test_stochastic_draft_monte_carlo(overlap):
+    """The float32 rule with drafts drawn by sample_draft: the emitted token follows p (chi-square) and
+    the acceptance rate is sum_x min(p, q) (binomial z-test)."""
+    V = 8
+    ids, p32, p = _dist(V, zero_tail=2)
+    qids, q32, q = _dist(V, zero_tail=2 if overlap == "disjoint_tail" else 0)
+    pf = np.zeros(V)
+    pf[ids] = p32
+    qf = np.zeros(V)
+    qf[qids] = q32
+    bonus = (ids, p32)
+    N = 60000
+    first = np.zeros(V)
+    acc = 0
+    for t in range(N):
+        n = 10 * t
+        d = S.sample_draft(qids, q32, 7, n + 1, 3)
+        out = S.decide_q([(ids, p32), bonus], [(qids, q32)], [d], n, 7, 3)
+        first[out[0]] += 1
+        acc += len(out) == 2
+    a = float(np.minimum(pf, qf).sum())
+    z = (acc / N - a) / np.sqrt(a * (1 - a) / N)
+    assert abs(z) < 4.5, z
+    sup = pf > 0
+    assert first[~sup].sum() == 0
+    assert scipy.stats.chisquare(first[sup], pf[sup] / pf[sup].sum() * N).pvalue > 1e-4
+
+
+def test_sample_draft_uses_stream_one():
+    ids = np.array([2, 0, 1])
+    q = np.array([0.5, 0.25, 0.25], dtype=np.float32)
+    for t in range(50):
+        u, _ = S.uniforms(5, t, 1, stream=1)
+        assert S.sample_draft(ids, q, 5, t, 1) == S.inverse_cdf(ids, q, u, None)

@@ -189,3 +189,24 @@ def test_planted_drafter_mean_acceptance_closed_form(rate):
     expect = (1 - (1 - rate) ** B) / rate
     var = sum((2 * j + 1) * (1 - rate) ** j for j in range(B)) - expect ** 2
     assert abs(taus.mean() - expect) < 4.5 * np.sqrt(var / len(taus)), (taus.mean(), expect)
+
+
+@pytest.mark.parametrize("block", [2, 3])
+@pytest.mark.parametrize("sampling", [Sampling(1.0, 4, 0.9, 1), Sampling(0.8, 3, 1.0, 1)])
+def test_exact_law_equality_stochastic_drafts(block, sampling):
+    """Brute-force enumeration with stochastic drafts (every draw of every draft, then every accept /
+    reject outcome): the law of the first 4 tokens equals plain decoding's."""
+    cfg, tg, dr = micro_models(vocab=5, block=block)
+    prompt = [1, 3]
+    la = ar_law(tg, prompt, 4, sampling)
+    ls = spec_law(SpecDecoder(tg, dr, block, sampling, stochastic=True), prompt, 4)
+    assert abs(sum(ls.values()) - 1.0) < 1e-12
+    keys = set(la) | set(ls)
+    assert max(abs(la.get(x, 0.0) - ls.get(x, 0.0)) for x in keys) <= 1e-12
+
+
+def test_stochastic_loop_runs_and_emits_requested_length():
+    cfg, tg, dr = micro_models(block=3)
+    dec = SpecDecoder(tg, dr, 3, Sampling(1.0, 4, 0.9, 3), stochastic=True)
+    st = dec.generate([1, 3], 12)
+    assert len(st.out) == 12 and all(1 <= t <= 3 for t in st.taus)
