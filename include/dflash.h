@@ -199,6 +199,32 @@ dflash_status dflash_accept_resample(dflash_ctx *ctx, hipStream_t stream, int32_
 dflash_status dflash_draft_block(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
                                  const void *d_feats, int32_t *d_block, float *d_logits);
 
+/* Stochastic drafts (the general rejection-sampling rule behind [P1]'s cost-model sentence on
+ * rejection sampling; a reading where the pages are silent: drafts drawn from the drafter's own
+ * distribution instead of its argmax).  As dflash_draft_block, except that d_i is drawn from q_i, the drafter's fp32 logits at
+ * position n+i passed through the same filter as the target's rows with the request's sampling
+ * (temperature 0: a point mass at the argmax), by inverse CDF with u = top 24 bits of word 0 of
+ * Philox4x64-10 with key (seed, 0) and counter (n+i, slot, 1, 0) (stream 1; dflash_accept_resample uses
+ * stream 0).  sampling is a host array [batch].  q_i's candidates go to d_q_ids / d_q_p
+ * [batch][B-1][DFLASH_MAX_TOPK] (sorted as the filter sorts them, ids -1 / probabilities 0 past the kept
+ * ones), caller-allocated; pass them to dflash_accept_resample_q.  d_logits as in dflash_draft_block. */
+dflash_status dflash_draft_block_sampled(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
+                                         const void *d_feats, const dflash_sampling *sampling, int32_t *d_block,
+                                         int32_t *d_q_ids, float *d_q_p, float *d_logits);
+
+/* Accept / resample for drafts drawn from known distributions q (d_q_ids / d_q_p as written by
+ * dflash_draft_block_sampled, or any caller-built rows in that layout whose q(d_i) > 0): draft d at
+ * position t is accepted iff u_acc(t) * q(d) < p(d) in fp32, i.e. with probability min(1, p(d)/q(d));
+ * at the first rejection the token is drawn by inverse CDF (u_smp(t)) from max(0, p - q) over p's
+ * candidates in their order, renormalised (from p itself should that residual be all zero).  The
+ * output law of every position is then p, whatever q is.  Everything else (uniforms, bonus token,
+ * commit, outputs, errors) as dflash_accept_resample, which is the case of q a point mass at the draft
+ * (the same decisions bit for bit).  d_q_ids / d_q_p may be NULL only when n_draft is 0. */
+dflash_status dflash_accept_resample_q(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
+                                       const float *d_logits, const int32_t *d_block, int32_t n_draft,
+                                       const dflash_sampling *sampling, const int32_t *d_q_ids, const float *d_q_p,
+                                       int32_t *d_out, int32_t *d_n_out, int32_t *d_cand_ids, float *d_cand_p);
+
 /* Operator-level access to the projection kernel used by every step (test and measurement access):
  * d_y[m][n] = sum_k d_x[m][k] * d_w[n][k] (fp32 output) for m < M, with d_x [M][K] and d_w [N][K] in
  * `dtype` (dflash_dtype), on the same code path as the model's projections.  N must be a multiple of

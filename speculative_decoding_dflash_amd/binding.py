@@ -79,6 +79,8 @@ def _load() -> C.CDLL:
         "dflash_verify_block": (I, [V, V, I, P(I), V, I, I, I, V, V]),
         "dflash_accept_resample": (I, [V, V, I, P(I), V, V, I, P(Sampling), V, V, V, V]),
         "dflash_draft_block": (I, [V, V, I, P(I), V, V, V]),
+        "dflash_draft_block_sampled": (I, [V, V, I, P(I), V, P(Sampling), V, V, V, V]),
+        "dflash_accept_resample_q": (I, [V, V, I, P(I), V, V, I, P(Sampling), V, V, V, V, V, V]),
         "dflash_device_status": (I, [V, V]),
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
         "dflash_profile": (I, [V, I]),
@@ -162,6 +164,21 @@ def dflash_accept_resample(ctx: int, slots: Sequence[int], logits, block, n_draf
 def dflash_draft_block(ctx: int, slots: Sequence[int], feats, block, logits=None, stream=None):
     _check(lib.dflash_draft_block(ctx, _stream(stream), len(slots), _slots(slots), _ptr(feats), _ptr(block),
                                   _ptr(logits)))
+
+
+def dflash_draft_block_sampled(ctx: int, slots: Sequence[int], feats, sampling: Sequence[Sampling], block, q_ids, q_p,
+                               logits=None, stream=None):
+    sp = (Sampling * len(slots))(*sampling)
+    _check(lib.dflash_draft_block_sampled(ctx, _stream(stream), len(slots), _slots(slots), _ptr(feats), sp,
+                                          _ptr(block), _ptr(q_ids), _ptr(q_p), _ptr(logits)))
+
+
+def dflash_accept_resample_q(ctx: int, slots: Sequence[int], logits, block, n_draft: int, sampling: Sequence[Sampling],
+                             q_ids, q_p, out, n_out, cand_ids=None, cand_p=None, stream=None):
+    sp = (Sampling * len(slots))(*sampling)
+    _check(lib.dflash_accept_resample_q(ctx, _stream(stream), len(slots), _slots(slots), _ptr(logits), _ptr(block),
+                                        n_draft, sp, _ptr(q_ids), _ptr(q_p), _ptr(out), _ptr(n_out), _ptr(cand_ids),
+                                        _ptr(cand_p)))
 
 
 def dflash_op_linear(dtype: int, M: int, N: int, K: int, x, w, y, stream=None):

@@ -468,6 +468,42 @@ bool same_slots(dflash_ctx *c, int batch, const int32_t *slots) {
   return true;
 }
 
+dflash_status check_sampling(const dflash_sampling *sampling, int batch) {
+  for (int b = 0; b < batch; ++b) {
+    const dflash_sampling &sp = sampling[b];
+    if (!(sp.temperature >= 0.f)) return fail(DFLASH_E_INVAL, "temperature must be >= 0");
+    if (sp.temperature > 0.f) {
+      if (sp.top_k < 1 || sp.top_k > DFLASH_MAX_TOPK) return fail(DFLASH_E_INVAL, "top_k must be in [1, %d]", DFLASH_MAX_TOPK);
+      if (!(sp.top_p > 0.f) || sp.top_p > 1.f) return fail(DFLASH_E_INVAL, "top_p must be in (0, 1]");
+    }
+  }
+  return DFLASH_OK;
+}
+
+// The candidate filter over `rows` logit rows, rows_per_seq of each request with its sampling.
+void filter_setup(dflash_ctx *c, FilterArgs &f, const float *logits, int rows, int rows_per_seq,
+                  const dflash_sampling *sampling, int batch, int32_t *cid, float *cp, int32_t *cn) {
+  memset(&f, 0, sizeof f);
+  f.logits = logits;
+  f.rows = rows;
+  f.vocab = c->cfg.vocab;
+  f.rows_per_seq = rows_per_seq;
+  for (int b = 0; b < batch; ++b) {
+    f.temperature[b] = sampling[b].temperature;
+    f.top_k[b] = sampling[b].top_k;
+    f.top_p[b] = sampling[b].top_p;
+  }
+  f.cand_id = cid;
+  f.cand_p = cp;
+  f.cand_n = cn;
+  f.stage_key = c->wsp<uint32_t>(c->L.skey);
+  f.stage_idx = c->wsp<int32_t>(c->L.sidx);
+  int kmax = 1;
+  for (int b = 0; b < batch; ++b)
+    if (sampling[b].temperature > 0.f) kmax = std::max(kmax, std::min(sampling[b].top_k, c->cfg.vocab));
+  filter_plan(f, kmax);
+}
+
 }  // namespace
 
 extern "C" {
@@ -661,10 +697,10 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   return DFLASH_OK;
 }
 
-dflash_status dflash_accept_resample(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots,
-                                     const float *d_logits, const int32_t *d_block, int32_t n_draft,
-                                     const dflash_sampling *sampling, int32_t *d_out, int32_t *d_n_out,
-                                     int32_t *d_cand_ids, float *d_cand_p) {
+namespace {
+dflash_status accept_impl(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const float *d_logits,
+                          const int32_t *d_block, int32_t n_draft, const dflash_sampling *sampling, const int32_t *d_q_ids,
+                          const float *d_q_p, int32_t *d_out, int32_t *d_n_out, int32_t *d_cand_ids, float *d_cand_p) {
   if (!c) return fail(DFLASH_E_INVAL, "null context");
   dflash_status st = check_slots(c, batch, slots, true);
   if (st != DFLASH_OK) return st;
@@ -674,37 +710,13 @@ dflash_status dflash_accept_resample(dflash_ctx *c, hipStream_t s, int32_t batch
     return fail(DFLASH_E_INVAL, "n_draft + 1 must equal the n_logit_rows of the last verify (%d)", c->last_nlogit);
   if (n_draft > 0 && !d_block) return fail(DFLASH_E_INVAL, "null block");
   if (!d_logits || !d_out || !d_n_out || !sampling) return fail(DFLASH_E_INVAL, "null argument");
-  for (int b = 0; b < batch; ++b) {
-    const dflash_sampling &sp = sampling[b];
-    if (!(sp.temperature >= 0.f)) return fail(DFLASH_E_INVAL, "temperature must be >= 0");
-    if (sp.temperature > 0.f) {
-      if (sp.top_k < 1 || sp.top_k > DFLASH_MAX_TOPK) return fail(DFLASH_E_INVAL, "top_k must be in [1, %d]", DFLASH_MAX_TOPK);
-      if (!(sp.top_p > 0.f) || sp.top_p > 1.f) return fail(DFLASH_E_INVAL, "top_p must be in (0, 1]");
-    }
-  }
+  if ((st = check_sampling(sampling, batch)) != DFLASH_OK) return st;
   const int rows = batch * (n_draft + 1);
   if ((size_t)rows > (size_t)c->cap.max_slots * std::max(1, c->dcfg.block_size))
     return fail(DFLASH_E_INVAL, "batch * (n_draft + 1) exceeds max_slots * block_size");
   FilterArgs f;
-  memset(&f, 0, sizeof f);
-  f.logits = d_logits;
-  f.rows = rows;
-  f.vocab = c->cfg.vocab;
-  f.rows_per_seq = n_draft + 1;
-  for (int b = 0; b < batch; ++b) {
-    f.temperature[b] = sampling[b].temperature;
-    f.top_k[b] = sampling[b].top_k;
-    f.top_p[b] = sampling[b].top_p;
-  }
-  f.cand_id = c->wsp<int32_t>(c->L.cid);
-  f.cand_p = c->wsp<float>(c->L.cp);
-  f.cand_n = c->wsp<int32_t>(c->L.cn);
-  f.stage_key = c->wsp<uint32_t>(c->L.skey);
-  f.stage_idx = c->wsp<int32_t>(c->L.sidx);
-  int kmax = 1;
-  for (int b = 0; b < batch; ++b)
-    if (sampling[b].temperature > 0.f) kmax = std::max(kmax, std::min(sampling[b].top_k, c->cfg.vocab));
-  filter_plan(f, kmax);
+  filter_setup(c, f, d_logits, rows, n_draft + 1, sampling, batch, c->wsp<int32_t>(c->L.cid), c->wsp<float>(c->L.cp),
+               c->wsp<int32_t>(c->L.cn));
   HIP_OK(launch_filter(f, s));
   DecideArgs d;
   memset(&d, 0, sizeof d);
@@ -722,18 +734,46 @@ dflash_status dflash_accept_resample(dflash_ctx *c, hipStream_t s, int32_t batch
   d.out = d_out;
   d.n_out = d_n_out;
   d.err = c->err();
+  d.q_id = n_draft > 0 ? d_q_ids : nullptr;
+  d.q_p = n_draft > 0 ? d_q_p : nullptr;
   HIP_OK(launch_decide(d, s));
   if (d_cand_ids || d_cand_p) HIP_OK(launch_copy_cands(f.cand_id, f.cand_p, f.cand_n, rows, d_cand_ids, d_cand_p, s));
   c->verified = false;
   return DFLASH_OK;
 }
+}  // namespace
 
-dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const void *d_feats,
-                                 int32_t *d_block, float *d_logits) {
+dflash_status dflash_accept_resample(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots,
+                                     const float *d_logits, const int32_t *d_block, int32_t n_draft,
+                                     const dflash_sampling *sampling, int32_t *d_out, int32_t *d_n_out,
+                                     int32_t *d_cand_ids, float *d_cand_p) {
+  return accept_impl(c, s, batch, slots, d_logits, d_block, n_draft, sampling, nullptr, nullptr, d_out, d_n_out,
+                     d_cand_ids, d_cand_p);
+}
+
+dflash_status dflash_accept_resample_q(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots,
+                                       const float *d_logits, const int32_t *d_block, int32_t n_draft,
+                                       const dflash_sampling *sampling, const int32_t *d_q_ids, const float *d_q_p,
+                                       int32_t *d_out, int32_t *d_n_out, int32_t *d_cand_ids, float *d_cand_p) {
+  if (n_draft > 0 && (!d_q_ids || !d_q_p)) return fail(DFLASH_E_INVAL, "null draft candidate buffers");
+  return accept_impl(c, s, batch, slots, d_logits, d_block, n_draft, sampling, d_q_ids, d_q_p, d_out, d_n_out,
+                     d_cand_ids, d_cand_p);
+}
+
+namespace {
+
+// dflash_draft_block (sampling null: argmax drafts) and dflash_draft_block_sampled.
+dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const void *d_feats,
+                               int32_t *d_block, float *d_logits, const dflash_sampling *sampling, int32_t *d_q_ids,
+                               float *d_q_p) {
   if (!c) return fail(DFLASH_E_INVAL, "null context");
   dflash_status st = check_slots(c, batch, slots, true);
   if (st != DFLASH_OK) return st;
   if (!d_feats || !d_block) return fail(DFLASH_E_INVAL, "null features or block");
+  if (sampling) {
+    if (!d_q_ids || !d_q_p) return fail(DFLASH_E_INVAL, "null draft candidate buffers");
+    if ((st = check_sampling(sampling, batch)) != DFLASH_OK) return st;
+  }
   if (c->last_qlen < 1 || !same_slots(c, batch, slots))
     return fail(DFLASH_E_STATE, "draft_block must use the slots of the last verified block");
   const dflash_model_cfg &m = c->cfg;
@@ -827,8 +867,42 @@ dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, co
   f.am_stride = B;
   f.am_offset = 1;
   filter_plan(f, 1);
+  if (sampling) {  // stochastic drafts: filter each row with the request's sampling, draw from it
+    filter_setup(c, f, logits, batch * nd, nd, sampling, batch, d_q_ids, d_q_p, c->wsp<int32_t>(c->L.cn));
+    HIP_OK(launch_filter(f, s));
+    DraftSampleArgs ds;
+    memset(&ds, 0, sizeof ds);
+    ds.batch = batch;
+    ds.nd = nd;
+    ds.block = B;
+    for (int b = 0; b < batch; ++b) {
+      ds.slots[b] = slots[b];
+      ds.seed[b] = sampling[b].seed;
+    }
+    ds.state = c->state();
+    ds.q_id = d_q_ids;
+    ds.q_p = d_q_p;
+    ds.q_n = f.cand_n;
+    ds.out = d_block;
+    HIP_OK(launch_draft_sample(ds, s));
+    return DFLASH_OK;
+  }
   HIP_OK(launch_filter(f, s));
   return DFLASH_OK;
+}
+
+}  // namespace
+
+dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const void *d_feats,
+                                 int32_t *d_block, float *d_logits) {
+  return draft_block_impl(c, s, batch, slots, d_feats, d_block, d_logits, nullptr, nullptr, nullptr);
+}
+
+dflash_status dflash_draft_block_sampled(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots,
+                                         const void *d_feats, const dflash_sampling *sampling, int32_t *d_block,
+                                         int32_t *d_q_ids, float *d_q_p, float *d_logits) {
+  if (!sampling) return fail(DFLASH_E_INVAL, "null sampling");
+  return draft_block_impl(c, s, batch, slots, d_feats, d_block, d_logits, sampling, d_q_ids, d_q_p);
 }
 
 dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,

@@ -8,6 +8,10 @@
 // accepted the bonus token at the next position is drawn from the last row.  Uniforms are Philox4x64
 // with 10 rounds (Salmon et al., SC 2011), key (seed, 0), counter (t, slot, 0, 0), using the top 24
 // bits of words 0 (u_acc) and 1 (u_smp).
+// Stochastic drafts (x drawn from the drafter's own distribution q, with the top 24 bits of word 0
+// of counter (t, slot, 1, 0)): x is accepted iff u_acc(t) * q(x) < p(x), i.e. with probability
+// min(1, p(x)/q(x)); the first rejected position is drawn from max(0, p - q) over p's candidates
+// (from p should that vanish).  q a point mass at x gives exactly the deterministic rule.
 #include "kernels.h"
 
 namespace df {
@@ -59,6 +63,37 @@ DF_DEVICE int inverse_cdf(const int32_t *ids, const float *p, int n, float u, in
   return last;
 }
 
+// q(y) from a candidate row padded with -1
+DF_DEVICE float q_of(const int32_t *qi, const float *qp, int y) {
+  float v = 0.f;
+  for (int j = 0; j < kMaxTopK && qi[j] >= 0; ++j)
+    if (qi[j] == y) v = qp[j];
+  return v;
+}
+
+// max(0, p - q) of candidate j
+DF_DEVICE float resid(const int32_t *ids, const float *p, int j, const int32_t *qi, const float *qp) {
+  const float d = p[j] - q_of(qi, qp, ids[j]);
+  return d > 0.f ? d : 0.f;
+}
+
+// Inverse CDF over the residual max(0, p - q) (candidate order); -1 if the residual is all zero.
+DF_DEVICE int inverse_cdf_resid(const int32_t *ids, const float *p, int n, const int32_t *qi, const float *qp, float u) {
+  float total = 0.f;
+  for (int j = 0; j < n; ++j) total = total + resid(ids, p, j, qi, qp);
+  if (!(total > 0.f)) return -1;
+  const float thr = u * total;
+  float acc = 0.f;
+  int last = -1;
+  for (int j = 0; j < n; ++j) {
+    const float r = resid(ids, p, j, qi, qp);
+    acc = acc + r;
+    if (thr < acc) return ids[j];
+    if (r > 0.f) last = ids[j];
+  }
+  return last;
+}
+
 __global__ void decide_kernel(DecideArgs a) {
   const int b = threadIdx.x;
   if (b >= a.batch) return;
@@ -79,11 +114,22 @@ __global__ void decide_kernel(DecideArgs a) {
     float pd = 0.f;
     for (int j = 0; j < n; ++j)
       if (ids[j] == d) pd = p[j];
-    if (u24(w.w[0]) < pd) {
-      out[tau++] = d;
-      continue;
+    if (!a.q_id) {
+      if (u24(w.w[0]) < pd) {
+        out[tau++] = d;
+        continue;
+      }
+      out[tau++] = inverse_cdf(ids, p, n, u24(w.w[1]), d);
+    } else {
+      const int32_t *qi = a.q_id + (size_t)(b * nd + i - 1) * kMaxTopK;
+      const float *qp = a.q_p + (size_t)(b * nd + i - 1) * kMaxTopK;
+      if (u24(w.w[0]) * q_of(qi, qp, d) < pd) {
+        out[tau++] = d;
+        continue;
+      }
+      const int y = inverse_cdf_resid(ids, p, n, qi, qp, u24(w.w[1]));
+      out[tau++] = y >= 0 ? y : inverse_cdf(ids, p, n, u24(w.w[1]), -1);
     }
-    out[tau++] = inverse_cdf(ids, p, n, u24(w.w[1]), d);
     rejected = true;
     break;
   }
@@ -101,6 +147,30 @@ __global__ void decide_kernel(DecideArgs a) {
   st.seq_len = st.pend_start + committed;
   st.anchor = out[tau - 1];
   if (out[tau - 1] < 0) raise_err(a.err, ERR_STATE);
+}
+
+__global__ void draft_sample_kernel(DraftSampleArgs a) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= a.batch * a.nd) return;
+  const int b = row / a.nd, i = row % a.nd + 1;
+  const int slot = a.slots[b];
+  const int t = a.state[slot].seq_len + i;
+  int32_t *ids = a.q_id + (size_t)row * kMaxTopK;
+  float *p = a.q_p + (size_t)row * kMaxTopK;
+  const int n = a.q_n[row];
+  const U4 w = philox4x64_10((uint64_t)t, (uint64_t)slot, 1, 0, a.seed[b], 0);
+  a.out[(size_t)b * a.block + i] = inverse_cdf(ids, p, n, u24(w.w[0]), -1);
+  for (int j = n; j < kMaxTopK; ++j) {
+    ids[j] = -1;
+    p[j] = 0.f;
+  }
+}
+
+hipError_t launch_draft_sample(const DraftSampleArgs &a, hipStream_t s) {
+  const int rows = a.batch * a.nd;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(draft_sample_kernel, dim3((rows + 63) / 64), dim3(64), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decide(const DecideArgs &a, hipStream_t s) {

@@ -225,8 +225,27 @@ struct DecideArgs {
   int32_t *out;
   int32_t *n_out;
   int32_t *err;
+  // Stochastic drafts (null: deterministic drafts): the drafter's candidate distribution of draft i of
+  // request b at row b * n_draft + i - 1, [rows][kMaxTopK] ids (-1 past the kept ones) and fp32 p.
+  const int32_t *q_id;
+  const float *q_p;
 };
 hipError_t launch_decide(const DecideArgs &a, hipStream_t s);
+
+// Stochastic drafts: draft i of request b (position seq_len + i) is drawn by inverse CDF from its
+// candidate row b * nd + i - 1 with the uniform of Philox stream 1; the rows are then padded with
+// -1 / 0 past their cand_n kept entries.
+struct DraftSampleArgs {
+  int32_t batch, nd, block;  // requests, drafts per request, block length (nd + 1)
+  int32_t slots[64];
+  uint64_t seed[64];
+  const SlotState *state;
+  int32_t *q_id;       // [batch * nd][kMaxTopK]
+  float *q_p;          // [batch * nd][kMaxTopK]
+  const int32_t *q_n;  // [batch * nd]
+  int32_t *out;        // [batch][block]: draft i goes to out[b * block + i]
+};
+hipError_t launch_draft_sample(const DraftSampleArgs &a, hipStream_t s);
 
 // copy candidate lists out for tests
 hipError_t launch_copy_cands(const int32_t *cid, const float *cp, const int32_t *cn, int32_t rows, int32_t *oid,

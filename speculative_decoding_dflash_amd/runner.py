@@ -72,6 +72,10 @@ class Engine:
         self.n_out = torch.zeros(max_slots, dtype=torch.int32, device=self.device)
         self.cand_ids = torch.zeros(nl * B.MAX_TOPK, dtype=torch.int32, device=self.device)
         self.cand_p = torch.zeros(nl * B.MAX_TOPK, dtype=torch.float32, device=self.device)
+        # stochastic drafts: the drafter's candidate distributions [max_slots][B-1][MAX_TOPK]
+        nq = max_slots * max(self.B - 1, 1) * B.MAX_TOPK
+        self.q_ids = torch.zeros(nq, dtype=torch.int32, device=self.device)
+        self.q_p = torch.zeros(nq, dtype=torch.float32, device=self.device)
 
     def close(self):
         if self.ctx:
@@ -97,14 +101,25 @@ class Engine:
                               self.logits if logits is None else logits, self.feats)
 
     def accept(self, slots: Sequence[int], n_draft: int, samplings: Sequence[B.Sampling], block=None, cands=False,
-               logits: Optional[torch.Tensor] = None):
-        B.dflash_accept_resample(self.ctx, slots, self.logits if logits is None else logits,
-                                 block if block is not None else (self.block if n_draft > 0 else None), n_draft,
-                                 samplings, self.out, self.n_out, self.cand_ids if cands else None,
-                                 self.cand_p if cands else None)
+               logits: Optional[torch.Tensor] = None, q: bool = False):
+        """q: the drafts were drawn from the distributions in q_ids / q_p (stochastic drafts)."""
+        lg = self.logits if logits is None else logits
+        blk = block if block is not None else (self.block if n_draft > 0 else None)
+        ci, cp = (self.cand_ids, self.cand_p) if cands else (None, None)
+        if q:
+            B.dflash_accept_resample_q(self.ctx, slots, lg, blk, n_draft, samplings, self.q_ids, self.q_p, self.out,
+                                       self.n_out, ci, cp)
+        else:
+            B.dflash_accept_resample(self.ctx, slots, lg, blk, n_draft, samplings, self.out, self.n_out, ci, cp)
 
-    def draft(self, slots: Sequence[int], want_logits: bool = False):
-        B.dflash_draft_block(self.ctx, slots, self.feats, self.block, self.draft_logits if want_logits else None)
+    def draft(self, slots: Sequence[int], want_logits: bool = False,
+              samplings: Optional[Sequence[B.Sampling]] = None):
+        """samplings: draw the drafts from the drafter's filtered distributions (stochastic drafts)."""
+        lg = self.draft_logits if want_logits else None
+        if samplings is not None:
+            B.dflash_draft_block_sampled(self.ctx, slots, self.feats, samplings, self.block, self.q_ids, self.q_p, lg)
+        else:
+            B.dflash_draft_block(self.ctx, slots, self.feats, self.block, lg)
 
     def status(self):
         B.dflash_device_status(self.ctx)
@@ -117,15 +132,16 @@ class Engine:
         self.accept(slots, 0, samplings)
 
     def spec_step(self, slots: Sequence[int], samplings: Sequence[B.Sampling], planted: Optional[torch.Tensor] = None,
-                  cands: bool = False, draft_logits: bool = False):
+                  cands: bool = False, draft_logits: bool = False, stochastic: bool = False):
         """One draft -> verify -> accept step.  planted: optional int32 device [batch, B-1] drafts that
-        replace the drafter's (the drafter still runs)."""
+        replace the drafter's (the drafter still runs).  stochastic: drafts drawn from the drafter's
+        own distributions and accepted with min(1, p/q)."""
         n = len(slots)
-        self.draft(slots, want_logits=draft_logits)
+        self.draft(slots, want_logits=draft_logits, samplings=samplings if stochastic else None)
         if planted is not None:
             self.block.view(-1, self.B)[:n, 1:] = planted
         self.verify(slots, self.block, self.B, False, self.B)
-        self.accept(slots, self.B - 1, samplings, cands=cands)
+        self.accept(slots, self.B - 1, samplings, cands=cands, q=stochastic)
 
     def capture_spec_step(self, slots: Sequence[int], samplings: Sequence[B.Sampling],
                           planted: Optional[torch.Tensor] = None) -> "torch.cuda.CUDAGraph":

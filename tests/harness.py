@@ -10,7 +10,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 from oracle.model import Drafter, Target
-from oracle.sampling import decide, sample_dist
+from oracle.sampling import decide, decide_q, sample_dist, sample_draft
 from synth import weights as sw
 
 
@@ -96,13 +96,38 @@ class OracleFollower:
         self.anchor = anchor
 
 
+def check_q_stage(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_dlogits: np.ndarray,
+                  g_qids: np.ndarray, g_qp: np.ndarray):
+    """Stochastic drafts: the device's q candidates are the oracle's filter of the device's draft logits
+    (ids exactly, probabilities up to the last bits of exp), and each draft is the oracle's draw from
+    the device's q with the same uniform (bit-exact).  Returns the device's q rows."""
+    qrows = []
+    for i in range(len(block) - 1):
+        k = int((g_qids[i] >= 0).sum())
+        ids_g, p_g = g_qids[i, :k].astype(np.int64), g_qp[i, :k].astype(np.float32)
+        qrows.append((ids_g, p_g))
+        ids_o, p_o = sample_dist(g_dlogits[i].astype(np.float32), sp.temperature, sp.top_k, sp.top_p)
+        if len(ids_o) != k or not np.array_equal(ids_o, ids_g) or np.abs(p_o.astype(np.float64) - p_g).max() > 2e-6:
+            m = min(len(ids_o), k)
+            assert np.array_equal(ids_o[:m], ids_g[:m]), ("draft filter ids", i, ids_o[:8], ids_g[:8])
+            rep.flagged += 1
+        want = sample_draft(ids_g, p_g, sp.seed, fol.n + 1 + i, fol.request)
+        assert want == int(block[1 + i]), ("draft draw", i, want, int(block[1 + i]))
+    return qrows
+
+
 def check_step(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_logits: np.ndarray,
-               g_dlogits: Optional[np.ndarray], g_ids: np.ndarray, g_p: np.ndarray, g_out: List[int], tol: float):
-    """Compare one device step with the oracle; returns the oracle's features for the commit."""
+               g_dlogits: Optional[np.ndarray], g_ids: np.ndarray, g_p: np.ndarray, g_out: List[int], tol: float,
+               qrows=None):
+    """Compare one device step with the oracle; returns the oracle's features for the commit.
+    qrows: the device's draft distributions (stochastic drafts, already checked by check_q_stage)."""
     B = len(block)
     n = fol.n
     assert int(block[0]) == fol.anchor, (block[0], fol.anchor)
-    if g_dlogits is not None:
+    if g_dlogits is not None and qrows is not None:
+        dz = fol.d.draft_logits(fol.dc, fol.anchor, n)
+        rep.draft_err.extend(rel_err_rows(g_dlogits, dz).tolist())
+    elif g_dlogits is not None:
         dz = fol.d.draft_logits(fol.dc, fol.anchor, n)
         rep.draft_err.extend(rel_err_rows(g_dlogits, dz).tolist())
         o_drafts = [int(np.argmax(r.astype(np.float32))) for r in dz]
@@ -119,7 +144,10 @@ def check_step(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_lo
     for r in range(B):
         k = int((g_ids[r] >= 0).sum())
         rows_g.append((g_ids[r, :k].astype(np.int64), g_p[r, :k].astype(np.float32)))
-    want = decide(rows_g, [int(x) for x in block[1:]], n, sp.seed, fol.request)
+    if qrows is None:
+        want = decide(rows_g, [int(x) for x in block[1:]], n, sp.seed, fol.request)
+    else:
+        want = decide_q(rows_g, qrows, [int(x) for x in block[1:]], n, sp.seed, fol.request)
     assert want == list(g_out), ("decide mismatch", want, list(g_out))
     # filter stage, same fp32 inputs: the oracle's filter applied to the device's logits gives the
     # device's candidates (ids exactly; probabilities up to the last bits of exp)

@@ -10,9 +10,9 @@ import pytest
 import torch
 
 import synth
-from harness import (OracleFollower, StepReport, check_step, log, near_tie_argmax, rel_err_rows, tol_of,
-                     torch_weights)
-from oracle.sampling import decide, sample_dist
+from harness import (OracleFollower, StepReport, check_q_stage, check_step, log, near_tie_argmax, rel_err_rows,
+                     tol_of, torch_weights)
+from oracle.sampling import decide, decide_q, sample_dist
 from oracle.spec import Sampling as OSampling
 from oracle.spec import SpecDecoder, ar_generate
 from synth import weights as sw
@@ -76,7 +76,7 @@ def test_prefill_logits_and_features(name):
     assert ef.max() <= (1e-4 if cfg.target.dtype == "fp32" else 2e-2)
 
 
-def run_e2e(cfg, W, sp, n_tokens, log_every=4):
+def run_e2e(cfg, W, sp, n_tokens, log_every=4, stochastic=False):
     tol = tol_of(cfg)
     B = cfg.drafter.block_size
     P = cfg.prompt_len
@@ -101,7 +101,7 @@ def run_e2e(cfg, W, sp, n_tokens, log_every=4):
     rep = StepReport()
     step = 0
     while len(stream) < n_tokens:
-        eng.spec_step([0], [s], cands=True, draft_logits=True)
+        eng.spec_step([0], [s], cands=True, draft_logits=True, stochastic=stochastic)
         block = eng.block[:B].cpu().numpy()
         g_logits = eng.logits[:B * V].view(B, V).cpu().numpy()
         g_dl = eng.draft_logits[:(B - 1) * V].view(B - 1, V).cpu().numpy()
@@ -110,7 +110,12 @@ def run_e2e(cfg, W, sp, n_tokens, log_every=4):
         tau = int(eng.n_out[0].item())
         outs = [int(x) for x in eng.out[:tau].cpu().numpy()]
         start = fol.n
-        feats = check_step(rep, fol, sp, block, g_logits, g_dl, ids, pp, outs, tol)
+        qrows = None
+        if stochastic:
+            qi = eng.q_ids[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
+            qp = eng.q_p[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
+            qrows = check_q_stage(rep, fol, sp, block, g_dl, qi, qp)
+        feats = check_step(rep, fol, sp, block, g_logits, g_dl, ids, pp, outs, tol, qrows=qrows)
         fol.commit(feats, start, tau, outs[-1])
         stream.extend(outs)
         if step % log_every == 0:
@@ -258,6 +263,95 @@ def test_sampler_chi_square_and_bitexact():
     sup = r > 0
     assert resample[~sup].sum() == 0
     assert scipy.stats.chisquare(resample[sup], r[sup] * resample.sum()).pvalue > 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_e2e_stochastic_drafts(name):
+    """Stochastic drafts end to end, teacher-forced: the drafter's candidate distributions match the
+    oracle's filter of the device's draft logits, each draft is the oracle's draw from them with the
+    same stream-1 uniform, and the min(1, p/q) / max(0, p - q) decisions are bit-exact with the oracle's
+    rule on the device's candidates; logits within tolerance of the oracle's forward."""
+    cfg = CASES[name]()
+    log(f"[e2e stochastic drafts] {name}")
+    W = sw.model_weights(cfg, gain_std=0.1)
+    sp = synth.SamplingCfg(temperature=1.0, top_k=8, top_p=0.95, seed=3)
+    stream, rep, prompt = run_e2e(cfg, W, sp, 48 if name == "tiny" else 24, stochastic=True)
+    tol = tol_of(cfg)
+    le, de = np.array(rep.logits_err), np.array(rep.draft_err)
+    log(f"  logits err max {le.max():.3e}, draft logits err max {de.max():.3e}, taus {rep.taus}")
+    assert le.max() <= tol and de.max() <= tol
+
+
+def test_stochastic_sampler_law():
+    """dflash_accept_resample_q with caller-built draft distributions q and drafts drawn from q: the
+    acceptance rate is sum_x min(p, q) (z-test), the emitted token follows p (chi-square), and every
+    decision is bit-exact with the oracle's rule on the device's candidates."""
+    import scipy.stats
+    from oracle.sampling import sample_draft
+    cfg = synth.TINY
+    W = sw.model_weights(cfg)
+    V, B = cfg.target.vocab, cfg.drafter.block_size
+    S = 64
+    eng = engine(cfg, W, max_slots=S, max_rows=S * B)
+    for s_ in range(S):
+        eng.kv_alloc(s_, 4 * B)
+    rng = np.random.default_rng(8)
+    base = np.full(V, -30.0, dtype=np.float32)
+    hot = rng.choice(V, 8, replace=False)
+    base[hot] = rng.normal(0, 1.0, 8).astype(np.float32)
+    ids_o, p_o = sample_dist(base, 1.0, 6, 0.9)
+    # q: another distribution over the hot tokens, with mass where p has none and vice versa
+    qb = np.full(V, -30.0, dtype=np.float32)
+    qb[hot] = rng.normal(0, 1.5, 8).astype(np.float32)
+    qids, qp = sample_dist(qb, 1.0, 7, 1.0)
+    nd = B - 1
+    qi_host = np.full((S * nd, 256), -1, dtype=np.int32)
+    qp_host = np.zeros((S * nd, 256), dtype=np.float32)
+    qi_host[:, :len(qids)] = qids
+    qp_host[:, :len(qids)] = qp
+    eng.q_ids[:S * nd * 256] = torch.from_numpy(qi_host.reshape(-1)).to("cuda")
+    eng.q_p[:S * nd * 256] = torch.from_numpy(qp_host.reshape(-1)).to("cuda")
+    logits = torch.from_numpy(np.tile(base, S * B)).to("cuda")
+    toks = torch.zeros(S * B, dtype=torch.int32, device="cuda")
+    pf = np.zeros(V)
+    pf[ids_o] = p_o
+    qf = np.zeros(V)
+    qf[qids] = qp
+    acc = first_n = 0
+    first = np.zeros(V)
+    for call in range(60):
+        seeds = [1000 * call + s_ for s_ in range(S)]
+        samplings = [samp(synth.SamplingCfg(1.0, 6, 0.9, sd)) for sd in seeds]
+        # drafts drawn from q (stream 1 at the draft positions 1 .. nd after an anchor at position 0)
+        drafts = np.array([[sample_draft(qids, qp, seeds[s_], i, s_) for i in range(1, nd + 1)] for s_ in range(S)],
+                          dtype=np.int32)
+        blk = np.zeros((S, B), dtype=np.int32)
+        blk[:, 1:] = drafts
+        block = torch.from_numpy(blk.reshape(-1)).to("cuda")
+        eng.verify(list(range(S)), toks, B, True, B)
+        eng.accept(list(range(S)), nd, samplings, block=block, cands=True, logits=logits, q=True)
+        out = eng.out[:S * B].view(S, B).cpu().numpy()
+        nout = eng.n_out[:S].cpu().numpy()
+        gi = eng.cand_ids[:256].cpu().numpy()
+        gp = eng.cand_p[:256].cpu().numpy()
+        k = int((gi >= 0).sum())
+        assert np.array_equal(gi[:k], ids_o) and np.abs(gp[:k] - p_o).max() <= 2e-6
+        rows = [(gi[:k].astype(np.int64), gp[:k])] * B
+        qrows = [(qids.astype(np.int64), qp)] * nd
+        for s_ in range(S):
+            tau = int(nout[s_])
+            want = decide_q(rows, qrows, [int(x) for x in drafts[s_]], 0, seeds[s_], s_)
+            assert want == list(out[s_, :tau]), (call, s_, want, out[s_, :tau])
+            first[out[s_, 0]] += 1
+            first_n += 1
+            acc += tau > 1
+    a = float(np.minimum(pf, qf).sum())
+    z = (acc / first_n - a) / np.sqrt(a * (1 - a) / first_n)
+    log(f"  accept rate {acc / first_n:.4f} vs sum min(p, q) {a:.4f} (z {z:.2f})")
+    assert abs(z) < 4.5
+    sup = pf > 0
+    assert first[~sup].sum() == 0
+    assert scipy.stats.chisquare(first[sup], pf[sup] / pf[sup].sum() * first_n).pvalue > 1e-4
 
 
 def test_gpu_generator_matches_cpu():
