@@ -11,7 +11,8 @@ Printed, one JSON line: `value` = accepted tokens/s of that run with the real dr
 emitted per second over the timed steps); with random weights the acceptance length is near 1, so
 the same kernels are also run with a planted drafter (drafts taken from the target's greedy stream
 and forced to fail at a chosen position, greedy verification) for acceptance lengths 1..8, and as
-plain decoding (one target forward per token) for the same-kernel AR baseline.  `roofline` reports
+plain decoding (one target forward per token) for the same-kernel AR baseline, and with stochastic
+drafts (drawn from the drafter's own distribution, accepted with min(1, p/q)).  `roofline` reports
 the projection kernel (the dominant one: ~99% of the step's bytes): the projection launches of one
 step are recorded by the library and replayed back to back between two HIP events on the step's
 stream; `traffic` is the HBM bytes per launch measured with rocprofv3 counters.  `cpu_baseline` times
@@ -84,23 +85,23 @@ class Timer:
         return self.e0.elapsed_time(self.e1)
 
 
-def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=False, graph=True):
+def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=False, graph=True, stochastic=False):
     """Prefill, then warmup + timed speculative steps with no host synchronisation inside the timed
     region (device-resident sequence state).  With graph=True the step is captured once into a HIP
     graph after the warmup and replayed (every launch parameter of a step is fixed on the host);
     planted drafts are then copied into the captured buffer before each replay.  Returns (ms for the
     timed steps, taus per step); with profile=True (eager steps) the library records the projection
-    launches of the timed steps."""
+    launches of the timed steps.  stochastic: drafts drawn from the drafter's own distributions."""
     from speculative_decoding_dflash_amd import binding as Bd
     taus = torch.zeros(warmup + steps, dtype=torch.int32, device="cuda")
     eng.prefill([0], prompt.view(1, -1), [samp])
     for i in range(warmup):
-        eng.spec_step([0], [samp], planted=None if planted is None else planted[i])
+        eng.spec_step([0], [samp], planted=None if planted is None else planted[i], stochastic=stochastic)
         taus[i:i + 1].copy_(eng.n_out[:1])
     g = pl = None
     if graph and not profile:
         pl = None if planted is None else planted[0].clone()
-        g = eng.capture_spec_step([0], [samp], planted=pl)
+        g = eng.capture_spec_step([0], [samp], planted=pl, stochastic=stochastic)
     tm = Timer(torch)
     tm.start()
     if profile:
@@ -111,7 +112,7 @@ def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=Fals
                 pl.copy_(planted[i])
             g.replay()
         else:
-            eng.spec_step([0], [samp], planted=None if planted is None else planted[i])
+            eng.spec_step([0], [samp], planted=None if planted is None else planted[i], stochastic=stochastic)
         taus[i:i + 1].copy_(eng.n_out[:1])
     ms = tm.stop()
     eng.status()
@@ -235,6 +236,14 @@ def main():
     log(f"[bench]   tau {tau:.3f}, {ms_step:.3f} ms/step, {tok_s:.1f} tok/s, "
         f"{bytes_step / ms_step / 1e6:.0f} GB/s algorithmic")
 
+    # 1b. the same configuration with stochastic drafts (each draft drawn from the drafter's own
+    #     filtered distribution, accepted with min(1, p/q))
+    ms_q, taus_q = run_spec(eng, torch, prompt, s_conf, Wm, K, graph=graph, stochastic=True)
+    tq = taus_q[Wm:]
+    stoch = {"tok_s": round(sum(tq) / (ms_q / 1e3), 2), "ms_per_step": round(ms_q / K, 4),
+             "tau": round(sum(tq) / K, 4)}
+    log(f"[bench]   stochastic drafts: {stoch}")
+
     # 2. roofline of the projection kernel: record the projection launches of one decode step, then
     #    replay exactly those launches back to back under one pair of HIP events on the step's stream
     run_spec(eng, torch, prompt, s_conf, 1, 1, profile=True)
@@ -325,6 +334,7 @@ def main():
         "step_bytes": bytes_step,
         "ar_baseline": ar,
         "tau_sweep_planted_greedy": sweep,
+        "stochastic_drafts": stoch,
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel + gemm_sk_kernel (all projections of the step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -144,7 +144,7 @@ class Engine:
         self.accept(slots, self.B - 1, samplings, cands=cands, q=stochastic)
 
     def capture_spec_step(self, slots: Sequence[int], samplings: Sequence[B.Sampling],
-                          planted: Optional[torch.Tensor] = None) -> "torch.cuda.CUDAGraph":
+                          planted: Optional[torch.Tensor] = None, stochastic: bool = False) -> "torch.cuda.CUDAGraph":
         """Captures one spec_step (draft -> verify -> accept) into a HIP graph; each replay performs the
         next step.  Every launch parameter of a step is fixed on the host for fixed slots and KV
         allocations (positions, lengths and the accepted tokens live in device memory), so one capture
@@ -153,7 +153,7 @@ class Engine:
         then only replay.  planted: a fixed device tensor copied into the drafts at every replay."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.spec_step(slots, samplings, planted=planted)
+            self.spec_step(slots, samplings, planted=planted, stochastic=stochastic)
         return g
 
     def ar_step(self, slots: Sequence[int], samplings: Sequence[B.Sampling]):

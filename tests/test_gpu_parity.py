@@ -389,13 +389,14 @@ def test_op_linear(dtype, M, N, K):
     assert err < 1e-5
 
 
+@pytest.mark.parametrize("stochastic", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "small"])
-def test_graph_replay_equals_eager_steps(name):
+def test_graph_replay_equals_eager_steps(name, stochastic):
     """A speculative step captured into a HIP graph and replayed performs exactly the eager steps: same
     emitted tokens, acceptance counts, drafts and logits at every replay, with eager work and device
-    synchronisation between the replays."""
+    synchronisation between the replays (argmax drafts and stochastic drafts)."""
     cfg = CASES[name]()
-    log(f"[graph replay] {name}")
+    log(f"[graph replay] {name} stochastic={stochastic}")
     W = sw.model_weights(cfg)
     P, B, V = cfg.prompt_len, cfg.drafter.block_size, cfg.target.vocab
     steps = 6
@@ -406,13 +407,13 @@ def test_graph_replay_equals_eager_steps(name):
         eng = engine(cfg, W)
         eng.kv_alloc(0, P + (steps + 2) * B)
         eng.prefill([0], prompt.view(1, -1), [s])
-        g = eng.capture_spec_step([0], [s]) if use_graph else None
+        g = eng.capture_spec_step([0], [s], stochastic=stochastic) if use_graph else None
         rec = []
         for _ in range(steps):
             if g is not None:
                 g.replay()
             else:
-                eng.spec_step([0], [s])
+                eng.spec_step([0], [s], stochastic=stochastic)
             torch.cuda.synchronize()
             n = int(eng.n_out[0])
             rec.append((n, eng.out[:n].cpu().clone(), eng.block[:B].cpu().clone(), eng.logits[: B * V].cpu().clone()))
