@@ -147,11 +147,17 @@ struct dflash_ctx {
   int last_qlen = 0, last_nlogit = 0, last_batch = 0;
   std::vector<int32_t> last_slots;
   bool verified = false;
+  // Set while a prefill (a verify that starts sequences) runs: its projections may take the tiled
+  // large-M kernel.  Every other call keeps the row-chunked kernels, whose result for a row does not
+  // depend on how many rows share the launch, so a decode step computes the same bits whether it is
+  // issued eagerly or replayed from a graph captured at another row count.
+  bool tiled = false;
   // measurement: the projection launches issued while profiling is on, kept for replay
   bool profiling = false;
   struct Rec {
     GemmArgs a;
     int rows;
+    bool tiled;
   };
   std::vector<Rec> recorded;
 
@@ -195,9 +201,19 @@ GemmArgs gemm_base(const void *x, int ldx, int M, int N, int K, int epi) {
 }
 
 // Run a GEMM over R rows in chunks of kGemmMaxRows.  `a.x` points at row 0; input rows advance by ldx.
+// tiled: the call may instead run all R rows at once on the tiled large-M kernel when the shape suits it.
 // e0 / e1 (may be null) time the first chunk's start and the last chunk's end.
-dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s, hipEvent_t e0 = nullptr,
+dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_t s, hipEvent_t e0 = nullptr,
                        hipEvent_t e1 = nullptr) {
+  if (tiled) {
+    GemmArgs b = a;
+    b.M = R;
+    b.row_off = 0;
+    if (gemm_mm_ok(b, dt)) {
+      HIP_OK(launch_gemm(b, dt, s, e0, e1));
+      return DFLASH_OK;
+    }
+  }
   const char *x0 = (const char *)a.x;
   for (int r0 = 0; r0 < R; r0 += kGemmMaxRows) {
     GemmArgs b = a;
@@ -214,8 +230,8 @@ dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
   a.sk_cnt = c->wsp<int32_t>(c->L.skc);
   a.sk_max_wg = kSkMaxWg;
   a.sk_max_tiles = c->L.sk_tiles;
-  if (c->profiling) c->recorded.push_back({a, R});
-  return run_gemm(c->es(), c->dt(), a, R, s);
+  if (c->profiling) c->recorded.push_back({a, R, c->tiled});
+  return run_gemm(c->es(), c->dt(), a, R, c->tiled, s);
 }
 
 // A projection whose K ranges write fp32 partial slices [range][R][N] into the partial buffer; the
@@ -668,6 +684,11 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   const int ctx_bound = c->max_ctx(slots, batch);
   const int ld_feat = c->dcfg.n_taps * H;
   const int nl = n_logit_rows;
+  struct TiledScope {  // a prefill's projections may take the tiled kernel; cleared on every exit
+    dflash_ctx *c;
+    ~TiledScope() { c->tiled = false; }
+  } tiled_scope{c};
+  c->tiled = new_sequence != 0;
   for (int l = 0; l < m.layers; ++l) {
     void *feat = nullptr;
     for (int t = 0; t < c->dcfg.n_taps; ++t)
@@ -916,7 +937,7 @@ dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t 
   a.seg[0] = GemmSeg{d_w, N};
   a.out_f32 = d_y;
   a.ld_out = N;
-  return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, s);
+  return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, true, s);
 }
 
 dflash_status dflash_profile(dflash_ctx *c, int32_t enable) {
@@ -943,7 +964,7 @@ dflash_status dflash_profile_replay(dflash_ctx *c, hipStream_t s, int32_t iters,
   HIP_OK(hipEventRecord(e0, s));
   for (int it = 0; it < iters; ++it)
     for (const auto &r : c->recorded) {
-      dflash_status st = run_gemm(c->es(), c->dt(), r.a, r.rows, s);
+      dflash_status st = run_gemm(c->es(), c->dt(), r.a, r.rows, r.tiled, s);
       if (st != DFLASH_OK) return st;
     }
   HIP_OK(hipEventRecord(e1, s));

@@ -513,12 +513,185 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   }
 }
 
+// Large-M projections (prefill, large batches; bf16): an MFMA-bound tiled GEMM.  A work-group owns a
+// 128 x 128 output tile (SWIGLU: 64 output columns, their 64 gate and 64 up weight rows interleaved in
+// 16-row groups so that a lane holds a column's gate and up sums), 4 waves of 64 x 64, K in steps of
+// 64: the next step's X and W tiles are loaded into registers (16 bytes per thread and row chunk)
+// while the current step's tiles are multiplied out of LDS (double buffer, one barrier per step),
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  The epilogues compute the same values as the
+// skinny kernel's (residual add + deferred RMSNorm inputs with per-32-column sums of squares,
+// SwiGLU, fp32 / activation stores, the 1/rms row scale).  Needs K % 64 == 0 and N (SWIGLU: output
+// columns) a multiple of the tile width with every segment a whole number of tiles.
+constexpr int kMmBM = 128, kMmBN = 128, kMmBK = 64;
+__global__ __launch_bounds__(256) void gemm_mm_kernel(GemmArgs a) {
+  using F = Frag<bf16>;
+  constexpr int BM = kMmBM, BN = kMmBN, BK = kMmBK, LDK = BK + 8;  // LDS row stride 144 B
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * LDK], sB[2][BN * LDK];
+  __shared__ float s_rstd[BM];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  const int m0 = blockIdx.y * BM;
+  const int n0 = blockIdx.x * (swiglu ? BN / 2 : BN);  // first output column of the tile
+  const int K = a.K;
+  // this thread's four 16-byte chunks of each tile per K step: chunk c = tid + 256 i -> row c / 8,
+  // elements 8 (c % 8) .. + 7 of the step's 64
+  const bf16 *pa[4], *pb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
+    pa[i] = (const bf16 *)a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + kc;
+    const bf16 *w;
+    if (swiglu) {  // B row -> (16-column group p = row / 32, gate or up = row / 16 % 2)
+      const int col = n0 + 16 * (row >> 5) + (row & 15);
+      w = (const bf16 *)a.seg[(row >> 4) & 1].w + (size_t)col * K;
+    } else {
+      int nr = n0 + row, si = 0;
+      while (si + 1 < a.nseg && nr >= a.seg[si].n) {
+        nr -= a.seg[si].n;
+        ++si;
+      }
+      w = (const bf16 *)a.seg[si].w + (size_t)nr * K;
+    }
+    pb[i] = w + kc;
+  }
+  if (tid < BM) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  u32x4 ra[4], rb[4];
+  auto load = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = ld16(pa[i] + k);
+      rb[i] = ld16(pb[i] + k);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, off = (c >> 3) * LDK + (c & 7) * 8;
+      *reinterpret_cast<u32x4 *>(&sA[buf][off]) = ra[i];
+      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = rb[i];
+    }
+  };
+  const int nk = K / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+      u32x4 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][(wm * 64 + 16 * i + r16) * LDK + 32 * s + 8 * g]);
+        fb[i] = *reinterpret_cast<const u32x4 *>(&sB[buf][(wn * 64 + 16 * i + r16) * LDK + 32 * s + 8 * g]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) F::mma(acc[i][j], fa[i], fb[j]);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // acc[i][j][r] = Y[row m0 + wm*64 + 16 i + 4 g + r][tile column wn*64 + 16 j + r16]
+  const bool rs = a.ss_in != nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ml = wm * 64 + 16 * i + 4 * g + r, m = m0 + ml;
+      const bool live = m < a.M;
+      const float sc = rs ? s_rstd[ml] : 1.f;
+      const int grow = a.row_off + m;
+      switch (a.epi) {
+        case EPI_STORE_F32:
+        case EPI_PARTIAL:
+          if (live)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              a.out_f32[(size_t)grow * a.ld_out + n0 + wn * 64 + 16 * j + r16] = acc[i][j][r] * sc;
+          break;
+        case EPI_STORE_ACT:
+          if (live)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              Elem<bf16>::store((bf16 *)a.out_act + (size_t)grow * a.ld_out + n0 + wn * 64 + 16 * j + r16, acc[i][j][r]);
+          break;
+        case EPI_SWIGLU:
+          if (live)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float gt = acc[i][2 * q][r] * sc, up = acc[i][2 * q + 1][r] * sc;
+              Elem<bf16>::store((bf16 *)a.out_act + (size_t)grow * a.ld_out + n0 + 16 * (2 * wn + q) + r16,
+                                silu(gt) * up);
+            }
+          break;
+        case EPI_RESID_NORM: {
+          const int jj = grow % a.sel_stride - a.sel_offset;
+          const bool sel = live && jj >= 0 && jj < a.sel_take;
+          const size_t o = (size_t)(grow / a.sel_stride) * a.sel_take + jj;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {  // the wave's two 32-column groups
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 2 * h; j < 2 * h + 2; ++j) {
+              const int n = n0 + wn * 64 + 16 * j + r16;
+              float v = acc[i][j][r];
+              if (live) {
+                if (a.resid) {
+                  const size_t idx = (size_t)grow * a.ld_resid + n;
+                  v += a.resid[idx];
+                  a.resid[idx] = v;
+                }
+                if (a.feat) Elem<bf16>::store((bf16 *)a.feat + (size_t)grow * a.ld_feat + n, v);
+                if (sel) Elem<bf16>::store((bf16 *)a.xg + o * a.ld_xg + n, v * a.gain[n]);
+              }
+              ss += v * v;
+            }
+            // sum over the group's 32 columns: the 16 lanes of this row (same g) hold 2 columns each
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            ss += __shfl_xor(ss, 4);
+            ss += __shfl_xor(ss, 8);
+            if (sel && r16 == 0) a.ss_out[o * a.ss_out_ld + (n0 + wn * 64 + 32 * h) / 32] = ss;
+          }
+          break;
+        }
+      }
+    }
+}
+
 namespace {
 int env_int(const char *name, int dflt) {
   const char *e = getenv(name);
   return e ? atoi(e) : dflt;
 }
 }  // namespace
+
+// The tiled kernel takes a projection when it is bf16, at least kMmMinRows rows and tile-shaped
+// (DFLASH_GEMM_MM=0, read per call, sends every projection to the row-chunked kernels instead).
+constexpr int kMmMinRows = 128;
+bool gemm_mm_ok(const GemmArgs &a, int dtype) {
+  if (dtype != 0 || a.M < kMmMinRows || a.ksplit != 1 || a.K % kMmBK) return false;
+  if (env_int("DFLASH_GEMM_MM", 1) == 0) return false;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  const int tn = swiglu ? kMmBN / 2 : kMmBN;
+  if (a.N % tn) return false;
+  if (!swiglu)
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].n % kMmBN) return false;
+  return true;
+}
 
 template <typename T, int MT, int CT, int NW, int XR>
 static void launch_xr(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
@@ -653,6 +826,12 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
     return hipErrorInvalidValue;
   if (a.ss_in && (a.ss_n < 1 || a.norm_dim < 1 || a.ss_ld % 4 || a.ss_n > a.ss_ld)) return hipErrorInvalidValue;
   if (a.epi == EPI_RESID_NORM && a.N / 32 > a.ss_out_ld) return hipErrorInvalidValue;
+  if (gemm_mm_ok(a, dtype)) {
+    const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
+    const dim3 grid(a.N / tn, (a.M + kMmBM - 1) / kMmBM), block(256);
+    hipExtLaunchKernelGGL(gemm_mm_kernel, grid, block, 0, s, e0, e1, 0, a);
+    return hipGetLastError();
+  }
   int n_wg = 0;
   if (const int per = sk_per(a, dtype, &n_wg)) {
     const dim3 grid(n_wg), block(512);

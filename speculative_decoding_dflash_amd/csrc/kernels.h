@@ -63,6 +63,8 @@ constexpr int kSkTileElems = 16 * 32;  // entries of one partial tile (16 rows x
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// Whether launch_gemm runs `a` (all of its M rows at once) on the tiled large-M kernel.
+bool gemm_mm_ok(const GemmArgs &a, int dtype);
 // K ranges for an EPI_PARTIAL projection of M rows: enough work-groups to cover the CUs several times
 // over, each range a whole number of 256-byte super-steps, and split * M * N <= cap_elems.
 int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);

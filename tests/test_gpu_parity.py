@@ -48,10 +48,11 @@ CASES = {
     "small": lambda: small_short(),
     "tiny_bf16": lambda: _variant(synth.TINY, dtype="bf16"),
     "small_fp32": lambda: _variant(small_short(32), dtype="fp32"),
+    "small_p300": lambda: small_short(300),
 }
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "tiny_bf16", "small_fp32"])
+@pytest.mark.parametrize("name", ["tiny", "small", "tiny_bf16", "small_fp32", "small_p300"])
 def test_prefill_logits_and_features(name):
     cfg = CASES[name]()
     log(f"[prefill] {name}")
@@ -149,7 +150,7 @@ def test_e2e_teacher_forced(name, mode):
 
 
 @pytest.mark.parametrize("variant", ["separate_post", "last_arriver", "one_page_splits", "gemm_one_tile_per_wg",
-                                     "gemm_stream_k_all"])
+                                     "gemm_stream_k_all", "prefill_row_chunks"])
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_e2e_kernel_variants(name, variant, monkeypatch):
     """The non-default kernel variants match the oracle like the defaults.  Attention (default: q / k / v
@@ -158,11 +159,13 @@ def test_e2e_kernel_variants(name, variant, monkeypatch):
     small model with a 320-token prompt: more than 16 splits, the merge kernel's general path).
     Projections (default: stream-K for the residual + norm and SwiGLU projections at M <= 16, one tile
     per work-group elsewhere): one tile per work-group everywhere; stream-K wherever the shape allows
-    (q/k/v, LM heads, drafter k/v too)."""
+    (q/k/v, LM heads, drafter k/v too).  Prefill (default: the tiled large-M kernel for bf16 prompts of
+    128+ rows): the row-chunked kernels."""
     monkeypatch.setenv("DFLASH_ATTN_FUSED", "0" if variant == "separate_post" else "1")
     monkeypatch.setenv("DFLASH_ATTN_MERGE", "1" if variant == "last_arriver" else "0")
     monkeypatch.setenv("DFLASH_ATTN_PPS", "1" if variant == "one_page_splits" else "0")
     monkeypatch.setenv("DFLASH_GEMM_SK", {"gemm_one_tile_per_wg": "0", "gemm_stream_k_all": "1"}.get(variant, "-1"))
+    monkeypatch.setenv("DFLASH_GEMM_MM", "0" if variant == "prefill_row_chunks" else "1")
     cfg = small_short(prompt_len=320) if (variant, name) == ("one_page_splits", "small") else CASES[name]()
     log(f"[e2e kernel variant] {name} {variant}")
     W = sw.model_weights(cfg, gain_std=0.1)
@@ -366,7 +369,8 @@ def test_gpu_generator_matches_cpu():
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (4, 384, 128), (8, 7168, 5120), (13, 5120, 17408), (64, 256, 1024),
-                                   (37, 512, 96), (100, 160, 64)])
+                                   (37, 512, 96), (100, 160, 64), (128, 256, 1024), (300, 512, 2816),
+                                   (1024, 7168, 5120)])
 def test_op_linear(dtype, M, N, K):
     """The projection kernel against float64 matmul of the same (storage-typed) inputs, tiles and ragged
     row counts included; fp32 accumulation bounds the error."""
