@@ -119,6 +119,41 @@ def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=Fals
     return ms, [int(x) for x in taus.cpu().tolist()]
 
 
+def step_bytes_batch(cfg, ns) -> float:
+    """step_bytes for a batch of requests at committed lengths ns: the weights are read once per step
+    whatever the batch, the KV and logits terms once per request."""
+    one_req = [step_bytes(cfg, n) for n in ns]
+    w = step_bytes(cfg, 0) - _kv_logit_bytes(cfg, 0)
+    return float(w + sum(b - w for b in one_req))
+
+
+def _kv_logit_bytes(cfg, n: int) -> float:
+    t, d = cfg.target, cfg.drafter
+    e = 2 if t.dtype == "bf16" else 4
+    B = d.block_size
+    kv_t, kv_d = t.layers * 2 * t.kv_dim * e, d.layers * 2 * t.kv_dim * e
+    keys_d = (min(n, d.window) if d.window else n) + B
+    return float((n + B) * kv_t + keys_d * kv_d + B * (kv_t + kv_d) + 2 * 4 * (2 * B - 1) * t.vocab)
+
+
+def step_flops_batch(cfg, ns, taus) -> float:
+    """Algorithmic flops of one batched step: 2 per multiply-add of every projection over the rows
+    that pass through it (block rows through both models, the drafter's LM head on B-1 rows, the
+    injection over the rows committed by the previous step) plus both attentions (QK^T and PV over
+    every key a query sees)."""
+    t, d = cfg.target, cfg.drafter
+    B, H, V = d.block_size, t.hidden, t.vocab
+    c = len(ns)
+    lp = t.layer_params()
+    f = 2.0 * c * B * (t.layers * lp + V * H)                      # verify + target LM head
+    f += 2.0 * c * B * d.layers * lp + 2.0 * c * (B - 1) * V * H   # drafter block forward + shared LM head
+    f += 2.0 * sum(taus) * (len(d.taps) * H * H + d.layers * 2 * t.kv_dim * H)  # injection
+    for n in ns:
+        f += 4.0 * B * t.q_heads * t.head_dim * (n + B) * t.layers
+        f += 4.0 * B * t.q_heads * t.head_dim * ((min(n, d.window) if d.window else n) + B) * d.layers
+    return f
+
+
 def cpu_baseline(cfg, tau: float):
     """The oracle (float64 numpy, as it stands) on a bounded sample of one step of the workload: one
     27B-shaped target layer over a block of 8 at context 1536 (random cache contents), the LM head over
@@ -166,6 +201,192 @@ def cpu_baseline(cfg, tau: float):
                       f"tau {tau:.3f}"}
 
 
+MFMA_PEAK_TFS = 2500.0  # dense bf16 MFMA, MI355X published
+
+
+def batch_main(args, cfg, conc: int):
+    """Batched steps: `conc` requests decoded together (each step verifies conc x B rows and drafts
+    conc blocks).  Requests are prefilled one by one (prompt lengths from the workload: fixed, or
+    uniform over the long-context range), their prompts injected into the drafter, then every timed
+    step is one captured HIP graph of verify -> accept -> draft over all requests.  Printed: one JSON
+    line with accepted tokens/s of the configured run (T=1 / top-k / top-p, real drafter) and a
+    planted sweep under greedy verification (every request forced to acceptance length tau*), each
+    with the step's algorithmic HBM and MFMA fractions."""
+    import numpy as np
+    import torch
+
+    from synth import gpu as sgpu
+    from synth import weights as sw
+    from speculative_decoding_dflash_amd import binding as Bd
+    from speculative_decoding_dflash_amd.runner import Engine, sampling
+
+    t, d = cfg.target, cfg.drafter
+    B, V = d.block_size, t.vocab
+    K, Wm = args.steps, args.warmup
+    if cfg.prompt_len_range:
+        lens = [int(x) for x in sw.prompt_lengths(cfg.prompt_len_range[0], cfg.prompt_len_range[1], conc, 0)]
+    else:
+        lens = [cfg.prompt_len] * conc
+    taus_sweep = [int(x) for x in args.tau_sweep.split(",")] if args.tau_sweep else list(range(1, B + 1))
+    log(f"[bench] {cfg.name}, concurrency {conc}, prompt lengths {min(lens)}..{max(lens)} "
+        f"(mean {sum(lens) / conc:.0f}): generating weights on the GPU")
+    weights = sgpu.model_weights(cfg)
+    torch.cuda.synchronize()
+    n_ar = (Wm + K + 1) * B + 2 * B  # greedy tokens needed per request by the planted sweep
+    max_tokens = max(lens) + max(n_ar, (Wm + K + 2) * B) + 2 * B
+    eng = Engine(cfg, weights, max_slots=conc, max_rows=max(max(lens), conc * B),
+                 max_pages_per_seq=max_tokens // 16 + 4)
+    slots = list(range(conc))
+    for r in slots:
+        eng.kv_alloc(r, max_tokens)
+    prompts = [torch.from_numpy(sw.prompt_ids(V, d.mask_id, lens[r], r)).to("cuda") for r in slots]
+    sp = cfg.sampling
+    s_conf = sampling(sp.temperature, sp.top_k, sp.top_p, sp.seed)
+    s_greedy = sampling(0.0, 0, 1.0, 1)
+
+    def prefill_all(samp, inject=True):
+        """Prefill every request; returns (seconds, first tokens [conc] on the device)."""
+        first = torch.zeros(conc, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for r in slots:
+            eng.prefill([r], prompts[r].view(1, -1), [samp])
+            first[r:r + 1].copy_(eng.out[:1])
+            if inject:  # the prompt's features go into the drafter cache before the next prefill
+                Bd.dflash_draft_block(eng.ctx, [r], eng.feats, eng.block[r * B:], None)
+        torch.cuda.synchronize()
+        return time.time() - t0, first
+
+    def step(samp, pl=None):
+        eng.verify(slots, eng.block, B, False, B)
+        eng.accept(slots, B - 1, [samp] * conc)
+        eng.draft(slots)
+        if pl is not None:
+            eng.block.view(-1, B)[:conc, 1:] = pl
+
+    def run(samp, planted=None):
+        """Prefill, warmup steps, then K timed replays of the captured step; returns (ms, taus [steps][conc],
+        committed lengths at the start of every timed step)."""
+        sec, _ = prefill_all(samp)
+        if planted is not None:
+            eng.block.view(-1, B)[:conc, 1:] = planted[0]
+        taus = torch.zeros(Wm + K, conc, dtype=torch.int32, device="cuda")
+        for i in range(Wm):
+            step(samp, None if planted is None else planted[i + 1])
+            taus[i].copy_(eng.n_out[:conc])
+        pl = None if planted is None else planted[Wm + 1].clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(samp, pl)
+        tm = Timer(torch)
+        tm.start()
+        for i in range(Wm, Wm + K):
+            if pl is not None:
+                pl.copy_(planted[i + 1])
+            g.replay()
+            taus[i].copy_(eng.n_out[:conc])
+        ms = tm.stop()
+        eng.status()
+        tl = taus.cpu().numpy()
+        ns = [[lens[r] + int(tl[:i, r].sum()) for r in slots] for i in range(Wm, Wm + K)]
+        return ms, tl[Wm:], ns, sec
+
+    def summary(ms, tl, ns):
+        tok = int(tl.sum())
+        byt = sum(step_bytes_batch(cfg, n) for n in ns) / K
+        # the injection of step i covers the rows committed by step i-1
+        fl = sum(step_flops_batch(cfg, ns[i], tl[i - 1] if i > 0 else tl[0]) for i in range(K)) / K
+        mss = ms / K
+        return {"tok_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(mss, 3),
+                "tau": round(tok / (K * conc), 4),
+                "step_hbm_gbs": round(byt / (mss / 1e3) / 1e9, 1),
+                "step_hbm_frac": round(byt / (mss / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "step_tflops": round(fl / (mss / 1e3) / 1e12, 1),
+                "step_mfma_frac": round(fl / (mss / 1e3) / 1e12 / MFMA_PEAK_TFS, 4),
+                "step_bytes": byt, "step_flops": fl}
+
+    log(f"[bench] configured run: {Wm} warmup + {K} timed steps")
+    ms, tl, ns, pre_s = run(s_conf)
+    conf = summary(ms, tl, ns)
+    log(f"[bench]   {conf} (prefill of all requests {pre_s:.1f} s)")
+
+    # projection roofline at this batch: the projection launches of one eager step, replayed
+    prefill_all(s_conf)
+    Bd.dflash_profile(eng.ctx, True)
+    step(s_conf)
+    Bd.dflash_profile(eng.ctx, False)
+    torch.cuda.synchronize()
+    reps = args.profile_steps
+    rep_ms, rep_bytes, rep_n = Bd.dflash_profile_replay(eng.ctx, reps)
+    gemm_ms = rep_ms / reps
+    rows_proj = conc * B
+    log(f"[bench] projections: {rep_n} launches per step, {gemm_ms:.3f} ms replayed back to back, "
+        f"{rep_bytes / (gemm_ms / 1e3) / 1e9:.0f} GB/s")
+
+    sweep = {}
+    if not args.no_sweep:
+        # The greedy stream of every request, emitted by greedy speculative decoding over the same batch:
+        # a verify row's logits depend only on its prefix, so the planted runs below (same kernels, same
+        # batch) reproduce it exactly, where plain decoding (other row tiles, other fp32 summation
+        # orders) may part from it at a near tie.
+        log(f"[bench] greedy stream for the planted drafter: {n_ar} tokens per request")
+        _, first = prefill_all(s_greedy)
+        gen = [[int(x)] for x in first.cpu().tolist()]
+        while min(len(x) for x in gen) < n_ar:
+            step(s_greedy)
+            taus = eng.n_out[:conc].cpu().tolist()
+            outs = eng.out[:conc * B].view(conc, B).cpu().numpy()
+            for r in slots:
+                gen[r].extend(int(x) for x in outs[r, :taus[r]])
+        eng.status()
+        G = [np.concatenate([prompts[r].cpu().numpy(), np.array(gen[r][:n_ar])]).astype(np.int64) for r in slots]
+        for ts in taus_sweep:
+            plans = []
+            for i in range(Wm + K + 1):
+                plans.append(np.stack([sw.planted_drafts(G[r], lens[r] + ts * i, B - 1, V, d.mask_id, 0.0,
+                                                         force_reject_at=ts if ts < B else None) for r in slots]))
+            planted = torch.from_numpy(np.stack(plans)).to("cuda")
+            ms_p, tl_p, ns_p, _ = run(s_greedy, planted)
+            assert (tl_p == ts).all(), (ts, tl_p)
+            sweep[str(ts)] = {k: v for k, v in summary(ms_p, tl_p, ns_p).items() if k not in ("step_bytes", "step_flops")}
+            log(f"[bench]   planted tau*={ts}: {sweep[str(ts)]}")
+
+    out = {
+        "metric": f"accepted tokens/s at conc {conc} ({cfg.name}-shape, block {B}); step HBM and MFMA fractions",
+        "value": conf["tok_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": conf["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if t.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}-shaped target ({t.layers} layers, hidden {t.hidden}, {t.q_heads}q/{t.kv_heads}kv x "
+                        f"{t.head_dim}, FFN {t.ffn}, vocab {t.vocab}) + {d.layers}-layer drafter (window {d.window}, "
+                        f"taps {list(d.taps)}); block {B}, concurrency {conc}, prompts of "
+                        + (f"{min(lens)}..{max(lens)} (uniform over {cfg.prompt_len_range}, mean "
+                           f"{sum(lens) / conc:.0f})" if cfg.prompt_len_range else f"{lens[0]}")
+                        + f" uniform ids, T={sp.temperature}/top-k {sp.top_k}/top-p {sp.top_p}, Philox seed {sp.seed}",
+            "block": B, "concurrency": conc, "prompt_lens": [min(lens), max(lens), round(sum(lens) / conc, 1)],
+        },
+        "configured": conf,
+        "prefill_s": round(pre_s, 2),
+        "prefill_tok_s": round(sum(lens) / pre_s, 1),
+        "tau_sweep_planted_greedy": sweep,
+        "projections": {"launches_per_step": rep_n, "ms_per_step": round(gemm_ms, 4), "rows": rows_proj,
+                        "hbm_gbs": round(rep_bytes / (gemm_ms / 1e3) / 1e9, 1),
+                        "hbm_frac": round(rep_bytes / (gemm_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "method": "the projection launches of one eager step recorded by the library and replayed "
+                                  f"{reps} times back to back between two HIP events on the step's stream"},
+    }
+    print(json.dumps(out), flush=True)
+    eng.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +399,10 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=8, help="replay passes for the projection roofline")
     ap.add_argument("--no-graph", action="store_true", help="issue every timed step eagerly instead of replaying "
                                                             "a captured HIP graph of the step")
+    ap.add_argument("--concurrency", type=int, default=None,
+                    help="requests decoded together (default: the workload's own, 1 for 27b); above 1 the "
+                         "batched measurement runs instead of the concurrency-1 line")
+    ap.add_argument("--tau-sweep", default="", help="planted acceptance lengths of the batched sweep, e.g. 1,3,5,7")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first copy 1 GiB device to device (a plain copy of known size, the reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -197,6 +422,10 @@ def main():
     from speculative_decoding_dflash_amd.runner import Engine, sampling
 
     cfg = synth.CONFIGS[args.config]
+    conc = args.concurrency or cfg.concurrency
+    if conc > 1 or cfg.prompt_len_range:
+        batch_main(args, cfg, conc)
+        return
     t, d = cfg.target, cfg.drafter
     B, P, V = d.block_size, cfg.prompt_len, t.vocab
     K, Wm = args.steps, args.warmup

@@ -237,7 +237,8 @@ dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int
  * profiling disabled, re-issues exactly those launches `iters` times back to back on `stream`
  * (the optional feature-tap side output is suppressed; every other buffer they write is workspace
  * scratch), bracketed by one pair of HIP events, and returns the elapsed ms, the algorithmic weight
- * bytes of one pass over the recorded launches and their number.  Enabling clears the record. */
+ * bytes of one pass over the recorded launches (every weight once per projection) and the number of
+ * recorded projections.  Enabling clears the record. */
 dflash_status dflash_profile(dflash_ctx *ctx, int32_t enable);
 dflash_status dflash_profile_replay(dflash_ctx *ctx, hipStream_t stream, int32_t iters, double *ms, double *bytes,
                                     int32_t *launches);

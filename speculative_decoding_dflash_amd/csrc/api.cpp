@@ -44,9 +44,9 @@ constexpr int kSkMaxWg = 1024;  // stream-K projection work-groups (one per CU)
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, att_o, att_ml, dlogits, cid,
-      cp, cn, skey, sidx, total;
-  size_t part_elems, att_rows;
+  size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, mbr, att_o, att_ml, dlogits,
+      cid, cp, cn, skey, sidx, total;
+  size_t part_elems, att_rows, mbr_elems;
   int ss_ld, sk_tiles;
 };
 
@@ -87,6 +87,11 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.part_elems = std::max(R, (size_t)kMaxKSplit * kGemmMaxRows) * part_cols;
   L.part = take(sizeof(float) * L.part_elems);
   L.skp = take(sizeof(float) * kSkMaxWg * 2 * kSkTileElems);  // stream-K partial tiles
+  // raw K-range sums of a decode-batch projection (kMbMinRows .. kMbMaxRows rows): room for
+  // kMbMaxSplit ranges of the widest hidden-size output (the launcher uses fewer ranges otherwise)
+  const size_t rdec = std::min<size_t>((size_t)cap->max_slots * B, kMbMaxRows);
+  L.mbr_elems = rdec >= (size_t)kMbMinRows ? kMbMaxSplit * rdec * part_cols : 0;
+  L.mbr = take(sizeof(float) * std::max<size_t>(L.mbr_elems, 1));
   L.att_rows = (size_t)cap->max_slots * B;
   L.att_o = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * c->head_dim);
   L.att_ml = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * 2);
@@ -205,12 +210,17 @@ GemmArgs gemm_base(const void *x, int ldx, int M, int N, int K, int epi) {
 // e0 / e1 (may be null) time the first chunk's start and the last chunk's end.
 dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_t s, hipEvent_t e0 = nullptr,
                        hipEvent_t e1 = nullptr) {
-  if (tiled) {
+  {
     GemmArgs b = a;
     b.M = R;
     b.row_off = 0;
-    if (gemm_mm_ok(b, dt)) {
+    if (tiled && gemm_mm_ok(b, dt)) {
       HIP_OK(launch_gemm(b, dt, s, e0, e1));
+      return DFLASH_OK;
+    }
+    // decode batches: all rows in one launch instead of row chunks that each stream the weights
+    if (!tiled && gemm_mb_ok(b, dt)) {
+      HIP_OK(launch_gemm_mb(b, s, e0, e1));
       return DFLASH_OK;
     }
   }
@@ -230,6 +240,8 @@ dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
   a.sk_cnt = c->wsp<int32_t>(c->L.skc);
   a.sk_max_wg = kSkMaxWg;
   a.sk_max_tiles = c->L.sk_tiles;
+  a.mb_raw = c->L.mbr_elems ? c->wsp<float>(c->L.mbr) : nullptr;
+  a.mb_raw_cap = (int64_t)c->L.mbr_elems;
   if (c->profiling) c->recorded.push_back({a, R, c->tiled});
   return run_gemm(c->es(), c->dt(), a, R, c->tiled, s);
 }
@@ -953,10 +965,9 @@ dflash_status dflash_profile_replay(dflash_ctx *c, hipStream_t s, int32_t iters,
   if (c->profiling) return fail(DFLASH_E_STATE, "disable profiling before replaying");
   double by = 0.0;
   int n = 0;
-  for (const auto &r : c->recorded) {
-    const int chunks = (r.rows + kGemmMaxRows - 1) / kGemmMaxRows;
-    by += (double)r.a.N * (r.a.epi == EPI_SWIGLU ? 2 : 1) * r.a.K * c->es() * chunks;
-    n += chunks;
+  for (const auto &r : c->recorded) {  // algorithmic bytes: every weight once per projection
+    by += (double)r.a.N * (r.a.epi == EPI_SWIGLU ? 2 : 1) * r.a.K * c->es();
+    ++n;
   }
   hipEvent_t e0, e1;
   HIP_OK(hipEventCreate(&e0));

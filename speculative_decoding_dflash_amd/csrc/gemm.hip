@@ -25,6 +25,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -522,10 +523,18 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
 // skinny kernel's (residual add + deferred RMSNorm inputs with per-32-column sums of squares,
 // SwiGLU, fp32 / activation stores, the 1/rms row scale).  Needs K % 64 == 0 and N (SWIGLU: output
 // columns) a multiple of the tile width with every segment a whole number of tiles.
+//
+// Decode batches (32 .. 256 rows) use the same kernel with 64-row tiles where M <= 64 and a K split
+// over grid z: narrow projections (o, down: 40 column tiles) would otherwise run on a sixth of the
+// CUs.  Each K range then writes its raw fp32 sums (`raw`, [range][M][N], SWIGLU: gate columns then
+// up columns) and gemm_mb_reduce_kernel adds the ranges in order and runs the epilogue.
 constexpr int kMmBM = 128, kMmBN = 128, kMmBK = 64;
-__global__ __launch_bounds__(256) void gemm_mm_kernel(GemmArgs a) {
+template <int BM>
+__global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw, int steps) {
   using F = Frag<bf16>;
-  constexpr int BM = kMmBM, BN = kMmBN, BK = kMmBK, LDK = BK + 8;  // LDS row stride 144 B
+  constexpr int BN = kMmBN, BK = kMmBK, LDK = BK + 8;  // LDS row stride 144 B
+  constexpr int MI = BM / 32;                          // 16-row fragments per wave (wave tile BM/2 x 64)
+  constexpr int CA = BM / 32;                          // X chunks per thread per K step
   __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * LDK], sB[2][BN * LDK];
   __shared__ float s_rstd[BM];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -535,13 +544,19 @@ __global__ __launch_bounds__(256) void gemm_mm_kernel(GemmArgs a) {
   const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * (swiglu ? BN / 2 : BN);  // first output column of the tile
   const int K = a.K;
-  // this thread's four 16-byte chunks of each tile per K step: chunk c = tid + 256 i -> row c / 8,
+  // this work-group's K steps: [kt0, kt1)
+  const int kt0 = blockIdx.z * steps, kt1 = min(K / BK, kt0 + steps);
+  // this thread's 16-byte chunks of each tile per K step: chunk c = tid + 256 i -> row c / 8,
   // elements 8 (c % 8) .. + 7 of the step's 64
-  const bf16 *pa[4], *pb[4];
+  const bf16 *pa[CA], *pb[4];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
+    pa[i] = (const bf16 *)a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + kc;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
-    pa[i] = (const bf16 *)a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + kc;
     const bf16 *w;
     if (swiglu) {  // B row -> (16-column group p = row / 32, gate or up = row / 16 % 2)
       const int col = n0 + 16 * (row >> 5) + (row & 15);
@@ -556,60 +571,100 @@ __global__ __launch_bounds__(256) void gemm_mm_kernel(GemmArgs a) {
     }
     pb[i] = w + kc;
   }
-  if (tid < BM) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
+  if (!raw && tid < BM) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
 
-  f32x4 acc[4][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  u32x4 ra[4], rb[4];
-  auto load = [&](int k) {
+  // Two register stages: the loads of step kt + 2 are issued while step kt is multiplied out of LDS and
+  // step kt + 1 waits in registers (a work-group streaming weights needs that many bytes in flight);
+  // loads past the range reload the range's last step (never stored).
+  u32x4 ra[2][CA], rb[2][4];
+  auto load = [&](int st, int kt) {
+    const int k = min(kt, kt1 - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ld16(pa[i] + k);
-      rb[i] = ld16(pb[i] + k);
-    }
+    for (int i = 0; i < CA; ++i) ra[st][i] = ld16(pa[i] + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[st][i] = ld16(pb[i] + k);
   };
-  auto store = [&](int buf) {
+  auto store = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + 256 * i, off = (c >> 3) * LDK + (c & 7) * 8;
+      *reinterpret_cast<u32x4 *>(&sA[buf][off]) = ra[st][i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, off = (c >> 3) * LDK + (c & 7) * 8;
-      *reinterpret_cast<u32x4 *>(&sA[buf][off]) = ra[i];
-      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = rb[i];
+      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = rb[st][i];
     }
   };
-  const int nk = K / BK;
-  load(0);
-  store(0);
+  load(0, kt0);
+  load(1, kt0 + 1);
+  store(0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
+  // One K step out of LDS buffer BUF (= its index in the range, mod 2): step kt + 1 waits in register
+  // stage 1 - BUF and step kt + 2 is loaded into stage BUF, freed by the previous step's store.  The
+  // stage and buffer indices are template constants, so the stages stay in registers.
+  // The loads are unconditional (past the range they reload its last step): a load issued on only
+  // some paths would make every later wait count it, so the waits for step kt + 1 would also wait for
+  // step kt + 2.
+  auto kstep = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    load(buf, kt + 2);
 #pragma unroll
     for (int s = 0; s < BK / 32; ++s) {
-      u32x4 fa[4], fb[4];
+      u32x4 fa[MI], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][(wm * 64 + 16 * i + r16) * LDK + 32 * s + 8 * g]);
-        fb[i] = *reinterpret_cast<const u32x4 *>(&sB[buf][(wn * 64 + 16 * i + r16) * LDK + 32 * s + 8 * g]);
-      }
+      for (int i = 0; i < MI; ++i)
+        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][(wm * (BM / 2) + 16 * i + r16) * LDK + 32 * s + 8 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        fb[i] = *reinterpret_cast<const u32x4 *>(&sB[buf][(wn * 64 + 16 * i + r16) * LDK + 32 * s + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) F::mma(acc[i][j], fa[i], fb[j]);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
+    if (kt + 1 < kt1) store(1 - buf, 1 - buf);
     __syncthreads();
+  };
+  int kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < kt1) kstep(kt, std::integral_constant<int, 0>{});
+
+  if (raw) {  // this K range's raw sums: [range][M][N] (SWIGLU: gate columns [0, N), up columns [N, 2N))
+    const int nraw = swiglu ? 2 * a.N : a.N;
+    float *dst = raw + (size_t)blockIdx.z * a.M * nraw;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // SWIGLU: fragment j holds gate (j even) or up (j odd) sums of output column
+          // n0 + 16 (2 wn + j / 2) + r16
+          const int col = swiglu ? (j & 1) * a.N + n0 + 16 * (2 * wn + j / 2) + r16 : n0 + wn * 64 + 16 * j + r16;
+          dst[(size_t)m * nraw + col] = acc[i][j][r];
+        }
+      }
+    return;
   }
 
-  // acc[i][j][r] = Y[row m0 + wm*64 + 16 i + 4 g + r][tile column wn*64 + 16 j + r16]
+  // acc[i][j][r] = Y[row m0 + wm*(BM/2) + 16 i + 4 g + r][tile column wn*64 + 16 j + r16]
   const bool rs = a.ss_in != nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int ml = wm * 64 + 16 * i + 4 * g + r, m = m0 + ml;
+      const int ml = wm * (BM / 2) + 16 * i + 4 * g + r, m = m0 + ml;
       const bool live = m < a.M;
       const float sc = rs ? s_rstd[ml] : 1.f;
       const int grow = a.row_off + m;
@@ -671,6 +726,29 @@ __global__ __launch_bounds__(256) void gemm_mm_kernel(GemmArgs a) {
     }
 }
 
+// Sum of the K ranges of gemm_mm_kernel's raw output, in range order, then the projection's epilogue,
+// for one 32-column tile (SWIGLU: 16 output columns, their gate and up sums) over all M <= 256 rows.
+__global__ __launch_bounds__(256) void gemm_mb_reduce_kernel(GemmArgs a, const float *raw, int ks) {
+  __shared__ float lds[kMbMaxRows * 32];
+  __shared__ float s_rstd[kMbMaxRows];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  const int nraw = swiglu ? 2 * a.N : a.N;
+  const size_t slice = (size_t)a.M * nraw;
+  for (int e = tid; e < a.M * 32; e += 256) {
+    const int m = e >> 5, j = e & 31;
+    const int col = swiglu ? (j < 16 ? 16 * c + j : a.N + 16 * c + j - 16) : 32 * c + j;
+    const float *p = raw + (size_t)m * nraw + col;
+    float v = p[0];
+    for (int z = 1; z < ks; ++z) v += p[z * slice];
+    lds[e] = v;
+  }
+  if (a.ss_in)
+    for (int m = tid; m < a.M; m += 256) s_rstd[m] = gemm_rstd(a, m, false, nullptr);
+  __syncthreads();
+  gemm_epilogue<bf16, 32, 256>(a, c, 0, lds, s_rstd);
+}
+
 namespace {
 int env_int(const char *name, int dflt) {
   const char *e = getenv(name);
@@ -682,7 +760,8 @@ int env_int(const char *name, int dflt) {
 // (DFLASH_GEMM_MM=0, read per call, sends every projection to the row-chunked kernels instead).
 constexpr int kMmMinRows = 128;
 bool gemm_mm_ok(const GemmArgs &a, int dtype) {
-  if (dtype != 0 || a.M < kMmMinRows || a.ksplit != 1 || a.K % kMmBK) return false;
+  static const int min_rows = env_int("DFLASH_GEMM_MM_MIN", kMmMinRows);
+  if (dtype != 0 || a.M < min_rows || a.ksplit != 1 || a.K % kMmBK) return false;
   if (env_int("DFLASH_GEMM_MM", 1) == 0) return false;
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int tn = swiglu ? kMmBN / 2 : kMmBN;
@@ -693,9 +772,59 @@ bool gemm_mm_ok(const GemmArgs &a, int dtype) {
   return true;
 }
 
+bool gemm_mb_ok(const GemmArgs &a, int dtype) {
+  if (dtype != 0 || a.M < kMbMinRows || a.M > kMbMaxRows || a.ksplit != 1 || a.K % kMmBK) return false;
+  if (!a.mb_raw || env_int("DFLASH_GEMM_MB", 1) == 0) return false;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  if (a.N % (swiglu ? kMmBN / 2 : kMmBN)) return false;
+  if (!swiglu)
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].n % kMmBN) return false;
+  return a.row_off == 0;
+}
+
+// K ranges per decode-batch projection: enough work-groups for two per CU (the kernel's LDS allows
+// two), each range at least four K steps, and the raw output within the caller's scratch.
+// Returns the number of ranges; *steps = K steps per range (the last may be shorter, none is empty).
+static int mb_splits(const GemmArgs &a, int tiles, int *steps) {
+  const int env = env_int("DFLASH_GEMM_MB_SPLIT", 0);
+  const int nk = a.K / kMmBK;
+  int ks = env > 0 ? env : (512 + tiles - 1) / tiles;
+  ks = std::max(1, std::min({ks, nk / 4, kMbMaxSplit}));
+  const size_t per = (size_t)a.M * (a.epi == EPI_SWIGLU ? 2 * a.N : a.N);
+  while (ks > 1 && (size_t)ks * per > (size_t)a.mb_raw_cap) --ks;
+  *steps = (nk + ks - 1) / ks;
+  return (nk + *steps - 1) / *steps;
+}
+
+hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  const int tn = swiglu ? kMmBN / 2 : kMmBN;
+  const int BM = a.M <= 64 ? 64 : 128;
+  const int tiles = (a.N / tn) * ((a.M + BM - 1) / BM);
+  int steps = 0;
+  const int ks = mb_splits(a, tiles, &steps);
+  const dim3 grid(a.N / tn, (a.M + BM - 1) / BM, ks), block(256);
+  float *raw = ks > 1 ? a.mb_raw : nullptr;
+  hipEvent_t end = ks > 1 ? nullptr : e1;
+  if (BM == 64) hipExtLaunchKernelGGL(gemm_mm_kernel<64>, grid, block, 0, s, e0, end, 0, a, raw, steps);
+  else hipExtLaunchKernelGGL(gemm_mm_kernel<128>, grid, block, 0, s, e0, end, 0, a, raw, steps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  hipExtLaunchKernelGGL(gemm_mb_reduce_kernel, dim3(swiglu ? a.N / 16 : a.N / 32), block, 0, s, nullptr, e1, 0, a,
+                        (const float *)raw, ks);
+  return hipGetLastError();
+}
+
 template <typename T, int MT, int CT, int NW, int XR>
 static void launch_xr(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   // hipExtLaunchKernelGGL carries the optional timing events in the dispatch itself
+  if constexpr (MT == 4) {
+    if (pd >= 2) {
+      hipExtLaunchKernelGGL((gemm_kernel<T, MT, CT, NW, 2, XR>), grid, dim3(NW * 64), 0, s, e0, e1, 0, a);
+      return;
+    }
+  }
   if constexpr (MT == 1) {
     if (pd == 3) {
       hipExtLaunchKernelGGL((gemm_kernel<T, MT, CT, NW, 3, XR>), grid, dim3(NW * 64), 0, s, e0, e1, 0, a);
@@ -829,7 +958,7 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
   if (gemm_mm_ok(a, dtype)) {
     const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
     const dim3 grid(a.N / tn, (a.M + kMmBM - 1) / kMmBM), block(256);
-    hipExtLaunchKernelGGL(gemm_mm_kernel, grid, block, 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(gemm_mm_kernel<kMmBM>, grid, block, 0, s, e0, e1, 0, a, (float *)nullptr, a.K / kMmBK);
     return hipGetLastError();
   }
   int n_wg = 0;

@@ -58,13 +58,23 @@ struct GemmArgs {
   float *sk_part;
   int32_t *sk_cnt;
   int32_t sk_max_wg, sk_max_tiles;
+  // Optional scratch of the decode-batch path (gemm_mb_ok): raw fp32 sums of up to mb_raw_cap
+  // elements ([K range][M][N]).
+  float *mb_raw;
+  int64_t mb_raw_cap;
 };
+// Decode batches of kMbMinRows .. kMbMaxRows rows run all rows in one tiled launch (K split over at
+// most kMbMaxSplit ranges, reduced by a second launch) instead of row chunks.
+constexpr int kMbMinRows = 32, kMbMaxRows = 256, kMbMaxSplit = 8;
 constexpr int kSkTileElems = 16 * 32;  // entries of one partial tile (16 rows x 32 columns)
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // Whether launch_gemm runs `a` (all of its M rows at once) on the tiled large-M kernel.
 bool gemm_mm_ok(const GemmArgs &a, int dtype);
+// Whether `a` (a decode batch, all M rows at once) runs on launch_gemm_mb.
+bool gemm_mb_ok(const GemmArgs &a, int dtype);
+hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // K ranges for an EPI_PARTIAL projection of M rows: enough work-groups to cover the CUs several times
 // over, each range a whole number of 256-byte super-steps, and split * M * N <= cap_elems.
 int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);

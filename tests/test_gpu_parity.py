@@ -49,10 +49,12 @@ CASES = {
     "tiny_bf16": lambda: _variant(synth.TINY, dtype="bf16"),
     "small_fp32": lambda: _variant(small_short(32), dtype="fp32"),
     "small_p300": lambda: small_short(300),
+    # more than 256 pages of keys: the prefill attention reads its block-table entries chunk by chunk
+    "tiny_bf16_p4200": lambda: _variant(synth.TINY, dtype="bf16", prompt_len=4200),
 }
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "tiny_bf16", "small_fp32", "small_p300"])
+@pytest.mark.parametrize("name", ["tiny", "small", "tiny_bf16", "small_fp32", "small_p300", "tiny_bf16_p4200"])
 def test_prefill_logits_and_features(name):
     cfg = CASES[name]()
     log(f"[prefill] {name}")
@@ -483,11 +485,18 @@ def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
     return reps
 
 
-@pytest.mark.parametrize("name,lens,mode", [("tiny", (32, 9, 21, 32), "sampled"), ("small", (128, 37, 90, 61), "greedy"),
-                                            ("small", (53, 128, 7, 100, 64, 31, 128, 80), "sampled")])
-def test_e2e_batched_ragged(name, lens, mode):
-    """Batched steps over requests at different lengths (rows M = batch x block: 16, 32 and 64, the
-    row-tile variants of the projections) match each request's oracle like the batch-1 runs."""
+@pytest.mark.parametrize("name,lens,mode,rows_path", [
+    ("tiny", (32, 9, 21, 32), "sampled", "default"),
+    ("small", (128, 37, 90, 61), "greedy", "default"),
+    ("small", (53, 128, 7, 100, 64, 31, 128, 80), "sampled", "default"),
+    ("small", (53, 128, 7, 100, 64, 31, 128, 80), "sampled", "row_chunks"),
+    ("small", (40, 17, 96, 33, 64, 9, 120, 75, 50, 28, 101, 66, 12, 88, 45, 70), "greedy", "default")])
+def test_e2e_batched_ragged(name, lens, mode, rows_path, monkeypatch):
+    """Batched steps over requests at different lengths match each request's oracle like the batch-1
+    runs.  Rows M = batch x block: 16 (tiny, fp32: row-chunk kernels), 32, 64 and 128 (bf16: all rows in
+    one tiled launch with 64- or 128-row tiles, K split over work-groups and the ranges reduced in
+    order by the epilogue kernel), and 64 again on the row-chunk kernels (DFLASH_GEMM_MB=0)."""
+    monkeypatch.setenv("DFLASH_GEMM_MB", "0" if rows_path == "row_chunks" else "1")
     cfg = CASES[name]()
     log(f"[e2e batched] {name} {mode} prompts {lens}")
     W = sw.model_weights(cfg, gain_std=0.1)
