@@ -38,6 +38,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 
 constexpr int kAttnSplitMax = 64;
+constexpr int kAttnWgTarget = 512;  // work-groups a batched decode attention call aims at
 constexpr int kMaxKSplit = 8;
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
 constexpr int kSkMaxWg = 1024;  // stream-K projection work-groups (one per CU)
@@ -370,8 +371,15 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   const int pages = (key_span + pt - 1) / pt;
   // Decode-sized calls split the keys into ranges of about nine pages (the fastest on MI355X at 1-2K
   // keys with one query tile per work-group; merged by attn_merge_kernel); larger calls keep one range.
+  // Batched calls already have (sequences x KV heads x query tiles) work-groups: they split the keys
+  // only as far as about kAttnWgTarget work-groups in all (more splits add merge work and rounds of
+  // work-groups, not parallelism).
   int splits = 1;
-  if ((size_t)n_seq * q_len <= c->L.att_rows) splits = std::min(kAttnSplitMax, std::max(1, (pages + 8) / 9));
+  if ((size_t)n_seq * q_len <= c->L.att_rows) {
+    const int wg_target = getenv("DFLASH_ATTN_WG") ? std::max(1, atoi(getenv("DFLASH_ATTN_WG"))) : kAttnWgTarget;
+    const int gx = n_seq * m.kv_heads * ntile;
+    splits = std::min({kAttnSplitMax, std::max(1, (pages + 8) / 9), std::max(1, (wg_target + gx - 1) / gx)});
+  }
   int pps = (pages + splits - 1) / splits;
   const int env_pps = getenv("DFLASH_ATTN_PPS") ? atoi(getenv("DFLASH_ATTN_PPS")) : 0;
   if (env_pps > 0 && (pages + env_pps - 1) / env_pps <= kAttnSplitMax && (size_t)n_seq * q_len <= c->L.att_rows)

@@ -727,26 +727,41 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
 }
 
 // Sum of the K ranges of gemm_mm_kernel's raw output, in range order, then the projection's epilogue,
-// for one 32-column tile (SWIGLU: 16 output columns, their gate and up sums) over all M <= 256 rows.
-__global__ __launch_bounds__(256) void gemm_mb_reduce_kernel(GemmArgs a, const float *raw, int ks) {
-  __shared__ float lds[kMbMaxRows * 32];
-  __shared__ float s_rstd[kMbMaxRows];
+// for one 32-column tile (SWIGLU: 16 output columns, their gate and up sums) of kMbRedRows rows:
+// thread t adds the ranges of 4 adjacent columns of row t / 8 (all ranges' loads issued at once).
+constexpr int kMbRedRows = 16;
+__global__ __launch_bounds__(128) void gemm_mb_reduce_kernel(GemmArgs a, const float *raw, int ks) {
+  __shared__ __attribute__((aligned(16))) float lds[kMbRedRows * 32];
+  __shared__ float s_rstd[kMbRedRows];
   const int c = blockIdx.x, tid = threadIdx.x;
+  const int r0 = blockIdx.y * kMbRedRows;
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int nraw = swiglu ? 2 * a.N : a.N;
   const size_t slice = (size_t)a.M * nraw;
-  for (int e = tid; e < a.M * 32; e += 256) {
-    const int m = e >> 5, j = e & 31;
+  GemmArgs b = a;  // the tile's rows as a projection of their own: row_off = r0
+  b.M = min(kMbRedRows, a.M - r0);
+  b.row_off = r0;
+  const int m = tid >> 3, j = (tid & 7) * 4;
+  if (m < b.M) {
     const int col = swiglu ? (j < 16 ? 16 * c + j : a.N + 16 * c + j - 16) : 32 * c + j;
-    const float *p = raw + (size_t)m * nraw + col;
-    float v = p[0];
-    for (int z = 1; z < ks; ++z) v += p[z * slice];
-    lds[e] = v;
+    const float4 *p = reinterpret_cast<const float4 *>(raw + (size_t)(r0 + m) * nraw + col);
+    float4 v[kMbMaxSplit];
+#pragma unroll
+    for (int z = 0; z < kMbMaxSplit; ++z) v[z] = p[(z < ks ? z : 0) * (slice / 4)];
+    float4 t = v[0];
+#pragma unroll
+    for (int z = 1; z < kMbMaxSplit; ++z)
+      if (z < ks) {
+        t.x += v[z].x;
+        t.y += v[z].y;
+        t.z += v[z].z;
+        t.w += v[z].w;
+      }
+    *reinterpret_cast<float4 *>(&lds[m * 32 + j]) = t;
   }
-  if (a.ss_in)
-    for (int m = tid; m < a.M; m += 256) s_rstd[m] = gemm_rstd(a, m, false, nullptr);
+  if (a.ss_in && tid < b.M) s_rstd[tid] = gemm_rstd(b, tid, false, nullptr);
   __syncthreads();
-  gemm_epilogue<bf16, 32, 256>(a, c, 0, lds, s_rstd);
+  gemm_epilogue<bf16, 32, 128>(b, c, 0, lds, s_rstd);
 }
 
 namespace {
@@ -811,8 +826,8 @@ hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEv
   else hipExtLaunchKernelGGL(gemm_mm_kernel<128>, grid, block, 0, s, e0, end, 0, a, raw, steps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
-  hipExtLaunchKernelGGL(gemm_mb_reduce_kernel, dim3(swiglu ? a.N / 16 : a.N / 32), block, 0, s, nullptr, e1, 0, a,
-                        (const float *)raw, ks);
+  const dim3 rgrid(swiglu ? a.N / 16 : a.N / 32, (a.M + kMbRedRows - 1) / kMbRedRows);
+  hipExtLaunchKernelGGL(gemm_mb_reduce_kernel, rgrid, dim3(128), 0, s, nullptr, e1, 0, a, (const float *)raw, ks);
   return hipGetLastError();
 }
 
