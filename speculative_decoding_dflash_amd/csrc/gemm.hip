@@ -529,6 +529,8 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
 // CUs.  Each K range then writes its raw fp32 sums (`raw`, [range][M][N], SWIGLU: gate columns then
 // up columns) and gemm_mb_reduce_kernel adds the ranges in order and runs the epilogue.
 constexpr int kMmBM = 128, kMmBN = 128, kMmBK = 64;
+constexpr int kMbWgTarget = 384;   // work-groups a split decode-batch projection aims at
+constexpr int kMbFullTiles = 256;  // output tiles from which a decode-batch projection is not split
 template <int BM>
 __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw, int steps) {
   using F = Frag<bf16>;
@@ -798,13 +800,16 @@ bool gemm_mb_ok(const GemmArgs &a, int dtype) {
   return a.row_off == 0;
 }
 
-// K ranges per decode-batch projection: enough work-groups for two per CU (the kernel's LDS allows
-// two), each range at least four K steps, and the raw output within the caller's scratch.
+// K ranges per decode-batch projection: about kMbWgTarget work-groups in all, each range at least four
+// K steps, and the raw output within the caller's scratch.
 // Returns the number of ranges; *steps = K steps per range (the last may be shorter, none is empty).
 static int mb_splits(const GemmArgs &a, int tiles, int *steps) {
   const int env = env_int("DFLASH_GEMM_MB_SPLIT", 0);
+  const int wg = std::max(1, env_int("DFLASH_GEMM_MB_WG", kMbWgTarget));
   const int nk = a.K / kMmBK;
-  int ks = env > 0 ? env : (512 + tiles - 1) / tiles;
+  // a projection with a tile for every CU streams without a split (and without the reduce launch)
+  const int full = env_int("DFLASH_GEMM_MB_FULL", kMbFullTiles);
+  int ks = env > 0 ? env : (full > 0 && tiles >= full ? 1 : (wg + tiles - 1) / tiles);
   ks = std::max(1, std::min({ks, nk / 4, kMbMaxSplit}));
   const size_t per = (size_t)a.M * (a.epi == EPI_SWIGLU ? 2 * a.N : a.N);
   while (ks > 1 && (size_t)ks * per > (size_t)a.mb_raw_cap) --ks;
