@@ -495,17 +495,22 @@ def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
     return reps
 
 
+_LENS24 = (40, 17, 96, 33, 64, 9, 120, 75, 50, 28, 101, 66, 12, 88, 45, 70, 31, 58, 110, 23, 77, 6, 92, 49)
+
+
 @pytest.mark.parametrize("name,lens,mode,rows_path", [
     ("tiny", (32, 9, 21, 32), "sampled", "default"),
     ("small", (128, 37, 90, 61), "greedy", "default"),
     ("small", (53, 128, 7, 100, 64, 31, 128, 80), "sampled", "default"),
     ("small", (53, 128, 7, 100, 64, 31, 128, 80), "sampled", "row_chunks"),
-    ("small", (40, 17, 96, 33, 64, 9, 120, 75, 50, 28, 101, 66, 12, 88, 45, 70), "greedy", "default")])
+    ("small", (40, 17, 96, 33, 64, 9, 120, 75, 50, 28, 101, 66, 12, 88, 45, 70), "greedy", "default"),
+    ("small", _LENS24, "sampled", "default")])
 def test_e2e_batched_ragged(name, lens, mode, rows_path, monkeypatch):
     """Batched steps over requests at different lengths match each request's oracle like the batch-1
     runs.  Rows M = batch x block: 16 (tiny, fp32: row-chunk kernels), 32, 64 and 128 (bf16: all rows in
     one tiled launch with 64- or 128-row tiles, K split over work-groups and the ranges reduced in
-    order by the epilogue kernel), and 64 again on the row-chunk kernels (DFLASH_GEMM_MB=0)."""
+    order by the epilogue kernel), 64 again on the row-chunk kernels (DFLASH_GEMM_MB=0), and 192 rows
+    (two 128-row tiles, the second partial)."""
     monkeypatch.setenv("DFLASH_GEMM_MB", "0" if rows_path == "row_chunks" else "1")
     cfg = CASES[name]()
     log(f"[e2e batched] {name} {mode} prompts {lens}")
