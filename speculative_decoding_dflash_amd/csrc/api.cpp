@@ -39,6 +39,7 @@ int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 
 constexpr int kAttnSplitMax = 64;
 constexpr int kAttnWgTarget = 512;  // work-groups a batched decode attention call aims at
+constexpr int kAttnFusedMaxSeqs = 4;  // decode calls of more sequences post-process q / k / v separately
 constexpr int kMaxKSplit = 8;
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
 constexpr int kSkMaxWg = 1024;  // stream-K projection work-groups (one per CU)
@@ -434,14 +435,17 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     with_norm(c, a, *ss_n);
     int np = 1;
     if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
-    // Decode-sized calls: the attention kernel post-processes q / k / v itself (one query tile per
-    // work-group keeps that prologue short; 0.2 ms per 27B step faster on MI355X than a separate
-    // post-processing launch).  DFLASH_ATTN_FUSED=0 selects the separate kernel.
+    // Decode-sized calls of up to kAttnFusedMaxSeqs sequences: the attention kernel post-processes
+    // q / k / v itself (one query tile per work-group keeps that prologue short; 0.2 ms per 27B step
+    // faster on MI355X than a separate post-processing launch at concurrency 1).  Larger batches take
+    // the separate kernel: the plain attention kernel holds fewer registers (two work-groups per CU
+    // instead of one), which measured 2-3% faster per step at concurrency 8 and 32.
+    // DFLASH_ATTN_FUSED=0 / =1 selects the separate / fused kernel for every decode-sized call.
     // The fused kernel needs q_len <= 16 (the block's keys form one LDS page) and a 16-byte aligned
     // q gain.
     const char *fz = getenv("DFLASH_ATTN_FUSED");
-    fused = !(fz && atoi(fz) == 0) && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 16 &&
-            ((uintptr_t)w.q_norm & 15) == 0;
+    const bool want = fz ? atoi(fz) != 0 : n_seq <= kAttnFusedMaxSeqs;
+    fused = want && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 16 && ((uintptr_t)w.q_norm & 15) == 0;
     if (!fused) {
       QkvPostArgs p = post_base(c, rows, R);
       p.ld_src = QD + 2 * KD;
