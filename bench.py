@@ -16,7 +16,11 @@ drafts (drawn from the drafter's own distribution, accepted with min(1, p/q)).  
 the projection kernel (the dominant one: ~99% of the step's bytes): the projection launches of one
 step are recorded by the library and replayed back to back between two HIP events on the step's
 stream; `traffic` is the HBM bytes per launch measured with rocprofv3 counters.  `cpu_baseline` times
-the CPU oracle on a bounded sample.
+the CPU oracle on a bounded sample.  `batched_configured_runs` adds short configured runs of the same
+step over 8 and 32 requests (prompts of 1024 tokens) on the same weights.
+
+--concurrency C and --config 27b-long run the batched measurement alone (with its planted sweep and the
+projection replay), printing their own JSON line.
 """
 from __future__ import annotations
 
@@ -204,14 +208,15 @@ def cpu_baseline(cfg, tau: float):
 MFMA_PEAK_TFS = 2500.0  # dense bf16 MFMA, MI355X published
 
 
-def batch_main(args, cfg, conc: int):
+def batch_main(args, cfg, conc: int, weights=None, quick: bool = False):
     """Batched steps: `conc` requests decoded together (each step verifies conc x B rows and drafts
     conc blocks).  Requests are prefilled one by one (prompt lengths from the workload: fixed, or
     uniform over the long-context range), their prompts injected into the drafter, then every timed
     step is one captured HIP graph of verify -> accept -> draft over all requests.  Printed: one JSON
     line with accepted tokens/s of the configured run (T=1 / top-k / top-p, real drafter) and a
     planted sweep under greedy verification (every request forced to acceptance length tau*), each
-    with the step's algorithmic HBM and MFMA fractions."""
+    with the step's algorithmic HBM and MFMA fractions.  quick: the configured run only, on the
+    given weights, returned as a dict instead of printed."""
     import numpy as np
     import torch
 
@@ -229,9 +234,11 @@ def batch_main(args, cfg, conc: int):
         lens = [cfg.prompt_len] * conc
     taus_sweep = [int(x) for x in args.tau_sweep.split(",")] if args.tau_sweep else list(range(1, B + 1))
     log(f"[bench] {cfg.name}, concurrency {conc}, prompt lengths {min(lens)}..{max(lens)} "
-        f"(mean {sum(lens) / conc:.0f}): generating weights on the GPU")
-    weights = sgpu.model_weights(cfg)
-    torch.cuda.synchronize()
+        f"(mean {sum(lens) / conc:.0f})")
+    if weights is None:
+        log("[bench] generating weights on the GPU")
+        weights = sgpu.model_weights(cfg)
+        torch.cuda.synchronize()
     n_ar = (Wm + K + 1) * B + 2 * B  # greedy tokens needed per request by the planted sweep
     max_tokens = max(lens) + max(n_ar, (Wm + K + 2) * B) + 2 * B
     eng = Engine(cfg, weights, max_slots=conc, max_rows=max(max(lens), conc * B),
@@ -309,6 +316,11 @@ def batch_main(args, cfg, conc: int):
     ms, tl, ns, pre_s = run(s_conf)
     conf = summary(ms, tl, ns)
     log(f"[bench]   {conf} (prefill of all requests {pre_s:.1f} s)")
+    if quick:
+        eng.close()
+        return {k: v for k, v in conf.items() if k not in ("step_bytes", "step_flops")} | {
+            "step_gbytes": round(conf["step_bytes"] / 1e9, 2), "step_tflop": round(conf["step_flops"] / 1e12, 3),
+            "prompt_len": lens[0], "steps": K, "warmup": Wm}
 
     # projection roofline at this batch: the projection launches of one eager step, replayed
     prefill_all(s_conf)
@@ -403,6 +415,8 @@ def main():
                     help="requests decoded together (default: the workload's own, 1 for 27b); above 1 the "
                          "batched measurement runs instead of the concurrency-1 line")
     ap.add_argument("--tau-sweep", default="", help="planted acceptance lengths of the batched sweep, e.g. 1,3,5,7")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the short configured runs at concurrency 8 and 32 appended to the default line")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first copy 1 GiB device to device (a plain copy of known size, the reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -525,6 +539,14 @@ def main():
                                   "step_hbm_gbs": round(gbs, 1)}
                 log(f"[bench]   planted tau*={ts}: {sweep[str(ts)]}")
 
+    # short configured runs of the same step over batches of requests (the batched path's kernels:
+    # all rows of a projection in one tiled launch, batch-aware attention splits), on the same weights
+    batched = None
+    if not args.no_batched and args.config == "27b":
+        eng.close()
+        qa = argparse.Namespace(**{**vars(args), "steps": min(K, 8), "warmup": min(Wm, 2)})
+        batched = {str(c): batch_main(qa, cfg, c, weights=weights, quick=True) for c in (8, 32)}
+
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -576,6 +598,7 @@ def main():
                      "method": "the projection launches of one decode step recorded by the library and replayed "
                                f"{reps} times back to back between two HIP events on the step's stream"},
         "cpu_baseline": cpu,
+        "batched_configured_runs": batched,
     }
     print(json.dumps(out), flush=True)
     eng.close()
