@@ -250,13 +250,35 @@ dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
 
 // A projection whose K ranges write fp32 partial slices [range][R][N] into the partial buffer; the
 // consumer (norm_kernel, qkv_post_kernel) adds the *n_part slices in order.
-dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *n_part) {
+// A projection whose K ranges leave fp32 partial slices [range][R][N] for the consumer (qkv_post_kernel,
+// norm_kernel) to add in order: *src, *stride and *n_part describe them.  Row chunks (R <= 16) use the
+// workspace's partial buffer; a decode batch that the tiled kernel splits over K hands its ranges over
+// as they are (each already scaled by the deferred norm's 1/rms), which saves a reduce launch.
+dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *n_part, const float **src,
+                          int64_t *stride) {
   a.epi = EPI_PARTIAL;
   a.out_f32 = c->wsp<float>(c->L.part);
   a.ld_out = a.N;
   a.ksplit = R <= kGemmMaxRows ? std::min(kMaxKSplit, gemm_ksplit(R, a.N, a.K, c->dt(), c->L.part_elems)) : 1;
   a.part_stride = (int64_t)R * a.N;
   *n_part = a.ksplit;
+  *src = a.out_f32;
+  *stride = a.part_stride;
+  if (!c->tiled && c->L.mbr_elems) {
+    GemmArgs b = a;
+    b.M = R;
+    b.row_off = 0;
+    b.mb_raw = c->wsp<float>(c->L.mbr);
+    b.mb_raw_cap = (int64_t)c->L.mbr_elems;
+    if (gemm_mb_ok(b, c->dt())) {
+      const int ks = gemm_mb_slices(b);
+      if (ks > 1) {
+        a.mb_direct = 1;
+        *n_part = ks;
+        *src = b.mb_raw;
+      }
+    }
+  }
   return run_gemm(c, a, R, s);
 }
 
@@ -434,7 +456,9 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     a.seg[2] = GemmSeg{w.wv, KD};
     with_norm(c, a, *ss_n);
     int np = 1;
-    if ((st = run_partial(c, a, R, s, &np)) != DFLASH_OK) return st;
+    const float *part = nullptr;
+    int64_t part_stride = 0;
+    if ((st = run_partial(c, a, R, s, &np, &part, &part_stride)) != DFLASH_OK) return st;
     // Decode-sized calls of up to kAttnFusedMaxSeqs sequences: the attention kernel post-processes
     // q / k / v itself (one query tile per work-group keeps that prologue short; 0.2 ms per 27B step
     // faster on MI355X than a separate post-processing launch at concurrency 1).  Larger batches take
@@ -448,9 +472,10 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     fused = want && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 16 && ((uintptr_t)w.q_norm & 15) == 0;
     if (!fused) {
       QkvPostArgs p = post_base(c, rows, R);
+      p.src = part;
       p.ld_src = QD + 2 * KD;
       p.n_part = np;
-      p.part_stride = (int64_t)R * (QD + 2 * KD);
+      p.part_stride = part_stride;
       p.nseg = 3;
       p.seg[0] = PostSeg{m.q_heads, ROLE_Q, (const float *)w.q_norm, c->wsp<void>(c->L.qbuf), QD};
       p.seg[1] = PostSeg{m.kv_heads, ROLE_K, (const float *)w.k_norm, kv_layer, 0};
@@ -867,9 +892,12 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
     p.total_heads = dc.layers * 2 * m.kv_heads;
     with_norm(c, a, ss_n);
     int np = 1;
-    if ((st = run_partial(c, a, Ri, s, &np)) != DFLASH_OK) return st;
+    const float *part = nullptr;
+    int64_t part_stride = 0;
+    if ((st = run_partial(c, a, Ri, s, &np, &part, &part_stride)) != DFLASH_OK) return st;
+    p.src = part;
     p.n_part = np;
-    p.part_stride = (int64_t)Ri * (dc.layers * 2 * KD);
+    p.part_stride = part_stride;
     HIP_OK(launch_qkv_post(p, c->dt(), s));
   }
   // 2. The block [anchor, MASK x (B-1)].

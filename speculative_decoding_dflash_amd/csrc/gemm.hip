@@ -573,7 +573,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
     }
     pb[i] = w + kc;
   }
-  if (!raw && tid < BM) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
+  const bool scaled = !raw || a.mb_direct;  // raw sums of a direct partial output carry the 1/rms
+  if (scaled && tid < BM) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
 
   f32x4 acc[MI][4];
 #pragma unroll
@@ -647,14 +648,15 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
+        const int ml = wm * (BM / 2) + 16 * i + 4 * g + r, m = m0 + ml;
         if (m >= a.M) continue;
+        const float sc = scaled ? s_rstd[ml] : 1.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // SWIGLU: fragment j holds gate (j even) or up (j odd) sums of output column
           // n0 + 16 (2 wn + j / 2) + r16
           const int col = swiglu ? (j & 1) * a.N + n0 + 16 * (2 * wn + j / 2) + r16 : n0 + wn * 64 + 16 * j + r16;
-          dst[(size_t)m * nraw + col] = acc[i][j][r];
+          dst[(size_t)m * nraw + col] = scaled ? acc[i][j][r] * sc : acc[i][j][r];
         }
       }
     return;
@@ -817,6 +819,13 @@ static int mb_splits(const GemmArgs &a, int tiles, int *steps) {
   return (nk + *steps - 1) / *steps;
 }
 
+int gemm_mb_slices(const GemmArgs &a) {
+  const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
+  const int BM = a.M <= 64 ? 64 : 128;
+  int steps = 0;
+  return mb_splits(a, (a.N / tn) * ((a.M + BM - 1) / BM), &steps);
+}
+
 hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int tn = swiglu ? kMmBN / 2 : kMmBN;
@@ -826,11 +835,12 @@ hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEv
   const int ks = mb_splits(a, tiles, &steps);
   const dim3 grid(a.N / tn, (a.M + BM - 1) / BM, ks), block(256);
   float *raw = ks > 1 ? a.mb_raw : nullptr;
-  hipEvent_t end = ks > 1 ? nullptr : e1;
+  const bool direct = a.mb_direct && a.epi == EPI_PARTIAL;  // the ranges are the output: no reduce
+  hipEvent_t end = ks > 1 && !direct ? nullptr : e1;
   if (BM == 64) hipExtLaunchKernelGGL(gemm_mm_kernel<64>, grid, block, 0, s, e0, end, 0, a, raw, steps);
   else hipExtLaunchKernelGGL(gemm_mm_kernel<128>, grid, block, 0, s, e0, end, 0, a, raw, steps);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ks == 1) return e;
+  if (e != hipSuccess || ks == 1 || direct) return e;
   const dim3 rgrid(swiglu ? a.N / 16 : a.N / 32, (a.M + kMbRedRows - 1) / kMbRedRows);
   hipExtLaunchKernelGGL(gemm_mb_reduce_kernel, rgrid, dim3(128), 0, s, nullptr, e1, 0, a, (const float *)raw, ks);
   return hipGetLastError();

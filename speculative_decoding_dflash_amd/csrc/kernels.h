@@ -62,6 +62,10 @@ struct GemmArgs {
   // elements ([K range][M][N]).
   float *mb_raw;
   int64_t mb_raw_cap;
+  // EPI_PARTIAL on that path with more than one K range: the ranges' sums, scaled by the deferred
+  // norm's 1/rms, are the output themselves ([range][M][N] in mb_raw, no reduce launch); the consumer
+  // adds gemm_mb_slices() slices in order.
+  int32_t mb_direct;
 };
 // Decode batches of kMbMinRows .. kMbMaxRows rows run all rows in one tiled launch (K split over at
 // most kMbMaxSplit ranges, reduced by a second launch) instead of row chunks.
@@ -75,6 +79,8 @@ bool gemm_mm_ok(const GemmArgs &a, int dtype);
 // Whether `a` (a decode batch, all M rows at once) runs on launch_gemm_mb.
 bool gemm_mb_ok(const GemmArgs &a, int dtype);
 hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// The number of K ranges launch_gemm_mb splits `a` into (call only where gemm_mb_ok holds).
+int gemm_mb_slices(const GemmArgs &a);
 // K ranges for an EPI_PARTIAL projection of M rows: enough work-groups to cover the CUs several times
 // over, each range a whole number of 256-byte super-steps, and split * M * N <= cap_elems.
 int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);
