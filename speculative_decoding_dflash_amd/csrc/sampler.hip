@@ -87,7 +87,22 @@ __global__ __launch_bounds__(kT1) void topk_stage1(FilterArgs a) {
   const int c0 = chunk * a.chunk, c1 = min(a.vocab, c0 + a.chunk);
   const int n = c1 - c0;
   const float *z = a.logits + (size_t)row * a.vocab + c0;
-  for (int j = tid; j < n; j += kT1) skey[j] = order_key(T > 0.0f ? __fdiv_rn(z[j], T) : z[j]);
+  {
+    // every load of the thread first (a loop of load -> convert -> LDS store waits for each load in
+    // turn), then the keys
+    constexpr int kPer = kChunkMax / kT1;
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = tid + i * kT1;
+      v[i] = z[j < n ? j : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = tid + i * kT1;
+      if (j < n) skey[j] = order_key(T > 0.0f ? __fdiv_rn(v[i], T) : v[i]);
+    }
+  }
   __syncthreads();
   const int Kc = min(K, n);
   uint32_t *okey = a.stage_key + ((size_t)row * a.n_chunks + chunk) * a.kmax;
