@@ -40,6 +40,7 @@ int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 constexpr int kAttnSplitMax = 64;
 constexpr int kAttnWgTarget = 512;  // work-groups a batched decode attention call aims at
 constexpr int kAttnFusedMaxSeqs = 4;  // decode calls of more sequences post-process q / k / v separately
+constexpr int kAttnWholeBlockPages = 256;  // key pages from which a batched call's work-groups hold whole blocks
 constexpr int kMaxKSplit = 8;
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
 constexpr int kSkMaxWg = 1024;  // stream-K projection work-groups (one per CU)
@@ -386,12 +387,18 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   const char *qz = getenv("DFLASH_ATTN_QTILE");
   const int qt_env = qz ? atoi(qz) : 0;
   const bool decode = (size_t)n_seq * q_len <= c->L.att_rows;
-  a.q_tile = std::max(1, std::min(q_len, !decode ? 64 / G : (qt_env > 0 ? qt_env : 16 / G)));
-  const int ntile = (q_len + a.q_tile - 1) / a.q_tile;
   const int pt = c->cap.page_tokens;
   int key_span = ctx_bound + pt;  // keys of the widest work-group, rounded out to pages
   if (mode == 1 && c->dcfg.window > 0) key_span = std::min(key_span, c->dcfg.window + q_len + 2 * pt);
   const int pages = (key_span + pt - 1) / pt;
+  // Batched calls (q/k/v post-processed separately) over long key ranges: one work-group per
+  // (sequence, KV head) holds the whole block, so each K/V page is read once instead of once per
+  // 16-wide query tile (at 6K keys and 32 sequences those re-reads bound the kernel: 47.0 -> 44.0 ms per
+  // 27B step); at 1K keys the lighter one-tile work-groups stay faster.
+  int qt = qt_env > 0 ? qt_env : 16 / G;
+  if (decode && qt_env <= 0 && !raw_w && pages >= kAttnWholeBlockPages) qt = q_len;
+  a.q_tile = std::max(1, std::min(q_len, !decode ? 64 / G : qt));
+  const int ntile = (q_len + a.q_tile - 1) / a.q_tile;
   // Decode-sized calls split the keys into ranges of about nine pages (the fastest on MI355X at 1-2K
   // keys with one query tile per work-group; merged by attn_merge_kernel); larger calls keep one range.
   // Batched calls already have (sequences x KV heads x query tiles) work-groups: they split the keys

@@ -641,15 +641,19 @@ def test_27b_width_vs_fp32_forward(layers):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("conc", [1, 8, 32])
-def test_27b_greedy_spec_equals_greedy_ar(conc):
+@pytest.mark.parametrize("conc,whole_block", [(1, False), (8, False), (32, False), (8, True)])
+def test_27b_greedy_spec_equals_greedy_ar(conc, whole_block, monkeypatch):
     """At the 27B shape with a 1024-token prompt (the measured configuration at concurrency 1, and the
     batched verify / draft at concurrency 8 and 32): greedy speculative decoding emits the device's own
-    greedy plain-decoding stream for every request, and every verify logit row at a position both runs
-    reach with the same prefix agrees with the plain-decoding row within twice the bf16 tolerance (each
-    device path is held to the tolerance against the exact forward; the batched rows use other row
-    tiles, so their fp32 sums, and the bf16 roundings that follow, differ along 64 layers).  A stream
-    may diverge only at a near tie of the plain-decoding logits."""
+    greedy plain-decoding stream for every request; a stream may diverge only at a near tie of the
+    plain-decoding logits; for the first 8 requests both paths' logit rows are held against an fp32
+    forward of the same tokens, and the verify rows against the plain-decoding rows, within 3x the bf16
+    tolerance (the bf16 roundings of 64 layers compound, see test_27b_width_vs_fp32_forward; the
+    batched rows use other row tiles and key splits, so their roundings differ).  whole_block: the batched attention
+    work-groups hold the whole block (three 16-wide query tiles at the 27B head ratio), as batched calls
+    over long key ranges do."""
+    if whole_block:
+        monkeypatch.setenv("DFLASH_ATTN_QTILE", "8")
     from speculative_decoding_dflash_amd import binding as Bd
     from synth import gpu as sg
     cfg = synth.CONFIGS["27b"]
