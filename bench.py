@@ -539,6 +539,22 @@ def main():
                                   "step_hbm_gbs": round(gbs, 1)}
                 log(f"[bench]   planted tau*={ts}: {sweep[str(ts)]}")
 
+    # streaming probe on the same box: a 1 GiB device-to-device copy (torch's copy kernel; 1 GiB read
+    # and 1 GiB written), best of 5, for context next to the 8 TB/s published peak
+    src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(5):
+        pt = Timer(torch)
+        pt.start()
+        dst.copy_(src)
+        t_ms = pt.stop()
+        best = t_ms if best is None else min(best, t_ms)
+    probe = {"kind": "device-to-device copy, 1 GiB read + 1 GiB written, best of 5",
+             "gbs": round(2 * (1 << 30) / (best / 1e3) / 1e9, 1)}
+    log(f"[bench] copy probe: {probe['gbs']} GB/s (read + write)")
+    del src, dst
+
     # short configured runs of the same step over batches of requests (the batched path's kernels:
     # all rows of a projection in one tiled launch, batch-aware attention splits), on the same weights
     batched = None
@@ -599,6 +615,7 @@ def main():
                                f"{reps} times back to back between two HIP events on the step's stream"},
         "cpu_baseline": cpu,
         "batched_configured_runs": batched,
+        "hbm_copy_probe": probe,
     }
     print(json.dumps(out), flush=True)
     eng.close()
