@@ -12,6 +12,7 @@
 // Stage 2: one work-group per row sorts the union of its chunks' candidates by (key desc, id asc) --
 // the row's top k is the top k of that union -- and computes the distribution.
 #include <algorithm>
+#include <cstdlib>
 
 #include "kernels.h"
 
@@ -154,15 +155,35 @@ __global__ __launch_bounds__(kT1) void topk_stage1(FilterArgs a) {
       hist_add(hist, (int)((k >> shift) & 255), j < n && (lvl == 0 || (k >> (shift + 8)) == prefix));
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        if (cum + hist[bin] >= need) {
-          s_bin = bin;
-          s_above = cum;
-          break;
+    if (tid < 64) {
+      // the bin holding the need-th largest key, found by wave 0: lane l holds bins 255 - 4l - i
+      // (i = 0..3, descending), a prefix sum over the lanes gives the count of every higher bin, and
+      // the one lane whose range reaches `need` walks its four bins (a single thread walking all 256
+      // bins waited on each LDS read in turn)
+      int c[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hist[255 - 4 * tid - i];
+        sum += c[i];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (tid >= off) incl += y;
+      }
+      const int excl = incl - sum;
+      if (excl < need && need <= incl) {
+        int cum = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (cum + c[i] >= need) {
+            s_bin = 255 - 4 * tid - i;
+            s_above = cum;
+            break;
+          }
+          cum += c[i];
         }
-        cum += hist[bin];
       }
     }
     __syncthreads();
@@ -293,7 +314,9 @@ __global__ __launch_bounds__(kT2) void topk_stage2(FilterArgs a) {
 // union (chunks * kmax) fits in LDS.
 void filter_plan(FilterArgs &a, int kmax) {
   a.kmax = kmax;
-  int chunks = (a.vocab + 3999) / 4000;
+  static const int env_chunk = getenv("DFLASH_TOPK_CHUNK") ? atoi(getenv("DFLASH_TOPK_CHUNK")) : 0;
+  const int target = env_chunk >= 256 && env_chunk <= kChunkMax ? env_chunk : 4000;  // elements per chunk
+  int chunks = (a.vocab + target - 1) / target;
   chunks = std::max(1, std::min(chunks, kMergeMax / kmax));
   int chunk = (a.vocab + chunks - 1) / chunks;
   a.chunk = chunk;
