@@ -100,8 +100,10 @@ def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=Fals
     taus = torch.zeros(warmup + steps, dtype=torch.int32, device="cuda")
     eng.prefill([0], prompt.view(1, -1), [samp])
     use_graph = graph and not profile
-    # with a graph, its first launch is the last warmup step (a first launch can carry one-time costs)
-    n_eager = warmup - 1 if use_graph and warmup > 0 else warmup
+    # with a graph, its first launch is the last warmup step; it is captured after at least one eager step,
+    # so that its launches have the decode shapes (right after a prefill the drafter's injection covers
+    # every prompt row)
+    n_eager = warmup - 1 if use_graph and warmup > 1 else warmup
     for i in range(n_eager):
         eng.spec_step([0], [samp], planted=None if planted is None else planted[i], stochastic=stochastic)
         taus[i:i + 1].copy_(eng.n_out[:1])
@@ -287,8 +289,8 @@ def batch_main(args, cfg, conc: int, weights=None, quick: bool = False):
         if planted is not None:
             eng.block.view(-1, B)[:conc, 1:] = planted[0]
         taus = torch.zeros(Wm + K, conc, dtype=torch.int32, device="cuda")
-        # the graph's first launch is the last warmup step (a first launch can carry one-time costs)
-        n_eager = Wm - 1 if Wm > 0 else 0
+        # the graph's first launch is the last warmup step; captured after at least one eager step
+        n_eager = Wm - 1 if Wm > 1 else Wm
         for i in range(n_eager):
             step(samp, None if planted is None else planted[i + 1])
             taus[i].copy_(eng.n_out[:conc])

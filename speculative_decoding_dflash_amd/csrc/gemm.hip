@@ -972,7 +972,8 @@ static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   const long items = ntile * (a.K / sk);
-  const long wg = std::min<long>(cus[dev], a.sk_max_wg);
+  const int env_wg = env_int("DFLASH_GEMM_SK_WG", 0);  // work-groups of a stream-K launch, for tuning
+  const long wg = std::min<long>(env_wg > 0 ? env_wg : cus[dev], a.sk_max_wg);
   if (wg < 1) return 0;
   const long per = (items + wg - 1) / wg;
   *n_wg = (int)((items + per - 1) / per);
@@ -1051,7 +1052,8 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
     v2 = v2 * r * sg.gain[i + half];
     const int pos = a.rows.pos[row];
     const float2 cr = (pos >= 0 && pos < a.rope_rows) ? a.rope[(size_t)pos * half + i] : make_float2(1.f, 0.f);
-    if ((pos < 0 || pos >= a.rope_rows) && live && i == 0) raise_err(a.err, ERR_PAGE);
+    // padding rows (a launch covering more rows than the call commits) are neither written nor checked
+    if ((pos < 0 || pos >= a.rope_rows) && live && i == 0 && a.rows.valid[row]) raise_err(a.err, ERR_PAGE);
     const float cs = cr.x, sn = cr.y;
     const float o1 = v1 * cs - v2 * sn, o2 = v2 * cs + v1 * sn;
     v1 = o1;

@@ -443,6 +443,38 @@ def test_graph_replay_equals_eager_steps(name, stochastic):
         assert torch.equal(a[3], b[3]), f"step {i}: logits differ"
 
 
+def test_graph_captured_after_prefill_tight_pages():
+    """A step captured right after a prefill launches the drafter's injection over every prompt row at
+    each replay (rows past the committed ones are padding).  With a page budget that just fits the run,
+    those padding rows' positions lie beyond the rotary table; they are neither written nor checked, so
+    the replays raise no device error, and they equal the eager steps."""
+    cfg = _variant(synth.TINY, prompt_len=96)
+    W = sw.model_weights(cfg)
+    P, B, V = cfg.prompt_len, cfg.drafter.block_size, cfg.target.vocab
+    steps = 4
+    prompt = torch.from_numpy(sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)).to("cuda")
+    s = samp(cfg.sampling)
+
+    def run(use_graph):
+        eng = engine(cfg, W, max_pages_per_seq=(P + (steps + 2) * B) // 16 + 1)
+        eng.kv_alloc(0, P + (steps + 2) * B)
+        eng.prefill([0], prompt.view(1, -1), [s])
+        g = eng.capture_spec_step([0], [s]) if use_graph else None
+        out = []
+        for _ in range(steps):
+            if g is not None:
+                g.replay()
+            else:
+                eng.spec_step([0], [s])
+            n = int(eng.n_out[0])
+            out.append(eng.out[:n].cpu().clone())
+        eng.status()  # raises on any device-side flag
+        return out
+
+    eager, graph = run(False), run(True)
+    assert all(torch.equal(a, b) for a, b in zip(eager, graph))
+
+
 def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
     """Several requests with ragged prompts: each is prefilled alone and drafts its first block alone
     (the drafter injects the features of the verify call it follows), then all slots are decoded
