@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per projection launch of the decode step, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # scaled by a plain 1 GiB copy (profiles/gemm_kernel_27b_conc1_traffic.txt), and the hash of the
 # kernel source they were taken on: a changed kernel reports null until the counters are retaken.
-GEMM_TRAFFIC = {"bytes_per_launch": 179166003, "gemm_src_sha256_16": "684423cf6084ebef"}
+GEMM_TRAFFIC = {"bytes_per_launch": 179160664, "gemm_src_sha256_16": "20bf9c150ec5166b"}
 
 
 def log(msg: str):
@@ -486,7 +486,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] weights ready in {time.time() - t0:.1f}s "
         f"({sum(w.numel() * w.element_size() for w in weights.values()) / 1e9:.2f} GB)")
-    settle = SETTLE_STEPS
+    settle = 0 if args.no_graph else SETTLE_STEPS  # the settle phase exists for graph launches
     max_tokens = P + (max(Wm + K, settle + 1) + 2) * B + 2 * B
     eng = Engine(cfg, weights, max_slots=1, max_rows=P, max_pages_per_seq=max_tokens // 16 + 4)
     eng.kv_alloc(0, max_tokens)
@@ -498,14 +498,15 @@ def main():
     # untimed settle phase: the first ~24 launches of the first captured graph of a process have run ~3%
     # slower on this part (per-step events: 11.2 ms, then 10.8 ms; graphs captured later run at full
     # speed from their first launch), so a throwaway graph is launched `settle` times before any timed leg
-    log(f"[bench] settle: {settle} untimed graph launches")
-    eng.prefill([0], prompt.view(1, -1), [s_conf])
-    eng.spec_step([0], [s_conf])  # captured after a step, like the timed legs' graphs
-    g_settle = eng.capture_spec_step([0], [s_conf])
-    for _ in range(settle):
-        g_settle.replay()
-    torch.cuda.synchronize()
-    del g_settle
+    if settle:
+        log(f"[bench] settle: {settle} untimed graph launches")
+        eng.prefill([0], prompt.view(1, -1), [s_conf])
+        eng.spec_step([0], [s_conf])  # captured after a step, like the timed legs' graphs
+        g_settle = eng.capture_spec_step([0], [s_conf])
+        for _ in range(settle):
+            g_settle.replay()
+        torch.cuda.synchronize()
+        del g_settle
 
     # 1. the configured run: real drafter, T=1 / top-k / top-p
     log(f"[bench] configured run: {Wm} warmup + {K} timed steps")
