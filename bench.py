@@ -103,7 +103,7 @@ def run_spec(eng, torch, prompt, samp, warmup, steps, planted=None, profile=Fals
     # with a graph, its first launch is the last warmup step; it is captured after at least one eager step,
     # so that its launches have the decode shapes (right after a prefill the drafter's injection covers
     # every prompt row)
-    n_eager = warmup - 1 if use_graph and warmup > 1 else warmup
+    n_eager = max(1, warmup - 1) if use_graph else warmup
     for i in range(n_eager):
         eng.spec_step([0], [samp], planted=None if planted is None else planted[i], stochastic=stochastic)
         taus[i:i + 1].copy_(eng.n_out[:1])

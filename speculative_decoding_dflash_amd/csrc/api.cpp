@@ -36,6 +36,8 @@ dflash_status fail(dflash_status st, const char *fmt, ...) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
+// Planes of a projection input (X operand): bf16 models hold a high and a low bf16 plane (store_x).
+int xplanes(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 1; }
 
 constexpr int kAttnSplitMax = 64;
 constexpr int kAttnWgTarget = 512;  // work-groups a batched decode attention call aims at
@@ -80,10 +82,12 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   // per-32-column sums of squares of the rows awaiting RMSNorm: [R][ss_ld]
   L.ss_ld = (int)((H / 32 + 3) / 4 * 4);
   L.ss = take(sizeof(float) * L.ss_ld * R);
-  L.xn = take(es * R * H);
-  L.qbuf = take(es * R * QD);
-  L.attn = take(es * R * QD);
-  L.ffn = take(es * R * F);
+  // projection inputs: xplanes planes of R rows each (the low plane follows the high one)
+  const size_t np = xplanes(c);
+  L.xn = take(np * es * R * H);
+  L.qbuf = take(es * R * QD);  // fp16 (bf16 models) or fp32 q
+  L.attn = take(np * es * R * QD);
+  L.ffn = take(np * es * R * F);
   // fp32 K-range partials of one projection: up to kMaxKSplit ranges of a single row chunk, or one
   // range over all rows
   const size_t part_cols = std::max({QD + 2 * KD, (size_t)d->layers * 2 * KD, H});
@@ -182,6 +186,19 @@ struct dflash_ctx {
     return r;
   }
   int dt() const { return cfg.dtype == DFLASH_BF16 ? 0 : 1; }
+  // Low plane of the projection-input buffer at workspace offset `off` whose planes hold `plane_elems`
+  // elements (null for fp32 models).
+  void *xlo(size_t off, size_t plane_elems) const {
+    return cfg.dtype == DFLASH_BF16 ? (void *)(ws + off + plane_elems * es()) : nullptr;
+  }
+  void *xn_lo() const { return xlo(L.xn, (size_t)cap.max_rows * cfg.hidden); }
+  void *attn_lo() const { return xlo(L.attn, (size_t)cap.max_rows * cfg.q_heads * cfg.head_dim); }
+  void *ffn_lo() const { return xlo(L.ffn, (size_t)cap.max_rows * cfg.ffn); }
+  // Low plane of caller features for `rows` rows (bf16 models: [2][rows][n_taps * hidden]).
+  void *feats_lo(const void *feats, int rows) const {
+    return cfg.dtype == DFLASH_BF16 ? (void *)((const char *)feats + (size_t)rows * dcfg.n_taps * cfg.hidden * es())
+                                    : nullptr;
+  }
   int rope_rows() const { return cap.max_pages_per_seq * cap.page_tokens; }
   int es() const { return esize(&cfg); }
   void *tlayer(int l) const { return tkv + (size_t)l * layer_elems * es(); }
@@ -227,13 +244,16 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_
       return DFLASH_OK;
     }
   }
-  const char *x0 = (const char *)a.x;
-  for (int r0 = 0; r0 < R; r0 += kGemmMaxRows) {
+  // row chunks whose X operand (both planes) fits the row-chunked kernels
+  const int cr = a.x_lo ? kGemmMaxRows / 2 : kGemmMaxRows;
+  const char *x0 = (const char *)a.x, *xl0 = (const char *)a.x_lo;
+  for (int r0 = 0; r0 < R; r0 += cr) {
     GemmArgs b = a;
-    b.M = std::min(kGemmMaxRows, R - r0);
+    b.M = std::min(cr, R - r0);
     b.x = x0 + (size_t)r0 * a.ldx * es;
+    b.x_lo = xl0 ? xl0 + (size_t)r0 * a.ldx * es : nullptr;
     b.row_off = r0;
-    HIP_OK(launch_gemm(b, dt, s, r0 == 0 ? e0 : nullptr, r0 + kGemmMaxRows >= R ? e1 : nullptr));
+    HIP_OK(launch_gemm(b, dt, s, r0 == 0 ? e0 : nullptr, r0 + cr >= R ? e1 : nullptr));
   }
   return DFLASH_OK;
 }
@@ -260,7 +280,9 @@ dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *
   a.epi = EPI_PARTIAL;
   a.out_f32 = c->wsp<float>(c->L.part);
   a.ld_out = a.N;
-  a.ksplit = R <= kGemmMaxRows ? std::min(kMaxKSplit, gemm_ksplit(R, a.N, a.K, c->dt(), c->L.part_elems)) : 1;
+  a.ksplit = R <= kGemmMaxRows / xplanes(&c->cfg)
+                 ? std::min(kMaxKSplit, gemm_ksplit(R, a.N, a.K, c->dt(), c->L.part_elems))
+                 : 1;
   a.part_stride = (int64_t)R * a.N;
   *n_part = a.ksplit;
   *src = a.out_f32;
@@ -302,6 +324,7 @@ dflash_status prep_norm(dflash_ctx *c, int R, const void *gain, hipStream_t s) {
   n.eps = c->cfg.rms_eps;
   n.hidden = c->cfg.hidden;
   n.out = c->wsp<void>(c->L.xn);
+  n.out_lo = c->xn_lo();
   n.ld_out = c->cfg.hidden;
   n.n_rows = R;
   n.take = R;
@@ -324,15 +347,17 @@ void with_norm(dflash_ctx *c, GemmArgs &a, int ss_n) {
 
 // A hidden-width projection whose output is added to the residual (resid may be null: the output is
 // the new row) and then RMS-normalised with the deferred scheme; returns ss_n for the consumer.
-dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, void *feat, int ld_feat,
+dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, void *feat, void *feat_lo, int ld_feat,
                              const NextNorm &nx, hipStream_t s, int *ss_n) {
   a.epi = EPI_RESID_NORM;
   a.resid = resid;
   a.ld_resid = c->cfg.hidden;
   a.feat = feat;
+  a.feat_lo = feat ? feat_lo : nullptr;
   a.ld_feat = ld_feat;
   a.gain = (const float *)nx.gain;
   a.xg = c->wsp<void>(c->L.xn);
+  a.xg_lo = c->xn_lo();
   a.ld_xg = c->cfg.hidden;
   a.ss_out = c->wsp<float>(c->L.ss);
   a.ss_out_ld = c->L.ss_ld;
@@ -423,6 +448,7 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.part_o = c->wsp<float>(c->L.att_o);
   a.part_ml = c->wsp<float>(c->L.att_ml);
   a.out = c->wsp<void>(c->L.attn);
+  a.out_lo = c->attn_lo();
   a.ldo = m.q_heads * m.head_dim;
   a.err = c->err();
   for (int i = 0; i < n_seq; ++i) a.seq_slot[i] = slots[i];
@@ -448,7 +474,7 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
 // logits); feat: optional tap of the layer's output.  Returns the ss_n of the deferred next norm.
 dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows,
                         const int32_t *slots, int n_seq, int q_len, int attn_mode, int ctx_bound, void *feat,
-                        int ld_feat, const NextNorm &next, int *ss_n, hipStream_t s) {
+                        void *feat_lo, int ld_feat, const NextNorm &next, int *ss_n, hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   const int R = n_seq * q_len, H = m.hidden, QD = m.q_heads * m.head_dim, KD = m.kv_heads * m.head_dim, F = m.ffn;
   float *x = c->wsp<float>(c->L.x);
@@ -457,6 +483,7 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   bool fused = false;
   {
     GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_PARTIAL);
+    a.x_lo = c->xn_lo();
     a.nseg = 3;
     a.seg[0] = GemmSeg{w.wq, QD};
     a.seg[1] = GemmSeg{w.wk, KD};
@@ -496,25 +523,30 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     return st;
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID_NORM);
+    a.x_lo = c->attn_lo();
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.wo, H};
-    if ((st = run_resid_norm(c, a, R, x, nullptr, 0, all_rows(w.ffn_norm, R), s, ss_n)) != DFLASH_OK) return st;
+    if ((st = run_resid_norm(c, a, R, x, nullptr, nullptr, 0, all_rows(w.ffn_norm, R), s, ss_n)) != DFLASH_OK)
+      return st;
   }
   {
     GemmArgs a = gemm_base(xn, H, R, F, H, EPI_SWIGLU);
+    a.x_lo = c->xn_lo();
     a.nseg = 2;
     a.seg[0] = GemmSeg{w.w_gate, F};
     a.seg[1] = GemmSeg{w.w_up, F};
     a.out_act = c->wsp<void>(c->L.ffn);
+    a.out_act_lo = c->ffn_lo();
     a.ld_out = F;
     with_norm(c, a, *ss_n);
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID_NORM);
+    a.x_lo = c->ffn_lo();
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.w_down, H};
-    if ((st = run_resid_norm(c, a, R, x, feat, ld_feat, next, s, ss_n)) != DFLASH_OK) return st;
+    if ((st = run_resid_norm(c, a, R, x, feat, feat_lo, ld_feat, next, s, ss_n)) != DFLASH_OK) return st;
   }
   return DFLASH_OK;
 }
@@ -746,17 +778,21 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   } tiled_scope{c};
   c->tiled = new_sequence != 0;
   for (int l = 0; l < m.layers; ++l) {
-    void *feat = nullptr;
+    void *feat = nullptr, *feat_lo = nullptr;
     for (int t = 0; t < c->dcfg.n_taps; ++t)
-      if (c->dcfg.taps[t] == l && d_feats) feat = (char *)d_feats + (size_t)t * H * c->es();
+      if (c->dcfg.taps[t] == l && d_feats) {
+        feat = (char *)d_feats + (size_t)t * H * c->es();
+        feat_lo = c->feats_lo(feat, R);
+      }
     // after the last layer: the final norm over the last nl rows of every sequence, packed
     const NextNorm next = l + 1 < m.layers ? all_rows(c->tl[l + 1].attn_norm, R)
                                            : NextNorm{c->final_norm, nl, q_len, q_len - nl};
-    st = run_layer(c, c->tl[l], c->tlayer(l), rows, slots, batch, q_len, 0, ctx_bound, feat, ld_feat, next, &ss_n,
-                   s);
+    st = run_layer(c, c->tl[l], c->tlayer(l), rows, slots, batch, q_len, 0, ctx_bound, feat, feat_lo, ld_feat, next,
+                   &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32);
+  a.x_lo = c->xn_lo();
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
   with_norm(c, a, ss_n);
@@ -879,13 +915,16 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   int ss_n = 1;
   {
     GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_RESID_NORM);
+    a.x_lo = c->feats_lo(d_feats, Ri);
     a.nseg = 1;
     a.seg[0] = GemmSeg{c->fc, H};
-    if ((st = run_resid_norm(c, a, Ri, nullptr, nullptr, 0, all_rows(c->hidden_norm, Ri), s, &ss_n)) != DFLASH_OK)
+    if ((st = run_resid_norm(c, a, Ri, nullptr, nullptr, nullptr, 0, all_rows(c->hidden_norm, Ri), s, &ss_n)) !=
+        DFLASH_OK)
       return st;
   }
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_PARTIAL);
+    a.x_lo = c->xn_lo();
     a.nseg = 2 * dc.layers;
     QkvPostArgs p = post_base(c, ri, Ri);
     p.ld_src = dc.layers * 2 * KD;
@@ -923,11 +962,12 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   for (int j = 0; j < dc.layers; ++j) {
     // after the last layer: the final norm over the B - 1 mask positions of every block, packed
     const NextNorm next = j + 1 < dc.layers ? all_rows(c->dl[j + 1].attn_norm, R) : NextNorm{c->d_final_norm, nd, B, 1};
-    st = run_layer(c, c->dl[j], c->dlayer(j), rd, slots, batch, B, 1, ctx_bound, nullptr, 0, next, &ss_n, s);
+    st = run_layer(c, c->dl[j], c->dlayer(j), rd, slots, batch, B, 1, ctx_bound, nullptr, nullptr, 0, next, &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32);
+  a.x_lo = c->xn_lo();
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
   with_norm(c, a, ss_n);

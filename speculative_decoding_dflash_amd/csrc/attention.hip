@@ -12,61 +12,65 @@
 // token-major and V dim-major inside a page, so both A operands are contiguous loads.
 // Softmax is online in fp32 (running max per qv, corrections applied to the accumulators); a split
 // that sees no allowed key publishes m = -inf, l = 0.  Several splits are merged by a second kernel.
+// Operand types: bf16 models keep q and the KV cache in fp16 and feed the probabilities to the PV
+// product as fp16 (fp32 accumulation throughout); fp32 models run the fp32 MFMA on fp32 operands.  The
+// output is the o projection's X operand (for bf16 models a pair of bf16 planes, see store_x).
 #include "kernels.h"
 
 namespace df {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, int D> struct AttnFrag;
 
 // K fragments: kSteps 16-byte vectors per lane (A operand of S^T = K Q^T, row = key = lane % 16).
 // V fragments: D/16 vectors per lane (A operand of O^T += V^T P^T, row = dim, 4 keys per lane).
-template <int D> struct AttnFrag<bf16, D> {
+template <int D> struct AttnFrag<f16, D> {
   static constexpr int kSteps = D / 32;  // QK^T steps of 32 dims (8 per lane)
   static constexpr int kEPL = 8;         // dims per lane per step: ks * 32 + (lane / 16) * 8 + e
-  using VF = u32x2;                      // 4 bf16 keys of one dim
+  using VF = u32x2;                      // 4 fp16 keys of one dim
   static DF_DEVICE u32x4 pack(const float *v) {
     u32x4 r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+    for (int j = 0; j < 4; ++j) r[j] = (uint32_t)f32_to_f16(v[2 * j]) | ((uint32_t)f32_to_f16(v[2 * j + 1]) << 16);
     return r;
   }
-  static DF_DEVICE u32x4 load_q(const bf16 *qrow, int ks, int g) {
+  static DF_DEVICE u32x4 load_q(const f16 *qrow, int ks, int g) {
     return *reinterpret_cast<const u32x4 *>(qrow + ks * 32 + g * 8);
   }
-  static DF_DEVICE void load_k(u32x4 *kf, const bf16 *kblk, int key, int g) {
+  static DF_DEVICE void load_k(u32x4 *kf, const f16 *kblk, int key, int g) {
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) kf[ks] = *reinterpret_cast<const u32x4 *>(kblk + key * D + ks * 32 + g * 8);
   }
-  static DF_DEVICE void load_v(VF *vf, const bf16 *vblk, int l16, int g) {
+  static DF_DEVICE void load_v(VF *vf, const f16 *vblk, int l16, int g) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x2 *>(vblk + (dt * 16 + l16) * 16 + 4 * g);
   }
   static DF_DEVICE void qk(f32x4 &acc, const u32x4 *kf, const u32x4 *q) {
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, q[ks]),
-                                                    acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, kf[ks]), __builtin_bit_cast(h16x8, q[ks]),
+                                                   acc, 0, 0, 0);
   }
   // element i (key 4g + i) of a V fragment, as raw bits
   static DF_DEVICE void set_v(VF &v, int i, uint32_t bits) {
     const int w = i >> 1, sh = (i & 1) * 16;
     v[w] = (v[w] & ~(0xFFFFu << sh)) | (bits << sh);
   }
-  static DF_DEVICE uint32_t raw(const bf16 &e) { return e.bits; }
-  // p[r]: probability of key 4g + r for this lane's qv.
+  static DF_DEVICE uint32_t raw(const f16 &e) { return e.bits; }
+  // p[r]: probability of key 4g + r for this lane's qv (in [0, 1]: fp16 keeps 11 significant bits of it).
   static DF_DEVICE void pv(f32x4 *o, const VF *vf, const float *p) {
-    s16x4 pb;
-    pb[0] = (short)f32_to_bf16(p[0]);
-    pb[1] = (short)f32_to_bf16(p[1]);
-    pb[2] = (short)f32_to_bf16(p[2]);
-    pb[3] = (short)f32_to_bf16(p[3]);
+    h16x4 pb;
+    pb[0] = (_Float16)p[0];
+    pb[1] = (_Float16)p[1];
+    pb[2] = (_Float16)p[2];
+    pb[3] = (_Float16)p[3];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf[dt]), pb, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, vf[dt]), pb, o[dt], 0, 0, 0);
   }
 };
 
@@ -123,6 +127,7 @@ DF_DEVICE X vload(const X *p, int i) {
 template <typename T, int D, int NQT, bool FUSED>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using F = AttnFrag<T, D>;
+  using XT = typename XOf<T>::type;  // output (X operand) type
   __shared__ __attribute__((aligned(16))) float so[4][16][D + 4];  // rows 16-byte aligned
   __shared__ float sm[4][NQT * 16], sl[4][NQT * 16];
   // fused calls: the block's own keys (K [16][D], V [D][16], row j = block row j), built here from raw k / v
@@ -621,9 +626,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
       const int row = rbase + qv / G, head = kh * G + qv % G;
       if (a.n_splits == 1) {
-        T *out = (T *)a.out + (size_t)row * a.ldo + head * D + d0;
+        const size_t oi = (size_t)row * a.ldo + head * D + d0;
 #pragma unroll
-        for (int d = 0; d < DPT; ++d) Elem<T>::store(out + d, L > 0.f ? O[d] / L : 0.f);
+        for (int d = 0; d < DPT; ++d) store_x((XT *)a.out, (XT *)a.out_lo, oi + d, L > 0.f ? O[d] / L : 0.f);
       } else {
         const size_t pi = ((size_t)row * a.q_heads + head) * a.n_splits + split;
         float *po = a.part_o + pi * D + d0;
@@ -725,18 +730,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       acc.w += w * u.w;
     }
     const float li = linv[qv];
-    T *out = (T *)a.out + (size_t)row * a.ldo + head * D + d4;
-    Elem<T>::store(out + 0, acc.x * li);
-    Elem<T>::store(out + 1, acc.y * li);
-    Elem<T>::store(out + 2, acc.z * li);
-    Elem<T>::store(out + 3, acc.w * li);
+    const size_t oi = (size_t)row * a.ldo + head * D + d4;
+    store_x((XT *)a.out, (XT *)a.out_lo, oi + 0, acc.x * li);
+    store_x((XT *)a.out, (XT *)a.out_lo, oi + 1, acc.y * li);
+    store_x((XT *)a.out, (XT *)a.out_lo, oi + 2, acc.z * li);
+    store_x((XT *)a.out, (XT *)a.out_lo, oi + 3, acc.w * li);
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // out[row][head] = sum_s 2^{m_s - M} O_s / sum_s 2^{m_s - M} l_s  (splits in order; m in log2 units).
 // One work-group per (row, head), thread d for dimension d.
-template <typename T>
+template <typename XT>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows) {
   // Up to kR splits: every thread loads all (m, l) pairs (the same addresses across the work-group)
   // and its dimension's partial outputs at once, so the merge waits for one round of loads.
@@ -770,7 +775,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows)
         L += w * lv[s];
         O += w * pv[s];
       }
-    if (tid < D) Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + tid, L > 0.f ? O / L : 0.f);
+    if (tid < D) store_x((XT *)a.out, (XT *)a.out_lo, (size_t)row * a.ldo + head * D + tid, L > 0.f ? O / L : 0.f);
     return;
   }
   __shared__ float sw[64];
@@ -791,7 +796,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows)
     float O = 0.f;
 #pragma unroll 8
     for (int s = 0; s < ns; ++s) O += sw[s] * po[(size_t)s * D + dim];
-    Elem<T>::store((T *)a.out + (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
+    store_x((XT *)a.out, (XT *)a.out_lo, (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
   }
 }
 
@@ -819,16 +824,16 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;
   const int n_rows = a.n_seq * a.q_len;
-  hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(n_rows * a.q_heads), dim3(128), 0, s, a, n_rows);
+  hipLaunchKernelGGL((attn_merge_kernel<typename XOf<T>::type>), dim3(n_rows * a.q_heads), dim3(128), 0, s, a, n_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s) {
   const int D = a.kvl.head_dim;
-  if (dtype == 0) {
-    if (D == 128) return launch_attn_t<bf16, 128>(a, s);
-    if (D == 64) return launch_attn_t<bf16, 64>(a, s);
-    if (D == 32) return launch_attn_t<bf16, 32>(a, s);
+  if (dtype == 0) {  // bf16 models: fp16 q and KV cache
+    if (D == 128) return launch_attn_t<f16, 128>(a, s);
+    if (D == 64) return launch_attn_t<f16, 64>(a, s);
+    if (D == 32) return launch_attn_t<f16, 32>(a, s);
   } else {
     if (D == 128) return launch_attn_t<float, 128>(a, s);
     if (D == 64) return launch_attn_t<float, 64>(a, s);

@@ -28,7 +28,12 @@ DF_HOST_DEVICE uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Element access for the two storage types.
+// IEEE binary16 stored as raw 16-bit words: the attention operands (q, the KV cache) of bf16 models.
+struct f16 {
+  uint16_t bits;
+};
+
+// Element access for the storage types.
 template <typename T> struct Elem;
 template <> struct Elem<bf16> {
   static DF_DEVICE float load(const bf16 *p) { return bf16_to_f32(p->bits); }
@@ -40,6 +45,39 @@ template <> struct Elem<float> {
   static DF_DEVICE void store(float *p, float v) { *p = v; }
   static constexpr int kPerVec = 4;
 };
+// Round to nearest even; magnitudes beyond the largest finite half (65504) saturate to it.
+DF_DEVICE uint16_t f32_to_f16(float f) {
+  const _Float16 h = (_Float16)fminf(fmaxf(f, -65504.f), 65504.f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+DF_DEVICE float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+template <> struct Elem<f16> {
+  static DF_DEVICE float load(const f16 *p) { return f16_to_f32(p->bits); }
+  static DF_DEVICE void store(f16 *p, float v) { p->bits = f32_to_f16(v); }
+  static constexpr int kPerVec = 8;
+};
+
+// Storage type of the attention operands (q, K, V) for a model whose weights are T: fp16 for bf16
+// models (11 significant bits where bf16 keeps 8; q and k are RMS-normalised and the softmax weights
+// lie in [0, 1]), fp32 for fp32 models.
+template <typename T> struct KvOf;
+template <> struct KvOf<bf16> { using type = f16; };
+template <> struct KvOf<float> { using type = float; };
+// and back: the projection-input type that goes with a KV storage type
+template <typename K> struct XOf;
+template <> struct XOf<f16> { using type = bf16; };
+template <> struct XOf<float> { using type = float; };
+
+// Projection inputs (the X operand of every weight product) of bf16 models are held as two bf16
+// planes, hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact in fp32), so that hi + lo carries v to
+// about 16 significant bits and the product W (hi + lo) = W hi + W lo loses nothing to the storage of
+// X.  fp32 models keep one plane (lo is null).
+DF_DEVICE void store_x(bf16 *hi, bf16 *lo, size_t i, float v) {
+  const uint16_t h = f32_to_bf16(v);
+  hi[i].bits = h;
+  if (lo) lo[i].bits = f32_to_bf16(v - bf16_to_f32(h));
+}
+DF_DEVICE void store_x(float *hi, float *, size_t i, float v) { hi[i] = v; }
 
 // Device state of one sequence slot (lives in the workspace).
 struct SlotState {

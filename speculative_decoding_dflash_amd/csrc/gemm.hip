@@ -55,6 +55,12 @@ template <> struct Frag<float> {
 
 template <typename T> DF_DEVICE u32x4 ld16(const T *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Row v of the X operand as the kernels see it: rows 0 .. M-1 of x, then (with a low plane) rows
+// 0 .. M-1 of x_lo.
+template <typename T> DF_DEVICE const T *x_row(const GemmArgs &a, int v) {
+  return v < a.M ? (const T *)a.x + (size_t)v * a.ldx : (const T *)a.x_lo + (size_t)(v - a.M) * a.ldx;
+}
+
 DF_DEVICE float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Prefetch of the deferred RMSNorm's partial sums of squares: those of X row m sit at
@@ -123,12 +129,6 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
         a.out_f32[(size_t)(a.row_off + m) * a.ld_out + COLS * c + j] = lds[m * COLS + j] * (rs ? s_rstd[m] : 1.f);
       }
       break;
-    case EPI_STORE_ACT:
-      for (int e = tid; e < M * COLS; e += NT) {
-        const int m = e / COLS, j = e % COLS;
-        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + COLS * c + j, lds[m * COLS + j]);
-      }
-      break;
     case EPI_PARTIAL: {
       float *o = a.out_f32 + (size_t)split * a.part_stride;
       for (int e = tid; e < M * COLS; e += NT) {
@@ -143,7 +143,7 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
         const int m = e / HC, j = e % HC;
         const float r = rs ? s_rstd[m] : 1.f;
         const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + HC + j] * r;
-        Elem<T>::store((T *)a.out_act + (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
+        store_x((T *)a.out_act, (T *)a.out_act_lo, (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
       }
       break;
     }
@@ -158,10 +158,10 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
             v += a.resid[idx];
             a.resid[idx] = v;
           }
-          if (a.feat) Elem<T>::store((T *)a.feat + (size_t)r * a.ld_feat + n, v);
+          if (a.feat) store_x((T *)a.feat, (T *)a.feat_lo, (size_t)r * a.ld_feat + n, v);
           const int jj = r % a.sel_stride - a.sel_offset;
           if (jj >= 0 && jj < a.sel_take)
-            Elem<T>::store((T *)a.xg + (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
+            store_x((T *)a.xg, (T *)a.xg_lo, (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
           lds[m * COLS + j] = v * v;  // entry owned by this thread
         }
         __syncthreads();
@@ -182,7 +182,8 @@ template <typename T, int MT, int CT, int NW, int PD, int XR>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Frag<T>;
   constexpr int COLS = 16 * CT;
-  // XR: X rows staged per super-step (8 when M <= 8, else padded to whole MFMA tiles, 16 * MT)
+  // XR: X operand rows staged per super-step (8 when there are at most 8, else padded to whole MFMA
+  // tiles, 16 * MT)
   static_assert(XR == 16 * MT || (MT == 1 && XR == 8), "X staging rows");
   constexpr int NT = NW * 64;
   constexpr int ROWB = 256 + 16;           // LDS bytes per staged row (256 B of K plus padding)
@@ -231,13 +232,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
         qrow[q] = (const T *)a.seg[q / 2].w + (size_t)(8 * c + 4 * (q % 2) + g) * a.K + k0 + r16 * F::kEPL;
     }
   }
-  // X rows >= M load row 0 (never read back: the operand read below masks them), so that every
-  // load in the streaming loop is unconditional and the compiler can count outstanding loads exactly.
+  // X rows: with a low plane the operand has Mv = 2M rows, rows M .. 2M-1 being the low parts of rows
+  // 0 .. M-1 (their products are added in the reduction below).  Rows >= Mv load row 0 (never read back:
+  // the operand read below masks them), so that every load in the streaming loop is unconditional and
+  // the compiler can count outstanding loads exactly.
+  const int Mv = a.x_lo ? 2 * a.M : a.M;
   const T *xrow[NXQ];
 #pragma unroll
   for (int q = 0; q < NXQ; ++q) {
     const int m = 4 * q + g;
-    xrow[q] = (const T *)a.x + (size_t)(m < a.M ? m : 0) * a.ldx + k0 + r16 * F::kEPL;
+    xrow[q] = x_row<T>(a, m < Mv ? m : 0) + k0 + r16 * F::kEPL;
   }
 
   f32x4 acc[MT][CT];
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
           u32x4 xv[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            xv[mt] = (mt * 16 + r16 < a.M)
+            xv[mt] = (mt * 16 + r16 < Mv)
                          ? *reinterpret_cast<const u32x4 *>(xt + (mt * 16 + (r16 < XR ? r16 : 0)) * ROWB + ks * 64 + 16 * g)
                          : zero;
 #pragma unroll
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r16;
-      const u32x4 xv = m < a.M ? ld16((const T *)a.x + (size_t)m * a.ldx + k) : zero;
+      const u32x4 xv = m < Mv ? ld16(x_row<T>(a, m) + k) : zero;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) F::mma(acc[mt][ct], xv, ld16(wbase[ct] + (size_t)r16 * a.K + k));
     }
@@ -328,18 +332,27 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) lds[wave * kEnt + (mt * 16 + g * 4 + r) * COLS + ct * 16 + r16] = acc[mt][ct][r];
   __syncthreads();
-  for (int e = tid; e < kEnt; e += NT) {
+  // output row m < M: the waves' sums of operand row m, plus those of its low part (row M + m)
+  const int lo_off = a.x_lo ? a.M * COLS : 0;
+  for (int e = tid; e < a.M * COLS; e += NT) {
     float v = lds[e];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += lds[w * kEnt + e];
-    lds[e] = v;  // entry e is read and written by this thread only
+    if (lo_off) {
+      float u = lds[e + lo_off];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) u += lds[w * kEnt + e + lo_off];
+      v += u;
+    }
+    lds[e] = v;  // entry e < M * COLS is read and written by this thread only
   }
   if (a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
   __syncthreads();
   gemm_epilogue<T, COLS, NT>(a, c, split, lds, s_rstd);
 }
 
-// Stream-K variant (M <= 16, ksplit 1, K a whole number of super-steps; 32-column tiles, 8 waves).
+// Stream-K variant (at most 16 X operand rows, low planes included; ksplit 1, K a whole number of
+// super-steps; 32-column tiles, 8 waves).
 // With one tile per work-group, projections whose tile count is not a multiple of the CU count leave
 // CUs idle while others stream (160 hidden-width tiles on 256 CUs).  Here the projection's items
 // (tile, super-step), numbered tile-major, are cut into equal contiguous ranges, one per work-group
@@ -397,11 +410,12 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   size_t qoff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) qoff[q] = (size_t)(4 * q + g) * a.K + r16 * F::kEPL;
+  const int Mv = a.x_lo ? 2 * a.M : a.M;  // X operand rows (low plane rows after the M rows)
   const T *xrow[NXQ];
 #pragma unroll
   for (int q = 0; q < NXQ; ++q) {
     const int m = 4 * q + g;
-    xrow[q] = (const T *)a.x + (size_t)(m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
+    xrow[q] = x_row<T>(a, m < Mv ? m : 0) + r16 * F::kEPL;
   }
   SsPrefetch<NT> ssp;
   ssp.load(a);
@@ -449,7 +463,7 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
       issue();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 xv = r16 < a.M
+        const u32x4 xv = r16 < Mv
                              ? *reinterpret_cast<const u32x4 *>(xt + (r16 < XR ? r16 : 0) * ROWB + ks * 64 + 16 * g)
                              : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
@@ -467,13 +481,21 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
       for (int r = 0; r < 4; ++r) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = acc[ct][r];
     __syncthreads();
     if (seg == 0 && a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
+    // output row m < M: the waves' sums of operand row m plus those of its low part (row M + m)
+    const int lo_off = a.x_lo ? a.M * COLS : 0;
     float v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = tid + i * NT;
       v[i] = 0.f;
-      if (e < a.M * COLS)
+      if (e < a.M * COLS) {
         for (int w = 0; w < NW; ++w) v[i] += rb[w * kEnt + e];
+        if (lo_off) {
+          float u = 0.f;
+          for (int w = 0; w < NW; ++w) u += rb[w * kEnt + e + lo_off];
+          v[i] += u;
+        }
+      }
     }
     if (t * nsup < lo || (t + 1) * nsup > hi) {  // shared tile
       const int q0 = (t * nsup) / per, q1 = ((t + 1) * nsup - 1) / per;
@@ -543,7 +565,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
   const int r16 = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const bool swiglu = a.epi == EPI_SWIGLU;
-  const int m0 = blockIdx.y * BM;
+  // With a low plane of X the tile's BM operand rows hold RT = BM / 2 output rows: in each wave the
+  // fragments i < MI / 2 carry the high parts of the wave's rows and fragments MI / 2 + i their low parts
+  // (added into the high fragments' sums after the K loop).
+  const bool lo = a.x_lo != nullptr;
+  const int RT = lo ? BM / 2 : BM;
+  const int nI = lo ? MI / 2 : MI;  // output fragments per wave
+  const int m0 = blockIdx.y * RT;
   const int n0 = blockIdx.x * (swiglu ? BN / 2 : BN);  // first output column of the tile
   const int K = a.K;
   // this work-group's K steps: [kt0, kt1)
@@ -554,7 +582,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
-    pa[i] = (const bf16 *)a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + kc;
+    int lr = row, plane = 0;  // the operand row's output row (in the tile) and plane
+    if (lo) {
+      const int w2 = row / (BM / 2), fi = (row % (BM / 2)) / 16;
+      plane = fi >= MI / 2;
+      lr = w2 * (RT / 2) + 16 * (fi % (MI / 2)) + row % 16;
+    }
+    pa[i] = (const bf16 *)(plane ? a.x_lo : a.x) + (size_t)min(m0 + lr, a.M - 1) * a.ldx + kc;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -574,7 +608,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
     pb[i] = w + kc;
   }
   const bool scaled = !raw || a.mb_direct;  // raw sums of a direct partial output carry the 1/rms
-  if (scaled && tid < BM) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
+  if (scaled && tid < RT) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
 
   f32x4 acc[MI][4];
 #pragma unroll
@@ -640,6 +674,12 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
     kstep(kt + 1, std::integral_constant<int, 1>{});
   }
   if (kt < kt1) kstep(kt, std::integral_constant<int, 0>{});
+  if (lo) {
+#pragma unroll
+    for (int i = 0; i < MI / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += acc[i + MI / 2][j];
+  }
 
   if (raw) {  // this K range's raw sums: [range][M][N] (SWIGLU: gate columns [0, N), up columns [N, 2N))
     const int nraw = swiglu ? 2 * a.N : a.N;
@@ -648,8 +688,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int ml = wm * (BM / 2) + 16 * i + 4 * g + r, m = m0 + ml;
-        if (m >= a.M) continue;
+        const int ml = wm * (RT / 2) + 16 * i + 4 * g + r, m = m0 + ml;
+        if (i >= nI || m >= a.M) continue;
         const float sc = scaled ? s_rstd[ml] : 1.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -662,13 +702,14 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
     return;
   }
 
-  // acc[i][j][r] = Y[row m0 + wm*(BM/2) + 16 i + 4 g + r][tile column wn*64 + 16 j + r16]
+  // acc[i][j][r] = Y[row m0 + wm*(RT/2) + 16 i + 4 g + r][tile column wn*64 + 16 j + r16], i < nI
   const bool rs = a.ss_in != nullptr;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int ml = wm * (BM / 2) + 16 * i + 4 * g + r, m = m0 + ml;
+      if (i >= nI) continue;
+      const int ml = wm * (RT / 2) + 16 * i + 4 * g + r, m = m0 + ml;
       const bool live = m < a.M;
       const float sc = rs ? s_rstd[ml] : 1.f;
       const int grow = a.row_off + m;
@@ -680,19 +721,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
             for (int j = 0; j < 4; ++j)
               a.out_f32[(size_t)grow * a.ld_out + n0 + wn * 64 + 16 * j + r16] = acc[i][j][r] * sc;
           break;
-        case EPI_STORE_ACT:
-          if (live)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              Elem<bf16>::store((bf16 *)a.out_act + (size_t)grow * a.ld_out + n0 + wn * 64 + 16 * j + r16, acc[i][j][r]);
-          break;
         case EPI_SWIGLU:
           if (live)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const float gt = acc[i][2 * q][r] * sc, up = acc[i][2 * q + 1][r] * sc;
-              Elem<bf16>::store((bf16 *)a.out_act + (size_t)grow * a.ld_out + n0 + 16 * (2 * wn + q) + r16,
-                                silu(gt) * up);
+              store_x((bf16 *)a.out_act, (bf16 *)a.out_act_lo, (size_t)grow * a.ld_out + n0 + 16 * (2 * wn + q) + r16,
+                      silu(gt) * up);
             }
           break;
         case EPI_RESID_NORM: {
@@ -712,8 +747,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
                   v += a.resid[idx];
                   a.resid[idx] = v;
                 }
-                if (a.feat) Elem<bf16>::store((bf16 *)a.feat + (size_t)grow * a.ld_feat + n, v);
-                if (sel) Elem<bf16>::store((bf16 *)a.xg + o * a.ld_xg + n, v * a.gain[n]);
+                if (a.feat) store_x((bf16 *)a.feat, (bf16 *)a.feat_lo, (size_t)grow * a.ld_feat + n, v);
+                if (sel) store_x((bf16 *)a.xg, (bf16 *)a.xg_lo, o * a.ld_xg + n, v * a.gain[n]);
               }
               ss += v * v;
             }
@@ -819,21 +854,34 @@ static int mb_splits(const GemmArgs &a, int tiles, int *steps) {
   return (nk + *steps - 1) / *steps;
 }
 
+// X operand rows of a projection (a low plane doubles them)
+static int x_rows(const GemmArgs &a) { return a.x_lo ? 2 * a.M : a.M; }
+
+// Tile height of a decode-batch projection: 64 operand rows up to 64 operand rows, else 128; *rt = the
+// output rows per tile (half the operand rows with a low plane).
+static int mb_bm(const GemmArgs &a, int *rt) {
+  const int BM = x_rows(a) <= 64 ? 64 : 128;
+  *rt = a.x_lo ? BM / 2 : BM;
+  return BM;
+}
+
 int gemm_mb_slices(const GemmArgs &a) {
   const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
-  const int BM = a.M <= 64 ? 64 : 128;
+  int rt = 0;
+  mb_bm(a, &rt);
   int steps = 0;
-  return mb_splits(a, (a.N / tn) * ((a.M + BM - 1) / BM), &steps);
+  return mb_splits(a, (a.N / tn) * ((a.M + rt - 1) / rt), &steps);
 }
 
 hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int tn = swiglu ? kMmBN / 2 : kMmBN;
-  const int BM = a.M <= 64 ? 64 : 128;
-  const int tiles = (a.N / tn) * ((a.M + BM - 1) / BM);
+  int rt = 0;
+  const int BM = mb_bm(a, &rt);
+  const int tiles = (a.N / tn) * ((a.M + rt - 1) / rt);
   int steps = 0;
   const int ks = mb_splits(a, tiles, &steps);
-  const dim3 grid(a.N / tn, (a.M + BM - 1) / BM, ks), block(256);
+  const dim3 grid(a.N / tn, (a.M + rt - 1) / rt, ks), block(256);
   float *raw = ks > 1 ? a.mb_raw : nullptr;
   const bool direct = a.mb_direct && a.epi == EPI_PARTIAL;  // the ranges are the output: no reduce
   hipEvent_t end = ks > 1 && !direct ? nullptr : e1;
@@ -871,7 +919,7 @@ static void launch_xr(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEv
 template <typename T, int MT, int CT, int NW>
 static void launch_pd(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if constexpr (MT == 1) {
-    if (a.M <= 8) {
+    if (x_rows(a) <= 8) {
       launch_xr<T, MT, CT, NW, 8>(a, pd, grid, s, e0, e1);
       return;
     }
@@ -956,7 +1004,7 @@ int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems) {
 // DFLASH_GEMM_SK=0 turns it off, =1 uses it wherever the shape allows.
 static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
   const int env = env_int("DFLASH_GEMM_SK", -1);  // read per launch: tests switch it
-  if (!a.sk_part || !a.sk_cnt || env == 0 || a.M < 1 || a.M > 16 || a.ksplit != 1) return 0;
+  if (!a.sk_part || !a.sk_cnt || env == 0 || a.M < 1 || x_rows(a) > 16 || a.ksplit != 1) return 0;
   const int sk = dtype == 0 ? 128 : 64;  // K elements per super-step
   if (a.K < sk || a.K % sk) return 0;
   const bool swiglu = a.epi == EPI_SWIGLU;
@@ -988,24 +1036,28 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
   if (a.epi == EPI_RESID_NORM && a.N / 32 > a.ss_out_ld) return hipErrorInvalidValue;
   if (gemm_mm_ok(a, dtype)) {
     const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
-    const dim3 grid(a.N / tn, (a.M + kMmBM - 1) / kMmBM), block(256);
+    const int rt = a.x_lo ? kMmBM / 2 : kMmBM;  // output rows per tile
+    const dim3 grid(a.N / tn, (a.M + rt - 1) / rt), block(256);
     hipExtLaunchKernelGGL(gemm_mm_kernel<kMmBM>, grid, block, 0, s, e0, e1, 0, a, (float *)nullptr, a.K / kMmBK);
     return hipGetLastError();
   }
   int n_wg = 0;
   if (const int per = sk_per(a, dtype, &n_wg)) {
     const dim3 grid(n_wg), block(512);
+    const bool x8 = x_rows(a) <= 8;
     if (dtype == 0) {
-      if (a.M <= 8) hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8>), grid, block, 0, s, e0, e1, 0, a, per);
+      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8>), grid, block, 0, s, e0, e1, 0, a, per);
       else hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16>), grid, block, 0, s, e0, e1, 0, a, per);
     } else {
-      if (a.M <= 8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8>), grid, block, 0, s, e0, e1, 0, a, per);
+      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8>), grid, block, 0, s, e0, e1, 0, a, per);
       else hipExtLaunchKernelGGL((gemm_sk_kernel<float, 16>), grid, block, 0, s, e0, e1, 0, a, per);
     }
     return hipGetLastError();
   }
   const TileCfg t = pick_tiles(a.epi, a.N, a.K);
-  const int MT = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
+  const int xr = x_rows(a);
+  if (xr > kGemmMaxRows) return hipErrorInvalidValue;  // the host chunks longer inputs
+  const int MT = xr <= 16 ? 1 : (xr <= 32 ? 2 : 4);
   if (dtype == 0) {
     if (MT == 1) launch_mt<bf16, 1>(a, t.ct, t.nw, t.pd, s, e0, e1);
     else if (MT == 2) launch_mt<bf16, 2>(a, t.ct, t.nw, t.pd, s, e0, e1);
@@ -1020,7 +1072,8 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
 
 // ------------------------------------------------------------------ per-head q/k RMSNorm + RoPE + scatter
 // One work-group per row and group of heads.  Lane i of a head's lane group holds elements i and
-// i + d/2, exactly the pair that rotate-half RoPE rotates together.
+// i + d/2, exactly the pair that rotate-half RoPE rotates together.  T: the storage type of q and of
+// the KV cache.
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
   const int row = blockIdx.x;
@@ -1089,7 +1142,8 @@ hipError_t launch_qkv_post(const QkvPostArgs &a, int dtype, hipStream_t s) {
   if (a.n_rows == 0) return hipSuccess;
   const int tpp = kWave / (a.kv.head_dim / 2);
   dim3 grid(a.n_rows, (a.total_heads + 4 * tpp - 1) / (4 * tpp));
-  if (dtype == 0) hipLaunchKernelGGL((qkv_post_kernel<bf16>), grid, dim3(256), 0, s, a);
+  // q and the KV cache hold the attention operands' storage type (fp16 for bf16 models)
+  if (dtype == 0) hipLaunchKernelGGL((qkv_post_kernel<f16>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((qkv_post_kernel<float>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -6,9 +6,9 @@ namespace df {
 
 // ---------------------------------------------------------------- GEMM: Y = X W^T with fused epilogues
 constexpr int kGemmMaxSeg = 16;
-constexpr int kGemmMaxRows = 64;  // rows per launch; longer inputs are chunked by the host
+constexpr int kGemmMaxRows = 64;  // X operand rows per launch (low planes included); the host chunks longer inputs
 
-enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_PARTIAL = 2, EPI_SWIGLU = 3, EPI_RESID_NORM = 4 };
+enum EpiKind { EPI_STORE_F32 = 0, EPI_PARTIAL = 2, EPI_SWIGLU = 3, EPI_RESID_NORM = 4 };
 enum SegRole { ROLE_PLAIN = 0, ROLE_Q = 1, ROLE_K = 2, ROLE_V = 3 };
 
 struct GemmSeg {
@@ -18,13 +18,15 @@ struct GemmSeg {
 
 struct GemmArgs {
   const void *x;
+  const void *x_lo;  // low plane of X (bf16 models: X = x + x_lo, see store_x), or null; same ldx
   int32_t ldx;
   int32_t M, N, K;      // N: output columns (SWIGLU: ffn width; otherwise total segment rows)
   int32_t nseg;         // segments concatenated along N (SWIGLU: 0 = gate, 1 = up)
   GemmSeg seg[kGemmMaxSeg];
   int32_t epi;
   float *out_f32;       // EPI_STORE_F32; EPI_PARTIAL: K range s writes out_f32 + s * part_stride
-  void *out_act;        // EPI_STORE_ACT, EPI_SWIGLU
+  void *out_act;        // EPI_SWIGLU (an X operand: hi plane)
+  void *out_act_lo;     //   its low plane (or null)
   int32_t ld_out;
   int32_t ksplit;       // K ranges, one per grid row (> 1 only with EPI_PARTIAL)
   int64_t part_stride;  // EPI_PARTIAL: elements between the K ranges' output slices
@@ -40,18 +42,21 @@ struct GemmArgs {
   // o = (r / sel_stride) * sel_take + r % sel_stride - sel_offset, also get xg[o][n] = act(v * gain[n])
   // and ss_out[o * ss_out_ld + tile] = the sum of v^2 over the tile's 32 columns (the next projection's
   // ss_in, ss_n = N / 32).
+  // feat and xg are X operands of later projections: hi planes, with their low planes feat_lo / xg_lo
+  // (null: one plane).
   float *resid;
   int32_t ld_resid;
-  void *feat;
+  void *feat, *feat_lo;
   int32_t ld_feat;
   const float *gain;
-  void *xg;
+  void *xg, *xg_lo;
   int32_t ld_xg;
   float *ss_out;
   int32_t ss_out_ld;
   int32_t sel_take, sel_stride, sel_offset;
-  // Optional stream-K scratch (null: one work-group per tile).  With it, M <= 16, ksplit 1 and K a
-  // whole number of 256-byte super-steps, the launcher may spread the projection's (tile, super-step)
+  // Optional stream-K scratch (null: one work-group per tile).  With it, at most 16 X operand rows (M,
+  // or 2M with a low plane), ksplit 1 and K a whole number of 256-byte super-steps, the launcher may
+  // spread the projection's (tile, super-step)
   // items evenly over one work-group per CU: sk_part holds 2 * kSkTileElems fp32 partial-tile entries
   // per work-group (at most sk_max_wg work-groups), sk_cnt one arrival counter per tile (at most
   // sk_max_tiles), zero before the launch and zero again after it.
@@ -145,12 +150,12 @@ struct NormArgs {
   const float *part;
   int32_t n_part, ld_part;
   int64_t part_stride;
-  void *feat;
+  void *feat, *feat_lo;  // X-operand planes (lo may be null)
   int32_t ld_feat;
   const float *gain;
   float eps;
   int32_t hidden;
-  void *out;
+  void *out, *out_lo;    // X-operand planes (lo may be null)
   int32_t ld_out;
   int32_t n_rows, take, stride, offset;
   // Deferred normalisation: when set, selected rows get out = act(v * gain) (no 1/rms factor) and
@@ -181,7 +186,7 @@ struct AttnArgs {
   int32_t split_tokens;  // keys per split (multiple of page_tokens)
   float *part_o;         // [rows*q_heads][n_splits][head_dim]
   float *part_ml;        // [rows*q_heads][n_splits][2]
-  void *out;             // [rows][q_heads*head_dim] act
+  void *out, *out_lo;    // [rows][q_heads*head_dim]: the o projection's X operand (planes; lo may be null)
   int32_t ldo;
   int32_t *err;
   // Fused post-processing (calls with one query tile per sequence; q is then unused): q, k, v of the

@@ -62,7 +62,10 @@ class Engine:
         self.ctx = B.dflash_create(self.mc, self.dc, self.tw, self.dw, self.cap, self.tkv, self.dkv, self.ws)
         act = torch.bfloat16 if t.dtype == "bf16" else torch.float32
         rows = max(max_rows, 1)
-        self.feats = torch.empty(rows * len(d.taps) * t.hidden, dtype=act, device=self.device)
+        # target features of the last verify: bf16 models hold a high and a low plane of the rows
+        # ([2][rows][taps * hidden], the low plane right after the call's rows), fp32 models one plane
+        self.x_planes = 2 if t.dtype == "bf16" else 1
+        self.feats = torch.empty(self.x_planes * rows * len(d.taps) * t.hidden, dtype=act, device=self.device)
         nl = max_slots * self.B
         self.logits = torch.empty(max(nl, 1) * t.vocab, dtype=torch.float32, device=self.device)
         self.draft_logits = torch.empty(max_slots * max(self.B - 1, 1) * t.vocab, dtype=torch.float32,
@@ -76,6 +79,7 @@ class Engine:
         nq = max_slots * max(self.B - 1, 1) * B.MAX_TOPK
         self.q_ids = torch.zeros(nq, dtype=torch.int32, device=self.device)
         self.q_p = torch.zeros(nq, dtype=torch.float32, device=self.device)
+        self._last_verify = None  # (slots, q_len) of the last verify call
 
     def close(self):
         if self.ctx:
@@ -99,6 +103,7 @@ class Engine:
                logits: Optional[torch.Tensor] = None):
         B.dflash_verify_block(self.ctx, slots, tokens, q_len, new_sequence, n_logit_rows,
                               self.logits if logits is None else logits, self.feats)
+        self._last_verify = (tuple(int(x) for x in slots), int(q_len))
 
     def accept(self, slots: Sequence[int], n_draft: int, samplings: Sequence[B.Sampling], block=None, cands=False,
                logits: Optional[torch.Tensor] = None, q: bool = False):
@@ -148,9 +153,18 @@ class Engine:
         """Captures one spec_step (draft -> verify -> accept) into a HIP graph; each replay performs the
         next step.  Every launch parameter of a step is fixed on the host for fixed slots and KV
         allocations (positions, lengths and the accepted tokens live in device memory), so one capture
-        serves every later step.  Capture records work without running it, so the library's host-side
-        bookkeeping advances as if a step had been issued; call it after the prefill (or a step) and
-        then only replay.  planted: a fixed device tensor copied into the drafts at every replay."""
+        serves every later step -- provided the captured launches have the steady-state shapes: the
+        step's drafter injection covers as many feature rows as the previous verify wrote, so the last
+        verify before the capture must be a block verify over the same slots (an eager spec_step);
+        right after a prefill (prompt-length rows, another row stride) or a plain-decoding step (one
+        row) the replays would inject the wrong rows, and this raises instead.  Capture records work
+        without running it, so the library's host-side bookkeeping advances as if a step had been
+        issued; after the capture only replay.  planted: a fixed device tensor copied into the drafts at
+        every replay."""
+        want = (tuple(int(x) for x in slots), self.B)
+        if self._last_verify != want:
+            raise RuntimeError(f"capture_spec_step: the last verify was {self._last_verify} (slots, q_len), not a "
+                               f"block verify {want} over the same slots; run one eager spec_step first")
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self.spec_step(slots, samplings, planted=planted, stochastic=stochastic)

@@ -69,7 +69,11 @@ def test_prefill_logits_and_features(name):
     eng.verify([0], toks, P, True, P, logits=logits)
     eng.status()
     g = logits.view(P, -1).cpu().numpy()
-    gf = eng.feats[:P * len(cfg.drafter.taps) * cfg.target.hidden].view(P, len(cfg.drafter.taps), -1).float().cpu().numpy()
+    nf = P * len(cfg.drafter.taps) * cfg.target.hidden
+    gf = eng.feats[:nf].float()
+    if cfg.target.dtype == "bf16":  # the feature planes: high part, then the low part of the same rows
+        gf = gf + eng.feats[nf:2 * nf].float()
+    gf = gf.view(P, len(cfg.drafter.taps), -1).cpu().numpy()
     fol = OracleFollower(cfg, W, request=0)
     z, feats = fol.prefill(prompt)
     e = rel_err_rows(g, z)
@@ -423,6 +427,7 @@ def test_graph_replay_equals_eager_steps(name, stochastic):
         eng = engine(cfg, W)
         eng.kv_alloc(0, P + (steps + 2) * B)
         eng.prefill([0], prompt.view(1, -1), [s])
+        eng.spec_step([0], [s], stochastic=stochastic)  # a capture needs the steady state (a block verify)
         g = eng.capture_spec_step([0], [s], stochastic=stochastic) if use_graph else None
         rec = []
         for _ in range(steps):
@@ -443,36 +448,60 @@ def test_graph_replay_equals_eager_steps(name, stochastic):
         assert torch.equal(a[3], b[3]), f"step {i}: logits differ"
 
 
-def test_graph_captured_after_prefill_tight_pages():
-    """A step captured right after a prefill launches the drafter's injection over every prompt row at
-    each replay (rows past the committed ones are padding).  With a page budget that just fits the run,
-    those padding rows' positions lie beyond the rotary table; they are neither written nor checked, so
-    the replays raise no device error, and they equal the eager steps."""
+def test_graph_capture_needs_steady_state():
+    """A captured step replays the drafter injection with the row count and feature stride of the verify
+    that preceded the capture, so a capture right after a prefill (prompt-length rows) or after a plain
+    decoding step (one row) is refused; captured after one eager step, at batch 2 and with a page budget
+    that just fits the run, the replays equal the eager steps bit for bit (tokens, acceptance counts,
+    drafts) and raise no device error (the injection's padding rows past the committed ones are neither
+    written nor checked)."""
     cfg = _variant(synth.TINY, prompt_len=96)
     W = sw.model_weights(cfg)
     P, B, V = cfg.prompt_len, cfg.drafter.block_size, cfg.target.vocab
-    steps = 4
-    prompt = torch.from_numpy(sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)).to("cuda")
+    steps = 5
+    prompts = torch.stack([torch.from_numpy(sw.prompt_ids(V, cfg.drafter.mask_id, P, r)) for r in range(2)]).to("cuda")
     s = samp(cfg.sampling)
+    slots = [0, 1]
+
+    def new_engine():
+        eng = engine(cfg, W, max_slots=2, max_rows=2 * P, max_pages_per_seq=(P + (steps + 3) * B) // 16 + 1)
+        for r in slots:
+            eng.kv_alloc(r, P + (steps + 3) * B)
+        return eng
+
+    eng = new_engine()
+    eng.prefill(slots, prompts, [s, s])
+    with pytest.raises(RuntimeError, match="block verify"):
+        eng.capture_spec_step(slots, [s, s])
+    eng.ar_step(slots, [s, s])
+    with pytest.raises(RuntimeError, match="block verify"):
+        eng.capture_spec_step(slots, [s, s])
+    eng.close()
 
     def run(use_graph):
-        eng = engine(cfg, W, max_pages_per_seq=(P + (steps + 2) * B) // 16 + 1)
-        eng.kv_alloc(0, P + (steps + 2) * B)
-        eng.prefill([0], prompt.view(1, -1), [s])
-        g = eng.capture_spec_step([0], [s]) if use_graph else None
+        eng = new_engine()
+        eng.prefill(slots, prompts, [s, s])
+        eng.spec_step(slots, [s, s])
+        g = eng.capture_spec_step(slots, [s, s]) if use_graph else None
         out = []
         for _ in range(steps):
             if g is not None:
                 g.replay()
             else:
-                eng.spec_step([0], [s])
-            n = int(eng.n_out[0])
-            out.append(eng.out[:n].cpu().clone())
+                eng.spec_step(slots, [s, s])
+            n = eng.n_out[:2].cpu().clone()
+            out.append((n, eng.out[:2 * B].view(2, B).cpu().clone(), eng.block[:2 * B].cpu().clone()))
         eng.status()  # raises on any device-side flag
+        eng.close()
         return out
 
     eager, graph = run(False), run(True)
-    assert all(torch.equal(a, b) for a, b in zip(eager, graph))
+    for i, (a, b) in enumerate(zip(eager, graph)):
+        assert torch.equal(a[0], b[0]), f"step {i}: n_out {a[0]} vs {b[0]}"
+        for r in slots:
+            n = int(a[0][r])
+            assert torch.equal(a[1][r, :n], b[1][r, :n]), f"step {i} slot {r}: tokens differ"
+        assert torch.equal(a[2], b[2]), f"step {i}: drafts differ"
 
 
 def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
@@ -633,10 +662,9 @@ def test_27b_width_vs_fp32_forward(layers):
     """The device at the full 27B width (hidden 5120, 40 q / 8 kv heads x 128, FFN 17408, vocab 151936)
     against an independent fp32 forward of the same tokens, as the depth grows: a 128-token prefill
     (tiled projections, every row's logits) and 8 plain-decoding steps (row-chunked projections, split
-    decode attention).  The device rounds every projection input to bf16; at 2 and 8 layers its logits
-    are within the bf16 tolerance (2e-2); deeper, the roundings of 64 random-weight layers compound
-    (measured ~4.5e-2 at 64 layers, logged here), which is why the full-depth property test bounds rows
-    at 3x the tolerance."""
+    decode attention).  Every depth is held to the bf16 tolerance (2e-2): the device keeps projection
+    inputs as high + low bf16 planes and the attention operands in fp16, so the independent roundings
+    that accumulate over 64 random-weight layers stay far below it."""
     from synth import gpu as sg
     from synth.configs import with_layers
     from speculative_decoding_dflash_amd.runner import Engine
@@ -667,7 +695,7 @@ def test_27b_width_vs_fp32_forward(layers):
     e_pre = rel_err_rows(g_pre, ref[:P])
     e_ar = rel_err_rows(np.stack(rows), ref[P:P + n])
     log(f"  prefill rows max {e_pre.max():.2e} mean {e_pre.mean():.2e}; decode rows max {e_ar.max():.2e}")
-    bound = 2e-2 if layers <= 8 else 3 * 2e-2
+    bound = 2e-2
     assert e_pre.max() <= bound and e_ar.max() <= bound
     del eng, Wt
     torch.cuda.empty_cache()
@@ -679,9 +707,9 @@ def test_27b_greedy_spec_equals_greedy_ar(conc, whole_block, monkeypatch):
     batched verify / draft at concurrency 8 and 32): greedy speculative decoding emits the device's own
     greedy plain-decoding stream for every request; a stream may diverge only at a near tie of the
     plain-decoding logits; for the first 8 requests both paths' logit rows are held against an fp32
-    forward of the same tokens, and the verify rows against the plain-decoding rows, within 3x the bf16
-    tolerance (the bf16 roundings of 64 layers compound, see test_27b_width_vs_fp32_forward; the
-    batched rows use other row tiles and key splits, so their roundings differ).  whole_block: the batched attention
+    forward of the same tokens, and the verify rows against the plain-decoding rows, within the bf16
+    tolerance (the batched rows use other row tiles and key splits, so their roundings differ from
+    plain decoding's).  whole_block: the batched attention
     work-groups hold the whole block (three 16-wide query tiles at the 27B head ratio), as batched calls
     over long key ranges do."""
     if whole_block:
@@ -749,10 +777,6 @@ def test_27b_greedy_spec_equals_greedy_ar(conc, whole_block, monkeypatch):
             msg += f"; vs fp32 forward: plain decoding {e_ar:.2e}, speculative {e_sp:.2e}"
         log(msg)
     log(f"  worst: spec vs plain {worst_pair:.2e}, plain vs fp32 {worst_ar:.2e}, spec vs fp32 {worst_spec:.2e}")
-    # bf16 roundings of 64 random-weight layers compound to ~4.5e-2 against the fp32 forward on either
-    # path (see test_27b_width_vs_fp32_forward: within 2e-2 at 2 and 8 layers); the bound is 3x the
-    # bf16 tolerance for each path against the fp32 forward and for the two device paths against each
-    # other
-    assert worst_ar <= 3 * tol and worst_spec <= 3 * tol and worst_pair <= 3 * tol
+    assert worst_ar <= tol and worst_spec <= tol and worst_pair <= tol
     del eng, Wt
     torch.cuda.empty_cache()
