@@ -148,7 +148,7 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
       break;
     }
     case EPI_RESID_NORM:
-      if constexpr (COLS == 32) {
+      if constexpr (COLS % 32 == 0) {
         for (int e = tid; e < M * COLS; e += NT) {
           const int m = e / COLS, j = e % COLS;
           const int r = a.row_off + m, n = COLS * c + j;
@@ -165,12 +165,15 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
           lds[m * COLS + j] = v * v;  // entry owned by this thread
         }
         __syncthreads();
-        if (tid < M) {
-          const int r = a.row_off + tid, jj = r % a.sel_stride - a.sel_offset;
+        // one sum of squares per row and 32-column group (the tile's groups are COLS / 32 .. + COLS / 32 - 1)
+        constexpr int NG = COLS / 32;
+        if (tid < M * NG) {
+          const int m = tid / NG, h = tid % NG;
+          const int r = a.row_off + m, jj = r % a.sel_stride - a.sel_offset;
           if (jj >= 0 && jj < a.sel_take) {
             float t = 0.f;
-            for (int j = 0; j < COLS; ++j) t += lds[tid * COLS + j];
-            a.ss_out[(size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ss_out_ld + c] = t;
+            for (int j = 0; j < 32; ++j) t += lds[m * COLS + 32 * h + j];
+            a.ss_out[(size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ss_out_ld + NG * c + h] = t;
           }
         }
       }
@@ -351,8 +354,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   gemm_epilogue<T, COLS, NT>(a, c, split, lds, s_rstd);
 }
 
-// Stream-K variant (at most 16 X operand rows, low planes included; ksplit 1, K a whole number of
-// super-steps; 32-column tiles, 8 waves).
+// Stream-K variant (ksplit 1, K a whole number of super-steps, 8 waves).  Two forms:
+//   * FOLD (bf16 projections with a low X plane, at most 8 rows): the 16 staged X rows are the 8 high
+//     rows then the 8 low rows, so each MFMA tile carries a row's high part in one half and its low part
+//     in the other, and a lane exchange adds the halves (row m + 8 sits 32 lanes after row m); a work
+//     item covers 64 output columns, its weights staged 32 rows at a time through the wave's LDS tile,
+//     which keeps the X bytes per weight byte at a quarter;
+//   * otherwise at most 16 X rows and 32 output columns per item.
 // With one tile per work-group, projections whose tile count is not a multiple of the CU count leave
 // CUs idle while others stream (160 hidden-width tiles on 256 CUs).  Here the projection's items
 // (tile, super-step), numbered tile-major, are cut into equal contiguous ranges, one per work-group
@@ -364,18 +372,23 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 // another XCD) and count their arrival on the tile's counter; the finisher adds the partials in
 // work-group order -- a fixed order, so the result does not depend on who arrives last -- runs the
 // epilogue and zeroes the counter for the next launch.  No work-group ever waits for another.
-template <typename T, int XR>
+template <typename T, int XR, bool FOLD, int COLS>
 __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   using F = Frag<T>;
-  constexpr int NW = 8, NT = NW * 64, CT = 2, COLS = 32;
+  constexpr int NW = 8, NT = NW * 64;
+  constexpr int CT = COLS / 16, ROWS = FOLD ? 8 : 16;
+  static_assert(COLS == 32 || (FOLD && COLS == 64), "item widths");
   static_assert(XR == 8 || XR == 16, "X staging rows");
+  static_assert(!FOLD || XR == 16, "a folded item stages 8 high and 8 low rows");
   constexpr int ROWB = 256 + 16;
   constexpr int NQ = COLS / 4, NXQ = XR / 4;
+  constexpr int NH = NQ / 8;  // halves of 8 weight quads (32 rows) staged one after the other
   constexpr int SK = 256 / sizeof(T);
   constexpr int KS = SK / F::kStep;
-  constexpr int kEnt = 16 * COLS;  // == kSkTileElems
+  constexpr int kEnt = ROWS * COLS;  // entries of one partial tile
+  static_assert(kEnt <= kSkTileElems, "partial tile size");
   constexpr int kPer = (kEnt + NT - 1) / NT;
-  constexpr int kTileB = NW * (COLS + XR) * ROWB, kRedB = 2 * NW * kEnt * 4;
+  constexpr int kTileB = NW * (32 + XR) * ROWB, kRedB = 2 * NW * kEnt * 4;
   // staging tiles (wave-private), then two reduction buffers (alternating tiles), then the tile sums
   __shared__ __attribute__((aligned(16))) unsigned char smem[kTileB + kRedB + kEnt * 4];
   __shared__ float s_ssp[kSS4 * NT], s_rstd[16];
@@ -385,17 +398,19 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const bool swiglu = a.epi == EPI_SWIGLU;
-  const int ntile = swiglu ? a.N / 16 : a.N / COLS;
+  const int ntile = swiglu ? a.N / (COLS / 2) : a.N / COLS;
   const int nsup = a.K / SK, items = ntile * nsup;
   const int p = blockIdx.x;
   const int lo = p * per, hi = min(items, lo + per);
 
-  // weight rows of tile t: SWIGLU takes 16 gate rows and 16 up rows; otherwise 32 consecutive rows of
-  // the concatenated segments (each segment a whole number of tiles)
+  // weight rows of tile t, as CT groups of 16 rows (accumulator ct = group ct): SWIGLU takes COLS / 2
+  // gate rows (groups 0 .. CT/2-1) and the same up rows (groups CT/2 ..); otherwise COLS consecutive
+  // rows of the concatenated segments (each segment a whole number of tiles)
+  // (w0: groups 0 .. CT/2-1, w1: groups CT/2 .., each a run of COLS / 2 rows)
   auto tile_base = [&](int t, const T *&w0, const T *&w1) {
     if (swiglu) {
-      w0 = (const T *)a.seg[0].w + (size_t)(16 * t) * a.K;
-      w1 = (const T *)a.seg[1].w + (size_t)(16 * t) * a.K;
+      w0 = (const T *)a.seg[0].w + (size_t)((COLS / 2) * t) * a.K;
+      w1 = (const T *)a.seg[1].w + (size_t)((COLS / 2) * t) * a.K;
       return;
     }
     int r0 = COLS * t, si = 0;
@@ -404,24 +419,31 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
       ++si;
     }
     w0 = (const T *)a.seg[si].w + (size_t)r0 * a.K;
-    w1 = w0 + (size_t)16 * a.K;
+    w1 = w0 + (size_t)(COLS / 2) * a.K;
   };
-  // quad layout as in gemm_kernel: load q covers rows 4 (q % 4) .. + 3 of the tile's 16-row half q / 4
+  const size_t gstep = (size_t)16 * a.K;  // elements between consecutive 16-row groups of a run
+  // quad layout as in gemm_kernel: quad q covers rows 4 (q % 4) .. + 3 of group q / 4
   size_t qoff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) qoff[q] = (size_t)(4 * q + g) * a.K + r16 * F::kEPL;
-  const int Mv = a.x_lo ? 2 * a.M : a.M;  // X operand rows (low plane rows after the M rows)
+  // X staging rows: FOLD stages high rows 0..7 then low rows 0..7 (rows >= M read row 0: their
+  // products land in output rows that are never stored); otherwise rows 0 .. XR-1 of x
   const T *xrow[NXQ];
 #pragma unroll
   for (int q = 0; q < NXQ; ++q) {
     const int m = 4 * q + g;
-    xrow[q] = x_row<T>(a, m < Mv ? m : 0) + r16 * F::kEPL;
+    if (FOLD) {
+      const int mr = m & 7;
+      xrow[q] = (const T *)(m < 8 ? a.x : a.x_lo) + (size_t)(mr < a.M ? mr : 0) * a.ldx + r16 * F::kEPL;
+    } else {
+      xrow[q] = (const T *)a.x + (size_t)(m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
+    }
   }
   SsPrefetch<NT> ssp;
   ssp.load(a);
 
-  unsigned char *wt = smem + wave * (COLS + XR) * ROWB;
-  unsigned char *xt = wt + COLS * ROWB;
+  unsigned char *wt = smem + wave * (32 + XR) * ROWB;
+  unsigned char *xt = wt + 32 * ROWB;
   const T *dummy = (const T *)a.x + r16 * F::kEPL;
   // load cursor: item li = (tile lt, super-step ls); the use cursor ui trails it by one item
   int li = lo + wave;
@@ -430,12 +452,21 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   const T *w0, *w1;
   tile_base(lt < ntile ? lt : 0, w0, w1);
   u32x4 buf[NQ], bufx[NXQ];
-  auto issue = [&]() {
+  // loads of the item at the cursor: weight quads of half h (and, with half 0, the X rows)
+  auto issue_half = [&](int h) {
     const bool ok = li < hi;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) buf[q] = ld16(ok ? (q < 4 ? w0 : w1) + qoff[q % 4] + (size_t)ls * SK : dummy);
+    for (int q = 8 * h; q < 8 * h + 8; ++q) {
+      const int gi = q / 4;  // the quad's 16-row group
+      const T *wq = (gi < CT / 2 ? w0 + (size_t)gi * gstep : w1 + (size_t)(gi - CT / 2) * gstep);
+      buf[q] = ld16(ok ? wq + qoff[q % 4] + (size_t)ls * SK : dummy);
+    }
+    if (h == 0) {
 #pragma unroll
-    for (int q = 0; q < NXQ; ++q) bufx[q] = ld16(ok ? xrow[q] + (size_t)ls * SK : dummy);
+      for (int q = 0; q < NXQ; ++q) bufx[q] = ld16(ok ? xrow[q] + (size_t)ls * SK : dummy);
+    }
+  };
+  auto advance = [&]() {
     li += NW;
     ls += NW;
     if (ls >= nsup) {
@@ -446,7 +477,9 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
       if (lt < ntile) tile_base(lt, w0, w1);
     }
   };
-  issue();
+#pragma unroll
+  for (int h = 0; h < NH; ++h) issue_half(h);
+  advance();
   ssp.store(a, s_ssp);  // read after the first tile's reduction barrier
 
   int seg = 0;
@@ -457,45 +490,49 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
     for (int ct = 0; ct < CT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (; ui < seg_hi; ui += NW) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = buf[q];
+      for (int h = 0; h < NH; ++h) {
+        // stage half h (and X with half 0), then load the next item's half h while it is multiplied
 #pragma unroll
-      for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[q];
-      issue();
+        for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = buf[8 * h + q];
+        if (h == 0) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 xv = r16 < Mv
-                             ? *reinterpret_cast<const u32x4 *>(xt + (r16 < XR ? r16 : 0) * ROWB + ks * 64 + 16 * g)
-                             : (u32x4){0u, 0u, 0u, 0u};
+          for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[q];
+        }
+        issue_half(h);
+        if (h == NH - 1) advance();
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * ct + r16) * ROWB + ks * 64 + 16 * g);
-          F::mma(acc[ct], xv, wv);
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 xv = (FOLD || r16 < a.M)
+                               ? *reinterpret_cast<const u32x4 *>(xt + (r16 < XR ? r16 : 0) * ROWB + ks * 64 + 16 * g)
+                               : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * c2 + r16) * ROWB + ks * 64 + 16 * g);
+            F::mma(acc[2 * h + c2], xv, wv);
+          }
         }
       }
     }
-    // C[m][n] of a wave's partial tile sits at lane (n % 16, 4 * (lane / 16) + r) of acc[n / 16]
+    // C[m][n] of a wave's partial tile sits at lane (n % 16, 4 * (lane / 16) + r) of acc[n / 16]; FOLD
+    // adds row m + 8 (the low part) into row m
     float *rb = red + (seg & 1) * NW * kEnt;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = acc[ct][r];
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[ct][r];
+        if (FOLD) v += __shfl_xor(v, 32);
+        if (!FOLD || g < 2) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = v;
+      }
     __syncthreads();
     if (seg == 0 && a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
-    // output row m < M: the waves' sums of operand row m plus those of its low part (row M + m)
-    const int lo_off = a.x_lo ? a.M * COLS : 0;
     float v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = tid + i * NT;
       v[i] = 0.f;
-      if (e < a.M * COLS) {
+      if (e < a.M * COLS)
         for (int w = 0; w < NW; ++w) v[i] += rb[w * kEnt + e];
-        if (lo_off) {
-          float u = 0.f;
-          for (int w = 0; w < NW; ++w) u += rb[w * kEnt + e + lo_off];
-          v[i] += u;
-        }
-      }
     }
     if (t * nsup < lo || (t + 1) * nsup > hi) {  // shared tile
       const int q0 = (t * nsup) / per, q1 = ((t + 1) * nsup - 1) / per;
@@ -951,15 +988,16 @@ struct TileCfg {
 
 // Tile width and waves per work-group, from MI355X sweeps at M = 8 (one launch per shape, weights
 // rotated through more memory than the memory-side cache holds): 32-row tiles with 8 waves stream best
-// for hidden-width outputs (o / down / fc projections) and SwiGLU pairs; 16-row tiles with 4 waves for
-// mid-sized outputs with short K (q/k/v, injected k/v); 32-row tiles with 4 waves for the LM head.
+// for hidden-width outputs (o / down / fc projections) and SwiGLU pairs; 32-row tiles with 4 waves for
+// mid-sized outputs with short K (q/k/v, injected k/v: 16-row tiles streamed as fast when X had one
+// plane, and lost ~1.5% per step once the 16 staged X rows of a low plane matched their weight rows)
+// and for the LM head.
 static TileCfg pick_tiles(int epi, int N, int K) {
   static const int env_ct = env_int("DFLASH_GEMM_CT", 0), env_nw = env_int("DFLASH_GEMM_NW", 0),
                    env_pd = env_int("DFLASH_GEMM_PD", 0), env_pct = env_int("DFLASH_GEMM_PART_CT", 0),
                    env_pnw = env_int("DFLASH_GEMM_PART_NW", 0);
   TileCfg t{2, 8, 1};
   if (epi != EPI_SWIGLU && N >= 6144 && N <= 12288 && K <= 8192) {
-    t.ct = 1;
     t.nw = 4;
   } else if (epi != EPI_SWIGLU && N >= 65536) {
     t.nw = 4;
@@ -997,6 +1035,14 @@ int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems) {
   return split;
 }
 
+// The folded stream-K form: a low X plane and at most 8 rows.
+static bool sk_fold(const GemmArgs &a) { return a.x_lo && a.M <= 8; }
+// Output columns of a folded stream-K item (DFLASH_GEMM_SK_COLS=32 or 64, read per launch).  64-column
+// items halve the X bytes per weight byte but measured slower on MI355X at the 27B decode shapes (each
+// wave then holds only one or two items of a 52 MB projection, 11.77 against 11.45 ms per step), so 32
+// is the default.
+static int sk_fold_cols() { return env_int("DFLASH_GEMM_SK_COLS", 32) == 64 ? 64 : 32; }
+
 // Stream-K launch: only with the caller's scratch, for shapes the kernel covers, and by default for the
 // hidden-width (residual + norm) and SwiGLU projections, where it measured faster on MI355X at M = 8
 // (o 15.0 -> 13.8 us, down 37.6 -> 33.7 us, gate/up 72 -> 64 us); q/k/v (448 16-column tiles) and the
@@ -1008,12 +1054,13 @@ static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
   const int sk = dtype == 0 ? 128 : 64;  // K elements per super-step
   if (a.K < sk || a.K % sk) return 0;
   const bool swiglu = a.epi == EPI_SWIGLU;
-  if (swiglu ? a.N % 16 : a.N % 32) return 0;
+  const int cols = sk_fold(a) ? sk_fold_cols() : 32;  // output columns per tile (SWIGLU: half gate, half up)
+  if (swiglu ? a.N % (cols / 2) : a.N % cols) return 0;
   if (!swiglu)
     for (int i = 0; i < a.nseg; ++i)
-      if (a.seg[i].n % 32) return 0;
+      if (a.seg[i].n % cols) return 0;
   if (env != 1 && a.epi != EPI_RESID_NORM && !swiglu) return 0;
-  const long ntile = swiglu ? a.N / 16 : a.N / 32;
+  const long ntile = swiglu ? a.N / (cols / 2) : a.N / cols;
   if (ntile > a.sk_max_tiles) return 0;
   static int cus[64] = {0};
   int dev = 0;
@@ -1046,11 +1093,19 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
     const dim3 grid(n_wg), block(512);
     const bool x8 = x_rows(a) <= 8;
     if (dtype == 0) {
-      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8>), grid, block, 0, s, e0, e1, 0, a, per);
-      else hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16>), grid, block, 0, s, e0, e1, 0, a, per);
+      if (sk_fold(a)) {
+        if (sk_fold_cols() == 64)
+          hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16, true, 64>), grid, block, 0, s, e0, e1, 0, a, per);
+        else
+          hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16, true, 32>), grid, block, 0, s, e0, e1, 0, a, per);
+      } else if (x8) {
+        hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
+      } else {
+        hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
+      }
     } else {
-      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8>), grid, block, 0, s, e0, e1, 0, a, per);
-      else hipExtLaunchKernelGGL((gemm_sk_kernel<float, 16>), grid, block, 0, s, e0, e1, 0, a, per);
+      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
+      else hipExtLaunchKernelGGL((gemm_sk_kernel<float, 16, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
     }
     return hipGetLastError();
   }
