@@ -157,6 +157,8 @@ struct dflash_ctx {
   std::vector<int> prefilled;
   // the last verify call, for draft / accept consistency
   int last_qlen = 0, last_nlogit = 0, last_batch = 0;
+  // drafts of the accept that followed the last verify (-1: no accept since that verify)
+  int last_nd = -1;
   std::vector<int32_t> last_slots;
   bool verified = false;
   // Set while a prefill (a verify that starts sequences) runs: its projections may take the tiled
@@ -238,8 +240,9 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_
       HIP_OK(launch_gemm(b, dt, s, e0, e1));
       return DFLASH_OK;
     }
-    // decode batches: all rows in one launch instead of row chunks that each stream the weights
-    if (!tiled && gemm_mb_ok(b, dt)) {
+    // decode batches (and prefills too short for the tiled kernel): all rows in one launch instead of
+    // row chunks that each stream the weights
+    if (gemm_mb_ok(b, dt)) {
       HIP_OK(launch_gemm_mb(b, s, e0, e1));
       return DFLASH_OK;
     }
@@ -250,8 +253,10 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_
   for (int r0 = 0; r0 < R; r0 += cr) {
     GemmArgs b = a;
     b.M = std::min(cr, R - r0);
-    b.x = x0 + (size_t)r0 * a.ldx * es;
-    b.x_lo = xl0 ? xl0 + (size_t)r0 * a.ldx * es : nullptr;
+    if (!a.x_take) {  // a row selection addresses X by global row (row_off) from the unmoved x
+      b.x = x0 + (size_t)r0 * a.ldx * es;
+      b.x_lo = xl0 ? xl0 + (size_t)r0 * a.ldx * es : nullptr;
+    }
     b.row_off = r0;
     HIP_OK(launch_gemm(b, dt, s, r0 == 0 ? e0 : nullptr, r0 + cr >= R ? e1 : nullptr));
   }
@@ -804,6 +809,7 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
     if (new_sequence) c->prefilled[slots[b]] = 1;
   c->last_qlen = q_len;
   c->last_nlogit = nl;
+  c->last_nd = -1;
   c->last_batch = batch;
   c->last_slots.assign(slots, slots + batch);
   c->verified = true;
@@ -852,6 +858,7 @@ dflash_status accept_impl(dflash_ctx *c, hipStream_t s, int32_t batch, const int
   HIP_OK(launch_decide(d, s));
   if (d_cand_ids || d_cand_p) HIP_OK(launch_copy_cands(f.cand_id, f.cand_p, f.cand_n, rows, d_cand_ids, d_cand_p, s));
   c->verified = false;
+  c->last_nd = n_draft;
   return DFLASH_OK;
 }
 }  // namespace
@@ -897,14 +904,20 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
     if ((int)c->pages[slots[b]].size() * c->cap.page_tokens < B)
       return fail(DFLASH_E_NOMEM, "slot %d holds fewer KV pages than the block", slots[b]);
 
-  // 1. KV injection of the rows committed by the last accept.
-  const int Q = c->last_qlen, Ri = batch * Q;
+  // 1. KV injection of the rows committed by the last accept.  With a sliding window only the last rows
+  // of a long verified block (a prefill) can ever be seen by a draft: the accept committed at least
+  // Q - nd of its Q rows, the next draft starts right after the committed ones, and a query at p sees
+  // context keys k > p - W; so rows before Q - nd - W are skipped (never computed, never stored).
+  const int Q = c->last_qlen;
+  const int skip = (dc.window > 0 && c->last_nd >= 0) ? std::max(0, Q - c->last_nd - dc.window) : 0;
+  const int L = Q - skip, Ri = batch * L;
   Rows ri = c->rows(1);
   PrepArgs p;
   memset(&p, 0, sizeof p);
   p.batch = batch;
   for (int b = 0; b < batch; ++b) p.slots[b] = slots[b];
-  p.q_len = Q;
+  p.q_len = L;
+  p.row_skip = skip;
   p.state = c->state();
   p.rows = ri;
   p.mode = 1;
@@ -913,9 +926,21 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
   int ss_n = 1;
+  // long injections (after a prefill) take the tiled large-M kernel; a decode step's (batch x B rows)
+  // keep the row-count-independent kernels
+  struct TiledScope {
+    dflash_ctx *c;
+    ~TiledScope() { c->tiled = false; }
+  } tiled_scope{c};
+  c->tiled = Ri > c->cap.max_slots * B;
   {
     GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_RESID_NORM);
-    a.x_lo = c->feats_lo(d_feats, Ri);
+    a.x_lo = c->feats_lo(d_feats, batch * Q);
+    if (skip) {  // the last L of every Q feature rows
+      a.x_take = L;
+      a.x_stride = Q;
+      a.x_off = skip;
+    }
     a.nseg = 1;
     a.seg[0] = GemmSeg{c->fc, H};
     if ((st = run_resid_norm(c, a, Ri, nullptr, nullptr, nullptr, 0, all_rows(c->hidden_norm, Ri), s, &ss_n)) !=
@@ -946,10 +971,12 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
     p.part_stride = part_stride;
     HIP_OK(launch_qkv_post(p, c->dt(), s));
   }
+  c->tiled = false;
   // 2. The block [anchor, MASK x (B-1)].
   Rows rd = c->rows(2);
   p.rows = rd;
   p.q_len = B;
+  p.row_skip = 0;
   p.mode = 2;
   p.block_out = d_block;
   HIP_OK(launch_prep(p, s));

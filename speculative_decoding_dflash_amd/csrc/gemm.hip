@@ -55,10 +55,18 @@ template <> struct Frag<float> {
 
 template <typename T> DF_DEVICE u32x4 ld16(const T *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// The X row that local row m (< M) reads: m itself, or with a row selection the selected row of global
+// row row_off + m.
+DF_DEVICE int x_src(const GemmArgs &a, int m) {
+  if (!a.x_take) return m;
+  const int r = a.row_off + m;
+  return (r / a.x_take) * a.x_stride + a.x_off + r % a.x_take;
+}
+
 // Row v of the X operand as the kernels see it: rows 0 .. M-1 of x, then (with a low plane) rows
 // 0 .. M-1 of x_lo.
 template <typename T> DF_DEVICE const T *x_row(const GemmArgs &a, int v) {
-  return v < a.M ? (const T *)a.x + (size_t)v * a.ldx : (const T *)a.x_lo + (size_t)(v - a.M) * a.ldx;
+  return v < a.M ? (const T *)a.x + (size_t)x_src(a, v) * a.ldx : (const T *)a.x_lo + (size_t)x_src(a, v - a.M) * a.ldx;
 }
 
 DF_DEVICE float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -434,9 +442,9 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
     const int m = 4 * q + g;
     if (FOLD) {
       const int mr = m & 7;
-      xrow[q] = (const T *)(m < 8 ? a.x : a.x_lo) + (size_t)(mr < a.M ? mr : 0) * a.ldx + r16 * F::kEPL;
+      xrow[q] = (const T *)(m < 8 ? a.x : a.x_lo) + (size_t)x_src(a, mr < a.M ? mr : 0) * a.ldx + r16 * F::kEPL;
     } else {
-      xrow[q] = (const T *)a.x + (size_t)(m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
+      xrow[q] = (const T *)a.x + (size_t)x_src(a, m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
     }
   }
   SsPrefetch<NT> ssp;
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw,
       plane = fi >= MI / 2;
       lr = w2 * (RT / 2) + 16 * (fi % (MI / 2)) + row % 16;
     }
-    pa[i] = (const bf16 *)(plane ? a.x_lo : a.x) + (size_t)min(m0 + lr, a.M - 1) * a.ldx + kc;
+    pa[i] = (const bf16 *)(plane ? a.x_lo : a.x) + (size_t)x_src(a, min(m0 + lr, a.M - 1)) * a.ldx + kc;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -31,6 +31,10 @@ struct GemmArgs {
   int32_t ksplit;       // K ranges, one per grid row (> 1 only with EPI_PARTIAL)
   int64_t part_stride;  // EPI_PARTIAL: elements between the K ranges' output slices
   int32_t row_off;      // global row of local row 0
+  // Optional selection of the X rows (x_take > 0): global row r reads X row (r / x_take) * x_stride +
+  // x_off + r % x_take of the unmoved x (and x_lo) -- e.g. the last x_take of every x_stride rows.
+  // Without it local row r reads X row r of x (row chunks move x).
+  int32_t x_take, x_stride, x_off;
   // Optional RMSNorm of the X rows, applied to Y (EPI_STORE_F32, EPI_PARTIAL, EPI_SWIGLU): X holds
   // act(x * gain) and Y[m] is scaled by rstd[m] = 1 / sqrt(sum_p ss_in[(row_off + m) * ss_ld + p] /
   // norm_dim + eps), the ss_n partial sums of squares added in order (ss_ld a multiple of 4).
@@ -128,6 +132,7 @@ struct PrepArgs {
   Rows rows;
   const int32_t *tokens;  // verify: caller tokens [batch*q_len]
   int32_t mode;           // 0 verify, 1 draft-inject rows, 2 draft block rows
+  int32_t row_skip;       // mode 1: the call's rows of a sequence are the verified rows row_skip .. + q_len - 1
   int32_t mask_id;
   int32_t vocab;
   int32_t *block_out;     // mode 2: block[b * q_len] = anchor

@@ -6,8 +6,9 @@ namespace df {
 // One work-group.  Reads the slots' device state, fills the per-row arrays, then updates the state.
 //   mode 0 (verify):  rows b*q_len + i at start + i (start = 0 for a new sequence, else seq_len);
 //                     records the block as pending for the next accept.
-//   mode 1 (inject):  rows b*q_len + i at inj_base + i, valid for i < inj_rows (the committed rows of
-//                     the last verified block, whose features are to be injected); clears inj_rows.
+//   mode 1 (inject):  rows b*q_len + i at inj_base + row_skip + i, valid for row_skip + i < inj_rows (the
+//                     committed rows of the last verified block, whose features are to be injected;
+//                     row_skip leading rows are left out); clears inj_rows.
 //   mode 2 (draft):   rows b*q_len + i at seq_len + i; token = anchor for i = 0, mask id otherwise.
 __global__ void prep_kernel(PrepArgs a) {
   __shared__ int s_start[64], s_lim[64], s_anchor[64];
@@ -17,9 +18,9 @@ __global__ void prep_kernel(PrepArgs a) {
     if (a.mode == 0) {
       s_start[tid] = a.new_sequence ? 0 : st.seq_len;
       s_lim[tid] = a.q_len;
-    } else if (a.mode == 1) {
-      s_start[tid] = st.inj_base;
-      s_lim[tid] = st.inj_rows;
+    } else if (a.mode == 1) {  // the verified rows row_skip .. row_skip + q_len - 1
+      s_start[tid] = st.inj_base + a.row_skip;
+      s_lim[tid] = st.inj_rows - a.row_skip;
     } else {
       s_start[tid] = st.seq_len;
       s_lim[tid] = a.q_len;

@@ -11,6 +11,7 @@ import numpy as np
 
 from oracle.model import Drafter, Target
 from oracle.sampling import decide, decide_q, sample_dist, sample_draft
+import synth
 from synth import weights as sw
 
 
@@ -169,3 +170,136 @@ def check_step(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_lo
                 rep.draft_flagged += 1
     rep.taus.append(len(g_out))
     return feats
+
+
+# ---------------------------------------------------------------- device runs compared with the oracle
+
+def engine(cfg, W, **kw):
+    from speculative_decoding_dflash_amd.runner import Engine
+    return Engine(cfg, torch_weights(W, cfg), **kw)
+
+
+def samp(sp):
+    from speculative_decoding_dflash_amd.runner import sampling
+    return sampling(sp.temperature, sp.top_k, sp.top_p, sp.seed)
+
+
+def small_short(prompt_len=128, layers=8):
+    from dataclasses import replace
+    c = synth.SMALL
+    return replace(c, prompt_len=prompt_len, target=replace(c.target, layers=layers))
+
+
+def _variant(base, dtype=None, layers=None, prompt_len=None):
+    from dataclasses import replace
+    t = base.target
+    t = replace(t, dtype=dtype or t.dtype, layers=layers or t.layers)
+    return replace(base, target=t, prompt_len=prompt_len or base.prompt_len)
+
+
+def run_e2e(cfg, W, sp, n_tokens, log_every=4, stochastic=False, eng=None):
+    """Prefill and speculative steps of one request on the device, every step compared with the
+    oracle teacher-forced on the device's tokens; returns (stream, StepReport, prompt)."""
+    import torch
+    tol = tol_of(cfg)
+    B = cfg.drafter.block_size
+    P = cfg.prompt_len
+    V = cfg.target.vocab
+    eng = eng or engine(cfg, W)
+    eng.kv_alloc(0, P + n_tokens + 2 * B)
+    prompt = sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)
+    fol = OracleFollower(cfg, W, request=0)
+    s = samp(sp)
+    # prefill
+    eng.verify([0], torch.from_numpy(prompt).to("cuda"), P, True, 1)
+    eng.accept([0], 0, [s], cands=True)
+    z, feats = fol.prefill(prompt)
+    g_ids = eng.cand_ids[:256].cpu().numpy()
+    g_p = eng.cand_p[:256].cpu().numpy()
+    k = int((g_ids >= 0).sum())
+    first = decide([(g_ids[:k].astype(np.int64), g_p[:k])], [], P - 1, sp.seed, 0)
+    out0 = int(eng.out[0].item())
+    assert first == [out0]
+    fol.commit(feats, 0, P, out0)
+    stream = [out0]
+    rep = StepReport()
+    step = 0
+    while len(stream) < n_tokens:
+        eng.spec_step([0], [s], cands=True, draft_logits=True, stochastic=stochastic)
+        block = eng.block[:B].cpu().numpy()
+        g_logits = eng.logits[:B * V].view(B, V).cpu().numpy()
+        g_dl = eng.draft_logits[:(B - 1) * V].view(B - 1, V).cpu().numpy()
+        ids = eng.cand_ids[:B * 256].view(B, 256).cpu().numpy()
+        pp = eng.cand_p[:B * 256].view(B, 256).cpu().numpy()
+        tau = int(eng.n_out[0].item())
+        outs = [int(x) for x in eng.out[:tau].cpu().numpy()]
+        start = fol.n
+        qrows = None
+        if stochastic:
+            qi = eng.q_ids[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
+            qp = eng.q_p[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
+            qrows = check_q_stage(rep, fol, sp, block, g_dl, qi, qp)
+        feats = check_step(rep, fol, sp, block, g_logits, g_dl, ids, pp, outs, tol, qrows=qrows)
+        fol.commit(feats, start, tau, outs[-1])
+        stream.extend(outs)
+        if step % log_every == 0:
+            log(f"  step {step} tau {tau} logits err {max(rep.logits_err[-B:]):.2e} draft err "
+                f"{max(rep.draft_err[-(B - 1):]):.2e}")
+        step += 1
+    eng.status()
+    return stream[:n_tokens], rep, prompt
+
+
+def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
+    """Several requests with ragged prompts: each is prefilled alone and drafts its first block alone
+    (the drafter injects the features of the verify call it follows), then all slots are decoded
+    together in batched verify -> accept -> draft calls, every slot compared with its own oracle."""
+    import torch
+    from speculative_decoding_dflash_amd import binding as Bd
+    tol = tol_of(cfg)
+    B, V = cfg.drafter.block_size, cfg.target.vocab
+    S = len(prompt_lens)
+    eng = engine(cfg, W, max_slots=S, max_rows=max(max(prompt_lens), S * B))
+    s = samp(sp)
+    fols = []
+    for b, P in enumerate(prompt_lens):
+        eng.kv_alloc(b, P + (n_steps + 2) * B)
+        prompt = sw.prompt_ids(V, cfg.drafter.mask_id, P, b)
+        eng.verify([b], torch.from_numpy(prompt).to("cuda"), P, True, 1)
+        eng.accept([b], 0, [s], cands=True)
+        fol = OracleFollower(cfg, W, request=b)
+        z, feats = fol.prefill(prompt)
+        g_ids = eng.cand_ids[:256].cpu().numpy()
+        g_p = eng.cand_p[:256].cpu().numpy()
+        k = int((g_ids >= 0).sum())
+        out0 = int(eng.out[0].item())
+        assert decide([(g_ids[:k].astype(np.int64), g_p[:k])], [], P - 1, sp.seed, b) == [out0]
+        fol.commit(feats, 0, P, out0)
+        fols.append(fol)
+        # this slot's first block, written at its place in the batched block / draft-logit buffers
+        Bd.dflash_draft_block(eng.ctx, [b], eng.feats, eng.block[b * B:], eng.draft_logits[b * (B - 1) * V:])
+    reps = [StepReport() for _ in range(S)]
+    slots = list(range(S))
+    for step in range(n_steps):
+        blocks = eng.block[:S * B].view(S, B).cpu().numpy()
+        dlog = eng.draft_logits[:S * (B - 1) * V].view(S, B - 1, V).cpu().numpy()
+        eng.verify(slots, eng.block, B, False, B)
+        eng.accept(slots, B - 1, [s] * S, cands=True)
+        logits = eng.logits[:S * B * V].view(S, B, V).cpu().numpy()
+        ids = eng.cand_ids[:S * B * 256].view(S, B, 256).cpu().numpy()
+        pp = eng.cand_p[:S * B * 256].view(S, B, 256).cpu().numpy()
+        taus = eng.n_out[:S].cpu().numpy()
+        outs = eng.out[:S * B].view(S, B).cpu().numpy()
+        for b in range(S):
+            tau = int(taus[b])
+            o = [int(x) for x in outs[b, :tau]]
+            start = fols[b].n
+            feats = check_step(reps[b], fols[b], sp, blocks[b], logits[b], dlog[b], ids[b], pp[b], o, tol)
+            fols[b].commit(feats, start, tau, o[-1])
+        log(f"  step {step} taus {[int(t) for t in taus]} logits err "
+            f"{max(max(r.logits_err[-B:]) for r in reps):.2e}")
+        eng.draft(slots, want_logits=True)
+    eng.status()
+    return reps
+
+

@@ -10,37 +10,14 @@ import pytest
 import torch
 
 import synth
-from harness import (OracleFollower, StepReport, check_q_stage, check_step, log, near_tie_argmax, rel_err_rows,
-                     tol_of, torch_weights)
+from harness import (OracleFollower, StepReport, _variant, engine, log, near_tie_argmax, rel_err_rows, run_e2e,
+                     run_e2e_batched, samp, small_short, tol_of, torch_weights)
 from oracle.sampling import decide, decide_q, sample_dist
 from oracle.spec import Sampling as OSampling
 from oracle.spec import SpecDecoder, ar_generate
 from synth import weights as sw
 
 pytestmark = pytest.mark.gpu
-
-
-def engine(cfg, W, **kw):
-    from speculative_decoding_dflash_amd.runner import Engine
-    return Engine(cfg, torch_weights(W, cfg), **kw)
-
-
-def samp(sp):
-    from speculative_decoding_dflash_amd.runner import sampling
-    return sampling(sp.temperature, sp.top_k, sp.top_p, sp.seed)
-
-
-def small_short(prompt_len=128, layers=8):
-    from dataclasses import replace
-    c = synth.SMALL
-    return replace(c, prompt_len=prompt_len, target=replace(c.target, layers=layers))
-
-
-def _variant(base, dtype=None, layers=None, prompt_len=None):
-    from dataclasses import replace
-    t = base.target
-    t = replace(t, dtype=dtype or t.dtype, layers=layers or t.layers)
-    return replace(base, target=t, prompt_len=prompt_len or base.prompt_len)
 
 
 CASES = {
@@ -81,56 +58,6 @@ def test_prefill_logits_and_features(name):
     log(f"  logits rel-err max {e.max():.3e} mean {e.mean():.3e}; features rel-err max {ef.max():.3e}")
     assert e.max() <= tol
     assert ef.max() <= (1e-4 if cfg.target.dtype == "fp32" else 2e-2)
-
-
-def run_e2e(cfg, W, sp, n_tokens, log_every=4, stochastic=False):
-    tol = tol_of(cfg)
-    B = cfg.drafter.block_size
-    P = cfg.prompt_len
-    V = cfg.target.vocab
-    eng = engine(cfg, W)
-    eng.kv_alloc(0, P + n_tokens + 2 * B)
-    prompt = sw.prompt_ids(V, cfg.drafter.mask_id, P, 0)
-    fol = OracleFollower(cfg, W, request=0)
-    s = samp(sp)
-    # prefill
-    eng.verify([0], torch.from_numpy(prompt).to("cuda"), P, True, 1)
-    eng.accept([0], 0, [s], cands=True)
-    z, feats = fol.prefill(prompt)
-    g_ids = eng.cand_ids[:256].cpu().numpy()
-    g_p = eng.cand_p[:256].cpu().numpy()
-    k = int((g_ids >= 0).sum())
-    first = decide([(g_ids[:k].astype(np.int64), g_p[:k])], [], P - 1, sp.seed, 0)
-    out0 = int(eng.out[0].item())
-    assert first == [out0]
-    fol.commit(feats, 0, P, out0)
-    stream = [out0]
-    rep = StepReport()
-    step = 0
-    while len(stream) < n_tokens:
-        eng.spec_step([0], [s], cands=True, draft_logits=True, stochastic=stochastic)
-        block = eng.block[:B].cpu().numpy()
-        g_logits = eng.logits[:B * V].view(B, V).cpu().numpy()
-        g_dl = eng.draft_logits[:(B - 1) * V].view(B - 1, V).cpu().numpy()
-        ids = eng.cand_ids[:B * 256].view(B, 256).cpu().numpy()
-        pp = eng.cand_p[:B * 256].view(B, 256).cpu().numpy()
-        tau = int(eng.n_out[0].item())
-        outs = [int(x) for x in eng.out[:tau].cpu().numpy()]
-        start = fol.n
-        qrows = None
-        if stochastic:
-            qi = eng.q_ids[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
-            qp = eng.q_p[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
-            qrows = check_q_stage(rep, fol, sp, block, g_dl, qi, qp)
-        feats = check_step(rep, fol, sp, block, g_logits, g_dl, ids, pp, outs, tol, qrows=qrows)
-        fol.commit(feats, start, tau, outs[-1])
-        stream.extend(outs)
-        if step % log_every == 0:
-            log(f"  step {step} tau {tau} logits err {max(rep.logits_err[-B:]):.2e} draft err "
-                f"{max(rep.draft_err[-(B - 1):]):.2e}")
-        step += 1
-    eng.status()
-    return stream[:n_tokens], rep, prompt
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
@@ -504,58 +431,6 @@ def test_graph_capture_needs_steady_state():
         assert torch.equal(a[2], b[2]), f"step {i}: drafts differ"
 
 
-def run_e2e_batched(cfg, W, sp, n_steps, prompt_lens):
-    """Several requests with ragged prompts: each is prefilled alone and drafts its first block alone
-    (the drafter injects the features of the verify call it follows), then all slots are decoded
-    together in batched verify -> accept -> draft calls, every slot compared with its own oracle."""
-    from speculative_decoding_dflash_amd import binding as Bd
-    tol = tol_of(cfg)
-    B, V = cfg.drafter.block_size, cfg.target.vocab
-    S = len(prompt_lens)
-    eng = engine(cfg, W, max_slots=S, max_rows=max(max(prompt_lens), S * B))
-    s = samp(sp)
-    fols = []
-    for b, P in enumerate(prompt_lens):
-        eng.kv_alloc(b, P + (n_steps + 2) * B)
-        prompt = sw.prompt_ids(V, cfg.drafter.mask_id, P, b)
-        eng.verify([b], torch.from_numpy(prompt).to("cuda"), P, True, 1)
-        eng.accept([b], 0, [s], cands=True)
-        fol = OracleFollower(cfg, W, request=b)
-        z, feats = fol.prefill(prompt)
-        g_ids = eng.cand_ids[:256].cpu().numpy()
-        g_p = eng.cand_p[:256].cpu().numpy()
-        k = int((g_ids >= 0).sum())
-        out0 = int(eng.out[0].item())
-        assert decide([(g_ids[:k].astype(np.int64), g_p[:k])], [], P - 1, sp.seed, b) == [out0]
-        fol.commit(feats, 0, P, out0)
-        fols.append(fol)
-        # this slot's first block, written at its place in the batched block / draft-logit buffers
-        Bd.dflash_draft_block(eng.ctx, [b], eng.feats, eng.block[b * B:], eng.draft_logits[b * (B - 1) * V:])
-    reps = [StepReport() for _ in range(S)]
-    slots = list(range(S))
-    for step in range(n_steps):
-        blocks = eng.block[:S * B].view(S, B).cpu().numpy()
-        dlog = eng.draft_logits[:S * (B - 1) * V].view(S, B - 1, V).cpu().numpy()
-        eng.verify(slots, eng.block, B, False, B)
-        eng.accept(slots, B - 1, [s] * S, cands=True)
-        logits = eng.logits[:S * B * V].view(S, B, V).cpu().numpy()
-        ids = eng.cand_ids[:S * B * 256].view(S, B, 256).cpu().numpy()
-        pp = eng.cand_p[:S * B * 256].view(S, B, 256).cpu().numpy()
-        taus = eng.n_out[:S].cpu().numpy()
-        outs = eng.out[:S * B].view(S, B).cpu().numpy()
-        for b in range(S):
-            tau = int(taus[b])
-            o = [int(x) for x in outs[b, :tau]]
-            start = fols[b].n
-            feats = check_step(reps[b], fols[b], sp, blocks[b], logits[b], dlog[b], ids[b], pp[b], o, tol)
-            fols[b].commit(feats, start, tau, o[-1])
-        log(f"  step {step} taus {[int(t) for t in taus]} logits err "
-            f"{max(max(r.logits_err[-B:]) for r in reps):.2e}")
-        eng.draft(slots, want_logits=True)
-    eng.status()
-    return reps
-
-
 _LENS24 = (40, 17, 96, 33, 64, 9, 120, 75, 50, 28, 101, 66, 12, 88, 45, 70, 31, 58, 110, 23, 77, 6, 92, 49)
 
 
@@ -657,10 +532,142 @@ def test_fp32_forward_matches_oracle():
     assert e.max() <= 1e-4
 
 
-@pytest.mark.parametrize("layers", [2, 8, 16, 64])
-def test_27b_width_vs_fp32_forward(layers):
+def _fp32_drafter_logits(cfg, Wt, feats, anchor, n):
+    """Independent fp32 forward of the drafter (torch on the GPU, bf16 weights upcast, fp32 activations):
+    the injected context of positions 0 .. n-1 from target features feats [n, taps, hidden] (c =
+    RMSNorm(fc [taps]); per layer K = RoPE(k_norm(W_k c)), V = W_v c), then the block [anchor, MASK x
+    (B-1)] at n .. n+B-1 through the drafter's layers, block keys visible to every block query, context
+    key k to query p only when p - k < window (window 0: all); final norm, shared LM head on the mask
+    rows.  Returns the [B-1, vocab] logits (float64, on the host)."""
+    t, d = cfg.target, cfg.drafter
+    dev = Wt["t.embed"].device
+    D, Hq, Hk, B, Wn = t.head_dim, t.q_heads, t.kv_heads, d.block_size, d.window
+    f = torch.as_tensor(feats, dtype=torch.float32, device=dev).reshape(n, -1)
+
+    def rms(x, g):
+        return x * torch.rsqrt((x * x).mean(-1, keepdim=True) + t.rms_eps) * g.float()
+
+    inv = t.rope_theta ** (-2.0 * torch.arange(D // 2, dtype=torch.float64, device=dev) / D)
+    ang = torch.arange(n + B, dtype=torch.float64, device=dev)[:, None] * inv[None]
+    cos, sin = torch.cos(ang).float()[:, None], torch.sin(ang).float()[:, None]
+
+    def rope(x, p0):  # [T, h, D] at positions p0 ..
+        c, s_ = cos[p0:p0 + len(x)], sin[p0:p0 + len(x)]
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return torch.cat([a * c - b * s_, b * c + a * s_], -1)
+
+    c = rms(f @ Wt["d.fc"].float().t(), Wt["d.hidden_norm"])
+    ids = torch.tensor([anchor] + [d.mask_id] * (B - 1), dtype=torch.int64, device=dev)
+    x = Wt["t.embed"][ids].float()
+    kpos = torch.arange(n + B, device=dev)
+    qpos = torch.arange(n, n + B, device=dev)
+    ctx_ok = (kpos[None] < n) & ((Wn <= 0) | (qpos[:, None] - kpos[None] < Wn))
+    allowed = ctx_ok | (kpos[None] >= n)  # [B, n + B]
+    for j in range(d.layers):
+        w = lambda k: Wt[f"d.L{j}.{k}"]
+        kc = rope(rms((c @ w("wk").float().t()).view(n, Hk, D), w("k_norm")), 0)
+        vc = (c @ w("wv").float().t()).view(n, Hk, D)
+        h = rms(x, w("attn_norm"))
+        q = rope(rms((h @ w("wq").float().t()).view(B, Hq, D), w("q_norm")), n)
+        kb = rope(rms((h @ w("wk").float().t()).view(B, Hk, D), w("k_norm")), n)
+        vb = (h @ w("wv").float().t()).view(B, Hk, D)
+        k = torch.cat([kc, kb]).repeat_interleave(Hq // Hk, 1)
+        v = torch.cat([vc, vb]).repeat_interleave(Hq // Hk, 1)
+        sc = torch.matmul(q.transpose(0, 1).contiguous(), k.permute(1, 2, 0).contiguous()) / (D ** 0.5)
+        sc = sc.masked_fill(~allowed[None], float("-inf"))
+        a = torch.matmul(torch.softmax(sc, -1), v.transpose(0, 1).contiguous()).transpose(0, 1).reshape(B, Hq * D)
+        x = x + a @ w("wo").float().t()
+        h = rms(x, w("ffn_norm"))
+        x = x + (torch.nn.functional.silu(h @ w("w_gate").float().t()) * (h @ w("w_up").float().t())) @ \
+            w("w_down").float().t()
+    h = rms(x[1:], Wt["d.final_norm"])
+    return (h @ Wt["t.lm_head"].float().t()).cpu().numpy().astype(np.float64)
+
+
+def test_fp32_drafter_matches_oracle():
+    """The fp32 torch drafter used at the 27B width reproduces the oracle's drafter (float64) on the
+    small shape with a 24-token window over a 96-token context and non-unit gains: draft logits within
+    1e-4 relative."""
+    from dataclasses import replace
+    from oracle.model import Drafter, Target
+    cfg = small_short(prompt_len=96, layers=2)
+    cfg = replace(cfg, drafter=replace(cfg.drafter, taps=(0, 1), window=24))
+    W = sw.model_weights(cfg, gain_std=0.1)
+    Wt = torch_weights(W, cfg)
+    prompt = sw.prompt_ids(cfg.target.vocab, cfg.drafter.mask_id, cfg.prompt_len, 0)
+    tg, dr = Target(cfg.target, W, taps=cfg.drafter.taps), Drafter(cfg.target, cfg.drafter, W)
+    _, feats = tg.forward(tg.new_cache(), list(prompt), 0)
+    dc = dr.new_cache()
+    dr.inject(dc, feats, 0)
+    n, anchor = cfg.prompt_len, 17
+    z = dr.draft_logits(dc, anchor, n)
+    ref = _fp32_drafter_logits(cfg, Wt, feats, anchor, n)
+    e = rel_err_rows(ref, z)
+    log(f"[fp32 drafter vs oracle] max rel-err {e.max():.2e}")
+    assert e.max() <= 1e-4
+
+
+def test_27b_width_drafter_vs_fp32_drafter():
+    """The drafter at the full 27B width -- five taps (the fc projection over K = 25600), two layers, the
+    2048-token window over a 2300-token context -- against the fp32 torch drafter fed the device's own
+    target features: the draft after the prefill (the injection skips prompt rows no draft can reach
+    and runs on the tiled kernel) and the draft after one speculative step (eight injected rows through
+    the stream-K fc), draft logits within 2e-2, drafts equal to the reference argmax except at near
+    ties."""
+    from dataclasses import replace
+    from speculative_decoding_dflash_amd import binding as Bd
+    from speculative_decoding_dflash_amd.runner import Engine
+    from synth import gpu as sg
+    from synth.configs import with_layers
+    base = synth.CONFIGS["27b"]
+    cfg = replace(with_layers(base, 5, 2, (0, 1, 2, 3, 4)), prompt_len=2300)
+    t, d = cfg.target, cfg.drafter
+    P, B, V, H = cfg.prompt_len, d.block_size, t.vocab, t.hidden
+    nt = len(d.taps)
+    log(f"[27b-width drafter vs fp32] taps {d.taps}, {d.layers} drafter layers, window {d.window}, prompt {P}")
+    Wt = sg.model_weights(cfg)
+    eng = Engine(cfg, Wt, max_slots=1, max_rows=P, max_pages_per_seq=(P + 8 * B) // 16 + 4)
+    eng.kv_alloc(0, P + 6 * B)
+    g = samp(synth.GREEDY)
+    prompt = torch.from_numpy(sw.prompt_ids(V, d.mask_id, P, 0)).to("cuda")
+
+    def feats_of(rows):  # the device's features (high + low planes) of the last verify, [rows, taps, H]
+        n_el = rows * nt * H
+        return (eng.feats[:n_el].float() + eng.feats[n_el:2 * n_el].float()).view(rows, nt, H).cpu().numpy()
+
+    eng.prefill([0], prompt.view(1, -1), [g])
+    ctx = feats_of(P)
+    anchor, n = int(eng.out[0]), P
+    worst = 0.0
+    for step in range(2):
+        Bd.dflash_draft_block(eng.ctx, [0], eng.feats, eng.block, eng.draft_logits)
+        got = eng.draft_logits[:(B - 1) * V].view(B - 1, V).cpu().numpy()
+        ref = _fp32_drafter_logits(cfg, Wt, ctx, anchor, n)
+        e = rel_err_rows(got, ref)
+        drafts = [int(x) for x in eng.block[1:B].cpu().numpy()]
+        for i in range(B - 1):
+            if drafts[i] != int(np.argmax(ref[i])):
+                assert near_tie_argmax(ref[i], 2e-2), f"step {step}: draft {i} differs without a near tie"
+        log(f"  draft {step} at n {n}: rel-err max {e.max():.2e}")
+        worst = max(worst, float(e.max()))
+        if step == 0:  # one verify + accept: its committed rows are injected by the next draft
+            eng.verify([0], eng.block, B, False, B)
+            eng.accept([0], B - 1, [g])
+            tau = int(eng.n_out[0])
+            ctx = np.concatenate([ctx, feats_of(B)[:tau]])
+            anchor, n = int(eng.out[tau - 1]), n + tau
+    eng.status()
+    assert worst <= 2e-2
+    eng.close()
+    del Wt
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("config,layers", [("27b", 2), ("27b", 8), ("27b", 16), ("27b", 64), ("4b", 2), ("4b", 36)])
+def test_width_vs_fp32_forward(config, layers):
     """The device at the full 27B width (hidden 5120, 40 q / 8 kv heads x 128, FFN 17408, vocab 151936)
-    against an independent fp32 forward of the same tokens, as the depth grows: a 128-token prefill
+    and the 4B width (hidden 2560, 32 q / 8 kv heads x 128: a GQA group of 4, FFN 9728) against an
+    independent fp32 forward of the same tokens, as the depth grows: a 128-token prefill
     (tiled projections, every row's logits) and 8 plain-decoding steps (row-chunked projections, split
     decode attention).  Every depth is held to the bf16 tolerance (2e-2): the device keeps projection
     inputs as high + low bf16 planes and the attention operands in fp16, so the independent roundings
@@ -668,14 +675,14 @@ def test_27b_width_vs_fp32_forward(layers):
     from synth import gpu as sg
     from synth.configs import with_layers
     from speculative_decoding_dflash_amd.runner import Engine
-    base = synth.CONFIGS["27b"]
+    base = synth.CONFIGS[config]
     taps = tuple(sorted({min(t, layers - 1) for t in base.drafter.taps}))
     cfg = with_layers(base, layers, 1, taps)
     from dataclasses import replace
     cfg = replace(cfg, prompt_len=128)
     t, d = cfg.target, cfg.drafter
     P, V, n = cfg.prompt_len, t.vocab, 8
-    log(f"[27b width vs fp32] {layers} layers")
+    log(f"[{config} width vs fp32] {layers} layers")
     Wt = sg.model_weights(cfg)
     eng = Engine(cfg, Wt, max_slots=1, max_rows=P, max_pages_per_seq=(P + 4 * n) // 16 + 4)
     eng.kv_alloc(0, P + 2 * n)
@@ -709,18 +716,29 @@ def test_27b_greedy_spec_equals_greedy_ar(conc, whole_block, monkeypatch):
     plain-decoding logits; for the first 8 requests both paths' logit rows are held against an fp32
     forward of the same tokens, and the verify rows against the plain-decoding rows, within the bf16
     tolerance (the batched rows use other row tiles and key splits, so their roundings differ from
-    plain decoding's).  whole_block: the batched attention
-    work-groups hold the whole block (three 16-wide query tiles at the 27B head ratio), as batched calls
-    over long key ranges do."""
+    plain decoding's).  whole_block: the batched attention work-groups hold the whole block (three
+    16-wide query tiles at the 27B head ratio), as batched calls over long key ranges do."""
     if whole_block:
         monkeypatch.setenv("DFLASH_ATTN_QTILE", "8")
+    _greedy_spec_vs_ar(synth.CONFIGS["27b"], conc, 16 if conc > 1 else 24)
+
+
+@pytest.mark.parametrize("block", [4, 8, 16])
+def test_4b_greedy_spec_equals_greedy_ar(block):
+    """The 4B shape (36 layers, hidden 2560, 32 q / 8 kv heads x 128, vocab 151936) with a 2048-token
+    prompt at blocks of 4, 8 and 16: the same properties as at the 27B shape."""
+    from dataclasses import replace
+    cfg = synth.CONFIGS["4b"]
+    cfg = replace(cfg, drafter=replace(cfg.drafter, block_size=block))
+    _greedy_spec_vs_ar(cfg, 1, 24)
+
+
+def _greedy_spec_vs_ar(cfg, conc, n):
     from speculative_decoding_dflash_amd import binding as Bd
     from synth import gpu as sg
-    cfg = synth.CONFIGS["27b"]
     t, d = cfg.target, cfg.drafter
     B, P, V = d.block_size, cfg.prompt_len, t.vocab
-    n = 16 if conc > 1 else 24
-    log(f"[27b greedy spec == AR] conc {conc}")
+    log(f"[{cfg.name} greedy spec == AR] conc {conc}, block {B}")
     Wt = sg.model_weights(cfg)
     from speculative_decoding_dflash_amd.runner import Engine
     eng = Engine(cfg, Wt, max_slots=conc, max_rows=max(P, conc * B), max_pages_per_seq=(P + (n + 4) * B) // 16 + 4)
