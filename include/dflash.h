@@ -30,10 +30,15 @@
  *     raise a sticky flag; dflash_device_status reports it as DFLASH_E_DEVICE.
  *   - Weight layout: projections are row-major [out, in] (y = x W^T) in the model dtype (bf16, or
  *     fp32 for DFLASH_F32 models); RMSNorm gains are fp32 vectors.  Nothing is copied or repacked.
- *   - KV pool layout, per layer: [page][2 (K, V)][kv_heads][page_tokens * head_dim] in the model
- *     dtype, K token-major ([token][dim]) and V dim-major ([dim][token]) inside a page.  Page ids are
- *     shared by the target pool (layers 0..L_t-1) and the drafter pool (layers 0..L_d-1): a slot's
- *     block table maps its position p to page table[p / page_tokens].
+ *   - KV pool layout, per layer: [page][2 (K, V)][kv_heads][page_tokens * head_dim], K token-major
+ *     ([token][dim]) and V dim-major ([dim][token]) inside a page, in IEEE fp16 for DFLASH_BF16 models
+ *     (the attention operands keep 11 significant bits; K is RMS-normalised, |V| saturates at 65504)
+ *     and fp32 for DFLASH_F32 models.  Page ids are shared by the target pool (layers 0..L_t-1) and the
+ *     drafter pool (layers 0..L_d-1): a slot's block table maps its position p to page
+ *     table[p / page_tokens].
+ *   - Target features (verify output, draft input) of DFLASH_BF16 models are two bf16 planes of the
+ *     same shape, hi = bf16(h) then lo = bf16(h - hi), so that hi + lo carries the fp32 residual
+ *     stream to about 16 significant bits; DFLASH_F32 models hold one fp32 plane.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -165,8 +170,9 @@ dflash_status dflash_kv_free(dflash_ctx *ctx, int32_t slot);
  * to keys 0 .. p.  The block's K/V are written into the target cache (positions past the committed
  * length are overwritten by later blocks; rollback is a length update).
  * Outputs: d_logits fp32 [batch][n_logit_rows][vocab] for the last n_logit_rows rows of each block;
- * d_feats [batch][q_len][n_taps][hidden] in the model dtype: the residual stream after each tapped
- * layer, for KV injection by the next dflash_draft_block. */
+ * d_feats: the residual stream after each tapped layer, for KV injection by the next
+ * dflash_draft_block -- [2][batch][q_len][n_taps][hidden] bf16 (high plane, then low plane) for
+ * DFLASH_BF16 models, [batch][q_len][n_taps][hidden] fp32 for DFLASH_F32 models. */
 dflash_status dflash_verify_block(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
                                   const int32_t *d_tokens, int32_t q_len, int32_t new_sequence,
                                   int32_t n_logit_rows, float *d_logits, void *d_feats);
@@ -191,7 +197,9 @@ dflash_status dflash_accept_resample(dflash_ctx *ctx, hipStream_t stream, int32_
  * request, the target features of the positions committed by the last dflash_accept_resample
  * (read from d_feats as written by the preceding dflash_verify_block for the same slots in the same
  * order): c = RMSNorm(W_fc [h_tap1..h_tapm]), then every drafter layer's K = RoPE(k_norm(W_k c)) and
- * V = W_v c go into the drafter cache.  Then runs the block [anchor, MASK x (B-1)] at positions
+ * V = W_v c go into the drafter cache.  With a window W, rows that no later draft can see (those more
+ * than W + n_draft before the end of a long verified block, i.e. of a prefill) are not injected.  Then
+ * runs the block [anchor, MASK x (B-1)] at positions
  * n .. n+B-1 (n = committed length): block queries see all block keys and the injected context keys
  * within the window.  Writes the block to verify, d_block [batch][B] = [anchor, d_1 .. d_{B-1}], where
  * d_i is the argmax (lowest id on ties) of the drafter's fp32 logits at position n+i.  Optionally
