@@ -240,6 +240,20 @@ dflash_status dflash_accept_resample_q(dflash_ctx *ctx, hipStream_t stream, int3
 dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
                                const void *d_w, float *d_y);
 
+/* The same product on the stream-K projection kernel that the step uses for its residual and SwiGLU
+ * projections (operator-level test and measurement access): the (16-or-32-column tile, 256-byte K
+ * window) items of the product are cut into equal ranges, one work-group per compute unit, and a tile
+ * shared by several work-groups is finished by the last to arrive.  1 <= M <= 16, N a multiple of 32,
+ * K a multiple of 128 (bf16) or 64 (fp32); d_x [M][K], d_w [N][K], d_y [M][N] fp32 as for
+ * dflash_op_linear.  d_scratch: caller device memory of dflash_op_linear_sk_scratch_bytes(N) bytes,
+ * 256-byte aligned (partial tiles and per-tile arrival counters; the call zeroes the counters on
+ * `stream` before its launch, so its contents need no preparation); calls that overlap on one
+ * scratch block race.  Asynchronous on `stream`; needs no context. */
+size_t dflash_op_linear_sk_scratch_bytes(int32_t N); /* 0 if N is not a positive multiple of 32 */
+dflash_status dflash_op_linear_sk(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K,
+                                  const void *d_x, const void *d_w, float *d_y, void *d_scratch,
+                                  size_t scratch_bytes);
+
 /* Measurement access.  While profiling is enabled, the library records the projection launches
  * (kernel, shape and pointers) issued by the step calls.  dflash_profile_replay, called with
  * profiling disabled, re-issues exactly those launches `iters` times back to back on `stream`

@@ -83,6 +83,8 @@ def _load() -> C.CDLL:
         "dflash_accept_resample_q": (I, [V, V, I, P(I), V, V, I, P(Sampling), V, V, V, V, V, V]),
         "dflash_device_status": (I, [V, V]),
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
+        "dflash_op_linear_sk_scratch_bytes": (S, [I]),
+        "dflash_op_linear_sk": (I, [V, I, I, I, I, V, V, V, V, S]),
         "dflash_profile": (I, [V, I]),
         "dflash_profile_replay": (I, [V, V, I, P(C.c_double), P(C.c_double), P(I)]),
         "dflash_last_error": (C.c_char_p, []),
@@ -183,6 +185,15 @@ def dflash_accept_resample_q(ctx: int, slots: Sequence[int], logits, block, n_dr
 
 def dflash_op_linear(dtype: int, M: int, N: int, K: int, x, w, y, stream=None):
     _check(lib.dflash_op_linear(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y)))
+
+
+def dflash_op_linear_sk_scratch_bytes(N: int) -> int:
+    return lib.dflash_op_linear_sk_scratch_bytes(N)
+
+
+def dflash_op_linear_sk(dtype: int, M: int, N: int, K: int, x, w, y, scratch, stream=None):
+    _check(lib.dflash_op_linear_sk(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y), _ptr(scratch),
+                                   scratch.numel() * scratch.element_size()))
 
 
 def dflash_profile(ctx: int, enable: bool):

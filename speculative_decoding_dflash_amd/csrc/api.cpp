@@ -45,7 +45,6 @@ constexpr int kAttnFusedMaxSeqs = 4;  // decode calls of more sequences post-pro
 constexpr int kAttnWholeBlockPages = 256;  // key pages from which a batched call's work-groups hold whole blocks
 constexpr int kMaxKSplit = 8;
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
-constexpr int kSkMaxWg = 1024;  // stream-K projection work-groups (one per CU)
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
@@ -615,6 +614,37 @@ void filter_setup(dflash_ctx *c, FilterArgs &f, const float *logits, int rows, i
 
 }  // namespace
 
+namespace df {
+
+dflash_status set_error(dflash_status st, const char *msg) { return fail(st, "%s", msg); }
+
+// The projection on the stream-K kernel with the scratch block at d_scratch (sk_scratch_bytes(N)
+// bytes: partial tiles, then the tile counters, which are zeroed here before the launch).
+dflash_status op_linear_sk(hipStream_t s, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
+                           const void *d_w, float *d_y, void *d_scratch) {
+  if (dtype != DFLASH_BF16 && dtype != DFLASH_F32) return fail(DFLASH_E_INVAL, "bad dtype");
+  const int ksup = dtype == DFLASH_BF16 ? 128 : 64;  // K elements per 256-byte super-step
+  if (M < 1 || M > 16 || N < 32 || N % 32 || K < ksup || K % ksup)
+    return fail(DFLASH_E_INVAL, "stream-K shape: need 1 <= M <= 16, N a multiple of 32, K a multiple of %d", ksup);
+  if (!d_x || !d_w || !d_y || !d_scratch) return fail(DFLASH_E_INVAL, "null pointer");
+  if ((uintptr_t)d_scratch & 255) return fail(DFLASH_E_INVAL, "scratch must be 256-byte aligned");
+  GemmArgs a = gemm_base(d_x, K, M, N, K, EPI_STORE_F32);
+  a.nseg = 1;
+  a.seg[0] = GemmSeg{d_w, N};
+  a.out_f32 = d_y;
+  a.ld_out = N;
+  a.sk_part = (float *)d_scratch;
+  a.sk_cnt = (int32_t *)((char *)d_scratch + kSkPartBytes);
+  a.sk_max_wg = kSkMaxWg;
+  a.sk_max_tiles = N / 16;
+  a.sk_force = 1;
+  HIP_OK(launch_zero_i32(a.sk_cnt, N / 16, s));
+  HIP_OK(launch_gemm(a, dtype == DFLASH_BF16 ? 0 : 1, s));
+  return DFLASH_OK;
+}
+
+}  // namespace df
+
 extern "C" {
 
 const char *dflash_last_error(void) { return g_err.c_str(); }
@@ -1064,6 +1094,15 @@ dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t 
   a.out_f32 = d_y;
   a.ld_out = N;
   return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, true, s);
+}
+
+size_t dflash_op_linear_sk_scratch_bytes(int32_t N) { return N > 0 && N % 32 == 0 ? sk_scratch_bytes(N) : 0; }
+
+dflash_status dflash_op_linear_sk(hipStream_t s, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
+                                  const void *d_w, float *d_y, void *d_scratch, size_t scratch_bytes) {
+  if (N > 0 && N % 32 == 0 && scratch_bytes < sk_scratch_bytes(N))
+    return fail(DFLASH_E_INVAL, "scratch of %zu bytes, %zu needed", scratch_bytes, sk_scratch_bytes(N));
+  return df::op_linear_sk(s, dtype, M, N, K, d_x, d_w, d_y, d_scratch);
 }
 
 dflash_status dflash_profile(dflash_ctx *c, int32_t enable) {

@@ -488,7 +488,9 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
 #pragma unroll
   for (int h = 0; h < NH; ++h) issue_half(h);
   advance();
-  ssp.store(a, s_ssp);  // read after the first tile's reduction barrier
+  ssp.store(a, s_ssp);
+  __syncthreads();  // the rows' 1/rms before the stream (computed inside the tile loop, the kernel kept a stack frame)
+  if (a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
 
   int seg = 0;
   for (int t = lo / nsup; t * nsup < hi; ++t, ++seg) {
@@ -533,7 +535,6 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
         if (!FOLD || g < 2) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = v;
       }
     __syncthreads();
-    if (seg == 0 && a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
     float v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -1058,7 +1059,7 @@ static int sk_fold_cols() { return env_int("DFLASH_GEMM_SK_COLS", 32) == 64 ? 64
 // DFLASH_GEMM_SK=0 turns it off, =1 uses it wherever the shape allows.
 static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
   const int env = env_int("DFLASH_GEMM_SK", -1);  // read per launch: tests switch it
-  if (!a.sk_part || !a.sk_cnt || env == 0 || a.M < 1 || x_rows(a) > 16 || a.ksplit != 1) return 0;
+  if (!a.sk_part || !a.sk_cnt || (env == 0 && !a.sk_force) || a.M < 1 || x_rows(a) > 16 || a.ksplit != 1) return 0;
   const int sk = dtype == 0 ? 128 : 64;  // K elements per super-step
   if (a.K < sk || a.K % sk) return 0;
   const bool swiglu = a.epi == EPI_SWIGLU;
@@ -1067,7 +1068,7 @@ static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
   if (!swiglu)
     for (int i = 0; i < a.nseg; ++i)
       if (a.seg[i].n % cols) return 0;
-  if (env != 1 && a.epi != EPI_RESID_NORM && !swiglu) return 0;
+  if (env != 1 && !a.sk_force && a.epi != EPI_RESID_NORM && !swiglu) return 0;
   const long ntile = swiglu ? a.N / (cols / 2) : a.N / cols;
   if (ntile > a.sk_max_tiles) return 0;
   static int cus[64] = {0};
@@ -1097,7 +1098,9 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
     return hipGetLastError();
   }
   int n_wg = 0;
-  if (const int per = sk_per(a, dtype, &n_wg)) {
+  const int sk = sk_per(a, dtype, &n_wg);
+  if (a.sk_force && !sk) return hipErrorInvalidValue;
+  if (const int per = sk) {
     const dim3 grid(n_wg), block(512);
     const bool x8 = x_rows(a) <= 8;
     if (dtype == 0) {

@@ -1,6 +1,7 @@
 // Internal launch interface between the host side (api.cpp) and the kernels.  Not part of the ABI.
 #pragma once
 #include "common.h"
+#include "../../include/dflash.h"
 
 namespace df {
 
@@ -67,6 +68,7 @@ struct GemmArgs {
   float *sk_part;
   int32_t *sk_cnt;
   int32_t sk_max_wg, sk_max_tiles;
+  int32_t sk_force;  // take the stream-K kernel whatever the epilogue (launch_gemm fails if it cannot)
   // Optional scratch of the decode-batch path (gemm_mb_ok): raw fp32 sums of up to mb_raw_cap
   // elements ([K range][M][N]).
   float *mb_raw;
@@ -80,6 +82,13 @@ struct GemmArgs {
 // most kMbMaxSplit ranges, reduced by a second launch) instead of row chunks.
 constexpr int kMbMinRows = 32, kMbMaxRows = 256, kMbMaxSplit = 8;
 constexpr int kSkTileElems = 16 * 32;  // entries of one partial tile (16 rows x 32 columns)
+constexpr int kSkMaxWg = 1024;         // stream-K work-groups at most (one per CU)
+// Stream-K scratch of a projection with N output columns, as one block: the partial tiles of up to
+// kSkMaxWg work-groups (fp32), then one arrival counter per 16-column tile (int32, zero between launches).
+constexpr size_t kSkPartBytes = (size_t)kSkMaxWg * 2 * kSkTileElems * sizeof(float);
+inline size_t sk_scratch_bytes(int N) { return kSkPartBytes + (size_t)(N / 16) * sizeof(int32_t); }
+// Zero n int32 values (a fill kernel, so that the call may be captured into a graph).
+hipError_t launch_zero_i32(int32_t *p, int32_t n, hipStream_t s);
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
@@ -274,6 +283,14 @@ struct DraftSampleArgs {
   int32_t *out;        // [batch][block]: draft i goes to out[b * block + i]
 };
 hipError_t launch_draft_sample(const DraftSampleArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- operator-level entry points (api.cpp)
+// The projection on the stream-K kernel, scratch block at d_scratch (sk_scratch_bytes(N) bytes, 256-byte
+// aligned): checks the arguments, zeroes the tile counters, launches.
+dflash_status op_linear_sk(hipStream_t s, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
+                           const void *d_w, float *d_y, void *d_scratch);
+// Records msg as the calling thread's last error and returns st.
+dflash_status set_error(dflash_status st, const char *msg);
 
 // copy candidate lists out for tests
 hipError_t launch_copy_cands(const int32_t *cid, const float *cp, const int32_t *cn, int32_t rows, int32_t *oid,

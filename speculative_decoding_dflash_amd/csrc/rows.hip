@@ -194,6 +194,17 @@ hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void zero_i32_kernel(int32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t *p, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 // Rotary table: the angle p * theta^(-2i/d) in fp64, then its cosine and sine rounded to fp32.
 __global__ void rope_table_kernel(float2 *table, double theta, int half, int d, int n_pos) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;

@@ -74,3 +74,21 @@ def test_null_context_calls_fail_cleanly():
     assert B.lib.dflash_verify_block(None, None, 1, None, None, 8, 0, 8, None, None) == B.E_INVAL
     assert B.lib.dflash_draft_block(None, None, 1, None, None, None, None) == B.E_INVAL
     assert B.lib.dflash_accept_resample(None, None, 1, None, None, None, 7, None, None, None, None, None) == B.E_INVAL
+
+
+def test_op_linear_sk_rejects_bad_arguments_on_the_host():
+    """dflash_op_linear_sk checks shapes, pointers and the scratch size before any device call (the
+    stream and pointers below are never used)."""
+    from speculative_decoding_dflash_amd import binding as B
+    lib = B.lib
+    assert lib.dflash_op_linear_sk_scratch_bytes(0) == 0 and lib.dflash_op_linear_sk_scratch_bytes(48) == 0
+    need = lib.dflash_op_linear_sk_scratch_bytes(5120)
+    assert need == 1024 * 2 * 512 * 4 + (5120 // 16) * 4
+    fake, aligned = 0x10000, 0x100000
+    ok = dict(dtype=B.BF16, M=8, N=5120, K=5120, x=fake, w=fake, y=fake, s=aligned, b=need)
+    bad = [dict(M=0), dict(M=17), dict(N=48), dict(K=96), dict(K=0), dict(dtype=7), dict(x=None), dict(y=None),
+           dict(s=None), dict(s=aligned + 16), dict(b=need - 1), dict(dtype=B.F32, K=96)]
+    for over in bad:
+        a = {**ok, **over}
+        st = lib.dflash_op_linear_sk(None, a["dtype"], a["M"], a["N"], a["K"], a["x"], a["w"], a["y"], a["s"], a["b"])
+        assert st == B.E_INVAL, over

@@ -336,6 +336,32 @@ def test_op_linear(dtype, M, N, K):
     assert err < 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 5120, 17408), (13, 34816, 5120), (16, 640, 256),
+                                   (5, 5120, 25600), (8, 96, 128)])
+def test_op_linear_sk(dtype, M, N, K):
+    """The stream-K projection kernel on its own (dflash_op_linear_sk, caller scratch): against float64
+    matmul of the same storage-typed inputs, and twice in a row on one scratch block (the counters the
+    first call leaves are cleared by the second), at 27B decode shapes, a ragged row count and a shape
+    with fewer items than work-groups."""
+    from speculative_decoding_dflash_amd import binding as Bd
+    rng = np.random.default_rng(M * 13 + N + K)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xt = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(tdt).cuda()
+    wt = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(tdt).cuda()
+    scratch = torch.empty(Bd.dflash_op_linear_sk_scratch_bytes(N), dtype=torch.uint8, device="cuda")
+    ys = [torch.zeros(M * N, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for y in ys:
+        Bd.dflash_op_linear_sk(Bd.BF16 if dtype == "bf16" else Bd.F32, M, N, K, xt, wt, y, scratch)
+    torch.cuda.synchronize()
+    ref = xt.double().cpu().numpy() @ wt.double().cpu().numpy().T
+    got = ys[0].view(M, N).cpu().numpy()
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    log(f"  stream-K linear {dtype} {M}x{N}x{K}: rel err {err:.2e}")
+    assert err < 1e-5
+    assert torch.equal(ys[0], ys[1])
+
+
 @pytest.mark.parametrize("stochastic", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_graph_replay_equals_eager_steps(name, stochastic):
