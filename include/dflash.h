@@ -254,6 +254,16 @@ dflash_status dflash_op_linear_sk(hipStream_t stream, int32_t dtype, int32_t M, 
                                   const void *d_x, const void *d_w, float *d_y, void *d_scratch,
                                   size_t scratch_bytes);
 
+/* dflash_op_linear_sk for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernel and result bit for bit, with
+ * the scratch in a static device array of the library (4.2 MB, held by each GPU the library runs on
+ * until the process ends) instead of caller memory.  N must not exceed 131072 (DFLASH_E_INVAL); other
+ * arguments and errors as dflash_op_linear_sk.  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array (the call clears its counters before launching): calls that overlap on one
+ * GPU race. */
+dflash_status dflash_op_linear_sk_noalloc(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K,
+                                          const void *d_x, const void *d_w, float *d_y);
+
 /* Measurement access.  While profiling is enabled, the library records the projection launches
  * (kernel, shape and pointers) issued by the step calls.  dflash_profile_replay, called with
  * profiling disabled, re-issues exactly those launches `iters` times back to back on `stream`

@@ -85,6 +85,7 @@ def _load() -> C.CDLL:
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
         "dflash_op_linear_sk_scratch_bytes": (S, [I]),
         "dflash_op_linear_sk": (I, [V, I, I, I, I, V, V, V, V, S]),
+        "dflash_op_linear_sk_noalloc": (I, [V, I, I, I, I, V, V, V]),
         "dflash_profile": (I, [V, I]),
         "dflash_profile_replay": (I, [V, V, I, P(C.c_double), P(C.c_double), P(I)]),
         "dflash_last_error": (C.c_char_p, []),
@@ -194,6 +195,10 @@ def dflash_op_linear_sk_scratch_bytes(N: int) -> int:
 def dflash_op_linear_sk(dtype: int, M: int, N: int, K: int, x, w, y, scratch, stream=None):
     _check(lib.dflash_op_linear_sk(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y), _ptr(scratch),
                                    scratch.numel() * scratch.element_size()))
+
+
+def dflash_op_linear_sk_noalloc(dtype: int, M: int, N: int, K: int, x, w, y, stream=None):
+    _check(lib.dflash_op_linear_sk_noalloc(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y)))
 
 
 def dflash_profile(ctx: int, enable: bool):

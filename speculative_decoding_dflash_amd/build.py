@@ -29,6 +29,7 @@ SOURCES = {
     "sampler.hip": [],
     "decide.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],
+    "op_static.cpp": ["-x", "hip"],
 }
 
 
