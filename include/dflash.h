@@ -38,7 +38,10 @@
  *     table[p / page_tokens].
  *   - Target features (verify output, draft input) of DFLASH_BF16 models are two bf16 planes of the
  *     same shape, hi = bf16(h) then lo = bf16(h - hi), so that hi + lo carries the fp32 residual
- *     stream to about 16 significant bits; DFLASH_F32 models hold one fp32 plane.
+ *     stream to about 16 significant bits -- except after a verify of DFLASH_F16_MIN_ROWS or more
+ *     rows (batch * q_len), which writes one IEEE fp16 plane (the first plane's place; 11 significant
+ *     bits, the precision of that call's projection inputs); DFLASH_F32 models hold one fp32 plane.
+ *     The buffer is sized for two planes in every case.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -55,6 +58,10 @@ extern "C" {
 #define DFLASH_MAX_BATCH 64
 #define DFLASH_MAX_BLOCK 16
 #define DFLASH_MAX_TOPK 256
+/* Calls of DFLASH_BF16 models over at least this many rows hold their projection inputs (and write their
+ * features) as one fp16 plane and run the tiled fp16 projection kernel (dflash_op_linear_f16x); smaller
+ * calls hold two bf16 planes. */
+#define DFLASH_F16_MIN_ROWS 32
 
 typedef enum {
   DFLASH_OK = 0,
@@ -172,7 +179,8 @@ dflash_status dflash_kv_free(dflash_ctx *ctx, int32_t slot);
  * Outputs: d_logits fp32 [batch][n_logit_rows][vocab] for the last n_logit_rows rows of each block;
  * d_feats: the residual stream after each tapped layer, for KV injection by the next
  * dflash_draft_block -- [2][batch][q_len][n_taps][hidden] bf16 (high plane, then low plane) for
- * DFLASH_BF16 models, [batch][q_len][n_taps][hidden] fp32 for DFLASH_F32 models. */
+ * DFLASH_BF16 models ([batch][q_len][n_taps][hidden] fp16 in the first plane's place when batch * q_len
+ * >= DFLASH_F16_MIN_ROWS), [batch][q_len][n_taps][hidden] fp32 for DFLASH_F32 models. */
 dflash_status dflash_verify_block(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
                                   const int32_t *d_tokens, int32_t q_len, int32_t new_sequence,
                                   int32_t n_logit_rows, float *d_logits, void *d_feats);
@@ -239,6 +247,18 @@ dflash_status dflash_accept_resample_q(dflash_ctx *ctx, hipStream_t stream, int3
  * 16 and K of 32 (bf16) or 16 (fp32).  Asynchronous on `stream`; needs no context. */
 dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
                                const void *d_w, float *d_y);
+
+/* The projection kernel of calls over many rows (decode batches of 32 or more rows, prefill) on its
+ * own: d_y = d_x d_w^T with d_x [M][K] in fp16 (IEEE binary16, one plane), d_w [N][K] in bf16 (converted
+ * to fp16 inside the kernel, exactly for |w| in [2^-14, 65504]), fp32 accumulation on the matrix cores.
+ * It is the arithmetic of bf16 models' large calls (the projection inputs are rounded once to fp16's 11
+ * significant bits; see the readings of the pages for why more than bf16's 8 are kept).  M >= 1,
+ * N a multiple of 32, K a multiple of 64.  The launch may cut K into up to max_ranges ranges (1 <=
+ * max_ranges <= 8): range z writes its fp32 sums to d_y + z * M * N (d_y holds max_ranges * M * N
+ * floats) and *ranges (host memory; may be null when max_ranges is 1) receives the count; the product
+ * is the sum of the ranges in order.  Asynchronous on `stream`; needs no context. */
+dflash_status dflash_op_linear_f16x(hipStream_t stream, int32_t M, int32_t N, int32_t K, const void *d_x,
+                                    const void *d_w, float *d_y, int32_t max_ranges, int32_t *ranges);
 
 /* The same product on the stream-K projection kernel that the step uses for its residual and SwiGLU
  * projections (operator-level test and measurement access): the (16-or-32-column tile, 256-byte K

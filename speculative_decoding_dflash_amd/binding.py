@@ -16,6 +16,7 @@ MAX_TAPS = 16
 MAX_BATCH = 64
 MAX_BLOCK = 16
 MAX_TOPK = 256
+F16_MIN_ROWS = 32  # DFLASH_F16_MIN_ROWS
 
 OK, E_INVAL, E_NOMEM, E_DEVICE, E_STATE = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
@@ -83,6 +84,7 @@ def _load() -> C.CDLL:
         "dflash_accept_resample_q": (I, [V, V, I, P(I), V, V, I, P(Sampling), V, V, V, V, V, V]),
         "dflash_device_status": (I, [V, V]),
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
+        "dflash_op_linear_f16x": (I, [V, I, I, I, V, V, V, I, P(I)]),
         "dflash_op_linear_sk_scratch_bytes": (S, [I]),
         "dflash_op_linear_sk": (I, [V, I, I, I, I, V, V, V, V, S]),
         "dflash_op_linear_sk_noalloc": (I, [V, I, I, I, I, V, V, V]),
@@ -186,6 +188,13 @@ def dflash_accept_resample_q(ctx: int, slots: Sequence[int], logits, block, n_dr
 
 def dflash_op_linear(dtype: int, M: int, N: int, K: int, x, w, y, stream=None):
     _check(lib.dflash_op_linear(_stream(stream), dtype, M, N, K, _ptr(x), _ptr(w), _ptr(y)))
+
+
+def dflash_op_linear_f16x(M: int, N: int, K: int, x, w, y, max_ranges: int = 1, stream=None) -> int:
+    """x fp16 [M, K], w bf16 [N, K], y fp32 [max_ranges, M, N]; returns the K ranges written."""
+    n = C.c_int32(1)
+    _check(lib.dflash_op_linear_f16x(_stream(stream), M, N, K, _ptr(x), _ptr(w), _ptr(y), max_ranges, C.byref(n)))
+    return n.value
 
 
 def dflash_op_linear_sk_scratch_bytes(N: int) -> int:

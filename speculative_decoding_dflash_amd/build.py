@@ -24,6 +24,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Xclang", "-t
           "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 SOURCES = {
     "gemm.hip": [],
+    "gemm_tc.hip": [],
     "attention.hip": [],
     "rows.hip": [],
     "sampler.hip": [],

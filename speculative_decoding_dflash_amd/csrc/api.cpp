@@ -44,6 +44,8 @@ constexpr int kAttnWgTarget = 512;  // work-groups a batched decode attention ca
 constexpr int kAttnFusedMaxSeqs = 4;  // decode calls of more sequences post-process q / k / v separately
 constexpr int kAttnWholeBlockPages = 256;  // key pages from which a batched call's work-groups hold whole blocks
 constexpr int kMaxKSplit = 8;
+// Calls of a bf16 model with at least this many rows run in x16 mode (dflash_ctx::x16).
+constexpr int kTcMinRows = DFLASH_F16_MIN_ROWS;
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
 
 // Workspace carve-up; offsets in bytes.
@@ -165,12 +167,23 @@ struct dflash_ctx {
   // depend on how many rows share the launch, so a decode step computes the same bits whether it is
   // issued eagerly or replayed from a graph captured at another row count.
   bool tiled = false;
+  // Set while a call of a bf16 model runs its projections with one fp16 plane per projection input
+  // (x16 mode: kTcMinRows rows or more, the tiled fp16 kernel of gemm_tc.hip).  In that mode the
+  // producers of projection inputs (norms, attention output, SwiGLU, feature taps) store fp16 (their low
+  // plane pointers are null), every RMSNorm is applied at once (no deferred 1/rms), and the residual
+  // projections write K-range partial sums that norm_kernel adds to the residual and normalises.
+  bool x16 = false;
+  // The features written by the last verify are fp16 (it ran in x16 mode); the next draft injects them
+  // in that mode.
+  bool feat16 = false;
   // measurement: the projection launches issued while profiling is on, kept for replay
   bool profiling = false;
   struct Rec {
     GemmArgs a;
     int rows;
     bool tiled;
+    bool x16;
+    TcPlan plan;
   };
   std::vector<Rec> recorded;
 
@@ -190,15 +203,16 @@ struct dflash_ctx {
   // Low plane of the projection-input buffer at workspace offset `off` whose planes hold `plane_elems`
   // elements (null for fp32 models).
   void *xlo(size_t off, size_t plane_elems) const {
-    return cfg.dtype == DFLASH_BF16 ? (void *)(ws + off + plane_elems * es()) : nullptr;
+    return cfg.dtype == DFLASH_BF16 && !x16 ? (void *)(ws + off + plane_elems * es()) : nullptr;
   }
   void *xn_lo() const { return xlo(L.xn, (size_t)cap.max_rows * cfg.hidden); }
   void *attn_lo() const { return xlo(L.attn, (size_t)cap.max_rows * cfg.q_heads * cfg.head_dim); }
   void *ffn_lo() const { return xlo(L.ffn, (size_t)cap.max_rows * cfg.ffn); }
   // Low plane of caller features for `rows` rows (bf16 models: [2][rows][n_taps * hidden]).
   void *feats_lo(const void *feats, int rows) const {
-    return cfg.dtype == DFLASH_BF16 ? (void *)((const char *)feats + (size_t)rows * dcfg.n_taps * cfg.hidden * es())
-                                    : nullptr;
+    return cfg.dtype == DFLASH_BF16 && !x16
+               ? (void *)((const char *)feats + (size_t)rows * dcfg.n_taps * cfg.hidden * es())
+               : nullptr;
   }
   int rope_rows() const { return cap.max_pages_per_seq * cap.page_tokens; }
   int es() const { return esize(&cfg); }
@@ -262,14 +276,40 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_
   return DFLASH_OK;
 }
 
+// x16 mode: all R rows in one launch of the tiled fp16 kernel (range_cap: elements of a.out_f32 that
+// K ranges may fill; 0 keeps one range).
+dflash_status plan_tc(GemmArgs &a, int R, int64_t range_cap, TcPlan *p) {
+  a.M = R;
+  a.row_off = 0;
+  a.x_lo = nullptr;
+  if (!gemm_tc_plan(a, range_cap, p))
+    return fail(DFLASH_E_INVAL, "projection %d x %d x %d (epilogue %d) does not suit the fp16 tiled kernel", R, a.N, a.K,
+                a.epi);
+  return DFLASH_OK;
+}
+
+dflash_status launch_tc(dflash_ctx *c, GemmArgs a, int R, const TcPlan &p, hipStream_t s) {
+  if (a.epi == EPI_PARTIAL) a.part_stride = (int64_t)R * a.N;
+  if (c->profiling) c->recorded.push_back({a, R, false, true, p});
+  HIP_OK(launch_gemm_tc(a, p, s));
+  return DFLASH_OK;
+}
+
+dflash_status run_gemm_tc(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
+  TcPlan p;
+  dflash_status st = plan_tc(a, R, 0, &p);
+  return st != DFLASH_OK ? st : launch_tc(c, a, R, p, s);
+}
+
 dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
+  if (c->x16) return run_gemm_tc(c, a, R, s);
   a.sk_part = c->wsp<float>(c->L.skp);
   a.sk_cnt = c->wsp<int32_t>(c->L.skc);
   a.sk_max_wg = kSkMaxWg;
   a.sk_max_tiles = c->L.sk_tiles;
   a.mb_raw = c->L.mbr_elems ? c->wsp<float>(c->L.mbr) : nullptr;
   a.mb_raw_cap = (int64_t)c->L.mbr_elems;
-  if (c->profiling) c->recorded.push_back({a, R, c->tiled});
+  if (c->profiling) c->recorded.push_back({a, R, c->tiled, false, TcPlan{}});
   return run_gemm(c->es(), c->dt(), a, R, c->tiled, s);
 }
 
@@ -282,6 +322,18 @@ dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
 dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *n_part, const float **src,
                           int64_t *stride) {
   a.epi = EPI_PARTIAL;
+  if (c->x16) {  // several K ranges go to the decode-batch buffer, one range to L.part
+    TcPlan p;
+    dflash_status st = plan_tc(a, R, (int64_t)c->L.mbr_elems, &p);
+    if (st != DFLASH_OK) return st;
+    a.out_f32 = p.ranges > 1 ? c->wsp<float>(c->L.mbr) : c->wsp<float>(c->L.part);
+    a.ld_out = a.N;
+    if ((st = launch_tc(c, a, R, p, s)) != DFLASH_OK) return st;
+    *n_part = p.ranges;
+    *src = a.out_f32;
+    *stride = (int64_t)R * a.N;
+    return DFLASH_OK;
+  }
   a.out_f32 = c->wsp<float>(c->L.part);
   a.ld_out = a.N;
   a.ksplit = R <= kGemmMaxRows / xplanes(&c->cfg)
@@ -334,7 +386,7 @@ dflash_status prep_norm(dflash_ctx *c, int R, const void *gain, hipStream_t s) {
   n.take = R;
   n.stride = R;
   n.offset = 0;
-  n.ss_out = c->wsp<float>(c->L.ss);
+  n.ss_out = c->x16 ? nullptr : c->wsp<float>(c->L.ss);  // x16 mode: normalised at once
   n.ss_ld = c->L.ss_ld;
   HIP_OK(launch_norm(n, c->dt(), s));
   return DFLASH_OK;
@@ -342,6 +394,7 @@ dflash_status prep_norm(dflash_ctx *c, int R, const void *gain, hipStream_t s) {
 
 // A projection whose X rows are xn awaiting their 1/rms factor (ss_n partial sums per row in L.ss).
 void with_norm(dflash_ctx *c, GemmArgs &a, int ss_n) {
+  if (c->x16) return;  // its inputs are normalised already
   a.ss_in = c->wsp<float>(c->L.ss);
   a.ss_n = ss_n;
   a.ss_ld = c->L.ss_ld;
@@ -353,6 +406,37 @@ void with_norm(dflash_ctx *c, GemmArgs &a, int ss_n) {
 // the new row) and then RMS-normalised with the deferred scheme; returns ss_n for the consumer.
 dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, void *feat, void *feat_lo, int ld_feat,
                              const NextNorm &nx, hipStream_t s, int *ss_n) {
+  if (c->x16) {  // K-range partial sums, then one pass per row: residual add, feature tap, RMSNorm
+    int np = 1;
+    const float *part = nullptr;
+    int64_t pstride = 0;
+    dflash_status st = run_partial(c, a, R, s, &np, &part, &pstride);
+    if (st != DFLASH_OK) return st;
+    NormArgs n;
+    memset(&n, 0, sizeof n);
+    n.x = resid;
+    n.ld_x = c->cfg.hidden;
+    n.part = part;
+    n.n_part = np;
+    n.ld_part = a.N;
+    n.part_stride = pstride;
+    n.feat = feat;
+    n.feat_lo = nullptr;
+    n.ld_feat = ld_feat;
+    n.gain = (const float *)nx.gain;
+    n.eps = c->cfg.rms_eps;
+    n.hidden = c->cfg.hidden;
+    n.out = c->wsp<void>(c->L.xn);
+    n.out_lo = nullptr;
+    n.ld_out = c->cfg.hidden;
+    n.n_rows = R;
+    n.take = nx.take;
+    n.stride = nx.stride;
+    n.offset = nx.offset;
+    HIP_OK(launch_norm(n, c->dt(), s));
+    *ss_n = 1;
+    return DFLASH_OK;
+  }
   a.epi = EPI_RESID_NORM;
   a.resid = resid;
   a.ld_resid = c->cfg.hidden;
@@ -787,6 +871,11 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
 
   const dflash_model_cfg &m = c->cfg;
   const int R = batch * q_len, H = m.hidden;
+  struct ModeScope {  // x16 mode for this call's projections; cleared on every exit
+    dflash_ctx *c;
+    ~ModeScope() { c->x16 = false; }
+  } mode_scope{c};
+  c->x16 = m.dtype == DFLASH_BF16 && R >= kTcMinRows;
   Rows rows = c->rows(0);
   PrepArgs p;
   memset(&p, 0, sizeof p);
@@ -837,6 +926,7 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
 
   for (int b = 0; b < batch; ++b)
     if (new_sequence) c->prefilled[slots[b]] = 1;
+  c->feat16 = c->x16;
   c->last_qlen = q_len;
   c->last_nlogit = nl;
   c->last_nd = -1;
@@ -960,9 +1050,13 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   // keep the row-count-independent kernels
   struct TiledScope {
     dflash_ctx *c;
-    ~TiledScope() { c->tiled = false; }
+    ~TiledScope() {
+      c->tiled = false;
+      c->x16 = false;
+    }
   } tiled_scope{c};
   c->tiled = Ri > c->cap.max_slots * B;
+  c->x16 = c->feat16;  // the injection runs in the mode its features were written in
   {
     GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_RESID_NORM);
     a.x_lo = c->feats_lo(d_feats, batch * Q);
@@ -1003,6 +1097,7 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   }
   c->tiled = false;
   // 2. The block [anchor, MASK x (B-1)].
+  c->x16 = m.dtype == DFLASH_BF16 && batch * B >= kTcMinRows;
   Rows rd = c->rows(2);
   p.rows = rd;
   p.q_len = B;
@@ -1096,6 +1191,25 @@ dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t 
   return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, true, s);
 }
 
+dflash_status dflash_op_linear_f16x(hipStream_t s, int32_t M, int32_t N, int32_t K, const void *d_x, const void *d_w,
+                                    float *d_y, int32_t max_ranges, int32_t *ranges) {
+  if (M < 1 || N < 32 || N % 32 || K < 64 || K % 64) return fail(DFLASH_E_INVAL, "bad GEMM shape");
+  if (max_ranges < 1 || max_ranges > kTcMaxRanges || (max_ranges > 1 && !ranges))
+    return fail(DFLASH_E_INVAL, "max_ranges out of range (or null ranges)");
+  if (!d_x || !d_w || !d_y) return fail(DFLASH_E_INVAL, "null pointer");
+  GemmArgs a = gemm_base(d_x, K, M, N, K, max_ranges > 1 ? EPI_PARTIAL : EPI_STORE_F32);
+  a.nseg = 1;
+  a.seg[0] = GemmSeg{d_w, N};
+  a.out_f32 = d_y;
+  a.ld_out = N;
+  a.part_stride = (int64_t)M * N;
+  TcPlan p;
+  if (!gemm_tc_plan(a, (int64_t)max_ranges * M * N, &p)) return fail(DFLASH_E_INVAL, "shape not supported");
+  HIP_OK(launch_gemm_tc(a, p, s));
+  if (ranges) *ranges = p.ranges;
+  return DFLASH_OK;
+}
+
 size_t dflash_op_linear_sk_scratch_bytes(int32_t N) { return N > 0 && N % 32 == 0 ? sk_scratch_bytes(N) : 0; }
 
 dflash_status dflash_op_linear_sk(hipStream_t s, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
@@ -1128,6 +1242,10 @@ dflash_status dflash_profile_replay(dflash_ctx *c, hipStream_t s, int32_t iters,
   HIP_OK(hipEventRecord(e0, s));
   for (int it = 0; it < iters; ++it)
     for (const auto &r : c->recorded) {
+      if (r.x16) {
+        HIP_OK(launch_gemm_tc(r.a, r.plan, s));
+        continue;
+      }
       dflash_status st = run_gemm(c->es(), c->dt(), r.a, r.rows, r.tiled, s);
       if (st != DFLASH_OK) return st;
     }

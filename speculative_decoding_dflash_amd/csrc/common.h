@@ -71,8 +71,13 @@ template <> struct XOf<float> { using type = float; };
 // Projection inputs (the X operand of every weight product) of bf16 models are held as two bf16
 // planes, hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact in fp32), so that hi + lo carries v to
 // about 16 significant bits and the product W (hi + lo) = W hi + W lo loses nothing to the storage of
-// X.  fp32 models keep one plane (lo is null).
+// X.  Calls over many rows instead hold one fp16 plane (lo null: the 16-bit words at hi are fp16), for
+// the tiled fp16 kernel.  fp32 models keep one plane (lo is null).
 DF_DEVICE void store_x(bf16 *hi, bf16 *lo, size_t i, float v) {
+  if (!lo) {
+    hi[i].bits = f32_to_f16(v);
+    return;
+  }
   const uint16_t h = f32_to_bf16(v);
   hi[i].bits = h;
   if (lo) lo[i].bits = f32_to_bf16(v - bf16_to_f32(h));

@@ -1,0 +1,284 @@
+// Tiled MFMA projection for many rows (decode batches of 32+ rows, prefill): Y[M, N] = X[M, K] W[N, K]^T
+// with X in fp16 (one plane) and the bf16 weights converted to fp16 as they are staged.
+//
+// Why fp16 here: a bf16 model's projection inputs need more than bf16's 8 significant bits to keep the
+// logits of a 64-layer forward within the bf16 tolerance.  At a handful of rows the skinny kernels carry
+// X as two bf16 planes (hi + lo) at no cost, since the matrix cores idle there; at hundreds of rows the
+// second plane would double the MFMA work of a product that is now compute-bound.  fp16 keeps 11
+// significant bits in one plane, and every bf16 weight inside fp16's normal range (|w| in
+// [2^-14, 65504]) converts to fp16 exactly (8 significant bits fit in 11); smaller ones land on fp16's
+// subnormal grid (absolute error below 2^-24).  So W x is the product of the exact weights with an X
+// rounded to 11 bits, accumulated in fp32 by v_mfma_f32_16x16x32_f16.
+//
+// Shape of the kernel:
+//   * a work-group (4 waves) computes a BM-row x (32 U)-column tile, U <= UM "units" of 32 weight rows
+//     (SWIGLU: 16 gate rows and the same 16 up rows, i.e. 16 output columns); each wave holds 64 rows of
+//     the tile and 1/WC of its columns (WC = 1, 2, 4 for BM = 256, 128, 64);
+//   * the units of a projection are cut into `nch` contiguous chunks of as equal a size as possible
+//     (grid x), so that a launch can have about one work-group per CU even when 32 UM does not divide
+//     N into the CU count (the 27B gate/up's 1088 units make 256 chunks of 4 or 5);
+//   * K runs in steps of 64 through a double-buffered LDS tile: the loads of step k + 2 are issued while
+//     step k is multiplied out of LDS and step k + 1 waits in registers; every load is unconditional
+//     (past the range, rows and steps are clamped onto valid memory and never used), so the waits count
+//     outstanding loads exactly;
+//   * grid z cuts K into ranges for projections with too few tiles to cover the CUs; each range writes
+//     its raw fp32 sums to out_f32 + z * part_stride (EPI_PARTIAL), and the consumer adds the ranges in
+//     order (qkv_post_kernel, norm_kernel);
+//   * epilogues: fp32 store (EPI_STORE_F32, EPI_PARTIAL) and SwiGLU with an fp16 store of silu(g) u.
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace df {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBK = 64;        // K per LDS step
+constexpr int kLDK = kBK + 8;  // LDS row stride in halfs (144 bytes: conflict-free 16-byte fragment reads)
+
+DF_DEVICE u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Two bf16 (low half: element 0) -> two fp16, exact in fp16's normal range (see the file comment).
+DF_DEVICE uint32_t bf2_to_h2(uint32_t w) {
+  const float e0 = __builtin_bit_cast(float, w << 16), e1 = __builtin_bit_cast(float, w & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+}
+DF_DEVICE u32x4 bf8_to_h8(u32x4 v) { return (u32x4){bf2_to_h2(v.x), bf2_to_h2(v.y), bf2_to_h2(v.z), bf2_to_h2(v.w)}; }
+
+DF_DEVICE void mma(f32x4 &acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+DF_DEVICE float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// X row of local row m (< M): m itself, or with a row selection the selected row of global row row_off + m.
+DF_DEVICE int tc_x_src(const GemmArgs &a, int m) {
+  if (!a.x_take) return m;
+  const int r = a.row_off + m;
+  return (r / a.x_take) * a.x_stride + a.x_off + r % a.x_take;
+}
+
+template <int BM, int UM>
+__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArgs a, int nch, int steps) {
+  constexpr int WC = BM == 256 ? 1 : (BM == 128 ? 2 : 4);  // waves across the tile's columns
+  constexpr int BN = UM * 32;                              // weight rows of a full chunk
+  constexpr int NJ = BN / 16 / WC;                         // 16-row weight fragments per wave
+  constexpr int CA = BM / 32, CB = UM;                     // 16-byte loads per thread and K step
+  static_assert(BM == 64 * (4 / WC), "each wave holds 64 rows");
+  static_assert(NJ * WC * 16 == BN && NJ % 2 == 0, "a wave holds whole units");
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kLDK];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wr = wave / WC, wc = wave % WC;
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  const int units = swiglu ? a.N / 16 : a.N / 32;
+  const int ch = blockIdx.x;
+  const int u0 = (int)((long)units * ch / nch), u1 = (int)((long)units * (ch + 1) / nch);
+  const int nrows = (u1 - u0) * 32;  // weight rows of this chunk (<= BN)
+  const int m0 = blockIdx.y * BM;
+  const int nk = a.K / kBK;
+  const int kt0 = blockIdx.z * steps, kt1 = min(nk, kt0 + steps);
+
+  // this thread's 16-byte chunks of a K step: chunk c = tid + 256 i -> tile row c / 8, halfs 8 (c % 8) ..
+  const uint16_t *pa[CA], *pb[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
+    pa[i] = (const uint16_t *)a.x + (size_t)tc_x_src(a, min(m0 + row, a.M - 1)) * a.ldx + kc;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + 256 * i, kc = (c & 7) * 8;
+    const int lr = (c >> 3) < nrows ? (c >> 3) : 0;  // rows past the chunk reload its first row
+    const uint16_t *w;
+    if (swiglu) {  // unit u: rows 0-15 gate rows 16 u .. 16 u + 15, rows 16-31 the same up rows
+      const int u = u0 + lr / 32;
+      w = (const uint16_t *)a.seg[(lr >> 4) & 1].w + (size_t)(16 * u + (lr & 15)) * a.K;
+    } else {
+      int nr = 32 * u0 + lr, si = 0;
+      while (si + 1 < a.nseg && nr >= a.seg[si].n) {
+        nr -= a.seg[si].n;
+        ++si;
+      }
+      w = (const uint16_t *)a.seg[si].w + (size_t)nr * a.K;
+    }
+    pb[i] = w + kc;
+  }
+
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[2][CA], rb[2][CB];
+  auto load = [&](int st, int kt) {
+    const int k = min(kt, kt1 - 1) * kBK;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) ra[st][i] = ld16(pa[i] + k);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) rb[st][i] = ld16(pb[i] + k);
+  };
+  auto store = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(&sA[buf][(c >> 3) * kLDK + (c & 7) * 8]) = ra[st][i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(&sB[buf][(c >> 3) * kLDK + (c & 7) * 8]) = bf8_to_h8(rb[st][i]);
+    }
+  };
+  load(0, kt0);
+  load(1, kt0 + 1);
+  store(0, 0);
+  __syncthreads();
+  // One K step out of LDS buffer BUF; the stage and buffer indices are template constants so that the
+  // register stages stay in registers.
+  auto kstep = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    load(buf, kt + 2);
+#pragma unroll
+    for (int s = 0; s < kBK / 32; ++s) {
+      u32x4 fa[4], fb[NJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][(wr * 64 + 16 * i + r16) * kLDK + 32 * s + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[j] = *reinterpret_cast<const u32x4 *>(&sB[buf][((wc * NJ + j) * 16 + r16) * kLDK + 32 * s + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mma(acc[i][j], fa[i], fb[j]);
+    }
+    if (kt + 1 < kt1) store(1 - buf, 1 - buf);
+    __syncthreads();
+  };
+  int kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < kt1) kstep(kt, std::integral_constant<int, 0>{});
+
+  // acc[i][j][r] = Y[row m0 + 64 wr + 16 i + 4 g + r][weight row 32 u0 + 16 (wc NJ + j) + r16]
+  if (swiglu) {
+    uint16_t *out = (uint16_t *)a.out_act;
+#pragma unroll
+    for (int q = 0; q < NJ / 2; ++q) {
+      const int lr = (wc * NJ + 2 * q) * 16;  // the unit's first (gate) row in the chunk
+      if (lr >= nrows) continue;
+      const int col = 16 * (u0 + lr / 32) + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 64 * wr + 16 * i + 4 * g + r;
+          if (m < a.M)
+            out[(size_t)(a.row_off + m) * a.ld_out + col] =
+                f32_to_f16(silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
+        }
+    }
+    return;
+  }
+  float *out = a.out_f32 + (size_t)blockIdx.z * a.part_stride;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int lr = (wc * NJ + j) * 16;
+    if (lr >= nrows) continue;
+    const int col = 32 * u0 + lr + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wr + 16 * i + 4 * g + r;
+        if (m < a.M) out[(size_t)(a.row_off + m) * a.ld_out + col] = acc[i][j][r];
+      }
+  }
+}
+
+int env_int(const char *name, int dflt) {
+  const char *e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = 256;
+  return cus[dev];
+}
+
+}  // namespace
+
+// Tile height, units per chunk, chunk count and K ranges of a projection.  The choice minimises a
+// simple model of the launch's time: rounds of work-groups (one per CU for 256-row tiles, two
+// otherwise) times the longest chunk's units times its K steps, plus a fixed cost per work-group and
+// the fp32 traffic of K-range partials.  DFLASH_TC_{BM,S,NCH} override it for sweeps.
+bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
+  const bool swiglu = a.epi == EPI_SWIGLU;
+  if (a.M < 1 || a.K % kBK || a.ksplit != 1 || a.ss_in || a.x_lo) return false;
+  if (a.epi != EPI_STORE_F32 && a.epi != EPI_PARTIAL && !swiglu) return false;
+  if (swiglu ? (a.N % 16 || a.nseg != 2) : a.N % 32) return false;
+  if (!swiglu)
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].n % 32) return false;
+  const int env_bm = env_int("DFLASH_TC_BM", 0);
+  int bm = a.M <= 64 ? 64 : (a.M <= 128 ? 128 : 256);
+  if (env_bm == 64 || env_bm == 128 || env_bm == 256) bm = env_bm;
+  const int um = bm == 256 ? 5 : 4;
+  const int units = swiglu ? a.N / 16 : a.N / 32;
+  const int rt = (a.M + bm - 1) / bm, nk = a.K / kBK;
+  const int slots = cu_count() * (bm == 256 ? 1 : 2);
+  const int env_s = env_int("DFLASH_TC_S", 0), env_nch = env_int("DFLASH_TC_NCH", 0);
+  // per-CU rate estimates (MI355X): ~60% of the dense fp16 MFMA peak, ~70% of an even share of HBM
+  const double mfma_us = (double)bm * 32 * kBK * 2 / (0.6 * 2.5e15 / 256) * 1e6;  // one unit x one K step
+  const double mem_us = (32.0 * kBK * 2) / (0.7 * 8e12 / 256) * 1e6;
+  double best = 1e30;
+  TcPlan bp{};
+  const int smax = a.epi == EPI_PARTIAL ? kTcMaxRanges : 1;
+  for (int s = 1; s <= smax; ++s) {
+    if (env_s > 0 && s != env_s) continue;
+    const int steps = (nk + s - 1) / s;
+    if (s > 1 && (steps < 4 || (int64_t)s * a.M * a.N > range_cap)) continue;
+    const int ranges = (nk + steps - 1) / steps;
+    if (ranges != s) continue;
+    const int nmin = (units + um - 1) / um;
+    for (int nch = nmin; nch <= std::min(units, nmin * 4); ++nch) {
+      if (env_nch > 0 && nch != env_nch) continue;
+      const int wgs = nch * rt * s;
+      const int rounds = (wgs + slots - 1) / slots;
+      const int umax = (units + nch - 1) / nch;
+      const double per = umax * steps * std::max(mfma_us, mem_us) + 1.5;
+      const double t = rounds * per + (s > 1 ? (double)s * a.M * a.N * 8 / 5e12 * 1e6 : 0.0);
+      if (t < best - 1e-9) {
+        best = t;
+        bp = TcPlan{bm, um, nch, s, steps};
+      }
+    }
+  }
+  if (best >= 1e30) return false;
+  *p = bp;
+  return true;
+}
+
+hipError_t launch_gemm_tc(const GemmArgs &a, const TcPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.ranges > 1 && a.epi != EPI_PARTIAL) return hipErrorInvalidValue;
+  const dim3 grid(p.nch, (a.M + p.bm - 1) / p.bm, p.ranges), block(256);
+  if (p.bm == 256) hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  else if (p.bm == 128) hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  else hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  return hipGetLastError();
+}
+
+}  // namespace df

@@ -103,6 +103,20 @@ int gemm_mb_slices(const GemmArgs &a);
 // over, each range a whole number of 256-byte super-steps, and split * M * N <= cap_elems.
 int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);
 
+// Tiled MFMA projection over many rows (gemm_tc.hip): X is one fp16 plane (x_lo null, no deferred
+// norm), the bf16 weights are converted to fp16 as they are staged.  EPI_STORE_F32, EPI_PARTIAL (with
+// up to kTcMaxRanges K ranges, range z at out_f32 + z * part_stride) and EPI_SWIGLU (fp16 activation).
+// bm: tile rows (64 / 128 / 256); um: units of 32 weight rows per chunk at most; nch: chunks of the
+// units (grid x); ranges, steps: K ranges (grid z) and 64-wide K steps per range.
+struct TcPlan {
+  int bm, um, nch, ranges, steps;
+};
+constexpr int kTcMaxRanges = 8;
+// false if the projection does not suit the kernel; range_cap: elements available for ranges * M * N
+bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p);
+hipError_t launch_gemm_tc(const GemmArgs &a, const TcPlan &p, hipStream_t s, hipEvent_t e0 = nullptr,
+                          hipEvent_t e1 = nullptr);
+
 // Per-head q/k RMSNorm + RoPE, then q to a dense buffer and k/v to the paged cache.
 struct PostSeg {
   int32_t heads;

@@ -126,6 +126,20 @@ class Engine:
         else:
             B.dflash_draft_block(self.ctx, slots, self.feats, self.block, lg)
 
+    def features(self, rows: int) -> torch.Tensor:
+        """The target features of the last verify (rows = its batch * q_len) as fp32 [rows, taps, hidden]:
+        bf16 models hold hi + lo bf16 planes, or one fp16 plane after a verify of F16_MIN_ROWS rows or
+        more; fp32 models one fp32 plane."""
+        nt, H = len(self.cfg.drafter.taps), self.cfg.target.hidden
+        n = rows * nt * H
+        if self.x_planes == 1:
+            f = self.feats[:n].float()
+        elif rows >= B.F16_MIN_ROWS:
+            f = self.feats[:n].view(torch.float16).float()
+        else:
+            f = self.feats[:n].float() + self.feats[n:2 * n].float()
+        return f.view(rows, nt, H)
+
     def status(self):
         B.dflash_device_status(self.ctx)
 

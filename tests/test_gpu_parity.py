@@ -46,11 +46,7 @@ def test_prefill_logits_and_features(name):
     eng.verify([0], toks, P, True, P, logits=logits)
     eng.status()
     g = logits.view(P, -1).cpu().numpy()
-    nf = P * len(cfg.drafter.taps) * cfg.target.hidden
-    gf = eng.feats[:nf].float()
-    if cfg.target.dtype == "bf16":  # the feature planes: high part, then the low part of the same rows
-        gf = gf + eng.feats[nf:2 * nf].float()
-    gf = gf.view(P, len(cfg.drafter.taps), -1).cpu().numpy()
+    gf = eng.features(P).cpu().numpy()
     fol = OracleFollower(cfg, W, request=0)
     z, feats = fol.prefill(prompt)
     e = rel_err_rows(g, z)
@@ -362,6 +358,37 @@ def test_op_linear_sk(dtype, M, N, K):
     assert torch.equal(ys[0], ys[1])
 
 
+@pytest.mark.parametrize("M,N,K,ranges", [(1, 128, 64, 1), (37, 96, 192, 1), (200, 640, 256, 1), (64, 5120, 5120, 8),
+                                          (256, 7168, 5120, 8), (256, 5120, 17408, 8), (256, 34816, 5120, 1),
+                                          (1000, 1024, 1024, 1), (130, 5120, 64, 1), (256, 151936, 5120, 1)])
+def test_op_linear_f16x(M, N, K, ranges):
+    """The tiled fp16 projection kernel of large calls (dflash_op_linear_f16x) against float64 matmul of
+    the same fp16 X and bf16 weights (converted exactly inside the kernel): tile tails in rows and
+    columns, one K step, 27B decode-batch shapes with K ranges (summed here in range order) and the
+    27B LM head.  Sampled rows at the largest shapes."""
+    from speculative_decoding_dflash_amd import binding as Bd
+    rng = np.random.default_rng(M * 31 + N + K)
+    xt = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.float16).cuda()
+    wt = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16).cuda()
+    y = torch.full((ranges * M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    got_r = Bd.dflash_op_linear_f16x(M, N, K, xt, wt, y, ranges)
+    torch.cuda.synchronize()
+    assert 1 <= got_r <= ranges
+    if ranges > 1 and M * N >= 256 * 5120:
+        assert got_r > 1, "a decode-batch shape with few tiles should split K"
+    parts = y.view(ranges, M, N)[:got_r]
+    tot = parts[0].clone()
+    for z in range(1, got_r):
+        tot += parts[z]
+    rows = np.arange(M) if M * N <= 1 << 22 else np.unique(rng.integers(0, M, 24))
+    ref = xt[rows].double().cpu().numpy() @ wt.double().cpu().numpy().T
+    got = tot[rows].cpu().numpy()
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    log(f"  f16x linear {M}x{N}x{K}: {got_r} K ranges, rel err {err:.2e}")
+    assert err < 1e-5
+
+
 @pytest.mark.parametrize("stochastic", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_graph_replay_equals_eager_steps(name, stochastic):
@@ -657,9 +684,8 @@ def test_27b_width_drafter_vs_fp32_drafter():
     g = samp(synth.GREEDY)
     prompt = torch.from_numpy(sw.prompt_ids(V, d.mask_id, P, 0)).to("cuda")
 
-    def feats_of(rows):  # the device's features (high + low planes) of the last verify, [rows, taps, H]
-        n_el = rows * nt * H
-        return (eng.feats[:n_el].float() + eng.feats[n_el:2 * n_el].float()).view(rows, nt, H).cpu().numpy()
+    def feats_of(rows):  # the device's features of the last verify, [rows, taps, H]
+        return eng.features(rows).cpu().numpy()
 
     eng.prefill([0], prompt.view(1, -1), [g])
     ctx = feats_of(P)
