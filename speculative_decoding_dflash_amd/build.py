@@ -24,7 +24,9 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Xclang", "-t
           "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 SOURCES = {
     "gemm.hip": [],
-    "gemm_tc.hip": [],
+    # accumulators of the MFMA loops in VGPRs: without this the 256-row tiles' loop body shuffled its
+    # accumulators between AGPRs and VGPRs around every MFMA
+    "gemm_tc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attention.hip": [],
     "rows.hip": [],
     "sampler.hip": [],

@@ -37,8 +37,13 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBK = 64;        // K per LDS step
-constexpr int kLDK = kBK + 8;  // LDS row stride in halfs (144 bytes: conflict-free 16-byte fragment reads)
+constexpr int kBK = 64;  // K per LDS step: one 128-byte LDS row per tile row
+
+// LDS tiles hold 128-byte rows of eight 16-byte chunks; chunk c of row r sits at chunk c ^ sw(r).  With
+// that swizzle the 16-byte fragment reads (16 rows, one chunk each) and the staging writes (8 lanes per
+// row) touch every bank once per 8 lanes (32 banks) and per 16 lanes (64 banks).
+DF_DEVICE int sw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+DF_DEVICE int lds_off(int r, int c) { return r * kBK + ((c ^ sw(r)) << 3); }
 
 DF_DEVICE u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
@@ -62,7 +67,7 @@ DF_DEVICE int tc_x_src(const GemmArgs &a, int m) {
   return (r / a.x_take) * a.x_stride + a.x_off + r % a.x_take;
 }
 
-template <int BM, int UM>
+template <int BM, int UM, int STG>
 __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArgs a, int nch, int steps) {
   constexpr int WC = BM == 256 ? 1 : (BM == 128 ? 2 : 4);  // waves across the tile's columns
   constexpr int BN = UM * 32;                              // weight rows of a full chunk
@@ -70,19 +75,31 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
   constexpr int CA = BM / 32, CB = UM;                     // 16-byte loads per thread and K step
   static_assert(BM == 64 * (4 / WC), "each wave holds 64 rows");
   static_assert(NJ * WC * 16 == BN && NJ % 2 == 0, "a wave holds whole units");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kLDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBK];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int wr = wave / WC, wc = wave % WC;
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int units = swiglu ? a.N / 16 : a.N / 32;
-  const int ch = blockIdx.x;
+  // XCD-aware order: work-group b runs on XCD b % 8 (round-robin dispatch); each XCD takes a contiguous
+  // range of the (K range, row tile, chunk) items, chunk fastest, so that the work-groups sharing an
+  // L2 share X row tiles.
+  int ch, ty, tz;
+  {
+    const int rt = gridDim.y, T = nch * rt * gridDim.z;
+    const int b = blockIdx.x + nch * (blockIdx.y + rt * blockIdx.z);
+    const int per = T / 8, rem = T % 8, xcd = b % 8;
+    const int l = xcd * per + min(xcd, rem) + b / 8;
+    ch = l % nch;
+    ty = (l / nch) % rt;
+    tz = l / (nch * rt);
+  }
   const int u0 = (int)((long)units * ch / nch), u1 = (int)((long)units * (ch + 1) / nch);
   const int nrows = (u1 - u0) * 32;  // weight rows of this chunk (<= BN)
-  const int m0 = blockIdx.y * BM;
+  const int m0 = ty * BM;
   const int nk = a.K / kBK;
-  const int kt0 = blockIdx.z * steps, kt1 = min(nk, kt0 + steps);
+  const int kt0 = tz * steps, kt1 = min(nk, kt0 + steps);
 
   // this thread's 16-byte chunks of a K step: chunk c = tid + 256 i -> tile row c / 8, halfs 8 (c % 8) ..
   const uint16_t *pa[CA], *pb[CB];
@@ -116,7 +133,10 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[2][CA], rb[2][CB];
+  // STG register stages (2 or 3): the loads of step k + STG are issued while step k is multiplied out of
+  // LDS buffer (k - k0) % 2 and steps k + 1 .. k + STG - 1 are in flight; the stage index of step k is
+  // (k - k0) % STG, a template constant in the unrolled loop so that the stages stay in registers.
+  u32x4 ra[STG][CA], rb[STG][CB];
   auto load = [&](int st, int kt) {
     const int k = min(kt, kt1 - 1) * kBK;
 #pragma unroll
@@ -128,46 +148,50 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(&sA[buf][(c >> 3) * kLDK + (c & 7) * 8]) = ra[st][i];
+      *reinterpret_cast<u32x4 *>(&sA[buf][lds_off(c >> 3, c & 7)]) = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(&sB[buf][(c >> 3) * kLDK + (c & 7) * 8]) = bf8_to_h8(rb[st][i]);
+      *reinterpret_cast<u32x4 *>(&sB[buf][lds_off(c >> 3, c & 7)]) = bf8_to_h8(rb[st][i]);
     }
   };
-  load(0, kt0);
-  load(1, kt0 + 1);
-  store(0, 0);
-  __syncthreads();
-  // One K step out of LDS buffer BUF; the stage and buffer indices are template constants so that the
-  // register stages stay in registers.
-  auto kstep = [&](int kt, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    load(buf, kt + 2);
+  auto mult = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < kBK / 32; ++s) {
       u32x4 fa[4], fb[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][(wr * 64 + 16 * i + r16) * kLDK + 32 * s + 8 * g]);
+        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][lds_off(wr * 64 + 16 * i + r16, 4 * s + g)]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        fb[j] = *reinterpret_cast<const u32x4 *>(&sB[buf][((wc * NJ + j) * 16 + r16) * kLDK + 32 * s + 8 * g]);
+        fb[j] = *reinterpret_cast<const u32x4 *>(&sB[buf][lds_off((wc * NJ + j) * 16 + r16, 4 * s + g)]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mma(acc[i][j], fa[i], fb[j]);
     }
-    if (kt + 1 < kt1) store(1 - buf, 1 - buf);
+  };
+#pragma unroll
+  for (int st = 0; st < STG; ++st) load(st, kt0 + st);
+  store(0, 0);
+  __syncthreads();
+  auto kstep = [&](int kt, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const int buf = (kt - kt0) & 1;
+    load(st, kt + STG);
+    mult(buf);
+    if (kt + 1 < kt1) store((st + 1) % STG, buf ^ 1);
     __syncthreads();
   };
   int kt = kt0;
-  for (; kt + 1 < kt1; kt += 2) {
+  for (; kt + STG <= kt1; kt += STG) {
     kstep(kt, std::integral_constant<int, 0>{});
     kstep(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (STG == 3) kstep(kt + 2, std::integral_constant<int, 2>{});
   }
   if (kt < kt1) kstep(kt, std::integral_constant<int, 0>{});
+  if (kt + 1 < kt1) kstep(kt + 1, std::integral_constant<int, 1>{});
 
   // acc[i][j][r] = Y[row m0 + 64 wr + 16 i + 4 g + r][weight row 32 u0 + 16 (wc NJ + j) + r16]
   if (swiglu) {
@@ -189,7 +213,7 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
     }
     return;
   }
-  float *out = a.out_f32 + (size_t)blockIdx.z * a.part_stride;
+  float *out = a.out_f32 + (size_t)tz * a.part_stride;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int lr = (wc * NJ + j) * 16;
@@ -236,7 +260,8 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   const int env_bm = env_int("DFLASH_TC_BM", 0);
   int bm = a.M <= 64 ? 64 : (a.M <= 128 ? 128 : 256);
   if (env_bm == 64 || env_bm == 128 || env_bm == 256) bm = env_bm;
-  const int um = bm == 256 ? 5 : 4;
+  const int env_um = env_int("DFLASH_TC_UM", 0);
+  const int um = bm == 256 && env_um != 4 ? 5 : 4;
   const int units = swiglu ? a.N / 16 : a.N / 32;
   const int rt = (a.M + bm - 1) / bm, nk = a.K / kBK;
   const int slots = cu_count() * (bm == 256 ? 1 : 2);
@@ -259,7 +284,8 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
       const int wgs = nch * rt * s;
       const int rounds = (wgs + slots - 1) / slots;
       const int umax = (units + nch - 1) / nch;
-      const double per = umax * steps * std::max(mfma_us, mem_us) + 1.5;
+      // a K step also stages BM X rows (from L2), worth about bm / 64 units of weight streaming
+      const double per = (umax + bm / 64.0) * steps * std::max(mfma_us, mem_us) + 1.5;
       const double t = rounds * per + (s > 1 ? (double)s * a.M * a.N * 8 / 5e12 * 1e6 : 0.0);
       if (t < best - 1e-9) {
         best = t;
@@ -272,12 +298,25 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   return true;
 }
 
+template <int STG>
+static void launch_stg(const GemmArgs &a, const TcPlan &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 block(256);
+  if (p.bm == 256) {
+    if (p.um == 5) hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    else hipExtLaunchKernelGGL((gemm_tc_kernel<256, 4, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  } else if (p.bm == 128) {
+    hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  } else {
+    hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  }
+}
+
 hipError_t launch_gemm_tc(const GemmArgs &a, const TcPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (p.ranges > 1 && a.epi != EPI_PARTIAL) return hipErrorInvalidValue;
-  const dim3 grid(p.nch, (a.M + p.bm - 1) / p.bm, p.ranges), block(256);
-  if (p.bm == 256) hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
-  else if (p.bm == 128) hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
-  else hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+  const dim3 grid(p.nch, (a.M + p.bm - 1) / p.bm, p.ranges);
+  static const int stg = env_int("DFLASH_TC_STG", 2) == 3 ? 3 : 2;
+  if (stg == 3) launch_stg<3>(a, p, grid, s, e0, e1);
+  else launch_stg<2>(a, p, grid, s, e0, e1);
   return hipGetLastError();
 }
 
