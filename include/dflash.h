@@ -36,12 +36,10 @@
  *     and fp32 for DFLASH_F32 models.  Page ids are shared by the target pool (layers 0..L_t-1) and the
  *     drafter pool (layers 0..L_d-1): a slot's block table maps its position p to page
  *     table[p / page_tokens].
- *   - Target features (verify output, draft input) of DFLASH_BF16 models are two bf16 planes of the
- *     same shape, hi = bf16(h) then lo = bf16(h - hi), so that hi + lo carries the fp32 residual
- *     stream to about 16 significant bits -- except after a verify of DFLASH_F16_MIN_ROWS or more
- *     rows (batch * q_len), which writes one IEEE fp16 plane (the first plane's place; 11 significant
- *     bits, the precision of that call's projection inputs); DFLASH_F32 models hold one fp32 plane.
- *     The buffer is sized for two planes in every case.
+ *   - Activations of DFLASH_BF16 models that meet a weight matrix or the attention -- projection
+ *     inputs, target features (verify output, draft input), q and the KV cache -- are IEEE fp16 (11
+ *     significant bits where bf16 keeps 8; magnitudes saturate at 65504); the bf16 weights enter those
+ *     products converted to fp16 (exactly for |w| in [2^-14, 65504]).  DFLASH_F32 models keep fp32.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -58,9 +56,9 @@ extern "C" {
 #define DFLASH_MAX_BATCH 64
 #define DFLASH_MAX_BLOCK 16
 #define DFLASH_MAX_TOPK 256
-/* Calls of DFLASH_BF16 models over at least this many rows hold their projection inputs (and write their
- * features) as one fp16 plane and run the tiled fp16 projection kernel (dflash_op_linear_f16x); smaller
- * calls hold two bf16 planes. */
+/* Calls of DFLASH_BF16 models over at least this many rows run their projections on the tiled MFMA kernel
+ * (dflash_op_linear_f16x) and apply every RMSNorm at once; smaller calls stream the weights through the
+ * row-chunked kernels (dflash_op_linear) with the norms deferred into the next projection. */
 #define DFLASH_F16_MIN_ROWS 32
 
 typedef enum {
@@ -178,9 +176,8 @@ dflash_status dflash_kv_free(dflash_ctx *ctx, int32_t slot);
  * length are overwritten by later blocks; rollback is a length update).
  * Outputs: d_logits fp32 [batch][n_logit_rows][vocab] for the last n_logit_rows rows of each block;
  * d_feats: the residual stream after each tapped layer, for KV injection by the next
- * dflash_draft_block -- [2][batch][q_len][n_taps][hidden] bf16 (high plane, then low plane) for
- * DFLASH_BF16 models ([batch][q_len][n_taps][hidden] fp16 in the first plane's place when batch * q_len
- * >= DFLASH_F16_MIN_ROWS), [batch][q_len][n_taps][hidden] fp32 for DFLASH_F32 models. */
+ * dflash_draft_block -- [batch][q_len][n_taps][hidden], fp16 for DFLASH_BF16 models and fp32 for
+ * DFLASH_F32 models. */
 dflash_status dflash_verify_block(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
                                   const int32_t *d_tokens, int32_t q_len, int32_t new_sequence,
                                   int32_t n_logit_rows, float *d_logits, void *d_feats);
@@ -242,17 +239,16 @@ dflash_status dflash_accept_resample_q(dflash_ctx *ctx, hipStream_t stream, int3
                                        int32_t *d_out, int32_t *d_n_out, int32_t *d_cand_ids, float *d_cand_p);
 
 /* Operator-level access to the projection kernel used by every step (test and measurement access):
- * d_y[m][n] = sum_k d_x[m][k] * d_w[n][k] (fp32 output) for m < M, with d_x [M][K] and d_w [N][K] in
- * `dtype` (dflash_dtype), on the same code path as the model's projections.  N must be a multiple of
- * 16 and K of 32 (bf16) or 16 (fp32).  Asynchronous on `stream`; needs no context. */
+ * d_y[m][n] = sum_k d_x[m][k] * d_w[n][k] (fp32 output) for m < M, with d_w [N][K] in `dtype`
+ * (dflash_dtype) and d_x [M][K] in the model's activation type (fp16 for DFLASH_BF16, fp32 for
+ * DFLASH_F32), on the row-chunked kernels of the model's projections.  N must be a multiple of 16 and K
+ * of 32 (bf16) or 16 (fp32).  Asynchronous on `stream`; needs no context. */
 dflash_status dflash_op_linear(hipStream_t stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void *d_x,
                                const void *d_w, float *d_y);
 
 /* The projection kernel of calls over many rows (decode batches of 32 or more rows, prefill) on its
- * own: d_y = d_x d_w^T with d_x [M][K] in fp16 (IEEE binary16, one plane), d_w [N][K] in bf16 (converted
- * to fp16 inside the kernel, exactly for |w| in [2^-14, 65504]), fp32 accumulation on the matrix cores.
- * It is the arithmetic of bf16 models' large calls (the projection inputs are rounded once to fp16's 11
- * significant bits; see the readings of the pages for why more than bf16's 8 are kept).  M >= 1,
+ * own: d_y = d_x d_w^T with d_x [M][K] in fp16, d_w [N][K] in bf16 (converted to fp16 inside the
+ * kernel, exactly for |w| in [2^-14, 65504]), fp32 accumulation on the matrix cores.  M >= 1,
  * N a multiple of 32, K a multiple of 64.  The launch may cut K into up to max_ranges ranges (1 <=
  * max_ranges <= 8): range z writes its fp32 sums to d_y + z * M * N (d_y holds max_ranges * M * N
  * floats) and *ranges (host memory; may be null when max_ranges is 1) receives the count; the product

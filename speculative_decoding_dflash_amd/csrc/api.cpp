@@ -37,7 +37,6 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int esize(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 // Planes of a projection input (X operand): bf16 models hold a high and a low bf16 plane (store_x).
-int xplanes(const dflash_model_cfg *c) { return c->dtype == DFLASH_BF16 ? 2 : 1; }
 
 constexpr int kAttnSplitMax = 64;
 constexpr int kAttnWgTarget = 512;  // work-groups a batched decode attention call aims at
@@ -46,13 +45,14 @@ constexpr int kAttnWholeBlockPages = 256;  // key pages from which a batched cal
 constexpr int kMaxKSplit = 8;
 // Calls of a bf16 model with at least this many rows run in x16 mode (dflash_ctx::x16).
 constexpr int kTcMinRows = DFLASH_F16_MIN_ROWS;
+constexpr size_t kTcRangeRows = 256;  // rows for which the workspace holds K-range partials
 constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized attention call
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, mbr, att_o, att_ml, dlogits,
+  size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, tcr, att_o, att_ml, dlogits,
       cid, cp, cn, skey, sidx, total;
-  size_t part_elems, att_rows, mbr_elems;
+  size_t part_elems, att_rows, tcr_elems;
   int ss_ld, sk_tiles;
 };
 
@@ -83,23 +83,23 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   // per-32-column sums of squares of the rows awaiting RMSNorm: [R][ss_ld]
   L.ss_ld = (int)((H / 32 + 3) / 4 * 4);
   L.ss = take(sizeof(float) * L.ss_ld * R);
-  // projection inputs: xplanes planes of R rows each (the low plane follows the high one)
-  const size_t np = xplanes(c);
-  L.xn = take(np * es * R * H);
-  L.qbuf = take(es * R * QD);  // fp16 (bf16 models) or fp32 q
-  L.attn = take(np * es * R * QD);
-  L.ffn = take(np * es * R * F);
+  // projection inputs, q: the activation type (fp16 for bf16 models, fp32 otherwise)
+  L.xn = take(es * R * H);
+  L.qbuf = take(es * R * QD);
+  L.attn = take(es * R * QD);
+  L.ffn = take(es * R * F);
   // fp32 K-range partials of one projection: up to kMaxKSplit ranges of a single row chunk, or one
   // range over all rows
   const size_t part_cols = std::max({QD + 2 * KD, (size_t)d->layers * 2 * KD, H});
   L.part_elems = std::max(R, (size_t)kMaxKSplit * kGemmMaxRows) * part_cols;
   L.part = take(sizeof(float) * L.part_elems);
   L.skp = take(sizeof(float) * kSkMaxWg * 2 * kSkTileElems);  // stream-K partial tiles
-  // raw K-range sums of a decode-batch projection (kMbMinRows .. kMbMaxRows rows): room for
-  // kMbMaxSplit ranges of the widest hidden-size output (the launcher uses fewer ranges otherwise)
-  const size_t rdec = std::min<size_t>((size_t)cap->max_slots * B, kMbMaxRows);
-  L.mbr_elems = rdec >= (size_t)kMbMinRows ? kMbMaxSplit * rdec * part_cols : 0;
-  L.mbr = take(sizeof(float) * std::max<size_t>(L.mbr_elems, 1));
+  // K-range partials of a tiled fp16 projection over a decode batch (kTcMinRows .. kTcRangeRows rows):
+  // room for kTcMaxRanges ranges of the widest partial output (the planner uses fewer ranges, or one
+  // range in L.part, where they do not fit)
+  const size_t rdec = std::min<size_t>((size_t)cap->max_slots * B, kTcRangeRows);
+  L.tcr_elems = rdec >= (size_t)kTcMinRows ? kTcMaxRanges * rdec * part_cols : 0;
+  L.tcr = take(sizeof(float) * std::max<size_t>(L.tcr_elems, 1));
   L.att_rows = (size_t)cap->max_slots * B;
   L.att_o = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * c->head_dim);
   L.att_ml = take(sizeof(float) * L.att_rows * c->q_heads * kAttnSplitMax * 2);
@@ -162,26 +162,16 @@ struct dflash_ctx {
   int last_nd = -1;
   std::vector<int32_t> last_slots;
   bool verified = false;
-  // Set while a prefill (a verify that starts sequences) runs: its projections may take the tiled
-  // large-M kernel.  Every other call keeps the row-chunked kernels, whose result for a row does not
-  // depend on how many rows share the launch, so a decode step computes the same bits whether it is
-  // issued eagerly or replayed from a graph captured at another row count.
-  bool tiled = false;
-  // Set while a call of a bf16 model runs its projections with one fp16 plane per projection input
-  // (x16 mode: kTcMinRows rows or more, the tiled fp16 kernel of gemm_tc.hip).  In that mode the
-  // producers of projection inputs (norms, attention output, SwiGLU, feature taps) store fp16 (their low
-  // plane pointers are null), every RMSNorm is applied at once (no deferred 1/rms), and the residual
-  // projections write K-range partial sums that norm_kernel adds to the residual and normalises.
+  // Set while a call of a bf16 model over kTcMinRows rows or more runs (x16 mode): its projections take
+  // the tiled fp16 kernel of gemm_tc.hip, every RMSNorm is applied at once (no deferred 1/rms), and the
+  // residual projections write K-range partial sums that norm_kernel adds to the residual and
+  // normalises.  Smaller calls keep the row-chunked kernels.
   bool x16 = false;
-  // The features written by the last verify are fp16 (it ran in x16 mode); the next draft injects them
-  // in that mode.
-  bool feat16 = false;
   // measurement: the projection launches issued while profiling is on, kept for replay
   bool profiling = false;
   struct Rec {
     GemmArgs a;
     int rows;
-    bool tiled;
     bool x16;
     TcPlan plan;
   };
@@ -200,20 +190,6 @@ struct dflash_ctx {
     return r;
   }
   int dt() const { return cfg.dtype == DFLASH_BF16 ? 0 : 1; }
-  // Low plane of the projection-input buffer at workspace offset `off` whose planes hold `plane_elems`
-  // elements (null for fp32 models).
-  void *xlo(size_t off, size_t plane_elems) const {
-    return cfg.dtype == DFLASH_BF16 && !x16 ? (void *)(ws + off + plane_elems * es()) : nullptr;
-  }
-  void *xn_lo() const { return xlo(L.xn, (size_t)cap.max_rows * cfg.hidden); }
-  void *attn_lo() const { return xlo(L.attn, (size_t)cap.max_rows * cfg.q_heads * cfg.head_dim); }
-  void *ffn_lo() const { return xlo(L.ffn, (size_t)cap.max_rows * cfg.ffn); }
-  // Low plane of caller features for `rows` rows (bf16 models: [2][rows][n_taps * hidden]).
-  void *feats_lo(const void *feats, int rows) const {
-    return cfg.dtype == DFLASH_BF16 && !x16
-               ? (void *)((const char *)feats + (size_t)rows * dcfg.n_taps * cfg.hidden * es())
-               : nullptr;
-  }
   int rope_rows() const { return cap.max_pages_per_seq * cap.page_tokens; }
   int es() const { return esize(&cfg); }
   void *tlayer(int l) const { return tkv + (size_t)l * layer_elems * es(); }
@@ -240,36 +216,16 @@ GemmArgs gemm_base(const void *x, int ldx, int M, int N, int K, int epi) {
   return a;
 }
 
-// Run a GEMM over R rows in chunks of kGemmMaxRows.  `a.x` points at row 0; input rows advance by ldx.
-// tiled: the call may instead run all R rows at once on the tiled large-M kernel when the shape suits it.
-// e0 / e1 (may be null) time the first chunk's start and the last chunk's end.
-dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_t s, hipEvent_t e0 = nullptr,
+// Run a GEMM over R rows in chunks of kGemmMaxRows on the row-chunked kernels.  `a.x` points at row 0;
+// input rows advance by ldx.  e0 / e1 (may be null) time the first chunk's start and the last chunk's end.
+dflash_status run_gemm(int es, int dt, GemmArgs a, int R, hipStream_t s, hipEvent_t e0 = nullptr,
                        hipEvent_t e1 = nullptr) {
-  {
-    GemmArgs b = a;
-    b.M = R;
-    b.row_off = 0;
-    if (tiled && gemm_mm_ok(b, dt)) {
-      HIP_OK(launch_gemm(b, dt, s, e0, e1));
-      return DFLASH_OK;
-    }
-    // decode batches (and prefills too short for the tiled kernel): all rows in one launch instead of
-    // row chunks that each stream the weights
-    if (gemm_mb_ok(b, dt)) {
-      HIP_OK(launch_gemm_mb(b, s, e0, e1));
-      return DFLASH_OK;
-    }
-  }
-  // row chunks whose X operand (both planes) fits the row-chunked kernels
-  const int cr = a.x_lo ? kGemmMaxRows / 2 : kGemmMaxRows;
-  const char *x0 = (const char *)a.x, *xl0 = (const char *)a.x_lo;
+  const int cr = kGemmMaxRows;
+  const char *x0 = (const char *)a.x;
   for (int r0 = 0; r0 < R; r0 += cr) {
     GemmArgs b = a;
     b.M = std::min(cr, R - r0);
-    if (!a.x_take) {  // a row selection addresses X by global row (row_off) from the unmoved x
-      b.x = x0 + (size_t)r0 * a.ldx * es;
-      b.x_lo = xl0 ? xl0 + (size_t)r0 * a.ldx * es : nullptr;
-    }
+    if (!a.x_take) b.x = x0 + (size_t)r0 * a.ldx * es;  // a row selection addresses X by global row
     b.row_off = r0;
     HIP_OK(launch_gemm(b, dt, s, r0 == 0 ? e0 : nullptr, r0 + cr >= R ? e1 : nullptr));
   }
@@ -281,7 +237,6 @@ dflash_status run_gemm(int es, int dt, GemmArgs a, int R, bool tiled, hipStream_
 dflash_status plan_tc(GemmArgs &a, int R, int64_t range_cap, TcPlan *p) {
   a.M = R;
   a.row_off = 0;
-  a.x_lo = nullptr;
   if (!gemm_tc_plan(a, range_cap, p))
     return fail(DFLASH_E_INVAL, "projection %d x %d x %d (epilogue %d) does not suit the fp16 tiled kernel", R, a.N, a.K,
                 a.epi);
@@ -290,7 +245,7 @@ dflash_status plan_tc(GemmArgs &a, int R, int64_t range_cap, TcPlan *p) {
 
 dflash_status launch_tc(dflash_ctx *c, GemmArgs a, int R, const TcPlan &p, hipStream_t s) {
   if (a.epi == EPI_PARTIAL) a.part_stride = (int64_t)R * a.N;
-  if (c->profiling) c->recorded.push_back({a, R, false, true, p});
+  if (c->profiling) c->recorded.push_back({a, R, true, p});
   HIP_OK(launch_gemm_tc(a, p, s));
   return DFLASH_OK;
 }
@@ -307,26 +262,20 @@ dflash_status run_gemm(dflash_ctx *c, GemmArgs a, int R, hipStream_t s) {
   a.sk_cnt = c->wsp<int32_t>(c->L.skc);
   a.sk_max_wg = kSkMaxWg;
   a.sk_max_tiles = c->L.sk_tiles;
-  a.mb_raw = c->L.mbr_elems ? c->wsp<float>(c->L.mbr) : nullptr;
-  a.mb_raw_cap = (int64_t)c->L.mbr_elems;
-  if (c->profiling) c->recorded.push_back({a, R, c->tiled, false, TcPlan{}});
-  return run_gemm(c->es(), c->dt(), a, R, c->tiled, s);
+  if (c->profiling) c->recorded.push_back({a, R, false, TcPlan{}});
+  return run_gemm(c->es(), c->dt(), a, R, s);
 }
 
-// A projection whose K ranges write fp32 partial slices [range][R][N] into the partial buffer; the
-// consumer (norm_kernel, qkv_post_kernel) adds the *n_part slices in order.
 // A projection whose K ranges leave fp32 partial slices [range][R][N] for the consumer (qkv_post_kernel,
-// norm_kernel) to add in order: *src, *stride and *n_part describe them.  Row chunks (R <= 16) use the
-// workspace's partial buffer; a decode batch that the tiled kernel splits over K hands its ranges over
-// as they are (each already scaled by the deferred norm's 1/rms), which saves a reduce launch.
+// norm_kernel) to add in order: *src, *stride and *n_part describe them.
 dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *n_part, const float **src,
                           int64_t *stride) {
   a.epi = EPI_PARTIAL;
-  if (c->x16) {  // several K ranges go to the decode-batch buffer, one range to L.part
+  if (c->x16) {  // several K ranges go to the range buffer, one range to L.part
     TcPlan p;
-    dflash_status st = plan_tc(a, R, (int64_t)c->L.mbr_elems, &p);
+    dflash_status st = plan_tc(a, R, (int64_t)c->L.tcr_elems, &p);
     if (st != DFLASH_OK) return st;
-    a.out_f32 = p.ranges > 1 ? c->wsp<float>(c->L.mbr) : c->wsp<float>(c->L.part);
+    a.out_f32 = p.ranges > 1 ? c->wsp<float>(c->L.tcr) : c->wsp<float>(c->L.part);
     a.ld_out = a.N;
     if ((st = launch_tc(c, a, R, p, s)) != DFLASH_OK) return st;
     *n_part = p.ranges;
@@ -336,28 +285,11 @@ dflash_status run_partial(dflash_ctx *c, GemmArgs a, int R, hipStream_t s, int *
   }
   a.out_f32 = c->wsp<float>(c->L.part);
   a.ld_out = a.N;
-  a.ksplit = R <= kGemmMaxRows / xplanes(&c->cfg)
-                 ? std::min(kMaxKSplit, gemm_ksplit(R, a.N, a.K, c->dt(), c->L.part_elems))
-                 : 1;
+  a.ksplit = R <= kGemmMaxRows ? std::min(kMaxKSplit, gemm_ksplit(R, a.N, a.K, c->dt(), c->L.part_elems)) : 1;
   a.part_stride = (int64_t)R * a.N;
   *n_part = a.ksplit;
   *src = a.out_f32;
   *stride = a.part_stride;
-  if (!c->tiled && c->L.mbr_elems) {
-    GemmArgs b = a;
-    b.M = R;
-    b.row_off = 0;
-    b.mb_raw = c->wsp<float>(c->L.mbr);
-    b.mb_raw_cap = (int64_t)c->L.mbr_elems;
-    if (gemm_mb_ok(b, c->dt())) {
-      const int ks = gemm_mb_slices(b);
-      if (ks > 1) {
-        a.mb_direct = 1;
-        *n_part = ks;
-        *src = b.mb_raw;
-      }
-    }
-  }
   return run_gemm(c, a, R, s);
 }
 
@@ -380,7 +312,6 @@ dflash_status prep_norm(dflash_ctx *c, int R, const void *gain, hipStream_t s) {
   n.eps = c->cfg.rms_eps;
   n.hidden = c->cfg.hidden;
   n.out = c->wsp<void>(c->L.xn);
-  n.out_lo = c->xn_lo();
   n.ld_out = c->cfg.hidden;
   n.n_rows = R;
   n.take = R;
@@ -404,7 +335,7 @@ void with_norm(dflash_ctx *c, GemmArgs &a, int ss_n) {
 
 // A hidden-width projection whose output is added to the residual (resid may be null: the output is
 // the new row) and then RMS-normalised with the deferred scheme; returns ss_n for the consumer.
-dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, void *feat, void *feat_lo, int ld_feat,
+dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, void *feat, int ld_feat,
                              const NextNorm &nx, hipStream_t s, int *ss_n) {
   if (c->x16) {  // K-range partial sums, then one pass per row: residual add, feature tap, RMSNorm
     int np = 1;
@@ -421,13 +352,11 @@ dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, voi
     n.ld_part = a.N;
     n.part_stride = pstride;
     n.feat = feat;
-    n.feat_lo = nullptr;
     n.ld_feat = ld_feat;
     n.gain = (const float *)nx.gain;
     n.eps = c->cfg.rms_eps;
     n.hidden = c->cfg.hidden;
     n.out = c->wsp<void>(c->L.xn);
-    n.out_lo = nullptr;
     n.ld_out = c->cfg.hidden;
     n.n_rows = R;
     n.take = nx.take;
@@ -441,11 +370,9 @@ dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, voi
   a.resid = resid;
   a.ld_resid = c->cfg.hidden;
   a.feat = feat;
-  a.feat_lo = feat ? feat_lo : nullptr;
   a.ld_feat = ld_feat;
   a.gain = (const float *)nx.gain;
   a.xg = c->wsp<void>(c->L.xn);
-  a.xg_lo = c->xn_lo();
   a.ld_xg = c->cfg.hidden;
   a.ss_out = c->wsp<float>(c->L.ss);
   a.ss_out_ld = c->L.ss_ld;
@@ -536,7 +463,6 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.part_o = c->wsp<float>(c->L.att_o);
   a.part_ml = c->wsp<float>(c->L.att_ml);
   a.out = c->wsp<void>(c->L.attn);
-  a.out_lo = c->attn_lo();
   a.ldo = m.q_heads * m.head_dim;
   a.err = c->err();
   for (int i = 0; i < n_seq; ++i) a.seq_slot[i] = slots[i];
@@ -562,7 +488,7 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
 // logits); feat: optional tap of the layer's output.  Returns the ss_n of the deferred next norm.
 dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_layer, const Rows &rows,
                         const int32_t *slots, int n_seq, int q_len, int attn_mode, int ctx_bound, void *feat,
-                        void *feat_lo, int ld_feat, const NextNorm &next, int *ss_n, hipStream_t s) {
+                        int ld_feat, const NextNorm &next, int *ss_n, hipStream_t s) {
   const dflash_model_cfg &m = c->cfg;
   const int R = n_seq * q_len, H = m.hidden, QD = m.q_heads * m.head_dim, KD = m.kv_heads * m.head_dim, F = m.ffn;
   float *x = c->wsp<float>(c->L.x);
@@ -571,7 +497,6 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   bool fused = false;
   {
     GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_PARTIAL);
-    a.x_lo = c->xn_lo();
     a.nseg = 3;
     a.seg[0] = GemmSeg{w.wq, QD};
     a.seg[1] = GemmSeg{w.wk, KD};
@@ -611,30 +536,26 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     return st;
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.attn), QD, R, H, QD, EPI_RESID_NORM);
-    a.x_lo = c->attn_lo();
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.wo, H};
-    if ((st = run_resid_norm(c, a, R, x, nullptr, nullptr, 0, all_rows(w.ffn_norm, R), s, ss_n)) != DFLASH_OK)
+    if ((st = run_resid_norm(c, a, R, x, nullptr, 0, all_rows(w.ffn_norm, R), s, ss_n)) != DFLASH_OK)
       return st;
   }
   {
     GemmArgs a = gemm_base(xn, H, R, F, H, EPI_SWIGLU);
-    a.x_lo = c->xn_lo();
     a.nseg = 2;
     a.seg[0] = GemmSeg{w.w_gate, F};
     a.seg[1] = GemmSeg{w.w_up, F};
     a.out_act = c->wsp<void>(c->L.ffn);
-    a.out_act_lo = c->ffn_lo();
     a.ld_out = F;
     with_norm(c, a, *ss_n);
     if ((st = run_gemm(c, a, R, s)) != DFLASH_OK) return st;
   }
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.ffn), F, R, H, F, EPI_RESID_NORM);
-    a.x_lo = c->ffn_lo();
     a.nseg = 1;
     a.seg[0] = GemmSeg{w.w_down, H};
-    if ((st = run_resid_norm(c, a, R, x, feat, feat_lo, ld_feat, next, s, ss_n)) != DFLASH_OK) return st;
+    if ((st = run_resid_norm(c, a, R, x, feat, ld_feat, next, s, ss_n)) != DFLASH_OK) return st;
   }
   return DFLASH_OK;
 }
@@ -896,27 +817,18 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
   const int ctx_bound = c->max_ctx(slots, batch);
   const int ld_feat = c->dcfg.n_taps * H;
   const int nl = n_logit_rows;
-  struct TiledScope {  // a prefill's projections may take the tiled kernel; cleared on every exit
-    dflash_ctx *c;
-    ~TiledScope() { c->tiled = false; }
-  } tiled_scope{c};
-  c->tiled = new_sequence != 0;
   for (int l = 0; l < m.layers; ++l) {
-    void *feat = nullptr, *feat_lo = nullptr;
+    void *feat = nullptr;
     for (int t = 0; t < c->dcfg.n_taps; ++t)
-      if (c->dcfg.taps[t] == l && d_feats) {
-        feat = (char *)d_feats + (size_t)t * H * c->es();
-        feat_lo = c->feats_lo(feat, R);
-      }
+      if (c->dcfg.taps[t] == l && d_feats) feat = (char *)d_feats + (size_t)t * H * c->es();
     // after the last layer: the final norm over the last nl rows of every sequence, packed
     const NextNorm next = l + 1 < m.layers ? all_rows(c->tl[l + 1].attn_norm, R)
                                            : NextNorm{c->final_norm, nl, q_len, q_len - nl};
-    st = run_layer(c, c->tl[l], c->tlayer(l), rows, slots, batch, q_len, 0, ctx_bound, feat, feat_lo, ld_feat, next,
+    st = run_layer(c, c->tl[l], c->tlayer(l), rows, slots, batch, q_len, 0, ctx_bound, feat, ld_feat, next,
                    &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nl, m.vocab, H, EPI_STORE_F32);
-  a.x_lo = c->xn_lo();
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
   with_norm(c, a, ss_n);
@@ -926,7 +838,6 @@ dflash_status dflash_verify_block(dflash_ctx *c, hipStream_t s, int32_t batch, c
 
   for (int b = 0; b < batch; ++b)
     if (new_sequence) c->prefilled[slots[b]] = 1;
-  c->feat16 = c->x16;
   c->last_qlen = q_len;
   c->last_nlogit = nl;
   c->last_nd = -1;
@@ -1046,20 +957,13 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   p.err = c->err();
   HIP_OK(launch_prep(p, s));
   int ss_n = 1;
-  // long injections (after a prefill) take the tiled large-M kernel; a decode step's (batch x B rows)
-  // keep the row-count-independent kernels
-  struct TiledScope {
+  struct ModeScope {  // x16 mode for this call's projections; cleared on every exit
     dflash_ctx *c;
-    ~TiledScope() {
-      c->tiled = false;
-      c->x16 = false;
-    }
-  } tiled_scope{c};
-  c->tiled = Ri > c->cap.max_slots * B;
-  c->x16 = c->feat16;  // the injection runs in the mode its features were written in
+    ~ModeScope() { c->x16 = false; }
+  } mode_scope{c};
+  c->x16 = m.dtype == DFLASH_BF16 && Ri >= kTcMinRows;
   {
     GemmArgs a = gemm_base(d_feats, dc.n_taps * H, Ri, H, dc.n_taps * H, EPI_RESID_NORM);
-    a.x_lo = c->feats_lo(d_feats, batch * Q);
     if (skip) {  // the last L of every Q feature rows
       a.x_take = L;
       a.x_stride = Q;
@@ -1067,13 +971,12 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
     }
     a.nseg = 1;
     a.seg[0] = GemmSeg{c->fc, H};
-    if ((st = run_resid_norm(c, a, Ri, nullptr, nullptr, nullptr, 0, all_rows(c->hidden_norm, Ri), s, &ss_n)) !=
+    if ((st = run_resid_norm(c, a, Ri, nullptr, nullptr, 0, all_rows(c->hidden_norm, Ri), s, &ss_n)) !=
         DFLASH_OK)
       return st;
   }
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_PARTIAL);
-    a.x_lo = c->xn_lo();
     a.nseg = 2 * dc.layers;
     QkvPostArgs p = post_base(c, ri, Ri);
     p.ld_src = dc.layers * 2 * KD;
@@ -1095,7 +998,6 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
     p.part_stride = part_stride;
     HIP_OK(launch_qkv_post(p, c->dt(), s));
   }
-  c->tiled = false;
   // 2. The block [anchor, MASK x (B-1)].
   c->x16 = m.dtype == DFLASH_BF16 && batch * B >= kTcMinRows;
   Rows rd = c->rows(2);
@@ -1114,12 +1016,11 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   for (int j = 0; j < dc.layers; ++j) {
     // after the last layer: the final norm over the B - 1 mask positions of every block, packed
     const NextNorm next = j + 1 < dc.layers ? all_rows(c->dl[j + 1].attn_norm, R) : NextNorm{c->d_final_norm, nd, B, 1};
-    st = run_layer(c, c->dl[j], c->dlayer(j), rd, slots, batch, B, 1, ctx_bound, nullptr, nullptr, 0, next, &ss_n, s);
+    st = run_layer(c, c->dl[j], c->dlayer(j), rd, slots, batch, B, 1, ctx_bound, nullptr, 0, next, &ss_n, s);
     if (st != DFLASH_OK) return st;
   }
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32);
-  a.x_lo = c->xn_lo();
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
   with_norm(c, a, ss_n);
@@ -1188,7 +1089,7 @@ dflash_status dflash_op_linear(hipStream_t s, int32_t dtype, int32_t M, int32_t 
   a.seg[0] = GemmSeg{d_w, N};
   a.out_f32 = d_y;
   a.ld_out = N;
-  return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, true, s);
+  return run_gemm(dtype == DFLASH_BF16 ? 2 : 4, dtype == DFLASH_BF16 ? 0 : 1, a, M, s);
 }
 
 dflash_status dflash_op_linear_f16x(hipStream_t s, int32_t M, int32_t N, int32_t K, const void *d_x, const void *d_w,
@@ -1246,7 +1147,7 @@ dflash_status dflash_profile_replay(dflash_ctx *c, hipStream_t s, int32_t iters,
         HIP_OK(launch_gemm_tc(r.a, r.plan, s));
         continue;
       }
-      dflash_status st = run_gemm(c->es(), c->dt(), r.a, r.rows, r.tiled, s);
+      dflash_status st = run_gemm(c->es(), c->dt(), r.a, r.rows, s);
       if (st != DFLASH_OK) return st;
     }
   HIP_OK(hipEventRecord(e1, s));

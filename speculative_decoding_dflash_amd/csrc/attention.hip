@@ -14,7 +14,7 @@
 // that sees no allowed key publishes m = -inf, l = 0.  Several splits are merged by a second kernel.
 // Operand types: bf16 models keep q and the KV cache in fp16 and feed the probabilities to the PV
 // product as fp16 (fp32 accumulation throughout); fp32 models run the fp32 MFMA on fp32 operands.  The
-// output is the o projection's X operand (for bf16 models a pair of bf16 planes, see store_x).
+// output is the o projection's X operand (fp16 for bf16 models, like q and the KV cache).
 #include "kernels.h"
 
 namespace df {
@@ -127,7 +127,7 @@ DF_DEVICE X vload(const X *p, int i) {
 template <typename T, int D, int NQT, bool FUSED>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using F = AttnFrag<T, D>;
-  using XT = typename XOf<T>::type;  // output (X operand) type
+  using XT = T;  // output (X operand) type: the attention operands' storage type
   __shared__ __attribute__((aligned(16))) float so[4][16][D + 4];  // rows 16-byte aligned
   __shared__ float sm[4][NQT * 16], sl[4][NQT * 16];
   // fused calls: the block's own keys (K [16][D], V [D][16], row j = block row j), built here from raw k / v
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       if (a.n_splits == 1) {
         const size_t oi = (size_t)row * a.ldo + head * D + d0;
 #pragma unroll
-        for (int d = 0; d < DPT; ++d) store_x((XT *)a.out, (XT *)a.out_lo, oi + d, L > 0.f ? O[d] / L : 0.f);
+        for (int d = 0; d < DPT; ++d) store_x((XT *)a.out, oi + d, L > 0.f ? O[d] / L : 0.f);
       } else {
         const size_t pi = ((size_t)row * a.q_heads + head) * a.n_splits + split;
         float *po = a.part_o + pi * D + d0;
@@ -731,10 +731,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
     const float li = linv[qv];
     const size_t oi = (size_t)row * a.ldo + head * D + d4;
-    store_x((XT *)a.out, (XT *)a.out_lo, oi + 0, acc.x * li);
-    store_x((XT *)a.out, (XT *)a.out_lo, oi + 1, acc.y * li);
-    store_x((XT *)a.out, (XT *)a.out_lo, oi + 2, acc.z * li);
-    store_x((XT *)a.out, (XT *)a.out_lo, oi + 3, acc.w * li);
+    store_x((XT *)a.out, oi + 0, acc.x * li);
+    store_x((XT *)a.out, oi + 1, acc.y * li);
+    store_x((XT *)a.out, oi + 2, acc.z * li);
+    store_x((XT *)a.out, oi + 3, acc.w * li);
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -775,7 +775,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows)
         L += w * lv[s];
         O += w * pv[s];
       }
-    if (tid < D) store_x((XT *)a.out, (XT *)a.out_lo, (size_t)row * a.ldo + head * D + tid, L > 0.f ? O / L : 0.f);
+    if (tid < D) store_x((XT *)a.out, (size_t)row * a.ldo + head * D + tid, L > 0.f ? O / L : 0.f);
     return;
   }
   __shared__ float sw[64];
@@ -796,7 +796,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_rows)
     float O = 0.f;
 #pragma unroll 8
     for (int s = 0; s < ns; ++s) O += sw[s] * po[(size_t)s * D + dim];
-    store_x((XT *)a.out, (XT *)a.out_lo, (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
+    store_x((XT *)a.out, (size_t)row * a.ldo + head * D + dim, L > 0.f ? O / L : 0.f);
   }
 }
 
@@ -824,7 +824,7 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;
   const int n_rows = a.n_seq * a.q_len;
-  hipLaunchKernelGGL((attn_merge_kernel<typename XOf<T>::type>), dim3(n_rows * a.q_heads), dim3(128), 0, s, a, n_rows);
+  hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(n_rows * a.q_heads), dim3(128), 0, s, a, n_rows);
   return hipGetLastError();
 }
 

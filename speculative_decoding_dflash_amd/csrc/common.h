@@ -57,32 +57,29 @@ template <> struct Elem<f16> {
   static constexpr int kPerVec = 8;
 };
 
-// Storage type of the attention operands (q, K, V) for a model whose weights are T: fp16 for bf16
-// models (11 significant bits where bf16 keeps 8; q and k are RMS-normalised and the softmax weights
-// lie in [0, 1]), fp32 for fp32 models.
+// Storage type of the activations that feed the matrix cores -- q, the KV cache, and the X operand of
+// every weight product (normed hidden rows, attention output, SwiGLU activation, target features) --
+// for a model whose weights are T: fp16 for bf16 models, fp32 for fp32 models.  fp16 keeps 11
+// significant bits where bf16 keeps 8: rounding every one of these operands to bf16 would put a 64-layer
+// forward's logits about 5e-2 from exact arithmetic (independent roundings adding up like the square
+// root of the depth), rounding them to fp16 keeps it near 5e-3.  The bf16 weights enter the fp16
+// products converted exactly (see bf16x2_to_f16x2).  q and k are RMS-normalised, the softmax weights lie
+// in [0, 1]; every other stored magnitude saturates at 65504.
 template <typename T> struct KvOf;
 template <> struct KvOf<bf16> { using type = f16; };
 template <> struct KvOf<float> { using type = float; };
-// and back: the projection-input type that goes with a KV storage type
-template <typename K> struct XOf;
-template <> struct XOf<f16> { using type = bf16; };
-template <> struct XOf<float> { using type = float; };
+template <typename T> using ActOf = typename KvOf<T>::type;
 
-// Projection inputs (the X operand of every weight product) of bf16 models are held as two bf16
-// planes, hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact in fp32), so that hi + lo carries v to
-// about 16 significant bits and the product W (hi + lo) = W hi + W lo loses nothing to the storage of
-// X.  Calls over many rows instead hold one fp16 plane (lo null: the 16-bit words at hi are fp16), for
-// the tiled fp16 kernel.  fp32 models keep one plane (lo is null).
-DF_DEVICE void store_x(bf16 *hi, bf16 *lo, size_t i, float v) {
-  if (!lo) {
-    hi[i].bits = f32_to_f16(v);
-    return;
-  }
-  const uint16_t h = f32_to_bf16(v);
-  hi[i].bits = h;
-  if (lo) lo[i].bits = f32_to_bf16(v - bf16_to_f32(h));
+// Store v as element i of a projection input (X operand) of storage type A (fp16 or fp32).
+template <typename A> DF_DEVICE void store_x(A *x, size_t i, float v) { Elem<A>::store(x + i, v); }
+
+// Two bf16 weights (element 0 in the low half) -> two fp16, exact wherever fp16 is normal (|w| in
+// [2^-14, 65504]: bf16's 8 significant bits fit in fp16's 11); smaller magnitudes land on fp16's
+// subnormal grid, truncated (error below 2^-24).
+DF_DEVICE uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float e0 = __builtin_bit_cast(float, w << 16), e1 = __builtin_bit_cast(float, w & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
 }
-DF_DEVICE void store_x(float *hi, float *, size_t i, float v) { hi[i] = v; }
 
 // Device state of one sequence slot (lives in the workspace).
 struct SlotState {

@@ -11,7 +11,8 @@
 //     a wave only ever reads what it wrote itself, so the main loop needs no barrier;
 //   * X windows take the same path (quad-layout loads, wave-private LDS), which costs a few percent
 //     where loading X directly in the MFMA layout cost a quarter of the bandwidth;
-//   * v_mfma_f32_16x16x32_bf16 (or 4 x v_mfma_f32_16x16x4f32 for fp32 models) accumulates in fp32;
+//   * bf16 models: X is fp16 and the weights are converted to fp16 (exactly) as they are staged, then
+//     v_mfma_f32_16x16x32_f16 accumulates in fp32 (fp32 models: 4 x v_mfma_f32_16x16x4f32);
 //   * the NW waves reduce their partial tiles through LDS in a fixed order, then the whole
 //     work-group runs the epilogue on its columns.  No state crosses work-groups, so no device-scope
 //     fences (which write back and invalidate the per-XCD L2s) are needed anywhere;
@@ -33,18 +34,27 @@ namespace df {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA operands per weight type: bf16 models multiply fp16 X (ActOf<bf16>) with their weights converted
+// to fp16 as they are staged (w(): exact, see bf16x2_to_f16x2) on v_mfma_f32_16x16x32_f16; fp32 models
+// use v_mfma_f32_16x16x4f32.
 template <typename T> struct Frag;
 template <> struct Frag<bf16> {
   static constexpr int kEPL = 8;   // elements per lane per K step
   static constexpr int kStep = 32; // K per step
+  static DF_DEVICE u32x4 w(u32x4 v) {
+    return (u32x4){bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+  }
   static DF_DEVICE void mma(f32x4 &acc, u32x4 a, u32x4 b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                  acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0,
+                                                 0);
   }
 };
 template <> struct Frag<float> {
   static constexpr int kEPL = 4;
   static constexpr int kStep = 16;
+  static DF_DEVICE u32x4 w(u32x4 v) { return v; }
   // Element j of every lane's 4-vector forms one K=4 slice (k = 4*(lane/16) + j), identically for A and B.
   static DF_DEVICE void mma(f32x4 &acc, u32x4 a, u32x4 b) {
     const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
@@ -63,11 +73,8 @@ DF_DEVICE int x_src(const GemmArgs &a, int m) {
   return (r / a.x_take) * a.x_stride + a.x_off + r % a.x_take;
 }
 
-// Row v of the X operand as the kernels see it: rows 0 .. M-1 of x, then (with a low plane) rows
-// 0 .. M-1 of x_lo.
-template <typename T> DF_DEVICE const T *x_row(const GemmArgs &a, int v) {
-  return v < a.M ? (const T *)a.x + (size_t)x_src(a, v) * a.ldx : (const T *)a.x_lo + (size_t)x_src(a, v - a.M) * a.ldx;
-}
+// Row v (< M) of the X operand.
+template <typename T> DF_DEVICE const T *x_row(const GemmArgs &a, int v) { return (const T *)a.x + (size_t)x_src(a, v) * a.ldx; }
 
 DF_DEVICE float silu(float g) { return g / (1.0f + expf(-g)); }
 
@@ -151,7 +158,7 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
         const int m = e / HC, j = e % HC;
         const float r = rs ? s_rstd[m] : 1.f;
         const float gt = lds[m * COLS + j] * r, up = lds[m * COLS + HC + j] * r;
-        store_x((T *)a.out_act, (T *)a.out_act_lo, (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
+        store_x((ActOf<T> *)a.out_act, (size_t)(a.row_off + m) * a.ld_out + HC * c + j, silu(gt) * up);
       }
       break;
     }
@@ -166,10 +173,10 @@ DF_DEVICE void gemm_epilogue(const GemmArgs &a, int c, int split, float *lds, co
             v += a.resid[idx];
             a.resid[idx] = v;
           }
-          if (a.feat) store_x((T *)a.feat, (T *)a.feat_lo, (size_t)r * a.ld_feat + n, v);
+          if (a.feat) store_x((ActOf<T> *)a.feat, (size_t)r * a.ld_feat + n, v);
           const int jj = r % a.sel_stride - a.sel_offset;
           if (jj >= 0 && jj < a.sel_take)
-            store_x((T *)a.xg, (T *)a.xg_lo, (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
+            store_x((ActOf<T> *)a.xg, (size_t)((r / a.sel_stride) * a.sel_take + jj) * a.ld_xg + n, v * a.gain[n]);
           lds[m * COLS + j] = v * v;  // entry owned by this thread
         }
         __syncthreads();
@@ -243,11 +250,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
         qrow[q] = (const T *)a.seg[q / 2].w + (size_t)(8 * c + 4 * (q % 2) + g) * a.K + k0 + r16 * F::kEPL;
     }
   }
-  // X rows: with a low plane the operand has Mv = 2M rows, rows M .. 2M-1 being the low parts of rows
-  // 0 .. M-1 (their products are added in the reduction below).  Rows >= Mv load row 0 (never read back:
-  // the operand read below masks them), so that every load in the streaming loop is unconditional and
-  // the compiler can count outstanding loads exactly.
-  const int Mv = a.x_lo ? 2 * a.M : a.M;
+  // X rows: rows >= M load row 0 (never read back: the operand read below masks them), so that every load
+  // in the streaming loop is unconditional and the compiler can count outstanding loads exactly.
+  const int Mv = a.M;
   const T *xrow[NXQ];
 #pragma unroll
   for (int q = 0; q < NXQ; ++q) {
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       const int cs = sup + p * NW;
       if (cs < nsup) {  // wave-uniform
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = buf[p][q];
+        for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = F::w(buf[p][q]);
 #pragma unroll
         for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[p][q];
       }
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       const int m = mt * 16 + r16;
       const u32x4 xv = m < Mv ? ld16(x_row<T>(a, m) + k) : zero;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) F::mma(acc[mt][ct], xv, ld16(wbase[ct] + (size_t)r16 * a.K + k));
+      for (int ct = 0; ct < CT; ++ct) F::mma(acc[mt][ct], xv, F::w(ld16(wbase[ct] + (size_t)r16 * a.K + k)));
     }
   }
 
@@ -343,18 +348,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) lds[wave * kEnt + (mt * 16 + g * 4 + r) * COLS + ct * 16 + r16] = acc[mt][ct][r];
   __syncthreads();
-  // output row m < M: the waves' sums of operand row m, plus those of its low part (row M + m)
-  const int lo_off = a.x_lo ? a.M * COLS : 0;
+  // output row m < M: the waves' sums
   for (int e = tid; e < a.M * COLS; e += NT) {
     float v = lds[e];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += lds[w * kEnt + e];
-    if (lo_off) {
-      float u = lds[e + lo_off];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) u += lds[w * kEnt + e + lo_off];
-      v += u;
-    }
     lds[e] = v;  // entry e < M * COLS is read and written by this thread only
   }
   if (a.ss_in && tid < a.M) s_rstd[tid] = gemm_rstd(a, tid, ssp.fast, s_ssp);
@@ -362,13 +360,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   gemm_epilogue<T, COLS, NT>(a, c, split, lds, s_rstd);
 }
 
-// Stream-K variant (ksplit 1, K a whole number of super-steps, 8 waves).  Two forms:
-//   * FOLD (bf16 projections with a low X plane, at most 8 rows): the 16 staged X rows are the 8 high
-//     rows then the 8 low rows, so each MFMA tile carries a row's high part in one half and its low part
-//     in the other, and a lane exchange adds the halves (row m + 8 sits 32 lanes after row m); a work
-//     item covers 64 output columns, its weights staged 32 rows at a time through the wave's LDS tile,
-//     which keeps the X bytes per weight byte at a quarter;
-//   * otherwise at most 16 X rows and 32 output columns per item.
+// Stream-K variant (ksplit 1, K a whole number of super-steps, 8 waves, at most 16 X rows, 32 output
+// columns per work item).
 // With one tile per work-group, projections whose tile count is not a multiple of the CU count leave
 // CUs idle while others stream (160 hidden-width tiles on 256 CUs).  Here the projection's items
 // (tile, super-step), numbered tile-major, are cut into equal contiguous ranges, one per work-group
@@ -380,17 +373,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 // another XCD) and count their arrival on the tile's counter; the finisher adds the partials in
 // work-group order -- a fixed order, so the result does not depend on who arrives last -- runs the
 // epilogue and zeroes the counter for the next launch.  No work-group ever waits for another.
-template <typename T, int XR, bool FOLD, int COLS>
+template <typename T, int XR>
 __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   using F = Frag<T>;
   constexpr int NW = 8, NT = NW * 64;
-  constexpr int CT = COLS / 16, ROWS = FOLD ? 8 : 16;
-  static_assert(COLS == 32 || (FOLD && COLS == 64), "item widths");
+  constexpr int COLS = 32, CT = COLS / 16, ROWS = 16;
   static_assert(XR == 8 || XR == 16, "X staging rows");
-  static_assert(!FOLD || XR == 16, "a folded item stages 8 high and 8 low rows");
   constexpr int ROWB = 256 + 16;
   constexpr int NQ = COLS / 4, NXQ = XR / 4;
-  constexpr int NH = NQ / 8;  // halves of 8 weight quads (32 rows) staged one after the other
   constexpr int SK = 256 / sizeof(T);
   constexpr int KS = SK / F::kStep;
   constexpr int kEnt = ROWS * COLS;  // entries of one partial tile
@@ -434,18 +424,12 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   size_t qoff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) qoff[q] = (size_t)(4 * q + g) * a.K + r16 * F::kEPL;
-  // X staging rows: FOLD stages high rows 0..7 then low rows 0..7 (rows >= M read row 0: their
-  // products land in output rows that are never stored); otherwise rows 0 .. XR-1 of x
+  // X staging rows 0 .. XR-1 (rows >= M read row 0; their products are never read back)
   const T *xrow[NXQ];
 #pragma unroll
   for (int q = 0; q < NXQ; ++q) {
     const int m = 4 * q + g;
-    if (FOLD) {
-      const int mr = m & 7;
-      xrow[q] = (const T *)(m < 8 ? a.x : a.x_lo) + (size_t)x_src(a, mr < a.M ? mr : 0) * a.ldx + r16 * F::kEPL;
-    } else {
-      xrow[q] = (const T *)a.x + (size_t)x_src(a, m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
-    }
+    xrow[q] = (const T *)a.x + (size_t)x_src(a, m < a.M ? m : 0) * a.ldx + r16 * F::kEPL;
   }
   SsPrefetch<NT> ssp;
   ssp.load(a);
@@ -460,19 +444,17 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   const T *w0, *w1;
   tile_base(lt < ntile ? lt : 0, w0, w1);
   u32x4 buf[NQ], bufx[NXQ];
-  // loads of the item at the cursor: weight quads of half h (and, with half 0, the X rows)
-  auto issue_half = [&](int h) {
+  // loads of the item at the cursor: its weight quads and X rows
+  auto issue = [&]() {
     const bool ok = li < hi;
 #pragma unroll
-    for (int q = 8 * h; q < 8 * h + 8; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int gi = q / 4;  // the quad's 16-row group
       const T *wq = (gi < CT / 2 ? w0 + (size_t)gi * gstep : w1 + (size_t)(gi - CT / 2) * gstep);
       buf[q] = ld16(ok ? wq + qoff[q % 4] + (size_t)ls * SK : dummy);
     }
-    if (h == 0) {
 #pragma unroll
-      for (int q = 0; q < NXQ; ++q) bufx[q] = ld16(ok ? xrow[q] + (size_t)ls * SK : dummy);
-    }
+    for (int q = 0; q < NXQ; ++q) bufx[q] = ld16(ok ? xrow[q] + (size_t)ls * SK : dummy);
   };
   auto advance = [&]() {
     li += NW;
@@ -485,8 +467,7 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
       if (lt < ntile) tile_base(lt, w0, w1);
     }
   };
-#pragma unroll
-  for (int h = 0; h < NH; ++h) issue_half(h);
+  issue();
   advance();
   ssp.store(a, s_ssp);
   __syncthreads();  // the rows' 1/rms before the stream (computed inside the tile loop, the kernel kept a stack frame)
@@ -499,41 +480,31 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (; ui < seg_hi; ui += NW) {
+      // stage the item, then load the next one while it is multiplied
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        // stage half h (and X with half 0), then load the next item's half h while it is multiplied
+      for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = F::w(buf[q]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4 *>(wt + (4 * q + g) * ROWB + 16 * r16) = buf[8 * h + q];
-        if (h == 0) {
+      for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[q];
+      issue();
+      advance();
 #pragma unroll
-          for (int q = 0; q < NXQ; ++q) *reinterpret_cast<u32x4 *>(xt + (4 * q + g) * ROWB + 16 * r16) = bufx[q];
-        }
-        issue_half(h);
-        if (h == NH - 1) advance();
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 xv = r16 < a.M
+                             ? *reinterpret_cast<const u32x4 *>(xt + (r16 < XR ? r16 : 0) * ROWB + ks * 64 + 16 * g)
+                             : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 xv = (FOLD || r16 < a.M)
-                               ? *reinterpret_cast<const u32x4 *>(xt + (r16 < XR ? r16 : 0) * ROWB + ks * 64 + 16 * g)
-                               : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * c2 + r16) * ROWB + ks * 64 + 16 * g);
-            F::mma(acc[2 * h + c2], xv, wv);
-          }
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const u32x4 wv = *reinterpret_cast<const u32x4 *>(wt + (16 * c2 + r16) * ROWB + ks * 64 + 16 * g);
+          F::mma(acc[c2], xv, wv);
         }
       }
     }
-    // C[m][n] of a wave's partial tile sits at lane (n % 16, 4 * (lane / 16) + r) of acc[n / 16]; FOLD
-    // adds row m + 8 (the low part) into row m
+    // C[m][n] of a wave's partial tile sits at lane (n % 16, 4 * (lane / 16) + r) of acc[n / 16]
     float *rb = red + (seg & 1) * NW * kEnt;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = acc[ct][r];
-        if (FOLD) v += __shfl_xor(v, 32);
-        if (!FOLD || g < 2) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = v;
-      }
+      for (int r = 0; r < 4; ++r) rb[wave * kEnt + (g * 4 + r) * COLS + ct * 16 + r16] = acc[ct][r];
     __syncthreads();
     float v[kPer];
 #pragma unroll
@@ -582,363 +553,12 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   }
 }
 
-// Large-M projections (prefill, large batches; bf16): an MFMA-bound tiled GEMM.  A work-group owns a
-// 128 x 128 output tile (SWIGLU: 64 output columns, their 64 gate and 64 up weight rows interleaved in
-// 16-row groups so that a lane holds a column's gate and up sums), 4 waves of 64 x 64, K in steps of
-// 64: the next step's X and W tiles are loaded into registers (16 bytes per thread and row chunk)
-// while the current step's tiles are multiplied out of LDS (double buffer, one barrier per step),
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  The epilogues compute the same values as the
-// skinny kernel's (residual add + deferred RMSNorm inputs with per-32-column sums of squares,
-// SwiGLU, fp32 / activation stores, the 1/rms row scale).  Needs K % 64 == 0 and N (SWIGLU: output
-// columns) a multiple of the tile width with every segment a whole number of tiles.
-//
-// Decode batches (32 .. 256 rows) use the same kernel with 64-row tiles where M <= 64 and a K split
-// over grid z: narrow projections (o, down: 40 column tiles) would otherwise run on a sixth of the
-// CUs.  Each K range then writes its raw fp32 sums (`raw`, [range][M][N], SWIGLU: gate columns then
-// up columns) and gemm_mb_reduce_kernel adds the ranges in order and runs the epilogue.
-constexpr int kMmBM = 128, kMmBN = 128, kMmBK = 64;
-constexpr int kMbWgTarget = 384;   // work-groups a split decode-batch projection aims at
-constexpr int kMbFullTiles = 256;  // output tiles from which a decode-batch projection is not split
-template <int BM>
-__global__ __launch_bounds__(256, 2) void gemm_mm_kernel(GemmArgs a, float *raw, int steps) {
-  using F = Frag<bf16>;
-  constexpr int BN = kMmBN, BK = kMmBK, LDK = BK + 8;  // LDS row stride 144 B
-  constexpr int MI = BM / 32;                          // 16-row fragments per wave (wave tile BM/2 x 64)
-  constexpr int CA = BM / 32;                          // X chunks per thread per K step
-  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * LDK], sB[2][BN * LDK];
-  __shared__ float s_rstd[BM];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  const bool swiglu = a.epi == EPI_SWIGLU;
-  // With a low plane of X the tile's BM operand rows hold RT = BM / 2 output rows: in each wave the
-  // fragments i < MI / 2 carry the high parts of the wave's rows and fragments MI / 2 + i their low parts
-  // (added into the high fragments' sums after the K loop).
-  const bool lo = a.x_lo != nullptr;
-  const int RT = lo ? BM / 2 : BM;
-  const int nI = lo ? MI / 2 : MI;  // output fragments per wave
-  const int m0 = blockIdx.y * RT;
-  const int n0 = blockIdx.x * (swiglu ? BN / 2 : BN);  // first output column of the tile
-  const int K = a.K;
-  // this work-group's K steps: [kt0, kt1)
-  const int kt0 = blockIdx.z * steps, kt1 = min(K / BK, kt0 + steps);
-  // this thread's 16-byte chunks of each tile per K step: chunk c = tid + 256 i -> row c / 8,
-  // elements 8 (c % 8) .. + 7 of the step's 64
-  const bf16 *pa[CA], *pb[4];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
-    int lr = row, plane = 0;  // the operand row's output row (in the tile) and plane
-    if (lo) {
-      const int w2 = row / (BM / 2), fi = (row % (BM / 2)) / 16;
-      plane = fi >= MI / 2;
-      lr = w2 * (RT / 2) + 16 * (fi % (MI / 2)) + row % 16;
-    }
-    pa[i] = (const bf16 *)(plane ? a.x_lo : a.x) + (size_t)x_src(a, min(m0 + lr, a.M - 1)) * a.ldx + kc;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
-    const bf16 *w;
-    if (swiglu) {  // B row -> (16-column group p = row / 32, gate or up = row / 16 % 2)
-      const int col = n0 + 16 * (row >> 5) + (row & 15);
-      w = (const bf16 *)a.seg[(row >> 4) & 1].w + (size_t)col * K;
-    } else {
-      int nr = n0 + row, si = 0;
-      while (si + 1 < a.nseg && nr >= a.seg[si].n) {
-        nr -= a.seg[si].n;
-        ++si;
-      }
-      w = (const bf16 *)a.seg[si].w + (size_t)nr * K;
-    }
-    pb[i] = w + kc;
-  }
-  const bool scaled = !raw || a.mb_direct;  // raw sums of a direct partial output carry the 1/rms
-  if (scaled && tid < RT) s_rstd[tid] = a.ss_in ? gemm_rstd(a, min(m0 + tid, a.M - 1), false, nullptr) : 1.f;
-
-  f32x4 acc[MI][4];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // Two register stages: the loads of step kt + 2 are issued while step kt is multiplied out of LDS and
-  // step kt + 1 waits in registers (a work-group streaming weights needs that many bytes in flight);
-  // loads past the range reload the range's last step (never stored).
-  u32x4 ra[2][CA], rb[2][4];
-  auto load = [&](int st, int kt) {
-    const int k = min(kt, kt1 - 1) * BK;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) ra[st][i] = ld16(pa[i] + k);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rb[st][i] = ld16(pb[i] + k);
-  };
-  auto store = [&](int st, int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + 256 * i, off = (c >> 3) * LDK + (c & 7) * 8;
-      *reinterpret_cast<u32x4 *>(&sA[buf][off]) = ra[st][i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, off = (c >> 3) * LDK + (c & 7) * 8;
-      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = rb[st][i];
-    }
-  };
-  load(0, kt0);
-  load(1, kt0 + 1);
-  store(0, 0);
-  __syncthreads();
-  // One K step out of LDS buffer BUF (= its index in the range, mod 2): step kt + 1 waits in register
-  // stage 1 - BUF and step kt + 2 is loaded into stage BUF, freed by the previous step's store.  The
-  // stage and buffer indices are template constants, so the stages stay in registers.
-  // The loads are unconditional (past the range they reload its last step): a load issued on only
-  // some paths would make every later wait count it, so the waits for step kt + 1 would also wait for
-  // step kt + 2.
-  auto kstep = [&](int kt, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    load(buf, kt + 2);
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      u32x4 fa[MI], fb[4];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][(wm * (BM / 2) + 16 * i + r16) * LDK + 32 * s + 8 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fb[i] = *reinterpret_cast<const u32x4 *>(&sB[buf][(wn * 64 + 16 * i + r16) * LDK + 32 * s + 8 * g]);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) F::mma(acc[i][j], fa[i], fb[j]);
-    }
-    if (kt + 1 < kt1) store(1 - buf, 1 - buf);
-    __syncthreads();
-  };
-  int kt = kt0;
-  for (; kt + 1 < kt1; kt += 2) {
-    kstep(kt, std::integral_constant<int, 0>{});
-    kstep(kt + 1, std::integral_constant<int, 1>{});
-  }
-  if (kt < kt1) kstep(kt, std::integral_constant<int, 0>{});
-  if (lo) {
-#pragma unroll
-    for (int i = 0; i < MI / 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += acc[i + MI / 2][j];
-  }
-
-  if (raw) {  // this K range's raw sums: [range][M][N] (SWIGLU: gate columns [0, N), up columns [N, 2N))
-    const int nraw = swiglu ? 2 * a.N : a.N;
-    float *dst = raw + (size_t)blockIdx.z * a.M * nraw;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ml = wm * (RT / 2) + 16 * i + 4 * g + r, m = m0 + ml;
-        if (i >= nI || m >= a.M) continue;
-        const float sc = scaled ? s_rstd[ml] : 1.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // SWIGLU: fragment j holds gate (j even) or up (j odd) sums of output column
-          // n0 + 16 (2 wn + j / 2) + r16
-          const int col = swiglu ? (j & 1) * a.N + n0 + 16 * (2 * wn + j / 2) + r16 : n0 + wn * 64 + 16 * j + r16;
-          dst[(size_t)m * nraw + col] = scaled ? acc[i][j][r] * sc : acc[i][j][r];
-        }
-      }
-    return;
-  }
-
-  // acc[i][j][r] = Y[row m0 + wm*(RT/2) + 16 i + 4 g + r][tile column wn*64 + 16 j + r16], i < nI
-  const bool rs = a.ss_in != nullptr;
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (i >= nI) continue;
-      const int ml = wm * (RT / 2) + 16 * i + 4 * g + r, m = m0 + ml;
-      const bool live = m < a.M;
-      const float sc = rs ? s_rstd[ml] : 1.f;
-      const int grow = a.row_off + m;
-      switch (a.epi) {
-        case EPI_STORE_F32:
-        case EPI_PARTIAL:
-          if (live)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              a.out_f32[(size_t)grow * a.ld_out + n0 + wn * 64 + 16 * j + r16] = acc[i][j][r] * sc;
-          break;
-        case EPI_SWIGLU:
-          if (live)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const float gt = acc[i][2 * q][r] * sc, up = acc[i][2 * q + 1][r] * sc;
-              store_x((bf16 *)a.out_act, (bf16 *)a.out_act_lo, (size_t)grow * a.ld_out + n0 + 16 * (2 * wn + q) + r16,
-                      silu(gt) * up);
-            }
-          break;
-        case EPI_RESID_NORM: {
-          const int jj = grow % a.sel_stride - a.sel_offset;
-          const bool sel = live && jj >= 0 && jj < a.sel_take;
-          const size_t o = (size_t)(grow / a.sel_stride) * a.sel_take + jj;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {  // the wave's two 32-column groups
-            float ss = 0.f;
-#pragma unroll
-            for (int j = 2 * h; j < 2 * h + 2; ++j) {
-              const int n = n0 + wn * 64 + 16 * j + r16;
-              float v = acc[i][j][r];
-              if (live) {
-                if (a.resid) {
-                  const size_t idx = (size_t)grow * a.ld_resid + n;
-                  v += a.resid[idx];
-                  a.resid[idx] = v;
-                }
-                if (a.feat) store_x((bf16 *)a.feat, (bf16 *)a.feat_lo, (size_t)grow * a.ld_feat + n, v);
-                if (sel) store_x((bf16 *)a.xg, (bf16 *)a.xg_lo, o * a.ld_xg + n, v * a.gain[n]);
-              }
-              ss += v * v;
-            }
-            // sum over the group's 32 columns: the 16 lanes of this row (same g) hold 2 columns each
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
-            ss += __shfl_xor(ss, 8);
-            if (sel && r16 == 0) a.ss_out[o * a.ss_out_ld + (n0 + wn * 64 + 32 * h) / 32] = ss;
-          }
-          break;
-        }
-      }
-    }
-}
-
-// Sum of the K ranges of gemm_mm_kernel's raw output, in range order, then the projection's epilogue,
-// for one 32-column tile (SWIGLU: 16 output columns, their gate and up sums) of kMbRedRows rows:
-// thread t adds the ranges of 4 adjacent columns of row t / 8 (all ranges' loads issued at once).
-constexpr int kMbRedRows = 16;
-__global__ __launch_bounds__(128) void gemm_mb_reduce_kernel(GemmArgs a, const float *raw, int ks) {
-  __shared__ __attribute__((aligned(16))) float lds[kMbRedRows * 32];
-  __shared__ float s_rstd[kMbRedRows];
-  const int c = blockIdx.x, tid = threadIdx.x;
-  const int r0 = blockIdx.y * kMbRedRows;
-  const bool swiglu = a.epi == EPI_SWIGLU;
-  const int nraw = swiglu ? 2 * a.N : a.N;
-  const size_t slice = (size_t)a.M * nraw;
-  GemmArgs b = a;  // the tile's rows as a projection of their own: row_off = r0
-  b.M = min(kMbRedRows, a.M - r0);
-  b.row_off = r0;
-  const int m = tid >> 3, j = (tid & 7) * 4;
-  if (m < b.M) {
-    const int col = swiglu ? (j < 16 ? 16 * c + j : a.N + 16 * c + j - 16) : 32 * c + j;
-    const float4 *p = reinterpret_cast<const float4 *>(raw + (size_t)(r0 + m) * nraw + col);
-    float4 v[kMbMaxSplit];
-#pragma unroll
-    for (int z = 0; z < kMbMaxSplit; ++z) v[z] = p[(z < ks ? z : 0) * (slice / 4)];
-    float4 t = v[0];
-#pragma unroll
-    for (int z = 1; z < kMbMaxSplit; ++z)
-      if (z < ks) {
-        t.x += v[z].x;
-        t.y += v[z].y;
-        t.z += v[z].z;
-        t.w += v[z].w;
-      }
-    *reinterpret_cast<float4 *>(&lds[m * 32 + j]) = t;
-  }
-  if (a.ss_in && tid < b.M) s_rstd[tid] = gemm_rstd(b, tid, false, nullptr);
-  __syncthreads();
-  gemm_epilogue<bf16, 32, 128>(b, c, 0, lds, s_rstd);
-}
-
 namespace {
 int env_int(const char *name, int dflt) {
   const char *e = getenv(name);
   return e ? atoi(e) : dflt;
 }
 }  // namespace
-
-// The tiled kernel takes a projection when it is bf16, at least kMmMinRows rows and tile-shaped
-// (DFLASH_GEMM_MM=0, read per call, sends every projection to the row-chunked kernels instead).
-constexpr int kMmMinRows = 128;
-bool gemm_mm_ok(const GemmArgs &a, int dtype) {
-  static const int min_rows = env_int("DFLASH_GEMM_MM_MIN", kMmMinRows);
-  if (dtype != 0 || a.M < min_rows || a.ksplit != 1 || a.K % kMmBK) return false;
-  if (env_int("DFLASH_GEMM_MM", 1) == 0) return false;
-  const bool swiglu = a.epi == EPI_SWIGLU;
-  const int tn = swiglu ? kMmBN / 2 : kMmBN;
-  if (a.N % tn) return false;
-  if (!swiglu)
-    for (int i = 0; i < a.nseg; ++i)
-      if (a.seg[i].n % kMmBN) return false;
-  return true;
-}
-
-bool gemm_mb_ok(const GemmArgs &a, int dtype) {
-  if (dtype != 0 || a.M < kMbMinRows || a.M > kMbMaxRows || a.ksplit != 1 || a.K % kMmBK) return false;
-  if (!a.mb_raw || env_int("DFLASH_GEMM_MB", 1) == 0) return false;
-  const bool swiglu = a.epi == EPI_SWIGLU;
-  if (a.N % (swiglu ? kMmBN / 2 : kMmBN)) return false;
-  if (!swiglu)
-    for (int i = 0; i < a.nseg; ++i)
-      if (a.seg[i].n % kMmBN) return false;
-  return a.row_off == 0;
-}
-
-// K ranges per decode-batch projection: about kMbWgTarget work-groups in all, each range at least four
-// K steps, and the raw output within the caller's scratch.
-// Returns the number of ranges; *steps = K steps per range (the last may be shorter, none is empty).
-static int mb_splits(const GemmArgs &a, int tiles, int *steps) {
-  const int env = env_int("DFLASH_GEMM_MB_SPLIT", 0);
-  const int wg = std::max(1, env_int("DFLASH_GEMM_MB_WG", kMbWgTarget));
-  const int nk = a.K / kMmBK;
-  // a projection with a tile for every CU streams without a split (and without the reduce launch)
-  const int full = env_int("DFLASH_GEMM_MB_FULL", kMbFullTiles);
-  int ks = env > 0 ? env : (full > 0 && tiles >= full ? 1 : (wg + tiles - 1) / tiles);
-  ks = std::max(1, std::min({ks, nk / 4, kMbMaxSplit}));
-  const size_t per = (size_t)a.M * (a.epi == EPI_SWIGLU ? 2 * a.N : a.N);
-  while (ks > 1 && (size_t)ks * per > (size_t)a.mb_raw_cap) --ks;
-  *steps = (nk + ks - 1) / ks;
-  return (nk + *steps - 1) / *steps;
-}
-
-// X operand rows of a projection (a low plane doubles them)
-static int x_rows(const GemmArgs &a) { return a.x_lo ? 2 * a.M : a.M; }
-
-// Tile height of a decode-batch projection: 64 operand rows up to 64 operand rows, else 128; *rt = the
-// output rows per tile (half the operand rows with a low plane).
-static int mb_bm(const GemmArgs &a, int *rt) {
-  const int BM = x_rows(a) <= 64 ? 64 : 128;
-  *rt = a.x_lo ? BM / 2 : BM;
-  return BM;
-}
-
-int gemm_mb_slices(const GemmArgs &a) {
-  const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
-  int rt = 0;
-  mb_bm(a, &rt);
-  int steps = 0;
-  return mb_splits(a, (a.N / tn) * ((a.M + rt - 1) / rt), &steps);
-}
-
-hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const bool swiglu = a.epi == EPI_SWIGLU;
-  const int tn = swiglu ? kMmBN / 2 : kMmBN;
-  int rt = 0;
-  const int BM = mb_bm(a, &rt);
-  const int tiles = (a.N / tn) * ((a.M + rt - 1) / rt);
-  int steps = 0;
-  const int ks = mb_splits(a, tiles, &steps);
-  const dim3 grid(a.N / tn, (a.M + rt - 1) / rt, ks), block(256);
-  float *raw = ks > 1 ? a.mb_raw : nullptr;
-  const bool direct = a.mb_direct && a.epi == EPI_PARTIAL;  // the ranges are the output: no reduce
-  hipEvent_t end = ks > 1 && !direct ? nullptr : e1;
-  if (BM == 64) hipExtLaunchKernelGGL(gemm_mm_kernel<64>, grid, block, 0, s, e0, end, 0, a, raw, steps);
-  else hipExtLaunchKernelGGL(gemm_mm_kernel<128>, grid, block, 0, s, e0, end, 0, a, raw, steps);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ks == 1 || direct) return e;
-  const dim3 rgrid(swiglu ? a.N / 16 : a.N / 32, (a.M + kMbRedRows - 1) / kMbRedRows);
-  hipExtLaunchKernelGGL(gemm_mb_reduce_kernel, rgrid, dim3(128), 0, s, nullptr, e1, 0, a, (const float *)raw, ks);
-  return hipGetLastError();
-}
 
 template <typename T, int MT, int CT, int NW, int XR>
 static void launch_xr(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
@@ -965,7 +585,7 @@ static void launch_xr(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEv
 template <typename T, int MT, int CT, int NW>
 static void launch_pd(const GemmArgs &a, int pd, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if constexpr (MT == 1) {
-    if (x_rows(a) <= 8) {
+    if (a.M <= 8) {
       launch_xr<T, MT, CT, NW, 8>(a, pd, grid, s, e0, e1);
       return;
     }
@@ -997,16 +617,16 @@ struct TileCfg {
 
 // Tile width and waves per work-group, from MI355X sweeps at M = 8 (one launch per shape, weights
 // rotated through more memory than the memory-side cache holds): 32-row tiles with 8 waves stream best
-// for hidden-width outputs (o / down / fc projections) and SwiGLU pairs; 32-row tiles with 4 waves for
-// mid-sized outputs with short K (q/k/v, injected k/v: 16-row tiles streamed as fast when X had one
-// plane, and lost ~1.5% per step once the 16 staged X rows of a low plane matched their weight rows)
-// and for the LM head.
+// for hidden-width outputs (o / down / fc projections) and SwiGLU pairs; 16-row tiles with 4 waves for
+// mid-sized outputs with short K (q/k/v, injected k/v: 448 tiles cover the CUs 1.75 times), 32-row tiles
+// with 4 waves for the LM head.
 static TileCfg pick_tiles(int epi, int N, int K) {
   static const int env_ct = env_int("DFLASH_GEMM_CT", 0), env_nw = env_int("DFLASH_GEMM_NW", 0),
                    env_pd = env_int("DFLASH_GEMM_PD", 0), env_pct = env_int("DFLASH_GEMM_PART_CT", 0),
                    env_pnw = env_int("DFLASH_GEMM_PART_NW", 0);
   TileCfg t{2, 8, 1};
   if (epi != EPI_SWIGLU && N >= 6144 && N <= 12288 && K <= 8192) {
+    t.ct = 1;
     t.nw = 4;
   } else if (epi != EPI_SWIGLU && N >= 65536) {
     t.nw = 4;
@@ -1044,14 +664,6 @@ int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems) {
   return split;
 }
 
-// The folded stream-K form: a low X plane and at most 8 rows.
-static bool sk_fold(const GemmArgs &a) { return a.x_lo && a.M <= 8; }
-// Output columns of a folded stream-K item (DFLASH_GEMM_SK_COLS=32 or 64, read per launch).  64-column
-// items halve the X bytes per weight byte but measured slower on MI355X at the 27B decode shapes (each
-// wave then holds only one or two items of a 52 MB projection, 11.77 against 11.45 ms per step), so 32
-// is the default.
-static int sk_fold_cols() { return env_int("DFLASH_GEMM_SK_COLS", 32) == 64 ? 64 : 32; }
-
 // Stream-K launch: only with the caller's scratch, for shapes the kernel covers, and by default for the
 // hidden-width (residual + norm) and SwiGLU projections, where it measured faster on MI355X at M = 8
 // (o 15.0 -> 13.8 us, down 37.6 -> 33.7 us, gate/up 72 -> 64 us); q/k/v (448 16-column tiles) and the
@@ -1059,11 +671,11 @@ static int sk_fold_cols() { return env_int("DFLASH_GEMM_SK_COLS", 32) == 64 ? 64
 // DFLASH_GEMM_SK=0 turns it off, =1 uses it wherever the shape allows.
 static int sk_per(const GemmArgs &a, int dtype, int *n_wg) {
   const int env = env_int("DFLASH_GEMM_SK", -1);  // read per launch: tests switch it
-  if (!a.sk_part || !a.sk_cnt || (env == 0 && !a.sk_force) || a.M < 1 || x_rows(a) > 16 || a.ksplit != 1) return 0;
+  if (!a.sk_part || !a.sk_cnt || (env == 0 && !a.sk_force) || a.M < 1 || a.M > 16 || a.ksplit != 1) return 0;
   const int sk = dtype == 0 ? 128 : 64;  // K elements per super-step
   if (a.K < sk || a.K % sk) return 0;
   const bool swiglu = a.epi == EPI_SWIGLU;
-  const int cols = sk_fold(a) ? sk_fold_cols() : 32;  // output columns per tile (SWIGLU: half gate, half up)
+  const int cols = 32;  // output columns per tile (SWIGLU: half gate, half up)
   if (swiglu ? a.N % (cols / 2) : a.N % cols) return 0;
   if (!swiglu)
     for (int i = 0; i < a.nseg; ++i)
@@ -1090,38 +702,23 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
     return hipErrorInvalidValue;
   if (a.ss_in && (a.ss_n < 1 || a.norm_dim < 1 || a.ss_ld % 4 || a.ss_n > a.ss_ld)) return hipErrorInvalidValue;
   if (a.epi == EPI_RESID_NORM && a.N / 32 > a.ss_out_ld) return hipErrorInvalidValue;
-  if (gemm_mm_ok(a, dtype)) {
-    const int tn = a.epi == EPI_SWIGLU ? kMmBN / 2 : kMmBN;
-    const int rt = a.x_lo ? kMmBM / 2 : kMmBM;  // output rows per tile
-    const dim3 grid(a.N / tn, (a.M + rt - 1) / rt), block(256);
-    hipExtLaunchKernelGGL(gemm_mm_kernel<kMmBM>, grid, block, 0, s, e0, e1, 0, a, (float *)nullptr, a.K / kMmBK);
-    return hipGetLastError();
-  }
   int n_wg = 0;
   const int sk = sk_per(a, dtype, &n_wg);
   if (a.sk_force && !sk) return hipErrorInvalidValue;
   if (const int per = sk) {
     const dim3 grid(n_wg), block(512);
-    const bool x8 = x_rows(a) <= 8;
+    const bool x8 = a.M <= 8;
     if (dtype == 0) {
-      if (sk_fold(a)) {
-        if (sk_fold_cols() == 64)
-          hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16, true, 64>), grid, block, 0, s, e0, e1, 0, a, per);
-        else
-          hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16, true, 32>), grid, block, 0, s, e0, e1, 0, a, per);
-      } else if (x8) {
-        hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
-      } else {
-        hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
-      }
+      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 8>), grid, block, 0, s, e0, e1, 0, a, per);
+      else hipExtLaunchKernelGGL((gemm_sk_kernel<bf16, 16>), grid, block, 0, s, e0, e1, 0, a, per);
     } else {
-      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
-      else hipExtLaunchKernelGGL((gemm_sk_kernel<float, 16, false, 32>), grid, block, 0, s, e0, e1, 0, a, per);
+      if (x8) hipExtLaunchKernelGGL((gemm_sk_kernel<float, 8>), grid, block, 0, s, e0, e1, 0, a, per);
+      else hipExtLaunchKernelGGL((gemm_sk_kernel<float, 16>), grid, block, 0, s, e0, e1, 0, a, per);
     }
     return hipGetLastError();
   }
   const TileCfg t = pick_tiles(a.epi, a.N, a.K);
-  const int xr = x_rows(a);
+  const int xr = a.M;
   if (xr > kGemmMaxRows) return hipErrorInvalidValue;  // the host chunks longer inputs
   const int MT = xr <= 16 ? 1 : (xr <= 32 ? 2 : 4);
   if (dtype == 0) {

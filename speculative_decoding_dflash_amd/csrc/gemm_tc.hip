@@ -1,14 +1,8 @@
-// Tiled MFMA projection for many rows (decode batches of 32+ rows, prefill): Y[M, N] = X[M, K] W[N, K]^T
-// with X in fp16 (one plane) and the bf16 weights converted to fp16 as they are staged.
-//
-// Why fp16 here: a bf16 model's projection inputs need more than bf16's 8 significant bits to keep the
-// logits of a 64-layer forward within the bf16 tolerance.  At a handful of rows the skinny kernels carry
-// X as two bf16 planes (hi + lo) at no cost, since the matrix cores idle there; at hundreds of rows the
-// second plane would double the MFMA work of a product that is now compute-bound.  fp16 keeps 11
-// significant bits in one plane, and every bf16 weight inside fp16's normal range (|w| in
-// [2^-14, 65504]) converts to fp16 exactly (8 significant bits fit in 11); smaller ones land on fp16's
-// subnormal grid (absolute error below 2^-24).  So W x is the product of the exact weights with an X
-// rounded to 11 bits, accumulated in fp32 by v_mfma_f32_16x16x32_f16.
+// Tiled MFMA projection for many rows (decode batches of 32+ rows, prefill) of bf16 models:
+// Y[M, N] = X[M, K] W[N, K]^T with X in fp16 (the activation type of bf16 models, see ActOf) and the bf16
+// weights converted to fp16 as they are staged (exactly wherever fp16 is normal, see bf16x2_to_f16x2),
+// accumulated in fp32 by v_mfma_f32_16x16x32_f16.  The row-chunked kernels of gemm.hip stream the
+// weights past a handful of rows; here the product is compute-bound and the tiles are MFMA-shaped.
 //
 // Shape of the kernel:
 //   * a work-group (4 waves) computes a BM-row x (32 U)-column tile, U <= UM "units" of 32 weight rows
@@ -47,12 +41,9 @@ DF_DEVICE int lds_off(int r, int c) { return r * kBK + ((c ^ sw(r)) << 3); }
 
 DF_DEVICE u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Two bf16 (low half: element 0) -> two fp16, exact in fp16's normal range (see the file comment).
-DF_DEVICE uint32_t bf2_to_h2(uint32_t w) {
-  const float e0 = __builtin_bit_cast(float, w << 16), e1 = __builtin_bit_cast(float, w & 0xffff0000u);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+DF_DEVICE u32x4 bf8_to_h8(u32x4 v) {
+  return (u32x4){bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
 }
-DF_DEVICE u32x4 bf8_to_h8(u32x4 v) { return (u32x4){bf2_to_h2(v.x), bf2_to_h2(v.y), bf2_to_h2(v.z), bf2_to_h2(v.w)}; }
 
 DF_DEVICE void mma(f32x4 &acc, u32x4 a, u32x4 b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
@@ -251,7 +242,7 @@ int cu_count() {
 // the fp32 traffic of K-range partials.  DFLASH_TC_{BM,S,NCH} override it for sweeps.
 bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   const bool swiglu = a.epi == EPI_SWIGLU;
-  if (a.M < 1 || a.K % kBK || a.ksplit != 1 || a.ss_in || a.x_lo) return false;
+  if (a.M < 1 || a.K % kBK || a.ksplit != 1 || a.ss_in) return false;
   if (a.epi != EPI_STORE_F32 && a.epi != EPI_PARTIAL && !swiglu) return false;
   if (swiglu ? (a.N % 16 || a.nseg != 2) : a.N % 32) return false;
   if (!swiglu)

@@ -18,22 +18,20 @@ struct GemmSeg {
 };
 
 struct GemmArgs {
-  const void *x;
-  const void *x_lo;  // low plane of X (bf16 models: X = x + x_lo, see store_x), or null; same ldx
+  const void *x;  // X in the activation type (fp16 for bf16 models, see ActOf)
   int32_t ldx;
   int32_t M, N, K;      // N: output columns (SWIGLU: ffn width; otherwise total segment rows)
   int32_t nseg;         // segments concatenated along N (SWIGLU: 0 = gate, 1 = up)
   GemmSeg seg[kGemmMaxSeg];
   int32_t epi;
   float *out_f32;       // EPI_STORE_F32; EPI_PARTIAL: K range s writes out_f32 + s * part_stride
-  void *out_act;        // EPI_SWIGLU (an X operand: hi plane)
-  void *out_act_lo;     //   its low plane (or null)
+  void *out_act;        // EPI_SWIGLU (an X operand, activation type)
   int32_t ld_out;
   int32_t ksplit;       // K ranges, one per grid row (> 1 only with EPI_PARTIAL)
   int64_t part_stride;  // EPI_PARTIAL: elements between the K ranges' output slices
   int32_t row_off;      // global row of local row 0
   // Optional selection of the X rows (x_take > 0): global row r reads X row (r / x_take) * x_stride +
-  // x_off + r % x_take of the unmoved x (and x_lo) -- e.g. the last x_take of every x_stride rows.
+  // x_off + r % x_take of the unmoved x -- e.g. the last x_take of every x_stride rows.
   // Without it local row r reads X row r of x (row chunks move x).
   int32_t x_take, x_stride, x_off;
   // Optional RMSNorm of the X rows, applied to Y (EPI_STORE_F32, EPI_PARTIAL, EPI_SWIGLU): X holds
@@ -47,14 +45,13 @@ struct GemmArgs {
   // o = (r / sel_stride) * sel_take + r % sel_stride - sel_offset, also get xg[o][n] = act(v * gain[n])
   // and ss_out[o * ss_out_ld + tile] = the sum of v^2 over the tile's 32 columns (the next projection's
   // ss_in, ss_n = N / 32).
-  // feat and xg are X operands of later projections: hi planes, with their low planes feat_lo / xg_lo
-  // (null: one plane).
+  // feat and xg are X operands of later projections (activation type).
   float *resid;
   int32_t ld_resid;
-  void *feat, *feat_lo;
+  void *feat;
   int32_t ld_feat;
   const float *gain;
-  void *xg, *xg_lo;
+  void *xg;
   int32_t ld_xg;
   float *ss_out;
   int32_t ss_out_ld;
@@ -69,18 +66,7 @@ struct GemmArgs {
   int32_t *sk_cnt;
   int32_t sk_max_wg, sk_max_tiles;
   int32_t sk_force;  // take the stream-K kernel whatever the epilogue (launch_gemm fails if it cannot)
-  // Optional scratch of the decode-batch path (gemm_mb_ok): raw fp32 sums of up to mb_raw_cap
-  // elements ([K range][M][N]).
-  float *mb_raw;
-  int64_t mb_raw_cap;
-  // EPI_PARTIAL on that path with more than one K range: the ranges' sums, scaled by the deferred
-  // norm's 1/rms, are the output themselves ([range][M][N] in mb_raw, no reduce launch); the consumer
-  // adds gemm_mb_slices() slices in order.
-  int32_t mb_direct;
 };
-// Decode batches of kMbMinRows .. kMbMaxRows rows run all rows in one tiled launch (K split over at
-// most kMbMaxSplit ranges, reduced by a second launch) instead of row chunks.
-constexpr int kMbMinRows = 32, kMbMaxRows = 256, kMbMaxSplit = 8;
 constexpr int kSkTileElems = 16 * 32;  // entries of one partial tile (16 rows x 32 columns)
 constexpr int kSkMaxWg = 1024;         // stream-K work-groups at most (one per CU)
 // Stream-K scratch of a projection with N output columns, as one block: the partial tiles of up to
@@ -92,18 +78,11 @@ hipError_t launch_zero_i32(int32_t *p, int32_t n, hipStream_t s);
 
 // dtype: 0 bf16, 1 fp32.  e0 / e1 (may be null): events recorded at the kernel's start and end.
 hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
-// Whether launch_gemm runs `a` (all of its M rows at once) on the tiled large-M kernel.
-bool gemm_mm_ok(const GemmArgs &a, int dtype);
-// Whether `a` (a decode batch, all M rows at once) runs on launch_gemm_mb.
-bool gemm_mb_ok(const GemmArgs &a, int dtype);
-hipError_t launch_gemm_mb(const GemmArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
-// The number of K ranges launch_gemm_mb splits `a` into (call only where gemm_mb_ok holds).
-int gemm_mb_slices(const GemmArgs &a);
 // K ranges for an EPI_PARTIAL projection of M rows: enough work-groups to cover the CUs several times
 // over, each range a whole number of 256-byte super-steps, and split * M * N <= cap_elems.
 int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);
 
-// Tiled MFMA projection over many rows (gemm_tc.hip): X is one fp16 plane (x_lo null, no deferred
+// Tiled MFMA projection over many rows (gemm_tc.hip): X in fp16 (no deferred
 // norm), the bf16 weights are converted to fp16 as they are staged.  EPI_STORE_F32, EPI_PARTIAL (with
 // up to kTcMaxRanges K ranges, range z at out_f32 + z * part_stride) and EPI_SWIGLU (fp16 activation).
 // bm: tile rows (64 / 128 / 256); um: units of 32 weight rows per chunk at most; nch: chunks of the
@@ -178,12 +157,12 @@ struct NormArgs {
   const float *part;
   int32_t n_part, ld_part;
   int64_t part_stride;
-  void *feat, *feat_lo;  // X-operand planes (lo may be null)
+  void *feat;            // X operand (activation type)
   int32_t ld_feat;
   const float *gain;
   float eps;
   int32_t hidden;
-  void *out, *out_lo;    // X-operand planes (lo may be null)
+  void *out;             // X operand (activation type)
   int32_t ld_out;
   int32_t n_rows, take, stride, offset;
   // Deferred normalisation: when set, selected rows get out = act(v * gain) (no 1/rms factor) and
@@ -214,7 +193,7 @@ struct AttnArgs {
   int32_t split_tokens;  // keys per split (multiple of page_tokens)
   float *part_o;         // [rows*q_heads][n_splits][head_dim]
   float *part_ml;        // [rows*q_heads][n_splits][2]
-  void *out, *out_lo;    // [rows][q_heads*head_dim]: the o projection's X operand (planes; lo may be null)
+  void *out;             // [rows][q_heads*head_dim]: the o projection's X operand (activation type)
   int32_t ldo;
   int32_t *err;
   // Fused post-processing (calls with one query tile per sequence; q is then unused): q, k, v of the

@@ -139,10 +139,10 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
       if (x && a.n_part) x[q] = t;
       if (a.feat) {
         const size_t fi = (size_t)r * a.ld_feat + 4 * q;
-        store_x((T *)a.feat, (T *)a.feat_lo, fi + 0, t.x);
-        store_x((T *)a.feat, (T *)a.feat_lo, fi + 1, t.y);
-        store_x((T *)a.feat, (T *)a.feat_lo, fi + 2, t.z);
-        store_x((T *)a.feat, (T *)a.feat_lo, fi + 3, t.w);
+        store_x((ActOf<T> *)a.feat, fi + 0, t.x);
+        store_x((ActOf<T> *)a.feat, fi + 1, t.y);
+        store_x((ActOf<T> *)a.feat, fi + 2, t.z);
+        store_x((ActOf<T> *)a.feat, fi + 3, t.w);
       }
     }
     v[k] = t;
@@ -159,17 +159,17 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
     rs = 1.f;
   }
   const size_t y = (size_t)o * a.ld_out;
-  T *yh = (T *)a.out, *yl = (T *)a.out_lo;
+  ActOf<T> *yh = (ActOf<T> *)a.out;
   const float4 *gv = reinterpret_cast<const float4 *>(a.gain);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int q = threadIdx.x + 256 * k;
     if (q < nv) {
       const float4 gg = gv[q];
-      store_x(yh, yl, y + 4 * q + 0, v[k].x * rs * gg.x);
-      store_x(yh, yl, y + 4 * q + 1, v[k].y * rs * gg.y);
-      store_x(yh, yl, y + 4 * q + 2, v[k].z * rs * gg.z);
-      store_x(yh, yl, y + 4 * q + 3, v[k].w * rs * gg.w);
+      store_x(yh, y + 4 * q + 0, v[k].x * rs * gg.x);
+      store_x(yh, y + 4 * q + 1, v[k].y * rs * gg.y);
+      store_x(yh, y + 4 * q + 2, v[k].z * rs * gg.z);
+      store_x(yh, y + 4 * q + 3, v[k].w * rs * gg.w);
     }
   }
 }

@@ -60,12 +60,11 @@ class Engine:
             raise B.DflashError(B.E_INVAL, "configuration rejected by dflash_workspace_bytes")
         self.ws = torch.empty(ws, **u8)
         self.ctx = B.dflash_create(self.mc, self.dc, self.tw, self.dw, self.cap, self.tkv, self.dkv, self.ws)
-        act = torch.bfloat16 if t.dtype == "bf16" else torch.float32
+        # activation type of the model: fp16 for bf16 models (projection inputs, features, q, KV), fp32 otherwise
+        act = torch.float16 if t.dtype == "bf16" else torch.float32
         rows = max(max_rows, 1)
-        # target features of the last verify: bf16 models hold a high and a low plane of the rows
-        # ([2][rows][taps * hidden], the low plane right after the call's rows), fp32 models one plane
-        self.x_planes = 2 if t.dtype == "bf16" else 1
-        self.feats = torch.empty(self.x_planes * rows * len(d.taps) * t.hidden, dtype=act, device=self.device)
+        # target features of the last verify: [rows][taps * hidden] in the activation type
+        self.feats = torch.empty(rows * len(d.taps) * t.hidden, dtype=act, device=self.device)
         nl = max_slots * self.B
         self.logits = torch.empty(max(nl, 1) * t.vocab, dtype=torch.float32, device=self.device)
         self.draft_logits = torch.empty(max_slots * max(self.B - 1, 1) * t.vocab, dtype=torch.float32,
@@ -127,18 +126,9 @@ class Engine:
             B.dflash_draft_block(self.ctx, slots, self.feats, self.block, lg)
 
     def features(self, rows: int) -> torch.Tensor:
-        """The target features of the last verify (rows = its batch * q_len) as fp32 [rows, taps, hidden]:
-        bf16 models hold hi + lo bf16 planes, or one fp16 plane after a verify of F16_MIN_ROWS rows or
-        more; fp32 models one fp32 plane."""
+        """The target features of the last verify (rows = its batch * q_len) as fp32 [rows, taps, hidden]."""
         nt, H = len(self.cfg.drafter.taps), self.cfg.target.hidden
-        n = rows * nt * H
-        if self.x_planes == 1:
-            f = self.feats[:n].float()
-        elif rows >= B.F16_MIN_ROWS:
-            f = self.feats[:n].view(torch.float16).float()
-        else:
-            f = self.feats[:n].float() + self.feats[n:2 * n].float()
-        return f.view(rows, nt, H)
+        return self.feats[:rows * nt * H].float().view(rows, nt, H)
 
     def status(self):
         B.dflash_device_status(self.ctx)

@@ -311,17 +311,17 @@ def test_gpu_generator_matches_cpu():
                                    (37, 512, 96), (100, 160, 64), (128, 256, 1024), (300, 512, 2816),
                                    (1024, 7168, 5120)])
 def test_op_linear(dtype, M, N, K):
-    """The projection kernel against float64 matmul of the same (storage-typed) inputs, tiles and ragged
-    row counts included; fp32 accumulation bounds the error."""
+    """The projection kernel against float64 matmul of the same (storage-typed) inputs -- bf16 models: fp16
+    X, bf16 weights; fp32 models: fp32 -- tiles and ragged row counts included; fp32 accumulation bounds
+    the error."""
     from speculative_decoding_dflash_amd import binding as Bd
     if dtype == "bf16" and K % 32:
         pytest.skip("bf16 needs K % 32 == 0")
     rng = np.random.default_rng(M * 7 + N + K)
     x = rng.standard_normal((M, K)).astype(np.float32)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    xt = torch.from_numpy(x).to(tdt).cuda()
-    wt = torch.from_numpy(w).to(tdt).cuda()
+    xt = torch.from_numpy(x).to(torch.float16 if dtype == "bf16" else torch.float32).cuda()
+    wt = torch.from_numpy(w).to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
     y = torch.zeros(M * N, dtype=torch.float32, device="cuda")
     Bd.dflash_op_linear(Bd.BF16 if dtype == "bf16" else Bd.F32, M, N, K, xt, wt, y)
     torch.cuda.synchronize()
@@ -342,9 +342,10 @@ def test_op_linear_sk(dtype, M, N, K):
     with fewer items than work-groups."""
     from speculative_decoding_dflash_amd import binding as Bd
     rng = np.random.default_rng(M * 13 + N + K)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    xt = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(tdt).cuda()
-    wt = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(tdt).cuda()
+    xt = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))
+    xt = xt.to(torch.float16 if dtype == "bf16" else torch.float32).cuda()
+    wt = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wt = wt.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
     scratch = torch.empty(Bd.dflash_op_linear_sk_scratch_bytes(N), dtype=torch.uint8, device="cuda")
     ys = [torch.zeros(M * N, dtype=torch.float32, device="cuda") for _ in range(2)]
     for y in ys:
@@ -721,9 +722,10 @@ def test_width_vs_fp32_forward(config, layers):
     and the 4B width (hidden 2560, 32 q / 8 kv heads x 128: a GQA group of 4, FFN 9728) against an
     independent fp32 forward of the same tokens, as the depth grows: a 128-token prefill
     (tiled projections, every row's logits) and 8 plain-decoding steps (row-chunked projections, split
-    decode attention).  Every depth is held to the bf16 tolerance (2e-2): the device keeps projection
-    inputs as high + low bf16 planes and the attention operands in fp16, so the independent roundings
-    that accumulate over 64 random-weight layers stay far below it."""
+    decode attention).  Every depth is held to the bf16 tolerance (2e-2): the device keeps every operand
+    of its matrix products other than the bf16 weights -- projection inputs, q, the KV cache, the
+    softmax weights -- in fp16, so the independent roundings that accumulate over 64 random-weight
+    layers stay far below it."""
     from synth import gpu as sg
     from synth.configs import with_layers
     from speculative_decoding_dflash_amd.runner import Engine

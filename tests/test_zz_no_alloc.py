@@ -10,9 +10,9 @@ pytestmark = pytest.mark.gpu
 
 def _inputs(M, N, K, dtype, seed):
     rng = np.random.default_rng(seed)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(tdt).cuda()
-    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(tdt).cuda()
+    xt, wt = (torch.float16, torch.bfloat16) if dtype == "bf16" else (torch.float32, torch.float32)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(xt).cuda()
+    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(wt).cuda()
     return x, w
 
 
