@@ -168,6 +168,23 @@ def step_flops_batch(cfg, ns, taus) -> float:
     return f
 
 
+def prefill_flops(cfg, lens) -> float:
+    """Algorithmic flops of prefilling prompts of the given lengths (one verify over every prompt row and
+    the drafter injection of the rows a sliding window can still see): 2 per multiply-add of every
+    projection over its rows (the LM head over one logits row per prompt), plus causal attention (QK^T
+    and PV over keys 0..p for the query at p)."""
+    t, d = cfg.target, cfg.drafter
+    H, V = t.hidden, t.vocab
+    lp = t.layer_params()
+    f = 0.0
+    for P in lens:
+        f += 2.0 * P * t.layers * lp + 2.0 * V * H
+        f += 4.0 * t.q_heads * t.head_dim * (P * (P + 1) / 2) * t.layers
+        inj = min(P, d.window + d.block_size) if d.window else P
+        f += 2.0 * inj * (len(d.taps) * H * H + d.layers * 2 * t.kv_dim * H)
+    return f
+
+
 def cpu_baseline(cfg, tau: float):
     """The oracle (float64 numpy, as it stands) on a bounded sample of one step of the workload: one
     27B-shaped target layer over a block of 8 at context 1536 (random cache contents), the LM head over
@@ -417,6 +434,12 @@ def batch_main(args, cfg, conc: int, weights=None, quick: bool = False):
         "configured": conf,
         "prefill_s": round(pre_s, 2),
         "prefill_tok_s": round(sum(lens) / pre_s, 1),
+        "prefill": {"requests": conc, "tokens": int(sum(lens)), "s": round(pre_s, 3),
+                    "tok_s": round(sum(lens) / pre_s, 1), "tflop": round(prefill_flops(cfg, lens) / 1e12, 2),
+                    "tflops": round(prefill_flops(cfg, lens) / pre_s / 1e12, 1),
+                    "mfma_frac": round(prefill_flops(cfg, lens) / pre_s / 1e12 / MFMA_PEAK_TFS, 4),
+                    "method": "each request prefilled in turn (one verify over its prompt rows, then the "
+                              "drafter injection), wall clock with a device synchronisation at both ends"},
         "tau_sweep_planted_greedy": sweep,
         "projections": {"launches_per_step": rep_n, "ms_per_step": round(gemm_ms, 4), "rows": rows_proj,
                         "hbm_gbs": round(rep_bytes / (gemm_ms / 1e3) / 1e9, 1),

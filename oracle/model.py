@@ -41,7 +41,7 @@ from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
-from . import ops
+from . import dflash2, ops
 
 
 @dataclass
@@ -92,9 +92,14 @@ class KVCache:
         return c
 
 
-def _layer_qkv(w: Dict[str, np.ndarray], p: str, s: Shape, x: np.ndarray, pos: np.ndarray, rowwise: bool):
-    """Pre-norm, q/k/v projections, per-head q/k RMSNorm and RoPE for rows x at positions pos."""
+def _layer_qkv(w: Dict[str, np.ndarray], p: str, s: Shape, x: np.ndarray, pos: np.ndarray, rowwise: bool,
+               conv: Tuple[int, int] = (0, 0)):
+    """Pre-norm, q/k/v projections, per-head q/k RMSNorm and RoPE for rows x at positions pos.
+    conv = (taps, group): the normed rows (one block, in order) first pass through the DFlash2 dynamic
+    convolution (oracle/dflash2.py)."""
     xn = ops.rms_norm(x, w[p + "attn_norm"], s.rms_eps)
+    if conv[0]:
+        xn = dflash2.dyn_conv(xn, w[p + "w_conv"], conv[0], conv[1])
     q = ops.linear(xn, w[p + "wq"], rowwise).reshape(len(x), s.q_heads, s.head_dim)
     k = ops.linear(xn, w[p + "wk"], rowwise).reshape(len(x), s.kv_heads, s.head_dim)
     v = ops.linear(xn, w[p + "wv"], rowwise).reshape(len(x), s.kv_heads, s.head_dim)
@@ -195,9 +200,10 @@ class Drafter:
         pos = np.arange(n, n + B)
         x = self.embed[toks].copy()
         keys = np.arange(n + B)
+        conv = (self.d.conv_kernel, self.d.conv_group)
         for j in range(self.d.layers):
             p = f"d.L{j}."
-            q, k, v = _layer_qkv(w, p, s, x, pos, self.rowwise)
+            q, k, v = _layer_qkv(w, p, s, x, pos, self.rowwise, conv)
             cache.write(j, pos, k, v)
             attn = []
             for i in range(B):
@@ -209,5 +215,9 @@ class Drafter:
         return ops.linear(xn, self.lm_head, self.rowwise)
 
     def draft(self, cache: KVCache, anchor: int, n: int) -> List[int]:
-        z = self.draft_logits(cache, anchor, n).astype(np.float32)
+        """Argmax drafts, or with the DFlash2 selector the best path through its candidates."""
+        z = self.draft_logits(cache, anchor, n)
+        if self.d.selector_top_k:
+            return dflash2.select(z, anchor, self.embed, self.w["d.sel_u"], self.w["d.sel_v"], self.d.selector_top_k)
+        z = z.astype(np.float32)
         return [int(np.argmax(row)) for row in z]

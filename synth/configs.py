@@ -47,6 +47,13 @@ class DrafterCfg:
     block_size: int
     mask_id: int
     window: int = 0  # sliding window in tokens; 0 means unbounded
+    # DFlash2 variants (oracle/dflash2.py): dynamic convolution taps along the block (0: off) and the
+    # channels sharing a tap set; selector candidates per draft position (0: argmax drafts) and the rank
+    # of its transition factors
+    conv_kernel: int = 0
+    conv_group: int = 16
+    selector_top_k: int = 0
+    selector_rank: int = 256
 
 
 @dataclass(frozen=True)
@@ -113,7 +120,18 @@ B27 = RunCfg(
 LONG = replace(B27, name="27b-long", concurrency=32, prompt_len=8192, prompt_len_range=(4096, 8192),
                gen_len=512)
 
-CONFIGS = {c.name: c for c in (TINY, SMALL, B4, B27, LONG)}
+# The same workloads with the DFlash2 drafter variants switched on (2-tap dynamic convolution over groups
+# of 16 channels, 16 selector candidates; rank 256, or 32 at the tiny width).
+def dflash2(cfg: RunCfg, rank: int = 256) -> RunCfg:
+    return replace(cfg, name=cfg.name + "-dflash2",
+                   drafter=replace(cfg.drafter, conv_kernel=2, conv_group=16, selector_top_k=16, selector_rank=rank))
+
+
+TINY2 = dflash2(TINY, rank=32)
+SMALL2 = dflash2(SMALL)
+B27_2 = dflash2(B27)
+
+CONFIGS = {c.name: c for c in (TINY, SMALL, B4, B27, LONG, TINY2, SMALL2, B27_2)}
 
 
 def with_layers(cfg: RunCfg, target_layers: int, drafter_layers: int, taps: Tuple[int, ...]) -> RunCfg:
@@ -156,5 +174,10 @@ def tensor_shapes(t: DecoderCfg, d: DrafterCfg) -> List[Tuple[str, Tuple[int, ..
     out.append(("d.hidden_norm", (h,), "g"))
     for j in range(d.layers):
         layer(f"d.L{j}.")
+        if d.conv_kernel:
+            out.append((f"d.L{j}.w_conv", (d.conv_kernel * h // d.conv_group, h), "w"))
     out.append(("d.final_norm", (h,), "g"))
+    if d.selector_top_k:
+        out.append(("d.sel_u", (d.selector_rank, h), "w"))
+        out.append(("d.sel_v", (d.selector_rank, h), "w"))
     return out

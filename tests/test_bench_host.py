@@ -57,3 +57,21 @@ def test_batched_bytes_and_flops():
     assert np.isclose(d_att, 4.0 * B * t.q_heads * t.head_dim * (t.layers + Ld))
     d_far = bench.step_flops_batch(cfg, [5001], [1]) - bench.step_flops_batch(cfg, [5000], [1])
     assert np.isclose(d_far, 4.0 * B * t.q_heads * t.head_dim * t.layers)
+
+
+def test_prefill_flops():
+    cfg = synth.CONFIGS["27b"]
+    t, d = cfg.target, cfg.drafter
+    # a prompt of P rows: every projection over P rows (2 flops per multiply-add of the layer's weight
+    # matrices), the LM head over one row, causal attention over P (P + 1) / 2 (query, key) pairs, and
+    # the injection of the rows the drafter's window can still see (at most W + B of them)
+    P = 100
+    lp = sum(math.prod(s) for n, s, k in synth.tensor_shapes(t, d) if n.startswith("t.L0.") and k == "w" and len(s) == 2)
+    inj = len(d.taps) * t.hidden * t.hidden + d.layers * 2 * t.kv_dim * t.hidden
+    want = (2.0 * P * t.layers * lp + 2.0 * t.vocab * t.hidden + 4.0 * t.q_heads * t.head_dim * P * (P + 1) / 2 * t.layers
+            + 2.0 * P * inj)
+    assert np.isclose(bench.prefill_flops(cfg, [P]), want)
+    long_p = 6000  # past the window: the injection is capped at W + B rows
+    extra = bench.prefill_flops(cfg, [long_p + 1]) - bench.prefill_flops(cfg, [long_p])
+    assert np.isclose(extra, 2.0 * t.layers * lp + 4.0 * t.q_heads * t.head_dim * (long_p + 1) * t.layers)
+    assert np.isclose(bench.prefill_flops(cfg, [P, P]), 2 * bench.prefill_flops(cfg, [P]))
