@@ -84,12 +84,23 @@ typedef struct {
  * taps[0..n_taps-1] are injected ([P3] "结构一览", target_layer_ids); block_size B positions per
  * draft, the first being the anchor and the rest mask_id ([P3] "DFlash 2 的三个设计"); context keys
  * limited to a sliding window of `window` tokens (0 = unbounded; [P3] "结构一览").  The drafter
- * uses the target's embedding table and LM head. */
+ * uses the target's embedding table and LM head.
+ * DFlash2 variants ([P3] "DFlash 2 的三个设计", configuration values only; 0 switches each off):
+ *   conv_kernel (1..4) taps of a dynamic convolution along the block applied to every drafter layer's
+ *     normed attention input before its q/k/v projections: y_i[c] = sum_{t < taps, i - t >= 0}
+ *     a_i[c / conv_group][t] x_{i-t}[c] with a_i[g][.] = softmax over t of (W_conv x_i)[g * taps + t]
+ *     (W_conv: dflash_layer_weights.w_conv, [conv_kernel * hidden / conv_group, hidden]);
+ *   selector_top_k (1..32) candidates per draft position (logit desc, id asc) and the draft path
+ *     through them maximising sum_i z_i + (U E[t_{i-1}]) . (V E[t_i]) / sqrt(selector_rank) from the
+ *     anchor t_0 (Viterbi in fp32; ties to the lowest candidate index; U, V: dflash_drafter_weights
+ *     sel_u, sel_v [selector_rank, hidden]; E the embedding table).  Not with stochastic drafts. */
 typedef struct {
   int32_t layers;
   int32_t n_taps;
   int32_t taps[DFLASH_MAX_TAPS];
   int32_t block_size, mask_id, window;
+  int32_t conv_kernel, conv_group;
+  int32_t selector_top_k, selector_rank;
 } dflash_drafter_cfg;
 
 /* One decoder layer: device pointers, borrowed. */
@@ -105,6 +116,7 @@ typedef struct {
   const void *w_gate;    /* [ffn, hidden] */
   const void *w_up;      /* [ffn, hidden] */
   const void *w_down;    /* [hidden, ffn] */
+  const void *w_conv;    /* drafter layers with conv_kernel > 0: [conv_kernel*hidden/conv_group, hidden]; else null */
 } dflash_layer_weights;
 
 typedef struct {
@@ -119,6 +131,7 @@ typedef struct {
   const void *hidden_norm;            /* fp32 [hidden] */
   const void *final_norm;             /* fp32 [hidden] */
   const dflash_layer_weights *layers; /* host array [layers] (wq..w_down as for the target) */
+  const void *sel_u, *sel_v;          /* selector_top_k > 0: [selector_rank, hidden] each; else null */
 } dflash_drafter_weights;
 
 /* Per-request sampling ([P1] model-card paragraph; [P3] "实测数据": temperature 1.0, top-p 0.95,
@@ -224,6 +237,13 @@ dflash_status dflash_draft_block(dflash_ctx *ctx, hipStream_t stream, int32_t ba
 dflash_status dflash_draft_block_sampled(dflash_ctx *ctx, hipStream_t stream, int32_t batch, const int32_t *slots,
                                          const void *d_feats, const dflash_sampling *sampling, int32_t *d_block,
                                          int32_t *d_q_ids, float *d_q_p, float *d_logits);
+
+/* Test access to the selector of the last dflash_draft_block call (selector_top_k > 0): the candidate
+ * ids [batch][B-1][K] and their logits, and the transitions [batch][B-1][K][K] (entry [b][i][k'][k]:
+ * from candidate k' of draft row i-1 -- the anchor, k' = 0, for i = 0 -- to candidate k of row i) in
+ * fp32, copied on `stream` into device buffers of the caller. */
+dflash_status dflash_selector_state(dflash_ctx *ctx, hipStream_t stream, int32_t batch, int32_t *d_cand_ids,
+                                    float *d_cand_logits, float *d_trans);
 
 /* Accept / resample for drafts drawn from known distributions q (d_q_ids / d_q_p as written by
  * dflash_draft_block_sampled, or any caller-built rows in that layout whose q(d_i) > 0): draft d at

@@ -36,12 +36,14 @@ class ModelCfg(C.Structure):
 
 class DrafterCfg(C.Structure):
     _fields_ = [("layers", C.c_int32), ("n_taps", C.c_int32), ("taps", C.c_int32 * MAX_TAPS),
-                ("block_size", C.c_int32), ("mask_id", C.c_int32), ("window", C.c_int32)]
+                ("block_size", C.c_int32), ("mask_id", C.c_int32), ("window", C.c_int32),
+                ("conv_kernel", C.c_int32), ("conv_group", C.c_int32), ("selector_top_k", C.c_int32),
+                ("selector_rank", C.c_int32)]
 
 
 class LayerWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm",
-                                          "w_gate", "w_up", "w_down")]
+                                          "w_gate", "w_up", "w_down", "w_conv")]
 
 
 class TargetWeights(C.Structure):
@@ -51,7 +53,7 @@ class TargetWeights(C.Structure):
 
 class DrafterWeights(C.Structure):
     _fields_ = [("fc", C.c_void_p), ("hidden_norm", C.c_void_p), ("final_norm", C.c_void_p),
-                ("layers", C.POINTER(LayerWeights))]
+                ("layers", C.POINTER(LayerWeights)), ("sel_u", C.c_void_p), ("sel_v", C.c_void_p)]
 
 
 class Sampling(C.Structure):
@@ -85,6 +87,7 @@ def _load() -> C.CDLL:
         "dflash_device_status": (I, [V, V]),
         "dflash_op_linear": (I, [V, I, I, I, I, V, V, V]),
         "dflash_op_linear_f16x": (I, [V, I, I, I, V, V, V, I, P(I)]),
+        "dflash_selector_state": (I, [V, V, I, V, V, V]),
         "dflash_op_linear_sk_scratch_bytes": (S, [I]),
         "dflash_op_linear_sk": (I, [V, I, I, I, I, V, V, V, V, S]),
         "dflash_op_linear_sk_noalloc": (I, [V, I, I, I, I, V, V, V]),
@@ -195,6 +198,11 @@ def dflash_op_linear_f16x(M: int, N: int, K: int, x, w, y, max_ranges: int = 1, 
     n = C.c_int32(1)
     _check(lib.dflash_op_linear_f16x(_stream(stream), M, N, K, _ptr(x), _ptr(w), _ptr(y), max_ranges, C.byref(n)))
     return n.value
+
+
+def dflash_selector_state(ctx: int, batch: int, ids, logits, trans, stream=None):
+    """The last draft's selector candidates [batch, B-1, K] (ids, logits) and transitions [batch, B-1, K, K]."""
+    _check(lib.dflash_selector_state(ctx, _stream(stream), batch, _ptr(ids), _ptr(logits), _ptr(trans)))
 
 
 def dflash_op_linear_sk_scratch_bytes(N: int) -> int:

@@ -29,6 +29,7 @@ SOURCES = {
     "gemm_tc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attention.hip": [],
     "rows.hip": [],
+    "dflash2.hip": [],
     "sampler.hip": [],
     "decide.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],

@@ -51,7 +51,7 @@ constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized at
 // Workspace carve-up; offsets in bytes.
 struct Layout {
   size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, tcr, att_o, att_ml, dlogits,
-      cid, cp, cn, skey, sidx, total;
+      cid, cp, cn, skey, sidx, cu, xc, sel_id, sel_s, sel_x, sel_y, sel_t, total;
   size_t part_elems, att_rows, tcr_elems;
   int ss_ld, sk_tiles;
 };
@@ -110,6 +110,20 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.cn = take(sizeof(int32_t) * srows);
   L.skey = take(sizeof(uint32_t) * srows * kFilterScratch);
   L.sidx = take(sizeof(int32_t) * srows * kFilterScratch);
+  // DFlash2 variants: the dynamic convolution's tap logits and output rows; the selector's candidates,
+  // gathered embedding rows, their rank-r projections and the transitions
+  if (d->conv_kernel > 0) {
+    L.cu = take(sizeof(float) * R * (d->conv_kernel * H / d->conv_group));
+    L.xc = take(es * R * H);
+  }
+  if (d->selector_top_k > 0) {
+    const size_t nd = B > 1 ? B - 1 : 1, K = d->selector_top_k, per = 1 + nd * K;
+    L.sel_id = take(sizeof(int32_t) * cap->max_slots * nd * kMaxTopK);
+    L.sel_s = take(sizeof(float) * cap->max_slots * nd * kMaxTopK);
+    L.sel_x = take(es * cap->max_slots * per * H);
+    L.sel_y = take(sizeof(float) * cap->max_slots * per * 2 * d->selector_rank);
+    L.sel_t = take(sizeof(float) * cap->max_slots * nd * K * K);
+  }
   L.total = off;
   return L;
 }
@@ -133,6 +147,16 @@ const char *check_cfg(const dflash_model_cfg *c, const dflash_drafter_cfg *d, co
   if (d->block_size < 1 || d->block_size > DFLASH_MAX_BLOCK) return "block_size out of range";
   if (d->mask_id < 0 || d->mask_id >= c->vocab) return "mask_id out of range";
   if (d->window < 0) return "window must be >= 0";
+  if (d->conv_kernel < 0 || d->conv_kernel > kConvMaxTaps) return "conv_kernel must be in [0, 4]";
+  if (d->conv_kernel > 0) {
+    if (d->conv_group < 1 || c->hidden % d->conv_group) return "conv_group must divide hidden";
+    const int n = d->conv_kernel * c->hidden / d->conv_group;
+    if (n % (c->dtype == DFLASH_BF16 ? 32 : 16)) return "conv_kernel * hidden / conv_group must be a multiple of 32 (bf16) or 16";
+  }
+  if (d->selector_top_k < 0 || d->selector_top_k > kSelMaxK || d->selector_top_k > c->vocab)
+    return "selector_top_k must be in [0, 32] and at most vocab";
+  if (d->selector_top_k > 0 && (d->selector_rank < 1 || d->selector_rank % 32 || d->block_size < 2))
+    return "selector_rank must be a positive multiple of 32 (and block_size >= 2)";
   if (cap->max_slots < 1 || cap->max_slots > DFLASH_MAX_BATCH) return "max_slots out of range";
   if (cap->max_rows < cap->max_slots * d->block_size) return "max_rows must be at least max_slots * block_size";
   if (cap->page_tokens != 16) return "page_tokens must be 16";
@@ -147,7 +171,7 @@ struct dflash_ctx {
   dflash_drafter_cfg dcfg;
   dflash_capacity cap;
   std::vector<dflash_layer_weights> tl, dl;
-  const void *embed, *final_norm, *lm_head, *fc, *hidden_norm, *d_final_norm;
+  const void *embed, *final_norm, *lm_head, *fc, *hidden_norm, *d_final_norm, *sel_u, *sel_v;
   char *tkv, *dkv, *ws;
   Layout L;
   KVLayout kvl;
@@ -167,6 +191,7 @@ struct dflash_ctx {
   // residual projections write K-range partial sums that norm_kernel adds to the residual and
   // normalises.  Smaller calls keep the row-chunked kernels.
   bool x16 = false;
+  int sel_batch = 0;  // requests of the last selector pass (dflash_selector_state)
   // measurement: the projection launches issued while profiling is on, kept for replay
   bool profiling = false;
   struct Rec {
@@ -495,13 +520,48 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
   void *xn = c->wsp<void>(c->L.xn);
   dflash_status st;
   bool fused = false;
+  const void *xq = xn;  // the q/k/v projections' input
+  bool normed = false;  // xq is normalised already (no deferred 1/rms)
+  if (attn_mode == 1 && c->dcfg.conv_kernel > 0) {
+    // DFlash2 dynamic convolution along the block: tap logits u = W_conv x (with the deferred 1/rms),
+    // then y_i = sum_t softmax_t(u_i)[group] x_{i-t} into L.xc
+    const dflash_drafter_cfg &dc = c->dcfg;
+    const int NU = dc.conv_kernel * H / dc.conv_group;
+    GemmArgs u = gemm_base(xn, H, R, NU, H, EPI_STORE_F32);
+    u.nseg = 1;
+    u.seg[0] = GemmSeg{w.w_conv, NU};
+    with_norm(c, u, *ss_n);
+    u.out_f32 = c->wsp<float>(c->L.cu);
+    u.ld_out = NU;
+    if ((st = run_gemm(c, u, R, s)) != DFLASH_OK) return st;
+    ConvArgs cv;
+    memset(&cv, 0, sizeof cv);
+    cv.x = xn;
+    cv.ldx = H;
+    cv.ss = c->x16 ? nullptr : c->wsp<float>(c->L.ss);
+    cv.ss_n = *ss_n;
+    cv.ss_ld = c->L.ss_ld;
+    cv.eps = m.rms_eps;
+    cv.u = u.out_f32;
+    cv.ld_u = NU;
+    cv.out = c->wsp<void>(c->L.xc);
+    cv.ld_out = H;
+    cv.rows = R;
+    cv.hidden = H;
+    cv.block = q_len;
+    cv.taps = dc.conv_kernel;
+    cv.group = dc.conv_group;
+    HIP_OK(launch_dyn_conv(cv, c->dt(), s));
+    xq = cv.out;
+    normed = true;
+  }
   {
-    GemmArgs a = gemm_base(xn, H, R, QD + 2 * KD, H, EPI_PARTIAL);
+    GemmArgs a = gemm_base(xq, H, R, QD + 2 * KD, H, EPI_PARTIAL);
     a.nseg = 3;
     a.seg[0] = GemmSeg{w.wq, QD};
     a.seg[1] = GemmSeg{w.wk, KD};
     a.seg[2] = GemmSeg{w.wv, KD};
-    with_norm(c, a, *ss_n);
+    if (!normed) with_norm(c, a, *ss_n);
     int np = 1;
     const float *part = nullptr;
     int64_t part_stride = 0;
@@ -679,8 +739,13 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
   };
   for (int l = 0; l < cfg->layers; ++l)
     if (!layer_ok(tw->layers[l])) return fail(DFLASH_E_INVAL, "missing weight pointer in target layer %d", l);
-  for (int l = 0; l < dcfg->layers; ++l)
+  for (int l = 0; l < dcfg->layers; ++l) {
     if (!layer_ok(dw->layers[l])) return fail(DFLASH_E_INVAL, "missing weight pointer in drafter layer %d", l);
+    if (dcfg->conv_kernel > 0 && !dw->layers[l].w_conv)
+      return fail(DFLASH_E_INVAL, "missing w_conv in drafter layer %d (conv_kernel > 0)", l);
+  }
+  if (dcfg->selector_top_k > 0 && (!dw->sel_u || !dw->sel_v))
+    return fail(DFLASH_E_INVAL, "missing selector factors sel_u / sel_v (selector_top_k > 0)");
   if (!d_target_kv || !d_drafter_kv || !d_workspace) return fail(DFLASH_E_INVAL, "null pool or workspace");
   if (((uintptr_t)d_target_kv | (uintptr_t)d_drafter_kv | (uintptr_t)d_workspace) & 255)
     return fail(DFLASH_E_INVAL, "pools and workspace must be 256-byte aligned");
@@ -697,6 +762,8 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
   c->fc = dw->fc;
   c->hidden_norm = dw->hidden_norm;
   c->d_final_norm = dw->final_norm;
+  c->sel_u = dw->sel_u;
+  c->sel_v = dw->sel_v;
   c->tkv = (char *)d_target_kv;
   c->dkv = (char *)d_drafter_kv;
   c->ws = (char *)d_workspace;
@@ -913,6 +980,66 @@ dflash_status dflash_accept_resample_q(dflash_ctx *c, hipStream_t s, int32_t bat
 
 namespace {
 
+// DFlash2 selector over the drafter's logits [batch * (B-1)][V]: top-K candidates per row (the sampler's
+// top-k stage in score mode, T = 1), their embedding rows and the anchor's gathered, projected by the
+// rank-r factors (one GEMM over both), then a Viterbi pass per request writes the drafts into d_block.
+dflash_status run_selector(dflash_ctx *c, hipStream_t s, int batch, const float *logits, int32_t *d_block) {
+  const dflash_model_cfg &m = c->cfg;
+  const dflash_drafter_cfg &dc = c->dcfg;
+  const int B = dc.block_size, nd = B - 1, K = dc.selector_top_k, r = dc.selector_rank, H = m.hidden;
+  FilterArgs f;
+  memset(&f, 0, sizeof f);
+  f.logits = logits;
+  f.rows = batch * nd;
+  f.vocab = m.vocab;
+  f.rows_per_seq = nd;
+  for (int b = 0; b < batch; ++b) {
+    f.temperature[b] = 1.f;
+    f.top_k[b] = K;
+    f.top_p[b] = 1.f;
+  }
+  f.cand_id = c->wsp<int32_t>(c->L.sel_id);
+  f.cand_s = c->wsp<float>(c->L.sel_s);
+  f.stage_key = c->wsp<uint32_t>(c->L.skey);
+  f.stage_idx = c->wsp<int32_t>(c->L.sidx);
+  filter_plan(f, K);
+  HIP_OK(launch_filter(f, s));
+  SelArgs a;
+  memset(&a, 0, sizeof a);
+  a.batch = batch;
+  a.nd = nd;
+  a.K = K;
+  a.rank = r;
+  a.hidden = H;
+  a.vocab = m.vocab;
+  a.block = d_block;
+  a.block_stride = B;
+  a.cand_id = f.cand_id;
+  a.cand_s = f.cand_s;
+  a.cand_ld = kMaxTopK;
+  a.embed = c->embed;
+  a.x = c->wsp<void>(c->L.sel_x);
+  a.proj = c->wsp<float>(c->L.sel_y);
+  a.ld_proj = 2 * r;
+  a.inv_sqrt_r = (float)(1.0 / std::sqrt((double)r));
+  a.trans = c->wsp<float>(c->L.sel_t);
+  a.out = d_block;
+  HIP_OK(launch_sel_gather(a, c->dt(), s));
+  const int rows = batch * (1 + nd * K);
+  GemmArgs g = gemm_base(a.x, H, rows, 2 * r, H, EPI_STORE_F32);
+  g.nseg = 2;
+  g.seg[0] = GemmSeg{c->sel_u, r};
+  g.seg[1] = GemmSeg{c->sel_v, r};
+  g.out_f32 = c->wsp<float>(c->L.sel_y);
+  g.ld_out = 2 * r;
+  c->x16 = m.dtype == DFLASH_BF16 && rows >= kTcMinRows;
+  dflash_status st = run_gemm(c, g, rows, s);
+  if (st != DFLASH_OK) return st;
+  HIP_OK(launch_sel_viterbi(a, s));
+  c->sel_batch = batch;
+  return DFLASH_OK;
+}
+
 // dflash_draft_block (sampling null: argmax drafts) and dflash_draft_block_sampled.
 dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const void *d_feats,
                                int32_t *d_block, float *d_logits, const dflash_sampling *sampling, int32_t *d_q_ids,
@@ -922,6 +1049,7 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   if (st != DFLASH_OK) return st;
   if (!d_feats || !d_block) return fail(DFLASH_E_INVAL, "null features or block");
   if (sampling) {
+    if (c->dcfg.selector_top_k > 0) return fail(DFLASH_E_INVAL, "stochastic drafts do not combine with the selector");
     if (!d_q_ids || !d_q_p) return fail(DFLASH_E_INVAL, "null draft candidate buffers");
     if ((st = check_sampling(sampling, batch)) != DFLASH_OK) return st;
   }
@@ -1020,6 +1148,7 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
     if (st != DFLASH_OK) return st;
   }
   float *logits = d_logits ? d_logits : c->wsp<float>(c->L.dlogits);
+  const bool selector = dc.selector_top_k > 0;
   GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, batch * nd, m.vocab, H, EPI_STORE_F32);
   a.nseg = 1;
   a.seg[0] = GemmSeg{c->lm_head, m.vocab};
@@ -1027,6 +1156,7 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   a.out_f32 = logits;
   a.ld_out = m.vocab;
   if ((st = run_gemm(c, a, batch * nd, s)) != DFLASH_OK) return st;
+  if (selector) return run_selector(c, s, batch, logits, d_block);
   FilterArgs f;
   memset(&f, 0, sizeof f);
   f.logits = logits;
@@ -1065,6 +1195,21 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
 }
 
 }  // namespace
+
+dflash_status dflash_selector_state(dflash_ctx *c, hipStream_t s, int32_t batch, int32_t *d_ids, float *d_logits,
+                                    float *d_trans) {
+  if (!c) return fail(DFLASH_E_INVAL, "null context");
+  if (c->dcfg.selector_top_k < 1) return fail(DFLASH_E_STATE, "the drafter has no selector");
+  if (batch < 1 || batch > c->sel_batch) return fail(DFLASH_E_STATE, "batch exceeds the last selector pass");
+  if (!d_ids || !d_logits || !d_trans) return fail(DFLASH_E_INVAL, "null buffer");
+  const size_t nd = c->dcfg.block_size - 1, K = c->dcfg.selector_top_k, rows = batch * nd;
+  HIP_OK(hipMemcpy2DAsync(d_ids, K * sizeof(int32_t), c->wsp<int32_t>(c->L.sel_id), kMaxTopK * sizeof(int32_t),
+                          K * sizeof(int32_t), rows, hipMemcpyDeviceToDevice, s));
+  HIP_OK(hipMemcpy2DAsync(d_logits, K * sizeof(float), c->wsp<float>(c->L.sel_s), kMaxTopK * sizeof(float),
+                          K * sizeof(float), rows, hipMemcpyDeviceToDevice, s));
+  HIP_OK(hipMemcpyAsync(d_trans, c->wsp<float>(c->L.sel_t), rows * K * K * sizeof(float), hipMemcpyDeviceToDevice, s));
+  return DFLASH_OK;
+}
 
 dflash_status dflash_draft_block(dflash_ctx *c, hipStream_t s, int32_t batch, const int32_t *slots, const void *d_feats,
                                  int32_t *d_block, float *d_logits) {

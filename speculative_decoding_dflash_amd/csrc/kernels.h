@@ -236,11 +236,51 @@ struct FilterArgs {
   // argmax mode (drafts): row r's argmax goes to argmax_out[(r / take) * stride + offset + r % take]
   int32_t *argmax_out;
   int32_t am_take, am_stride, am_offset;
+  // score mode (the selector's candidates): the top_k ids and their scores z / T (z for T = 1) go to
+  // cand_id / cand_s, no distribution
+  float *cand_s;
 };
 constexpr int kMaxTopK = 256;
 constexpr int kFilterScratch = 8192;  // stage-1 candidates per row (chunks * kmax)
 void filter_plan(FilterArgs &a, int kmax);
 hipError_t launch_filter(const FilterArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- DFlash2 drafter variants (dflash2.hip)
+constexpr int kConvMaxTaps = 4;
+constexpr int kSelMaxK = 32;
+constexpr int kSelMaxSteps = DFLASH_MAX_BLOCK - 1;
+// Dynamic convolution of the block rows x (the layer's attention input, rows b * block + i) into out.
+struct ConvArgs {
+  const void *x;     // [rows][ldx] activation type: act(x * gain) awaiting 1/rms (ss set) or normalised
+  int32_t ldx;
+  const float *ss;   // deferred-norm partial sums of squares of the rows (or null), ss_n per row
+  int32_t ss_n, ss_ld;
+  float eps;
+  const float *u;    // [rows][ld_u] tap logits (group-major: u[g * taps + t]), already scaled by 1/rms
+  int32_t ld_u;
+  void *out;         // [rows][ld_out] activation type
+  int32_t ld_out;
+  int32_t rows, hidden, block, taps, group;
+};
+hipError_t launch_dyn_conv(const ConvArgs &a, int dtype, hipStream_t s);
+// Selector over `batch` requests of nd draft rows with K candidates each.
+struct SelArgs {
+  int32_t batch, nd, K, rank, hidden, vocab;
+  const int32_t *block;  // anchors at block[b * block_stride]
+  int32_t block_stride;
+  const int32_t *cand_id;  // [batch * nd][cand_ld] (logit desc, id asc)
+  const float *cand_s;     // their logits
+  int32_t cand_ld;
+  const void *embed;       // [vocab][hidden] model type
+  void *x;                 // gather output: [batch][1 + nd K][hidden] activation type
+  const float *proj;       // [batch][1 + nd K][ld_proj] fp32: U E (rank r), then V E (rank r)
+  int32_t ld_proj;
+  float inv_sqrt_r;
+  float *trans;            // [batch][nd][K][K] fp32 transitions (row 0 of the first: from the anchor)
+  int32_t *out;            // drafts at out[b * block_stride + i], i = 1 .. nd
+};
+hipError_t launch_sel_gather(const SelArgs &a, int dtype, hipStream_t s);
+hipError_t launch_sel_viterbi(const SelArgs &a, hipStream_t s);
 
 struct DecideArgs {
   int32_t batch;

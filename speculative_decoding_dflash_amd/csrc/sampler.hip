@@ -262,6 +262,15 @@ __global__ __launch_bounds__(kT2) void topk_stage2(FilterArgs a) {
     return;
   }
   int32_t *cid = a.cand_id + (size_t)row * kMaxTopK;
+  if (a.cand_s) {  // score mode: the top K ids and their scores
+    const int Kr = min(K, a.vocab);
+    float *cs = a.cand_s + (size_t)row * kMaxTopK;
+    for (int j = tid; j < Kr; j += kT2) {
+      cid[j] = gidx[j];
+      cs[j] = key_value(gkey[j]);
+    }
+    return;
+  }
   float *cp = a.cand_p + (size_t)row * kMaxTopK;
   if (!(T > 0.0f)) {
     for (int j = tid; j < kMaxTopK; j += kT2) {

@@ -21,7 +21,9 @@ def model_cfg(t) -> B.ModelCfg:
 
 def drafter_cfg(d) -> B.DrafterCfg:
     taps = (C.c_int32 * B.MAX_TAPS)(*list(d.taps))
-    return B.DrafterCfg(d.layers, len(d.taps), taps, d.block_size, d.mask_id, d.window)
+    return B.DrafterCfg(d.layers, len(d.taps), taps, d.block_size, d.mask_id, d.window,
+                        getattr(d, "conv_kernel", 0), getattr(d, "conv_group", 16), getattr(d, "selector_top_k", 0),
+                        getattr(d, "selector_rank", 256))
 
 
 def sampling(temperature: float, top_k: int, top_p: float, seed: int) -> B.Sampling:
@@ -45,13 +47,14 @@ class Engine:
         max_pages_per_seq = max_pages_per_seq or (cfg.prompt_len + cfg.gen_len + 4 * d.block_size) // 16 + 2
         num_pages = num_pages or max_slots * max_pages_per_seq
         self.cap = B.Capacity(max_slots, max_rows, 16, num_pages, max_pages_per_seq)
-        lw = lambda p: B.LayerWeights(*[weights[p + k].data_ptr() for k in _LAYER_KEYS])
+        ptr = lambda k: weights[k].data_ptr() if k in weights else None  # optional tensors: null when absent
+        lw = lambda p: B.LayerWeights(*[weights[p + k].data_ptr() for k in _LAYER_KEYS], ptr(p + "w_conv"))
         self._tl = (B.LayerWeights * t.layers)(*[lw(f"t.L{l}.") for l in range(t.layers)])
         self._dl = (B.LayerWeights * d.layers)(*[lw(f"d.L{j}.") for j in range(d.layers)])
         self.tw = B.TargetWeights(weights["t.embed"].data_ptr(), weights["t.final_norm"].data_ptr(),
                                   weights["t.lm_head"].data_ptr(), self._tl)
         self.dw = B.DrafterWeights(weights["d.fc"].data_ptr(), weights["d.hidden_norm"].data_ptr(),
-                                   weights["d.final_norm"].data_ptr(), self._dl)
+                                   weights["d.final_norm"].data_ptr(), self._dl, ptr("d.sel_u"), ptr("d.sel_v"))
         u8 = dict(dtype=torch.uint8, device=self.device)
         self.tkv = torch.empty(B.dflash_kv_pool_bytes(self.mc, t.layers, self.cap), **u8)
         self.dkv = torch.empty(B.dflash_kv_pool_bytes(self.mc, d.layers, self.cap), **u8)

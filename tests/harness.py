@@ -9,6 +9,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
+from oracle import dflash2
 from oracle.model import Drafter, Target
 from oracle.sampling import decide, decide_q, sample_dist, sample_draft
 import synth
@@ -72,6 +73,8 @@ class StepReport:
     draft_flagged: int = 0
     draft_mismatch: int = 0
     taus: List[int] = field(default_factory=list)
+    sel_trans_err: List[float] = field(default_factory=list)  # selector transitions, max rel err per step
+    sel_steps: int = 0
 
 
 class OracleFollower:
@@ -128,6 +131,9 @@ def check_step(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_lo
     if g_dlogits is not None and qrows is not None:
         dz = fol.d.draft_logits(fol.dc, fol.anchor, n)
         rep.draft_err.extend(rel_err_rows(g_dlogits, dz).tolist())
+    elif g_dlogits is not None and fol.cfg.drafter.selector_top_k:  # drafts checked by check_selector
+        dz = fol.d.draft_logits(fol.dc, fol.anchor, n)
+        rep.draft_err.extend(rel_err_rows(g_dlogits, dz).tolist())
     elif g_dlogits is not None:
         dz = fol.d.draft_logits(fol.dc, fol.anchor, n)
         rep.draft_err.extend(rel_err_rows(g_dlogits, dz).tolist())
@@ -170,6 +176,41 @@ def check_step(rep: StepReport, fol: OracleFollower, sp, block: np.ndarray, g_lo
                 rep.draft_flagged += 1
     rep.taus.append(len(g_out))
     return feats
+
+
+def check_selector(rep: StepReport, fol: OracleFollower, block: np.ndarray, g_dlogits: np.ndarray, eng, tol: float):
+    """The DFlash2 selector of one request's block: its candidates are the oracle's top-K of the device's
+    draft logits (ids and logits exactly), its transitions those of the oracle's rank-r factors on the
+    same candidates (float64) within tol, and its drafts the oracle's float32 Viterbi over the device's
+    own candidate logits and transitions, bit for bit."""
+    import torch
+    from speculative_decoding_dflash_amd import binding as Bd
+    d = fol.cfg.drafter
+    nd, K = d.block_size - 1, d.selector_top_k
+    ids = torch.empty(nd * K, dtype=torch.int32, device="cuda")
+    lg = torch.empty(nd * K, dtype=torch.float32, device="cuda")
+    tr = torch.empty(nd * K * K, dtype=torch.float32, device="cuda")
+    Bd.dflash_selector_state(eng.ctx, 1, ids, lg, tr)
+    torch.cuda.synchronize()
+    ids = ids.view(nd, K).cpu().numpy().astype(np.int64)
+    lg = lg.view(nd, K).cpu().numpy()
+    tr = tr.view(nd, K, K).cpu().numpy()
+    w = fol.d.w
+    worst = 0.0
+    for i in range(nd):
+        o_ids, o_z = dflash2.top_candidates(g_dlogits[i].astype(np.float32), K)
+        assert np.array_equal(o_ids, ids[i]), ("selector candidates", i, o_ids[:6], ids[i][:6])
+        assert np.array_equal(o_z, lg[i]), ("selector candidate logits", i)
+        src = [int(block[0])] if i == 0 else ids[i - 1]
+        t_o = dflash2.transitions(fol.d.embed, w["d.sel_u"], w["d.sel_v"], src, ids[i])
+        t_g = tr[i][:len(src)]
+        worst = max(worst, float(np.abs(t_g - t_o).max() / max(np.abs(t_o).max(), 1e-30)))
+    rep.sel_trans_err.append(worst)
+    assert worst <= tol, ("selector transitions", worst)
+    path = dflash2.viterbi(lg.astype(np.float32), [tr[0][:1]] + [tr[i] for i in range(1, nd)])
+    want = [int(ids[i][path[i]]) for i in range(nd)]
+    assert want == [int(x) for x in block[1:]], ("selector drafts", want, list(block[1:]))
+    rep.sel_steps += 1
 
 
 # ---------------------------------------------------------------- device runs compared with the oracle
@@ -239,6 +280,8 @@ def run_e2e(cfg, W, sp, n_tokens, log_every=4, stochastic=False, eng=None):
             qi = eng.q_ids[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
             qp = eng.q_p[:(B - 1) * 256].view(B - 1, 256).cpu().numpy()
             qrows = check_q_stage(rep, fol, sp, block, g_dl, qi, qp)
+        if cfg.drafter.selector_top_k:
+            check_selector(rep, fol, block, g_dl, eng, tol)
         feats = check_step(rep, fol, sp, block, g_logits, g_dl, ids, pp, outs, tol, qrows=qrows)
         fol.commit(feats, start, tau, outs[-1])
         stream.extend(outs)
