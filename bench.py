@@ -312,6 +312,20 @@ def batch_main(args, cfg, conc: int, weights=None, quick: bool = False):
             step(samp, None if planted is None else planted[i + 1])
             taus[i].copy_(eng.n_out[:conc])
         pl = None if planted is None else planted[n_eager + 1].clone()
+        if getattr(args, "no_graph", False):  # counter runs: every step issued eagerly
+            for i in range(n_eager, Wm):
+                step(samp, None if planted is None else planted[i + 1])
+                taus[i].copy_(eng.n_out[:conc])
+            tm = Timer(torch)
+            tm.start()
+            for i in range(Wm, Wm + K):
+                step(samp, None if planted is None else planted[i + 1])
+                taus[i].copy_(eng.n_out[:conc])
+            ms = tm.stop()
+            eng.status()
+            tl = taus.cpu().numpy()
+            ns = [[lens[r] + int(tl[:i, r].sum()) for r in slots] for i in range(Wm, Wm + K)]
+            return ms, tl[Wm:], ns, sec
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(samp, pl)
@@ -547,11 +561,13 @@ def main():
 
     # 1b. the same configuration with stochastic drafts (each draft drawn from the drafter's own
     #     filtered distribution, accepted with min(1, p/q))
-    ms_q, taus_q = run_spec(eng, torch, prompt, s_conf, Wm, K, graph=graph, stochastic=True)
-    tq = taus_q[Wm:]
-    stoch = {"tok_s": round(sum(tq) / (ms_q / 1e3), 2), "ms_per_step": round(ms_q / K, 4),
-             "tau": round(sum(tq) / K, 4)}
-    log(f"[bench]   stochastic drafts: {stoch}")
+    stoch = None
+    if not d.selector_top_k:  # the DFlash2 selector proposes one deterministic path
+        ms_q, taus_q = run_spec(eng, torch, prompt, s_conf, Wm, K, graph=graph, stochastic=True)
+        tq = taus_q[Wm:]
+        stoch = {"tok_s": round(sum(tq) / (ms_q / 1e3), 2), "ms_per_step": round(ms_q / K, 4),
+                 "tau": round(sum(tq) / K, 4)}
+        log(f"[bench]   stochastic drafts: {stoch}")
 
     # 2. roofline of the projection kernel: record the projection launches of one decode step, then
     #    replay exactly those launches back to back under one pair of HIP events on the step's stream

@@ -93,7 +93,8 @@ typedef struct {
  *   selector_top_k (1..32) candidates per draft position (logit desc, id asc) and the draft path
  *     through them maximising sum_i z_i + (U E[t_{i-1}]) . (V E[t_i]) / sqrt(selector_rank) from the
  *     anchor t_0 (Viterbi in fp32; ties to the lowest candidate index; U, V: dflash_drafter_weights
- *     sel_u, sel_v [selector_rank, hidden]; E the embedding table).  Not with stochastic drafts. */
+ *     sel_u, sel_v [selector_rank, hidden], selector_rank a multiple of 32 up to 512; E the embedding
+ *     table).  Not with stochastic drafts. */
 typedef struct {
   int32_t layers;
   int32_t n_taps;

@@ -155,8 +155,8 @@ const char *check_cfg(const dflash_model_cfg *c, const dflash_drafter_cfg *d, co
   }
   if (d->selector_top_k < 0 || d->selector_top_k > kSelMaxK || d->selector_top_k > c->vocab)
     return "selector_top_k must be in [0, 32] and at most vocab";
-  if (d->selector_top_k > 0 && (d->selector_rank < 1 || d->selector_rank % 32 || d->block_size < 2))
-    return "selector_rank must be a positive multiple of 32 (and block_size >= 2)";
+  if (d->selector_top_k > 0 && (d->selector_rank < 1 || d->selector_rank % 32 || d->selector_rank > 512 || d->block_size < 2))
+    return "selector_rank must be a multiple of 32 in [32, 512] (and block_size >= 2)";
   if (cap->max_slots < 1 || cap->max_slots > DFLASH_MAX_BATCH) return "max_slots out of range";
   if (cap->max_rows < cap->max_slots * d->block_size) return "max_rows must be at least max_slots * block_size";
   if (cap->page_tokens != 16) return "page_tokens must be 16";

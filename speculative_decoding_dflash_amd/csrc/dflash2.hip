@@ -73,10 +73,13 @@ __global__ __launch_bounds__(256) void sel_gather_kernel(SelArgs a) {
   for (int c = threadIdx.x; c < a.hidden; c += 256) store_x(o, c, Elem<T>::load(e + c));
 }
 
-// One work-group per request: transitions of every draft row into LDS, then the Viterbi pass by one
-// wave (lane k: candidate k of the current row).
+// One work-group per request and draft row after row: the row's source and destination factors staged
+// in LDS (rows padded by one float so that the 16 destinations of a wave sit in different banks), its
+// transitions computed one per thread, then one Viterbi step by one wave (lane k: candidate k).
+constexpr int kSelRankMax = 512;
 __global__ __launch_bounds__(256) void sel_viterbi_kernel(SelArgs a) {
   __shared__ float s_t[kSelMaxK * kSelMaxK];
+  __shared__ float s_phi[kSelMaxK * (kSelRankMax + 1)], s_psi[kSelMaxK * (kSelRankMax + 1)];
   __shared__ float s_delta[kSelMaxK];
   __shared__ int8_t s_back[kSelMaxSteps][kSelMaxK];
   const int b = blockIdx.x, tid = threadIdx.x, K = a.K, r = a.rank;
@@ -85,12 +88,16 @@ __global__ __launch_bounds__(256) void sel_viterbi_kernel(SelArgs a) {
   for (int i = 1; i <= a.nd; ++i) {
     const int nsrc = i == 1 ? 1 : K;
     const int src0 = i == 1 ? 0 : 1 + (i - 2) * K, dst0 = 1 + (i - 1) * K;
+    const int rp = r + 1;
+    for (int e = tid; e < nsrc * r; e += 256) s_phi[(e / r) * rp + e % r] = y[(size_t)(src0 + e / r) * a.ld_proj + e % r];
+    for (int e = tid; e < K * r; e += 256) s_psi[(e / r) * rp + e % r] = y[(size_t)(dst0 + e / r) * a.ld_proj + r + e % r];
+    __syncthreads();
     // T[k'][k] = phi(src k') . psi(dst k) / sqrt(r), summed in order over the rank
     for (int e = tid; e < K * K; e += 256) {
       const int kp = e / K, k = e % K;
       float t = 0.f;
       if (kp < nsrc) {
-        const float *ph = y + (size_t)(src0 + kp) * a.ld_proj, *ps = y + (size_t)(dst0 + k) * a.ld_proj + r;
+        const float *ph = s_phi + kp * rp, *ps = s_psi + k * rp;
         for (int q = 0; q < r; ++q) t += ph[q] * ps[q];
         t *= a.inv_sqrt_r;
       }
@@ -140,7 +147,7 @@ hipError_t launch_sel_gather(const SelArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_sel_viterbi(const SelArgs &a, hipStream_t s) {
-  if (a.K < 1 || a.K > kSelMaxK || a.nd < 1 || a.nd > kSelMaxSteps) return hipErrorInvalidValue;
+  if (a.K < 1 || a.K > kSelMaxK || a.nd < 1 || a.nd > kSelMaxSteps || a.rank > kSelRankMax) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sel_viterbi_kernel, dim3(a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
