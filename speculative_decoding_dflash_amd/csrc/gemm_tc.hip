@@ -5,9 +5,10 @@
 // weights past a handful of rows; here the product is compute-bound and the tiles are MFMA-shaped.
 //
 // Shape of the kernel:
-//   * a work-group (4 waves) computes a BM-row x (32 U)-column tile, U <= UM "units" of 32 weight rows
-//     (SWIGLU: 16 gate rows and the same 16 up rows, i.e. 16 output columns); each wave holds 64 rows of
-//     the tile and 1/WC of its columns (WC = 1, 2, 4 for BM = 256, 128, 64);
+//   * a work-group (4 waves, or 8 -- two per SIMD -- for 256-row tiles) computes a BM-row x (32 U)-
+//     column tile, U <= UM "units" of 32 weight rows (SWIGLU: 16 output columns, as two 16-row fragments
+//     of 8 gate rows and the same 8 up rows, paired in the epilogue by a lane exchange); each wave holds
+//     64 rows of the tile and 1/WC of its 16-row fragments;
 //   * the units of a projection are cut into `nch` contiguous chunks of as equal a size as possible
 //     (grid x), so that a launch can have about one work-group per CU even when 32 UM does not divide
 //     N into the CU count (the 27B gate/up's 1088 units make 256 chunks of 4 or 5);
@@ -58,14 +59,15 @@ DF_DEVICE int tc_x_src(const GemmArgs &a, int m) {
   return (r / a.x_take) * a.x_stride + a.x_off + r % a.x_take;
 }
 
-template <int BM, int UM, int STG>
-__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArgs a, int nch, int steps) {
-  constexpr int WC = BM == 256 ? 1 : (BM == 128 ? 2 : 4);  // waves across the tile's columns
-  constexpr int BN = UM * 32;                              // weight rows of a full chunk
-  constexpr int NJ = BN / 16 / WC;                         // 16-row weight fragments per wave
-  constexpr int CA = BM / 32, CB = UM;                     // 16-byte loads per thread and K step
-  static_assert(BM == 64 * (4 / WC), "each wave holds 64 rows");
-  static_assert(NJ * WC * 16 == BN && NJ % 2 == 0, "a wave holds whole units");
+template <int BM, int UM, int STG, int NWV>
+__global__ __launch_bounds__(NWV * 64, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArgs a, int nch, int steps) {
+  constexpr int NT = NWV * 64;
+  constexpr int WR = BM / 64, WC = NWV / WR;  // waves across the tile's rows (64 each) and columns
+  constexpr int BN = UM * 32;                 // weight rows of a full chunk
+  constexpr int NJ = BN / 16 / WC;            // 16-row weight fragments per wave
+  // 16-byte loads per thread and K step (chunks past the tile load a valid address and are not stored)
+  constexpr int CA = (BM * 8 + NT - 1) / NT, CB = (BN * 8 + NT - 1) / NT;
+  static_assert(WR * WC == NWV && NJ * WC * 16 == BN, "wave layout");
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBK];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -96,17 +98,17 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
   const uint16_t *pa[CA], *pb[CB];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
+    const int c = tid + NT * i, row = min(c >> 3, BM - 1), kc = (c & 7) * 8;
     pa[i] = (const uint16_t *)a.x + (size_t)tc_x_src(a, min(m0 + row, a.M - 1)) * a.ldx + kc;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
-    const int c = tid + 256 * i, kc = (c & 7) * 8;
-    const int lr = (c >> 3) < nrows ? (c >> 3) : 0;  // rows past the chunk reload its first row
+    const int c = tid + NT * i, kc = (c & 7) * 8;
+    const int lr = (c >> 3) < nrows ? (c >> 3) : 0;  // rows past the chunk (or the tile) reload its first row
     const uint16_t *w;
-    if (swiglu) {  // unit u: rows 0-15 gate rows 16 u .. 16 u + 15, rows 16-31 the same up rows
-      const int u = u0 + lr / 32;
-      w = (const uint16_t *)a.seg[(lr >> 4) & 1].w + (size_t)(16 * u + (lr & 15)) * a.K;
+    if (swiglu) {  // unit u, half h (16-row fragment 2 u + h): rows 0-7 gate rows 16 u + 8 h .., 8-15 the same up rows
+      const int u = u0 + lr / 32, h = (lr >> 4) & 1;
+      w = (const uint16_t *)a.seg[(lr >> 3) & 1].w + (size_t)(16 * u + 8 * h + (lr & 7)) * a.K;
     } else {
       int nr = 32 * u0 + lr, si = 0;
       while (si + 1 < a.nseg && nr >= a.seg[si].n) {
@@ -138,13 +140,14 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
   auto store = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(&sA[buf][lds_off(c >> 3, c & 7)]) = ra[st][i];
+      const int c = tid + NT * i;
+      if ((BM * 8) % NT == 0 || c < BM * 8) *reinterpret_cast<u32x4 *>(&sA[buf][lds_off(c >> 3, c & 7)]) = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(&sB[buf][lds_off(c >> 3, c & 7)]) = bf8_to_h8(rb[st][i]);
+      const int c = tid + NT * i;
+      if ((BN * 8) % NT == 0 || c < BN * 8)
+        *reinterpret_cast<u32x4 *>(&sB[buf][lds_off(c >> 3, c & 7)]) = bf8_to_h8(rb[st][i]);
     }
   };
   auto mult = [&](int buf) {
@@ -185,21 +188,20 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArg
   if (kt + 1 < kt1) kstep(kt + 1, std::integral_constant<int, 1>{});
 
   // acc[i][j][r] = Y[row m0 + 64 wr + 16 i + 4 g + r][weight row 32 u0 + 16 (wc NJ + j) + r16]
-  if (swiglu) {
+  if (swiglu) {  // a fragment's gate sums sit in lanes r16 < 8, the matching up sums 8 lanes further
     uint16_t *out = (uint16_t *)a.out_act;
 #pragma unroll
-    for (int q = 0; q < NJ / 2; ++q) {
-      const int lr = (wc * NJ + 2 * q) * 16;  // the unit's first (gate) row in the chunk
-      if (lr >= nrows) continue;
-      const int col = 16 * (u0 + lr / 32) + r16;
+    for (int j = 0; j < NJ; ++j) {
+      const int fl = wc * NJ + j;  // the fragment in the chunk
+      if (fl * 16 >= nrows) continue;  // wave-uniform
+      const int col = 16 * (u0 + fl / 2) + 8 * (fl & 1) + (r16 & 7);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          const float gt = acc[i][j][r], up = __shfl_xor(gt, 8);
           const int m = m0 + 64 * wr + 16 * i + 4 * g + r;
-          if (m < a.M)
-            out[(size_t)(a.row_off + m) * a.ld_out + col] =
-                f32_to_f16(silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
+          if (r16 < 8 && m < a.M) out[(size_t)(a.row_off + m) * a.ld_out + col] = f32_to_f16(silu(gt) * up);
         }
     }
     return;
@@ -251,8 +253,13 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   const int env_bm = env_int("DFLASH_TC_BM", 0);
   int bm = a.M <= 64 ? 64 : (a.M <= 128 ? 128 : 256);
   if (env_bm == 64 || env_bm == 128 || env_bm == 256) bm = env_bm;
+  // 256-row tiles: eight waves (two per SIMD; DFLASH_TC_W8=0: four) with 5 or 6 units per chunk (6 only
+  // where it saves a round of work-groups: a chunk of 6 runs a few per cent slower per unit); 64- and
+  // 128-row tiles: four waves, 4 units.  DFLASH_TC_UM fixes the unit count.
   const int env_um = env_int("DFLASH_TC_UM", 0);
-  const int um = bm == 256 && env_um != 4 ? 5 : 4;
+  const int nwv = bm == 256 && env_int("DFLASH_TC_W8", 1) ? 8 : 4;
+  const int um_lo = bm != 256 ? 4 : (env_um == 4 && nwv == 4) || (env_um == 6 && nwv == 8) ? env_um : 5;
+  const int um_hi = bm == 256 && nwv == 8 && env_um == 0 ? 6 : um_lo;
   const int units = swiglu ? a.N / 16 : a.N / 32;
   const int rt = (a.M + bm - 1) / bm, nk = a.K / kBK;
   const int slots = cu_count() * (bm == 256 ? 1 : 2);
@@ -269,18 +276,20 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
     if (s > 1 && (steps < 4 || (int64_t)s * a.M * a.N > range_cap)) continue;
     const int ranges = (nk + steps - 1) / steps;
     if (ranges != s) continue;
-    const int nmin = (units + um - 1) / um;
-    for (int nch = nmin; nch <= std::min(units, nmin * 4); ++nch) {
-      if (env_nch > 0 && nch != env_nch) continue;
-      const int wgs = nch * rt * s;
-      const int rounds = (wgs + slots - 1) / slots;
-      const int umax = (units + nch - 1) / nch;
-      // a K step also stages BM X rows (from L2), worth about bm / 64 units of weight streaming
-      const double per = (umax + bm / 64.0) * steps * std::max(mfma_us, mem_us) + 1.5;
-      const double t = rounds * per + (s > 1 ? (double)s * a.M * a.N * 8 / 5e12 * 1e6 : 0.0);
-      if (t < best - 1e-9) {
-        best = t;
-        bp = TcPlan{bm, um, nch, s, steps};
+    for (int um = um_lo; um <= um_hi; ++um) {
+      const int nmin = (units + um - 1) / um;
+      for (int nch = nmin; nch <= std::min(units, nmin * 4); ++nch) {
+        if (env_nch > 0 && nch != env_nch) continue;
+        const int wgs = nch * rt * s;
+        const int rounds = (wgs + slots - 1) / slots;
+        const int umax = (units + nch - 1) / nch;
+        // a K step also stages BM X rows (from L2), worth about bm / 64 units of weight streaming
+        const double per = (umax + bm / 64.0) * steps * std::max(mfma_us, mem_us) + 1.5;
+        const double t = rounds * per + (s > 1 ? (double)s * a.M * a.N * 8 / 5e12 * 1e6 : 0.0);
+        if (t < best - 1e-9) {
+          best = t;
+          bp = TcPlan{bm, um, nch, s, steps, nwv};  // ties keep the smaller unit count
+        }
       }
     }
   }
@@ -291,14 +300,20 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
 
 template <int STG>
 static void launch_stg(const GemmArgs &a, const TcPlan &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 block(256);
+  const dim3 b4(256), b8(512);
   if (p.bm == 256) {
-    if (p.um == 5) hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
-    else hipExtLaunchKernelGGL((gemm_tc_kernel<256, 4, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    if (p.nwv == 8 && p.um == 6)
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 6, STG, 8>), grid, b8, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    else if (p.nwv == 8)
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG, 8>), grid, b8, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    else if (p.um == 5)
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    else
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 4, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   } else if (p.bm == 128) {
-    hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   } else {
-    hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG>), grid, block, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   }
 }
 

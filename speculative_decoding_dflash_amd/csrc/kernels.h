@@ -86,9 +86,10 @@ int gemm_ksplit(int M, int N, int K, int dtype, size_t cap_elems);
 // norm), the bf16 weights are converted to fp16 as they are staged.  EPI_STORE_F32, EPI_PARTIAL (with
 // up to kTcMaxRanges K ranges, range z at out_f32 + z * part_stride) and EPI_SWIGLU (fp16 activation).
 // bm: tile rows (64 / 128 / 256); um: units of 32 weight rows per chunk at most; nch: chunks of the
-// units (grid x); ranges, steps: K ranges (grid z) and 64-wide K steps per range.
+// units (grid x); ranges, steps: K ranges (grid z) and 64-wide K steps per range; nwv: waves per work-group.
 struct TcPlan {
   int bm, um, nch, ranges, steps;
+  int nwv;  // waves per work-group (4 or 8)
 };
 constexpr int kTcMaxRanges = 8;
 // false if the projection does not suit the kernel; range_cap: elements available for ranges * M * N
