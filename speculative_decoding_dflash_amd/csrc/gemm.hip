@@ -733,82 +733,4 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t s, hipEvent_t e
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ per-head q/k RMSNorm + RoPE + scatter
-// One work-group per row and group of heads.  Lane i of a head's lane group holds elements i and
-// i + d/2, exactly the pair that rotate-half RoPE rotates together.  T: the storage type of q and of
-// the KV cache.
-template <typename T>
-__global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int d = a.kv.head_dim, half = d / 2;
-  const int tpp = kWave / half;  // heads per wave
-  const int sub = lane / half, i = lane % half;
-  const int head_all = (blockIdx.y * 4 + wave) * tpp + sub;
-  const bool live = head_all < a.total_heads;
-  int si = 0, base = 0;
-  if (live)
-    while (si + 1 < a.nseg && head_all >= base + a.seg[si].heads) {
-      base += a.seg[si].heads;
-      ++si;
-    }
-  const PostSeg &sg = a.seg[si];
-  const int head = head_all - base;
-  const float *src = a.src + (size_t)row * a.ld_src + (size_t)(live ? head_all : 0) * d;
-  float v1 = src[i], v2 = src[i + half];
-  for (int sp = 1; sp < a.n_part; ++sp) {  // K-range partial sums, in order
-    v1 += src[(size_t)sp * a.part_stride + i];
-    v2 += src[(size_t)sp * a.part_stride + i + half];
-  }
-  if (sg.role == ROLE_Q || sg.role == ROLE_K) {
-    float ss = v1 * v1 + v2 * v2;
-    for (int off = half / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
-    v1 = v1 * r * sg.gain[i];
-    v2 = v2 * r * sg.gain[i + half];
-    const int pos = a.rows.pos[row];
-    const float2 cr = (pos >= 0 && pos < a.rope_rows) ? a.rope[(size_t)pos * half + i] : make_float2(1.f, 0.f);
-    // padding rows (a launch covering more rows than the call commits) are neither written nor checked
-    if ((pos < 0 || pos >= a.rope_rows) && live && i == 0 && a.rows.valid[row]) raise_err(a.err, ERR_PAGE);
-    const float cs = cr.x, sn = cr.y;
-    const float o1 = v1 * cs - v2 * sn, o2 = v2 * cs + v1 * sn;
-    v1 = o1;
-    v2 = o2;
-  }
-  if (!live) return;
-  if (sg.role == ROLE_Q) {
-    T *q = (T *)sg.dst + (size_t)row * sg.ld_dst + head * d;
-    Elem<T>::store(q + i, v1);
-    Elem<T>::store(q + i + half, v2);
-    return;
-  }
-  if (!a.rows.valid[row]) return;
-  const int pos = a.rows.pos[row], slot = a.rows.slot[row];
-  const int pidx = pos / a.kv.page_tokens;
-  const int page = (pidx < a.bt_stride) ? a.block_table[(size_t)slot * a.bt_stride + pidx] : -1;
-  if (page < 0) {
-    raise_err(a.err, ERR_PAGE);
-    return;
-  }
-  const int tok = pos % a.kv.page_tokens;
-  T *dst = (T *)sg.dst;
-  if (sg.role == ROLE_K) {
-    Elem<T>::store(dst + a.kv.k_index(page, head, tok, i), v1);
-    Elem<T>::store(dst + a.kv.k_index(page, head, tok, i + half), v2);
-  } else {
-    Elem<T>::store(dst + a.kv.v_index(page, head, tok, i), v1);
-    Elem<T>::store(dst + a.kv.v_index(page, head, tok, i + half), v2);
-  }
-}
-
-hipError_t launch_qkv_post(const QkvPostArgs &a, int dtype, hipStream_t s) {
-  if (a.n_rows == 0) return hipSuccess;
-  const int tpp = kWave / (a.kv.head_dim / 2);
-  dim3 grid(a.n_rows, (a.total_heads + 4 * tpp - 1) / (4 * tpp));
-  // q and the KV cache hold the attention operands' storage type (fp16 for bf16 models)
-  if (dtype == 0) hipLaunchKernelGGL((qkv_post_kernel<f16>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((qkv_post_kernel<float>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 }  // namespace df

@@ -1,4 +1,4 @@
-// Per-call row bookkeeping, embedding gather, RMSNorm and argmax (gfx950).
+// Per-call row bookkeeping, embedding gather, RMSNorm, q/k/v post-processing and argmax (gfx950).
 #include "kernels.h"
 
 namespace df {
@@ -109,11 +109,13 @@ DF_DEVICE float block_sum(float v, float *red) {
 
 // One work-group per row: the row value is the fp32 residual plus the projection's K-range partial
 // sums (added in range order), written back and optionally copied out as a feature tap; selected rows
-// are then RMS-normalised.  Every thread keeps its float4 slices in registers between the passes, and
-// the sum of squares is reduced in a fixed order.
-template <typename T, int VPT>
-__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
-  __shared__ float red[4];
+// are then RMS-normalised.  Each of the NT threads keeps its VPT float4 slices (the row's, rounded up to
+// a whole slice per thread) in registers between the passes; the partial ranges are read up to eight at
+// a time with every load of a round issued before the first add, so that a row's loads overlap instead
+// of waiting in turn.  The sum of squares is reduced in a fixed order.
+template <typename T, int VPT, int NT>
+__global__ __launch_bounds__(NT) void norm_kernel(NormArgs a) {
+  __shared__ float red[NT / 64];
   const int r = blockIdx.x;
   const int j = r % a.stride - a.offset;
   const bool sel = a.out != nullptr && j >= 0 && j < a.take;
@@ -122,30 +124,51 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   float4 *x = a.x ? reinterpret_cast<float4 *>(a.x + (size_t)r * a.ld_x) : nullptr;
   const float4 *p = a.part ? reinterpret_cast<const float4 *>(a.part + (size_t)r * a.ld_part) : nullptr;
   const size_t ps = (size_t)(a.part_stride / 4);
-  float4 v[VPT];
+  // slice k of this thread: q = tid + NT k; past the row it reads slice 0 again and is never stored
+  int qc[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int q = threadIdx.x + NT * k;
+    qc[k] = q < nv ? q : 0;
+  }
+  float4 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) v[k] = x ? x[qc[k]] : make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int kRound = 8;
+  for (int sp = 0; sp < a.n_part; sp += kRound) {
+    const int nr = min(kRound, a.n_part - sp);  // uniform
+    float4 u[kRound][VPT];
+#pragma unroll
+    for (int i = 0; i < kRound; ++i)
+      if (i < nr)
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) u[i][k] = p[(sp + i) * ps + qc[k]];
+#pragma unroll
+    for (int i = 0; i < kRound; ++i)
+      if (i < nr)
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          v[k].x += u[i][k].x;
+          v[k].y += u[i][k].y;
+          v[k].z += u[i][k].z;
+          v[k].w += u[i][k].w;
+        }
+  }
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int q = threadIdx.x + NT * k;
     if (q < nv) {
-      if (x) t = x[q];
-      for (int sp = 0; sp < a.n_part; ++sp) {  // K-range partial sums, in order
-        const float4 u = p[sp * ps + q];
-        t.x += u.x;
-        t.y += u.y;
-        t.z += u.z;
-        t.w += u.w;
-      }
-      if (x && a.n_part) x[q] = t;
+      if (x && a.n_part) x[q] = v[k];
       if (a.feat) {
         const size_t fi = (size_t)r * a.ld_feat + 4 * q;
-        store_x((ActOf<T> *)a.feat, fi + 0, t.x);
-        store_x((ActOf<T> *)a.feat, fi + 1, t.y);
-        store_x((ActOf<T> *)a.feat, fi + 2, t.z);
-        store_x((ActOf<T> *)a.feat, fi + 3, t.w);
+        store_x((ActOf<T> *)a.feat, fi + 0, v[k].x);
+        store_x((ActOf<T> *)a.feat, fi + 1, v[k].y);
+        store_x((ActOf<T> *)a.feat, fi + 2, v[k].z);
+        store_x((ActOf<T> *)a.feat, fi + 3, v[k].w);
       }
+    } else {
+      v[k] = make_float4(0.f, 0.f, 0.f, 0.f);  // outside the row: no part of the sum of squares
     }
-    v[k] = t;
   }
   if (!sel) return;
   float ss = 0.f;
@@ -163,7 +186,7 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   const float4 *gv = reinterpret_cast<const float4 *>(a.gain);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int q = threadIdx.x + 256 * k;
+    const int q = threadIdx.x + NT * k;
     if (q < nv) {
       const float4 gg = gv[q];
       store_x(yh, y + 4 * q + 0, v[k].x * rs * gg.x);
@@ -176,13 +199,14 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
 
 template <typename T>
 static void launch_norm_t(const NormArgs &a, hipStream_t s) {
-  const int vpt = (a.hidden / 4 + 255) / 256;
-  dim3 g(a.n_rows), b(256);
-  if (vpt <= 1) hipLaunchKernelGGL((norm_kernel<T, 1>), g, b, 0, s, a);
-  else if (vpt <= 2) hipLaunchKernelGGL((norm_kernel<T, 2>), g, b, 0, s, a);
-  else if (vpt <= 4) hipLaunchKernelGGL((norm_kernel<T, 4>), g, b, 0, s, a);
-  else if (vpt <= 8) hipLaunchKernelGGL((norm_kernel<T, 8>), g, b, 0, s, a);
-  else hipLaunchKernelGGL((norm_kernel<T, 16>), g, b, 0, s, a);
+  // 512 threads a row (two waves per SIMD with one row per CU) while that leaves each at most 4 slices
+  const int nv = a.hidden / 4;
+  const dim3 g(a.n_rows);
+  if (nv <= 512) hipLaunchKernelGGL((norm_kernel<T, 1, 512>), g, dim3(512), 0, s, a);
+  else if (nv <= 1024) hipLaunchKernelGGL((norm_kernel<T, 2, 512>), g, dim3(512), 0, s, a);
+  else if (nv <= 1536) hipLaunchKernelGGL((norm_kernel<T, 3, 512>), g, dim3(512), 0, s, a);
+  else if (nv <= 2048) hipLaunchKernelGGL((norm_kernel<T, 4, 512>), g, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((norm_kernel<T, 8, 512>), g, dim3(512), 0, s, a);
 }
 
 hipError_t launch_norm(const NormArgs &a, int dtype, hipStream_t s) {
@@ -220,6 +244,102 @@ hipError_t launch_rope_table(float2 *table, float theta, int32_t head_dim, int32
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, table, (double)theta, half, head_dim,
                      n_pos);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ per-head q/k RMSNorm + RoPE + scatter
+// One work-group per row and group of heads.  Lane i of a head's lane group holds elements i and
+// i + d/2, exactly the pair that rotate-half RoPE rotates together.  T: the storage type of q and of
+// the KV cache.
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int d = a.kv.head_dim, half = d / 2;
+  const int tpp = kWave / half;  // heads per wave
+  const int sub = lane / half, i = lane % half;
+  const int head_all = (blockIdx.y * 4 + wave) * tpp + sub;
+  const bool live = head_all < a.total_heads;
+  int si = 0, base = 0;
+  if (live)
+    while (si + 1 < a.nseg && head_all >= base + a.seg[si].heads) {
+      base += a.seg[si].heads;
+      ++si;
+    }
+  const PostSeg &sg = a.seg[si];
+  const int head = head_all - base;
+  const bool qk = sg.role == ROLE_Q || sg.role == ROLE_K;
+  // every load that does not wait on another is issued first: the row's position, the norm gains and
+  // the K-range partial sums (up to kR of them at once; they are added in range order below)
+  const int pos = a.rows.pos[row];
+  const float g1 = qk ? sg.gain[i] : 0.f, g2 = qk ? sg.gain[i + half] : 0.f;
+  const float *src = a.src + (size_t)row * a.ld_src + (size_t)(live ? head_all : 0) * d;
+  constexpr int kR = 8;
+  float u1[kR], u2[kR];
+#pragma unroll
+  for (int sp = 0; sp < kR; ++sp)
+    if (sp == 0 || sp < a.n_part) {
+      u1[sp] = src[(size_t)sp * a.part_stride + i];
+      u2[sp] = src[(size_t)sp * a.part_stride + i + half];
+    }
+  const float2 cr = (qk && pos >= 0 && pos < a.rope_rows) ? a.rope[(size_t)pos * half + i] : make_float2(1.f, 0.f);
+  float v1 = u1[0], v2 = u2[0];
+#pragma unroll
+  for (int sp = 1; sp < kR; ++sp)
+    if (sp < a.n_part) {
+      v1 += u1[sp];
+      v2 += u2[sp];
+    }
+  for (int sp = kR; sp < a.n_part; ++sp) {
+    v1 += src[(size_t)sp * a.part_stride + i];
+    v2 += src[(size_t)sp * a.part_stride + i + half];
+  }
+  if (qk) {
+    float ss = v1 * v1 + v2 * v2;
+    for (int off = half / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
+    v1 = v1 * r * g1;
+    v2 = v2 * r * g2;
+    // padding rows (a launch covering more rows than the call commits) are neither written nor checked
+    if ((pos < 0 || pos >= a.rope_rows) && live && i == 0 && a.rows.valid[row]) raise_err(a.err, ERR_PAGE);
+    const float cs = cr.x, sn = cr.y;
+    const float o1 = v1 * cs - v2 * sn, o2 = v2 * cs + v1 * sn;
+    v1 = o1;
+    v2 = o2;
+  }
+  if (!live) return;
+  if (sg.role == ROLE_Q) {
+    T *q = (T *)sg.dst + (size_t)row * sg.ld_dst + head * d;
+    Elem<T>::store(q + i, v1);
+    Elem<T>::store(q + i + half, v2);
+    return;
+  }
+  if (!a.rows.valid[row]) return;
+  const int slot = a.rows.slot[row];
+  const int pidx = pos / a.kv.page_tokens;
+  const int page = (pidx < a.bt_stride) ? a.block_table[(size_t)slot * a.bt_stride + pidx] : -1;
+  if (page < 0) {
+    raise_err(a.err, ERR_PAGE);
+    return;
+  }
+  const int tok = pos % a.kv.page_tokens;
+  T *dst = (T *)sg.dst;
+  if (sg.role == ROLE_K) {
+    Elem<T>::store(dst + a.kv.k_index(page, head, tok, i), v1);
+    Elem<T>::store(dst + a.kv.k_index(page, head, tok, i + half), v2);
+  } else {
+    Elem<T>::store(dst + a.kv.v_index(page, head, tok, i), v1);
+    Elem<T>::store(dst + a.kv.v_index(page, head, tok, i + half), v2);
+  }
+}
+
+hipError_t launch_qkv_post(const QkvPostArgs &a, int dtype, hipStream_t s) {
+  if (a.n_rows == 0) return hipSuccess;
+  const int tpp = kWave / (a.kv.head_dim / 2);
+  dim3 grid(a.n_rows, (a.total_heads + 4 * tpp - 1) / (4 * tpp));
+  // q and the KV cache hold the attention operands' storage type (fp16 for bf16 models)
+  if (dtype == 0) hipLaunchKernelGGL((qkv_post_kernel<f16>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((qkv_post_kernel<float>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

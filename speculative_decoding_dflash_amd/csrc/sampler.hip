@@ -6,9 +6,11 @@
 // reproduce them exactly.  For T = 0 the single candidate is the argmax (lowest id on ties).
 //
 // Stage 1: each row is cut into chunks of at most kChunkMax elements, one work-group per chunk.  The
-// chunk's order-preserving 32-bit keys are cached in LDS; an 8-bit-digit radix select finds the
-// chunk's k-th largest key; the chunk then emits exactly k candidates: every key above it, plus the
-// lowest-id keys equal to it (ordered by an exclusive scan over contiguous sub-ranges).
+// chunk's order-preserving 32-bit keys are cached in LDS and the chunk emits exactly its top k by
+// (key desc, id asc).  For k <= 64 the keys at or above a lower bound of the k-th largest (from the
+// waves' lane maxima) are usually few and are ranked directly; otherwise an 8-bit-digit radix select
+// finds the k-th largest key and the chunk emits every key above it plus the lowest-id keys equal to
+// it (ordered by an exclusive scan over contiguous sub-ranges).
 // Stage 2: one work-group per row sorts the union of its chunks' candidates by (key desc, id asc) --
 // the row's top k is the top k of that union -- and computes the distribution.
 #include <algorithm>
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(kT1) void topk_stage1(FilterArgs a) {
   const int c0 = chunk * a.chunk, c1 = min(a.vocab, c0 + a.chunk);
   const int n = c1 - c0;
   const float *z = a.logits + (size_t)row * a.vocab + c0;
+  uint32_t tmax = 0u;  // the largest key of this thread's elements
   {
     // every load of the thread first (a loop of load -> convert -> LDS store waits for each load in
     // turn), then the keys
@@ -101,7 +104,11 @@ __global__ __launch_bounds__(kT1) void topk_stage1(FilterArgs a) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int j = tid + i * kT1;
-      if (j < n) skey[j] = order_key(T > 0.0f ? __fdiv_rn(v[i], T) : v[i]);
+      if (j < n) {
+        const uint32_t k = order_key(T > 0.0f ? __fdiv_rn(v[i], T) : v[i]);
+        skey[j] = k;
+        tmax = max(tmax, k);
+      }
     }
   }
   __syncthreads();
@@ -141,6 +148,56 @@ __global__ __launch_bounds__(kT1) void topk_stage1(FilterArgs a) {
       oidx[0] = c0 + ri[0];
     }
     return;
+  }
+  if (Kc <= 64) {
+    // Candidates by a lower bound: the Kc largest lane maxima of a wave are Kc distinct keys of the
+    // chunk, so the chunk's Kc-th largest key is at least the Kc-th largest lane maximum of every wave
+    // (found by a bitonic sort across the wave, descending), hence at least tau, their largest.  Every
+    // key of the chunk's top Kc is then >= tau; when few keys are, each is ranked directly by
+    // (key desc, id asc) among them and the first Kc are emitted in rank order.
+    __shared__ uint32_t s_tau[kT1 / 64];
+    __shared__ uint32_t ck[kT1];
+    __shared__ int ci[kT1];
+    const int lane = tid & 63;
+    uint32_t m = tmax;
+    for (int k = 2; k <= 64; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const uint32_t o = __shfl_xor(m, j);
+        m = (((lane & k) == 0) == ((lane & j) == 0)) ? max(m, o) : min(m, o);
+      }
+    const uint32_t tw = __shfl(m, Kc - 1);
+    if (lane == 0) s_tau[tid >> 6] = tw;
+    __syncthreads();
+    uint32_t tau = s_tau[0];
+#pragma unroll
+    for (int w = 1; w < kT1 / 64; ++w) tau = max(tau, s_tau[w]);
+    int mine = 0;
+    for (int j = tid; j < n; j += kT1) mine += skey[j] >= tau;
+    int total;
+    int slot = block_excl_scan<kT1>(mine, wsum, &total);
+    if (total <= kT1) {  // uniform; otherwise (many equal keys) the radix select below
+      for (int j = tid; j < n; j += kT1)
+        if (skey[j] >= tau) {
+          ck[slot] = skey[j];
+          ci[slot] = j;
+          ++slot;
+        }
+      __syncthreads();
+      if (tid < total) {
+        const uint32_t k = ck[tid];
+        const int ix = ci[tid];
+        int rank = 0;
+        for (int e = 0; e < total; ++e) {
+          const uint32_t k2 = ck[e];
+          rank += k2 > k || (k2 == k && ci[e] < ix);
+        }
+        if (rank < Kc) {
+          okey[rank] = k;
+          oidx[rank] = c0 + ix;
+        }
+      }
+      return;
+    }
   }
   // radix select of the Kc-th largest key, 8 bits at a time
   uint32_t prefix = 0;

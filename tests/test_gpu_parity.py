@@ -207,6 +207,52 @@ def test_sampler_chi_square_and_bitexact():
     assert scipy.stats.chisquare(resample[sup], r[sup] * resample.sum()).pvalue > 1e-4
 
 
+def test_candidate_filter_paths():
+    """The sampler's candidate filter on planted logits over a 151936-token vocabulary (38 chunks of 4000
+    per row), against the oracle filter row by row: ids exact, probabilities within 2e-6.  Covers the
+    chunk shortcut (top-k <= 64: keys ranked above a bound from the waves' lane maxima) at k = 2, 7, 20
+    and 64, the radix select at k = 65, 100 and 256, rows whose keys tie heavily (values on a coarse grid:
+    the shortcut's candidate set overflows and the radix select decides), equal keys straddling the k-th
+    place (the lowest ids win), and a temperature that divides the logits."""
+    from dataclasses import replace
+    cfg = replace(synth.TINY, target=replace(synth.TINY.target, vocab=151936))
+    W = sw.model_weights(cfg)
+    V, B = cfg.target.vocab, cfg.drafter.block_size
+    S = 8
+    eng = engine(cfg, W, max_slots=S, max_rows=S * B)
+    for s_ in range(S):
+        eng.kv_alloc(s_, 4 * B)
+    rng = np.random.default_rng(11)
+    ks = [2, 7, 20, 64, 65, 100, 256, 20]
+    temps = [1.0, 0.7, 1.0, 1.0, 1.3, 1.0, 1.0, 1.0]
+    tops = [1.0, 0.95, 0.9, 1.0, 1.0, 0.8, 1.0, 1.0]
+    z = rng.standard_normal((S * B, V)).astype(np.float32) * 2.0
+    for r in range(S * B):
+        kind = r % B
+        if kind == 1:  # a coarse grid: thousands of equal keys
+            z[r] = np.round(z[r] * 2.0) / 2.0
+        elif kind == 2:  # 40 equal keys straddling the k-th place, spread over the chunks
+            top = np.argsort(-z[r], kind="stable")[:8]
+            z[r, top] = 12.0 + np.arange(8, dtype=np.float32)
+            tie = rng.choice(np.setdiff1d(np.arange(V), top), 40, replace=False)
+            z[r, tie] = 11.5
+    toks = torch.zeros(S * B, dtype=torch.int32, device="cuda")
+    samplings = [samp(synth.SamplingCfg(temps[i], ks[i], tops[i], i)) for i in range(S)]
+    eng.verify(list(range(S)), toks, B, True, B)
+    block = torch.zeros(S * B, dtype=torch.int32, device="cuda")
+    eng.accept(list(range(S)), B - 1, samplings, block=block, cands=True, logits=torch.from_numpy(z).to("cuda"))
+    gi_all = eng.cand_ids[:S * B * 256].view(S * B, 256).cpu().numpy()
+    gp_all = eng.cand_p[:S * B * 256].view(S * B, 256).cpu().numpy()
+    for r in range(S * B):
+        i = r // B
+        ids_o, p_o = sample_dist(z[r], temps[i], ks[i], tops[i])
+        k = int((gi_all[r] >= 0).sum())
+        assert k == len(ids_o), (r, ks[i], k, len(ids_o))
+        assert np.array_equal(gi_all[r, :k], ids_o), (r, ks[i])
+        assert np.abs(gp_all[r, :k] - p_o).max() <= 2e-6, (r, ks[i])
+    log(f"  candidate filter: {S * B} rows, k in {sorted(set(ks))}, ids exact")
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_e2e_stochastic_drafts(name):
     """Stochastic drafts end to end, teacher-forced: the drafter's candidate distributions match the
