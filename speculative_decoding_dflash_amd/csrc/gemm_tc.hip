@@ -59,7 +59,7 @@ DF_DEVICE int tc_x_src(const GemmArgs &a, int m) {
   return (r / a.x_take) * a.x_stride + a.x_off + r % a.x_take;
 }
 
-template <int BM, int UM, int STG, int NWV>
+template <int BM, int UM, int STG, int NWV, bool PIPE>
 __global__ __launch_bounds__(NWV * 64, BM == 256 ? 1 : 2) void gemm_tc_kernel(GemmArgs a, int nch, int steps) {
   constexpr int NT = NWV * 64;
   constexpr int WR = BM / 64, WC = NWV / WR;  // waves across the tile's rows (64 each) and columns
@@ -170,12 +170,39 @@ __global__ __launch_bounds__(NWV * 64, BM == 256 ? 1 : 2) void gemm_tc_kernel(Ge
   for (int st = 0; st < STG; ++st) load(st, kt0 + st);
   store(0, 0);
   __syncthreads();
+  // PIPE: both K halves' fragments are read first (the second half's reads overlap the first half's
+  // MFMAs) and the next step's LDS stores go between the halves, so that the MFMAs of a step are not
+  // preceded by the wait for their own fragments and followed by the stores
+  auto frags = [&](int buf, int s, u32x4 *fa, u32x4 *fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][lds_off(wr * 64 + 16 * i + r16, 4 * s + g)]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      fb[j] = *reinterpret_cast<const u32x4 *>(&sB[buf][lds_off((wc * NJ + j) * 16 + r16, 4 * s + g)]);
+  };
+  auto mmas = [&](const u32x4 *fa, const u32x4 *fb) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mma(acc[i][j], fa[i], fb[j]);
+  };
   auto kstep = [&](int kt, auto stc) {
     constexpr int st = decltype(stc)::value;
     const int buf = (kt - kt0) & 1;
-    load(st, kt + STG);
-    mult(buf);
-    if (kt + 1 < kt1) store((st + 1) % STG, buf ^ 1);
+    if constexpr (PIPE) {
+      u32x4 fa0[4], fb0[NJ], fa1[4], fb1[NJ];
+      frags(buf, 0, fa0, fb0);
+      load(st, kt + STG);
+      frags(buf, 1, fa1, fb1);
+      mmas(fa0, fb0);
+      if (kt + 1 < kt1) store((st + 1) % STG, buf ^ 1);
+      mmas(fa1, fb1);
+    } else {
+      load(st, kt + STG);
+      mult(buf);
+      if (kt + 1 < kt1) store((st + 1) % STG, buf ^ 1);
+    }
     __syncthreads();
   };
   int kt = kt0;
@@ -298,22 +325,22 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   return true;
 }
 
-template <int STG>
+template <int STG, bool PIPE>
 static void launch_stg(const GemmArgs &a, const TcPlan &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const dim3 b4(256), b8(512);
   if (p.bm == 256) {
     if (p.nwv == 8 && p.um == 6)
-      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 6, STG, 8>), grid, b8, 0, s, e0, e1, 0, a, p.nch, p.steps);
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 6, STG, 8, PIPE>), grid, b8, 0, s, e0, e1, 0, a, p.nch, p.steps);
     else if (p.nwv == 8)
-      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG, 8>), grid, b8, 0, s, e0, e1, 0, a, p.nch, p.steps);
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG, 8, PIPE>), grid, b8, 0, s, e0, e1, 0, a, p.nch, p.steps);
     else if (p.um == 5)
-      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 5, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
     else
-      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 4, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+      hipExtLaunchKernelGGL((gemm_tc_kernel<256, 4, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   } else if (p.bm == 128) {
-    hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   } else {
-    hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG, 4>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   }
 }
 
@@ -321,8 +348,14 @@ hipError_t launch_gemm_tc(const GemmArgs &a, const TcPlan &p, hipStream_t s, hip
   if (p.ranges > 1 && a.epi != EPI_PARTIAL) return hipErrorInvalidValue;
   const dim3 grid(p.nch, (a.M + p.bm - 1) / p.bm, p.ranges);
   static const int stg = env_int("DFLASH_TC_STG", 2) == 3 ? 3 : 2;
-  if (stg == 3) launch_stg<3>(a, p, grid, s, e0, e1);
-  else launch_stg<2>(a, p, grid, s, e0, e1);
+  static const bool pipe = env_int("DFLASH_TC_PIPE", 1) != 0;
+  if (pipe) {
+    if (stg == 3) launch_stg<3, true>(a, p, grid, s, e0, e1);
+    else launch_stg<2, true>(a, p, grid, s, e0, e1);
+  } else {
+    if (stg == 3) launch_stg<3, false>(a, p, grid, s, e0, e1);
+    else launch_stg<2, false>(a, p, grid, s, e0, e1);
+  }
   return hipGetLastError();
 }
 
