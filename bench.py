@@ -483,10 +483,15 @@ def main():
     ap.add_argument("--tau-sweep", default="", help="planted acceptance lengths of the batched sweep, e.g. 1,3,5,7")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the short configured runs at concurrency 8 and 32 appended to the default line")
+    ap.add_argument("--block", type=int, default=None,
+                    help="block size (1 anchor + block-1 drafts) instead of the configuration's own")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first copy 1 GiB device to device (a plain copy of known size, the reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.block is not None and not 2 <= args.block <= 16:
+        print("--block takes 2 .. 16", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build measures the "
               "single-GPU step; the path would shard by request, see the design notes.", file=sys.stderr)
@@ -502,6 +507,9 @@ def main():
     from speculative_decoding_dflash_amd.runner import Engine, sampling
 
     cfg = synth.CONFIGS[args.config]
+    if args.block is not None:
+        from dataclasses import replace
+        cfg = replace(cfg, drafter=replace(cfg.drafter, block_size=args.block))
     conc = args.concurrency or cfg.concurrency
     if conc > 1 or cfg.prompt_len_range:
         batch_main(args, cfg, conc)
@@ -640,7 +648,7 @@ def main():
     # short configured runs of the same step over batches of requests (the batched path's kernels:
     # all rows of a projection in one tiled launch, batch-aware attention splits), on the same weights
     batched = None
-    if not args.no_batched and args.config == "27b":
+    if not args.no_batched and args.config == "27b" and B == 8:
         eng.close()
         qa = argparse.Namespace(**{**vars(args), "steps": min(K, 8), "warmup": min(Wm, 2)})
         batched = {str(c): batch_main(qa, cfg, c, weights=weights, quick=True) for c in (8, 32)}
@@ -654,10 +662,11 @@ def main():
     step_gbs = bytes_step / (ms_step / 1e3) / 1e9
     import hashlib
     src = os.path.join(ROOT, "speculative_decoding_dflash_amd", "csrc", "gemm.hip")
-    traffic = GEMM_TRAFFIC["bytes_per_launch"] if args.config == "27b" and hashlib.sha256(
+    traffic = GEMM_TRAFFIC["bytes_per_launch"] if args.config == "27b" and B == 8 and hashlib.sha256(
         open(src, "rb").read()).hexdigest()[:16] == GEMM_TRAFFIC["gemm_src_sha256_16"] else None
     out = {
-        "metric": METRIC,
+        "metric": METRIC if (cfg.name, B) == ("27b", 8) else
+                  f"accepted tokens/s at conc 1 ({cfg.name}-shape, block {B}); step HBM GB/s vs peak",
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
