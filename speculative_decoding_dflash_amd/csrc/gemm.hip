@@ -405,18 +405,29 @@ __global__ __launch_bounds__(512) void gemm_sk_kernel(GemmArgs a, int per) {
   // gate rows (groups 0 .. CT/2-1) and the same up rows (groups CT/2 ..); otherwise COLS consecutive
   // rows of the concatenated segments (each segment a whole number of tiles)
   // (w0: groups 0 .. CT/2-1, w1: groups CT/2 .., each a run of COLS / 2 rows)
-  // the first two segments' bases are held from the start: the cursor reaches a new tile every few
+  // the first three segments' bases are held from the start: the cursor reaches a new tile every few
   // items, and a table read there (a vector load, as the wave index is not known to be uniform) would
   // wait for every weight load in flight
-  const T *const sw0 = (const T *)a.seg[0].w, *const sw1 = (const T *)a.seg[1].w;
+  const T *const sw0 = (const T *)a.seg[0].w, *const sw1 = (const T *)a.seg[1].w, *const sw2 = (const T *)a.seg[2].w;
+  const int sn0 = a.seg[0].n, sn1 = a.seg[1].n;
   auto tile_base = [&](int t, const T *&w0, const T *&w1) {
     if (swiglu) {
       w0 = sw0 + (size_t)((COLS / 2) * t) * a.K;
       w1 = sw1 + (size_t)((COLS / 2) * t) * a.K;
       return;
     }
-    if (a.nseg == 1) {
-      w0 = sw0 + (size_t)(COLS * t) * a.K;
+    if (a.nseg <= 3) {  // one segment, or q / k / v
+      int r0 = COLS * t;
+      const T *w = sw0;
+      if (a.nseg > 1 && r0 >= sn0) {
+        r0 -= sn0;
+        w = sw1;
+        if (a.nseg > 2 && r0 >= sn1) {
+          r0 -= sn1;
+          w = sw2;
+        }
+      }
+      w0 = w + (size_t)r0 * a.K;
       w1 = w0 + (size_t)(COLS / 2) * a.K;
       return;
     }
