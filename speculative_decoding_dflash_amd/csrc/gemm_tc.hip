@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NWV * 64, BM == 256 ? 1 : 2) void gemm_tc_kernel(Ge
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // STG register stages (2 or 3): the loads of step k + STG are issued while step k is multiplied out of
+  // STG register stages: the loads of step k + STG are issued while step k is multiplied out of
   // LDS buffer (k - k0) % 2 and steps k + 1 .. k + STG - 1 are in flight; the stage index of step k is
   // (k - k0) % STG, a template constant in the unrolled loop so that the stages stay in registers.
   u32x4 ra[STG][CA], rb[STG][CB];
@@ -347,15 +347,11 @@ static void launch_stg(const GemmArgs &a, const TcPlan &p, dim3 grid, hipStream_
 hipError_t launch_gemm_tc(const GemmArgs &a, const TcPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (p.ranges > 1 && a.epi != EPI_PARTIAL) return hipErrorInvalidValue;
   const dim3 grid(p.nch, (a.M + p.bm - 1) / p.bm, p.ranges);
-  static const int stg = env_int("DFLASH_TC_STG", 2) == 3 ? 3 : 2;
+  // two register stages (three measured no faster, and with the pipelined step they spill); the
+  // pipelined step by default, DFLASH_TC_PIPE=0 for the plain one
   static const bool pipe = env_int("DFLASH_TC_PIPE", 1) != 0;
-  if (pipe) {
-    if (stg == 3) launch_stg<3, true>(a, p, grid, s, e0, e1);
-    else launch_stg<2, true>(a, p, grid, s, e0, e1);
-  } else {
-    if (stg == 3) launch_stg<3, false>(a, p, grid, s, e0, e1);
-    else launch_stg<2, false>(a, p, grid, s, e0, e1);
-  }
+  if (pipe) launch_stg<2, true>(a, p, grid, s, e0, e1);
+  else launch_stg<2, false>(a, p, grid, s, e0, e1);
   return hipGetLastError();
 }
 
