@@ -188,8 +188,8 @@ def prefill_flops(cfg, lens) -> float:
 def cpu_baseline(cfg, tau: float):
     """The oracle (float64 numpy, as it stands) on a bounded sample of one step of the workload: one
     27B-shaped target layer over a block of 8 at context 1536 (random cache contents), the LM head over
-    a 1/16 slice of the vocabulary and the drafter's fc projection, each timed, then scaled by layer
-    and vocabulary counts to one draft + verify step."""
+    a 1/16 slice of the vocabulary and the drafter's fc projection, each run repeatedly for a few seconds
+    and averaged, then scaled by layer and vocabulary counts to one draft + verify step."""
     import numpy as np
     import synth
     from oracle import ops
@@ -209,27 +209,34 @@ def cpu_baseline(cfg, tau: float):
     cache.k[0][:ctx] = rng.standard_normal(cache.k[0][:ctx].shape)
     cache.v[0][:ctx] = rng.standard_normal(cache.v[0][:ctx].shape)
     toks = list(range(B))
-    t0 = time.perf_counter()
-    tg.forward(cache, toks, ctx, logit_rows=B)
-    t_fwd = time.perf_counter() - t0
+
+    def timed(fn, budget_s: float):
+        """Mean wall time of fn over repeated calls until about budget_s seconds have run (at least 2)."""
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if n >= 2 and el >= budget_s:
+                return el / n, n
+
+    # the one-layer forward (its LM head over the vocabulary slice included), the slice alone, the fc
+    t_fwd, n_fwd = timed(lambda: tg.forward(cache, toks, ctx, logit_rows=B), 8.0)
     x = rng.standard_normal((B, t.hidden))
-    t0 = time.perf_counter()
-    ops.linear(x, tg.w["t.lm_head"])
-    t_lm = time.perf_counter() - t0
+    t_lm, n_lm = timed(lambda: ops.linear(x, tg.w["t.lm_head"]), 2.0)
     fc = sw.tensor("d.fc", (t.hidden, len(d.taps) * t.hidden), "w", cfg.weight_seed, cfg.weight_std, t.dtype)
     fc = fc.astype(np.float64)
-    t0 = time.perf_counter()
-    ops.linear(rng.standard_normal((B, len(d.taps) * t.hidden)), fc)
-    t_fc = time.perf_counter() - t0
+    xf = rng.standard_normal((B, len(d.taps) * t.hidden))
+    t_fc, n_fc = timed(lambda: ops.linear(xf, fc), 2.0)
     t_layer = max(t_fwd - t_lm, 1e-9)
     lm_full = t_lm * t.vocab / vs
     step_s = (t.layers + d.layers) * t_layer + t_fc + lm_full * (1 + (B - 1) / B)
     return {"value": round(tau / step_s, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "step_s": round(step_s, 3),
-            "sample": f"oracle (float64 numpy) timed on one target layer over a block of {B} at context {ctx}, the LM "
-                      f"head over {vs} of {t.vocab} vocabulary rows and the drafter fc; scaled to "
-                      f"{t.layers}+{d.layers} layers and the full vocabulary; accepted tokens/s at the GPU run's "
-                      f"tau {tau:.3f}"}
+            "sample": f"oracle (float64 numpy) timed on one target layer over a block of {B} at context {ctx} "
+                      f"({n_fwd} runs), the LM head over {vs} of {t.vocab} vocabulary rows ({n_lm} runs) and the "
+                      f"drafter fc ({n_fc} runs), means over ~12 s of CPU work; scaled to {t.layers}+{d.layers} "
+                      f"layers and the full vocabulary; accepted tokens/s at the GPU run's tau {tau:.3f}"}
 
 
 MFMA_PEAK_TFS = 2500.0  # dense bf16 MFMA, MI355X published
