@@ -503,6 +503,13 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
     a.rope_rows = c->rope_rows();
     a.counters = arrive ? c->wsp<int32_t>(c->L.cnt) : nullptr;
   }
+  // Prefill-sized causal calls: the flash-style kernel (one work-group per 128 query rows and query
+  // head, keys staged once per work-group through LDS); DFLASH_ATTN_PREFILL=0 keeps the general kernel.
+  static const bool flash_prefill = !getenv("DFLASH_ATTN_PREFILL") || atoi(getenv("DFLASH_ATTN_PREFILL")) != 0;
+  if (flash_prefill && !decode && !raw_w && attn_prefill_fits(a, c->dt(), ctx_bound - 1)) {
+    HIP_OK(launch_attn_prefill(a, s));
+    return DFLASH_OK;
+  }
   HIP_OK(launch_attention(a, c->dt(), s));
   return DFLASH_OK;
 }

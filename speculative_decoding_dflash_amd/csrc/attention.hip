@@ -842,4 +842,223 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+
+// ------------------------------------------------------------------ prefill attention (flash-style)
+// Causal attention of long query blocks (prefill) for bf16 models (fp16 q and KV cache), head_dim D.
+// One work-group per (block of 128 query rows, query head, sequence), heaviest blocks first; each of its
+// 4 waves owns 32 rows (two 16-row MFMA tiles) outright, so no partial results cross waves.  Keys run
+// in blocks of 64 (4 pages): the block's K ([key][dim]) and V^T ([dim][key]) are staged in swizzled,
+// double-buffered LDS by the whole work-group, the next block's loads in registers while the current
+// one is multiplied (one barrier per block).  Per block and wave: S^T = K Q^T (v_mfma 16x16x32, q held
+// in registers), masked (key position > query position) and scaled to log2 units, an online softmax
+// per query row, then O^T += V^T P^T (v_mfma 16x16x16) with P^T taken from the S^T accumulators as they
+// lie (their layout is the B operand's), all in fp32 with fp16 operands.  The sequence's block-table
+// entries for its key range sit in LDS.
+constexpr int kPfBq = 128, kPfBk = 64, kPfMaxPages = 1024;
+// V^T rows are 128 bytes: with chunk c of row r at c ^ vsw(r), the 16 rows of a fragment read cover
+// every bank once per 32 lanes (two rows per 64 banks), as do the staging writes.
+DF_DEVICE int vsw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;            // QK^T steps of 32 dims
+  constexpr int DT = D / 16;            // 16-dim output tiles
+  constexpr int KROW = D * 2;           // LDS bytes per K row: D / 8 16-byte chunks, chunk c at c ^ (key % 16)
+  constexpr int VROW = kPfBk * 2;       // LDS bytes per V^T row: 8 chunks, chunk c at c ^ vsw(dim)
+  static_assert(D / 8 >= 16, "the K swizzle spans 16 chunks");
+  constexpr int KCH = kPfBk * D / 8 / 256, VCH = D * kPfBk / 8 / 256;  // 16-byte chunks per thread
+  static_assert(KCH * 256 * 8 == kPfBk * D && VCH * 256 * 8 == D * kPfBk, "chunking");
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2][kPfBk * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sV[2][D * VROW];
+  __shared__ int s_bt[kPfMaxPages];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int nqb = (a.q_len + kPfBq - 1) / kPfBq;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest key ranges start first
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int G = a.q_heads / a.kvl.kv_heads, kh = head / G;
+  const int pt = a.kvl.page_tokens;
+  const int row0 = b * a.q_len;                    // the sequence's first row
+  const int rlast = min(a.q_len, (qb + 1) * kPfBq) - 1;
+  const int kmax = a.rows.pos[row0 + rlast];       // the work-group's last key position (rows are in order)
+  const int nkb = (kmax + kPfBk) / kPfBk;
+  const int npg = nkb * (kPfBk / 16);
+  if (npg > kPfMaxPages) {  // a position past what the host sized the call for (uniform exit)
+    if (tid == 0) raise_err(a.err, ERR_PAGE);
+    return;
+  }
+  const int32_t *bt = a.block_table + (size_t)a.seq_slot[b] * a.bt_stride;
+  for (int i = tid; i < npg; i += 256) s_bt[i] = i < a.bt_stride ? bt[i] : -1;
+
+  // this wave's query rows: tile t holds rows rw + 16 t + l16 (B operand: dims 8 g .. 8 g + 7 of each step)
+  const int rw = qb * kPfBq + wave * 32;
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  u32x4 q[2][KS];
+  int qpos[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = rw + 16 * t + l16;
+    const bool ok = r < a.q_len;
+    qpos[t] = ok ? a.rows.pos[row0 + r] : -1;
+    const f16 *qr = (const f16 *)a.q + (size_t)(row0 + (ok ? r : 0)) * a.ldq + head * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) q[t][ks] = *reinterpret_cast<const u32x4 *>(qr + ks * 32 + g * 8);
+  }
+  __syncthreads();  // s_bt
+
+  // the key block kb's K and V chunks of this thread: K chunk c = tid + 256 i -> key c / (D / 8), dims
+  // 8 (c % (D / 8)) ..; V chunk c -> page c / (2 D), dim (c % (2 D)) / 2, keys 8 (c % 2) .. of the page
+  const f16 *kv = (const f16 *)a.kv;
+  u32x4 rk[KCH], rv[VCH];
+  int err = 0;
+  auto load = [&](int kb) {
+    const int k0 = kb * kPfBk;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, key = c / (D / 8), col = c % (D / 8);
+      const int pi = (k0 + key) / pt, pg = kb < nkb ? s_bt[min(pi, npg - 1)] : -1;
+      const size_t off = pg >= 0 ? a.kvl.block(pg, 0, kh) + (size_t)((k0 + key) % pt) * D + col * 8 : 0;
+      rk[i] = *reinterpret_cast<const u32x4 *>(kv + off);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i, p = c / (2 * D), d = (c % (2 * D)) / 2, h = c % 2;
+      const int pi = k0 / pt + p, pg = kb < nkb ? s_bt[min(pi, npg - 1)] : -1;
+      const size_t off = pg >= 0 ? a.kvl.block(pg, 1, kh) + (size_t)d * pt + h * 8 : 0;
+      rv[i] = *reinterpret_cast<const u32x4 *>(kv + off);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, key = c / (D / 8), col = c % (D / 8);
+      *reinterpret_cast<u32x4 *>(&sK[buf][key * KROW + ((col ^ (key & 15)) << 4)]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i, p = c / (2 * D), d = (c % (2 * D)) / 2, h = c % 2;
+      *reinterpret_cast<u32x4 *>(&sV[buf][d * VROW + (((2 * p + h) ^ vsw(d)) << 4)]) = rv[i];
+    }
+  };
+  // a needed page (one holding a key at or below kmax) without a block-table entry is an error
+  for (int i = tid; i < min(npg, kmax / pt + 1); i += 256) err |= s_bt[i] < 0;
+
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  const float NEG = -INFINITY;
+  float m[2] = {NEG, NEG}, l[2] = {0.f, 0.f};
+  f32x4 o[2][DT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  store(0);
+  load(1);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    const unsigned char *K = sK[buf], *V = sV[buf];
+    // S^T[key 16 kt + 4 g + r][query l16] of both query tiles
+    f32x4 s[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      u32x4 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *reinterpret_cast<const u32x4 *>(K + (16 * kt + l16) * KROW + (((ks * 4 + g) ^ l16) << 4));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t][kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kf[ks]), __builtin_bit_cast(h8, q[t][ks]),
+                                                           s[t][kt], 0, 0, 0);
+      }
+    }
+    // online softmax per query row (the row's 64 scores sit in the 4 lanes l16, l16 + 16, + 32, + 48)
+    h4 pf[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float mx = NEG;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kp = kb * kPfBk + 16 * kt + 4 * g + r;
+          const float v = kp <= qpos[t] ? s[t][kt][r] * scale : NEG;
+          s[t][kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[t], mx);
+      const float mb = mn == NEG ? 0.f : mn;
+      const float corr = __builtin_amdgcn_exp2f(m[t] - mb);
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[t][kt][r] - mb);
+          ps += p;
+          pf[t][kt][r] = (_Float16)p;
+        }
+      l[t] = l[t] * corr + ps;
+      m[t] = mn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= corr;
+    }
+    // O^T[dim 16 dt + 4 g + r][query l16] += V^T[dim][keys 16 kt + 4 g ..] P^T
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      u32x2 vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vf[dt] = *reinterpret_cast<const u32x2 *>(V + (16 * dt + l16) * VROW + (((2 * kt + (g >> 1)) ^ vsw(l16)) << 4) +
+                                                   (g & 1) * 8);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, vf[dt]), pf[t][kt], o[t][dt], 0, 0, 0);
+    }
+    if (kb + 1 < nkb) store(buf ^ 1);
+    load(kb + 2);  // past the key range: dummy loads of the pool's first bytes, never used
+    __syncthreads();
+  }
+  // normalise and store: lane holds dims 16 dt + 4 g + r of query row rw + 16 t + l16
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int r = rw + 16 * t + l16;
+    if (r >= a.q_len) continue;
+    f16 *out = (f16 *)a.out + (size_t)(row0 + r) * a.ldo + head * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Elem<f16>::store(out + 16 * dt + 4 * g + i, o[t][dt][i] * inv);
+  }
+  err = __any(err);
+  if (err && lane == 0) raise_err(a.err, ERR_PAGE);
+}
+
+// Prefill attention through attn_prefill_kernel: causal calls of fp16 models at head_dim 128 with
+// 16-token pages and at most kPfMaxPages pages of keys.
+bool attn_prefill_fits(const AttnArgs &a, int dtype, int max_key_pos) {
+  return dtype == 0 && a.mode == 0 && a.raw == nullptr && a.kvl.head_dim == 128 && a.kvl.page_tokens == 16 &&
+         a.n_seq >= 1 && a.n_seq <= 64 && (max_key_pos + kPfBk) / kPfBk * (kPfBk / 16) <= kPfMaxPages &&
+         a.q_heads % a.kvl.kv_heads == 0 && a.ldq % 8 == 0;
+}
+
+hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t s) {
+  if (a.q_len < 1) return hipSuccess;
+  const dim3 grid((a.q_len + kPfBq - 1) / kPfBq, a.q_heads, a.n_seq);
+  hipLaunchKernelGGL((attn_prefill_kernel<128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace df

@@ -218,6 +218,11 @@ struct AttnArgs {
   int32_t seq_slot[64];
 };
 hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s);
+// Flash-style prefill attention (causal, fp16 models, head_dim 128, 16-token pages): whether a call
+// with keys up to max_key_pos qualifies, and its launch (a.q, rows, block table, out as for
+// launch_attention; no splits).
+bool attn_prefill_fits(const AttnArgs &a, int dtype, int max_key_pos);
+hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- sampler
 struct FilterArgs {

@@ -56,6 +56,55 @@ def test_prefill_logits_and_features(name):
     assert ef.max() <= (1e-4 if cfg.target.dtype == "fp32" else 2e-2)
 
 
+def _hd128_bf16(prompt_len):
+    """A narrow bf16 model at head_dim 128 with a GQA group of 4 (8 q / 2 kv heads)."""
+    from dataclasses import replace
+    t = replace(synth.TINY.target, hidden=256, q_heads=8, kv_heads=2, head_dim=128, ffn=512, dtype="bf16")
+    return replace(synth.TINY, target=t, prompt_len=prompt_len)
+
+
+@pytest.mark.parametrize("P,P2,batch", [(300, 0, 1), (1100, 0, 1), (200, 0, 3), (257, 150, 2)])
+def test_flash_prefill_attention(P, P2, batch):
+    """Prefill-sized calls of a bf16 model at head_dim 128, which take the flash-style prefill attention
+    (128-row query blocks, 64-key blocks, causal masking on the diagonal blocks): ragged last blocks
+    (300 = 2 x 128 + 44), more than 1024 keys, several prompts in one call (slots given out of order, so
+    each sequence reads its own page list), and a second 150-row call at positions P .. P + 149 over the
+    cached prefix.  Every row's logits against the oracle within the bf16 tolerance."""
+    cfg = _hd128_bf16(P)
+    log(f"[flash prefill] P {P} then {P2}, batch {batch}")
+    W = sw.model_weights(cfg, gain_std=0.1)
+    V, tol = cfg.target.vocab, tol_of(cfg)
+    eng = engine(cfg, W, max_slots=batch, max_rows=batch * max(P, P2),
+                 max_pages_per_seq=(P + P2 + 64) // 16 + 2)
+    assert batch * P > batch * cfg.drafter.block_size  # prefill-sized, not a decode-sized call
+    for b in range(batch):
+        eng.kv_alloc(b, P + P2 + 32)
+    slots = list(reversed(range(batch)))
+    prompts = np.stack([sw.prompt_ids(V, cfg.drafter.mask_id, P, 7 + b) for b in range(batch)])
+    logits = torch.empty(batch * max(P, P2) * V, dtype=torch.float32, device="cuda")
+    tp = torch.from_numpy(prompts.astype(np.int32)).to("cuda")
+    eng.verify(slots, tp, P, True, P, logits=logits)
+    eng.status()
+    g = logits[:batch * P * V].view(batch, P, V).cpu().numpy()
+    fols = [OracleFollower(cfg, W, request=b) for b in range(batch)]
+    worst = 0.0
+    for b in range(batch):
+        z, _ = fols[b].prefill(prompts[b])
+        worst = max(worst, float(rel_err_rows(g[b], z).max()))
+    if P2:
+        g2 = sw.prompt_ids(V, cfg.drafter.mask_id, P2, 99)
+        chunk = np.stack([np.roll(g2, b) for b in range(batch)])
+        eng.prefill(slots, tp, [samp(synth.GREEDY)] * batch)  # the same prompts, committed
+        eng.verify(slots, torch.from_numpy(chunk.astype(np.int32)).to("cuda"), P2, False, P2, logits=logits)
+        eng.status()
+        g = logits[:batch * P2 * V].view(batch, P2, V).cpu().numpy()
+        for b in range(batch):
+            z, _ = fols[b].t.forward(fols[b].tc, list(chunk[b]), P, logit_rows=P2)
+            worst = max(worst, float(rel_err_rows(g[b], z).max()))
+    log(f"  logits rel-err max {worst:.3e}")
+    assert worst <= tol
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 @pytest.mark.parametrize("mode", ["greedy", "sampled"])
 def test_e2e_teacher_forced(name, mode):
