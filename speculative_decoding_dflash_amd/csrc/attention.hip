@@ -844,55 +844,80 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s) {
 
 
 // ------------------------------------------------------------------ prefill attention (flash-style)
-// Causal attention of long query blocks (prefill) for bf16 models (fp16 q and KV cache), head_dim D.
-// One work-group per (block of 128 query rows, query head, sequence), heaviest blocks first; each of its
-// 4 waves owns 32 rows (two 16-row MFMA tiles) outright, so no partial results cross waves.  Keys run
-// in blocks of 64 (4 pages): the block's K ([key][dim]) and V^T ([dim][key]) are staged in swizzled,
-// double-buffered LDS by the whole work-group, the next block's loads in registers while the current
-// one is multiplied (one barrier per block).  Per block and wave: S^T = K Q^T (v_mfma 16x16x32, q held
-// in registers), masked (key position > query position) and scaled to log2 units, an online softmax
-// per query row, then O^T += V^T P^T (v_mfma 16x16x16) with P^T taken from the S^T accumulators as they
-// lie (their layout is the B operand's), all in fp32 with fp16 operands.  The sequence's block-table
-// entries for its key range sit in LDS.
+// Causal attention of long query blocks (prefill) for bf16 models (fp16 q and KV cache), head_dim 128,
+// 16-token pages.  One work-group per (block of 128 query rows, query head, sequence), heaviest blocks
+// first, XCD by XCD per KV head; each of its 4 waves owns 32 rows (two 16-row MFMA tiles) outright, so
+// no partial results cross waves.  Keys run in blocks of 64 (4 pages): the block's K ([key][dim]) and V^T ([dim][key]) are
+// staged in swizzled, double-buffered LDS by the whole work-group, the next block's loads in registers
+// while the current one is multiplied (one barrier per block); each thread stages 32 bytes of each of
+// the block's 4 pages, through buffer loads whose range is the page (empty for pages past the key range
+// or without a block-table entry, whose reads return zeros).  Per block and wave: S^T = K Q^T
+// (v_mfma 16x16x32, q held in registers), then an online softmax per query row in log2 units, then
+// O^T += V^T P^T (v_mfma 16x16x32) with P^T taken from the S^T accumulators as they lie, all in fp32 with
+// fp16 operands.  Only the blocks that reach past a wave's first query position are masked (key
+// position > query position).  The running maximum of a row moves only when a block's maximum exceeds
+// it by more than kPfLazy (log2 units): the probabilities then stay below 2^kPfLazy, the rescaling of
+// the accumulators is skipped for most blocks, and o / l is unchanged up to rounding.  The sequence's
+// block-table entries for its key range sit in LDS.  The waves raise their priority over their product
+// sections (s_setprio), so that of the two waves sharing a SIMD the one with products ready issues them
+// while the other works through its softmax.
 constexpr int kPfBq = 128, kPfBk = 64, kPfMaxPages = 1024;
-// V^T rows are 128 bytes: with chunk c of row r at c ^ vsw(r), the 16 rows of a fragment read cover
-// every bank once per 32 lanes (two rows per 64 banks), as do the staging writes.
-DF_DEVICE int vsw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+constexpr float kPfLazy = 8.f;
+// LDS layouts.  The S^T tile kt of a 64-key block holds keys kidx(kt, i) (row i), chosen so that tiles
+// 2 kk and 2 kk + 1 together give lane group g the 8 consecutive keys 32 kk + 8 g .. + 7: then the P^T
+// operand of the PV product is the two tiles' accumulators as they lie, and its V^T operand is one 16-byte
+// piece of a V^T row in key order (8 tokens of one page).  K rows (256 bytes, one per key) keep chunk c
+// at c ^ ksw(key), where ksw(kidx(kt, i)) = i; V^T rows (128 bytes, one per dim) keep chunk c at
+// c ^ (dim % 8).  Both fragment reads then run at the full LDS rate on gfx950 (measured: 4 cycles per
+// 16-byte wave read; the swizzle (r % 8) ^ ((r / 8) % 2) on 128-byte rows takes twice that).
+DF_DEVICE int pf_kidx(int kt, int i) { return 32 * (kt >> 1) + 8 * (i >> 2) + 4 * (kt & 1) + (i & 3); }
+DF_DEVICE int pf_ksw(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
 
-template <int D>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;            // QK^T steps of 32 dims
-  constexpr int DT = D / 16;            // 16-dim output tiles
-  constexpr int KROW = D * 2;           // LDS bytes per K row: D / 8 16-byte chunks, chunk c at c ^ (key % 16)
-  constexpr int VROW = kPfBk * 2;       // LDS bytes per V^T row: 8 chunks, chunk c at c ^ vsw(dim)
-  static_assert(D / 8 >= 16, "the K swizzle spans 16 chunks");
-  constexpr int KCH = kPfBk * D / 8 / 256, VCH = D * kPfBk / 8 / 256;  // 16-byte chunks per thread
-  static_assert(KCH * 256 * 8 == kPfBk * D && VCH * 256 * 8 == D * kPfBk, "chunking");
+  constexpr int D = 128, PT = 16;
+  constexpr int KS = D / 32;       // QK^T steps of 32 dims
+  constexpr int DT = D / 16;       // 16-dim output tiles
+  constexpr int KROW = D * 2;      // LDS bytes per K row: 16 16-byte chunks, chunk c at c ^ pf_ksw(key)
+  constexpr int VROW = kPfBk * 2;  // LDS bytes per V^T row: 8 chunks, chunk c at c ^ (dim % 8)
   __shared__ __attribute__((aligned(16))) unsigned char sK[2][kPfBk * KROW];
   __shared__ __attribute__((aligned(16))) unsigned char sV[2][D * VROW];
-  __shared__ int s_bt[kPfMaxPages];
+  __shared__ __attribute__((aligned(16))) int s_bt[kPfMaxPages + 8];
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  // Work-group order: heaviest query blocks (the longest key ranges) first.  Work-groups go to the 8 XCDs
+  // round-robin (L mod 8); when the (sequence, KV head) units divide evenly, each XCD takes whole units,
+  // so that a unit's K/V stays in one XCD's L2 for all its query heads and blocks.
   const int nqb = (a.q_len + kPfBq - 1) / kPfBq;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest key ranges start first
-  const int head = blockIdx.y, b = blockIdx.z;
-  const int G = a.q_heads / a.kvl.kv_heads, kh = head / G;
-  const int pt = a.kvl.page_tokens;
+  const int kvh = a.kvl.kv_heads, G = a.q_heads / kvh, U = a.n_seq * kvh;
+  const int L = blockIdx.x;
+  int qb_rev, unit, gq;
+  if (U % 8 == 0) {
+    const int j = L >> 3, per = (U >> 3) * G;
+    qb_rev = j / per;
+    unit = (L & 7) + 8 * ((j % per) / G);
+    gq = (j % per) % G;
+  } else {
+    const int per = U * G;
+    qb_rev = L / per;
+    unit = (L % per) / G;
+    gq = (L % per) % G;
+  }
+  const int qb = nqb - 1 - qb_rev, b = unit / kvh, kh = unit % kvh, head = kh * G + gq;
   const int row0 = b * a.q_len;                    // the sequence's first row
   const int rlast = min(a.q_len, (qb + 1) * kPfBq) - 1;
   const int kmax = a.rows.pos[row0 + rlast];       // the work-group's last key position (rows are in order)
-  const int nkb = (kmax + kPfBk) / kPfBk;
-  const int npg = nkb * (kPfBk / 16);
+  const int nkb = kmax >= 0 ? kmax / kPfBk + 1 : 0;
+  const int npg = nkb * (kPfBk / PT);
   if (npg > kPfMaxPages) {  // a position past what the host sized the call for (uniform exit)
     if (tid == 0) raise_err(a.err, ERR_PAGE);
     return;
   }
   const int32_t *bt = a.block_table + (size_t)a.seq_slot[b] * a.bt_stride;
-  for (int i = tid; i < npg; i += 256) s_bt[i] = i < a.bt_stride ? bt[i] : -1;
+  for (int i = tid; i < npg + 8; i += 256) s_bt[i] = i < npg && i < a.bt_stride ? bt[i] : -1;  // + 2 blocks past
 
   // this wave's query rows: tile t holds rows rw + 16 t + l16 (B operand: dims 8 g .. 8 g + 7 of each step)
   const int rw = qb * kPfBq + wave * 32;
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   u32x4 q[2][KS];
   int qpos[2];
 #pragma unroll
@@ -904,127 +929,164 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) q[t][ks] = *reinterpret_cast<const u32x4 *>(qr + ks * 32 + g * 8);
   }
+  // blocks whose last key is at or below the wave's first query position need no mask
+  const int first_pos = __builtin_amdgcn_readfirstlane(qpos[0]);
   __syncthreads();  // s_bt
 
-  // the key block kb's K and V chunks of this thread: K chunk c = tid + 256 i -> key c / (D / 8), dims
-  // 8 (c % (D / 8)) ..; V chunk c -> page c / (2 D), dim (c % (2 D)) / 2, keys 8 (c % 2) .. of the page
-  const f16 *kv = (const f16 *)a.kv;
-  u32x4 rk[KCH], rv[VCH];
-  int err = 0;
-  auto load = [&](int kb) {
-    const int k0 = kb * kPfBk;
+  // Staging from page i of the block (one buffer resource per page; a page past the key range or without
+  // a block-table entry has an empty range, and its reads return zeros): thread tid loads K token tid / 16,
+  // dims 8 (tid % 16) .. and V^T dim tid / 2, tokens 8 (tid % 2) .. (16 bytes each).
+  const uint32_t page_bytes = (uint32_t)a.kvl.page_elems() * 2;
+  const uint32_t k_off = ((uint32_t)kh * PT * D + (tid >> 4) * D + (tid & 15) * 8) * 2;
+  const uint32_t v_off = ((uint32_t)(a.kvl.kv_heads + kh) * PT * D + (tid >> 1) * PT + (tid & 1) * 8) * 2;
+  u32x4 rk[4], rv[4];
+  auto load = [&](int4 pgs) {  // the block's 4 block-table entries
+    const int pg[4] = {pgs.x, pgs.y, pgs.z, pgs.w};
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, key = c / (D / 8), col = c % (D / 8);
-      const int pi = (k0 + key) / pt, pg = kb < nkb ? s_bt[min(pi, npg - 1)] : -1;
-      const size_t off = pg >= 0 ? a.kvl.block(pg, 0, kh) + (size_t)((k0 + key) % pt) * D + col * 8 : 0;
-      rk[i] = *reinterpret_cast<const u32x4 *>(kv + off);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i, p = c / (2 * D), d = (c % (2 * D)) / 2, h = c % 2;
-      const int pi = k0 / pt + p, pg = kb < nkb ? s_bt[min(pi, npg - 1)] : -1;
-      const size_t off = pg >= 0 ? a.kvl.block(pg, 1, kh) + (size_t)d * pt + h * 8 : 0;
-      rv[i] = *reinterpret_cast<const u32x4 *>(kv + off);
+    for (int i = 0; i < 4; ++i) {
+      const int e = __builtin_amdgcn_readfirstlane(pg[i]);
+      const char *base = (const char *)a.kv + (size_t)(e >= 0 ? e : 0) * page_bytes;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, e >= 0 ? (int)page_bytes : 0,
+                                                                        0x00020000);
+      rk[i] = __builtin_amdgcn_raw_buffer_load_b128(r, k_off, 0, 0);
+      rv[i] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off, 0, 0);
     }
   };
+  int kst[4], vst[4];  // LDS byte offsets of the thread's pieces of page i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = 16 * i + (tid >> 4), d = tid >> 1;
+    kst[i] = key * KROW + (((tid & 15) ^ pf_ksw(key)) << 4);
+    vst[i] = d * VROW + (((2 * i + (tid & 1)) ^ (d & 7)) << 4);
+  }
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, key = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4 *>(&sK[buf][key * KROW + ((col ^ (key & 15)) << 4)]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i, p = c / (2 * D), d = (c % (2 * D)) / 2, h = c % 2;
-      *reinterpret_cast<u32x4 *>(&sV[buf][d * VROW + (((2 * p + h) ^ vsw(d)) << 4)]) = rv[i];
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4 *>(&sK[buf][kst[i]]) = rk[i];
+      *reinterpret_cast<u32x4 *>(&sV[buf][vst[i]]) = rv[i];
     }
   };
   // a needed page (one holding a key at or below kmax) without a block-table entry is an error
-  for (int i = tid; i < min(npg, kmax / pt + 1); i += 256) err |= s_bt[i] < 0;
+  int err = 0;
+  for (int i = tid; i <= kmax / PT && i < npg; i += 256) err |= s_bt[i] < 0;
 
-  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
   const float NEG = -INFINITY;
-  float m[2] = {NEG, NEG}, l[2] = {0.f, 0.f};
+  float m[2] = {NEG, NEG}, l[2] = {0.f, 0.f};  // running maximum (log2 units) and sum per query row
+  float mb[2] = {0.f, 0.f};                     // m, or 0 while a row has seen no key
   f32x4 o[2][DT];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  load(0);
+  auto entries = [&](int kb) { return *reinterpret_cast<const int4 *>(&s_bt[kb * 4]); };
+  load(entries(0));
   store(0);
-  load(1);
+  load(entries(1));
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
+    const int4 next = entries(kb + 2);  // read early: the loads at the end of the block use them
     const unsigned char *K = sK[buf], *V = sV[buf];
-    // S^T[key 16 kt + 4 g + r][query l16] of both query tiles
+    // S^T[key pf_kidx(kt, 4 g + r)][query l16] of both query tiles
+    __builtin_amdgcn_s_setprio(1);  // products first while both waves of the SIMD are ready
+    // (dims step outermost: the 8 accumulators take turns, so no product waits on the one before it)
     f32x4 s[2][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      u32x4 kf[KS];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = *reinterpret_cast<const u32x4 *>(K + (16 * kt + l16) * KROW + (((ks * 4 + g) ^ l16) << 4));
+      for (int kt = 0; kt < 4; ++kt) s[t][kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t][kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 kf[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kf[ks]), __builtin_bit_cast(h8, q[t][ks]),
-                                                           s[t][kt], 0, 0, 0);
-      }
-    }
-    // online softmax per query row (the row's 64 scores sit in the 4 lanes l16, l16 + 16, + 32, + 48)
-    h4 pf[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float mx = NEG;
+      for (int kt = 0; kt < 4; ++kt)
+        kf[kt] = *reinterpret_cast<const u32x4 *>(K + pf_kidx(kt, l16) * KROW + (((ks * 4 + g) ^ l16) << 4));
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kp = kb * kPfBk + 16 * kt + 4 * g + r;
-          const float v = kp <= qpos[t] ? s[t][kt][r] * scale : NEG;
-          s[t][kt][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[t], mx);
-      const float mb = mn == NEG ? 0.f : mn;
-      const float corr = __builtin_amdgcn_exp2f(m[t] - mb);
+        for (int t = 0; t < 2; ++t)
+          s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kf[kt]), __builtin_bit_cast(h8, q[t][ks]),
+                                                           s[t][kt], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // mask (blocks reaching past the wave's first query position only) and each row's block maximum
+    // (the row's 64 scores sit in the 4 lanes l16, l16 + 16, + 32, + 48)
+    if (kb * kPfBk + kPfBk - 1 > first_pos) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * kPfBk + pf_kidx(kt, 4 * g + r) > qpos[t]) s[t][kt][r] = NEG;
+    }
+    // The grow test needs only each lane's own maximum (the row's maximum exceeds m + kPfLazy iff one of
+    // its 4 lanes' does); the row's maximum itself is gathered only when some row of the wave grows.
+    float mx[2];
+    bool grow = false;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float v = NEG;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v = __builtin_elementwise_max(v, s[t][kt][r]);
+      mx[t] = v * scale;
+      grow |= mx[t] > m[t] + kPfLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // some row's maximum moves: rescale (wave-uniform branch)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float v = mx[t];
+        v = __builtin_elementwise_max(v, __shfl_xor(v, 16));
+        v = __builtin_elementwise_max(v, __shfl_xor(v, 32));
+        const float mn = v > m[t] + kPfLazy ? v : m[t];
+        const float corr = __builtin_amdgcn_exp2f(m[t] - mn);  // 0 for a row's first keys, 1 if unmoved
+        m[t] = mn;
+        mb[t] = mn == NEG ? 0.f : mn;  // a row with no key yet: every score is -inf
+        l[t] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] *= corr;
+      }
+    }
+    h4 pf[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[t][kt][r] - mb);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[t][kt][r], scale, -mb[t]));
           ps += p;
           pf[t][kt][r] = (_Float16)p;
         }
-      l[t] = l[t] * corr + ps;
-      m[t] = mn;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= corr;
+      l[t] += ps;
     }
-    // O^T[dim 16 dt + 4 g + r][query l16] += V^T[dim][keys 16 kt + 4 g ..] P^T
+    // O^T[dim 16 dt + 4 g + r][query l16] += V^T P^T over 32-key groups kk with 16x16x32 products: the
+    // B operand of lane (query l16, g) is P^T of keys 32 kk + 8 g .. + 7, the accumulators of tiles 2 kk
+    // and 2 kk + 1 as they lie; the A operand of lane (dim l16, g) is V^T of the same keys, chunk 4 kk + g
+    // of the dim's row.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      u32x2 vf[DT];
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        vf[dt] = *reinterpret_cast<const u32x2 *>(V + (16 * dt + l16) * VROW + (((2 * kt + (g >> 1)) ^ vsw(l16)) << 4) +
-                                                   (g & 1) * 8);
+        vf[dt] = *reinterpret_cast<const u32x4 *>(V + (16 * dt + l16) * VROW + (((4 * kk + g) ^ (l16 & 7)) << 4));
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        const h8 pb = __builtin_shufflevector(pf[t][2 * kk], pf[t][2 * kk + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, vf[dt]), pf[t][kt], o[t][dt], 0, 0, 0);
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, vf[dt]), pb, o[t][dt], 0, 0, 0);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (kb + 1 < nkb) store(buf ^ 1);
-    load(kb + 2);  // past the key range: dummy loads of the pool's first bytes, never used
+    load(next);  // past the key range: empty ranges, zeros, never used
     __syncthreads();
   }
   // normalise and store: lane holds dims 16 dt + 4 g + r of query row rw + 16 t + l16
@@ -1050,14 +1112,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 // 16-token pages and at most kPfMaxPages pages of keys.
 bool attn_prefill_fits(const AttnArgs &a, int dtype, int max_key_pos) {
   return dtype == 0 && a.mode == 0 && a.raw == nullptr && a.kvl.head_dim == 128 && a.kvl.page_tokens == 16 &&
-         a.n_seq >= 1 && a.n_seq <= 64 && (max_key_pos + kPfBk) / kPfBk * (kPfBk / 16) <= kPfMaxPages &&
+         a.n_seq >= 1 && a.n_seq <= 64 && max_key_pos / kPfBk + 1 <= kPfMaxPages / (kPfBk / 16) &&
          a.q_heads % a.kvl.kv_heads == 0 && a.ldq % 8 == 0;
 }
 
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t s) {
   if (a.q_len < 1) return hipSuccess;
-  const dim3 grid((a.q_len + kPfBq - 1) / kPfBq, a.q_heads, a.n_seq);
-  hipLaunchKernelGGL((attn_prefill_kernel<128>), grid, dim3(256), 0, s, a);
+  const dim3 grid((a.q_len + kPfBq - 1) / kPfBq * a.q_heads * a.n_seq);
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
