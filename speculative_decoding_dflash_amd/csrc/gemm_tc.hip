@@ -77,17 +77,25 @@ __global__ __launch_bounds__(NWV * 64, BM == 256 ? 1 : 2) void gemm_tc_kernel(Ge
   const bool swiglu = a.epi == EPI_SWIGLU;
   const int units = swiglu ? a.N / 16 : a.N / 32;
   // XCD-aware order: work-group b runs on XCD b % 8 (round-robin dispatch); each XCD takes a contiguous
-  // range of the (K range, row tile, chunk) items, chunk fastest, so that the work-groups sharing an
-  // L2 share X row tiles.
+  // range of the (K range, row tile, chunk) items.  Within a K range the items run in blocks of up to
+  // RB row tiles x CB chunks (chunk fastest, then row tile), about the work-groups an XCD holds at once,
+  // so that those share both their X row tiles and their weight chunks through the XCD's L2 (with
+  // chunk-fastest order alone every row tile re-reads every weight chunk from memory).
   int ch, ty, tz;
   {
+    constexpr int RB = BM == 256 ? 4 : 8, CB = 8;
     const int rt = gridDim.y, T = nch * rt * gridDim.z;
     const int b = blockIdx.x + nch * (blockIdx.y + rt * blockIdx.z);
     const int per = T / 8, rem = T % 8, xcd = b % 8;
     const int l = xcd * per + min(xcd, rem) + b / 8;
-    ch = l % nch;
-    ty = (l / nch) % rt;
     tz = l / (nch * rt);
+    const int lz = l - tz * nch * rt;
+    const int rg = lz / (RB * nch), rb = min(RB, rt - rg * RB);  // row group and its row tiles
+    const int lr = lz - rg * RB * nch;
+    const int cg = lr / (rb * CB), cb = min(CB, nch - cg * CB);  // chunk group and its chunks
+    const int lc = lr - cg * rb * CB;
+    ty = rg * RB + lc / cb;
+    ch = cg * CB + lc % cb;
   }
   const int u0 = (int)((long)units * ch / nch), u1 = (int)((long)units * (ch + 1) / nch);
   const int nrows = (u1 - u0) * 32;  // weight rows of this chunk (<= BN)
