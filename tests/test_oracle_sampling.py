@@ -225,3 +225,62 @@ def test_sample_draft_uses_stream_one():
     for t in range(50):
         u, _ = S.uniforms(5, t, 1, stream=1)
         assert S.sample_draft(ids, q, 5, t, 1) == S.inverse_cdf(ids, q, u, None)
+
+
+def _brute_dist64(z, T, top_k, top_p):
+    """The filter written out with Python floats: order by (logit desc, id asc), keep the top k, weights
+    exp(s - s_max) normalised with fsum, keep the shortest prefix whose running sum reaches top_p
+    (inclusive), renormalise."""
+    import math
+    s = [float(v) / T for v in z]
+    order = sorted(range(len(s)), key=lambda i: (-s[i], i))
+    k = len(s) if top_k <= 0 else min(top_k, len(s))
+    ids = order[:k]
+    w = [math.exp(s[i] - s[ids[0]]) for i in ids]
+    tot = math.fsum(w)
+    q = [x / tot for x in w]
+    keep = k
+    if top_p < 1.0:
+        run = 0.0
+        for j, x in enumerate(q):
+            run += x
+            if run >= top_p:
+                keep = j + 1
+                break
+    kept = q[:keep]
+    t2 = math.fsum(kept)
+    return ids[:keep], [x / t2 for x in kept]
+
+
+@pytest.mark.parametrize("T", [0.6, 1.0, 1.7])
+@pytest.mark.parametrize("top_k", [0, 1, 7, 20, 100])
+@pytest.mark.parametrize("top_p", [0.3, 0.8, 0.95, 1.0])
+def test_filter64_against_brute_force(T, top_k, top_p):
+    """sample_dist64 (the float64 filter the law enumerations use) against the filter written out in
+    Python floats, ties planted: same ids in the same order, probabilities to 1e-12."""
+    V = 48
+    for trial in range(4):
+        z = RNG.standard_normal(V) * 2.0
+        z[RNG.integers(0, V, 5)] = z[7]  # plant ties
+        ids, p = S.sample_dist64(z, T, top_k, top_p)
+        bid, bp = _brute_dist64(z, T, top_k, top_p)
+        assert list(ids) == bid
+        np.testing.assert_allclose(p, bp, rtol=1e-12, atol=1e-15)
+        assert p.dtype == np.float64 and abs(float(p.sum()) - 1.0) < 1e-12
+
+
+def test_filter64_edge_cases():
+    """The top-p cut is inclusive (a prefix whose sum equals top_p exactly stops there), ties keep the
+    lower id first, top_k <= 0 keeps the whole vocabulary, top_k past the vocabulary clamps, and
+    temperature 0 is the argmax with the lowest id."""
+    z = np.array([1.0, 1.0, -40.0, -40.0])  # two equal heads hold half the mass each (to 1e-30)
+    ids, p = S.sample_dist64(z, 1.0, 0, 0.5)
+    assert list(ids) == [0] and list(p) == [1.0]
+    ids, p = S.sample_dist64(z, 1.0, 0, 0.5000001)
+    assert list(ids) == [0, 1] and np.allclose(p, [0.5, 0.5])
+    ids, p = S.sample_dist64(np.array([0.3, 2.0, 2.0, -1.0]), 1.0, 0, 1.0)
+    assert list(ids) == [1, 2, 0, 3]
+    ids, p = S.sample_dist64(np.array([0.3, 2.0, 2.0, -1.0]), 1.0, 10, 1.0)
+    assert list(ids) == [1, 2, 0, 3] and abs(p.sum() - 1.0) < 1e-15
+    ids, p = S.sample_dist64(np.array([0.3, 2.0, 2.0, -1.0]), 0.0, 20, 0.95)
+    assert list(ids) == [1] and list(p) == [1.0]
