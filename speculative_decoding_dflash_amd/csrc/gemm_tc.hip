@@ -78,12 +78,13 @@ __global__ __launch_bounds__(NWV * 64, BM == 256 ? 1 : 2) void gemm_tc_kernel(Ge
   const int units = swiglu ? a.N / 16 : a.N / 32;
   // XCD-aware order: work-group b runs on XCD b % 8 (round-robin dispatch); each XCD takes a contiguous
   // range of the (K range, row tile, chunk) items.  Within a K range the items run in blocks of up to
-  // RB row tiles x CB chunks (chunk fastest, then row tile), about the work-groups an XCD holds at once,
-  // so that those share both their X row tiles and their weight chunks through the XCD's L2 (with
-  // chunk-fastest order alone every row tile re-reads every weight chunk from memory).
+  // RB row tiles x CB chunks (chunk fastest, then row tile), so that the work-groups an XCD holds at
+  // once share both their X row tiles and their weight chunks through the XCD's L2 (with chunk-fastest
+  // order alone every row tile re-reads every weight chunk from memory).  8 x 8 measured best at 6400
+  // rows (gate/up 13% faster than 4 x 8, 19% than chunk-fastest).
   int ch, ty, tz;
   {
-    constexpr int RB = BM == 256 ? 4 : 8, CB = 8;
+    constexpr int RB = 8, CB = 8;
     const int rt = gridDim.y, T = nch * rt * gridDim.z;
     const int b = blockIdx.x + nch * (blockIdx.y + rt * blockIdx.z);
     const int per = T / 8, rem = T % 8, xcd = b % 8;
