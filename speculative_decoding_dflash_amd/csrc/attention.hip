@@ -24,6 +24,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 
+constexpr float kAttnLazy = 8.f;  // see the softmax state of attn_kernel
+
 template <typename T, int D> struct AttnFrag;
 
 // K fragments: kSteps 16-byte vectors per lane (A operand of S^T = K Q^T, row = key = lane % 16).
@@ -429,11 +431,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  float m[NQT], l[NQT];
+  // Online softmax state per query vector: the reference maximum m (log2 units) moves only when a page's
+  // scores exceed it by more than kAttnLazy, so the probabilities stay below 2^kAttnLazy, the lanes of a
+  // query vector exchange their maxima only when one of them grows, and the accumulators are rescaled
+  // only then; mb is m, or 0 while no key has been seen.  o / l (and the merges, which take any reference
+  // maximum) are unchanged up to rounding.
+  float m[NQT], l[NQT], mb[NQT];
   f32x4 o[NQT][D / 16];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     m[t] = NEG;
+    mb[t] = 0.f;
     l[t] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[t][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -510,24 +518,27 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int kp = ps + 4 * g + r;
         sv[r] = (kp >= lo[t] && kp < hi[t] && kp >= klim_lo && kp < klim_hi) ? s[r] * scale : NEG;
-        mx = fmaxf(mx, sv[r]);
+        mx = __builtin_elementwise_max(mx, sv[r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[t], mx);
-      const float mb = (mn == NEG) ? 0.f : mn;  // exp2(-inf - mb) = 0 for masked keys
-      const float corr = __builtin_amdgcn_exp2f(m[t] - mb);
+      if (__builtin_amdgcn_ballot_w64(mx > m[t] + kAttnLazy)) {  // some query vector's maximum moves
+        mx = __builtin_elementwise_max(mx, __shfl_xor(mx, 16));
+        mx = __builtin_elementwise_max(mx, __shfl_xor(mx, 32));
+        const float mn = mx > m[t] + kAttnLazy ? mx : m[t];
+        const float corr = mn == m[t] ? 1.f : __builtin_amdgcn_exp2f(m[t] - mn);  // 0 for the first keys
+        l[t] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
+        m[t] = mn;
+        mb[t] = mn == NEG ? 0.f : mn;
+      }
       float pr[4], ps_sum = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(sv[r] - mb);
+        pr[r] = __builtin_amdgcn_exp2f(sv[r] - mb[t]);  // 0 for masked keys
         ps_sum += pr[r];
       }
-      l[t] = l[t] * corr + ps_sum;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[t][dt] *= corr;
+      l[t] += ps_sum;
       F::pv(o[t], vfp, pr);
-      m[t] = mn;
     }
   };
   if (!pre) {  // the first chunk's pages, now that the key range is known
