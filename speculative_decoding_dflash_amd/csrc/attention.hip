@@ -858,12 +858,12 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, hipStream_t s) {
 // Causal attention of long query blocks (prefill) for bf16 models (fp16 q and KV cache), head_dim 128,
 // 16-token pages.  One work-group per (block of 128 query rows, query head, sequence), heaviest blocks
 // first, XCD by XCD per KV head; each of its 4 waves owns 32 rows (two 16-row MFMA tiles) outright, so
-// no partial results cross waves.  Keys run in blocks of 64 (4 pages): the block's K ([key][dim]) and V^T ([dim][key]) are
-// staged in swizzled, double-buffered LDS by the whole work-group, the next block's loads in registers
-// while the current one is multiplied (one barrier per block); each thread stages 32 bytes of each of
-// the block's 4 pages, through buffer loads whose range is the page (empty for pages past the key range
-// or without a block-table entry, whose reads return zeros).  Per block and wave: S^T = K Q^T
-// (v_mfma 16x16x32, q held in registers), then an online softmax per query row in log2 units, then
+// no partial results cross waves.  Keys run in blocks of 64 (4 pages): the block's K ([key][dim]) and
+// V^T ([dim][key]) are staged in swizzled, double-buffered LDS by the whole work-group, the next block's
+// loads in registers while the current one is multiplied (one barrier per block); each thread stages 32
+// bytes of each of the block's 4 pages, through buffer loads whose range is the page (empty for pages
+// past the key range or without a block-table entry, whose reads return zeros).  Per block and wave:
+// S^T = K Q^T (v_mfma 16x16x32, q held in registers), then an online softmax per query row in log2 units, then
 // O^T += V^T P^T (v_mfma 16x16x32) with P^T taken from the S^T accumulators as they lie, all in fp32 with
 // fp16 operands.  Only the blocks that reach past a wave's first query position are masked (key
 // position > query position).  The running maximum of a row moves only when a block's maximum exceeds
