@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per projection launch of the decode step, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # scaled by a plain 1 GiB copy (profiles/gemm_kernel_27b_conc1_traffic.txt), and the hash of the
 # kernel source they were taken on: a changed kernel reports null until the counters are retaken.
-GEMM_TRAFFIC = {"bytes_per_launch": 177542691, "gemm_src_sha256_16": "b7e9ec76474e2219"}
+GEMM_TRAFFIC = {"bytes_per_launch": 177535881, "gemm_src_sha256_16": "b7e9ec76474e2219"}
 
 
 def log(msg: str):
