@@ -35,7 +35,7 @@
  *     (the attention operands keep 11 significant bits; K is RMS-normalised, |V| saturates at 65504)
  *     and fp32 for DFLASH_F32 models.  Page ids are shared by the target pool (layers 0..L_t-1) and the
  *     drafter pool (layers 0..L_d-1): a slot's block table maps its position p to page
- *     table[p / page_tokens].
+ *     table[p / page_tokens] -- except for a windowed drafter's page ring (dflash_drafter_pool_bytes).
  *   - Activations of DFLASH_BF16 models that meet a weight matrix or the attention -- projection
  *     inputs, target features (verify output, draft input), q and the KV cache -- are IEEE fp16 (11
  *     significant bits where bf16 keeps 8; magnitudes saturate at 65504); the bf16 weights enter those
@@ -160,12 +160,24 @@ typedef struct dflash_ctx dflash_ctx;
 /* Bytes of one KV pool holding `pages` pages for `layers` layers. */
 size_t dflash_kv_pool_bytes(const dflash_model_cfg *cfg, int32_t layers, const dflash_capacity *cap);
 
+/* Bytes of the drafter's KV pool (0 if an argument is NULL or dcfg->layers < 1).  With a window W
+ * ([P3] "结构一览") the drafter never reads keys more than W positions behind a block, so each slot
+ * recycles a ring of R = ceil((W + 2 B) / page_tokens) + 1 pages (page index i of a slot lives in ring
+ * page slot * R + i mod R): dcfg->layers * max_slots * R pages.  Without a window, or when that is not
+ * smaller than num_pages (or R >= max_pages_per_seq), it is dflash_kv_pool_bytes(cfg, dcfg->layers,
+ * cap) and the drafter uses the target's page ids.  With the ring, dflash_draft_block must follow a
+ * dflash_accept_resample of at most (page_tokens * R - W) / 2 drafts (at least B + 8), else it returns
+ * DFLASH_E_STATE: one draft touches up to W + nd + max(B, nd) consecutive positions after an accept of
+ * nd drafts. */
+size_t dflash_drafter_pool_bytes(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg,
+                                 const dflash_capacity *cap);
+
 /* Bytes of the workspace for this model, drafter and capacity (0 if the arguments are invalid). */
 size_t dflash_workspace_bytes(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg,
                               const dflash_capacity *cap);
 
 /* Create a context.  Pointers are borrowed.  d_target_kv must hold dflash_kv_pool_bytes(cfg,
- * cfg->layers, cap) bytes, d_drafter_kv dflash_kv_pool_bytes(cfg, dcfg->layers, cap) bytes and
+ * cfg->layers, cap) bytes, d_drafter_kv dflash_drafter_pool_bytes(cfg, dcfg, cap) bytes and
  * d_workspace dflash_workspace_bytes(...) bytes, 256-byte aligned.  Zero-fills both KV pools and the
  * workspace's state on `stream` and waits for it (unwritten key slots of a page take part in the
  * attention product with zero weight, which is exact only for finite contents). */

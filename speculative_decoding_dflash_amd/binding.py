@@ -73,6 +73,7 @@ def _load() -> C.CDLL:
     P, I, S, V = C.POINTER, C.c_int32, C.c_size_t, C.c_void_p
     sig = {
         "dflash_kv_pool_bytes": (S, [P(ModelCfg), I, P(Capacity)]),
+        "dflash_drafter_pool_bytes": (S, [P(ModelCfg), P(DrafterCfg), P(Capacity)]),
         "dflash_workspace_bytes": (S, [P(ModelCfg), P(DrafterCfg), P(Capacity)]),
         "dflash_create": (I, [P(ModelCfg), P(DrafterCfg), P(TargetWeights), P(DrafterWeights), P(Capacity), V, V, V, V,
                               P(V)]),
@@ -130,6 +131,10 @@ def _slots(slots: Sequence[int]):
 
 def dflash_kv_pool_bytes(cfg: ModelCfg, layers: int, cap: Capacity) -> int:
     return lib.dflash_kv_pool_bytes(C.byref(cfg), layers, C.byref(cap))
+
+
+def dflash_drafter_pool_bytes(cfg: ModelCfg, dcfg: DrafterCfg, cap: Capacity) -> int:
+    return lib.dflash_drafter_pool_bytes(C.byref(cfg), C.byref(dcfg), C.byref(cap))
 
 
 def dflash_workspace_bytes(cfg: ModelCfg, dcfg: DrafterCfg, cap: Capacity) -> int:

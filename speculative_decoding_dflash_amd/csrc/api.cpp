@@ -50,11 +50,23 @@ constexpr int kMaxQTiles = 64;  // query tiles per sequence in a decode-sized at
 
 // Workspace carve-up; offsets in bytes.
 struct Layout {
-  size_t state, err, cnt, skc, bt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, tcr, att_o, att_ml, dlogits,
+  size_t state, err, cnt, skc, bt, dbt, rows[3][4], x, xn, ss, rope, qbuf, attn, ffn, part, skp, tcr, att_o, att_ml, dlogits,
       cid, cp, cn, skey, sidx, cu, xc, sel_id, sel_s, sel_x, sel_y, sel_t, total;
   size_t part_elems, att_rows, tcr_elems;
   int ss_ld, sk_tiles;
 };
+
+// Pages per slot of the drafter's page ring ([P3] "结构一览": the drafter attends over a sliding window
+// of W context keys).  A drafter call for a block at n reads keys [n - W + 1, n + B) and, after an accept
+// of nd < B drafts, injects rows from n - nd - W at the lowest, so it touches fewer than W + 2 B
+// consecutive positions, and keys older than the window are never read again: position p of a slot can
+// live at ring position p mod R pt (page index i in ring page i mod R).  0 (no ring: the drafter shares
+// the target's page ids) without a window, or when the ring would not make the drafter pool smaller.
+int drafter_ring_pages(const dflash_drafter_cfg *d, const dflash_capacity *cap) {
+  if (d->window <= 0 || cap->page_tokens < 1) return 0;
+  const int r = (d->window + 2 * d->block_size + cap->page_tokens - 1) / cap->page_tokens + 1;
+  return r < cap->max_pages_per_seq && (int64_t)cap->max_slots * r < cap->num_pages ? r : 0;
+}
 
 Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const dflash_capacity *cap) {
   Layout L{};
@@ -75,6 +87,7 @@ Layout make_layout(const dflash_model_cfg *c, const dflash_drafter_cfg *d, const
   L.sk_tiles = (int)(std::max({(size_t)c->ffn, (size_t)c->vocab, QD + 2 * KD, (size_t)d->layers * 2 * KD, H}) / 16);
   L.skc = take(sizeof(int32_t) * L.sk_tiles);
   L.bt = take(sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq);
+  L.dbt = take(sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq);  // the drafter's page ring
   for (int s = 0; s < 3; ++s)
     for (int k = 0; k < 4; ++k) L.rows[s][k] = take(sizeof(int32_t) * R);
   L.x = take(sizeof(float) * R * H);
@@ -176,6 +189,8 @@ struct dflash_ctx {
   Layout L;
   KVLayout kvl;
   size_t layer_elems;  // elements of one layer's pool
+  size_t d_layer_elems;  // elements of one drafter layer's pool (the page ring when dring > 0)
+  int dring = 0;         // drafter pages per slot when the drafter's window recycles them, else 0
   // host page tables
   std::vector<std::vector<int32_t>> pages;
   std::vector<int32_t> free_pages;
@@ -206,6 +221,9 @@ struct dflash_ctx {
   SlotState *state() const { return wsp<SlotState>(L.state); }
   int32_t *err() const { return wsp<int32_t>(L.err); }
   int32_t *bt() const { return wsp<int32_t>(L.bt); }
+  // the drafter's block table: its page ring (slot s, page index i -> page s * dring + i % dring) when
+  // the window recycles pages, else the target's table (page ids shared by both pools)
+  int32_t *dbt() const { return dring ? wsp<int32_t>(L.dbt) : bt(); }
   Rows rows(int s) const {
     Rows r;
     r.pos = wsp<int32_t>(L.rows[s][0]);
@@ -218,7 +236,7 @@ struct dflash_ctx {
   int rope_rows() const { return cap.max_pages_per_seq * cap.page_tokens; }
   int es() const { return esize(&cfg); }
   void *tlayer(int l) const { return tkv + (size_t)l * layer_elems * es(); }
-  void *dlayer(int l) const { return dkv + (size_t)l * layer_elems * es(); }
+  void *dlayer(int l) const { return dkv + (size_t)l * d_layer_elems * es(); }
   int max_ctx(const int32_t *slots, int batch) const {
     int m = 0;
     for (int b = 0; b < batch; ++b) m = std::max<int>(m, (int)pages[slots[b]].size() * cap.page_tokens);
@@ -408,14 +426,14 @@ dflash_status run_resid_norm(dflash_ctx *c, GemmArgs a, int R, float *resid, voi
   return run_gemm(c, a, R, s);
 }
 
-QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows) {
+QkvPostArgs post_base(dflash_ctx *c, const Rows &rows, int n_rows, bool drafter) {
   QkvPostArgs p;
   memset(&p, 0, sizeof p);
   p.src = c->wsp<float>(c->L.part);
   p.n_part = 1;
   p.n_rows = n_rows;
   p.rows = rows;
-  p.block_table = c->bt();
+  p.block_table = drafter ? c->dbt() : c->bt();
   p.bt_stride = c->cap.max_pages_per_seq;
   p.kv = c->kvl;
   p.rope = c->wsp<float2>(c->L.rope);
@@ -436,7 +454,7 @@ dflash_status run_attention(dflash_ctx *c, const Rows &rows, int n_seq, int q_le
   a.ldq = m.q_heads * m.head_dim;
   a.kv = kv;
   a.kvl = c->kvl;
-  a.block_table = c->bt();
+  a.block_table = mode == 1 ? c->dbt() : c->bt();  // mode 1: the drafter's layers
   a.bt_stride = c->cap.max_pages_per_seq;
   a.rows = rows;
   a.n_seq = n_seq;
@@ -585,7 +603,7 @@ dflash_status run_layer(dflash_ctx *c, const dflash_layer_weights &w, void *kv_l
     const bool want = fz ? atoi(fz) != 0 : n_seq <= kAttnFusedMaxSeqs;
     fused = want && np == 1 && (size_t)R <= c->L.att_rows && q_len <= 16 && ((uintptr_t)w.q_norm & 15) == 0;
     if (!fused) {
-      QkvPostArgs p = post_base(c, rows, R);
+      QkvPostArgs p = post_base(c, rows, R, attn_mode == 1);
       p.src = part;
       p.ld_src = QD + 2 * KD;
       p.n_part = np;
@@ -726,6 +744,15 @@ size_t dflash_kv_pool_bytes(const dflash_model_cfg *cfg, int32_t layers, const d
   return (size_t)layers * cap->num_pages * 2 * cfg->kv_heads * cap->page_tokens * cfg->head_dim * esize(cfg);
 }
 
+size_t dflash_drafter_pool_bytes(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg,
+                                 const dflash_capacity *cap) {
+  if (!cfg || !dcfg || !cap || dcfg->layers < 1 || cap->max_slots < 1) return 0;
+  const int r = drafter_ring_pages(dcfg, cap);
+  if (!r) return dflash_kv_pool_bytes(cfg, dcfg->layers, cap);
+  return (size_t)dcfg->layers * cap->max_slots * r * 2 * cfg->kv_heads * cap->page_tokens * cfg->head_dim *
+         esize(cfg);
+}
+
 size_t dflash_workspace_bytes(const dflash_model_cfg *cfg, const dflash_drafter_cfg *dcfg, const dflash_capacity *cap) {
   if (check_cfg(cfg, dcfg, cap)) return 0;
   return make_layout(cfg, dcfg, cap).total;
@@ -777,16 +804,20 @@ dflash_status dflash_create(const dflash_model_cfg *cfg, const dflash_drafter_cf
   c->L = make_layout(cfg, dcfg, cap);
   c->kvl = KVLayout{cap->page_tokens, cfg->kv_heads, cfg->head_dim};
   c->layer_elems = (size_t)cap->num_pages * c->kvl.page_elems();
+  c->dring = drafter_ring_pages(dcfg, cap);
+  c->d_layer_elems = c->dring ? (size_t)cap->max_slots * c->dring * c->kvl.page_elems() : c->layer_elems;
   c->pages.assign(cap->max_slots, {});
   c->prefilled.assign(cap->max_slots, 0);
   for (int p = cap->num_pages - 1; p >= 0; --p) c->free_pages.push_back(p);
   // Pools start zeroed: unwritten key slots of a page are multiplied by zero probabilities in the
   // attention product, which is only exact for finite contents.  Only finite values are stored later.
   hipError_t e = hipMemsetAsync(c->tkv, 0, dflash_kv_pool_bytes(cfg, cfg->layers, cap), stream);
-  if (e == hipSuccess) e = hipMemsetAsync(c->dkv, 0, dflash_kv_pool_bytes(cfg, dcfg->layers, cap), stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->dkv, 0, dflash_drafter_pool_bytes(cfg, dcfg, cap), stream);
   if (e == hipSuccess) e = hipMemsetAsync(c->ws + c->L.state, 0, c->L.rows[0][0] - c->L.state, stream);
   if (e == hipSuccess)
     e = hipMemsetAsync(c->ws + c->L.bt, 0xff, sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq, stream);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(c->ws + c->L.dbt, 0xff, sizeof(int32_t) * cap->max_slots * cap->max_pages_per_seq, stream);
   if (e == hipSuccess)
     e = launch_rope_table(c->wsp<float2>(c->L.rope), cfg->rope_theta, cfg->head_dim, c->rope_rows(), stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -822,6 +853,12 @@ dflash_status dflash_kv_alloc(dflash_ctx *c, int32_t slot, int32_t n_tokens) {
   }
   hipError_t e = hipMemcpy(c->bt() + (size_t)slot * c->cap.max_pages_per_seq + have, pg.data() + have,
                            sizeof(int32_t) * (need - have), hipMemcpyHostToDevice);
+  if (e == hipSuccess && c->dring) {  // the drafter's ring: page index i of the slot -> slot * dring + i % dring
+    std::vector<int32_t> ring(need - have);
+    for (int i = have; i < need; ++i) ring[i - have] = slot * c->dring + i % c->dring;
+    e = hipMemcpy(c->dbt() + (size_t)slot * c->cap.max_pages_per_seq + have, ring.data(), sizeof(int32_t) * ring.size(),
+                  hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     for (int i = need - 1; i >= have; --i) {
       c->free_pages.push_back(pg[i]);
@@ -840,6 +877,9 @@ dflash_status dflash_kv_free(dflash_ctx *c, int32_t slot) {
     std::vector<int32_t> neg(pg.size(), -1);
     hipError_t e = hipMemcpy(c->bt() + (size_t)slot * c->cap.max_pages_per_seq, neg.data(), sizeof(int32_t) * neg.size(),
                              hipMemcpyHostToDevice);
+    if (e == hipSuccess && c->dring)
+      e = hipMemcpy(c->dbt() + (size_t)slot * c->cap.max_pages_per_seq, neg.data(), sizeof(int32_t) * neg.size(),
+                    hipMemcpyHostToDevice);
     if (e != hipSuccess) return fail(DFLASH_E_DEVICE, "block-table clear: %s", hipGetErrorString(e));
     for (int i = (int)pg.size() - 1; i >= 0; --i) c->free_pages.push_back(pg[i]);
     pg.clear();
@@ -1076,6 +1116,13 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   // context keys k > p - W; so rows before Q - nd - W are skipped (never computed, never stored).
   const int Q = c->last_qlen;
   const int skip = (dc.window > 0 && c->last_nd >= 0) ? std::max(0, Q - c->last_nd - dc.window) : 0;
+  // With the drafter's page ring, the positions one call touches (injected rows from n - nd - W, reads
+  // from n - W + 1, block rows and injected rows up to n + max(B, nd) - 1, where n >= n0 + Q - nd after an
+  // accept of nd drafts of a block at n0) must not alias modulo the ring's R * pt positions.
+  const int ring_pos = c->dring * c->cap.page_tokens;
+  if (c->dring && (c->last_nd < 0 || dc.window + c->last_nd + std::max(B, c->last_nd) > ring_pos))
+    return fail(DFLASH_E_STATE, "with a windowed drafter, draft_block must follow an accept of at most %d drafts",
+                (ring_pos - dc.window) / 2);
   const int L = Q - skip, Ri = batch * L;
   Rows ri = c->rows(1);
   PrepArgs p;
@@ -1113,7 +1160,7 @@ dflash_status draft_block_impl(dflash_ctx *c, hipStream_t s, int32_t batch, cons
   {
     GemmArgs a = gemm_base(c->wsp<void>(c->L.xn), H, Ri, dc.layers * 2 * KD, H, EPI_PARTIAL);
     a.nseg = 2 * dc.layers;
-    QkvPostArgs p = post_base(c, ri, Ri);
+    QkvPostArgs p = post_base(c, ri, Ri, true);  // the drafter's K / V
     p.ld_src = dc.layers * 2 * KD;
     p.nseg = 2 * dc.layers;
     for (int j = 0; j < dc.layers; ++j) {

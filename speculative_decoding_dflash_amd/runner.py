@@ -57,7 +57,7 @@ class Engine:
                                    weights["d.final_norm"].data_ptr(), self._dl, ptr("d.sel_u"), ptr("d.sel_v"))
         u8 = dict(dtype=torch.uint8, device=self.device)
         self.tkv = torch.empty(B.dflash_kv_pool_bytes(self.mc, t.layers, self.cap), **u8)
-        self.dkv = torch.empty(B.dflash_kv_pool_bytes(self.mc, d.layers, self.cap), **u8)
+        self.dkv = torch.empty(B.dflash_drafter_pool_bytes(self.mc, self.dc, self.cap), **u8)
         ws = B.dflash_workspace_bytes(self.mc, self.dc, self.cap)
         if ws == 0:
             raise B.DflashError(B.E_INVAL, "configuration rejected by dflash_workspace_bytes")

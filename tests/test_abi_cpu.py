@@ -50,6 +50,18 @@ def test_sizes_and_validation():
     assert ws > 0
     # KV pool: layers * pages * 2 * kv_heads * 16 * head_dim * 2 bytes
     assert B.dflash_kv_pool_bytes(mc, 8, cap) == 8 * 256 * 2 * 8 * 16 * 64 * 2
+    # the drafter's pool: every page without a window; with one, a ring of
+    # ceil((W + 2 B) / 16) + 1 pages per slot, unless that is not smaller
+    page = 2 * 8 * 16 * 64 * 2
+    dc.window = 0
+    assert B.dflash_drafter_pool_bytes(mc, dc, cap) == B.dflash_kv_pool_bytes(mc, dc.layers, cap)
+    r200 = -(-(200 + 2 * dc.block_size) // 16) + 1
+    for w, pages, ring in ((64, 256, -(-(64 + 2 * dc.block_size) // 16) + 1), (200, 256, r200),
+                           (200, 4 * r200, 0), (1000, 256, 0), (4096, 256, 0)):
+        dc.window, cap.num_pages = w, pages
+        want = dc.layers * cap.max_slots * ring * page if ring else B.dflash_kv_pool_bytes(mc, dc.layers, cap)
+        assert B.dflash_drafter_pool_bytes(mc, dc, cap) == want, (w, pages)
+    cap.num_pages = 256
     for bad in (dict(head_dim=48), dict(q_heads=12), dict(block_size=0), dict(block_size=17), dict(mask_id=32000),
                 dict(page_tokens=8), dict(max_slots=65), dict(window=-1), dict(hidden=1000), dict(dtype=7)):
         mc, dc, cap = _cfgs(**bad)

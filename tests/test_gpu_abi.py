@@ -97,6 +97,42 @@ def test_out_of_order_calls_refused():
     eng.close()
 
 
+def test_windowed_drafter_page_ring():
+    """A windowed drafter recycles a ring of ceil((W + 2 B) / 16) + 1 pages per slot: its pool is that
+    size (the full pool when the page pool is no larger than the rings), a draft straight after a
+    verify -- no accept to say which rows were committed -- is refused with DFLASH_E_STATE, and a
+    greedy run whose context wraps the ring several times is bit-identical (tokens and every verify
+    logit) to the same run on a context whose drafter uses the target's page ids."""
+    from dataclasses import replace
+
+    from speculative_decoding_dflash_amd import binding as Bd
+    cfg = replace(synth.TINY, drafter=replace(synth.TINY.drafter, window=24), prompt_len=96)
+    W = sw.model_weights(cfg)
+    P, B, n = cfg.prompt_len, cfg.drafter.block_size, 40
+    R = -(-(24 + 2 * B) // 16) + 1
+    g = samp(synth.GREEDY)
+    runs = []
+    for ring in (True, False):
+        eng = engine(cfg, W, max_slots=4, **({} if ring else dict(num_pages=4 * R)))
+        page = 2 * cfg.target.kv_heads * 16 * cfg.target.head_dim * 4
+        full = Bd.dflash_kv_pool_bytes(eng.mc, cfg.drafter.layers, eng.cap)
+        assert eng.dkv.numel() == (cfg.drafter.layers * 4 * R * page if ring else full)
+        eng.kv_alloc(0, P + n + 2 * B)
+        if ring:  # (the pool without the ring holds one such slot)
+            eng.kv_alloc(1, P + 2 * B)
+            eng.verify([1], _prompt(cfg, 1), P, True, 1)
+            with pytest.raises(Bd.DflashError) as e:
+                Bd.dflash_draft_block(eng.ctx, [1], eng.feats, eng.block, None)
+            assert e.value.status == Bd.E_STATE
+            eng.accept([1], 0, [g])
+            Bd.dflash_draft_block(eng.ctx, [1], eng.feats, eng.block, None)
+        runs.append(_greedy_run(eng, 0, _prompt(cfg, 0), n, g))
+        eng.close()
+    assert P + n > 2 * R * 16 and runs[0][0] == runs[1][0]
+    assert all(torch.equal(a, b) for a, b in zip(runs[0][1], runs[1][1]))
+    log(f"[drafter ring] {R} pages per slot, {len(runs[0][1])} verify steps bit-identical")
+
+
 def test_bad_token_raises_device_flag():
     """A token id outside [0, vocab) is a condition only the device sees: the verify is accepted on the
     host, the row preparation substitutes a safe id and raises its sticky flag, dflash_device_status
