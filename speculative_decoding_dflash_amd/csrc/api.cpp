@@ -63,7 +63,8 @@ struct Layout {
 // live at ring position p mod R pt (page index i in ring page i mod R).  0 (no ring: the drafter shares
 // the target's page ids) without a window, or when the ring would not make the drafter pool smaller.
 int drafter_ring_pages(const dflash_drafter_cfg *d, const dflash_capacity *cap) {
-  if (d->window <= 0 || cap->page_tokens < 1) return 0;
+  static const bool off = getenv("DFLASH_DRAFTER_RING") && atoi(getenv("DFLASH_DRAFTER_RING")) == 0;  // A/B runs
+  if (off || d->window <= 0 || cap->page_tokens < 1) return 0;
   const int r = (d->window + 2 * d->block_size + cap->page_tokens - 1) / cap->page_tokens + 1;
   return r < cap->max_pages_per_seq && (int64_t)cap->max_slots * r < cap->num_pages ? r : 0;
 }
