@@ -861,6 +861,12 @@ dflash_status dflash_kv_alloc(dflash_ctx *c, int32_t slot, int32_t n_tokens) {
                   hipMemcpyHostToDevice);
   }
   if (e != hipSuccess) {
+    // best effort: the new entries of both tables back to "no page", so that no kernel reaches pages
+    // returned to the pool through this slot
+    const std::vector<int32_t> neg(need - have, -1);
+    for (int32_t *t : {c->bt(), c->dbt()})
+      (void)hipMemcpy(t + (size_t)slot * c->cap.max_pages_per_seq + have, neg.data(), sizeof(int32_t) * neg.size(),
+                      hipMemcpyHostToDevice);
     for (int i = need - 1; i >= have; --i) {
       c->free_pages.push_back(pg[i]);
       pg.pop_back();
