@@ -104,3 +104,40 @@ def test_op_linear_sk_rejects_bad_arguments_on_the_host():
         a = {**ok, **over}
         st = lib.dflash_op_linear_sk(None, a["dtype"], a["M"], a["N"], a["K"], a["x"], a["w"], a["y"], a["s"], a["b"])
         assert st == B.E_INVAL, over
+
+
+@pytest.mark.parametrize("window,block", [(24, 4), (32, 8), (64, 16), (100, 16), (2048, 16)])
+def test_drafter_ring_never_loses_a_visible_key(window, block):
+    """The drafter's page ring (ring size R read back from dflash_drafter_pool_bytes) against a
+    simulation of the positions each draft call touches, over random accept lengths: a prefill, then
+    draft / block verify / accept steps.  A draft after an accept of nd drafts of a verify of Q rows at
+    n0 injects rows [n0 + max(0, Q - nd - W), n0 + Q), writes its block rows [n, n + B) and reads context
+    keys [n - W + 1, n) and the block.  Checked: the positions one call touches are distinct modulo the
+    ring's R x 16 positions, and every key a call reads still holds its own position in the ring."""
+    from speculative_decoding_dflash_amd import binding as B
+    import numpy as np
+    mc, dc, cap = _cfgs(window=window, block_size=block)
+    cap.max_slots, cap.max_pages_per_seq, cap.num_pages = 2, 4096, 8192
+    page = 2 * mc.kv_heads * 16 * mc.head_dim * 2
+    nbytes = B.dflash_drafter_pool_bytes(mc, dc, cap)
+    R = nbytes // (dc.layers * cap.max_slots * page)
+    assert R * dc.layers * cap.max_slots * page == nbytes and R == -(-(window + 2 * block) // 16) + 1
+    span = R * 16
+    rng = np.random.default_rng(window * 31 + block)
+    for trial in range(6):
+        ring = {}
+        P = int(rng.integers(1, 3 * window + 40))
+        n0, Q, nd, n = 0, P, 0, P  # the prefill, accepted: P rows committed
+        for step in range(60):
+            skip = max(0, Q - nd - window)
+            writes = list(range(n0 + skip, n0 + Q)) + list(range(n, n + block))
+            reads = list(range(max(0, n - window + 1), n + block))
+            touched = set(writes) | set(reads)
+            assert len({p % span for p in touched}) == len(touched), (trial, step)
+            for p in writes:
+                ring[p % span] = p
+            for p in reads:
+                assert ring.get(p % span) == p, (trial, step, p)
+            # block verify at n, accept of tau in 1 .. B (nd = B - 1 drafts)
+            n0, Q, nd = n, block, block - 1
+            n = n + int(rng.integers(1, block + 1))
