@@ -304,7 +304,15 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   // per-CU rate estimates (MI355X): ~60% of the dense fp16 MFMA peak, ~70% of an even share of HBM
   const double mfma_us = (double)bm * 32 * kBK * 2 / (0.6 * 2.5e15 / 256) * 1e6;  // one unit x one K step
   const double mem_us = (32.0 * kBK * 2) / (0.7 * 8e12 / 256) * 1e6;
+  // 64-row tiles also pay a fixed ~0.6 us per K step (a fit to 64-row down / o / q-k-v launches: 1.24
+  // us per step at 3 units of a chunk, 1.39 at 4, 1.08 at 2), so that fewer, longer-ranged steps win
+  // there: 8 K ranges over 2 work-groups per CU measured 13% (down), 15% (q/k/v) and 6% (o) faster
+  // than the plans without it.  Among equal estimates such calls take the most work-groups.
+  static const bool step_cost = env_int("DFLASH_TC_STEP", 1) != 0;  // 0: without it (A/B runs)
+  const double step_us = step_cost && bm == 64 ? 0.6 : 0.0;
+  const bool more_wgs = step_cost && bm == 64 && a.epi == EPI_PARTIAL;
   double best = 1e30;
+  int best_wgs = 0;
   TcPlan bp{};
   const int smax = a.epi == EPI_PARTIAL ? kTcMaxRanges : 1;
   for (int s = 1; s <= smax; ++s) {
@@ -321,11 +329,12 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
         const int rounds = (wgs + slots - 1) / slots;
         const int umax = (units + nch - 1) / nch;
         // a K step also stages BM X rows (from L2), worth about bm / 64 units of weight streaming
-        const double per = (umax + bm / 64.0) * steps * std::max(mfma_us, mem_us) + 1.5;
+        const double per = (umax + bm / 64.0) * steps * std::max(mfma_us, mem_us) + steps * step_us + 1.5;
         const double t = rounds * per + (s > 1 ? (double)s * a.M * a.N * 8 / 5e12 * 1e6 : 0.0);
-        if (t < best - 1e-9) {
+        if (t < best - 1e-9 || (more_wgs && t < best + 1e-9 && wgs > best_wgs)) {
           best = t;
-          bp = TcPlan{bm, um, nch, s, steps, nwv};  // ties keep the smaller unit count
+          best_wgs = wgs;
+          bp = TcPlan{bm, um, nch, s, steps, nwv};  // other ties keep the smaller unit count
         }
       }
     }
