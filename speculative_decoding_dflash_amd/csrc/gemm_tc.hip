@@ -293,13 +293,19 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   // 256-row tiles: eight waves (two per SIMD; DFLASH_TC_W8=0: four) with 5 or 6 units per chunk (6 only
   // where it saves a round of work-groups: a chunk of 6 runs a few per cent slower per unit); 64- and
   // 128-row tiles: four waves, 4 units.  DFLASH_TC_UM fixes the unit count.
+  // SwiGLU projections on 64-row tiles (no K ranges: the epilogue needs whole sums) plan for one
+  // work-group per CU with chunks of up to 6 units: two work-groups on one CU share its LDS and run at
+  // about half speed each, so 363 chunks of 3 (27B gate/up, 64 rows) took 93 us against 78.5 us for 218
+  // chunks of 5 alone on their CUs.  DFLASH_TC_STEP=0 switches this and the step cost below off.
+  static const bool step_cost = env_int("DFLASH_TC_STEP", 1) != 0;
   const int env_um = env_int("DFLASH_TC_UM", 0);
+  const bool glu64 = step_cost && bm == 64 && swiglu && env_um == 0;
   const int nwv = bm == 256 && env_int("DFLASH_TC_W8", 1) ? 8 : 4;
-  const int um_lo = bm != 256 ? 4 : (env_um == 4 && nwv == 4) || (env_um == 6 && nwv == 8) ? env_um : 5;
-  const int um_hi = bm == 256 && nwv == 8 && env_um == 0 ? 6 : um_lo;
+  const int um_lo = bm == 64 && env_um == 6 ? 6 : bm != 256 ? 4 : (env_um == 4 && nwv == 4) || (env_um == 6 && nwv == 8) ? env_um : 5;
+  const int um_hi = glu64 ? 6 : bm == 256 && nwv == 8 && env_um == 0 ? 6 : um_lo;
   const int units = swiglu ? a.N / 16 : a.N / 32;
   const int rt = (a.M + bm - 1) / bm, nk = a.K / kBK;
-  const int slots = cu_count() * (bm == 256 ? 1 : 2);
+  const int slots = cu_count() * (bm == 256 || glu64 ? 1 : 2);
   const int env_s = env_int("DFLASH_TC_S", 0), env_nch = env_int("DFLASH_TC_NCH", 0);
   // per-CU rate estimates (MI355X): ~60% of the dense fp16 MFMA peak, ~70% of an even share of HBM
   const double mfma_us = (double)bm * 32 * kBK * 2 / (0.6 * 2.5e15 / 256) * 1e6;  // one unit x one K step
@@ -308,7 +314,6 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   // us per step at 3 units of a chunk, 1.39 at 4, 1.08 at 2), so that fewer, longer-ranged steps win
   // there: 8 K ranges over 2 work-groups per CU measured 13% (down), 15% (q/k/v) and 6% (o) faster
   // than the plans without it.  Among equal estimates such calls take the most work-groups.
-  static const bool step_cost = env_int("DFLASH_TC_STEP", 1) != 0;  // 0: without it (A/B runs)
   const double step_us = step_cost && bm == 64 ? 0.6 : 0.0;
   const bool more_wgs = step_cost && bm == 64 && a.epi == EPI_PARTIAL;
   double best = 1e30;
@@ -322,6 +327,7 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
     const int ranges = (nk + steps - 1) / steps;
     if (ranges != s) continue;
     for (int um = um_lo; um <= um_hi; ++um) {
+      if (bm == 64 && um == 5) continue;  // 64-row tiles split a chunk over four waves: an even unit count
       const int nmin = (units + um - 1) / um;
       for (int nch = nmin; nch <= std::min(units, nmin * 4); ++nch) {
         if (env_nch > 0 && nch != env_nch) continue;
@@ -359,7 +365,10 @@ static void launch_stg(const GemmArgs &a, const TcPlan &p, dim3 grid, hipStream_
   } else if (p.bm == 128) {
     hipExtLaunchKernelGGL((gemm_tc_kernel<128, 4, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   } else {
-    hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    if (p.um == 6)
+      hipExtLaunchKernelGGL((gemm_tc_kernel<64, 6, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
+    else
+      hipExtLaunchKernelGGL((gemm_tc_kernel<64, 4, STG, 4, PIPE>), grid, b4, 0, s, e0, e1, 0, a, p.nch, p.steps);
   }
 }
 
