@@ -293,13 +293,14 @@ bool gemm_tc_plan(const GemmArgs &a, int64_t range_cap, TcPlan *p) {
   // 256-row tiles: eight waves (two per SIMD; DFLASH_TC_W8=0: four) with 5 or 6 units per chunk (6 only
   // where it saves a round of work-groups: a chunk of 6 runs a few per cent slower per unit); 64- and
   // 128-row tiles: four waves, 4 units.  DFLASH_TC_UM fixes the unit count.
-  // SwiGLU projections on 64-row tiles (no K ranges: the epilogue needs whole sums) plan for one
+  // The decode layers' projections on 64-row tiles (SwiGLU, and K-range partials) plan for one
   // work-group per CU with chunks of up to 6 units: two work-groups on one CU share its LDS and run at
-  // about half speed each, so 363 chunks of 3 (27B gate/up, 64 rows) took 93 us against 78.5 us for 218
-  // chunks of 5 alone on their CUs.  DFLASH_TC_STEP=0 switches this and the step cost below off.
+  // about half speed each.  27B, 64 rows: gate/up in 363 chunks of 3 took 93 us against 78.5 us for 218
+  // chunks of 5-6 alone on their CUs; down in 8 K ranges 42.3 against 36.8 us.  DFLASH_TC_STEP=0
+  // switches this and the step cost below off.
   static const bool step_cost = env_int("DFLASH_TC_STEP", 1) != 0;
   const int env_um = env_int("DFLASH_TC_UM", 0);
-  const bool glu64 = step_cost && bm == 64 && swiglu && env_um == 0;
+  const bool glu64 = step_cost && bm == 64 && env_um == 0 && (swiglu || a.epi == EPI_PARTIAL);
   const int nwv = bm == 256 && env_int("DFLASH_TC_W8", 1) ? 8 : 4;
   const int um_lo = bm == 64 && env_um == 6 ? 6 : bm != 256 ? 4 : (env_um == 4 && nwv == 4) || (env_um == 6 && nwv == 8) ? env_um : 5;
   const int um_hi = glu64 ? 6 : bm == 256 && nwv == 8 && env_um == 0 ? 6 : um_lo;
